@@ -1,0 +1,500 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Nothing here compares the oracle with itself or retypes its arithmetic: each
+test checks a law, a printed value, a closed form or a special case, and the
+planted-mistake variants of the oracle (``oracle.MUT_*``) show that the checks
+have the power to catch the plausible mistakes.
+"""
+import os
+
+import numpy as np
+import pytest
+import scipy.stats
+import torch
+
+import oracle
+import synthetic
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    if not os.path.exists(oracle.LIB_PATH):
+        oracle.build()
+    oracle.lib()
+
+
+def u24(rng, shape):
+    return (rng.integers(0, 1 << 24, size=shape) / float(1 << 24)).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Closed forms printed on the pages
+# ---------------------------------------------------------------------------
+def expected_tokens(a, k):
+    # production blog, "Predicting the speedup": (1 - a^(k+1)) / (1 - a)
+    return (1 - a ** (k + 1)) / (1 - a)
+
+
+def pgf_coefficients(a, k):
+    """Coefficients of phi(x) = 1 + (x-1)(1 - a^(k+1) x^(k+1))/(1 - a x)
+    (Cascade Speculative Drafting, Theorem 4.1), expanded by polynomial algebra:
+    (1 - (ax)^(k+1))/(1 - ax) is the finite geometric sum of (ax)^j, j <= k."""
+    geo = np.array([a ** j for j in range(k + 1)])
+    poly = np.zeros(k + 2)
+    poly[0] += 1.0
+    poly[1:] += geo          # x * geo
+    poly[:-1] -= geo         # -1 * geo
+    return poly
+
+
+def test_golden_blog_values():
+    """The closed forms reproduce every number the blog prints."""
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "blog_expected_tokens.txt"))
+            if l.strip() and not l.startswith("#")]
+    assert len(rows) == 5
+    for kind, a, k, c, val, dec in rows:
+        a, k, val, dec = float(a), int(k), float(val), int(dec)
+        e = expected_tokens(a, k)
+        got = e if kind == "expected_tokens" else e / (k * float(c) + 1)
+        assert round(got, dec) == pytest.approx(val), (kind, a, k, got, val)
+
+
+@pytest.mark.parametrize("a,k", [(0.8, 4), (0.6, 4), (0.39, 16), (0.5, 1)])
+def test_pgf_expansion_matches_printed_coefficients(a, k):
+    """Theorem 4.1 of the Cascade page: the x^i coefficient is a^(i-1) - a^i
+    for 1 <= i <= k and a^k for i = k+1; phi'(1) is the blog's expected value.
+    The coefficient of x^i is read as P(i tokens committed in the round)."""
+    c = pgf_coefficients(a, k)
+    assert abs(c[0]) < 1e-15
+    for i in range(1, k + 1):
+        assert c[i] == pytest.approx(a ** (i - 1) - a ** i, abs=1e-14)
+    assert c[k + 1] == pytest.approx(a ** k, abs=1e-14)
+    assert c.sum() == pytest.approx(1.0, abs=1e-14)
+    assert (np.arange(k + 2) * c).sum() == pytest.approx(expected_tokens(a, k), abs=1e-12)
+
+
+def iid_acceptance_rows(a, rng):
+    """V = 8.  m: a mixture over tokens 0..5.  p = a m + (1-a) e7, q = a m + (1-a) e6.
+    A draft x ~ q is then accepted with certainty when x < 6 (p = q there) and
+    never when x = 6 (p = 0), so acceptance is Bernoulli(a), independently per
+    position, and sum_v min(p_v, q_v) = a."""
+    m = rng.dirichlet(np.ones(6))
+    p = np.zeros(8)
+    q = np.zeros(8)
+    p[:6] = a * m
+    q[:6] = a * m
+    p[7] = 1 - a
+    q[6] = 1 - a
+    with np.errstate(divide="ignore"):
+        return np.log(p).astype(np.float32), np.log(q).astype(np.float32), q
+
+
+def run_iid_rounds(a, k, n, seed, mutation=oracle.MUT_NONE):
+    rng = np.random.default_rng(seed)
+    zl, yl, q = iid_acceptance_rows(a, rng)
+    z = np.broadcast_to(zl, (n, k + 1, 8)).copy()
+    y = np.broadcast_to(yl, (n, k, 8)).copy()
+    x = rng.choice(8, size=(n, k), p=q / q.sum()).astype(np.int32)
+    u = u24(rng, (n, k + 1))
+    _, na = oracle.sample(z, y, x, u, 1.0, mutation=mutation)
+    return na + 1  # committed tokens per round
+
+
+@pytest.mark.parametrize("a,k", [(0.8, 4), (0.6, 4)])
+def test_iid_acceptance_mean_and_law(a, k):
+    """Mean committed tokens per round = (1 - a^(k+1))/(1 - a) (blog: 3.36 at
+    a = 0.8, 2.31 at a = 0.6, k = 4) within 4 standard errors, and the full
+    committed-count histogram follows the Theorem 4.1 coefficients."""
+    n = 200_000
+    committed = run_iid_rounds(a, k, n, seed=11)
+    coef = pgf_coefficients(a, k)[1:]
+    mean = (np.arange(1, k + 2) * coef).sum()
+    sd = np.sqrt((np.arange(1, k + 2) ** 2 * coef).sum() - mean ** 2)
+    assert abs(committed.mean() - expected_tokens(a, k)) < 4 * sd / np.sqrt(n)
+    hist = np.bincount(committed, minlength=k + 2)[1:]
+    chi = scipy.stats.chisquare(hist, coef * n)
+    assert chi.pvalue > 1e-4, (hist, coef * n)
+
+
+def test_iid_acceptance_detects_inverted_ratio():
+    committed = run_iid_rounds(0.8, 4, 50_000, seed=12, mutation=oracle.MUT_RATIO_INVERTED)
+    assert abs(committed.mean() - expected_tokens(0.8, 4)) > 0.2
+
+
+# ---------------------------------------------------------------------------
+# Exact law of the committed tokens at V = 8 (brute force over the draft token
+# and exact integration over the uniforms by bisection on the 2^-24 grid)
+# ---------------------------------------------------------------------------
+GRID = 1 << 24
+
+
+class Probe:
+    """Calls the oracle on one fixed set of rows with many uniform vectors."""
+
+    def __init__(self, P, Q, T, mutation):
+        self.k = Q.shape[0]
+        V = P.shape[1]
+        with np.errstate(divide="ignore"):
+            self.z = (T * np.log(P)).astype(np.float32)
+            self.y = (T * np.log(Q)).astype(np.float32)
+        self.T = T
+        self.mut = mutation
+        self.V = V
+
+    def run(self, x, U):
+        n = U.shape[0]
+        z = np.broadcast_to(self.z, (n,) + self.z.shape).copy()
+        y = np.broadcast_to(self.y, (n,) + self.y.shape).copy()
+        xx = np.broadcast_to(np.asarray(x, np.int32), (n, self.k)).copy()
+        return oracle.sample(z, y, xx, U.astype(np.float32), self.T, mutation=self.mut)
+
+    def measure(self, x, base_u, coord, pred):
+        """Number of grid points g in [0, 2^24) with pred(out(u[coord] = g/2^24))
+        true, for predicates that hold on an initial segment; vectorised over a
+        batch of predicates (pred returns a bool array over the batch)."""
+        npred = pred(None)
+        lo = np.zeros(npred, np.int64)
+        hi = np.full(npred, GRID, np.int64)
+        while np.any(lo < hi):
+            mid = (lo + hi) // 2
+            U = np.broadcast_to(base_u, (npred, base_u.size)).copy()
+            U[:, coord] = mid / GRID
+            tokens, na = self.run(x, U)
+            ok = pred((tokens, na))
+            act = lo < hi
+            lo = np.where(act & ok, mid + 1, lo)
+            hi = np.where(act & ~ok, mid, hi)
+        return lo / GRID
+
+
+def committed_law(P, Q, T, mutation=oracle.MUT_NONE):
+    """Exact law (on the uniform grid) of the token committed at each position i,
+    given that the round reaches i, and the acceptance probability at i."""
+    k, V = Q.shape
+    pr = Probe(P, Q, T, mutation)
+    # a draft that is surely accepted with u = 0 (p > 0 there) for the prefix
+    safe = [int(np.argmax(np.minimum(P[i], Q[i]) + 1e-3 * (P[i] > 0))) for i in range(k)]
+    laws, acc = [], []
+    for i in range(k):
+        law = np.zeros(V)
+        a_tot = 0.0
+        for xv in range(V):
+            if Q[i, xv] == 0:
+                continue
+            x = safe.copy()
+            x[i] = xv
+            base = np.zeros(k + 1)
+            a = pr.measure(x, base, i, lambda r: 1 if r is None else (r[1] > i))[0]
+            a_tot += Q[i, xv] * a
+            law[xv] += Q[i, xv] * a
+            if a < 1.0:
+                base[i] = a          # the first grid point that rejects
+                cdf = pr.measure(x, base, k,
+                                 lambda r: V if r is None else (r[0][:, i] <= np.arange(V)))
+                law += Q[i, xv] * (1 - a) * np.diff(np.concatenate([[0.0], cdf]))
+        laws.append(law)
+        acc.append(a_tot)
+    # bonus: every draft accepted
+    x = safe.copy()
+    base = np.zeros(k + 1)
+    cdf = pr.measure(x, base, k, lambda r: V if r is None else (r[0][:, k] <= np.arange(V)))
+    assert all(P[i, safe[i]] > 0 for i in range(k))
+    laws.append(np.diff(np.concatenate([[0.0], cdf])))
+    return np.array(laws), np.array(acc)
+
+
+def v8_cases():
+    rng = np.random.default_rng(5)
+    k = 3
+    cases = []
+    # generic: full support
+    cases.append(("dirichlet", rng.dirichlet(np.ones(8), k + 1), rng.dirichlet(np.ones(8), k), 1.0))
+    # temperature other than 1, uneven distributions
+    cases.append(("peaked_T0.7", rng.dirichlet(0.3 * np.ones(8), k + 1),
+                  rng.dirichlet(0.3 * np.ones(8), k), 0.7))
+    # masked tokens (zero probability, logit -inf) on both sides
+    P = rng.dirichlet(np.ones(8), k + 1)
+    Q = rng.dirichlet(np.ones(8), k)
+    P[:, [1, 5]] = 0
+    Q[:, [2, 5]] = 0
+    P /= P.sum(1, keepdims=True)
+    Q /= Q.sum(1, keepdims=True)
+    cases.append(("masked_T1.6", P, Q, 1.6))
+    # disjoint supports: every draft is rejected, the residual is p
+    P = np.zeros((k + 1, 8))
+    Q = np.zeros((k, 8))
+    P[:, :4] = rng.dirichlet(np.ones(4), k + 1)
+    Q[:, 4:] = rng.dirichlet(np.ones(4), k)
+    cases.append(("disjoint", P, Q, 1.0))
+    return cases
+
+
+@pytest.mark.parametrize("name,P,Q,T", v8_cases(), ids=lambda v: v if isinstance(v, str) else "")
+def test_v8_committed_token_is_target_distributed(name, P, Q, T):
+    """Blog, "The acceptance rule": every committed token is distributed exactly
+    as a sample from the target; the acceptance probability at a position is
+    sum_v min(p_v, q_v) (the standard identity for x ~ q kept w.p. min(1, p/q))."""
+    laws, acc = committed_law(P, Q, T)
+    k = Q.shape[0]
+    for i in range(k + 1):
+        np.testing.assert_allclose(laws[i], P[i], atol=2e-6, err_msg=f"{name} position {i}")
+    np.testing.assert_allclose(acc, np.minimum(P[:k], Q).sum(1), atol=2e-6)
+
+
+@pytest.mark.parametrize("mutation", [oracle.MUT_RESIDUAL_IS_P, oracle.MUT_RESIDUAL_IS_Q,
+                                      oracle.MUT_BONUS_FROM_Q, oracle.MUT_RATIO_INVERTED,
+                                      oracle.MUT_RESIDUAL_SIGN])
+def test_v8_law_catches_planted_mistakes(mutation):
+    name, P, Q, T = v8_cases()[0]
+    laws, acc = committed_law(P, Q, T, mutation)
+    k = Q.shape[0]
+    dev = max(np.abs(laws - P).max(), np.abs(acc - np.minimum(P[:k], Q).sum(1)).max())
+    assert dev > 1e-2, dev
+
+
+# ---------------------------------------------------------------------------
+# Histogram test with and without speculation (blog: compare token histograms
+# of continuations sampled with and without speculation)
+# ---------------------------------------------------------------------------
+def merged_two_sample_pvalue(a, b, V, min_pooled=40):
+    ca = np.bincount(a, minlength=V).astype(np.float64)
+    cb = np.bincount(b, minlength=V).astype(np.float64)
+    order = np.argsort(-(ca + cb), kind="stable")
+    groups_a, groups_b = [], []
+    acc_a = acc_b = 0.0
+    for t in order:
+        acc_a += ca[t]
+        acc_b += cb[t]
+        if acc_a + acc_b >= min_pooled:
+            groups_a.append(acc_a)
+            groups_b.append(acc_b)
+            acc_a = acc_b = 0.0
+    if acc_a + acc_b > 0 and groups_a:
+        groups_a[-1] += acc_a
+        groups_b[-1] += acc_b
+    table = np.array([groups_a, groups_b])
+    return scipy.stats.chi2_contingency(table)[1]
+
+
+def histogram_experiment(mutation, n=60_000, V=500, k=3, T=1.0, seed=21):
+    g = torch.Generator().manual_seed(seed)
+    z = torch.randn((k + 1, V), generator=g) * np.sqrt(2.0)
+    y = z[:k] + torch.randn((k, V), generator=g)
+    rng = np.random.default_rng(seed)
+    # without speculation: direct draws from each target row
+    direct = [synthetic.gumbel_max_sample(z[i:i + 1].expand(n, V), T, g).numpy() for i in range(k + 1)]
+    toks, nas = [], []
+    chunk = 4096
+    zz = z.numpy().astype(np.float32)
+    yy = y.numpy().astype(np.float32)
+    for s0 in range(0, n, chunk):
+        m = min(chunk, n - s0)
+        x = torch.stack([synthetic.gumbel_max_sample(y[i:i + 1].expand(m, V), T, g)
+                         for i in range(k)], dim=1).numpy()
+        u = u24(rng, (m, k + 1))
+        t, na = oracle.sample(np.broadcast_to(zz, (m, k + 1, V)).copy(),
+                              np.broadcast_to(yy, (m, k, V)).copy(), x, u, T, mutation=mutation)
+        toks.append(t)
+        nas.append(na)
+    toks = np.concatenate(toks)
+    nas = np.concatenate(nas)
+    pvals = []
+    for i in (0, 1, k):
+        reach = nas >= i
+        pvals.append(merged_two_sample_pvalue(toks[reach, i], direct[i][: reach.sum()], V))
+    return pvals, nas
+
+
+def test_histogram_with_and_without_speculation():
+    pvals, nas = histogram_experiment(oracle.MUT_NONE)
+    assert (nas == 3).sum() > 3000   # the bonus position is reached often enough
+    assert min(pvals) > 1e-4, pvals
+
+
+@pytest.mark.parametrize("mutation", [oracle.MUT_RESIDUAL_IS_P, oracle.MUT_RESIDUAL_IS_Q,
+                                      oracle.MUT_BONUS_FROM_Q, oracle.MUT_RESIDUAL_SIGN])
+def test_histogram_catches_planted_mistakes(mutation):
+    pvals, _ = histogram_experiment(mutation, n=30_000)
+    assert min(pvals) < 1e-6, pvals
+
+
+# ---------------------------------------------------------------------------
+# Special cases
+# ---------------------------------------------------------------------------
+def test_one_hot_rows_sampling_equals_greedy():
+    """Greedy collapse (blog, end of "The acceptance rule"; Double, D.2: with
+    T = 0 replacing a rejected draft by the target token is residual sampling):
+    with one-hot p and q the sampling rule gives the greedy result for any u."""
+    rng = np.random.default_rng(3)
+    n, k, V = 4000, 5, 16
+    ta = rng.integers(0, V, (n, k + 1))
+    xa = np.where(rng.random((n, k)) < 0.7, ta[:, :k], rng.integers(0, V, (n, k)))
+    z = np.full((n, k + 1, V), -np.inf, np.float32)
+    y = np.full((n, k, V), -np.inf, np.float32)
+    np.put_along_axis(z, ta[..., None], 0.0, axis=2)
+    np.put_along_axis(y, xa[..., None], 0.0, axis=2)
+    u = u24(rng, (n, k + 1))
+    ts, ns = oracle.sample(z, y, xa, u, 1.0)
+    tg, ng = oracle.greedy(z, xa)
+    np.testing.assert_array_equal(ns, ng)
+    np.testing.assert_array_equal(ts, tg)
+
+
+def test_low_temperature_sampling_equals_greedy():
+    """The T -> 0 limit of the sampling rule is the greedy rule."""
+    rng = np.random.default_rng(4)
+    n, k, V = 500, 4, 64
+    z = rng.integers(-20, 20, (n, k + 1, V)).astype(np.float32)
+    y = rng.integers(-20, 20, (n, k, V)).astype(np.float32)
+    # unique maxima, a margin of 1 above the rest
+    tz = rng.integers(0, V, (n, k + 1))
+    ty = np.where(rng.random((n, k)) < 0.6, tz[:, :k], rng.integers(0, V, (n, k)))
+    np.put_along_axis(z, tz[..., None], 21.0, axis=2)
+    np.put_along_axis(y, ty[..., None], 21.0, axis=2)
+    x = ty.astype(np.int32)          # the draft's (almost sure) sample
+    u = np.clip(u24(rng, (n, k + 1)), 1e-3, 1 - 1e-3).astype(np.float32)
+    ts, ns = oracle.sample(z, y, x, u, 0.01)
+    tg, ng = oracle.greedy(z, x)
+    np.testing.assert_array_equal(ns, ng)
+    np.testing.assert_array_equal(ts, tg)
+
+
+def test_identical_target_and_draft_accepts_everything():
+    rng = np.random.default_rng(6)
+    n, k, V = 300, 6, 50
+    z = rng.normal(0, 2, (n, k + 1, V)).astype(np.float32)
+    y = z[:, :k].copy()
+    x = rng.integers(0, V, (n, k)).astype(np.int32)
+    u = u24(rng, (n, k + 1))
+    t, na = oracle.sample(z, y, x, u, 0.8)
+    assert (na == k).all()
+    np.testing.assert_array_equal(t[:, :k], x)
+    assert ((t[:, k] >= 0) & (t[:, k] < V)).all()
+
+
+def test_invalid_draft_token_is_rejected():
+    rng = np.random.default_rng(7)
+    n, k, V = 200, 4, 32
+    z = rng.normal(0, 1, (n, k + 1, V)).astype(np.float32)
+    y = z[:, :k].copy()                  # p = q: every valid token is accepted
+    x = np.argmax(z[:, :k], axis=2).astype(np.int32)   # and greedy accepts these
+    pos = rng.integers(0, k, n)
+    bad = np.where(rng.random(n) < 0.5, -1 - rng.integers(0, 5, n), V + rng.integers(0, 5, n))
+    x[np.arange(n), pos] = bad
+    u = u24(rng, (n, k + 1))
+    t, na = oracle.sample(z, y, x, u, 1.0)
+    np.testing.assert_array_equal(na, pos)
+    tg, ng = oracle.greedy(z, x)
+    np.testing.assert_array_equal(ng, pos)
+    assert ((t[np.arange(n), pos] >= 0) & (t[np.arange(n), pos] < V)).all()
+
+
+def test_greedy_argmax_is_first_maximum():
+    """Greedy against numpy's first-occurrence argmax on tie-heavy rows,
+    including -0.0 / +0.0 ties, all -inf rows (index 0) and NaN entries."""
+    rng = np.random.default_rng(8)
+    n, k, V = 2000, 3, 40
+    z = rng.integers(-3, 3, (n, k + 1, V)).astype(np.float32)
+    z[z == 0] = np.where(rng.random((z == 0).sum()) < 0.5, -0.0, 0.0)
+    z[::17] = -np.inf
+    nan_mask = rng.random(z.shape) < 0.02
+    z[nan_mask] = np.nan
+    ref = np.argmax(np.where(np.isnan(z), -np.inf, z), axis=2)
+    # drafts: the reference argmax at a random number of leading positions
+    j = rng.integers(0, k + 1, n)
+    x = rng.integers(0, V, (n, k))
+    for b in range(n):
+        x[b, :j[b]] = ref[b, :j[b]]
+    t, na = oracle.greedy(z, x.astype(np.int32))
+    for b in range(n):
+        jb = 0
+        while jb < k and x[b, jb] == ref[b, jb]:
+            jb += 1
+        assert na[b] == jb
+        exp = list(x[b, :jb]) + [ref[b, jb]] + [-1] * (k - jb)
+        np.testing.assert_array_equal(t[b], exp)
+
+
+def test_residual_mass_zero_falls_back_to_target():
+    """A rejection needs p(x) < q(x), and then some token has p > q, so the
+    residual total S is positive in exact arithmetic (the S = 0 reading, sample
+    from p, only guards rounding).  Every rejection here samples the residual and
+    every full acceptance the bonus row."""
+    rng = np.random.default_rng(9)
+    n, k, V = 2000, 3, 12
+    z = rng.normal(0, 1, (n, k + 1, V)).astype(np.float32)
+    y = (z[:, :k] + rng.normal(0, 1, (n, k, V))).astype(np.float32)
+    x = rng.integers(0, V, (n, k)).astype(np.int32)
+    u = u24(rng, (n, k + 1))
+    _, na, tr = oracle.sample(z, y, x, u, 1.0, traces=True)
+    kinds = np.array([t.sample_kind for t in tr])
+    assert set(kinds[na < k]) == {0}
+    assert set(kinds[na == k]) <= {1}
+
+
+# ---------------------------------------------------------------------------
+# Multi-candidate selection
+# ---------------------------------------------------------------------------
+def candidates_closed_form(a, C, L, prefix):
+    """E[A] when every token independently equals its row's argmax w.p. a, the
+    first `prefix` tokens shared by all C candidates: P(A >= n) = a^n for
+    n <= prefix, a^prefix (1 - (1 - a^(n - prefix))^C) beyond."""
+    e = 0.0
+    for n in range(1, L + 1):
+        if n <= prefix:
+            e += a ** n
+        else:
+            e += a ** prefix * (1 - (1 - a ** (n - prefix)) ** C)
+    return e
+
+
+def test_candidates_closed_form_expected_length():
+    assert candidates_closed_form(0.8, 8, 8, 2) == pytest.approx(5.18537, abs=1e-5)
+    rng = np.random.default_rng(10)
+    B, C, L, V = 20000, 8, 8, 16
+    R = L
+    z = rng.normal(0, 1, (B, C, R, V)).astype(np.float32)
+    spikes = rng.integers(0, V, (B, C, R))
+    spikes[:, :, :3] = spikes[:, :1, :3]
+    z[:, :, :3] = z[:, :1, :3]
+    np.put_along_axis(z, spikes[..., None], 100.0, axis=3)   # the argmax by construction
+    hit = rng.random((B, C, L)) < 0.8
+    other = (spikes[:, :, :L] + rng.integers(1, V, (B, C, L))) % V
+    cand = np.where(hit, spikes[:, :, :L], other)
+    cand[:, :, :2] = cand[:, :1, :2]
+    out, A, best = oracle.greedy_candidates(z, cand.astype(np.int32))
+    e = candidates_closed_form(0.8, C, L, 2)
+    assert abs(A.mean() - e) < 4 * A.std() / np.sqrt(B)
+
+
+def test_candidates_selection_properties():
+    """Ouroboros 3.4.3 selection: the committed prefix is the chosen candidate's
+    accepted tokens, no candidate has a longer accepted run, ties go to the lowest
+    candidate index, and the correction is the argmax at the first mismatch."""
+    rng = np.random.default_rng(11)
+    B, C, L, V = 3000, 4, 5, 6
+    for R in (L, L + 1):
+        z = rng.integers(0, 4, (B, C, R, V)).astype(np.float32)
+        ref = np.argmax(z, axis=3)
+        cand = np.where(rng.random((B, C, L)) < 0.75, ref[:, :, :L], rng.integers(0, V, (B, C, L)))
+        out, A, best = oracle.greedy_candidates(z, cand.astype(np.int32))
+        for b in range(B):
+            runs = []
+            for c in range(C):
+                a = 0
+                while a < L and cand[b, c, a] == ref[b, c, a]:
+                    a += 1
+                runs.append(a)
+            assert A[b] == max(runs)
+            assert best[b] == runs.index(max(runs))
+            cs = best[b]
+            np.testing.assert_array_equal(out[b, :A[b]], cand[b, cs, :A[b]])
+            if A[b] < L:
+                assert out[b, A[b]] == ref[b, cs, A[b]]
+                assert (out[b, A[b] + 1:] == -1).all()
+            elif R == L + 1:
+                assert out[b, L] == ref[b, cs, L]
+            else:
+                assert out[b, L] == -1
