@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Throughput of the verification step on one MI355X.
+
+A step is one spec_verify_sample call over workload 5: B = 512 sequences,
+k = 16 drafts, V = 128256, bf16 logits, T = 1.0 (the largest workload; all
+inputs already resident in HBM).  One call runs the whole hot path: the
+vocabulary-streaming statistics pass over every target and draft row, the
+per-sequence decisions, and the residual/bonus draw.  The metric counts
+verified positions: B * (k+1) rows per call.
+
+Prints one JSON line.  Also reports, for the dominant kernel (the statistics
+pass), its average duration from HIP events recorded on the launch stream
+during the timed region and its achieved HBM bandwidth against the 8 TB/s
+peak, and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "verified positions/sec (B·(k+1) rows/s) and achieved HBM GB/s vs peak"
+STATS_SOURCES = ["sv_stats.hip", "sv_device.h", "sv_launch.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_softmax_stats_workload5_traffic.json")
+
+
+def stats_kernel_digest() -> str:
+    h = hashlib.sha256()
+    for f in STATS_SOURCES:
+        with open(os.path.join(ROOT, "draft_verification_verify_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    h.update(open(os.path.join(ROOT, "draft_verification_verify_amd", "build.py"), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(bytes_algo: float):
+    """HBM bytes per launch of the statistics kernel from the committed
+    rocprofv3 counter runs, if they were taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_digest") != stats_kernel_digest():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--mode", default="sample", choices=["sample", "greedy", "candidates"],
+                    help="sample: workload 5 (the benchmark line); greedy: workload 5 greedy; "
+                         "candidates: workload 4")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU oracle baseline budget (0 disables it)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the verification step has no multi-GPU path in "
+              "this build (sequences shard over GPUs with no exchange); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import draft_verification_verify_amd as sv
+    import synthetic
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    cid = 4 if args.mode == "candidates" else 5
+    t0 = time.perf_counter()
+    w = synthetic.generate(cid, device=dev)
+    torch.cuda.synchronize()
+    gen_s = time.perf_counter() - t0
+    cfg = w.cfg
+    es = w.target.element_size()
+
+    if args.mode == "candidates":
+        B, C, R, V = w.target.shape
+        L = w.tokens.shape[2]
+        rows = B * C * R
+        out = (torch.empty((B, L + 1), dtype=torch.int32, device=dev),
+               torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev))
+        ws = torch.empty(sv.workspace_bytes(B, C * R, V, w.target.dtype), dtype=torch.uint8, device=dev)
+
+        def step():
+            sv.greedy_candidates(w.target, w.tokens, out_tokens=out[0], out_num_accepted=out[1],
+                                 out_best=out[2], workspace=ws)
+        stats_rows = rows
+        workload = f"spec_verify_greedy_candidates B={B} C={C} L={L} R={R} V={V} bf16"
+    else:
+        B, k1, V = w.target.shape
+        k = k1 - 1
+        rows = B * k1
+        out_t = torch.empty((B, k1), dtype=torch.int32, device=dev)
+        out_n = torch.empty(B, dtype=torch.int32, device=dev)
+        if args.mode == "sample":
+            ws = torch.empty(sv.workspace_bytes(B, 2 * k + 1, V, w.target.dtype), dtype=torch.uint8,
+                             device=dev)
+
+            def step():
+                sv.sample(w.target, w.draft, w.tokens, w.uniforms, w.T, out_tokens=out_t,
+                          out_num_accepted=out_n, workspace=ws)
+            stats_rows = B * (2 * k + 1)
+            workload = f"spec_verify_sample B={B} k={k} V={V} bf16 T={w.T}"
+        else:
+            ws = torch.empty(sv.workspace_bytes(B, k + 1, V, w.target.dtype), dtype=torch.uint8,
+                             device=dev)
+
+            def step():
+                sv.greedy(w.target, w.tokens, out_tokens=out_t, out_num_accepted=out_n, workspace=ws)
+            stats_rows = rows
+            workload = f"spec_verify_greedy B={B} k={k} V={V} bf16"
+
+    # algorithmic bytes of the statistics kernel: every logit row read once
+    # (V * element size) plus its 8-byte partial written
+    bytes_per_row = V * es + 8
+    stats_bytes = stats_rows * bytes_per_row
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    sv.profile_begin(args.steps)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - w0
+    kernel_ms = sv.profile_end()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    value = rows * args.steps / (total_ms / 1e3)
+
+    k_avg_ms = statistics.fmean(kernel_ms)
+    achieved = stats_bytes / (k_avg_ms / 1e3) / 1e9
+    traffic = measured_traffic(stats_bytes)
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": workload,
+            "input_dtype": "bf16",
+            "rows_per_call": rows,
+            "logit_bytes_per_call": stats_rows * V * es,
+            "call_effective_GBps": stats_rows * V * es / (ms_per_step / 1e3) / 1e9,
+            "wall_s_timed_region": wall_s,
+            "input_generation_s": gen_s,
+            "device": torch.cuda.get_device_name(0),
+        },
+        "roofline": {
+            "kernel": "k_softmax_stats" if args.mode == "sample" else "k_argmax_stats",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS,
+            "traffic": traffic,
+            "kernel_ms_avg": k_avg_ms,
+            "kernel_ms_min": min(kernel_ms),
+            "kernel_ms_max": max(kernel_ms),
+            "algorithmic_bytes_per_launch": stats_bytes,
+        },
+    }
+
+    if args.cpu_seconds > 0 and args.mode == "sample":
+        line["cpu_baseline"] = cpu_baseline(w, out_t, out_n, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, out_t, out_n, budget_s):
+    """The CPU oracle, as written (one thread, double precision), timed on the
+    first sequences of the same workload until `budget_s` of oracle time is
+    spent.  Host copies are outside the timed part.  The oracle's results on
+    those sequences are compared with the GPU's last call."""
+    import numpy as np
+
+    import oracle
+    from oracle import parity
+    if not os.path.exists(oracle.LIB_PATH):
+        oracle.build()
+    B, k1, V = w.target.shape
+    chunk = 16
+    done, spent = 0, 0.0
+    gt = out_t.cpu().numpy()
+    gn = out_n.cpu().numpy()
+    rep = parity.SampleReport()
+    for b0 in range(0, B, chunk):
+        b1 = min(B, b0 + chunk)
+        z = w.target[b0:b1].float().cpu().numpy()
+        y = w.draft[b0:b1].float().cpu().numpy()
+        x = w.tokens[b0:b1].cpu().numpy()
+        u = w.uniforms[b0:b1].cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.sample(z, y, x, u, w.T)
+        spent += time.perf_counter() - t0
+        done = b1
+        parity.check_sample(z, y, x, u, w.T, gt[b0:b1], gn[b0:b1], report=rep,
+                            seq_ids=np.arange(b0, b1))
+        if spent >= budget_s:
+            break
+    return {
+        "value": done * k1 / spent,
+        "unit": "rows/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"first {done} of {B} sequences of the same workload ({done * k1} rows); "
+                   f"single-threaded C oracle in double precision, {spent:.1f} s; it stops at "
+                   f"each sequence's first rejection, so it reads fewer rows than it counts"),
+        "parity_vs_gpu": rep.summary(),
+    }
+
+
+if __name__ == "__main__":
+    main()

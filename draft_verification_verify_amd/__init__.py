@@ -1,0 +1,214 @@
+"""Python binding of libspecverify.so, the MI355X speculative-decoding
+verification library.
+
+Argument marshalling only: every step of the verification runs in the HIP
+kernels behind the C ABI declared in ``include/spec_verify.h``.  PyTorch
+provides device memory (tensors) and streams.  There is no fallback: if the
+library is not built, importing this package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch  # loads torch's HIP runtime first, so the library binds to the same one
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+
+SV_OK, SV_EINVAL, SV_EDTYPE, SV_EWORKSPACE, SV_EHIP = 0, 1, 2, 3, 4
+SV_F32, SV_F16, SV_BF16 = 0, 1, 2
+MAX_K = 63
+
+_DTYPE = {torch.float32: SV_F32, torch.float16: SV_F16, torch.bfloat16: SV_BF16}
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, status: int, fn: str):
+        self.status = status
+        super().__init__(f"{fn}: {lib().spec_verify_status_string(status).decode()}")
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libspecverify.so is not built ({LIB_PATH}); run __graft_entry__.build()")
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, LL, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_float, ctypes.c_size_t
+        L.spec_verify_version.restype = I
+        L.spec_verify_status_string.argtypes = [I]
+        L.spec_verify_status_string.restype = ctypes.c_char_p
+        L.spec_verify_workspace_bytes.argtypes = [I, I, I, I]
+        L.spec_verify_workspace_bytes.restype = SZ
+        L.spec_verify_greedy.argtypes = [P, LL, P, I, I, I, I, P, P, P, SZ, P]
+        L.spec_verify_greedy.restype = I
+        L.spec_verify_sample.argtypes = [P, LL, P, LL, P, P, F, I, I, I, I, P, P, P, P, P, SZ, P]
+        L.spec_verify_sample.restype = I
+        L.spec_verify_greedy_candidates.argtypes = [P, LL, P, I, I, I, I, I, I, P, P, P, P, SZ, P]
+        L.spec_verify_greedy_candidates.restype = I
+        L.spec_verify_profile_begin.argtypes = [I]
+        L.spec_verify_profile_begin.restype = I
+        L.spec_verify_profile_end.argtypes = [P, I]
+        L.spec_verify_profile_end.restype = I
+        _lib = L
+    return _lib
+
+
+EXPORTED = (
+    "spec_verify_version", "spec_verify_status_string", "spec_verify_workspace_bytes",
+    "spec_verify_greedy", "spec_verify_sample", "spec_verify_greedy_candidates",
+    "spec_verify_profile_begin", "spec_verify_profile_end",
+)
+
+
+def hip_runtimes_loaded() -> list:
+    """Paths of every libamdhip64 mapped into this process (must be exactly one)."""
+    seen = set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64" in line:
+                seen.add(line.split()[-1])
+    return sorted(seen)
+
+
+def check_single_hip_runtime():
+    rts = hip_runtimes_loaded()
+    if len(rts) > 1:
+        raise RuntimeError(f"more than one HIP runtime is loaded: {rts}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def workspace_bytes(B: int, rows_per_seq: int, V: int, dtype: torch.dtype) -> int:
+    return int(lib().spec_verify_workspace_bytes(B, rows_per_seq, V, _DTYPE[dtype]))
+
+
+def _workspace(ws, B, rows_per_seq, V, dtype, device):
+    need = workspace_bytes(B, rows_per_seq, V, dtype)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    return ws
+
+
+def _row_stride(t: torch.Tensor) -> int:
+    if t.stride(-1) != 1:
+        raise ValueError("logit rows must be contiguous along the vocabulary")
+    return t.stride(-2)
+
+
+def _check_rows(t: torch.Tensor, ndim_lead: int):
+    """Rows of the leading dims must be evenly spaced by the row stride."""
+    rs = _row_stride(t)
+    expect = rs
+    for d in range(t.dim() - 2, -1, -1):
+        if t.size(d) > 1 and t.stride(d) != expect:
+            raise ValueError("logits must be a [.., V] tensor whose rows are evenly spaced")
+        expect *= t.size(d)
+    return rs
+
+
+def greedy(target: torch.Tensor, draft_tokens: torch.Tensor, *, out_tokens=None,
+           out_num_accepted=None, workspace=None, stream=None):
+    """Greedy verification.  target [B, k+1, V] (fp32/fp16/bf16, rows contiguous
+    along V), draft_tokens [B, k] int32.  Returns (tokens [B, k+1], num_accepted [B])."""
+    B, k1, V = target.shape
+    k = k1 - 1
+    dev = target.device
+    if out_tokens is None:
+        out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
+    if out_num_accepted is None:
+        out_num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    ws = _workspace(workspace, B, k + 1, V, target.dtype, dev)
+    st = lib().spec_verify_greedy(_ptr(target), _check_rows(target, 2), _ptr(draft_tokens), B, k, V,
+                                  _DTYPE[target.dtype], _ptr(out_tokens), _ptr(out_num_accepted),
+                                  _ptr(ws), ws.numel(), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_greedy")
+    return out_tokens, out_num_accepted
+
+
+def sample(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
+           uniforms: torch.Tensor, temperature: float, *, return_probs: bool = False,
+           out_tokens=None, out_num_accepted=None, out_p_x=None, out_q_x=None,
+           workspace=None, stream=None):
+    """Sampling verification.  target [B, k+1, V], draft [B, k, V] (same dtype),
+    draft_tokens [B, k] int32, uniforms [B, k+1] float32 in [0, 1).
+    Returns (tokens [B, k+1], num_accepted [B]) and, with return_probs,
+    also (p_x [B, k], q_x [B, k])."""
+    B, k1, V = target.shape
+    k = k1 - 1
+    dev = target.device
+    if out_tokens is None:
+        out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
+    if out_num_accepted is None:
+        out_num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    if return_probs:
+        if out_p_x is None:
+            out_p_x = torch.empty((B, k), dtype=torch.float32, device=dev)
+        if out_q_x is None:
+            out_q_x = torch.empty((B, k), dtype=torch.float32, device=dev)
+    ws = _workspace(workspace, B, 2 * k + 1, V, target.dtype, dev)
+    st = lib().spec_verify_sample(_ptr(target), _check_rows(target, 2), _ptr(draft), _check_rows(draft, 2),
+                                  _ptr(draft_tokens), _ptr(uniforms), float(temperature), B, k, V,
+                                  _DTYPE[target.dtype], _ptr(out_tokens), _ptr(out_num_accepted),
+                                  _ptr(out_p_x), _ptr(out_q_x), _ptr(ws), ws.numel(), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_sample")
+    if return_probs:
+        return out_tokens, out_num_accepted, out_p_x, out_q_x
+    return out_tokens, out_num_accepted
+
+
+def greedy_candidates(target: torch.Tensor, cand_tokens: torch.Tensor, *, out_tokens=None,
+                      out_num_accepted=None, out_best=None, workspace=None, stream=None):
+    """Multi-candidate greedy verification.  target [B, C, R, V] with R = L or L+1,
+    cand_tokens [B, C, L] int32.  Returns (tokens [B, L+1], A [B], best [B])."""
+    B, C, R, V = target.shape
+    L = cand_tokens.shape[2]
+    dev = target.device
+    if out_tokens is None:
+        out_tokens = torch.empty((B, L + 1), dtype=torch.int32, device=dev)
+    if out_num_accepted is None:
+        out_num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    if out_best is None:
+        out_best = torch.empty((B,), dtype=torch.int32, device=dev)
+    ws = _workspace(workspace, B, C * R, V, target.dtype, dev)
+    st = lib().spec_verify_greedy_candidates(_ptr(target), _check_rows(target, 3), _ptr(cand_tokens),
+                                             B, C, L, R, V, _DTYPE[target.dtype], _ptr(out_tokens),
+                                             _ptr(out_num_accepted), _ptr(out_best), _ptr(ws),
+                                             ws.numel(), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_greedy_candidates")
+    return out_tokens, out_num_accepted, out_best
+
+
+def profile_begin(max_calls: int):
+    st = lib().spec_verify_profile_begin(int(max_calls))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_profile_begin")
+
+
+def profile_end(max_out: int = 1 << 16):
+    buf = (ctypes.c_float * max_out)()
+    n = lib().spec_verify_profile_end(buf, max_out)
+    if n < 0:
+        raise RuntimeError(f"spec_verify_profile_end failed: {n}")
+    return [buf[i] for i in range(min(n, max_out))]
+
+
+lib()
+check_single_hip_runtime()

@@ -1,0 +1,369 @@
+// sv_api.hip -- the C ABI of libspecverify.so: argument validation, workspace
+// layout and kernel launches on the caller's stream.  Declared and documented
+// in include/spec_verify.h.
+
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "spec_verify.h"
+#include "sv_launch.h"
+
+using namespace sv;
+
+namespace {
+
+constexpr int kMaxV = 1 << 28;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool dtype_ok(int dt) { return dt == SV_F32 || dt == SV_F16 || dt == SV_BF16; }
+
+// How a set of rows is split along the vocabulary: enough workgroups to fill
+// the 256 CUs several times over, each streaming at least 256 logical vectors
+// (4 KiB of bf16, one vector per thread) so the partial write stays small
+// against the bytes read.
+struct StatsPlan {
+    int nvec;
+    int splits;
+    int vec_per_split;
+};
+
+StatsPlan plan_stats(long long rows, int V)
+{
+    StatsPlan p;
+    p.nvec = (V + kVec - 1) / kVec;
+    const long long target_units = 16384;
+    long long s = (target_units + rows - 1) / rows;
+    long long smax = p.nvec / 1024;
+    if (smax < 1) smax = 1;
+    if (s > smax) s = smax;
+    if (s < 1) s = 1;
+    if (s > 64) s = 64;
+    p.splits = (int)s;
+    p.vec_per_split = (p.nvec + p.splits - 1) / p.splits;
+    // drop splits that would be empty
+    p.splits = (p.nvec + p.vec_per_split - 1) / p.vec_per_split;
+    return p;
+}
+
+// Chunks per sampled row: about 4096 workgroups in total, at least one round
+// (kBlock vectors) per chunk where the row allows it.
+struct SamplePlan {
+    int nchunks;
+    int vec_per_chunk;
+};
+
+SamplePlan plan_sample(int B, int nvec)
+{
+    SamplePlan p;
+    int n = (4096 + B - 1) / B;
+    int nmax = (nvec + kBlock - 1) / kBlock;
+    if (n > nmax) n = nmax;
+    if (n > kMaxChunks) n = kMaxChunks;
+    if (n < 1) n = 1;
+    p.vec_per_chunk = (nvec + n - 1) / n;
+    p.nchunks = (nvec + p.vec_per_chunk - 1) / p.vec_per_chunk;
+    return p;
+}
+
+struct Workspace {
+    void* partials;
+    SampleDesc* desc;
+    float* chunk_sums;
+    unsigned* counters;
+    size_t bytes;
+};
+
+// Layout: [split partials][sample descriptors][chunk totals][counters],
+// each region 256-byte aligned.
+Workspace layout(char* base, int B, long long rows, int V)
+{
+    Workspace w;
+    const StatsPlan sp = plan_stats(rows, V);
+    const SamplePlan pp = plan_sample(B, sp.nvec);
+    size_t off = 0;
+    w.partials = base ? base + off : nullptr;
+    off += align_up((size_t)rows * sp.splits * 8);
+    w.desc = base ? reinterpret_cast<SampleDesc*>(base + off) : nullptr;
+    off += align_up((size_t)B * sizeof(SampleDesc));
+    w.chunk_sums = base ? reinterpret_cast<float*>(base + off) : nullptr;
+    off += align_up((size_t)B * pp.nchunks * sizeof(float));
+    w.counters = base ? reinterpret_cast<unsigned*>(base + off) : nullptr;
+    off += align_up((size_t)B * sizeof(unsigned));
+    w.bytes = off;
+    return w;
+}
+
+bool fits_grid(long long rows, int V)
+{
+    const StatsPlan sp = plan_stats(rows, V);
+    return rows * sp.splits < (1LL << 31);
+}
+
+bool vec_ok(const void* p, long long stride, int dt)
+{
+    const long long es = elem_size(dt);
+    return ((uintptr_t)p % 16 == 0) && ((stride * es) % 16 == 0);
+}
+
+// ---- measurement aid: per-call events around the statistics kernel ---------
+struct Profile {
+    hipEvent_t* ev = nullptr;
+    int max_calls = 0;
+    int count = 0;
+    bool on = false;
+};
+Profile g_prof;
+
+void prof_mark(hipStream_t st, bool begin)
+{
+    if (!g_prof.on || g_prof.count >= g_prof.max_calls) return;
+    hipEventRecord(g_prof.ev[2 * g_prof.count + (begin ? 0 : 1)], st);
+    if (!begin) g_prof.count++;
+}
+
+}  // namespace
+
+extern "C" {
+
+int spec_verify_version(void) { return 100; }
+
+const char* spec_verify_status_string(int s)
+{
+    switch (s) {
+    case SV_OK: return "SV_OK";
+    case SV_EINVAL: return "SV_EINVAL: invalid argument";
+    case SV_EDTYPE: return "SV_EDTYPE: unknown dtype";
+    case SV_EWORKSPACE: return "SV_EWORKSPACE: workspace missing or too small";
+    case SV_EHIP: return "SV_EHIP: HIP launch error";
+    default: return "unknown status";
+    }
+}
+
+size_t spec_verify_workspace_bytes(int B, int rows_per_seq, int V, int dtype)
+{
+    if (B < 1 || rows_per_seq < 1 || V < 1 || V > kMaxV || !dtype_ok(dtype)) return 0;
+    const long long rows = (long long)B * rows_per_seq;
+    if (!fits_grid(rows, V)) return 0;
+    return layout(nullptr, B, rows, V).bytes;
+}
+
+int spec_verify_greedy(const void* target_logits, long long target_row_stride,
+                       const int* draft_tokens, int B, int k, int V, int dtype,
+                       int* out_tokens, int* out_num_accepted,
+                       void* workspace, size_t workspace_bytes, void* hip_stream)
+{
+    if (!dtype_ok(dtype)) return SV_EDTYPE;
+    if (!target_logits || !draft_tokens || !out_tokens || !out_num_accepted) return SV_EINVAL;
+    if (B < 1 || k < 1 || k > SV_MAX_K || V < 1 || V > kMaxV || target_row_stride < V) return SV_EINVAL;
+    const long long rows = (long long)B * (k + 1);
+    if (!fits_grid(rows, V)) return SV_EINVAL;
+    Workspace w = layout(static_cast<char*>(workspace), B, rows, V);
+    if (!workspace || workspace_bytes < w.bytes) return SV_EWORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+
+    const StatsPlan sp = plan_stats(rows, V);
+    StatsArgs sa;
+    sa.target = target_logits;
+    sa.t_stride = target_row_stride;
+    sa.draft = nullptr;
+    sa.d_stride = 0;
+    sa.n_target_rows = (int)rows;
+    sa.n_rows = (int)rows;
+    sa.V = V;
+    sa.nvec = sp.nvec;
+    sa.splits = sp.splits;
+    sa.vec_per_split = sp.vec_per_split;
+    sa.c = 0.f;
+    sa.partials = w.partials;
+    prof_mark(st, true);
+    if (launch_argmax_stats(dtype, vec_ok(target_logits, target_row_stride, dtype), sa, st) != hipSuccess)
+        return SV_EHIP;
+    prof_mark(st, false);
+
+    DecideGreedyArgs da;
+    da.tokens = draft_tokens;
+    da.B = B;
+    da.k = k;
+    da.splits = sp.splits;
+    da.partials = static_cast<const ArgPartial*>(w.partials);
+    da.out_tokens = out_tokens;
+    da.out_num_accepted = out_num_accepted;
+    if (launch_decide_greedy(da, st) != hipSuccess) return SV_EHIP;
+    return SV_OK;
+}
+
+int spec_verify_sample(const void* target_logits, long long target_row_stride,
+                       const void* draft_logits, long long draft_row_stride,
+                       const int* draft_tokens, const float* uniforms, float temperature,
+                       int B, int k, int V, int dtype,
+                       int* out_tokens, int* out_num_accepted,
+                       float* out_p_x, float* out_q_x,
+                       void* workspace, size_t workspace_bytes, void* hip_stream)
+{
+    if (!dtype_ok(dtype)) return SV_EDTYPE;
+    if (!target_logits || !draft_logits || !draft_tokens || !uniforms || !out_tokens ||
+        !out_num_accepted)
+        return SV_EINVAL;
+    if (B < 1 || k < 1 || k > SV_MAX_K || V < 1 || V > kMaxV) return SV_EINVAL;
+    if (target_row_stride < V || draft_row_stride < V) return SV_EINVAL;
+    if (!(temperature > 0.f) || !isfinite(temperature)) return SV_EINVAL;
+    const double cd = 1.4426950408889634 / (double)temperature;
+    if (!isfinite(cd) || cd > 3.0e38) return SV_EINVAL;
+    const long long rows = (long long)B * (2 * k + 1);
+    if (!fits_grid(rows, V)) return SV_EINVAL;
+    Workspace w = layout(static_cast<char*>(workspace), B, rows, V);
+    if (!workspace || workspace_bytes < w.bytes) return SV_EWORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    const float c = (float)cd;
+    const bool vec = vec_ok(target_logits, target_row_stride, dtype) &&
+                     vec_ok(draft_logits, draft_row_stride, dtype);
+
+    const StatsPlan sp = plan_stats(rows, V);
+    StatsArgs sa;
+    sa.target = target_logits;
+    sa.t_stride = target_row_stride;
+    sa.draft = draft_logits;
+    sa.d_stride = draft_row_stride;
+    sa.n_target_rows = B * (k + 1);
+    sa.n_rows = (int)rows;
+    sa.V = V;
+    sa.nvec = sp.nvec;
+    sa.splits = sp.splits;
+    sa.vec_per_split = sp.vec_per_split;
+    sa.c = c;
+    sa.partials = w.partials;
+    prof_mark(st, true);
+    if (launch_softmax_stats(dtype, vec, sa, st) != hipSuccess) return SV_EHIP;
+    prof_mark(st, false);
+
+    DecideSampleArgs da;
+    da.target = target_logits;
+    da.t_stride = target_row_stride;
+    da.draft = draft_logits;
+    da.d_stride = draft_row_stride;
+    da.tokens = draft_tokens;
+    da.uniforms = uniforms;
+    da.B = B;
+    da.k = k;
+    da.V = V;
+    da.splits = sp.splits;
+    da.c = c;
+    da.partials = static_cast<const SoftPartial*>(w.partials);
+    da.out_tokens = out_tokens;
+    da.out_num_accepted = out_num_accepted;
+    da.out_p_x = out_p_x;
+    da.out_q_x = out_q_x;
+    da.desc = w.desc;
+    da.counters = w.counters;
+    if (launch_decide_sample(dtype, da, st) != hipSuccess) return SV_EHIP;
+
+    const SamplePlan pp = plan_sample(B, sp.nvec);
+    SampleArgs ma;
+    ma.target = target_logits;
+    ma.t_stride = target_row_stride;
+    ma.draft = draft_logits;
+    ma.d_stride = draft_row_stride;
+    ma.V = V;
+    ma.nvec = sp.nvec;
+    ma.nchunks = pp.nchunks;
+    ma.vec_per_chunk = pp.vec_per_chunk;
+    ma.c = c;
+    ma.desc = w.desc;
+    ma.chunk_sums = w.chunk_sums;
+    ma.counters = w.counters;
+    ma.out_tokens = out_tokens;
+    ma.out_row = k + 1;
+    if (launch_sample(dtype, vec, B, ma, st) != hipSuccess) return SV_EHIP;
+    return SV_OK;
+}
+
+int spec_verify_greedy_candidates(const void* target_logits, long long row_stride,
+                                  const int* cand_tokens, int B, int C, int L, int R, int V,
+                                  int dtype, int* out_tokens, int* out_num_accepted,
+                                  int* out_best_candidate,
+                                  void* workspace, size_t workspace_bytes, void* hip_stream)
+{
+    if (!dtype_ok(dtype)) return SV_EDTYPE;
+    if (!target_logits || !cand_tokens || !out_tokens || !out_num_accepted || !out_best_candidate)
+        return SV_EINVAL;
+    if (B < 1 || C < 1 || L < 1 || L > SV_MAX_K || C * L > SV_MAX_CANDIDATE_TOKENS) return SV_EINVAL;
+    if ((R != L && R != L + 1) || V < 1 || V > kMaxV || row_stride < V) return SV_EINVAL;
+    const long long rows = (long long)B * C * R;
+    if (!fits_grid(rows, V)) return SV_EINVAL;
+    Workspace w = layout(static_cast<char*>(workspace), B, rows, V);
+    if (!workspace || workspace_bytes < w.bytes) return SV_EWORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+
+    const StatsPlan sp = plan_stats(rows, V);
+    StatsArgs sa;
+    sa.target = target_logits;
+    sa.t_stride = row_stride;
+    sa.draft = nullptr;
+    sa.d_stride = 0;
+    sa.n_target_rows = (int)rows;
+    sa.n_rows = (int)rows;
+    sa.V = V;
+    sa.nvec = sp.nvec;
+    sa.splits = sp.splits;
+    sa.vec_per_split = sp.vec_per_split;
+    sa.c = 0.f;
+    sa.partials = w.partials;
+    prof_mark(st, true);
+    if (launch_argmax_stats(dtype, vec_ok(target_logits, row_stride, dtype), sa, st) != hipSuccess)
+        return SV_EHIP;
+    prof_mark(st, false);
+
+    DecideCandArgs da;
+    da.cand = cand_tokens;
+    da.B = B;
+    da.C = C;
+    da.L = L;
+    da.R = R;
+    da.splits = sp.splits;
+    da.partials = static_cast<const ArgPartial*>(w.partials);
+    da.out_tokens = out_tokens;
+    da.out_num_accepted = out_num_accepted;
+    da.out_best = out_best_candidate;
+    if (launch_decide_candidates(da, st) != hipSuccess) return SV_EHIP;
+    return SV_OK;
+}
+
+int spec_verify_profile_begin(int max_calls)
+{
+    if (max_calls < 1 || g_prof.on) return SV_EINVAL;
+    g_prof.ev = static_cast<hipEvent_t*>(calloc((size_t)2 * max_calls, sizeof(hipEvent_t)));
+    if (!g_prof.ev) return SV_EINVAL;
+    for (int i = 0; i < 2 * max_calls; ++i) {
+        if (hipEventCreate(&g_prof.ev[i]) != hipSuccess) {
+            for (int j = 0; j < i; ++j) hipEventDestroy(g_prof.ev[j]);
+            free(g_prof.ev);
+            g_prof.ev = nullptr;
+            return SV_EHIP;
+        }
+    }
+    g_prof.max_calls = max_calls;
+    g_prof.count = 0;
+    g_prof.on = true;
+    return SV_OK;
+}
+
+int spec_verify_profile_end(float* out_ms, int max_out)
+{
+    if (!g_prof.on) return -1;
+    int rc = g_prof.count;
+    for (int i = 0; i < g_prof.count; ++i) {
+        if (hipEventSynchronize(g_prof.ev[2 * i + 1]) != hipSuccess) { rc = -2; break; }
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]) != hipSuccess) { rc = -2; break; }
+        if (out_ms && i < max_out) out_ms[i] = ms;
+    }
+    for (int i = 0; i < 2 * g_prof.max_calls; ++i) hipEventDestroy(g_prof.ev[i]);
+    free(g_prof.ev);
+    g_prof = Profile();
+    return rc;
+}
+
+}  // extern "C"

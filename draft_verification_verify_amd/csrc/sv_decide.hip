@@ -1,0 +1,223 @@
+// sv_decide.hip -- per-sequence decisions, one wave64 per sequence.
+//
+// Lane i handles draft position i (k <= 63, so the k+1 positions fit one
+// wave).  The lanes merge their rows' split partials in a fixed order, take
+// their own accept/reject decision independently, and a 64-bit ballot plus a
+// find-first-set gives the first rejection: the left-to-right scan of the
+// rule (production blog, "The acceptance rule") without a serial loop.
+
+#include "sv_device.h"
+
+namespace sv {
+
+constexpr int kSeqPerBlock = kBlock / 64;
+
+__device__ __forceinline__ void merge_soft(const SoftPartial* p, int splits, float c, float& m, float& s)
+{
+    m = p[0].m;
+    s = p[0].s;
+    for (int i = 1; i < splits; ++i) {
+        const float m2 = p[i].m, s2 = p[i].s;
+        const float mn = fmaxf(m, m2);
+        if (mn == -INFINITY) {
+            s = 0.f;
+        } else {
+            s = s * exp2f((m - mn) * c) + s2 * exp2f((m2 - mn) * c);
+        }
+        m = mn;
+    }
+}
+
+// Larger value wins; equal values keep the smaller index.  An all -inf row
+// has index INT32_MAX in every split and maps to 0.
+__device__ __forceinline__ int merge_arg(const ArgPartial* p, int splits)
+{
+    float v = p[0].v;
+    int idx = p[0].i;
+    for (int i = 1; i < splits; ++i) {
+        const float v2 = p[i].v;
+        const int i2 = p[i].i;
+        if (v2 > v || (v2 == v && i2 < idx)) {
+            v = v2;
+            idx = i2;
+        }
+    }
+    return idx == INT32_MAX ? 0 : idx;
+}
+
+__device__ __forceinline__ unsigned long long ballot64(bool pred)
+{
+    return __ballot(pred);
+}
+
+// ---- sampling --------------------------------------------------------------
+// log2 p_i(x) = (z_x - m) * c - log2 s with c = log2(e)/T.  The ratio test is
+// taken in the log domain so that no probability underflows: accept iff
+// log q <= log p (ratio >= 1, and q = 0) or u < exp2(log p - log q).
+template <int DT>
+__global__ __launch_bounds__(kBlock) void k_decide_sample(DecideSampleArgs a)
+{
+    constexpr int ES = DT == DT_F32 ? 4 : 2;
+    const int b = blockIdx.x * kSeqPerBlock + (threadIdx.x >> 6);
+    if (b >= a.B) return;
+    const int lane = threadIdx.x & 63;
+    const int k = a.k;
+    const float c = a.c;
+    const int nT = a.B * (k + 1);
+
+    float mt = -INFINITY, st = 0.f, md = -INFINITY, sd = 0.f;
+    bool reject = false;
+    int x = -1;
+    float px = 0.f, qx = 0.f;
+    if (lane <= k) {
+        const int tr = b * (k + 1) + lane;
+        merge_soft(a.partials + (long long)tr * a.splits, a.splits, c, mt, st);
+    }
+    if (lane < k) {
+        const int dr = b * k + lane;
+        merge_soft(a.partials + (long long)(nT + dr) * a.splits, a.splits, c, md, sd);
+        x = a.tokens[(long long)b * k + lane];
+        const bool valid = x >= 0 && x < a.V;
+        if (valid) {
+            const float zx = load_elem<DT>(row_ptr(a.target, b * (k + 1) + lane, a.t_stride, ES), x);
+            const float yx = load_elem<DT>(row_ptr(a.draft, dr, a.d_stride, ES), x);
+            const float lp = (zx - mt) * c - log2f(st);
+            const float lq = (yx - md) * c - log2f(sd);
+            const float u = a.uniforms[(long long)b * (k + 1) + lane];
+            const bool accept = (lq <= lp) || (u < exp2f(lp - lq));
+            reject = !accept;
+            px = exp2f(lp);
+            qx = exp2f(lq);
+        } else {
+            reject = true;
+        }
+    }
+    const unsigned long long rej = ballot64(reject);
+    const int j = rej ? (__ffsll((long long)rej) - 1) : k;
+
+    int* out = a.out_tokens + (long long)b * (k + 1);
+    if (lane < j) out[lane] = x;
+    else if (lane > j && lane <= k) out[lane] = -1;
+    if (lane < k) {
+        if (a.out_p_x) a.out_p_x[(long long)b * k + lane] = px;
+        if (a.out_q_x) a.out_q_x[(long long)b * k + lane] = qx;
+    }
+    if (lane == j) {
+        SampleDesc d;
+        d.t_row = b * (k + 1) + j;
+        d.d_row = j < k ? b * k + j : -1;
+        d.out_pos = j;
+        d.kind = j < k ? 0 : 1;
+        d.off_t = mt * c + log2f(st);
+        d.off_d = j < k ? md * c + log2f(sd) : 0.f;
+        d.u = a.uniforms[(long long)b * (k + 1) + k];
+        d.pad = 0;
+        a.desc[b] = d;
+        a.counters[b] = 0u;
+        a.out_num_accepted[b] = j;
+    }
+}
+
+// ---- greedy ----------------------------------------------------------------
+__global__ __launch_bounds__(kBlock) void k_decide_greedy(DecideGreedyArgs a)
+{
+    const int b = blockIdx.x * kSeqPerBlock + (threadIdx.x >> 6);
+    if (b >= a.B) return;
+    const int lane = threadIdx.x & 63;
+    const int k = a.k;
+    int amax = 0, x = -1;
+    bool miss = false;
+    if (lane <= k) amax = merge_arg(a.partials + (long long)(b * (k + 1) + lane) * a.splits, a.splits);
+    if (lane < k) {
+        x = a.tokens[(long long)b * k + lane];
+        miss = x != amax;
+    }
+    const unsigned long long mm = ballot64(miss);
+    const int j = mm ? (__ffsll((long long)mm) - 1) : k;
+    if (lane <= k) {
+        int* out = a.out_tokens + (long long)b * (k + 1);
+        out[lane] = lane < j ? x : (lane == j ? amax : -1);
+    }
+    if (lane == 0) a.out_num_accepted[b] = j;
+}
+
+// ---- multi-candidate greedy ------------------------------------------------
+// Lane c*L + i holds candidate c's position i (C*L <= 64).  Candidate c's
+// accepted length is the index of its first mismatch bit; the longest wins,
+// ties to the lowest c (Ouroboros 3.4.3, "Selecting the accepted tokens").
+__global__ __launch_bounds__(kBlock) void k_decide_candidates(DecideCandArgs a)
+{
+    const int b = blockIdx.x * kSeqPerBlock + (threadIdx.x >> 6);
+    if (b >= a.B) return;
+    const int lane = threadIdx.x & 63;
+    const int C = a.C, L = a.L, R = a.R;
+    const bool active = lane < C * L;
+    const int c = active ? lane / L : 0;
+    const int i = active ? lane - c * L : 0;
+    int amax = 0, tok = -1;
+    bool miss = false;
+    if (active) {
+        const long long row = ((long long)b * C + c) * R + i;
+        amax = merge_arg(a.partials + row * a.splits, a.splits);
+        tok = a.cand[((long long)b * C + c) * L + i];
+        miss = tok != amax;
+    }
+    const unsigned long long mm = ballot64(miss);
+    int acc = 0;
+    if (active) {
+        const unsigned long long lo_mask = (L == 64) ? ~0ull : ((1ull << L) - 1ull);
+        const unsigned long long bits = (mm >> (c * L)) & lo_mask;
+        acc = bits ? (__ffsll((long long)bits) - 1) : L;
+    }
+    int A = wave_max_int(active ? acc : -1);
+    const int cs = wave_min_int(active && acc == A ? c : 1 << 30);
+    // committed tokens: cand(c*, 0..A-1), then the correction or the bonus row
+    const int src = cs * L + (lane < L ? lane : 0);
+    const int ctok = __shfl(tok, src, 64);
+    const int camx = __shfl(amax, src, 64);
+    int bonus = -1;
+    if (A == L && R == L + 1 && lane == L) {
+        const long long row = ((long long)b * C + cs) * R + L;
+        bonus = merge_arg(a.partials + row * a.splits, a.splits);
+    }
+    if (lane <= L) {
+        int v;
+        if (lane < A) v = ctok;
+        else if (lane == A && A < L) v = camx;
+        else if (lane == L && A == L && R == L + 1) v = bonus;
+        else v = -1;
+        a.out_tokens[(long long)b * (L + 1) + lane] = v;
+    }
+    if (lane == 0) {
+        a.out_num_accepted[b] = A;
+        a.out_best[b] = cs;
+    }
+}
+
+hipError_t launch_decide_sample(int dt, const DecideSampleArgs& a, hipStream_t st)
+{
+    void* args[] = {const_cast<DecideSampleArgs*>(&a)};
+    const unsigned grid = (unsigned)((a.B + kSeqPerBlock - 1) / kSeqPerBlock);
+    const void* f = dt == DT_F32 ? reinterpret_cast<const void*>(k_decide_sample<DT_F32>)
+                  : dt == DT_F16 ? reinterpret_cast<const void*>(k_decide_sample<DT_F16>)
+                                 : reinterpret_cast<const void*>(k_decide_sample<DT_BF16>);
+    return hipLaunchKernel(f, dim3(grid), dim3(kBlock), args, 0, st);
+}
+
+hipError_t launch_decide_greedy(const DecideGreedyArgs& a, hipStream_t st)
+{
+    void* args[] = {const_cast<DecideGreedyArgs*>(&a)};
+    const unsigned grid = (unsigned)((a.B + kSeqPerBlock - 1) / kSeqPerBlock);
+    return hipLaunchKernel(reinterpret_cast<const void*>(k_decide_greedy), dim3(grid), dim3(kBlock),
+                           args, 0, st);
+}
+
+hipError_t launch_decide_candidates(const DecideCandArgs& a, hipStream_t st)
+{
+    void* args[] = {const_cast<DecideCandArgs*>(&a)};
+    const unsigned grid = (unsigned)((a.B + kSeqPerBlock - 1) / kSeqPerBlock);
+    return hipLaunchKernel(reinterpret_cast<const void*>(k_decide_candidates), dim3(grid), dim3(kBlock),
+                           args, 0, st);
+}
+
+}  // namespace sv

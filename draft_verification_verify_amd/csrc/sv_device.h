@@ -1,0 +1,209 @@
+// sv_device.h -- device-side building blocks of libspecverify.so: loading
+// logical 8-element vectors of a logit row, and workgroup reductions/scans in
+// a fixed order (so every result is reproducible bit for bit).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sv_launch.h"
+
+namespace sv {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// ---- element decoding ------------------------------------------------------
+// bf16 -> f32 is exact: the bf16 bits are the high half of the f32.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float f16_bits(uint32_t h)
+{
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(h & 0xffffu));
+}
+
+template <int DT>
+__device__ __forceinline__ float load_elem(const char* row, long long i)
+{
+    if constexpr (DT == DT_F32) {
+        return reinterpret_cast<const float*>(row)[i];
+    } else if constexpr (DT == DT_BF16) {
+        return bf16_lo(reinterpret_cast<const unsigned short*>(row)[i]);
+    } else {
+        return f16_bits(reinterpret_cast<const unsigned short*>(row)[i]);
+    }
+}
+
+// The raw bits of one logical vector (8 elements).
+template <int DT>
+struct Raw {
+    u32x4 a;
+    u32x4 b;                           // used by fp32 only
+};
+
+// Load logical vector v (elements 8v .. 8v+7, all inside the row).  VEC: the
+// row is 16-byte aligned and the vector is one (two for fp32) 16-byte
+// non-temporal loads; otherwise element loads.
+template <int DT, bool VEC>
+__device__ __forceinline__ Raw<DT> load_raw(const char* row, int v)
+{
+    Raw<DT> r;
+    if constexpr (VEC) {
+        if constexpr (DT == DT_F32) {
+            const u32x4* p = reinterpret_cast<const u32x4*>(row) + 2 * v;
+            r.a = __builtin_nontemporal_load(p);
+            r.b = __builtin_nontemporal_load(p + 1);
+        } else {
+            const u32x4* p = reinterpret_cast<const u32x4*>(row) + v;
+            r.a = __builtin_nontemporal_load(p);
+        }
+    } else {
+        if constexpr (DT == DT_F32) {
+            const uint32_t* p = reinterpret_cast<const uint32_t*>(row) + 8 * (long long)v;
+            r.a = u32x4{p[0], p[1], p[2], p[3]};
+            r.b = u32x4{p[4], p[5], p[6], p[7]};
+        } else {
+            const unsigned short* p = reinterpret_cast<const unsigned short*>(row) + 8 * (long long)v;
+            r.a = u32x4{p[0] | ((uint32_t)p[1] << 16), p[2] | ((uint32_t)p[3] << 16),
+                        p[4] | ((uint32_t)p[5] << 16), p[6] | ((uint32_t)p[7] << 16)};
+        }
+    }
+    return r;
+}
+
+template <int DT>
+__device__ __forceinline__ void decode(const Raw<DT>& r, float* e)
+{
+    if constexpr (DT == DT_F32) {
+        e[0] = __uint_as_float(r.a.x); e[1] = __uint_as_float(r.a.y);
+        e[2] = __uint_as_float(r.a.z); e[3] = __uint_as_float(r.a.w);
+        e[4] = __uint_as_float(r.b.x); e[5] = __uint_as_float(r.b.y);
+        e[6] = __uint_as_float(r.b.z); e[7] = __uint_as_float(r.b.w);
+    } else if constexpr (DT == DT_BF16) {
+        e[0] = bf16_lo(r.a.x); e[1] = bf16_hi(r.a.x);
+        e[2] = bf16_lo(r.a.y); e[3] = bf16_hi(r.a.y);
+        e[4] = bf16_lo(r.a.z); e[5] = bf16_hi(r.a.z);
+        e[6] = bf16_lo(r.a.w); e[7] = bf16_hi(r.a.w);
+    } else {
+        e[0] = f16_bits(r.a.x); e[1] = f16_bits(r.a.x >> 16);
+        e[2] = f16_bits(r.a.y); e[3] = f16_bits(r.a.y >> 16);
+        e[4] = f16_bits(r.a.z); e[5] = f16_bits(r.a.z >> 16);
+        e[6] = f16_bits(r.a.w); e[7] = f16_bits(r.a.w >> 16);
+    }
+}
+
+// The row's last, partial vector (n < 8 valid elements); the rest is `fill`.
+template <int DT>
+__device__ __forceinline__ void load_partial(const char* row, int v, int n, float fill, float* e)
+{
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) e[j] = j < n ? load_elem<DT>(row, 8LL * v + j) : fill;
+}
+
+// Any logical vector: full ones through load_raw, the partial tail element-wise.
+template <int DT, bool VEC>
+__device__ __forceinline__ void load8(const char* row, int v, int nfull, int V, float fill, float* e)
+{
+    if (v < nfull) {
+        Raw<DT> r = load_raw<DT, VEC>(row, v);
+        decode<DT>(r, e);
+    } else {
+        load_partial<DT>(row, v, V - 8 * v, fill, e);
+    }
+}
+
+__device__ __forceinline__ const char* row_ptr(const void* base, long long row, long long stride, int es)
+{
+    return reinterpret_cast<const char*>(base) + row * stride * es;
+}
+
+// ---- fixed-order workgroup collectives -------------------------------------
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ int wave_min_int(int v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ int wave_max_int(int v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// Block-wide reductions; `lds` holds at least kWaves entries.  Every thread
+// gets the result.
+__device__ __forceinline__ float block_max(float v, float* lds)
+{
+    v = wave_max(v);
+    if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float r = lds[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) r = fmaxf(r, lds[w]);
+    __syncthreads();
+    return r;
+}
+
+__device__ __forceinline__ int block_min_int(int v, int* lds)
+{
+    v = wave_min_int(v);
+    if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = v;
+    __syncthreads();
+    int r = lds[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) r = min(r, lds[w]);
+    __syncthreads();
+    return r;
+}
+
+__device__ __forceinline__ int block_max_int(int v, int* lds)
+{
+    v = wave_max_int(v);
+    if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = v;
+    __syncthreads();
+    int r = lds[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) r = max(r, lds[w]);
+    __syncthreads();
+    return r;
+}
+
+// Inclusive scan of x over the workgroup in thread order.  Returns the
+// inclusive value; *excl gets the exclusive value, bitwise equal to the
+// inclusive value of the previous thread (0 for thread 0); *total gets the
+// block total, bitwise equal to the last thread's inclusive value.
+__device__ __forceinline__ float block_scan(float x, float* excl, float* total, float* lds)
+{
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    float incl = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        float y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+    }
+    float wex = __shfl_up(incl, 1, 64);
+    if (lane == 0) wex = 0.f;
+    if (lane == 63) lds[w] = incl;
+    __syncthreads();
+    float pre = 0.f;
+    for (int i = 0; i < w; ++i) pre += lds[i];
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < kWaves - 1; ++i) tot += lds[i];
+    tot += lds[kWaves - 1];
+    __syncthreads();
+    *excl = pre + wex;
+    *total = tot;
+    return pre + incl;
+}
+
+}  // namespace sv

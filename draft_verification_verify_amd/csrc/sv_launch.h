@@ -1,0 +1,120 @@
+// sv_launch.h -- argument blocks and launchers shared by the host layer
+// (sv_api.hip) and the kernel files.  Internal to libspecverify.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kBlock = 256;            // threads per workgroup (4 wave64s)
+constexpr int kWaves = kBlock / 64;
+constexpr int kVec = 8;                // elements per logical vector (16 B of bf16/fp16)
+
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+
+inline int elem_size(int dt) { return dt == DT_F32 ? 4 : 2; }
+
+// Per-(row, split) partial of the softmax statistics: running max m (raw
+// logit units) and s = sum exp2((z - m) * c), c = log2(e) / T.
+struct SoftPartial { float m; float s; };
+// Per-(row, split) partial of the argmax: value and lowest index (INT32_MAX
+// when the split holds nothing above -inf).
+struct ArgPartial { float v; int i; };
+
+// Vocabulary-streaming statistics over a set of rows.  Rows [0, n_target_rows)
+// are target rows r at target + r * t_stride; the rest are draft rows
+// (r - n_target_rows) at draft + (r - n_target_rows) * d_stride (strides in
+// elements).  Row r, split s covers logical vectors
+// [s * vec_per_split, min((s + 1) * vec_per_split, nvec)).
+struct StatsArgs {
+    const void* target;
+    long long t_stride;
+    const void* draft;
+    long long d_stride;
+    int n_target_rows;
+    int n_rows;
+    int V;
+    int nvec;                          // ceil(V / 8)
+    int splits;
+    int vec_per_split;
+    float c;                           // log2(e) / T (softmax statistics only)
+    void* partials;                    // [n_rows][splits] SoftPartial or ArgPartial
+};
+
+// One sampling step per sequence, prepared by the decision kernel: draw from
+// target row t_row (weights exp2(z*c - off_t)) or, for kind 0, from the
+// residual max(0, exp2(z*c - off_t) - exp2(y*c - off_d)) against draft row
+// d_row; write the token at out_pos of the sequence's output row.
+struct SampleDesc {
+    int t_row;
+    int d_row;
+    int out_pos;
+    int kind;                          // 0 residual, 1 target row (bonus)
+    float off_t;
+    float off_d;
+    float u;
+    int pad;
+};
+
+struct DecideSampleArgs {
+    const void* target;
+    long long t_stride;
+    const void* draft;
+    long long d_stride;
+    const int* tokens;                 // [B][k]
+    const float* uniforms;             // [B][k+1]
+    int B, k, V, splits;
+    float c;
+    const SoftPartial* partials;       // target rows then draft rows
+    int* out_tokens;                   // [B][k+1]
+    int* out_num_accepted;             // [B]
+    float* out_p_x;                    // [B][k] or null
+    float* out_q_x;                    // [B][k] or null
+    SampleDesc* desc;                  // [B]
+    unsigned* counters;                // [B], zeroed here for the sampler
+};
+
+struct DecideGreedyArgs {
+    const int* tokens;                 // [B][k]
+    int B, k, splits;
+    const ArgPartial* partials;        // [B*(k+1)][splits]
+    int* out_tokens;
+    int* out_num_accepted;
+};
+
+struct DecideCandArgs {
+    const int* cand;                   // [B][C][L]
+    int B, C, L, R, splits;
+    const ArgPartial* partials;        // [B*C*R][splits]
+    int* out_tokens;                   // [B][L+1]
+    int* out_num_accepted;
+    int* out_best;
+};
+
+struct SampleArgs {
+    const void* target;
+    long long t_stride;
+    const void* draft;
+    long long d_stride;
+    int V, nvec;
+    int nchunks;                       // chunks per sampled row
+    int vec_per_chunk;
+    float c;
+    const SampleDesc* desc;
+    float* chunk_sums;                 // [B][nchunks]
+    unsigned* counters;                // [B]
+    int* out_tokens;                   // [B][out_row]
+    int out_row;
+};
+
+constexpr int kMaxChunks = 64;
+
+hipError_t launch_softmax_stats(int dt, bool vec, const StatsArgs& a, hipStream_t st);
+hipError_t launch_argmax_stats(int dt, bool vec, const StatsArgs& a, hipStream_t st);
+hipError_t launch_decide_sample(int dt, const DecideSampleArgs& a, hipStream_t st);
+hipError_t launch_decide_greedy(const DecideGreedyArgs& a, hipStream_t st);
+hipError_t launch_decide_candidates(const DecideCandArgs& a, hipStream_t st);
+hipError_t launch_sample(int dt, bool vec, int B, const SampleArgs& a, hipStream_t st);
+
+}  // namespace sv

@@ -1,0 +1,243 @@
+// sv_stats.hip -- the vocabulary-streaming pass: one read of every logit row.
+//
+// Sampling needs, per row, the softmax normaliser of z / T (production blog,
+// "The acceptance rule": p and q at every position); greedy needs the argmax
+// (same section, greedy collapse).  Both are row reductions over V with no
+// contraction, bound by HBM bandwidth: each workgroup streams a contiguous
+// slice of one row with 16-byte non-temporal loads (four per thread in
+// flight), reduces it in registers and writes one 8-byte partial.  The
+// partials of a row's slices are merged in a fixed order by the decision
+// kernels.
+//
+// Built with -fno-honor-nans: NaN logits are outside the library's contract,
+// which lets max() map to bare v_max3_f32.
+
+#include "sv_device.h"
+
+namespace sv {
+
+// Online softmax statistics in base 2: s = sum exp2(z*c - m*c), m = max z.
+// Rescales s once per group of N elements (one exp2), not per element.
+template <int N>
+__device__ __forceinline__ void soft_update(const float* e, float& m, float& s, float c)
+{
+    float cm0 = e[0], cm1 = e[1];
+#pragma unroll
+    for (int j = 2; j < N; j += 2) {
+        cm0 = fmaxf(cm0, e[j]);
+        cm1 = fmaxf(cm1, e[j + 1]);
+    }
+    const float mn = fmaxf(m, fmaxf(cm0, cm1));
+    const float scale = (m == mn) ? 1.f : __builtin_amdgcn_exp2f((m - mn) * c);
+    const float off = (mn == -INFINITY) ? 0.f : -mn * c;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+    for (int j = 0; j < N; j += 4) {
+        a0 += __builtin_amdgcn_exp2f(__builtin_fmaf(e[j + 0], c, off));
+        a1 += __builtin_amdgcn_exp2f(__builtin_fmaf(e[j + 1], c, off));
+        a2 += __builtin_amdgcn_exp2f(__builtin_fmaf(e[j + 2], c, off));
+        a3 += __builtin_amdgcn_exp2f(__builtin_fmaf(e[j + 3], c, off));
+    }
+    s = s * scale + ((a0 + a1) + (a2 + a3));
+    m = mn;
+}
+
+__device__ __forceinline__ void soft_merge(float& m, float& s, float m2, float s2, float c)
+{
+    const float mn = fmaxf(m, m2);
+    if (mn == -INFINITY) {
+        m = mn;
+        s = 0.f;
+        return;
+    }
+    s = s * __builtin_amdgcn_exp2f((m - mn) * c) + s2 * __builtin_amdgcn_exp2f((m2 - mn) * c);
+    m = mn;
+}
+
+__device__ __forceinline__ const char* stats_row(const StatsArgs& a, int row, int es)
+{
+    return row < a.n_target_rows
+               ? row_ptr(a.target, row, a.t_stride, es)
+               : row_ptr(a.draft, row - a.n_target_rows, a.d_stride, es);
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kBlock) void k_softmax_stats(StatsArgs a)
+{
+    __shared__ float lds_m[kWaves], lds_s[kWaves];
+    constexpr int ES = DT == DT_F32 ? 4 : 2;
+    const int unit = blockIdx.x;
+    const int row = unit / a.splits;
+    const int split = unit - row * a.splits;
+    const char* rp = stats_row(a, row, ES);
+    const int v0 = split * a.vec_per_split;
+    const int v1 = min(v0 + a.vec_per_split, a.nvec);
+    const int nfull = a.V >> 3;
+    const int vend = min(v1, nfull);
+    const float c = a.c;
+
+    float m = -INFINITY, s = 0.f;
+    int v = v0 + (int)threadIdx.x;
+    for (; v + 3 * kBlock < vend; v += 4 * kBlock) {
+        Raw<DT> r0 = load_raw<DT, VEC>(rp, v);
+        Raw<DT> r1 = load_raw<DT, VEC>(rp, v + kBlock);
+        Raw<DT> r2 = load_raw<DT, VEC>(rp, v + 2 * kBlock);
+        Raw<DT> r3 = load_raw<DT, VEC>(rp, v + 3 * kBlock);
+        float e[4 * kVec];
+        decode<DT>(r0, e);
+        decode<DT>(r1, e + 8);
+        decode<DT>(r2, e + 16);
+        decode<DT>(r3, e + 24);
+        soft_update<4 * kVec>(e, m, s, c);
+    }
+    for (; v < vend; v += kBlock) {
+        Raw<DT> r0 = load_raw<DT, VEC>(rp, v);
+        float e[kVec];
+        decode<DT>(r0, e);
+        soft_update<kVec>(e, m, s, c);
+    }
+    if (v == nfull && nfull < v1) {    // the row's partial last vector
+        float e[kVec];
+        load_partial<DT>(rp, nfull, a.V - 8 * nfull, -INFINITY, e);
+        soft_update<kVec>(e, m, s, c);
+    }
+
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        float m2 = __shfl_xor(m, o, 64);
+        float s2 = __shfl_xor(s, o, 64);
+        soft_merge(m, s, m2, s2, c);
+    }
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 0) {
+        lds_m[w] = m;
+        lds_s[w] = s;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float M = lds_m[0], S = lds_s[0];
+        for (int i = 1; i < kWaves; ++i) soft_merge(M, S, lds_m[i], lds_s[i], c);
+        reinterpret_cast<SoftPartial*>(a.partials)[unit] = SoftPartial{M, S};
+    }
+}
+
+// Argmax with the lowest index among equal maxima.  Each thread keeps the
+// largest value it has seen and the first group of vectors where it appeared
+// (strictly-greater updates keep the first occurrence, in ascending index
+// order within the thread).  After the block maximum M is known, only the
+// threads holding M reload that one group to locate their first index of M;
+// the block takes the smallest.  -0.0 and +0.0 compare equal throughout.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kBlock) void k_argmax_stats(StatsArgs a)
+{
+    __shared__ float lds_f[kWaves];
+    __shared__ int lds_i[kWaves];
+    constexpr int ES = DT == DT_F32 ? 4 : 2;
+    const int unit = blockIdx.x;
+    const int row = unit / a.splits;
+    const int split = unit - row * a.splits;
+    const char* rp = stats_row(a, row, ES);
+    const int v0 = split * a.vec_per_split;
+    const int v1 = min(v0 + a.vec_per_split, a.nvec);
+    const int nfull = a.V >> 3;
+    const int vend = min(v1, nfull);
+
+    float bv = -INFINITY;
+    int bvec = -1, bcnt = 0;
+    int v = v0 + (int)threadIdx.x;
+    for (; v + 3 * kBlock < vend; v += 4 * kBlock) {
+        Raw<DT> r0 = load_raw<DT, VEC>(rp, v);
+        Raw<DT> r1 = load_raw<DT, VEC>(rp, v + kBlock);
+        Raw<DT> r2 = load_raw<DT, VEC>(rp, v + 2 * kBlock);
+        Raw<DT> r3 = load_raw<DT, VEC>(rp, v + 3 * kBlock);
+        float e[4 * kVec];
+        decode<DT>(r0, e);
+        decode<DT>(r1, e + 8);
+        decode<DT>(r2, e + 16);
+        decode<DT>(r3, e + 24);
+        float cm0 = e[0], cm1 = e[1];
+#pragma unroll
+        for (int j = 2; j < 4 * kVec; j += 2) {
+            cm0 = fmaxf(cm0, e[j]);
+            cm1 = fmaxf(cm1, e[j + 1]);
+        }
+        const float cm = fmaxf(cm0, cm1);
+        const bool up = cm > bv;
+        bv = up ? cm : bv;
+        bvec = up ? v : bvec;
+        bcnt = up ? 4 : bcnt;
+    }
+    for (; v < vend; v += kBlock) {
+        Raw<DT> r0 = load_raw<DT, VEC>(rp, v);
+        float e[kVec];
+        decode<DT>(r0, e);
+        float cm = e[0];
+#pragma unroll
+        for (int j = 1; j < kVec; ++j) cm = fmaxf(cm, e[j]);
+        const bool up = cm > bv;
+        bv = up ? cm : bv;
+        bvec = up ? v : bvec;
+        bcnt = up ? 1 : bcnt;
+    }
+    if (v == nfull && nfull < v1) {
+        float e[kVec];
+        load_partial<DT>(rp, nfull, a.V - 8 * nfull, -INFINITY, e);
+        float cm = e[0];
+#pragma unroll
+        for (int j = 1; j < kVec; ++j) cm = fmaxf(cm, e[j]);
+        if (cm > bv) {
+            bv = cm;
+            bvec = nfull;
+            bcnt = 1;
+        }
+    }
+
+    const float M = block_max(bv, lds_f);
+    int idx = INT32_MAX;
+    if (bv == M && M > -INFINITY) {
+        for (int j = 0; j < bcnt && idx == INT32_MAX; ++j) {
+            const int vv = bvec + j * kBlock;
+            float e[kVec];
+            load8<DT, VEC>(rp, vv, nfull, a.V, -INFINITY, e);
+#pragma unroll
+            for (int t = kVec - 1; t >= 0; --t)
+                if (e[t] == M) idx = 8 * vv + t;
+        }
+    }
+    idx = block_min_int(idx, lds_i);
+    if (threadIdx.x == 0) reinterpret_cast<ArgPartial*>(a.partials)[unit] = ArgPartial{M, idx};
+}
+
+template <typename K>
+static hipError_t launch_rows(K kernel, const StatsArgs& a, hipStream_t st)
+{
+    void* args[] = {const_cast<StatsArgs*>(&a)};
+    const unsigned grid = (unsigned)((long long)a.n_rows * a.splits);
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(grid), dim3(kBlock), args, 0, st);
+}
+
+hipError_t launch_softmax_stats(int dt, bool vec, const StatsArgs& a, hipStream_t st)
+{
+    switch (dt) {
+    case DT_F32: return vec ? launch_rows(k_softmax_stats<DT_F32, true>, a, st)
+                            : launch_rows(k_softmax_stats<DT_F32, false>, a, st);
+    case DT_F16: return vec ? launch_rows(k_softmax_stats<DT_F16, true>, a, st)
+                            : launch_rows(k_softmax_stats<DT_F16, false>, a, st);
+    default:     return vec ? launch_rows(k_softmax_stats<DT_BF16, true>, a, st)
+                            : launch_rows(k_softmax_stats<DT_BF16, false>, a, st);
+    }
+}
+
+hipError_t launch_argmax_stats(int dt, bool vec, const StatsArgs& a, hipStream_t st)
+{
+    switch (dt) {
+    case DT_F32: return vec ? launch_rows(k_argmax_stats<DT_F32, true>, a, st)
+                            : launch_rows(k_argmax_stats<DT_F32, false>, a, st);
+    case DT_F16: return vec ? launch_rows(k_argmax_stats<DT_F16, true>, a, st)
+                            : launch_rows(k_argmax_stats<DT_F16, false>, a, st);
+    default:     return vec ? launch_rows(k_argmax_stats<DT_BF16, true>, a, st)
+                            : launch_rows(k_argmax_stats<DT_BF16, false>, a, st);
+    }
+}
+
+}  // namespace sv

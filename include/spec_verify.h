@@ -1,0 +1,154 @@
+/*
+ * spec_verify.h -- C ABI of the MI355X (gfx950) speculative-decoding
+ * verification library (libspecverify.so).
+ *
+ * The operation.  A speculative-decoding round proposes k draft tokens
+ * x_0..x_{k-1} per sequence; the target model scores all of them in one pass
+ * and returns logits at k+1 positions.  The library applies the acceptance
+ * rule to a batch of B sequences and returns the committed tokens and the
+ * accepted length of each:
+ *
+ *  - sampling (production blog "Speculative Decoding: Faster Generation Without
+ *    Changing the Model", section "The acceptance rule"; the review function of
+ *    "Cascade Speculative Drafting", section "The Vertical Cascade", with
+ *    lenience 1): p_i = softmax(target_i / T), q_i = softmax(draft_i / T);
+ *    left to right, x_i is accepted iff u_i < min(1, p_i(x_i) / q_i(x_i))
+ *    (q_i(x_i) <= p_i(x_i) always accepts); the first rejected position j is
+ *    replaced by a draw from max(0, p_j - q_j) normalised, and the round ends;
+ *    if all k are accepted, a bonus token is drawn from p_k.
+ *  - greedy (same blog section, last sentences): x_i is accepted while it
+ *    equals argmax target_i; the first mismatch is replaced by that argmax; if
+ *    all k match, the bonus is argmax target_k.
+ *  - greedy candidates (Ouroboros, section 3.4.3, "Selecting the accepted
+ *    tokens"): C candidate drafts of L tokens verified in one pass; each
+ *    candidate's accepted length is its number of leading tokens equal to the
+ *    argmax of their rows; the longest wins (lowest candidate index on ties);
+ *    its accepted tokens are committed followed by the argmax correction.
+ *
+ * Conventions shared by every entry point.
+ *  - Pointers marked DEVICE are device memory (hipMalloc / torch tensors on
+ *    the GPU); the caller owns every buffer.  The library allocates no device
+ *    memory: scratch space comes from the caller's `workspace`.
+ *  - Logits are row-major: a row is V contiguous elements of `dtype`
+ *    (SV_F32 / SV_F16 / SV_BF16); consecutive rows are `*_row_stride`
+ *    ELEMENTS apart (stride >= V).  Target rows of sequence b are rows
+ *    b*(k+1) .. b*(k+1)+k; draft rows are b*k .. b*k+k-1.  With 16-byte aligned
+ *    base pointers and (stride * element size) % 16 == 0 the 16-byte vector
+ *    path runs; otherwise an element-wise path gives identical results.
+ *  - Draft tokens are int32.  A token outside [0, V) is rejected at its
+ *    position (its p and q are reported as 0); it never causes an
+ *    out-of-range read.
+ *  - Argmax: the lowest index among equal maxima; -0.0 equals +0.0; a row
+ *    whose elements are all -inf gives index 0.  Greedy ignores temperature.
+ *  - Sampling logits may hold -inf (masked tokens) but must hold at least one
+ *    finite value per row and no +inf or NaN; greedy logits must not hold NaN.
+ *    Inputs outside these contracts give unspecified tokens (always in
+ *    [0, V)), never a fault.
+ *  - Uniforms are float32 in [0, 1): `uniforms[b][i]` (i < k) decides draft
+ *    i; `uniforms[b][k]` drives the round's single draw (residual or bonus),
+ *    made by inverse CDF over the vocabulary in ascending index order: the
+ *    smallest token whose cumulative weight exceeds u times the total.
+ *  - Outputs: out_tokens[b] holds the committed tokens followed by -1 up to
+ *    its row length; out_num_accepted[b] is the number of accepted draft
+ *    tokens.  Sampling and greedy commit out_num_accepted[b] + 1 tokens.
+ *  - Asynchrony: every call validates its arguments on the host, then enqueues
+ *    its kernels on `hip_stream` (a hipStream_t, NULL = the null stream) and
+ *    returns without waiting.  Results are valid once the stream reaches
+ *    that point.  No host synchronisation, no host/device copies.
+ *  - Errors: argument checks run before anything is enqueued; on an error
+ *    nothing is launched and the outputs are untouched.  SV_EINVAL: a NULL
+ *    required pointer or a size/stride/temperature out of range; SV_EDTYPE:
+ *    an unknown dtype; SV_EWORKSPACE: workspace NULL or smaller than
+ *    spec_verify_workspace_bytes(); SV_EHIP: a launch failed (the HIP error
+ *    is reported by the runtime's error state).
+ *  - Re-entrancy: calls keep no state between them; concurrent calls must use
+ *    distinct workspaces.  Results are deterministic: the same inputs and
+ *    shapes give bit-identical outputs (no floating-point atomics).
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { SV_OK = 0, SV_EINVAL = 1, SV_EDTYPE = 2, SV_EWORKSPACE = 3, SV_EHIP = 4 };
+enum { SV_F32 = 0, SV_F16 = 1, SV_BF16 = 2 };
+
+#define SV_MAX_K 63
+#define SV_MAX_CANDIDATE_TOKENS 64
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int spec_verify_version(void);
+
+/* Human-readable name of a status code (static storage). */
+const char* spec_verify_status_string(int status);
+
+/* Bytes of device workspace a call needs.  `rows_per_seq` is the number of
+ * logit rows the call reads per sequence: k+1 for spec_verify_greedy, 2k+1 for
+ * spec_verify_sample, C*R for spec_verify_greedy_candidates.  Pure host
+ * function; returns 0 for arguments that any call would reject. */
+size_t spec_verify_workspace_bytes(int B, int rows_per_seq, int V, int dtype);
+
+/* Greedy verification (see the header comment).
+ *   target_logits  DEVICE [B][k+1][V] dtype, rows `target_row_stride` apart
+ *   draft_tokens   DEVICE [B][k] int32
+ *   1 <= B, 1 <= k <= 63, 1 <= V
+ *   out_tokens       DEVICE [B][k+1] int32 (x_0..x_{j-1}, correction, then -1)
+ *   out_num_accepted DEVICE [B] int32, j in [0, k]
+ *   workspace        DEVICE, >= spec_verify_workspace_bytes(B, k+1, V, dtype) */
+int spec_verify_greedy(const void* target_logits, long long target_row_stride,
+                       const int* draft_tokens, int B, int k, int V, int dtype,
+                       int* out_tokens, int* out_num_accepted,
+                       void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Sampling verification (see the header comment).
+ *   target_logits DEVICE [B][k+1][V], draft_logits DEVICE [B][k][V], same dtype
+ *   draft_tokens  DEVICE [B][k] int32, drawn by the proposer from q = softmax(draft / T)
+ *   uniforms      DEVICE [B][k+1] float32 in [0, 1)
+ *   temperature   > 0 and finite; applied to target and draft logits alike
+ *   out_tokens       DEVICE [B][k+1] int32, out_num_accepted DEVICE [B] int32
+ *   out_p_x, out_q_x DEVICE [B][k] float32, optional (NULL skips): p_i(x_i) and
+ *                    q_i(x_i) at every draft position (0 for invalid tokens)
+ *   workspace        DEVICE, >= spec_verify_workspace_bytes(B, 2k+1, V, dtype) */
+int spec_verify_sample(const void* target_logits, long long target_row_stride,
+                       const void* draft_logits, long long draft_row_stride,
+                       const int* draft_tokens, const float* uniforms, float temperature,
+                       int B, int k, int V, int dtype,
+                       int* out_tokens, int* out_num_accepted,
+                       float* out_p_x, float* out_q_x,
+                       void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Multi-candidate greedy verification (see the header comment).
+ *   target_logits DEVICE [B][C][R][V]; row (c, i) scores candidate token (c, i).
+ *                 R = L (no row after the last token: a fully accepted candidate
+ *                 commits L tokens) or R = L+1 (the last row gives one more
+ *                 greedy token).
+ *   cand_tokens   DEVICE [B][C][L] int32; 1 <= C, 1 <= L, C*L <= 64
+ *   out_tokens         DEVICE [B][L+1] int32, committed tokens then -1
+ *   out_num_accepted   DEVICE [B] int32: accepted length A of the chosen candidate
+ *   out_best_candidate DEVICE [B] int32: the chosen candidate c*
+ *   workspace          DEVICE, >= spec_verify_workspace_bytes(B, C*R, V, dtype) */
+int spec_verify_greedy_candidates(const void* target_logits, long long row_stride,
+                                  const int* cand_tokens, int B, int C, int L, int R, int V,
+                                  int dtype, int* out_tokens, int* out_num_accepted,
+                                  int* out_best_candidate,
+                                  void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Measurement aid (not thread-safe; for a single profiling thread).  While
+ * enabled, each of the next `max_calls` verification calls records a pair of
+ * HIP events on its stream around its vocabulary-streaming statistics kernel
+ * (the kernel that reads every logit).  spec_verify_profile_end waits for the
+ * recorded events, writes up to `max_out` durations in milliseconds, frees the
+ * events, disables recording and returns the number of recorded calls (or a
+ * negative value on a HIP error).  spec_verify_profile_begin returns a status. */
+int spec_verify_profile_begin(int max_calls);
+int spec_verify_profile_end(float* out_ms, int max_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

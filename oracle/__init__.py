@@ -74,8 +74,9 @@ def lib():
         L.oracle_sample.argtypes = [P, LL, P, LL, P, P, D, I, I, I, P, P, P, I]
         L.oracle_greedy_candidates.argtypes = [P, LL, P, I, I, I, I, I, P, P, P]
         L.oracle_token_probs_seq.argtypes = [P, LL, P, LL, P, D, I, I, P, P]
+        L.oracle_draw_interval.argtypes = [P, P, D, I, I, P, P, P]
         for f in ("oracle_greedy", "oracle_sample", "oracle_greedy_candidates",
-                  "oracle_token_probs_seq", "oracle_trace_size"):
+                  "oracle_token_probs_seq", "oracle_trace_size", "oracle_draw_interval"):
             getattr(L, f).restype = I
         if L.oracle_trace_size() != ctypes.sizeof(Trace):
             raise RuntimeError("oracle_trace layout mismatch")
@@ -150,6 +151,22 @@ def token_probs(target_seq, draft_seq, draft_tokens_seq, temperature):
     if rc:
         raise RuntimeError(f"oracle_token_probs_seq failed: {rc}")
     return px, qx
+
+
+def draw_interval(target_row, draft_row, temperature, token):
+    """(lo, hi, weight): where `token` sits in the cumulative distribution a
+    round draws from (residual against `draft_row`, or p if draft_row is None)."""
+    z = _f32(target_row)
+    y = None if draft_row is None else _f32(draft_row)
+    lo = ctypes.c_double()
+    hi = ctypes.c_double()
+    w = ctypes.c_double()
+    rc = lib().oracle_draw_interval(_ptr(z), None if y is None else _ptr(y), float(temperature),
+                                    z.shape[-1], int(token), ctypes.byref(lo), ctypes.byref(hi),
+                                    ctypes.byref(w))
+    if rc:
+        raise RuntimeError(f"oracle_draw_interval failed: {rc}")
+    return lo.value, hi.value, w.value
 
 
 def greedy_candidates(target, cand_tokens, R=None):

@@ -271,6 +271,47 @@ int oracle_token_probs_seq(const float* target, long long ts, const float* draft
     return rc;
 }
 
+/* The CDF interval of one token in the distribution a round draws from
+ * (residual or p), by the same ascending-index convention as inverse_cdf. */
+int oracle_draw_interval(const float* target_row, const float* draft_row, double T, int V,
+                         int token, double* lo, double* hi, double* weight)
+{
+    if (!target_row || !lo || !hi || !weight || V < 1 || token < 0 || token >= V) return -1;
+    if (!(T > 0.0) || !isfinite(T)) return -1;
+    double* p = (double*)malloc(sizeof(double) * (size_t)V);
+    double* w = (double*)malloc(sizeof(double) * (size_t)V);
+    if (!p || !w) { free(p); free(w); return -2; }
+    int rc = softmax_row(target_row, V, T, p);
+    if (rc == 0) {
+        double total = 0.0;
+        if (draft_row) {
+            rc = softmax_row(draft_row, V, T, w);
+            if (rc == 0) {
+                for (int t = 0; t < V; ++t) {
+                    double d = p[t] - w[t];
+                    w[t] = d > 0.0 ? d : 0.0;
+                    total += w[t];
+                }
+            }
+        }
+        if (rc == 0) {
+            if (!draft_row || !(total > 0.0)) {
+                memcpy(w, p, sizeof(double) * (size_t)V);
+                total = 0.0;
+                for (int t = 0; t < V; ++t) total += w[t];
+            }
+            double c = 0.0;
+            for (int t = 0; t < token; ++t) c += w[t];
+            *lo = c / total;
+            *hi = (c + w[token]) / total;
+            *weight = w[token] / total;
+        }
+    }
+    free(p);
+    free(w);
+    return rc;
+}
+
 /* ---- multi-candidate greedy --------------------------------------------
  * Ouroboros, section 3.4.3, "Selecting the accepted tokens": the candidates
  * share their first tokens (the base draft) and are verified together.  For

@@ -133,6 +133,16 @@ int oracle_greedy_candidates(const float* target, long long row_stride,
                              const int* cand_tokens, int B, int C, int L, int R, int V,
                              int* out_tokens, int* out_num_accepted, int* out_best);
 
+/* The interval [lo, hi] of cumulative probability (ascending token order)
+ * that `token` occupies in the distribution one round draws from: the
+ * residual max(0, p - q) normalised when `draft_row` is given (p itself if
+ * that residual has no mass), else p.  *weight is the token's probability in
+ * that distribution.  A draw with uniform u picks `token` exactly when
+ * lo <= u < hi.  Used to check that a draw whose u lies within rounding of a
+ * boundary picked one of the tokens on either side. */
+int oracle_draw_interval(const float* target_row, const float* draft_row, double temperature,
+                         int V, int token, double* lo, double* hi, double* weight);
+
 int oracle_trace_size(void);
 
 #ifdef __cplusplus

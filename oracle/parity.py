@@ -1,0 +1,112 @@
+"""Comparison of the GPU library's outputs with the CPU oracle.
+
+TEST INFRASTRUCTURE ONLY (tests, smoke check).  Receives plain arrays; never
+imports or calls the GPU library.
+
+Greedy and candidate results must be bit-exact.  Sampling results must match
+exactly, except in rounds where the oracle's own decision lies within `eps`
+of its boundary, where float32 rounding on the GPU may legitimately go the
+other way:
+  - an acceptance decision with |u_i - min(1, p/q)| < eps: the rounds may
+    then diverge from that position on (the accepted drafts before it must
+    still agree);
+  - the round's draw with u_k within eps of a boundary of the drawn token's
+    CDF interval: the GPU's token must then be a token of positive weight
+    whose own interval lies within eps of u_k.
+Such rounds are counted, not hidden.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+from . import draw_interval, greedy, greedy_candidates, sample, token_probs
+
+
+@dataclasses.dataclass
+class SampleReport:
+    rounds: int = 0
+    exact: int = 0
+    tie_accept: int = 0
+    tie_sample: int = 0
+    failures: list = dataclasses.field(default_factory=list)
+    committed: int = 0
+
+    def ok(self):
+        return not self.failures
+
+    def summary(self):
+        return (f"rounds={self.rounds} exact={self.exact} tie_accept={self.tie_accept} "
+                f"tie_sample={self.tie_sample} failures={len(self.failures)} "
+                f"mean_committed={self.committed / max(1, self.rounds):.4f}")
+
+
+def check_sample(z, y, x, u, T, gpu_tokens, gpu_nacc, eps=1e-5, report=None,
+                 seq_ids=None) -> SampleReport:
+    """z [B,k+1,V], y [B,k,V] float32; x [B,k]; u [B,k+1]; GPU outputs as numpy."""
+    rep = report or SampleReport()
+    ot, on, tr = sample(z, y, x, u, T, traces=True)
+    B, k1 = ot.shape
+    k = k1 - 1
+    for b in range(B):
+        sid = b if seq_ids is None else seq_ids[b]
+        rep.rounds += 1
+        rep.committed += int(gpu_nacc[b]) + 1
+        gt, gn = gpu_tokens[b], int(gpu_nacc[b])
+        if gn == on[b] and (gt == ot[b]).all():
+            rep.exact += 1
+            continue
+        t = tr[b]
+        first = min(gn, int(on[b]))
+        if not (0 <= gn <= k) or not (gt[:first] == ot[b, :first]).all():
+            rep.failures.append((sid, "accepted prefix differs", gt.tolist(), ot[b].tolist()))
+            continue
+        if (gt[gn + 1:] != -1).any():
+            rep.failures.append((sid, "padding", gt.tolist(), ot[b].tolist()))
+            continue
+        if gn != on[b]:
+            if first < t.evaluated and t.accept_margin[first] < eps:
+                rep.tie_accept += 1
+            else:
+                rep.failures.append((sid, f"accepted length {gn} vs {on[b]}", gt.tolist(),
+                                     ot[b].tolist(), t.accept_margin[first]))
+            continue
+        j = gn
+        if t.sample_margin < eps:
+            lo, hi, w = draw_interval(z[b, j], y[b, j] if j < k else None, T, int(gt[j])) \
+                if 0 <= gt[j] < z.shape[2] else (0.0, 0.0, 0.0)
+            if w > 0 and lo - eps <= u[b, k] <= hi + eps:
+                rep.tie_sample += 1
+                continue
+        rep.failures.append((sid, f"drawn token {gt[j]} vs {ot[b, j]}", float(u[b, k]),
+                             t.sample_lo, t.sample_hi, t.sample_margin))
+    return rep
+
+
+def check_probs(z, y, x, T, gpu_px, gpu_qx, rtol=1e-5):
+    """Largest relative error of the exported p_i(x_i), q_i(x_i) over all positions."""
+    worst = 0.0
+    for b in range(z.shape[0]):
+        px, qx = token_probs(z[b], y[b], x[b], T)
+        for ref, got in ((px, gpu_px[b]), (qx, gpu_qx[b])):
+            zero = ref == 0
+            if (got[zero] != 0).any():
+                return float("inf")
+            if (~zero).any():
+                rel = np.abs(got[~zero].astype(np.float64) - ref[~zero]) / ref[~zero]
+                worst = max(worst, float(rel.max()))
+    return worst
+
+
+def check_greedy(z, x, gpu_tokens, gpu_nacc):
+    """Bit-exact comparison; returns the list of mismatching sequence indices."""
+    ot, on = greedy(z, x)
+    bad = np.nonzero((on != gpu_nacc) | (ot != gpu_tokens).any(axis=1))[0]
+    return bad.tolist(), ot, on
+
+
+def check_candidates(z, cand, gpu_tokens, gpu_A, gpu_best):
+    ot, oa, ob = greedy_candidates(z, cand)
+    bad = np.nonzero((oa != gpu_A) | (ob != gpu_best) | (ot != gpu_tokens).any(axis=1))[0]
+    return bad.tolist(), ot, oa, ob

@@ -212,3 +212,22 @@ def _generate_candidates(cfg: Config, gen, device, chunk_seqs) -> Workload:
         tok[:, :, :P] = tok[:, :1, :P]
         cand[b0:b1] = tok.to(torch.int32)
     return Workload(cfg, target, None, cand, None, 1.0)
+
+
+def chain(B: int, k: int, V: int, dtype: str = "bf16", var_target: float = 2.0,
+          var_noise: float = 1.0, spike: float = 0.0, T: float = 1.0, seed: int = 0,
+          device="cpu") -> Workload:
+    """A chain-draft workload of any shape (test cases beyond the five workloads)."""
+    cfg = Config(0, B=B, k=k, V=V, dtype=dtype, var_target=var_target, var_noise=var_noise,
+                 spike=spike, T=T, modes=("greedy", "sample"))
+    return _generate_chain(cfg, make_generator(seed, device), device, None)
+
+
+def candidates(B: int, C: int, L: int, R: int, V: int, dtype: str = "bf16",
+               var_target: float = 3.0, spike: float = 8.0, p_match: float = 0.8,
+               shared_rows: int = 3, seed: int = 0, device="cpu") -> Workload:
+    """A multi-candidate workload of any shape."""
+    cfg = Config(0, B=B, k=L, V=V, dtype=dtype, var_target=var_target, var_noise=0.0,
+                 spike=spike, T=1.0, modes=("candidates",), C=C, L=L, R=R,
+                 shared_rows=min(shared_rows, L), p_match=p_match)
+    return _generate_candidates(cfg, make_generator(seed, device), device, None)

@@ -1,0 +1,356 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on the GPU.
+
+Greedy and candidate selection: bit-exact.  Sampling: exact except in rounds
+where the oracle's own decision lies within 1e-5 of its boundary (counted, and
+checked for validity: see oracle/parity.py); exported p_i(x_i), q_i(x_i)
+within 1e-5 relative.  Shapes span several workgroup slices and a ragged tail
+(V not a multiple of 8, rows not 16-byte aligned, V < 8, k = 1 and 63), the
+five workloads at full size, and the degenerate cases of the rule.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from oracle import parity
+
+pytestmark = pytest.mark.gpu
+
+EPS = 1e-5
+PROB_RTOL = 1e-5
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def sv():
+    assert torch.cuda.is_available(), "GPU tests need the MI355X"
+    if not os.path.exists(oracle.LIB_PATH):
+        oracle.build()
+    import draft_verification_verify_amd as m
+    return m
+
+
+def f32(t):
+    return t.float().cpu().numpy()
+
+
+def npi(t):
+    return t.cpu().numpy()
+
+
+def corrupt_after_argmax(target, k, gen, p_keep=0.7):
+    """Drafts equal to the target argmax for a random prefix, then random:
+    greedy acceptance lengths spread over 0..k."""
+    B, _, V = target.shape
+    am = torch.argmax(target[:, :k].float(), dim=2).to(torch.int32)
+    keep = torch.rand((B, k), generator=gen, device=target.device) < p_keep
+    rnd = torch.randint(0, V, (B, k), generator=gen, device=target.device, dtype=torch.int32)
+    return torch.where(keep, am, rnd)
+
+
+def with_layout(t, layout, gen):
+    """Return a view of `t` with the requested memory layout: 'dense', 'padded'
+    (row stride V+1: not 16-byte aligned), or 'offset' (base shifted by one
+    element inside a wider buffer)."""
+    if layout == "dense":
+        return t
+    *lead, V = t.shape
+    pad = 1 if layout == "padded" else 9
+    big = torch.randn((*lead, V + pad), generator=gen, device=t.device).to(t.dtype)
+    off = 0 if layout == "padded" else 1
+    big[..., off:off + V] = t
+    return big[..., off:off + V]
+
+
+# ---------------------------------------------------------------------------
+# greedy
+# ---------------------------------------------------------------------------
+SHAPES = [(1, 1, 1), (3, 2, 7), (5, 4, 8), (4, 3, 1000), (2, 5, 4097), (6, 4, 32000),
+          (2, 63, 300), (1, 4, 128256), (9, 8, 12345)]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("B,k,V", SHAPES)
+@pytest.mark.parametrize("layout", ["dense", "padded", "offset"])
+def test_greedy_parity(sv, dtype, B, k, V, layout):
+    g = torch.Generator(device=DEV).manual_seed(B * 7919 + k * 31 + V)
+    w = synthetic.chain(B, k, V, dtype, seed=B + k + V, device=DEV)
+    x = corrupt_after_argmax(w.target, k, g)
+    tgt = with_layout(w.target, layout, g)
+    toks, na = sv.greedy(tgt, x)
+    torch.cuda.synchronize()
+    bad, ot, on = parity.check_greedy(f32(w.target), npi(x), npi(toks), npi(na))
+    assert not bad, (bad[:5], npi(toks)[bad[:3]], ot[bad[:3]])
+
+
+def test_greedy_ties_zeros_and_masked_rows(sv):
+    """Tie-heavy integer logits, -0.0/+0.0 ties, rows that are all -inf."""
+    g = torch.Generator(device=DEV).manual_seed(5)
+    B, k, V = 64, 6, 3001
+    for dtype in (torch.float32, torch.float16, torch.bfloat16):
+        z = torch.randint(-3, 3, (B, k + 1, V), generator=g, device=DEV).to(dtype)
+        zero = z == 0
+        neg = torch.rand(z.shape, generator=g, device=DEV) < 0.5
+        z = torch.where(zero & neg, torch.tensor(-0.0, dtype=dtype, device=DEV), z)
+        z[::7] = -float("inf")
+        z[3, 2, :] = 2.0                  # a whole row tied: index 0
+        x = corrupt_after_argmax(z, k, g, 0.8)
+        toks, na = sv.greedy(z, x)
+        torch.cuda.synchronize()
+        bad, _, _ = parity.check_greedy(f32(z), npi(x), npi(toks), npi(na))
+        assert not bad, (dtype, bad[:5])
+
+
+def test_greedy_invalid_tokens(sv):
+    g = torch.Generator(device=DEV).manual_seed(6)
+    w = synthetic.chain(32, 5, 2000, "bf16", seed=6, device=DEV)
+    x = corrupt_after_argmax(w.target, 5, g, 1.0)
+    pos = torch.randint(0, 5, (32,), generator=g, device=DEV)
+    bad_vals = torch.tensor([-1, 2000, 2001, -(2 ** 31), 2 ** 31 - 1], device=DEV, dtype=torch.int32)
+    x[torch.arange(32, device=DEV), pos] = bad_vals[torch.arange(32, device=DEV) % 5]
+    toks, na = sv.greedy(w.target, x)
+    torch.cuda.synchronize()
+    assert (npi(na) == npi(pos)).all()
+    bad, _, _ = parity.check_greedy(f32(w.target), npi(x), npi(toks), npi(na))
+    assert not bad
+
+
+# ---------------------------------------------------------------------------
+# sampling
+# ---------------------------------------------------------------------------
+def run_sample(sv, w, layout="dense", gen=None):
+    tgt = with_layout(w.target, layout, gen) if layout != "dense" else w.target
+    dft = with_layout(w.draft, layout, gen) if layout != "dense" else w.draft
+    toks, na, px, qx = sv.sample(tgt, dft, w.tokens, w.uniforms, w.T, return_probs=True)
+    torch.cuda.synchronize()
+    return npi(toks), npi(na), npi(px), npi(qx)
+
+
+def assert_sample_parity(w, toks, na, px, qx):
+    z, y = f32(w.target), f32(w.draft)
+    x, u = npi(w.tokens), npi(w.uniforms)
+    rep = parity.check_sample(z, y, x, u, w.T, toks, na, eps=EPS)
+    assert rep.ok(), (rep.summary(), rep.failures[:3])
+    print(rep.summary())
+    worst = parity.check_probs(z, y, x, w.T, px, qx)
+    assert worst <= PROB_RTOL, worst
+    return rep
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("B,k,V", SHAPES)
+@pytest.mark.parametrize("T", [0.6, 1.0])
+def test_sample_parity(sv, dtype, B, k, V, T):
+    w = synthetic.chain(B, k, V, dtype, var_target=2.0, var_noise=0.5, T=T, seed=B * 3 + k + V,
+                        device=DEV)
+    toks, na, px, qx = run_sample(sv, w)
+    assert_sample_parity(w, toks, na, px, qx)
+
+
+@pytest.mark.parametrize("layout", ["padded", "offset"])
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+def test_sample_parity_unaligned(sv, dtype, layout):
+    g = torch.Generator(device=DEV).manual_seed(9)
+    w = synthetic.chain(12, 4, 5003, dtype, var_noise=0.5, T=0.8, seed=17, device=DEV)
+    toks, na, px, qx = run_sample(sv, w, layout, g)
+    assert_sample_parity(w, toks, na, px, qx)
+
+
+def test_sample_identical_draft_takes_bonus(sv):
+    """p = q: every draft is accepted and the bonus is drawn from p_k."""
+    w = synthetic.chain(64, 7, 3000, "bf16", T=1.3, seed=21, device=DEV)
+    w.draft.copy_(w.target[:, :7])
+    toks, na, px, qx = run_sample(sv, w)
+    assert (na == 7).all()
+    assert_sample_parity(w, toks, na, px, qx)
+
+
+def test_sample_masked_tokens(sv):
+    """Grammar-style masking: the same columns are -inf in target and draft."""
+    g = torch.Generator(device=DEV).manual_seed(22)
+    w = synthetic.chain(48, 5, 4000, "fp16", var_noise=1.0, T=1.0, seed=22, device=DEV)
+    mask = torch.rand((48, 1, 4000), generator=g, device=DEV) < 0.4
+    w.target.masked_fill_(mask, -float("inf"))
+    w.draft.masked_fill_(mask, -float("inf"))
+    w.tokens.copy_(synthetic.gumbel_max_sample(w.draft.reshape(-1, 4000), 1.0, g).reshape(48, 5))
+    toks, na, px, qx = run_sample(sv, w)
+    assert_sample_parity(w, toks, na, px, qx)
+    m = npi(mask[:, 0])
+    for b in range(48):
+        assert not m[b, toks[b, : na[b] + 1]].any()
+
+
+def test_sample_invalid_tokens(sv):
+    g = torch.Generator(device=DEV).manual_seed(23)
+    w = synthetic.chain(40, 6, 1000, "bf16", seed=23, device=DEV)
+    w.draft.copy_(w.target[:, :6])                       # valid drafts always accepted
+    pos = torch.randint(0, 6, (40,), generator=g, device=DEV)
+    vals = torch.tensor([-1, 1000, 5000, -(2 ** 31)], device=DEV, dtype=torch.int32)
+    w.tokens[torch.arange(40, device=DEV), pos] = vals[torch.arange(40, device=DEV) % 4]
+    toks, na, px, qx = run_sample(sv, w)
+    assert (na == npi(pos)).all()
+    assert_sample_parity(w, toks, na, px, qx)
+
+
+def test_sample_low_temperature_matches_greedy(sv):
+    """Low temperature: the sampling path reproduces the greedy path's tokens
+    (the greedy collapse), both through the library."""
+    g = torch.Generator(device=DEV).manual_seed(24)
+    B, k, V = 64, 5, 2048
+    z = torch.randint(-20, 20, (B, k + 1, V), generator=g, device=DEV).float()
+    am = torch.randint(0, V, (B, k + 1), generator=g, device=DEV)
+    z.scatter_(2, am[..., None], 21.0)
+    y = z[:, :k].clone()
+    x = corrupt_after_argmax(z, k, g, 0.7)
+    y.scatter_(2, x[..., None].long(), 40.0)           # the draft puts its mass on x
+    u = (torch.rand((B, k + 1), generator=g, device=DEV) * 0.998 + 0.001).float()
+    ts, ns = sv.sample(z, y, x, u, 0.02)
+    tg, ng = sv.greedy(z, x)
+    torch.cuda.synchronize()
+    assert (npi(ns) == npi(ng)).all() and (npi(ts) == npi(tg)).all()
+
+
+# ---------------------------------------------------------------------------
+# candidates
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("B,C,L,R,V", [(1, 1, 1, 1, 5), (3, 2, 4, 4, 999), (5, 8, 8, 8, 3000),
+                                       (4, 8, 8, 9, 3000), (2, 1, 63, 63, 500), (2, 1, 63, 64, 500),
+                                       (6, 4, 16, 17, 20000)])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_candidates_parity(sv, B, C, L, R, V, dtype):
+    w = synthetic.candidates(B, C, L, R, V, dtype, spike=8.0, seed=B + C + L + V, device=DEV)
+    toks, A, best = sv.greedy_candidates(w.target, w.tokens)
+    torch.cuda.synchronize()
+    bad, ot, oa, ob = parity.check_candidates(f32(w.target), npi(w.tokens), npi(toks), npi(A),
+                                              npi(best))
+    assert not bad, (bad[:5], npi(toks)[bad[:2]], ot[bad[:2]])
+
+
+# ---------------------------------------------------------------------------
+# the five workloads at full size
+# ---------------------------------------------------------------------------
+def test_workload1_rounds(sv):
+    """B=1, k=4, V=32000 fp32: 1000 rounds, one call each, greedy and sampling."""
+    w = synthetic.generate(1, device=DEV, B=1000)
+    tg, ng, ts, ns = [], [], [], []
+    for r in range(1000):
+        a, b = sv.greedy(w.target[r:r + 1], w.tokens[r:r + 1])
+        c, d = sv.sample(w.target[r:r + 1], w.draft[r:r + 1], w.tokens[r:r + 1],
+                         w.uniforms[r:r + 1], w.T)
+        tg.append(a); ng.append(b); ts.append(c); ns.append(d)
+    torch.cuda.synchronize()
+    tg, ng = npi(torch.cat(tg)), npi(torch.cat(ng))
+    ts, ns = npi(torch.cat(ts)), npi(torch.cat(ns))
+    z, y = f32(w.target), f32(w.draft)
+    bad, _, _ = parity.check_greedy(z, npi(w.tokens), tg, ng)
+    assert not bad
+    rep = parity.check_sample(z, y, npi(w.tokens), npi(w.uniforms), w.T, ts, ns, eps=EPS)
+    assert rep.ok(), (rep.summary(), rep.failures[:3])
+    print("workload 1:", rep.summary())
+
+
+def test_workload2(sv):
+    for s in range(3):
+        w = synthetic.generate(2, device=DEV, set_index=s)
+        toks, na, px, qx = run_sample(sv, w)
+        rep = assert_sample_parity(w, toks, na, px, qx)
+        print(f"workload 2 set {s}:", rep.summary())
+
+
+@pytest.fixture(scope="module")
+def w3():
+    return synthetic.generate(3, device=DEV)
+
+
+def test_workload3_sample(sv, w3):
+    toks, na, px, qx = run_sample(sv, w3)
+    rep = assert_sample_parity(w3, toks, na, px, qx)
+    print("workload 3 sample:", rep.summary())
+
+
+def test_workload3_greedy(sv, w3):
+    toks, na = sv.greedy(w3.target, w3.tokens)
+    torch.cuda.synchronize()
+    bad, _, on = parity.check_greedy(f32(w3.target), npi(w3.tokens), npi(toks), npi(na))
+    assert not bad
+    print("workload 3 greedy: mean committed", on.mean() + 1)
+
+
+def test_workload3_deterministic(sv, w3):
+    a = run_sample(sv, w3)
+    b = run_sample(sv, w3)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+    g1 = [npi(t) for t in sv.greedy(w3.target, w3.tokens)]
+    g2 = [npi(t) for t in sv.greedy(w3.target, w3.tokens)]
+    assert all(np.array_equal(u, v) for u, v in zip(g1, g2))
+
+
+def test_workload4(sv):
+    w = synthetic.generate(4, device=DEV)
+    toks, A, best = sv.greedy_candidates(w.target, w.tokens)
+    torch.cuda.synchronize()
+    bad, ot, oa, ob = parity.check_candidates(f32(w.target), npi(w.tokens), npi(toks), npi(A),
+                                              npi(best))
+    assert not bad
+    print("workload 4: mean accepted", oa.mean())
+
+
+@pytest.fixture(scope="module")
+def w5():
+    return synthetic.generate(5, device=DEV)
+
+
+def test_workload5_sample(sv, w5):
+    """Full B=512, k=16, V=128256 bf16 call; every sequence checked for the
+    rule's invariants, 64 evenly spaced sequences against the oracle."""
+    toks, na, px, qx = run_sample(sv, w5)
+    x = npi(w5.tokens)
+    assert ((na >= 0) & (na <= 16)).all()
+    for b in range(512):
+        assert (toks[b, : na[b]] == x[b, : na[b]]).all()
+        assert 0 <= toks[b, na[b]] < 128256
+        assert (toks[b, na[b] + 1:] == -1).all()
+    idx = np.arange(0, 512, 8)
+    ti = torch.as_tensor(idx, device=DEV)
+    z, y = f32(w5.target[ti]), f32(w5.draft[ti])
+    u = npi(w5.uniforms)[idx]
+    rep = parity.check_sample(z, y, x[idx], u, w5.T, toks[idx], na[idx], eps=EPS, seq_ids=idx)
+    assert rep.ok(), (rep.summary(), rep.failures[:3])
+    worst = parity.check_probs(z, y, x[idx], w5.T, px[idx], qx[idx])
+    assert worst <= PROB_RTOL, worst
+    print("workload 5 sample:", rep.summary())
+
+
+def test_workload5_greedy(sv, w5):
+    toks, na = sv.greedy(w5.target, w5.tokens)
+    torch.cuda.synchronize()
+    idx = np.arange(0, 512, 4)
+    ti = torch.as_tensor(idx, device=DEV)
+    bad, _, _ = parity.check_greedy(f32(w5.target[ti]), npi(w5.tokens)[idx], npi(toks)[idx],
+                                    npi(na)[idx])
+    assert not bad
+
+
+# ---------------------------------------------------------------------------
+# streams and the measurement aid
+# ---------------------------------------------------------------------------
+def test_side_stream_and_profile(sv):
+    w = synthetic.chain(16, 4, 20000, "bf16", seed=31, device=DEV)
+    ref = run_sample(sv, w)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    sv.profile_begin(4)
+    with torch.cuda.stream(s):
+        out = sv.sample(w.target, w.draft, w.tokens, w.uniforms, w.T, return_probs=True)
+        out2 = sv.greedy(w.target, w.tokens)
+    ms = sv.profile_end()
+    torch.cuda.synchronize()
+    assert len(ms) == 2 and all(m > 0 for m in ms)
+    for a, b in zip(ref, out):
+        assert np.array_equal(a, npi(b))
+    bad, _, _ = parity.check_greedy(f32(w.target), npi(w.tokens), npi(out2[0]), npi(out2[1]))
+    assert not bad
