@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 METRIC = "verified positions/sec (B·(k+1) rows/s) and achieved HBM GB/s vs peak"
-STATS_SOURCES = ["sv_stats.hip", "sv_device.h", "sv_launch.h"]
+STATS_SOURCES = ["sv_stats.hip", "sv_device.h", "sv_launch.h", "sv_api.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_softmax_stats_workload5_traffic.json")
 
 
@@ -63,7 +63,15 @@ def main():
                          "candidates: workload 4")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU oracle baseline budget (0 disables it)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 1 GiB device copy (scale for the rocprofv3 byte counters)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the statistics kernel's measured HBM traffic from two "
+                         "rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) and exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from_pmc(*args.traffic_from)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the verification step has no multi-GPU path in "
@@ -192,14 +200,17 @@ def main():
 
     if args.cpu_seconds > 0 and args.mode == "sample":
         line["cpu_baseline"] = cpu_baseline(w, out_t, out_n, args.cpu_seconds)
+    if args.calibrate_copy:
+        calibrate_copy()
     print(json.dumps(line), flush=True)
 
 
 def cpu_baseline(w, out_t, out_n, budget_s):
     """The CPU oracle, as written (one thread, double precision), timed on the
-    first sequences of the same workload until `budget_s` of oracle time is
-    spent.  Host copies are outside the timed part.  The oracle's results on
-    those sequences are compared with the GPU's last call."""
+    sequences of the same workload, in order, passing over the batch again if
+    needed, until `budget_s` of oracle time is spent.  Host copies are outside
+    the timed part.  The oracle's results on the first pass are compared with
+    the GPU's last call."""
     import numpy as np
 
     import oracle
@@ -208,34 +219,101 @@ def cpu_baseline(w, out_t, out_n, budget_s):
         oracle.build()
     B, k1, V = w.target.shape
     chunk = 16
-    done, spent = 0, 0.0
+    done, spent, passes = 0, 0.0, 0
     gt = out_t.cpu().numpy()
     gn = out_n.cpu().numpy()
     rep = parity.SampleReport()
-    for b0 in range(0, B, chunk):
-        b1 = min(B, b0 + chunk)
-        z = w.target[b0:b1].float().cpu().numpy()
-        y = w.draft[b0:b1].float().cpu().numpy()
-        x = w.tokens[b0:b1].cpu().numpy()
-        u = w.uniforms[b0:b1].cpu().numpy()
-        t0 = time.perf_counter()
-        oracle.sample(z, y, x, u, w.T)
-        spent += time.perf_counter() - t0
-        done = b1
-        parity.check_sample(z, y, x, u, w.T, gt[b0:b1], gn[b0:b1], report=rep,
-                            seq_ids=np.arange(b0, b1))
-        if spent >= budget_s:
-            break
+    while spent < budget_s:
+        for b0 in range(0, B, chunk):
+            b1 = min(B, b0 + chunk)
+            z = w.target[b0:b1].float().cpu().numpy()
+            y = w.draft[b0:b1].float().cpu().numpy()
+            x = w.tokens[b0:b1].cpu().numpy()
+            u = w.uniforms[b0:b1].cpu().numpy()
+            t0 = time.perf_counter()
+            oracle.sample(z, y, x, u, w.T)
+            spent += time.perf_counter() - t0
+            done += b1 - b0
+            if passes == 0:
+                parity.check_sample(z, y, x, u, w.T, gt[b0:b1], gn[b0:b1], report=rep,
+                                    seq_ids=np.arange(b0, b1))
+            if spent >= budget_s:
+                break
+        passes += 1
     return {
         "value": done * k1 / spent,
         "unit": "rows/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"first {done} of {B} sequences of the same workload ({done * k1} rows); "
-                   f"single-threaded C oracle in double precision, {spent:.1f} s; it stops at "
-                   f"each sequence's first rejection, so it reads fewer rows than it counts"),
-        "parity_vs_gpu": rep.summary(),
+        "sample": (f"{done} sequences ({done * k1} rows) of the same workload, in batch order"
+                   f"{' over ' + str(passes) + ' passes' if passes > 1 else ''}; single-threaded "
+                   f"C oracle in double precision, {spent:.1f} s; it stops at each sequence's "
+                   f"first rejection, so it reads fewer rows than it counts"),
+        "parity_vs_gpu_first_pass": rep.summary(),
     }
+
+
+def calibrate_copy(nbytes=1 << 30):
+    """A plain device-to-device copy of known size, for scaling the rocprofv3
+    FETCH_SIZE / WRITE_SIZE counters (run under --pmc)."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": nbytes}), flush=True)
+
+
+def traffic_from_pmc(fetch_csv, write_csv, out_path=TRAFFIC_FILE, copy_bytes=1 << 30):
+    """Turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, then
+    WRITE_SIZE, in KiB per dispatch) into HBM bytes per launch of the
+    statistics kernel, each counter scaled by what it reads for the
+    calibration copy of `copy_bytes`."""
+    import csv
+
+    def dispatches(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r.get("Counter_Name") == counter]
+        return sorted(rows, key=lambda r: int(r["Dispatch_Id"]))
+
+    def stats_mean(rows):
+        v = [float(r["Counter_Value"]) for r in rows if "k_softmax_stats" in r["Kernel_Name"]]
+        if not v:
+            raise SystemExit("no k_softmax_stats dispatch in the counter file")
+        return statistics.fmean(v), next(r["Kernel_Name"] for r in rows if "k_softmax_stats" in r["Kernel_Name"])
+
+    def last_copy(rows):
+        # the calibration copy is the process's last dispatch
+        r = rows[-1]
+        if "copy" not in r["Kernel_Name"].lower():
+            raise SystemExit(f"last dispatch is not the calibration copy: {r['Kernel_Name']}")
+        return float(r["Counter_Value"]), r["Kernel_Name"]
+
+    f = dispatches(fetch_csv, "FETCH_SIZE")
+    wr = dispatches(write_csv, "WRITE_SIZE")
+    fk, fname = stats_mean(f)
+    wk, _ = stats_mean(wr)
+    fc, cname = last_copy(f)
+    wc, _ = last_copy(wr)
+    f_scale = fc * 1024 / copy_bytes
+    w_scale = wc * 1024 / copy_bytes
+    out = {
+        "kernel": fname,
+        "kernel_digest": stats_kernel_digest(),
+        "fetch_kib_per_dispatch": fk,
+        "write_kib_per_dispatch": wk,
+        "copy_kernel": cname,
+        "copy_bytes": copy_bytes,
+        "copy_fetch_kib": fc,
+        "copy_write_kib": wc,
+        "fetch_scale": f_scale,
+        "write_scale": w_scale,
+        "bytes_per_launch": fk * 1024 / f_scale + wk * 1024 / w_scale,
+    }
+    with open(out_path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
 
 
 if __name__ == "__main__":

@@ -113,7 +113,6 @@ __global__ __launch_bounds__(kBlock) void k_decide_sample(DecideSampleArgs a)
         d.u = a.uniforms[(long long)b * (k + 1) + k];
         d.pad = 0;
         a.desc[b] = d;
-        a.counters[b] = 0u;
         a.out_num_accepted[b] = j;
     }
 }

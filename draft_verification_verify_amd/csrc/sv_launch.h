@@ -72,7 +72,6 @@ struct DecideSampleArgs {
     float* out_p_x;                    // [B][k] or null
     float* out_q_x;                    // [B][k] or null
     SampleDesc* desc;                  // [B]
-    unsigned* counters;                // [B], zeroed here for the sampler
 };
 
 struct DecideGreedyArgs {
@@ -92,23 +91,29 @@ struct DecideCandArgs {
     int* out_best;
 };
 
+// The draw of each sequence (sv_sample.hip).  The sampled row (pair) is cut
+// into `nchunks` chunks of `vec_per_chunk` logical vectors (a multiple of
+// kBlock); k_sample_chunks writes every chunk's total weight, `chunks_per_block`
+// chunks per workgroup; k_sample_pick (one workgroup per sequence) locates
+// u * total among the chunk totals and resolves the token inside one chunk.
 struct SampleArgs {
     const void* target;
     long long t_stride;
     const void* draft;
     long long d_stride;
     int V, nvec;
-    int nchunks;                       // chunks per sampled row
+    int nchunks;
     int vec_per_chunk;
+    int chunks_per_block;
+    int blocks_per_seq;
     float c;
     const SampleDesc* desc;
     float* chunk_sums;                 // [B][nchunks]
-    unsigned* counters;                // [B]
     int* out_tokens;                   // [B][out_row]
     int out_row;
 };
 
-constexpr int kMaxChunks = 64;
+constexpr int kMaxChunks = 128;
 
 hipError_t launch_softmax_stats(int dt, bool vec, const StatsArgs& a, hipStream_t st);
 hipError_t launch_argmax_stats(int dt, bool vec, const StatsArgs& a, hipStream_t st);

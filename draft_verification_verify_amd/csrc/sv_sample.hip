@@ -7,42 +7,53 @@
 // in ascending index order: the smallest token whose cumulative weight
 // exceeds u times the total.
 //
-// Work split: the sampled row (pair) of each sequence is cut into `nchunks`
-// chunks, one workgroup each.  A workgroup streams its chunk once and writes
-// the chunk's total weight.  The last workgroup of a sequence to finish
-// (elected by an atomic counter) reads the chunk totals in chunk order, finds
-// the chunk where u * total is crossed, rescans only that chunk and resolves
-// the token with a workgroup prefix scan.  Chunk totals are recomputed by the
-// same code in the rescan, so the two passes agree bit for bit; every
-// reduction runs in a fixed order, so the result is deterministic.
+// Two kernels, so that no workgroup waits on another inside a launch:
+//  - k_sample_chunks streams the sampled row (pair) of every sequence once and
+//    writes the total weight of each chunk (a whole number of rounds of kBlock
+//    logical vectors), several rounds' loads in flight per thread;
+//  - k_sample_pick, one workgroup per sequence, accumulates the chunk totals
+//    in chunk order, finds the chunk where u * total is crossed, rescans only
+//    that chunk and resolves the token with a workgroup prefix scan.
+// A round's total is the same block scan in both kernels and a chunk's total
+// is the sequential sum of its rounds' totals, so the two kernels agree bit
+// for bit; every reduction runs in a fixed order, so draws are deterministic.
 
 #include "sv_device.h"
 
 namespace sv {
 
-// Weights of logical vector v: kind 0 the residual, otherwise p (unnormalised
-// by a common factor that cancels).  Padding elements get weight 0.
+// The weight arithmetic, shared by every pass: the residual
+// max(0, p - q) (kind 0) or p (otherwise), each exp2(z*c - off) with off the
+// row's log2 normaliser, so both are normalised probabilities.
+__device__ __forceinline__ float weight_of(float ez, float ey, int kind, float c, float off_t, float off_d)
+{
+    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(ez, c, -off_t));
+    if (kind != 0) return p;
+    const float q = __builtin_amdgcn_exp2f(__builtin_fmaf(ey, c, -off_d));
+    return fmaxf(p - q, 0.f);
+}
+
+// Weights of logical vector v (0 past the row's end).
 template <int DT, bool VEC>
 __device__ __forceinline__ void weights8(const char* zr, const char* yr, int v, int nfull, int V,
                                          int kind, float c, float off_t, float off_d, float* w)
 {
-    float ez[kVec];
+    float ez[kVec], ey[kVec];
     load8<DT, VEC>(zr, v, nfull, V, -INFINITY, ez);
-    if (kind == 0) {
-        float ey[kVec];
-        load8<DT, VEC>(yr, v, nfull, V, -INFINITY, ey);
+    if (kind == 0) load8<DT, VEC>(yr, v, nfull, V, -INFINITY, ey);
 #pragma unroll
-        for (int j = 0; j < kVec; ++j) {
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(ez[j], c, -off_t));
-            const float q = __builtin_amdgcn_exp2f(__builtin_fmaf(ey[j], c, -off_d));
-            w[j] = fmaxf(p - q, 0.f);
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < kVec; ++j) w[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(ez[j], c, -off_t));
-    }
+    for (int j = 0; j < kVec; ++j) w[j] = weight_of(ez[j], kind == 0 ? ey[j] : 0.f, kind, c, off_t, off_d);
 }
 
+__device__ __forceinline__ float sum8(const float* w)
+{
+    float ts = 0.f;
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) ts += w[j];
+    return ts;
+}
+
+// Total weight of chunk [c0, c1), one round (kBlock vectors) at a time.
 template <int DT, bool VEC>
 __device__ float chunk_total(const SampleArgs& a, const char* zr, const char* yr, int kind,
                              float off_t, float off_d, int c0, int c1, float* lds)
@@ -55,8 +66,7 @@ __device__ float chunk_total(const SampleArgs& a, const char* zr, const char* yr
         if (v < c1) {
             float w[kVec];
             weights8<DT, VEC>(zr, yr, v, nfull, a.V, kind, a.c, off_t, off_d, w);
-#pragma unroll
-            for (int j = 0; j < kVec; ++j) ts += w[j];
+            ts = sum8(w);
         }
         float ex, rt;
         block_scan(ts, &ex, &rt, lds);
@@ -140,39 +150,91 @@ __device__ int chunk_pick(const SampleArgs& a, const char* zr, const char* yr, i
     return last_tok;
 }
 
+constexpr int kRoundsInFlight = 4;
+
+// Chunk totals: workgroup (b, g) covers chunks [g * chunks_per_block, ...) of
+// sequence b's sampled row, kRoundsInFlight rounds per step with every load of
+// the step issued before any arithmetic.
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kBlock) void k_sample(SampleArgs a)
+__global__ __launch_bounds__(kBlock) void k_sample_chunks(SampleArgs a)
+{
+    __shared__ float lds[kWaves];
+    constexpr int ES = DT == DT_F32 ? 4 : 2;
+    const int b = blockIdx.x / a.blocks_per_seq;
+    const int g = blockIdx.x - b * a.blocks_per_seq;
+    const SampleDesc d = a.desc[b];
+    const int ch0 = g * a.chunks_per_block;
+    const int ch1 = min(ch0 + a.chunks_per_block, a.nchunks);
+    if (ch0 >= ch1) return;                       // uniform across the workgroup
+    const char* zr = row_ptr(a.target, d.t_row, a.t_stride, ES);
+    const char* yr = d.kind == 0 ? row_ptr(a.draft, d.d_row, a.d_stride, ES) : zr;
+    const int v0 = ch0 * a.vec_per_chunk;
+    const int v1 = min(ch1 * a.vec_per_chunk, a.nvec);
+    const int nfull = a.V >> 3;
+    const int vfull = min(v1, nfull);
+    const int kind = d.kind;
+
+    float acc = 0.f;
+    for (int r0 = v0; r0 < v1; r0 += kRoundsInFlight * kBlock) {
+        Raw<DT> rz[kRoundsInFlight], ry[kRoundsInFlight];
+#pragma unroll
+        for (int u = 0; u < kRoundsInFlight; ++u) {
+            const int v = r0 + u * kBlock + (int)threadIdx.x;
+            if (v < vfull) {
+                rz[u] = load_raw<DT, VEC>(zr, v);
+                if (kind == 0) ry[u] = load_raw<DT, VEC>(yr, v);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kRoundsInFlight; ++u) {
+            const int rr = r0 + u * kBlock;
+            if (rr >= v1) break;                  // uniform
+            const int v = rr + (int)threadIdx.x;
+            float ts = 0.f;
+            if (v < v1) {
+                float ez[kVec], ey[kVec], w[kVec];
+                if (v < nfull) {
+                    decode<DT>(rz[u], ez);
+                    if (kind == 0) decode<DT>(ry[u], ey);
+                } else {
+                    load_partial<DT>(zr, v, a.V - 8 * v, -INFINITY, ez);
+                    if (kind == 0) load_partial<DT>(yr, v, a.V - 8 * v, -INFINITY, ey);
+                }
+#pragma unroll
+                for (int j = 0; j < kVec; ++j)
+                    w[j] = weight_of(ez[j], kind == 0 ? ey[j] : 0.f, kind, a.c, d.off_t, d.off_d);
+                ts = sum8(w);
+            }
+            float ex, rt;
+            block_scan(ts, &ex, &rt, lds);
+            acc += rt;
+            const int ch = rr / a.vec_per_chunk;
+            const int cend = min((ch + 1) * a.vec_per_chunk, a.nvec);
+            if (rr + kBlock >= cend) {            // the chunk's last round
+                if (threadIdx.x == 0) a.chunk_sums[(long long)b * a.nchunks + ch] = acc;
+                acc = 0.f;
+            }
+        }
+    }
+}
+
+// The draw: one workgroup per sequence.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kBlock) void k_sample_pick(SampleArgs a)
 {
     __shared__ float lds[kWaves];
     __shared__ int ilds[kWaves];
     __shared__ float s_sums[kMaxChunks];
-    __shared__ int s_last, s_chunk, s_kind;
+    __shared__ int s_chunk;
     __shared__ float s_rem;
     constexpr int ES = DT == DT_F32 ? 4 : 2;
 
-    const int b = blockIdx.x / a.nchunks;
-    const int ch = blockIdx.x - b * a.nchunks;
+    const int b = blockIdx.x;
     const SampleDesc d = a.desc[b];
     const char* zr = row_ptr(a.target, d.t_row, a.t_stride, ES);
     const char* yr = d.kind == 0 ? row_ptr(a.draft, d.d_row, a.d_stride, ES) : zr;
-    const int c0 = ch * a.vec_per_chunk;
-    const int c1 = min(c0 + a.vec_per_chunk, a.nvec);
 
-    const float tot = chunk_total<DT, VEC>(a, zr, yr, d.kind, d.off_t, d.off_d, c0, c1, lds);
-    if (threadIdx.x == 0) {
-        __hip_atomic_store(&a.chunk_sums[(long long)b * a.nchunks + ch], tot, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-        const unsigned old = __hip_atomic_fetch_add(&a.counters[b], 1u, __ATOMIC_ACQ_REL,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-        s_last = old == (unsigned)(a.nchunks - 1);
-    }
-    __syncthreads();
-    if (!s_last) return;
-
-    // the last workgroup of sequence b: locate the chunk holding u * total
-    if (threadIdx.x < a.nchunks)
-        s_sums[threadIdx.x] = __hip_atomic_load(&a.chunk_sums[(long long)b * a.nchunks + threadIdx.x],
-                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((int)threadIdx.x < a.nchunks) s_sums[threadIdx.x] = a.chunk_sums[(long long)b * a.nchunks + threadIdx.x];
     __syncthreads();
     int kind = d.kind;
     double S = 0.0;
@@ -204,39 +266,42 @@ __global__ __launch_bounds__(kBlock) void k_sample(SampleArgs a)
             }
             pre = nx;
         }
-        if (cs < 0) {                  // rounding left no crossing: last positive chunk, its end
+        if (cs < 0) {                  // rounding left no crossing: the last positive chunk, its end
             cs = lastpos < 0 ? 0 : lastpos;
             rem = s_sums[cs];
         }
         s_chunk = cs;
         s_rem = fmaxf(rem, 0.f);
-        s_kind = kind;
     }
     __syncthreads();
     const int cs = s_chunk;
     const int e0 = cs * a.vec_per_chunk;
     const int e1 = min(e0 + a.vec_per_chunk, a.nvec);
-    int tok = chunk_pick<DT, VEC>(a, zr, yr, s_kind, d.off_t, d.off_d, e0, e1, s_rem, lds, ilds);
+    int tok = chunk_pick<DT, VEC>(a, zr, yr, kind, d.off_t, d.off_d, e0, e1, s_rem, lds, ilds);
     if (threadIdx.x == 0) {
         if (tok < 0 || tok >= a.V) tok = 0;    // only for inputs outside the contract
         a.out_tokens[(long long)b * a.out_row + d.out_pos] = tok;
     }
 }
 
-hipError_t launch_sample(int dt, bool vec, int B, const SampleArgs& a, hipStream_t st)
+template <int DT, bool VEC>
+static hipError_t launch_pair(int B, const SampleArgs& a, hipStream_t st)
 {
     void* args[] = {const_cast<SampleArgs*>(&a)};
-    const unsigned grid = (unsigned)((long long)B * a.nchunks);
-    const void* f;
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(k_sample_chunks<DT, VEC>),
+                                   dim3((unsigned)((long long)B * a.blocks_per_seq)), dim3(kBlock), args, 0, st);
+    if (e != hipSuccess) return e;
+    return hipLaunchKernel(reinterpret_cast<const void*>(k_sample_pick<DT, VEC>), dim3((unsigned)B),
+                           dim3(kBlock), args, 0, st);
+}
+
+hipError_t launch_sample(int dt, bool vec, int B, const SampleArgs& a, hipStream_t st)
+{
     switch (dt) {
-    case DT_F32: f = vec ? reinterpret_cast<const void*>(k_sample<DT_F32, true>)
-                         : reinterpret_cast<const void*>(k_sample<DT_F32, false>); break;
-    case DT_F16: f = vec ? reinterpret_cast<const void*>(k_sample<DT_F16, true>)
-                         : reinterpret_cast<const void*>(k_sample<DT_F16, false>); break;
-    default:     f = vec ? reinterpret_cast<const void*>(k_sample<DT_BF16, true>)
-                         : reinterpret_cast<const void*>(k_sample<DT_BF16, false>); break;
+    case DT_F32: return vec ? launch_pair<DT_F32, true>(B, a, st) : launch_pair<DT_F32, false>(B, a, st);
+    case DT_F16: return vec ? launch_pair<DT_F16, true>(B, a, st) : launch_pair<DT_F16, false>(B, a, st);
+    default:     return vec ? launch_pair<DT_BF16, true>(B, a, st) : launch_pair<DT_BF16, false>(B, a, st);
     }
-    return hipLaunchKernel(f, dim3(grid), dim3(kBlock), args, 0, st);
 }
 
 }  // namespace sv
