@@ -74,8 +74,8 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the verification step has no multi-GPU path in "
-              "this build (sequences shard over GPUs with no exchange); run with --gpus 1.",
+        print("bench.py measures one GPU only: the library has no multi-GPU path (sequences "
+              "shard over GPUs with no exchange, so one GPU's rate is its share); run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 
