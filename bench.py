@@ -63,6 +63,8 @@ def main():
                          "candidates: workload 4")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU oracle baseline budget (0 disables it)")
+    ap.add_argument("--profile-every", type=int, default=5,
+                    help="time the statistics kernel on every N-th timed call")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (scale for the rocprofv3 byte counters)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -140,7 +142,10 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    sv.profile_begin(args.steps)
+    # the statistics kernel is timed by events around it on every
+    # `profile_every`-th call of the timed region (each event pair adds a few
+    # microseconds of queue time to the call it brackets)
+    sv.profile_begin(args.steps, args.profile_every)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -194,6 +199,7 @@ def main():
             "kernel_ms_avg": k_avg_ms,
             "kernel_ms_min": min(kernel_ms),
             "kernel_ms_max": max(kernel_ms),
+            "kernel_launches_timed": len(kernel_ms),
             "algorithmic_bytes_per_launch": stats_bytes,
         },
     }

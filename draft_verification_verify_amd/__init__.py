@@ -52,7 +52,7 @@ def lib():
         L.spec_verify_sample.restype = I
         L.spec_verify_greedy_candidates.argtypes = [P, LL, P, I, I, I, I, I, I, P, P, P, P, SZ, P]
         L.spec_verify_greedy_candidates.restype = I
-        L.spec_verify_profile_begin.argtypes = [I]
+        L.spec_verify_profile_begin.argtypes = [I, I]
         L.spec_verify_profile_begin.restype = I
         L.spec_verify_profile_end.argtypes = [P, I]
         L.spec_verify_profile_end.restype = I
@@ -196,8 +196,9 @@ def greedy_candidates(target: torch.Tensor, cand_tokens: torch.Tensor, *, out_to
     return out_tokens, out_num_accepted, out_best
 
 
-def profile_begin(max_calls: int):
-    st = lib().spec_verify_profile_begin(int(max_calls))
+def profile_begin(max_calls: int, every: int = 1):
+    """Record the statistics kernel's duration on every `every`-th call."""
+    st = lib().spec_verify_profile_begin(int(max_calls), int(every))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_profile_begin")
 

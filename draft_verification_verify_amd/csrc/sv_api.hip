@@ -20,11 +20,12 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool dtype_ok(int dt) { return dt == SV_F32 || dt == SV_F16 || dt == SV_BF16; }
 
-// How a set of rows is split along the vocabulary: about 32768 workgroups
-// (16 resident rounds of 8 per CU on 256 CUs, so the last round's tail is
-// short), each streaming at least 1024 logical vectors (16 KiB of bf16) so the
-// 8-byte partial is negligible against the bytes read.  Measured on the
-// 512 x 33 x 128256 bf16 shape: 2 slices per row beat 1, 3, 4, 6 and 8.
+// How a set of rows is split along the vocabulary for the streaming pass
+// (512-thread workgroups): slices of about 4096 logical vectors (8 per
+// thread, 64 KiB of bf16), more slices when there are too few rows for 2048
+// workgroups, and never slices under 512 vectors (one per thread).  Measured
+// on the 512 x 33 x 128256 bf16 shape: 4 slices of 512 threads per row beat
+// 1-8 slices of 256 and 1024-thread workgroups.
 struct StatsPlan {
     int nvec;
     int splits;
@@ -35,13 +36,14 @@ StatsPlan plan_stats(long long rows, int V)
 {
     StatsPlan p;
     p.nvec = (V + kVec - 1) / kVec;
-    const long long target_units = 32768;
-    long long s = (target_units + rows - 1) / rows;
-    long long smax = p.nvec / 1024;
+    long long s = (p.nvec + 2048) / 4096;
+    const long long fill = (2048 + rows - 1) / rows;
+    if (s < fill) s = fill;
+    long long smax = p.nvec / 512;
     if (smax < 1) smax = 1;
     if (s > smax) s = smax;
-    if (s < 1) s = 1;
     if (s > 64) s = 64;
+    if (s < 1) s = 1;
     p.splits = (int)s;
     p.vec_per_split = (p.nvec + p.splits - 1) / p.splits;
     // drop splits that would be empty
@@ -114,20 +116,33 @@ bool vec_ok(const void* p, long long stride, int dt)
     return ((uintptr_t)p % 16 == 0) && ((stride * es) % 16 == 0);
 }
 
-// ---- measurement aid: per-call events around the statistics kernel ---------
+// ---- measurement aid: events around the statistics kernel of every
+// `every`-th call, up to max_calls recorded calls ----------------------------
 struct Profile {
     hipEvent_t* ev = nullptr;
     int max_calls = 0;
+    int every = 1;
     int count = 0;
+    long long seen = 0;
+    bool armed = false;
     bool on = false;
 };
 Profile g_prof;
 
-void prof_mark(hipStream_t st, bool begin)
+void prof_begin(hipStream_t st)
 {
-    if (!g_prof.on || g_prof.count >= g_prof.max_calls) return;
-    hipEventRecord(g_prof.ev[2 * g_prof.count + (begin ? 0 : 1)], st);
-    if (!begin) g_prof.count++;
+    if (!g_prof.on) return;
+    g_prof.armed = (g_prof.seen % g_prof.every == 0) && g_prof.count < g_prof.max_calls;
+    g_prof.seen++;
+    if (g_prof.armed) hipEventRecord(g_prof.ev[2 * g_prof.count], st);
+}
+
+void prof_end(hipStream_t st)
+{
+    if (!g_prof.armed) return;
+    hipEventRecord(g_prof.ev[2 * g_prof.count + 1], st);
+    g_prof.count++;
+    g_prof.armed = false;
 }
 
 }  // namespace
@@ -184,10 +199,10 @@ int spec_verify_greedy(const void* target_logits, long long target_row_stride,
     sa.vec_per_split = sp.vec_per_split;
     sa.c = 0.f;
     sa.partials = w.partials;
-    prof_mark(st, true);
+    prof_begin(st);
     if (launch_argmax_stats(dtype, vec_ok(target_logits, target_row_stride, dtype), sa, st) != hipSuccess)
         return SV_EHIP;
-    prof_mark(st, false);
+    prof_end(st);
 
     DecideGreedyArgs da;
     da.tokens = draft_tokens;
@@ -241,9 +256,9 @@ int spec_verify_sample(const void* target_logits, long long target_row_stride,
     sa.vec_per_split = sp.vec_per_split;
     sa.c = c;
     sa.partials = w.partials;
-    prof_mark(st, true);
+    prof_begin(st);
     if (launch_softmax_stats(dtype, vec, sa, st) != hipSuccess) return SV_EHIP;
-    prof_mark(st, false);
+    prof_end(st);
 
     DecideSampleArgs da;
     da.target = target_logits;
@@ -317,10 +332,10 @@ int spec_verify_greedy_candidates(const void* target_logits, long long row_strid
     sa.vec_per_split = sp.vec_per_split;
     sa.c = 0.f;
     sa.partials = w.partials;
-    prof_mark(st, true);
+    prof_begin(st);
     if (launch_argmax_stats(dtype, vec_ok(target_logits, row_stride, dtype), sa, st) != hipSuccess)
         return SV_EHIP;
-    prof_mark(st, false);
+    prof_end(st);
 
     DecideCandArgs da;
     da.cand = cand_tokens;
@@ -337,9 +352,9 @@ int spec_verify_greedy_candidates(const void* target_logits, long long row_strid
     return SV_OK;
 }
 
-int spec_verify_profile_begin(int max_calls)
+int spec_verify_profile_begin(int max_calls, int every)
 {
-    if (max_calls < 1 || g_prof.on) return SV_EINVAL;
+    if (max_calls < 1 || every < 1 || g_prof.on) return SV_EINVAL;
     g_prof.ev = static_cast<hipEvent_t*>(calloc((size_t)2 * max_calls, sizeof(hipEvent_t)));
     if (!g_prof.ev) return SV_EINVAL;
     for (int i = 0; i < 2 * max_calls; ++i) {
@@ -351,7 +366,10 @@ int spec_verify_profile_begin(int max_calls)
         }
     }
     g_prof.max_calls = max_calls;
+    g_prof.every = every;
     g_prof.count = 0;
+    g_prof.seen = 0;
+    g_prof.armed = false;
     g_prof.on = true;
     return SV_OK;
 }

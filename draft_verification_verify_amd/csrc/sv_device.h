@@ -138,8 +138,9 @@ __device__ __forceinline__ int wave_max_int(int v)
     return v;
 }
 
-// Block-wide reductions; `lds` holds at least kWaves entries.  Every thread
-// gets the result.
+// Block-wide reductions over a workgroup of NW wave64s; `lds` holds at least
+// NW entries.  Every thread gets the result.
+template <int NW = kWaves>
 __device__ __forceinline__ float block_max(float v, float* lds)
 {
     v = wave_max(v);
@@ -147,11 +148,12 @@ __device__ __forceinline__ float block_max(float v, float* lds)
     __syncthreads();
     float r = lds[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) r = fmaxf(r, lds[w]);
+    for (int w = 1; w < NW; ++w) r = fmaxf(r, lds[w]);
     __syncthreads();
     return r;
 }
 
+template <int NW = kWaves>
 __device__ __forceinline__ int block_min_int(int v, int* lds)
 {
     v = wave_min_int(v);
@@ -159,11 +161,12 @@ __device__ __forceinline__ int block_min_int(int v, int* lds)
     __syncthreads();
     int r = lds[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) r = min(r, lds[w]);
+    for (int w = 1; w < NW; ++w) r = min(r, lds[w]);
     __syncthreads();
     return r;
 }
 
+template <int NW = kWaves>
 __device__ __forceinline__ int block_max_int(int v, int* lds)
 {
     v = wave_max_int(v);
@@ -171,7 +174,7 @@ __device__ __forceinline__ int block_max_int(int v, int* lds)
     __syncthreads();
     int r = lds[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) r = max(r, lds[w]);
+    for (int w = 1; w < NW; ++w) r = max(r, lds[w]);
     __syncthreads();
     return r;
 }

@@ -9,6 +9,7 @@ namespace sv {
 
 constexpr int kBlock = 256;            // threads per workgroup (4 wave64s)
 constexpr int kWaves = kBlock / 64;
+constexpr int kStatsBlock = 512;       // the vocabulary-streaming pass: 8 wave64s
 constexpr int kVec = 8;                // elements per logical vector (16 B of bf16/fp16)
 
 enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };

@@ -3,9 +3,9 @@
 // Sampling needs, per row, the softmax normaliser of z / T (production blog,
 // "The acceptance rule": p and q at every position); greedy needs the argmax
 // (same section, greedy collapse).  Both are row reductions over V with no
-// contraction, bound by HBM bandwidth: each workgroup streams a contiguous
-// slice of one row with 16-byte non-temporal loads (four per thread in
-// flight), reduces it in registers and writes one 8-byte partial.  The
+// contraction, bound by HBM bandwidth: each 512-thread workgroup streams a
+// contiguous slice of one row with 16-byte non-temporal loads (four per
+// thread in flight), reduces it in registers and writes one 8-byte partial.  The
 // partials of a row's slices are merged in a fixed order by the decision
 // kernels.
 //
@@ -61,10 +61,13 @@ __device__ __forceinline__ const char* stats_row(const StatsArgs& a, int row, in
                : row_ptr(a.draft, row - a.n_target_rows, a.d_stride, es);
 }
 
+constexpr int kSB = kStatsBlock;
+constexpr int kSW = kStatsBlock / 64;
+
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kBlock) void k_softmax_stats(StatsArgs a)
+__global__ __launch_bounds__(kStatsBlock) void k_softmax_stats(StatsArgs a)
 {
-    __shared__ float lds_m[kWaves], lds_s[kWaves];
+    __shared__ float lds_m[kSW], lds_s[kSW];
     constexpr int ES = DT == DT_F32 ? 4 : 2;
     const int unit = blockIdx.x;
     const int row = unit / a.splits;
@@ -78,11 +81,11 @@ __global__ __launch_bounds__(kBlock) void k_softmax_stats(StatsArgs a)
 
     float m = -INFINITY, s = 0.f;
     int v = v0 + (int)threadIdx.x;
-    for (; v + 3 * kBlock < vend; v += 4 * kBlock) {
+    for (; v + 3 * kSB < vend; v += 4 * kSB) {
         Raw<DT> r0 = load_raw<DT, VEC>(rp, v);
-        Raw<DT> r1 = load_raw<DT, VEC>(rp, v + kBlock);
-        Raw<DT> r2 = load_raw<DT, VEC>(rp, v + 2 * kBlock);
-        Raw<DT> r3 = load_raw<DT, VEC>(rp, v + 3 * kBlock);
+        Raw<DT> r1 = load_raw<DT, VEC>(rp, v + kSB);
+        Raw<DT> r2 = load_raw<DT, VEC>(rp, v + 2 * kSB);
+        Raw<DT> r3 = load_raw<DT, VEC>(rp, v + 3 * kSB);
         float e[4 * kVec];
         decode<DT>(r0, e);
         decode<DT>(r1, e + 8);
@@ -90,7 +93,7 @@ __global__ __launch_bounds__(kBlock) void k_softmax_stats(StatsArgs a)
         decode<DT>(r3, e + 24);
         soft_update<4 * kVec>(e, m, s, c);
     }
-    for (; v < vend; v += kBlock) {
+    for (; v < vend; v += kSB) {
         Raw<DT> r0 = load_raw<DT, VEC>(rp, v);
         float e[kVec];
         decode<DT>(r0, e);
@@ -116,7 +119,7 @@ __global__ __launch_bounds__(kBlock) void k_softmax_stats(StatsArgs a)
     __syncthreads();
     if (threadIdx.x == 0) {
         float M = lds_m[0], S = lds_s[0];
-        for (int i = 1; i < kWaves; ++i) soft_merge(M, S, lds_m[i], lds_s[i], c);
+        for (int i = 1; i < kSW; ++i) soft_merge(M, S, lds_m[i], lds_s[i], c);
         reinterpret_cast<SoftPartial*>(a.partials)[unit] = SoftPartial{M, S};
     }
 }
@@ -128,10 +131,10 @@ __global__ __launch_bounds__(kBlock) void k_softmax_stats(StatsArgs a)
 // threads holding M reload that one group to locate their first index of M;
 // the block takes the smallest.  -0.0 and +0.0 compare equal throughout.
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kBlock) void k_argmax_stats(StatsArgs a)
+__global__ __launch_bounds__(kStatsBlock) void k_argmax_stats(StatsArgs a)
 {
-    __shared__ float lds_f[kWaves];
-    __shared__ int lds_i[kWaves];
+    __shared__ float lds_f[kSW];
+    __shared__ int lds_i[kSW];
     constexpr int ES = DT == DT_F32 ? 4 : 2;
     const int unit = blockIdx.x;
     const int row = unit / a.splits;
@@ -145,11 +148,11 @@ __global__ __launch_bounds__(kBlock) void k_argmax_stats(StatsArgs a)
     float bv = -INFINITY;
     int bvec = -1, bcnt = 0;
     int v = v0 + (int)threadIdx.x;
-    for (; v + 3 * kBlock < vend; v += 4 * kBlock) {
+    for (; v + 3 * kSB < vend; v += 4 * kSB) {
         Raw<DT> r0 = load_raw<DT, VEC>(rp, v);
-        Raw<DT> r1 = load_raw<DT, VEC>(rp, v + kBlock);
-        Raw<DT> r2 = load_raw<DT, VEC>(rp, v + 2 * kBlock);
-        Raw<DT> r3 = load_raw<DT, VEC>(rp, v + 3 * kBlock);
+        Raw<DT> r1 = load_raw<DT, VEC>(rp, v + kSB);
+        Raw<DT> r2 = load_raw<DT, VEC>(rp, v + 2 * kSB);
+        Raw<DT> r3 = load_raw<DT, VEC>(rp, v + 3 * kSB);
         float e[4 * kVec];
         decode<DT>(r0, e);
         decode<DT>(r1, e + 8);
@@ -167,7 +170,7 @@ __global__ __launch_bounds__(kBlock) void k_argmax_stats(StatsArgs a)
         bvec = up ? v : bvec;
         bcnt = up ? 4 : bcnt;
     }
-    for (; v < vend; v += kBlock) {
+    for (; v < vend; v += kSB) {
         Raw<DT> r0 = load_raw<DT, VEC>(rp, v);
         float e[kVec];
         decode<DT>(r0, e);
@@ -192,11 +195,11 @@ __global__ __launch_bounds__(kBlock) void k_argmax_stats(StatsArgs a)
         }
     }
 
-    const float M = block_max(bv, lds_f);
+    const float M = block_max<kSW>(bv, lds_f);
     int idx = INT32_MAX;
     if (bv == M && M > -INFINITY) {
         for (int j = 0; j < bcnt && idx == INT32_MAX; ++j) {
-            const int vv = bvec + j * kBlock;
+            const int vv = bvec + j * kSB;
             float e[kVec];
             load8<DT, VEC>(rp, vv, nfull, a.V, -INFINITY, e);
 #pragma unroll
@@ -204,7 +207,7 @@ __global__ __launch_bounds__(kBlock) void k_argmax_stats(StatsArgs a)
                 if (e[t] == M) idx = 8 * vv + t;
         }
     }
-    idx = block_min_int(idx, lds_i);
+    idx = block_min_int<kSW>(idx, lds_i);
     if (threadIdx.x == 0) reinterpret_cast<ArgPartial*>(a.partials)[unit] = ArgPartial{M, idx};
 }
 
@@ -213,7 +216,7 @@ static hipError_t launch_rows(K kernel, const StatsArgs& a, hipStream_t st)
 {
     void* args[] = {const_cast<StatsArgs*>(&a)};
     const unsigned grid = (unsigned)((long long)a.n_rows * a.splits);
-    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(grid), dim3(kBlock), args, 0, st);
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(grid), dim3(kStatsBlock), args, 0, st);
 }
 
 hipError_t launch_softmax_stats(int dt, bool vec, const StatsArgs& a, hipStream_t st)

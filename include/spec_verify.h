@@ -126,7 +126,7 @@ int spec_verify_sample(const void* target_logits, long long target_row_stride,
  *                 R = L (no row after the last token: a fully accepted candidate
  *                 commits L tokens) or R = L+1 (the last row gives one more
  *                 greedy token).
- *   cand_tokens   DEVICE [B][C][L] int32; 1 <= C, 1 <= L, C*L <= 64
+ *   cand_tokens   DEVICE [B][C][L] int32; 1 <= C, 1 <= L <= 63, C*L <= 64
  *   out_tokens         DEVICE [B][L+1] int32, committed tokens then -1
  *   out_num_accepted   DEVICE [B] int32: accepted length A of the chosen candidate
  *   out_best_candidate DEVICE [B] int32: the chosen candidate c*
@@ -138,13 +138,16 @@ int spec_verify_greedy_candidates(const void* target_logits, long long row_strid
                                   void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* Measurement aid (not thread-safe; for a single profiling thread).  While
- * enabled, each of the next `max_calls` verification calls records a pair of
- * HIP events on its stream around its vocabulary-streaming statistics kernel
- * (the kernel that reads every logit).  spec_verify_profile_end waits for the
- * recorded events, writes up to `max_out` durations in milliseconds, frees the
- * events, disables recording and returns the number of recorded calls (or a
- * negative value on a HIP error).  spec_verify_profile_begin returns a status. */
-int spec_verify_profile_begin(int max_calls);
+ * enabled, every `every`-th verification call (the first, then every
+ * `every` calls), up to `max_calls` of them, records a pair of HIP events on
+ * its stream around its vocabulary-streaming statistics kernel (the kernel
+ * that reads every logit).  Each pair costs a few microseconds of queue time.
+ * spec_verify_profile_end waits for the recorded events, writes up to
+ * `max_out` durations in milliseconds, frees the events, disables recording
+ * and returns the number of recorded calls (or a negative value: -1 if not
+ * enabled, -2 on a HIP error).  spec_verify_profile_begin returns a status
+ * (SV_EINVAL for max_calls < 1, every < 1 or when already enabled). */
+int spec_verify_profile_begin(int max_calls, int every);
 int spec_verify_profile_end(float* out_ms, int max_out);
 
 #ifdef __cplusplus

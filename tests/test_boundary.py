@@ -166,7 +166,8 @@ def test_candidates_rejects_bad_arguments(sv):
 
 def test_profile_api_without_calls(sv):
     L = sv.lib()
-    assert L.spec_verify_profile_begin(0) == sv.SV_EINVAL
+    assert L.spec_verify_profile_begin(0, 1) == sv.SV_EINVAL
+    assert L.spec_verify_profile_begin(4, 0) == sv.SV_EINVAL
     assert L.spec_verify_profile_end(None, 0) == -1      # not enabled
 
 

@@ -354,3 +354,9 @@ def test_side_stream_and_profile(sv):
         assert np.array_equal(a, npi(b))
     bad, _, _ = parity.check_greedy(f32(w.target), npi(w.tokens), npi(out2[0]), npi(out2[1]))
     assert not bad
+    # every third call, at most two of them
+    sv.profile_begin(2, 3)
+    for _ in range(9):
+        sv.greedy(w.target, w.tokens)
+    ms = sv.profile_end()
+    assert len(ms) == 2 and all(m > 0 for m in ms)
