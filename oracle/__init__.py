@@ -75,8 +75,12 @@ def lib():
         L.oracle_greedy_candidates.argtypes = [P, LL, P, I, I, I, I, I, P, P, P]
         L.oracle_token_probs_seq.argtypes = [P, LL, P, LL, P, D, I, I, P, P]
         L.oracle_draw_interval.argtypes = [P, P, D, I, I, P, P, P]
+        L.oracle_sample_lenient.argtypes = [P, LL, P, LL, P, P, D, D, I, I, I, P, P, P]
+        L.oracle_greedy_matches.argtypes = [P, LL, P, I, I, I, P, P, P]
+        L.oracle_row_argmax.argtypes = [P, LL, LL, I, P]
         for f in ("oracle_greedy", "oracle_sample", "oracle_greedy_candidates",
-                  "oracle_token_probs_seq", "oracle_trace_size", "oracle_draw_interval"):
+                  "oracle_token_probs_seq", "oracle_trace_size", "oracle_draw_interval",
+                  "oracle_sample_lenient", "oracle_greedy_matches", "oracle_row_argmax"):
             getattr(L, f).restype = I
         if L.oracle_trace_size() != ctypes.sizeof(Trace):
             raise RuntimeError("oracle_trace layout mismatch")
@@ -135,6 +139,54 @@ def sample(target, draft, draft_tokens, uniforms, temperature, mutation=MUT_NONE
     if traces:
         return out, na, list(tr)
     return out, na
+
+
+def sample_lenient(target, draft, draft_tokens, uniforms, temperature, lenience, traces=False):
+    """The sampling rule with lenience l >= 1 (l = 1 is `sample`)."""
+    z = _f32(target)
+    y = _f32(draft)
+    x = _i32(draft_tokens)
+    u = _f32(uniforms)
+    B, k1, V = z.shape
+    k = k1 - 1
+    out = np.full((B, k + 1), -1, np.int32)
+    na = np.zeros(B, np.int32)
+    tr = (Trace * B)() if traces else None
+    rc = lib().oracle_sample_lenient(_ptr(z), V, _ptr(y), V, _ptr(x), _ptr(u), float(temperature),
+                                     float(lenience), B, k, V, _ptr(out), _ptr(na),
+                                     ctypes.cast(tr, ctypes.c_void_p) if traces else None)
+    if rc:
+        raise RuntimeError(f"oracle_sample_lenient failed: {rc}")
+    if traces:
+        return out, na, list(tr)
+    return out, na
+
+
+def greedy_matches(target, draft_tokens):
+    """target [B, k+1, V], tokens [B, k] -> (v [B, k+1], match mask [B] uint64, #Match [B])."""
+    z = _f32(target)
+    x = _i32(draft_tokens)
+    B, k1, V = z.shape
+    k = k1 - 1
+    v = np.zeros((B, k + 1), np.int32)
+    mask = np.zeros(B, np.uint64)
+    cnt = np.zeros(B, np.int32)
+    rc = lib().oracle_greedy_matches(_ptr(z), V, _ptr(x), B, k, V, _ptr(v), _ptr(mask), _ptr(cnt))
+    if rc:
+        raise RuntimeError(f"oracle_greedy_matches failed: {rc}")
+    return v, mask, cnt
+
+
+def row_argmax(rows):
+    """rows [..., V] -> argmax of every row, shape [...]."""
+    z = _f32(rows)
+    V = z.shape[-1]
+    n = z.size // V
+    out = np.zeros(n, np.int32)
+    rc = lib().oracle_row_argmax(_ptr(z), V, n, V, _ptr(out))
+    if rc:
+        raise RuntimeError(f"oracle_row_argmax failed: {rc}")
+    return out.reshape(z.shape[:-1])
 
 
 def token_probs(target_seq, draft_seq, draft_tokens_seq, temperature):

@@ -117,12 +117,13 @@ int oracle_greedy_seq(const float* target, long long row_stride, const int* draf
  * replacement from the residual proportional to max(0, p - q) and stop; if
  * all k are kept, sample one bonus token from p at position k+1.           */
 static int sample_seq(const float* target, long long ts, const float* draft, long long ds,
-                      const int* x, const float* u, double T, int k, int V,
+                      const int* x, const float* u, double T, double l, int k, int V,
                       int* out_tokens, int* out_num_accepted, oracle_trace* tr, int mut)
 {
     if (!target || !draft || !x || !u || !out_tokens || !out_num_accepted) return -1;
     if (k < 1 || k > ORACLE_MAX_K || V < 1 || ts < V || ds < V) return -1;
     if (!(T > 0.0) || !isfinite(T)) return -1;
+    if (!(l >= 1.0) || !isfinite(l)) return -1;
 
     oracle_trace local;
     if (!tr) tr = &local;
@@ -152,11 +153,11 @@ static int sample_seq(const float* target, long long ts, const float* draft, lon
         } else if (mut == ORACLE_MUT_RATIO_INVERTED) {
             ratio = (px <= qx) ? 1.0 : qx / px;
             accept = (double)u[i] < ratio;
-        } else if (qx <= px) {
-            ratio = 1.0;                  /* min(1, p/q) = 1, q = 0 included */
+        } else if (qx <= l * px) {
+            ratio = 1.0;                  /* min(1, l p/q) = 1, q = 0 included */
             accept = 1;
         } else {
-            ratio = px / qx;
+            ratio = l * px / qx;
             accept = (double)u[i] < ratio;
         }
         tr->ratio[i] = ratio;
@@ -231,7 +232,7 @@ int oracle_sample_seq(const float* target, long long target_row_stride,
                       oracle_trace* trace)
 {
     return sample_seq(target, target_row_stride, draft, draft_row_stride, draft_tokens,
-                      uniforms, temperature, k, V, out_tokens, out_num_accepted, trace,
+                      uniforms, temperature, 1.0, k, V, out_tokens, out_num_accepted, trace,
                       ORACLE_MUT_NONE);
 }
 
@@ -242,7 +243,7 @@ int oracle_sample_seq_mutant(const float* target, long long target_row_stride,
                              oracle_trace* trace, int mutation)
 {
     return sample_seq(target, target_row_stride, draft, draft_row_stride, draft_tokens,
-                      uniforms, temperature, k, V, out_tokens, out_num_accepted, trace,
+                      uniforms, temperature, 1.0, k, V, out_tokens, out_num_accepted, trace,
                       mutation);
 }
 
@@ -374,11 +375,64 @@ int oracle_sample(const float* target, long long ts, const float* draft, long lo
     for (int b = 0; b < B; ++b) {
         int rc = sample_seq(target + (long long)b * (k + 1) * ts, ts,
                             draft + (long long)b * k * ds, ds,
-                            x + (long long)b * k, u + (long long)b * (k + 1), T, k, V,
+                            x + (long long)b * k, u + (long long)b * (k + 1), T, 1.0, k, V,
                             out_tokens + (long long)b * (k + 1), out_num_accepted + b,
                             traces ? traces + b : NULL, mutation);
         if (rc) return rc;
     }
+    return 0;
+}
+
+/* Lenience l (Cascade Speculative Drafting, "The Vertical Cascade", review
+ * function): the acceptance test becomes q <= l p, else reject with
+ * probability 1 - l p/q; the residual is unchanged. */
+int oracle_sample_lenient(const float* target, long long ts, const float* draft, long long ds,
+                          const int* x, const float* u, double T, double l, int B, int k, int V,
+                          int* out_tokens, int* out_num_accepted, oracle_trace* traces)
+{
+    if (B < 0) return -1;
+    for (int b = 0; b < B; ++b) {
+        int rc = sample_seq(target + (long long)b * (k + 1) * ts, ts,
+                            draft + (long long)b * k * ds, ds,
+                            x + (long long)b * k, u + (long long)b * (k + 1), T, l, k, V,
+                            out_tokens + (long long)b * (k + 1), out_num_accepted + b,
+                            traces ? traces + b : NULL, ORACLE_MUT_NONE);
+        if (rc) return rc;
+    }
+    return 0;
+}
+
+/* Ouroboros section 3.4.4, Eq. 10: #Match counts the positions where the
+ * draft token equals the target's verification token v_i (its argmax under
+ * greedy decoding), whether or not they lie in the accepted prefix. */
+int oracle_greedy_matches(const float* target, long long row_stride, const int* x,
+                          int B, int k, int V, int* out_v, unsigned long long* out_mask,
+                          int* out_num_match)
+{
+    if (!target || !x || !out_v || !out_mask || !out_num_match) return -1;
+    if (B < 0 || k < 1 || k > ORACLE_MAX_K || V < 1 || row_stride < V) return -1;
+    for (int b = 0; b < B; ++b) {
+        const float* seq = target + (long long)b * (k + 1) * row_stride;
+        unsigned long long mask = 0;
+        int count = 0;
+        for (int i = 0; i <= k; ++i) {
+            int v = argmax_row(seq + (long long)i * row_stride, V);
+            out_v[(long long)b * (k + 1) + i] = v;
+            if (i < k && x[(long long)b * k + i] == v) {
+                mask |= 1ull << i;
+                count++;
+            }
+        }
+        out_mask[b] = mask;
+        out_num_match[b] = count;
+    }
+    return 0;
+}
+
+int oracle_row_argmax(const float* rows, long long row_stride, long long n_rows, int V, int* out)
+{
+    if (!rows || !out || n_rows < 0 || V < 1 || row_stride < V) return -1;
+    for (long long r = 0; r < n_rows; ++r) out[r] = argmax_row(rows + r * row_stride, V);
     return 0;
 }
 

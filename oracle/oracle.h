@@ -105,6 +105,28 @@ int oracle_sample_seq_mutant(const float* target, long long target_row_stride,
                              int k, int V, int* out_tokens, int* out_num_accepted,
                              oracle_trace* trace, int mutation);
 
+/* Sampling rule with lenience l >= 1 (Cascade Speculative Drafting, "The
+ * Vertical Cascade", the review function): accept if q(x) <= l p(x), else
+ * reject with probability 1 - l p(x)/q(x), i.e. accept iff u < min(1, l p/q);
+ * the residual stays max(0, p - q).  l = 1 is oracle_sample_seq. */
+int oracle_sample_lenient(const float* target, long long target_row_stride,
+                          const float* draft, long long draft_row_stride,
+                          const int* draft_tokens, const float* uniforms, double temperature,
+                          double lenience, int B, int k, int V, int* out_tokens,
+                          int* out_num_accepted, oracle_trace* traces);
+
+/* Verification by-products of the greedy pass (Ouroboros section 3.4.4,
+ * Eq. 10): v_i = argmax of target row i for i <= k (the target's own token at
+ * every position, accepted or not), bit i of the match mask = [x_i == v_i]
+ * for i < k, and #Match = the number of set bits. */
+int oracle_greedy_matches(const float* target, long long row_stride, const int* draft_tokens,
+                          int B, int k, int V, int* out_v, unsigned long long* out_mask,
+                          int* out_num_match);
+
+/* The argmax of every row (candidates: the verification token of every
+ * candidate position, used to correct unused candidates). */
+int oracle_row_argmax(const float* rows, long long row_stride, long long n_rows, int V, int* out);
+
 /* p_i(x_i) and q_i(x_i) for every draft position i < k (0 for an invalid x_i). */
 int oracle_token_probs_seq(const float* target, long long target_row_stride,
                            const float* draft, long long draft_row_stride,

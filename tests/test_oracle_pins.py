@@ -133,7 +133,8 @@ GRID = 1 << 24
 class Probe:
     """Calls the oracle on one fixed set of rows with many uniform vectors."""
 
-    def __init__(self, P, Q, T, mutation):
+    def __init__(self, P, Q, T, mutation, lenience=None):
+        self.lenience = lenience
         self.k = Q.shape[0]
         V = P.shape[1]
         with np.errstate(divide="ignore"):
@@ -148,6 +149,8 @@ class Probe:
         z = np.broadcast_to(self.z, (n,) + self.z.shape).copy()
         y = np.broadcast_to(self.y, (n,) + self.y.shape).copy()
         xx = np.broadcast_to(np.asarray(x, np.int32), (n, self.k)).copy()
+        if self.lenience is not None:
+            return oracle.sample_lenient(z, y, xx, U.astype(np.float32), self.T, self.lenience)
         return oracle.sample(z, y, xx, U.astype(np.float32), self.T, mutation=self.mut)
 
     def measure(self, x, base_u, coord, pred):
@@ -169,11 +172,11 @@ class Probe:
         return lo / GRID
 
 
-def committed_law(P, Q, T, mutation=oracle.MUT_NONE):
+def committed_law(P, Q, T, mutation=oracle.MUT_NONE, lenience=None):
     """Exact law (on the uniform grid) of the token committed at each position i,
     given that the round reaches i, and the acceptance probability at i."""
     k, V = Q.shape
-    pr = Probe(P, Q, T, mutation)
+    pr = Probe(P, Q, T, mutation, lenience)
     # a draft that is surely accepted with u = 0 (p > 0 there) for the prefix
     safe = [int(np.argmax(np.minimum(P[i], Q[i]) + 1e-3 * (P[i] > 0))) for i in range(k)]
     laws, acc = [], []
@@ -498,3 +501,78 @@ def test_candidates_selection_properties():
                 assert out[b, L] == ref[b, cs, L]
             else:
                 assert out[b, L] == -1
+
+
+# ---------------------------------------------------------------------------
+# Lenience (Cascade Speculative Drafting, "The Vertical Cascade": accept if
+# q <= l p, else reject with probability 1 - l p / q; residual max(0, p - q))
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("lenience", [1.5, 4.0])
+def test_v8_lenient_law(lenience):
+    """With x ~ q kept w.p. min(1, l p/q), a position accepts with probability
+    sum_v min(q_v, l p_v), and commits v with probability
+    min(q_v, l p_v) + (1 - sum_w min(q_w, l p_w)) r_v / sum r, r = max(0, p - q)."""
+    name, P, Q, T = v8_cases()[1]
+    laws, acc = committed_law(P, Q, T, lenience=lenience)
+    k = Q.shape[0]
+    for i in range(k):
+        a = np.minimum(Q[i], lenience * P[i])
+        r = np.maximum(P[i] - Q[i], 0.0)
+        expect = a + (1 - a.sum()) * r / r.sum()
+        np.testing.assert_allclose(laws[i], expect, atol=3e-6, err_msg=f"position {i}")
+        assert acc[i] == pytest.approx(a.sum(), abs=3e-6)
+    np.testing.assert_allclose(laws[k], P[k], atol=3e-6)
+    # lenience moves mass toward q: the law is no longer p
+    assert np.abs(laws[:k] - P[:k]).max() > 1e-2
+
+
+def test_lenience_one_is_the_rule_and_large_lenience_accepts_all():
+    rng = np.random.default_rng(13)
+    n, k, V = 400, 5, 64
+    z = rng.normal(0, 1.5, (n, k + 1, V)).astype(np.float32)
+    y = (z[:, :k] + rng.normal(0, 1.5, (n, k, V))).astype(np.float32)
+    x = rng.integers(0, V, (n, k)).astype(np.int32)
+    u = u24(rng, (n, k + 1))
+    t1, n1 = oracle.sample(z, y, x, u, 0.9)
+    t2, n2 = oracle.sample_lenient(z, y, x, u, 0.9, 1.0)
+    np.testing.assert_array_equal(t1, t2)
+    np.testing.assert_array_equal(n1, n2)
+    # l = 1e30: every finite-logit draft passes q <= l p
+    t3, n3 = oracle.sample_lenient(z, y, x, u, 0.9, 1e30)
+    assert (n3 == k).all()
+    np.testing.assert_array_equal(t3[:, :k], x)
+
+
+# ---------------------------------------------------------------------------
+# #Match (Ouroboros section 3.4.4, Eq. 10)
+# ---------------------------------------------------------------------------
+def test_greedy_matches_definition_and_bound():
+    """v_i is the first-occurrence argmax of row i (numpy, independently of the
+    oracle), the mask marks x_i == v_i, #Match is its popcount, and #Match is at
+    least the accepted length A, with equality when the rejected tail has no
+    match (the page: #Match is always at least A)."""
+    rng = np.random.default_rng(14)
+    n, k, V = 3000, 7, 30
+    z = rng.integers(-4, 4, (n, k + 1, V)).astype(np.float32)
+    ref = np.argmax(z, axis=2)
+    x = np.where(rng.random((n, k)) < 0.6, ref[:, :k], rng.integers(0, V, (n, k))).astype(np.int32)
+    v, mask, cnt = oracle.greedy_matches(z, x)
+    np.testing.assert_array_equal(v, ref)
+    bits = (x == ref[:, :k])
+    want_mask = (bits * (1 << np.arange(k))).sum(axis=1).astype(np.uint64)
+    np.testing.assert_array_equal(mask, want_mask)
+    np.testing.assert_array_equal(cnt, bits.sum(axis=1))
+    _, A = oracle.greedy(z, x)
+    assert (cnt >= A).all()
+    tail_match = np.array([bits[b, A[b] + 1:].any() if A[b] < k else False for b in range(n)])
+    np.testing.assert_array_equal(cnt == A, ~tail_match)
+    # the committed tokens are v up to and including the first mismatch
+    toks, _ = oracle.greedy(z, x)
+    for b in range(0, n, 97):
+        np.testing.assert_array_equal(toks[b, : A[b] + 1], v[b, : A[b] + 1])
+
+
+def test_row_argmax_matches_numpy():
+    rng = np.random.default_rng(15)
+    z = rng.integers(-3, 3, (50, 7, 41)).astype(np.float32)
+    np.testing.assert_array_equal(oracle.row_argmax(z), np.argmax(z, axis=2))
