@@ -58,9 +58,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--mode", default="sample", choices=["sample", "greedy", "candidates"],
-                    help="sample: workload 5 (the benchmark line); greedy: workload 5 greedy; "
-                         "candidates: workload 4")
+    ap.add_argument("--mode", default="sample",
+                    choices=["sample", "greedy", "candidates", "greedy_ext", "lenient", "candidates_ext"],
+                    help="sample: workload 5 (the benchmark line); greedy / greedy_ext: workload 5 "
+                         "greedy (ext: with the #Match by-products); lenient: workload 5 sampling "
+                         "with --lenience; candidates / candidates_ext: workload 4")
+    ap.add_argument("--lenience", type=float, default=2.0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU oracle baseline budget (0 disables it)")
     ap.add_argument("--profile-every", type=int, default=5,
@@ -88,7 +91,7 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    cid = 4 if args.mode == "candidates" else 5
+    cid = 4 if args.mode.startswith("candidates") else 5
     t0 = time.perf_counter()
     w = synthetic.generate(cid, device=dev)
     torch.cuda.synchronize()
@@ -96,7 +99,7 @@ def main():
     cfg = w.cfg
     es = w.target.element_size()
 
-    if args.mode == "candidates":
+    if args.mode.startswith("candidates"):
         B, C, R, V = w.target.shape
         L = w.tokens.shape[2]
         rows = B * C * R
@@ -104,11 +107,15 @@ def main():
                torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev))
         ws = torch.empty(sv.workspace_bytes(B, C * R, V, w.target.dtype), dtype=torch.uint8, device=dev)
 
-        def step():
-            sv.greedy_candidates(w.target, w.tokens, out_tokens=out[0], out_num_accepted=out[1],
-                                 out_best=out[2], workspace=ws)
+        if args.mode == "candidates":
+            def step():
+                sv.greedy_candidates(w.target, w.tokens, out_tokens=out[0], out_num_accepted=out[1],
+                                     out_best=out[2], workspace=ws)
+        else:
+            def step():
+                sv.greedy_candidates_ext(w.target, w.tokens, workspace=ws)
         stats_rows = rows
-        workload = f"spec_verify_greedy_candidates B={B} C={C} L={L} R={R} V={V} bf16"
+        workload = f"spec_verify_greedy_{args.mode} B={B} C={C} L={L} R={R} V={V} bf16"
     else:
         B, k1, V = w.target.shape
         k = k1 - 1
@@ -124,6 +131,23 @@ def main():
                           out_num_accepted=out_n, workspace=ws)
             stats_rows = B * (2 * k + 1)
             workload = f"spec_verify_sample B={B} k={k} V={V} bf16 T={w.T}"
+        elif args.mode == "lenient":
+            ws = torch.empty(sv.workspace_bytes(B, 2 * k + 1, V, w.target.dtype), dtype=torch.uint8,
+                             device=dev)
+
+            def step():
+                sv.sample_lenient(w.target, w.draft, w.tokens, w.uniforms, w.T, args.lenience,
+                                  workspace=ws)
+            stats_rows = B * (2 * k + 1)
+            workload = f"spec_verify_sample_lenient B={B} k={k} V={V} bf16 T={w.T} l={args.lenience}"
+        elif args.mode == "greedy_ext":
+            ws = torch.empty(sv.workspace_bytes(B, k + 1, V, w.target.dtype), dtype=torch.uint8,
+                             device=dev)
+
+            def step():
+                sv.greedy_ext(w.target, w.tokens, workspace=ws)
+            stats_rows = rows
+            workload = f"spec_verify_greedy_ext B={B} k={k} V={V} bf16"
         else:
             ws = torch.empty(sv.workspace_bytes(B, k + 1, V, w.target.dtype), dtype=torch.uint8,
                              device=dev)
@@ -189,7 +213,7 @@ def main():
             "device": torch.cuda.get_device_name(0),
         },
         "roofline": {
-            "kernel": "k_softmax_stats" if args.mode == "sample" else "k_argmax_stats",
+            "kernel": "k_softmax_stats" if args.mode in ("sample", "lenient") else "k_argmax_stats",
             "bound": "hbm",
             "achieved": achieved,
             "peak": PEAK_HBM_GBS,

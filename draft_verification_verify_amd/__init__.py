@@ -52,6 +52,12 @@ def lib():
         L.spec_verify_sample.restype = I
         L.spec_verify_greedy_candidates.argtypes = [P, LL, P, I, I, I, I, I, I, P, P, P, P, SZ, P]
         L.spec_verify_greedy_candidates.restype = I
+        L.spec_verify_greedy_ext.argtypes = [P, LL, P, I, I, I, I, P, P, P, P, P, P, SZ, P]
+        L.spec_verify_greedy_ext.restype = I
+        L.spec_verify_sample_lenient.argtypes = [P, LL, P, LL, P, P, F, F, I, I, I, I, P, P, P, P, P, SZ, P]
+        L.spec_verify_sample_lenient.restype = I
+        L.spec_verify_greedy_candidates_ext.argtypes = [P, LL, P, I, I, I, I, I, I, P, P, P, P, P, SZ, P]
+        L.spec_verify_greedy_candidates_ext.restype = I
         L.spec_verify_profile_begin.argtypes = [I, I]
         L.spec_verify_profile_begin.restype = I
         L.spec_verify_profile_end.argtypes = [P, I]
@@ -63,6 +69,7 @@ def lib():
 EXPORTED = (
     "spec_verify_version", "spec_verify_status_string", "spec_verify_workspace_bytes",
     "spec_verify_greedy", "spec_verify_sample", "spec_verify_greedy_candidates",
+    "spec_verify_greedy_ext", "spec_verify_sample_lenient", "spec_verify_greedy_candidates_ext",
     "spec_verify_profile_begin", "spec_verify_profile_end",
 )
 
@@ -171,6 +178,73 @@ def sample(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor
     if return_probs:
         return out_tokens, out_num_accepted, out_p_x, out_q_x
     return out_tokens, out_num_accepted
+
+
+def greedy_ext(target: torch.Tensor, draft_tokens: torch.Tensor, *, workspace=None, stream=None):
+    """Greedy verification plus its phrase-harvesting by-products.  Returns
+    (tokens [B, k+1], num_accepted [B], target_argmax [B, k+1],
+    match_mask [B] (int64 bit pattern of the uint64 mask), num_match [B])."""
+    B, k1, V = target.shape
+    k = k1 - 1
+    dev = target.device
+    out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
+    out_na = torch.empty((B,), dtype=torch.int32, device=dev)
+    out_v = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
+    out_mask = torch.empty((B,), dtype=torch.int64, device=dev)
+    out_cnt = torch.empty((B,), dtype=torch.int32, device=dev)
+    ws = _workspace(workspace, B, k + 1, V, target.dtype, dev)
+    st = lib().spec_verify_greedy_ext(_ptr(target), _check_rows(target, 2), _ptr(draft_tokens), B, k, V,
+                                      _DTYPE[target.dtype], _ptr(out_tokens), _ptr(out_na), _ptr(out_v),
+                                      _ptr(out_mask), _ptr(out_cnt), _ptr(ws), ws.numel(), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_greedy_ext")
+    return out_tokens, out_na, out_v, out_mask, out_cnt
+
+
+def sample_lenient(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
+                   uniforms: torch.Tensor, temperature: float, lenience: float, *,
+                   return_probs: bool = False, workspace=None, stream=None):
+    """Sampling verification with lenience l >= 1 (l = 1: `sample`)."""
+    B, k1, V = target.shape
+    k = k1 - 1
+    dev = target.device
+    out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
+    out_na = torch.empty((B,), dtype=torch.int32, device=dev)
+    out_p_x = torch.empty((B, k), dtype=torch.float32, device=dev) if return_probs else None
+    out_q_x = torch.empty((B, k), dtype=torch.float32, device=dev) if return_probs else None
+    ws = _workspace(workspace, B, 2 * k + 1, V, target.dtype, dev)
+    st = lib().spec_verify_sample_lenient(_ptr(target), _check_rows(target, 2), _ptr(draft),
+                                          _check_rows(draft, 2), _ptr(draft_tokens), _ptr(uniforms),
+                                          float(temperature), float(lenience), B, k, V,
+                                          _DTYPE[target.dtype], _ptr(out_tokens), _ptr(out_na),
+                                          _ptr(out_p_x), _ptr(out_q_x), _ptr(ws), ws.numel(),
+                                          _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_sample_lenient")
+    if return_probs:
+        return out_tokens, out_na, out_p_x, out_q_x
+    return out_tokens, out_na
+
+
+def greedy_candidates_ext(target: torch.Tensor, cand_tokens: torch.Tensor, *, workspace=None,
+                          stream=None):
+    """Multi-candidate greedy verification plus the argmax of every scored row.
+    Returns (tokens [B, L+1], A [B], best [B], target_argmax [B, C, R])."""
+    B, C, R, V = target.shape
+    L = cand_tokens.shape[2]
+    dev = target.device
+    out_tokens = torch.empty((B, L + 1), dtype=torch.int32, device=dev)
+    out_na = torch.empty((B,), dtype=torch.int32, device=dev)
+    out_best = torch.empty((B,), dtype=torch.int32, device=dev)
+    out_v = torch.empty((B, C, R), dtype=torch.int32, device=dev)
+    ws = _workspace(workspace, B, C * R, V, target.dtype, dev)
+    st = lib().spec_verify_greedy_candidates_ext(_ptr(target), _check_rows(target, 3), _ptr(cand_tokens),
+                                                 B, C, L, R, V, _DTYPE[target.dtype], _ptr(out_tokens),
+                                                 _ptr(out_na), _ptr(out_best), _ptr(out_v), _ptr(ws),
+                                                 ws.numel(), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_greedy_candidates_ext")
+    return out_tokens, out_na, out_best, out_v
 
 
 def greedy_candidates(target: torch.Tensor, cand_tokens: torch.Tensor, *, out_tokens=None,

@@ -145,36 +145,11 @@ void prof_end(hipStream_t st)
     g_prof.armed = false;
 }
 
-}  // namespace
-
-extern "C" {
-
-int spec_verify_version(void) { return 100; }
-
-const char* spec_verify_status_string(int s)
-{
-    switch (s) {
-    case SV_OK: return "SV_OK";
-    case SV_EINVAL: return "SV_EINVAL: invalid argument";
-    case SV_EDTYPE: return "SV_EDTYPE: unknown dtype";
-    case SV_EWORKSPACE: return "SV_EWORKSPACE: workspace missing or too small";
-    case SV_EHIP: return "SV_EHIP: HIP launch error";
-    default: return "unknown status";
-    }
-}
-
-size_t spec_verify_workspace_bytes(int B, int rows_per_seq, int V, int dtype)
-{
-    if (B < 1 || rows_per_seq < 1 || V < 1 || V > kMaxV || !dtype_ok(dtype)) return 0;
-    const long long rows = (long long)B * rows_per_seq;
-    if (!fits_grid(rows, V)) return 0;
-    return layout(nullptr, B, rows, V).bytes;
-}
-
-int spec_verify_greedy(const void* target_logits, long long target_row_stride,
-                       const int* draft_tokens, int B, int k, int V, int dtype,
-                       int* out_tokens, int* out_num_accepted,
-                       void* workspace, size_t workspace_bytes, void* hip_stream)
+int greedy_impl(const void* target_logits, long long target_row_stride,
+                const int* draft_tokens, int B, int k, int V, int dtype,
+                int* out_tokens, int* out_num_accepted, int* out_argmax,
+                unsigned long long* out_match_mask, int* out_num_match,
+                void* workspace, size_t workspace_bytes, void* hip_stream)
 {
     if (!dtype_ok(dtype)) return SV_EDTYPE;
     if (!target_logits || !draft_tokens || !out_tokens || !out_num_accepted) return SV_EINVAL;
@@ -212,17 +187,20 @@ int spec_verify_greedy(const void* target_logits, long long target_row_stride,
     da.partials = static_cast<const ArgPartial*>(w.partials);
     da.out_tokens = out_tokens;
     da.out_num_accepted = out_num_accepted;
+    da.out_argmax = out_argmax;
+    da.out_match_mask = out_match_mask;
+    da.out_num_match = out_num_match;
     if (launch_decide_greedy(da, st) != hipSuccess) return SV_EHIP;
     return SV_OK;
 }
 
-int spec_verify_sample(const void* target_logits, long long target_row_stride,
-                       const void* draft_logits, long long draft_row_stride,
-                       const int* draft_tokens, const float* uniforms, float temperature,
-                       int B, int k, int V, int dtype,
-                       int* out_tokens, int* out_num_accepted,
-                       float* out_p_x, float* out_q_x,
-                       void* workspace, size_t workspace_bytes, void* hip_stream)
+int sample_impl(const void* target_logits, long long target_row_stride,
+                const void* draft_logits, long long draft_row_stride,
+                const int* draft_tokens, const float* uniforms, float temperature,
+                float lenience, int B, int k, int V, int dtype,
+                int* out_tokens, int* out_num_accepted,
+                float* out_p_x, float* out_q_x,
+                void* workspace, size_t workspace_bytes, void* hip_stream)
 {
     if (!dtype_ok(dtype)) return SV_EDTYPE;
     if (!target_logits || !draft_logits || !draft_tokens || !uniforms || !out_tokens ||
@@ -231,6 +209,7 @@ int spec_verify_sample(const void* target_logits, long long target_row_stride,
     if (B < 1 || k < 1 || k > SV_MAX_K || V < 1 || V > kMaxV) return SV_EINVAL;
     if (target_row_stride < V || draft_row_stride < V) return SV_EINVAL;
     if (!(temperature > 0.f) || !isfinite(temperature)) return SV_EINVAL;
+    if (!(lenience >= 1.f) || !isfinite(lenience)) return SV_EINVAL;
     const double cd = 1.4426950408889634 / (double)temperature;
     if (!isfinite(cd) || cd > 3.0e38) return SV_EINVAL;
     const long long rows = (long long)B * (2 * k + 1);
@@ -272,6 +251,7 @@ int spec_verify_sample(const void* target_logits, long long target_row_stride,
     da.V = V;
     da.splits = sp.splits;
     da.c = c;
+    da.log2_lenience = (float)log2((double)lenience);
     da.partials = static_cast<const SoftPartial*>(w.partials);
     da.out_tokens = out_tokens;
     da.out_num_accepted = out_num_accepted;
@@ -301,11 +281,11 @@ int spec_verify_sample(const void* target_logits, long long target_row_stride,
     return SV_OK;
 }
 
-int spec_verify_greedy_candidates(const void* target_logits, long long row_stride,
-                                  const int* cand_tokens, int B, int C, int L, int R, int V,
-                                  int dtype, int* out_tokens, int* out_num_accepted,
-                                  int* out_best_candidate,
-                                  void* workspace, size_t workspace_bytes, void* hip_stream)
+int candidates_impl(const void* target_logits, long long row_stride,
+                    const int* cand_tokens, int B, int C, int L, int R, int V,
+                    int dtype, int* out_tokens, int* out_num_accepted,
+                    int* out_best_candidate, int* out_argmax,
+                    void* workspace, size_t workspace_bytes, void* hip_stream)
 {
     if (!dtype_ok(dtype)) return SV_EDTYPE;
     if (!target_logits || !cand_tokens || !out_tokens || !out_num_accepted || !out_best_candidate)
@@ -348,8 +328,104 @@ int spec_verify_greedy_candidates(const void* target_logits, long long row_strid
     da.out_tokens = out_tokens;
     da.out_num_accepted = out_num_accepted;
     da.out_best = out_best_candidate;
+    da.out_argmax = out_argmax;
     if (launch_decide_candidates(da, st) != hipSuccess) return SV_EHIP;
     return SV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int spec_verify_version(void) { return 200; }
+
+const char* spec_verify_status_string(int s)
+{
+    switch (s) {
+    case SV_OK: return "SV_OK";
+    case SV_EINVAL: return "SV_EINVAL: invalid argument";
+    case SV_EDTYPE: return "SV_EDTYPE: unknown dtype";
+    case SV_EWORKSPACE: return "SV_EWORKSPACE: workspace missing or too small";
+    case SV_EHIP: return "SV_EHIP: HIP launch error";
+    default: return "unknown status";
+    }
+}
+
+size_t spec_verify_workspace_bytes(int B, int rows_per_seq, int V, int dtype)
+{
+    if (B < 1 || rows_per_seq < 1 || V < 1 || V > kMaxV || !dtype_ok(dtype)) return 0;
+    const long long rows = (long long)B * rows_per_seq;
+    if (!fits_grid(rows, V)) return 0;
+    return layout(nullptr, B, rows, V).bytes;
+}
+
+int spec_verify_greedy(const void* target_logits, long long target_row_stride,
+                       const int* draft_tokens, int B, int k, int V, int dtype,
+                       int* out_tokens, int* out_num_accepted,
+                       void* workspace, size_t workspace_bytes, void* hip_stream)
+{
+    return greedy_impl(target_logits, target_row_stride, draft_tokens, B, k, V, dtype, out_tokens,
+                       out_num_accepted, nullptr, nullptr, nullptr, workspace, workspace_bytes,
+                       hip_stream);
+}
+
+int spec_verify_greedy_ext(const void* target_logits, long long target_row_stride,
+                           const int* draft_tokens, int B, int k, int V, int dtype,
+                           int* out_tokens, int* out_num_accepted, int* out_target_argmax,
+                           unsigned long long* out_match_mask, int* out_num_match,
+                           void* workspace, size_t workspace_bytes, void* hip_stream)
+{
+    return greedy_impl(target_logits, target_row_stride, draft_tokens, B, k, V, dtype, out_tokens,
+                       out_num_accepted, out_target_argmax, out_match_mask, out_num_match,
+                       workspace, workspace_bytes, hip_stream);
+}
+
+int spec_verify_sample(const void* target_logits, long long target_row_stride,
+                       const void* draft_logits, long long draft_row_stride,
+                       const int* draft_tokens, const float* uniforms, float temperature,
+                       int B, int k, int V, int dtype,
+                       int* out_tokens, int* out_num_accepted,
+                       float* out_p_x, float* out_q_x,
+                       void* workspace, size_t workspace_bytes, void* hip_stream)
+{
+    return sample_impl(target_logits, target_row_stride, draft_logits, draft_row_stride,
+                       draft_tokens, uniforms, temperature, 1.f, B, k, V, dtype, out_tokens,
+                       out_num_accepted, out_p_x, out_q_x, workspace, workspace_bytes, hip_stream);
+}
+
+int spec_verify_sample_lenient(const void* target_logits, long long target_row_stride,
+                               const void* draft_logits, long long draft_row_stride,
+                               const int* draft_tokens, const float* uniforms, float temperature,
+                               float lenience, int B, int k, int V, int dtype,
+                               int* out_tokens, int* out_num_accepted,
+                               float* out_p_x, float* out_q_x,
+                               void* workspace, size_t workspace_bytes, void* hip_stream)
+{
+    return sample_impl(target_logits, target_row_stride, draft_logits, draft_row_stride,
+                       draft_tokens, uniforms, temperature, lenience, B, k, V, dtype, out_tokens,
+                       out_num_accepted, out_p_x, out_q_x, workspace, workspace_bytes, hip_stream);
+}
+
+int spec_verify_greedy_candidates(const void* target_logits, long long row_stride,
+                                  const int* cand_tokens, int B, int C, int L, int R, int V,
+                                  int dtype, int* out_tokens, int* out_num_accepted,
+                                  int* out_best_candidate,
+                                  void* workspace, size_t workspace_bytes, void* hip_stream)
+{
+    return candidates_impl(target_logits, row_stride, cand_tokens, B, C, L, R, V, dtype, out_tokens,
+                           out_num_accepted, out_best_candidate, nullptr, workspace,
+                           workspace_bytes, hip_stream);
+}
+
+int spec_verify_greedy_candidates_ext(const void* target_logits, long long row_stride,
+                                      const int* cand_tokens, int B, int C, int L, int R, int V,
+                                      int dtype, int* out_tokens, int* out_num_accepted,
+                                      int* out_best_candidate, int* out_target_argmax,
+                                      void* workspace, size_t workspace_bytes, void* hip_stream)
+{
+    return candidates_impl(target_logits, row_stride, cand_tokens, B, C, L, R, V, dtype, out_tokens,
+                           out_num_accepted, out_best_candidate, out_target_argmax, workspace,
+                           workspace_bytes, hip_stream);
 }
 
 int spec_verify_profile_begin(int max_calls, int every)

@@ -53,7 +53,9 @@ __device__ __forceinline__ unsigned long long ballot64(bool pred)
 // ---- sampling --------------------------------------------------------------
 // log2 p_i(x) = (z_x - m) * c - log2 s with c = log2(e)/T.  The ratio test is
 // taken in the log domain so that no probability underflows: accept iff
-// log q <= log p (ratio >= 1, and q = 0) or u < exp2(log p - log q).
+// log q <= log p + log l (ratio >= 1, and q = 0) or u < exp2(log p + log l -
+// log q).  Lenience l (Cascade Speculative Drafting, review function) is 1
+// for the exact rule, where log l = 0 leaves the test unchanged.
 template <int DT>
 __global__ __launch_bounds__(kBlock) void k_decide_sample(DecideSampleArgs a)
 {
@@ -84,7 +86,8 @@ __global__ __launch_bounds__(kBlock) void k_decide_sample(DecideSampleArgs a)
             const float lp = (zx - mt) * c - log2f(st);
             const float lq = (yx - md) * c - log2f(sd);
             const float u = a.uniforms[(long long)b * (k + 1) + lane];
-            const bool accept = (lq <= lp) || (u < exp2f(lp - lq));
+            const float lpl = lp + a.log2_lenience;
+            const bool accept = (lq <= lpl) || (u < exp2f(lpl - lq));
             reject = !accept;
             px = exp2f(lp);
             qx = exp2f(lq);
@@ -136,8 +139,16 @@ __global__ __launch_bounds__(kBlock) void k_decide_greedy(DecideGreedyArgs a)
     if (lane <= k) {
         int* out = a.out_tokens + (long long)b * (k + 1);
         out[lane] = lane < j ? x : (lane == j ? amax : -1);
+        if (a.out_argmax) a.out_argmax[(long long)b * (k + 1) + lane] = amax;
     }
-    if (lane == 0) a.out_num_accepted[b] = j;
+    // by-products for phrase harvesting (Ouroboros 3.4.4, Eq. 10): matches
+    // anywhere among the k drafts, not only in the accepted prefix
+    const unsigned long long match = ballot64(lane < k && !miss);
+    if (lane == 0) {
+        a.out_num_accepted[b] = j;
+        if (a.out_match_mask) a.out_match_mask[b] = match;
+        if (a.out_num_match) a.out_num_match[b] = __popcll(match);
+    }
 }
 
 // ---- multi-candidate greedy ------------------------------------------------
@@ -178,6 +189,13 @@ __global__ __launch_bounds__(kBlock) void k_decide_candidates(DecideCandArgs a)
     if (A == L && R == L + 1 && lane == L) {
         const long long row = ((long long)b * C + cs) * R + L;
         bonus = merge_arg(a.partials + row * a.splits, a.splits);
+    }
+    if (a.out_argmax) {
+        if (active) a.out_argmax[((long long)b * C + c) * R + i] = amax;
+        if (R == L + 1 && lane < C) {
+            const long long row = ((long long)b * C + lane) * R + L;
+            a.out_argmax[row] = merge_arg(a.partials + row * a.splits, a.splits);
+        }
     }
     if (lane <= L) {
         int v;

@@ -67,6 +67,7 @@ struct DecideSampleArgs {
     const float* uniforms;             // [B][k+1]
     int B, k, V, splits;
     float c;
+    float log2_lenience;               // log2 l, 0 for the exact rule (l = 1)
     const SoftPartial* partials;       // target rows then draft rows
     int* out_tokens;                   // [B][k+1]
     int* out_num_accepted;             // [B]
@@ -81,6 +82,9 @@ struct DecideGreedyArgs {
     const ArgPartial* partials;        // [B*(k+1)][splits]
     int* out_tokens;
     int* out_num_accepted;
+    int* out_argmax;                   // [B][k+1] or null: v_i, the target argmax per position
+    unsigned long long* out_match_mask;  // [B] or null: bit i = [x_i == v_i], i < k
+    int* out_num_match;                // [B] or null: #Match
 };
 
 struct DecideCandArgs {
@@ -90,6 +94,7 @@ struct DecideCandArgs {
     int* out_tokens;                   // [B][L+1]
     int* out_num_accepted;
     int* out_best;
+    int* out_argmax;                   // [B][C][R] or null: argmax of every scored row
 };
 
 // The draw of each sequence (sv_sample.hip).  The sampled row (pair) is cut

@@ -121,6 +121,37 @@ int spec_verify_sample(const void* target_logits, long long target_row_stride,
                        float* out_p_x, float* out_q_x,
                        void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* Greedy verification plus the by-products of the same pass that phrase
+ * harvesting uses (Ouroboros section 3.4.4, Eq. 10; no extra logit bytes):
+ *   out_target_argmax DEVICE [B][k+1] int32 or NULL: v_i = argmax target_i at
+ *                     every position, accepted or not (the target's own tokens,
+ *                     from which the rejected tail's matching runs are read)
+ *   out_match_mask    DEVICE [B] uint64 or NULL: bit i (i < k) = [x_i == v_i]
+ *   out_num_match     DEVICE [B] int32 or NULL: #Match, the number of set bits
+ *                     (always >= out_num_accepted)
+ * Other arguments and errors as spec_verify_greedy. */
+int spec_verify_greedy_ext(const void* target_logits, long long target_row_stride,
+                           const int* draft_tokens, int B, int k, int V, int dtype,
+                           int* out_tokens, int* out_num_accepted, int* out_target_argmax,
+                           unsigned long long* out_match_mask, int* out_num_match,
+                           void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Sampling verification with lenience l (Cascade Speculative Drafting,
+ * section "The Vertical Cascade", the review function): x_i is accepted if
+ * q_i(x_i) <= l p_i(x_i), else rejected with probability 1 - l p/q, i.e.
+ * iff u_i < min(1, l p/q); the residual stays max(0, p - q).  l must be >= 1
+ * and finite (SV_EINVAL otherwise); l = 1 gives exactly spec_verify_sample's
+ * results.  With l > 1 the committed tokens are no longer distributed as p:
+ * the cascade applies it only where a draft model reviews another draft.
+ * Other arguments and errors as spec_verify_sample. */
+int spec_verify_sample_lenient(const void* target_logits, long long target_row_stride,
+                               const void* draft_logits, long long draft_row_stride,
+                               const int* draft_tokens, const float* uniforms, float temperature,
+                               float lenience, int B, int k, int V, int dtype,
+                               int* out_tokens, int* out_num_accepted,
+                               float* out_p_x, float* out_q_x,
+                               void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* Multi-candidate greedy verification (see the header comment).
  *   target_logits DEVICE [B][C][R][V]; row (c, i) scores candidate token (c, i).
  *                 R = L (no row after the last token: a fully accepted candidate
@@ -136,6 +167,18 @@ int spec_verify_greedy_candidates(const void* target_logits, long long row_strid
                                   int dtype, int* out_tokens, int* out_num_accepted,
                                   int* out_best_candidate,
                                   void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Multi-candidate greedy verification plus the argmax of every scored row:
+ *   out_target_argmax DEVICE [B][C][R] int32 or NULL: the target's token v at
+ *                     every candidate position (Ouroboros 3.4.4: an unused
+ *                     candidate c is corrected to its first token followed by
+ *                     v(c, 1..)).
+ * Other arguments and errors as spec_verify_greedy_candidates. */
+int spec_verify_greedy_candidates_ext(const void* target_logits, long long row_stride,
+                                      const int* cand_tokens, int B, int C, int L, int R, int V,
+                                      int dtype, int* out_tokens, int* out_num_accepted,
+                                      int* out_best_candidate, int* out_target_argmax,
+                                      void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* Measurement aid (not thread-safe; for a single profiling thread).  While
  * enabled, every `every`-th verification call (the first, then every

@@ -21,7 +21,8 @@ import dataclasses
 
 import numpy as np
 
-from . import draw_interval, greedy, greedy_candidates, sample, token_probs
+from . import (draw_interval, greedy, greedy_candidates, greedy_matches, row_argmax, sample,
+               sample_lenient, token_probs)
 
 
 @dataclasses.dataclass
@@ -43,10 +44,14 @@ class SampleReport:
 
 
 def check_sample(z, y, x, u, T, gpu_tokens, gpu_nacc, eps=1e-5, report=None,
-                 seq_ids=None) -> SampleReport:
-    """z [B,k+1,V], y [B,k,V] float32; x [B,k]; u [B,k+1]; GPU outputs as numpy."""
+                 seq_ids=None, lenience=None) -> SampleReport:
+    """z [B,k+1,V], y [B,k,V] float32; x [B,k]; u [B,k+1]; GPU outputs as numpy.
+    `lenience` (l >= 1) compares against the lenient rule instead."""
     rep = report or SampleReport()
-    ot, on, tr = sample(z, y, x, u, T, traces=True)
+    if lenience is None:
+        ot, on, tr = sample(z, y, x, u, T, traces=True)
+    else:
+        ot, on, tr = sample_lenient(z, y, x, u, T, lenience, traces=True)
     B, k1 = ot.shape
     k = k1 - 1
     for b in range(B):
@@ -110,3 +115,16 @@ def check_candidates(z, cand, gpu_tokens, gpu_A, gpu_best):
     ot, oa, ob = greedy_candidates(z, cand)
     bad = np.nonzero((oa != gpu_A) | (ob != gpu_best) | (ot != gpu_tokens).any(axis=1))[0]
     return bad.tolist(), ot, oa, ob
+
+
+def check_greedy_matches(z, x, gpu_v, gpu_mask, gpu_count):
+    """Bit-exact comparison of the #Match by-products; returns mismatching rows."""
+    v, mask, cnt = greedy_matches(z, x)
+    gm = np.asarray(gpu_mask).astype(np.int64).view(np.uint64)
+    bad = np.nonzero((v != gpu_v).any(axis=1) | (mask != gm) | (cnt != gpu_count))[0]
+    return bad.tolist()
+
+
+def check_row_argmax(z, gpu_v):
+    ref = row_argmax(z)
+    return np.argwhere(ref != gpu_v).tolist()

@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_header_symbols_exported(sv):
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 11, names
     assert sorted(sv.EXPORTED) == names
     for n in names:
         assert hasattr(sv.lib(), n), n
@@ -48,7 +48,7 @@ def test_single_hip_runtime(sv):
 
 def test_status_strings_and_version(sv):
     L = sv.lib()
-    assert L.spec_verify_version() >= 100
+    assert L.spec_verify_version() >= 200
     for s in range(5):
         assert L.spec_verify_status_string(s).startswith(b"SV_")
     assert L.spec_verify_status_string(99) == b"unknown status"
@@ -182,3 +182,26 @@ def test_binding_fails_loudly_without_library(tmp_path):
     r = subprocess.run([sys.executable, "-c", "import draft_verification_verify_amd"],
                        cwd=tmp_path, capture_output=True, text=True)
     assert r.returncode != 0 and "not built" in r.stderr
+
+
+def test_lenient_and_ext_reject_bad_arguments(sv):
+    L = sv.lib()
+    out, po = host_buf(64)
+    f = fake()[1]
+
+    def lenient(lv, **kw):
+        a = dict(target=f, ts=100, draft=f, ds=100, tokens=f, u=f, T=1.0, B=2, k=3, V=100, dt=2,
+                 out=po, nacc=f, ws=f, wsb=1 << 30)
+        a.update(kw)
+        return L.spec_verify_sample_lenient(a["target"], a["ts"], a["draft"], a["ds"], a["tokens"],
+                                            a["u"], a["T"], lv, a["B"], a["k"], a["V"], a["dt"],
+                                            a["out"], a["nacc"], None, None, a["ws"], a["wsb"], None)
+
+    for lv in (0.999, 0.0, -2.0, float("inf"), float("nan")):
+        assert lenient(lv) == sv.SV_EINVAL, lv
+    assert lenient(2.0, wsb=8) == sv.SV_EWORKSPACE
+    assert L.spec_verify_greedy_ext(f, 100, None, 2, 3, 100, 2, po, f, f, f, f, f, 1 << 30, None) == sv.SV_EINVAL
+    assert L.spec_verify_greedy_ext(f, 100, f, 2, 0, 100, 2, po, f, f, f, f, f, 1 << 30, None) == sv.SV_EINVAL
+    assert L.spec_verify_greedy_candidates_ext(f, 100, f, 2, 8, 8, 10, 100, 2, po, f, f, f, f, 1 << 30,
+                                               None) == sv.SV_EINVAL
+    assert (out == SENT).all()

@@ -336,6 +336,79 @@ def test_workload5_greedy(sv, w5):
 
 
 # ---------------------------------------------------------------------------
+# verification by-products (Ouroboros 3.4.4, Eq. 10) and lenience (Cascade)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("B,k,V", [(1, 1, 1), (5, 4, 1000), (9, 8, 12345), (3, 63, 300), (2, 16, 128256)])
+def test_greedy_ext_parity(sv, dtype, B, k, V):
+    g = torch.Generator(device=DEV).manual_seed(B + k + V)
+    w = synthetic.chain(B, k, V, dtype, seed=B * 5 + k + V, device=DEV)
+    x = corrupt_after_argmax(w.target, k, g, 0.8)
+    toks, na, v, mask, cnt = sv.greedy_ext(w.target, x)
+    t2, n2 = sv.greedy(w.target, x)
+    torch.cuda.synchronize()
+    assert np.array_equal(npi(toks), npi(t2)) and np.array_equal(npi(na), npi(n2))
+    z = f32(w.target)
+    bad, _, _ = parity.check_greedy(z, npi(x), npi(toks), npi(na))
+    assert not bad
+    bad = parity.check_greedy_matches(z, npi(x), npi(v), npi(mask), npi(cnt))
+    assert not bad, bad[:5]
+    assert (npi(cnt) >= npi(na)).all()
+
+
+def test_greedy_ext_workload3(sv, w3):
+    toks, na, v, mask, cnt = sv.greedy_ext(w3.target, w3.tokens)
+    torch.cuda.synchronize()
+    z = f32(w3.target)
+    assert not parity.check_greedy(z, npi(w3.tokens), npi(toks), npi(na))[0]
+    assert not parity.check_greedy_matches(z, npi(w3.tokens), npi(v), npi(mask), npi(cnt))
+    print("workload 3 greedy: mean #Match", npi(cnt).mean(), "mean accepted", npi(na).mean())
+
+
+@pytest.mark.parametrize("B,C,L,R,V", [(3, 2, 4, 4, 999), (4, 8, 8, 9, 3000), (2, 1, 63, 64, 500)])
+def test_candidates_ext_parity(sv, B, C, L, R, V):
+    w = synthetic.candidates(B, C, L, R, V, "bf16", seed=B + C + L + V + 1, device=DEV)
+    toks, A, best, v = sv.greedy_candidates_ext(w.target, w.tokens)
+    torch.cuda.synchronize()
+    z = f32(w.target)
+    bad, _, _, _ = parity.check_candidates(z, npi(w.tokens), npi(toks), npi(A), npi(best))
+    assert not bad
+    assert not parity.check_row_argmax(z, npi(v))
+
+
+def test_candidates_ext_workload4(sv):
+    w = synthetic.generate(4, device=DEV)
+    toks, A, best, v = sv.greedy_candidates_ext(w.target, w.tokens)
+    torch.cuda.synchronize()
+    z = f32(w.target)
+    assert not parity.check_candidates(z, npi(w.tokens), npi(toks), npi(A), npi(best))[0]
+    assert not parity.check_row_argmax(z, npi(v))
+
+
+def test_lenience_one_is_bitwise_the_rule(sv, w3):
+    a = sv.sample(w3.target, w3.draft, w3.tokens, w3.uniforms, w3.T, return_probs=True)
+    b = sv.sample_lenient(w3.target, w3.draft, w3.tokens, w3.uniforms, w3.T, 1.0, return_probs=True)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert np.array_equal(npi(u), npi(v))
+
+
+@pytest.mark.parametrize("lenience", [1.5, 3.0, 1e6])
+@pytest.mark.parametrize("dtype,B,k,V", [("bf16", 32, 6, 5003), ("fp16", 8, 4, 32000), ("fp32", 16, 8, 999)])
+def test_lenient_parity(sv, lenience, dtype, B, k, V):
+    w = synthetic.chain(B, k, V, dtype, var_noise=1.5, T=0.9, seed=B + k + V, device=DEV)
+    toks, na, px, qx = sv.sample_lenient(w.target, w.draft, w.tokens, w.uniforms, w.T, lenience,
+                                         return_probs=True)
+    torch.cuda.synchronize()
+    z, y = f32(w.target), f32(w.draft)
+    rep = parity.check_sample(z, y, npi(w.tokens), npi(w.uniforms), w.T, npi(toks), npi(na),
+                              eps=EPS, lenience=lenience)
+    assert rep.ok(), (rep.summary(), rep.failures[:3])
+    assert parity.check_probs(z, y, npi(w.tokens), w.T, npi(px), npi(qx)) <= PROB_RTOL
+    print(f"lenience {lenience}:", rep.summary())
+
+
+# ---------------------------------------------------------------------------
 # streams and the measurement aid
 # ---------------------------------------------------------------------------
 def test_side_stream_and_profile(sv):
