@@ -59,10 +59,12 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--mode", default="sample",
-                    choices=["sample", "greedy", "candidates", "greedy_ext", "lenient", "candidates_ext"],
+                    choices=["sample", "greedy", "candidates", "greedy_ext", "lenient", "candidates_ext",
+                             "tree"],
                     help="sample: workload 5 (the benchmark line); greedy / greedy_ext: workload 5 "
                          "greedy (ext: with the #Match by-products); lenient: workload 5 sampling "
-                         "with --lenience; candidates / candidates_ext: workload 4")
+                         "with --lenience; candidates / candidates_ext: workload 4; tree: workload 4 "
+                         "with shared rows stored once")
     ap.add_argument("--lenience", type=float, default=2.0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU oracle baseline budget (0 disables it)")
@@ -91,7 +93,7 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    cid = 4 if args.mode.startswith("candidates") else 5
+    cid = 4 if args.mode.startswith("candidates") or args.mode == "tree" else 5
     t0 = time.perf_counter()
     w = synthetic.generate(cid, device=dev)
     torch.cuda.synchronize()
@@ -99,7 +101,19 @@ def main():
     cfg = w.cfg
     es = w.target.element_size()
 
-    if args.mode.startswith("candidates"):
+    if args.mode == "tree":
+        nodes, cand_rows = synthetic.as_tree(w)
+        B, C, R, V = w.target.shape
+        L = w.tokens.shape[2]
+        N = nodes.shape[1]
+        rows = B * C * R
+        ws = torch.empty(sv.workspace_bytes(B, N, V, nodes.dtype), dtype=torch.uint8, device=dev)
+
+        def step():
+            sv.greedy_tree(nodes, w.tokens, cand_rows, workspace=ws)
+        stats_rows = B * N
+        workload = f"spec_verify_greedy_tree B={B} C={C} L={L} R={R} N={N} V={V} bf16"
+    elif args.mode.startswith("candidates"):
         B, C, R, V = w.target.shape
         L = w.tokens.shape[2]
         rows = B * C * R
@@ -214,6 +228,8 @@ def main():
         },
         "roofline": {
             "kernel": "k_softmax_stats" if args.mode in ("sample", "lenient") else "k_argmax_stats",
+            "note": ("rows counts every scored candidate position (B*C*R); the kernel reads "
+                     "B*N unique node rows") if args.mode == "tree" else None,
             "bound": "hbm",
             "achieved": achieved,
             "peak": PEAK_HBM_GBS,

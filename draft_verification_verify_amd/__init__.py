@@ -58,6 +58,8 @@ def lib():
         L.spec_verify_sample_lenient.restype = I
         L.spec_verify_greedy_candidates_ext.argtypes = [P, LL, P, I, I, I, I, I, I, P, P, P, P, P, SZ, P]
         L.spec_verify_greedy_candidates_ext.restype = I
+        L.spec_verify_greedy_tree.argtypes = [P, LL, I, P, P, I, I, I, I, I, I, P, P, P, P, SZ, P]
+        L.spec_verify_greedy_tree.restype = I
         L.spec_verify_profile_begin.argtypes = [I, I]
         L.spec_verify_profile_begin.restype = I
         L.spec_verify_profile_end.argtypes = [P, I]
@@ -70,6 +72,7 @@ EXPORTED = (
     "spec_verify_version", "spec_verify_status_string", "spec_verify_workspace_bytes",
     "spec_verify_greedy", "spec_verify_sample", "spec_verify_greedy_candidates",
     "spec_verify_greedy_ext", "spec_verify_sample_lenient", "spec_verify_greedy_candidates_ext",
+    "spec_verify_greedy_tree",
     "spec_verify_profile_begin", "spec_verify_profile_end",
 )
 
@@ -245,6 +248,28 @@ def greedy_candidates_ext(target: torch.Tensor, cand_tokens: torch.Tensor, *, wo
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_greedy_candidates_ext")
     return out_tokens, out_na, out_best, out_v
+
+
+def greedy_tree(nodes: torch.Tensor, cand_tokens: torch.Tensor, cand_rows: torch.Tensor, *,
+                workspace=None, stream=None):
+    """Multi-candidate greedy verification over a token tree.  nodes [B, N, V],
+    cand_tokens [B, C, L] int32, cand_rows [B, C, R] int32 (node row per
+    candidate position).  Returns (tokens [B, L+1], A [B], best [B])."""
+    B, N, V = nodes.shape
+    _, C, L = cand_tokens.shape
+    R = cand_rows.shape[2]
+    dev = nodes.device
+    out_tokens = torch.empty((B, L + 1), dtype=torch.int32, device=dev)
+    out_na = torch.empty((B,), dtype=torch.int32, device=dev)
+    out_best = torch.empty((B,), dtype=torch.int32, device=dev)
+    ws = _workspace(workspace, B, N, V, nodes.dtype, dev)
+    st = lib().spec_verify_greedy_tree(_ptr(nodes), _check_rows(nodes, 2), N, _ptr(cand_tokens),
+                                       _ptr(cand_rows), B, C, L, R, V, _DTYPE[nodes.dtype],
+                                       _ptr(out_tokens), _ptr(out_na), _ptr(out_best), _ptr(ws),
+                                       ws.numel(), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_greedy_tree")
+    return out_tokens, out_na, out_best
 
 
 def greedy_candidates(target: torch.Tensor, cand_tokens: torch.Tensor, *, out_tokens=None,

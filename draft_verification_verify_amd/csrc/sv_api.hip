@@ -282,8 +282,8 @@ int sample_impl(const void* target_logits, long long target_row_stride,
 }
 
 int candidates_impl(const void* target_logits, long long row_stride,
-                    const int* cand_tokens, int B, int C, int L, int R, int V,
-                    int dtype, int* out_tokens, int* out_num_accepted,
+                    const int* cand_tokens, const int* cand_rows, int N, int B, int C, int L, int R,
+                    int V, int dtype, int* out_tokens, int* out_num_accepted,
                     int* out_best_candidate, int* out_argmax,
                     void* workspace, size_t workspace_bytes, void* hip_stream)
 {
@@ -292,7 +292,8 @@ int candidates_impl(const void* target_logits, long long row_stride,
         return SV_EINVAL;
     if (B < 1 || C < 1 || L < 1 || L > SV_MAX_K || C * L > SV_MAX_CANDIDATE_TOKENS) return SV_EINVAL;
     if ((R != L && R != L + 1) || V < 1 || V > kMaxV || row_stride < V) return SV_EINVAL;
-    const long long rows = (long long)B * C * R;
+    if (cand_rows && N < 1) return SV_EINVAL;
+    const long long rows = (long long)B * (cand_rows ? (long long)N : (long long)C * R);
     if (!fits_grid(rows, V)) return SV_EINVAL;
     Workspace w = layout(static_cast<char*>(workspace), B, rows, V);
     if (!workspace || workspace_bytes < w.bytes) return SV_EWORKSPACE;
@@ -319,6 +320,8 @@ int candidates_impl(const void* target_logits, long long row_stride,
 
     DecideCandArgs da;
     da.cand = cand_tokens;
+    da.cand_rows = cand_rows;
+    da.N = N;
     da.B = B;
     da.C = C;
     da.L = L;
@@ -412,8 +415,20 @@ int spec_verify_greedy_candidates(const void* target_logits, long long row_strid
                                   int* out_best_candidate,
                                   void* workspace, size_t workspace_bytes, void* hip_stream)
 {
-    return candidates_impl(target_logits, row_stride, cand_tokens, B, C, L, R, V, dtype, out_tokens,
-                           out_num_accepted, out_best_candidate, nullptr, workspace,
+    return candidates_impl(target_logits, row_stride, cand_tokens, nullptr, 0, B, C, L, R, V, dtype,
+                           out_tokens, out_num_accepted, out_best_candidate, nullptr, workspace,
+                           workspace_bytes, hip_stream);
+}
+
+int spec_verify_greedy_tree(const void* node_logits, long long row_stride, int N,
+                            const int* cand_tokens, const int* cand_rows, int B, int C, int L, int R,
+                            int V, int dtype, int* out_tokens, int* out_num_accepted,
+                            int* out_best_candidate,
+                            void* workspace, size_t workspace_bytes, void* hip_stream)
+{
+    if (!cand_rows) return SV_EINVAL;
+    return candidates_impl(node_logits, row_stride, cand_tokens, cand_rows, N, B, C, L, R, V, dtype,
+                           out_tokens, out_num_accepted, out_best_candidate, nullptr, workspace,
                            workspace_bytes, hip_stream);
 }
 
@@ -423,9 +438,9 @@ int spec_verify_greedy_candidates_ext(const void* target_logits, long long row_s
                                       int* out_best_candidate, int* out_target_argmax,
                                       void* workspace, size_t workspace_bytes, void* hip_stream)
 {
-    return candidates_impl(target_logits, row_stride, cand_tokens, B, C, L, R, V, dtype, out_tokens,
-                           out_num_accepted, out_best_candidate, out_target_argmax, workspace,
-                           workspace_bytes, hip_stream);
+    return candidates_impl(target_logits, row_stride, cand_tokens, nullptr, 0, B, C, L, R, V, dtype,
+                           out_tokens, out_num_accepted, out_best_candidate, out_target_argmax,
+                           workspace, workspace_bytes, hip_stream);
 }
 
 int spec_verify_profile_begin(int max_calls, int every)

@@ -155,6 +155,22 @@ __global__ __launch_bounds__(kBlock) void k_decide_greedy(DecideGreedyArgs a)
 // Lane c*L + i holds candidate c's position i (C*L <= 64).  Candidate c's
 // accepted length is the index of its first mismatch bit; the longest wins,
 // ties to the lowest c (Ouroboros 3.4.3, "Selecting the accepted tokens").
+// Flat layout: row (c, i) of sequence b is row (b*C + c)*R + i.  Tree layout
+// (Ouroboros Figure 3, each node scored once): the row is b*N + cand_rows[b][c][i];
+// an index outside [0, N) never matches and gives the correction -1.
+__device__ __forceinline__ int cand_argmax(const DecideCandArgs& a, int b, int c, int i)
+{
+    long long row;
+    if (a.cand_rows) {
+        const int r = a.cand_rows[((long long)b * a.C + c) * a.R + i];
+        if (r < 0 || r >= a.N) return -1;
+        row = (long long)b * a.N + r;
+    } else {
+        row = ((long long)b * a.C + c) * a.R + i;
+    }
+    return merge_arg(a.partials + row * a.splits, a.splits);
+}
+
 __global__ __launch_bounds__(kBlock) void k_decide_candidates(DecideCandArgs a)
 {
     const int b = blockIdx.x * kSeqPerBlock + (threadIdx.x >> 6);
@@ -167,8 +183,7 @@ __global__ __launch_bounds__(kBlock) void k_decide_candidates(DecideCandArgs a)
     int amax = 0, tok = -1;
     bool miss = false;
     if (active) {
-        const long long row = ((long long)b * C + c) * R + i;
-        amax = merge_arg(a.partials + row * a.splits, a.splits);
+        amax = cand_argmax(a, b, c, i);
         tok = a.cand[((long long)b * C + c) * L + i];
         miss = tok != amax;
     }
@@ -186,16 +201,10 @@ __global__ __launch_bounds__(kBlock) void k_decide_candidates(DecideCandArgs a)
     const int ctok = __shfl(tok, src, 64);
     const int camx = __shfl(amax, src, 64);
     int bonus = -1;
-    if (A == L && R == L + 1 && lane == L) {
-        const long long row = ((long long)b * C + cs) * R + L;
-        bonus = merge_arg(a.partials + row * a.splits, a.splits);
-    }
+    if (A == L && R == L + 1 && lane == L) bonus = cand_argmax(a, b, cs, L);
     if (a.out_argmax) {
         if (active) a.out_argmax[((long long)b * C + c) * R + i] = amax;
-        if (R == L + 1 && lane < C) {
-            const long long row = ((long long)b * C + lane) * R + L;
-            a.out_argmax[row] = merge_arg(a.partials + row * a.splits, a.splits);
-        }
+        if (R == L + 1 && lane < C) a.out_argmax[((long long)b * C + lane) * R + L] = cand_argmax(a, b, lane, L);
     }
     if (lane <= L) {
         int v;

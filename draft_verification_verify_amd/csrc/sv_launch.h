@@ -89,6 +89,8 @@ struct DecideGreedyArgs {
 
 struct DecideCandArgs {
     const int* cand;                   // [B][C][L]
+    const int* cand_rows;              // [B][C][R] node row per position (tree layout) or null (flat)
+    int N;                             // node rows per sequence (tree layout)
     int B, C, L, R, splits;
     const ArgPartial* partials;        // [B*C*R][splits]
     int* out_tokens;                   // [B][L+1]

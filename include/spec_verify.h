@@ -180,6 +180,26 @@ int spec_verify_greedy_candidates_ext(const void* target_logits, long long row_s
                                       int* out_best_candidate, int* out_target_argmax,
                                       void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* Multi-candidate greedy verification over a token tree (Ouroboros section
+ * 3.4.3, Figure 3): the target scores each node of the candidate tree once,
+ * so candidates that share a prefix share its rows and fewer rows are read.
+ *   node_logits DEVICE [B][N][V]: row n of sequence b is the target
+ *               distribution after the context plus the path to node n
+ *   cand_tokens DEVICE [B][C][L] int32
+ *   cand_rows   DEVICE [B][C][R] int32: the node row (0 <= row < N) that scores
+ *               candidate token (c, i) for i < L, and for R = L+1 the row
+ *               after its last token.  A row outside [0, N) is never read: that
+ *               position never matches and its correction token is -1.
+ *   N >= 1.  Selection, outputs and errors as spec_verify_greedy_candidates;
+ *   the result equals spec_verify_greedy_candidates on the flat layout whose
+ *   row (c, i) is node row cand_rows[c][i].
+ *   workspace   DEVICE, >= spec_verify_workspace_bytes(B, N, V, dtype) */
+int spec_verify_greedy_tree(const void* node_logits, long long row_stride, int N,
+                            const int* cand_tokens, const int* cand_rows, int B, int C, int L, int R,
+                            int V, int dtype, int* out_tokens, int* out_num_accepted,
+                            int* out_best_candidate,
+                            void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* Measurement aid (not thread-safe; for a single profiling thread).  While
  * enabled, every `every`-th verification call (the first, then every
  * `every` calls), up to `max_calls` of them, records a pair of HIP events on

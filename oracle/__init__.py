@@ -78,9 +78,11 @@ def lib():
         L.oracle_sample_lenient.argtypes = [P, LL, P, LL, P, P, D, D, I, I, I, P, P, P]
         L.oracle_greedy_matches.argtypes = [P, LL, P, I, I, I, P, P, P]
         L.oracle_row_argmax.argtypes = [P, LL, LL, I, P]
+        L.oracle_greedy_tree.argtypes = [P, LL, I, P, P, I, I, I, I, I, P, P, P]
         for f in ("oracle_greedy", "oracle_sample", "oracle_greedy_candidates",
                   "oracle_token_probs_seq", "oracle_trace_size", "oracle_draw_interval",
-                  "oracle_sample_lenient", "oracle_greedy_matches", "oracle_row_argmax"):
+                  "oracle_sample_lenient", "oracle_greedy_matches", "oracle_row_argmax",
+                  "oracle_greedy_tree"):
             getattr(L, f).restype = I
         if L.oracle_trace_size() != ctypes.sizeof(Trace):
             raise RuntimeError("oracle_trace layout mismatch")
@@ -236,4 +238,22 @@ def greedy_candidates(target, cand_tokens, R=None):
                                         _ptr(out), _ptr(na), _ptr(best))
     if rc:
         raise RuntimeError(f"oracle_greedy_candidates failed: {rc}")
+    return out, na, best
+
+
+def greedy_tree(nodes, cand_tokens, cand_rows):
+    """nodes [B, N, V] float32, cand [B, C, L], cand_rows [B, C, R] -> (tokens [B, L+1], A, best)."""
+    z = _f32(nodes)
+    c = _i32(cand_tokens)
+    r = _i32(cand_rows)
+    B, N, V = z.shape
+    _, C, L = c.shape
+    R = r.shape[2]
+    out = np.full((B, L + 1), -1, np.int32)
+    na = np.zeros(B, np.int32)
+    best = np.zeros(B, np.int32)
+    rc = lib().oracle_greedy_tree(_ptr(z), V, N, _ptr(c), _ptr(r), B, C, L, R, V,
+                                  _ptr(out), _ptr(na), _ptr(best))
+    if rc:
+        raise RuntimeError(f"oracle_greedy_tree failed: {rc}")
     return out, na, best

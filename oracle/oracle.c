@@ -429,6 +429,45 @@ int oracle_greedy_matches(const float* target, long long row_stride, const int* 
     return 0;
 }
 
+/* Ouroboros 3.4.3 on a token tree: the same selection as the flat form, each
+ * candidate position reading the node row that scores it. */
+int oracle_greedy_tree(const float* nodes, long long row_stride, int N, const int* cand,
+                       const int* cand_rows, int B, int C, int L, int R, int V,
+                       int* out_tokens, int* out_num_accepted, int* out_best)
+{
+    if (!nodes || !cand || !cand_rows || !out_tokens || !out_num_accepted || !out_best) return -1;
+    if (B < 0 || N < 1 || C < 1 || L < 1 || C * L > 64 || (R != L && R != L + 1) || V < 1 ||
+        row_stride < V)
+        return -1;
+    for (int b = 0; b < B; ++b) {
+        const float* seq = nodes + (long long)b * N * row_stride;
+        const int* rows = cand_rows + (long long)b * C * R;
+        const int* cb = cand + (long long)b * C * L;
+        int* out = out_tokens + (long long)b * (L + 1);
+        int best_c = 0, best_a = -1;
+        for (int c = 0; c < C; ++c) {
+            int a = L;
+            for (int i = 0; i < L; ++i) {
+                int r = rows[c * R + i];
+                int v = (r >= 0 && r < N) ? argmax_row(seq + (long long)r * row_stride, V) : -1;
+                if (cb[c * L + i] != v) { a = i; break; }
+            }
+            if (a > best_a) { best_a = a; best_c = c; }
+        }
+        for (int i = 0; i <= L; ++i) out[i] = -1;
+        for (int i = 0; i < best_a; ++i) out[i] = cb[best_c * L + i];
+        int next = -1;
+        if (best_a < L || R == L + 1) {
+            int r = rows[best_c * R + best_a];
+            next = (r >= 0 && r < N) ? argmax_row(seq + (long long)r * row_stride, V) : -1;
+            out[best_a] = next;
+        }
+        out_num_accepted[b] = best_a;
+        out_best[b] = best_c;
+    }
+    return 0;
+}
+
 int oracle_row_argmax(const float* rows, long long row_stride, long long n_rows, int V, int* out)
 {
     if (!rows || !out || n_rows < 0 || V < 1 || row_stride < V) return -1;

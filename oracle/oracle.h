@@ -123,6 +123,18 @@ int oracle_greedy_matches(const float* target, long long row_stride, const int* 
                           int B, int k, int V, int* out_v, unsigned long long* out_mask,
                           int* out_num_match);
 
+/* Multi-candidate greedy selection over a token tree (Ouroboros section 3.4.3,
+ * Figure 3: the target scores every node of the tree once; candidates that
+ * share a prefix share its rows).  Sequence b has N node rows; cand_rows
+ * [B][C][R] names the node row that scores candidate token (c, i) for i < L,
+ * and for R = L+1 the row after the last token.  Otherwise as
+ * oracle_greedy_candidates (the flat layout is the tree with every row
+ * spelled out).  A row index outside [0, N) never matches and yields the
+ * correction token -1. */
+int oracle_greedy_tree(const float* nodes, long long row_stride, int N, const int* cand_tokens,
+                       const int* cand_rows, int B, int C, int L, int R, int V,
+                       int* out_tokens, int* out_num_accepted, int* out_best);
+
 /* The argmax of every row (candidates: the verification token of every
  * candidate position, used to correct unused candidates). */
 int oracle_row_argmax(const float* rows, long long row_stride, long long n_rows, int V, int* out);

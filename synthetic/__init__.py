@@ -231,3 +231,20 @@ def candidates(B: int, C: int, L: int, R: int, V: int, dtype: str = "bf16",
                  spike=spike, T=1.0, modes=("candidates",), C=C, L=L, R=R,
                  shared_rows=min(shared_rows, L), p_match=p_match)
     return _generate_candidates(cfg, make_generator(seed, device), device, None)
+
+
+def as_tree(w: Workload):
+    """The token-tree form of a candidate workload: rows that every candidate
+    shares (its first `shared_rows` rows) are stored once, then each
+    candidate's own rows.  Returns (nodes [B, N, V], cand_rows [B, C, R]) with
+    nodes[b, cand_rows[b, c, i]] == w.target[b, c, i]."""
+    cfg = w.cfg
+    B, C, R, V = w.target.shape
+    S = cfg.shared_rows
+    own = R - S
+    nodes = torch.cat([w.target[:, 0, :S], w.target[:, :, S:].reshape(B, C * own, V)], dim=1)
+    rows = torch.empty((C, R), dtype=torch.int32)
+    for c in range(C):
+        rows[c, :S] = torch.arange(S)
+        rows[c, S:] = S + c * own + torch.arange(own)
+    return nodes.contiguous(), rows.to(w.target.device).expand(B, C, R).contiguous()

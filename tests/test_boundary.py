@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_header_symbols_exported(sv):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     assert sorted(sv.EXPORTED) == names
     for n in names:
         assert hasattr(sv.lib(), n), n
@@ -161,6 +161,14 @@ def test_candidates_rejects_bad_arguments(sv):
     ]
     for kw, want in cases:
         assert call(**kw) == want, kw
+    assert (out == SENT).all()
+    # tree layout: missing row map, N < 1, bad R
+    assert L.spec_verify_greedy_tree(f, 100, 5, f, None, 2, 2, 3, 3, 100, 2, po, f, f, f, 1 << 30,
+                                     None) == sv.SV_EINVAL
+    assert L.spec_verify_greedy_tree(f, 100, 0, f, f, 2, 2, 3, 3, 100, 2, po, f, f, f, 1 << 30,
+                                     None) == sv.SV_EINVAL
+    assert L.spec_verify_greedy_tree(f, 100, 5, f, f, 2, 2, 3, 5, 100, 2, po, f, f, f, 1 << 30,
+                                     None) == sv.SV_EINVAL
     assert (out == SENT).all()
 
 

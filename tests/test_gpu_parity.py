@@ -409,6 +409,41 @@ def test_lenient_parity(sv, lenience, dtype, B, k, V):
 
 
 # ---------------------------------------------------------------------------
+# token tree (Ouroboros Figure 3: each node scored once)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("B,N,C,L,R,V", [(1, 1, 1, 1, 1, 5), (7, 10, 4, 5, 5, 999), (5, 20, 8, 8, 9, 3001),
+                                         (3, 70, 1, 63, 64, 300), (4, 43, 8, 8, 8, 20000)])
+def test_tree_parity(sv, B, N, C, L, R, V):
+    g = torch.Generator(device=DEV).manual_seed(B * N + C + L + V)
+    nodes = (torch.randn((B, N, V), generator=g, device=DEV) * 2).to(torch.bfloat16)
+    rows = torch.randint(0, N, (B, C, R), generator=g, device=DEV, dtype=torch.int32)
+    if N > 2:                                    # a few invalid row indices
+        rows[0, 0, -1] = N
+        rows[-1, C - 1, 0] = -7
+    ref = torch.gather(torch.argmax(nodes.float(), dim=2), 1, rows.clamp(0, N - 1).long().reshape(B, -1))
+    ref = ref.reshape(B, C, R)[:, :, :L].to(torch.int32)
+    keep = torch.rand((B, C, L), generator=g, device=DEV) < 0.85
+    cand = torch.where(keep, ref, torch.randint(0, V, (B, C, L), generator=g, device=DEV, dtype=torch.int32))
+    toks, A, best = sv.greedy_tree(nodes, cand, rows)
+    torch.cuda.synchronize()
+    ot, oa, ob = oracle.greedy_tree(f32(nodes), npi(cand), npi(rows))
+    assert np.array_equal(ot, npi(toks)) and np.array_equal(oa, npi(A)) and np.array_equal(ob, npi(best))
+
+
+def test_tree_workload4_equals_flat(sv):
+    w = synthetic.generate(4, device=DEV)
+    nodes, rows = synthetic.as_tree(w)
+    assert nodes.shape[1] == 43
+    t1, a1, b1 = sv.greedy_tree(nodes, w.tokens, rows)
+    t2, a2, b2 = sv.greedy_candidates(w.target, w.tokens)
+    torch.cuda.synchronize()
+    for u, v in ((t1, t2), (a1, a2), (b1, b2)):
+        assert np.array_equal(npi(u), npi(v))
+    ot, oa, ob = oracle.greedy_tree(f32(nodes), npi(w.tokens), npi(rows))
+    assert np.array_equal(ot, npi(t1)) and np.array_equal(oa, npi(a1)) and np.array_equal(ob, npi(b1))
+
+
+# ---------------------------------------------------------------------------
 # streams and the measurement aid
 # ---------------------------------------------------------------------------
 def test_side_stream_and_profile(sv):

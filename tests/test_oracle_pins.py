@@ -576,3 +576,45 @@ def test_row_argmax_matches_numpy():
     rng = np.random.default_rng(15)
     z = rng.integers(-3, 3, (50, 7, 41)).astype(np.float32)
     np.testing.assert_array_equal(oracle.row_argmax(z), np.argmax(z, axis=2))
+
+
+# ---------------------------------------------------------------------------
+# Token tree (Ouroboros 3.4.3, Figure 3): the tree is the flat candidate
+# layout with shared rows stored once
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("R_extra", [0, 1])
+def test_tree_equals_flat_layout(R_extra):
+    """Spelling every candidate's rows out of the tree gives the flat layout;
+    the tree selection must equal the (pinned) flat selection on it."""
+    rng = np.random.default_rng(16)
+    B, C, L, V, S = 400, 5, 6, 12, 3
+    R = L + R_extra
+    N = S + C * (R - S)
+    nodes = rng.integers(-3, 3, (B, N, V)).astype(np.float32)
+    rows = np.zeros((B, C, R), np.int32)
+    for c in range(C):
+        rows[:, c, :S] = np.arange(S)
+        rows[:, c, S:] = S + c * (R - S) + np.arange(R - S)
+    flat = np.take_along_axis(nodes[:, None, :, :], rows[..., None].astype(np.int64), axis=2)
+    ref = np.argmax(flat, axis=3)
+    cand = np.where(rng.random((B, C, L)) < 0.8, ref[:, :, :L], rng.integers(0, V, (B, C, L)))
+    cand[:, :, :S - 1] = cand[:, :1, :S - 1]
+    t1, a1, b1 = oracle.greedy_tree(nodes, cand, rows)
+    t2, a2, b2 = oracle.greedy_candidates(flat, cand)
+    np.testing.assert_array_equal(t1, t2)
+    np.testing.assert_array_equal(a1, a2)
+    np.testing.assert_array_equal(b1, b2)
+
+
+def test_tree_invalid_row_index_never_matches():
+    rng = np.random.default_rng(17)
+    B, C, L, V, N = 50, 2, 3, 9, 6
+    nodes = rng.normal(size=(B, N, V)).astype(np.float32)
+    rows = rng.integers(0, N, (B, C, L)).astype(np.int32)
+    ref = np.argmax(np.take_along_axis(nodes[:, None], rows[..., None].astype(np.int64), axis=2), axis=3)
+    cand = ref.copy()                                   # everything matches ...
+    rows[:, 1, 1] = N + 3                               # ... except where the row is invalid
+    rows[:, 0, 2] = -1
+    t, a, best = oracle.greedy_tree(nodes, cand, rows)
+    assert (a == 2).all() and (best == 0).all()
+    assert (t[:, 2] == -1).all()                        # correction from an invalid row
