@@ -60,11 +60,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--mode", default="sample",
                     choices=["sample", "greedy", "candidates", "greedy_ext", "lenient", "candidates_ext",
-                             "tree"],
+                             "tree", "sample_lazy", "greedy_lazy"],
                     help="sample: workload 5 (the benchmark line); greedy / greedy_ext: workload 5 "
                          "greedy (ext: with the #Match by-products); lenient: workload 5 sampling "
                          "with --lenience; candidates / candidates_ext: workload 4; tree: workload 4 "
-                         "with shared rows stored once")
+                         "with shared rows stored once; sample_lazy / greedy_lazy: workload 5 with "
+                         "early exit")
     ap.add_argument("--lenience", type=float, default=2.0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU oracle baseline budget (0 disables it)")
@@ -154,6 +155,24 @@ def main():
                                   workspace=ws)
             stats_rows = B * (2 * k + 1)
             workload = f"spec_verify_sample_lenient B={B} k={k} V={V} bf16 T={w.T} l={args.lenience}"
+        elif args.mode == "sample_lazy":
+            ws = torch.empty(sv.workspace_bytes(B, 2 * k + 1, V, w.target.dtype), dtype=torch.uint8,
+                             device=dev)
+
+            def step():
+                sv.sample_lazy(w.target, w.draft, w.tokens, w.uniforms, w.T, out_tokens=out_t,
+                               out_num_accepted=out_n, workspace=ws)
+            stats_rows = B * (2 * k + 1)
+            workload = f"spec_verify_sample_lazy B={B} k={k} V={V} bf16 T={w.T}"
+        elif args.mode == "greedy_lazy":
+            ws = torch.empty(sv.workspace_bytes(B, k + 1, V, w.target.dtype), dtype=torch.uint8,
+                             device=dev)
+
+            def step():
+                sv.greedy_lazy(w.target, w.tokens, out_tokens=out_t, out_num_accepted=out_n,
+                               workspace=ws)
+            stats_rows = rows
+            workload = f"spec_verify_greedy_lazy B={B} k={k} V={V} bf16"
         elif args.mode == "greedy_ext":
             ws = torch.empty(sv.workspace_bytes(B, k + 1, V, w.target.dtype), dtype=torch.uint8,
                              device=dev)
@@ -199,9 +218,12 @@ def main():
     ms_per_step = total_ms / args.steps
     value = rows * args.steps / (total_ms / 1e3)
 
-    k_avg_ms = statistics.fmean(kernel_ms)
-    achieved = stats_bytes / (k_avg_ms / 1e3) / 1e9
-    traffic = measured_traffic(stats_bytes)
+    lazy = args.mode.endswith("_lazy")
+    if lazy:                           # early exit: no single streaming kernel per call
+        kernel_ms = []
+    k_avg_ms = statistics.fmean(kernel_ms) if kernel_ms else None
+    achieved = stats_bytes / (k_avg_ms / 1e3) / 1e9 if kernel_ms else None
+    traffic = measured_traffic(stats_bytes) if args.mode == "sample" else None
 
     line = {
         "metric": METRIC,
@@ -226,7 +248,7 @@ def main():
             "input_generation_s": gen_s,
             "device": torch.cuda.get_device_name(0),
         },
-        "roofline": {
+        "roofline": None if lazy else {
             "kernel": "k_softmax_stats" if args.mode in ("sample", "lenient") else "k_argmax_stats",
             "note": ("rows counts every scored candidate position (B*C*R); the kernel reads "
                      "B*N unique node rows") if args.mode == "tree" else None,
@@ -234,11 +256,11 @@ def main():
             "achieved": achieved,
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
-            "frac": achieved / PEAK_HBM_GBS,
+            "frac": achieved / PEAK_HBM_GBS if achieved else None,
             "traffic": traffic,
             "kernel_ms_avg": k_avg_ms,
-            "kernel_ms_min": min(kernel_ms),
-            "kernel_ms_max": max(kernel_ms),
+            "kernel_ms_min": min(kernel_ms) if kernel_ms else None,
+            "kernel_ms_max": max(kernel_ms) if kernel_ms else None,
             "kernel_launches_timed": len(kernel_ms),
             "algorithmic_bytes_per_launch": stats_bytes,
         },

@@ -60,6 +60,10 @@ def lib():
         L.spec_verify_greedy_candidates_ext.restype = I
         L.spec_verify_greedy_tree.argtypes = [P, LL, I, P, P, I, I, I, I, I, I, P, P, P, P, SZ, P]
         L.spec_verify_greedy_tree.restype = I
+        L.spec_verify_sample_lazy.argtypes = [P, LL, P, LL, P, P, F, I, I, I, I, P, P, P, SZ, P]
+        L.spec_verify_sample_lazy.restype = I
+        L.spec_verify_greedy_lazy.argtypes = [P, LL, P, I, I, I, I, P, P, P, SZ, P]
+        L.spec_verify_greedy_lazy.restype = I
         L.spec_verify_profile_begin.argtypes = [I, I]
         L.spec_verify_profile_begin.restype = I
         L.spec_verify_profile_end.argtypes = [P, I]
@@ -72,7 +76,7 @@ EXPORTED = (
     "spec_verify_version", "spec_verify_status_string", "spec_verify_workspace_bytes",
     "spec_verify_greedy", "spec_verify_sample", "spec_verify_greedy_candidates",
     "spec_verify_greedy_ext", "spec_verify_sample_lenient", "spec_verify_greedy_candidates_ext",
-    "spec_verify_greedy_tree",
+    "spec_verify_greedy_tree", "spec_verify_sample_lazy", "spec_verify_greedy_lazy",
     "spec_verify_profile_begin", "spec_verify_profile_end",
 )
 
@@ -248,6 +252,49 @@ def greedy_candidates_ext(target: torch.Tensor, cand_tokens: torch.Tensor, *, wo
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_greedy_candidates_ext")
     return out_tokens, out_na, out_best, out_v
+
+
+def sample_lazy(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
+                uniforms: torch.Tensor, temperature: float, *, out_tokens=None, out_num_accepted=None,
+                workspace=None, stream=None):
+    """Early-exit sampling verification: `sample`'s results, reading only the rows
+    the rule looks at.  Returns (tokens [B, k+1], num_accepted [B])."""
+    B, k1, V = target.shape
+    k = k1 - 1
+    dev = target.device
+    if out_tokens is None:
+        out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
+    if out_num_accepted is None:
+        out_num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    ws = _workspace(workspace, B, 2 * k + 1, V, target.dtype, dev)
+    st = lib().spec_verify_sample_lazy(_ptr(target), _check_rows(target, 2), _ptr(draft),
+                                       _check_rows(draft, 2), _ptr(draft_tokens), _ptr(uniforms),
+                                       float(temperature), B, k, V, _DTYPE[target.dtype],
+                                       _ptr(out_tokens), _ptr(out_num_accepted), _ptr(ws), ws.numel(),
+                                       _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_sample_lazy")
+    return out_tokens, out_num_accepted
+
+
+def greedy_lazy(target: torch.Tensor, draft_tokens: torch.Tensor, *, out_tokens=None,
+                out_num_accepted=None, workspace=None, stream=None):
+    """Early-exit greedy verification: `greedy`'s results, reading only the rows
+    the rule looks at.  Returns (tokens [B, k+1], num_accepted [B])."""
+    B, k1, V = target.shape
+    k = k1 - 1
+    dev = target.device
+    if out_tokens is None:
+        out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
+    if out_num_accepted is None:
+        out_num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    ws = _workspace(workspace, B, k + 1, V, target.dtype, dev)
+    st = lib().spec_verify_greedy_lazy(_ptr(target), _check_rows(target, 2), _ptr(draft_tokens), B, k, V,
+                                       _DTYPE[target.dtype], _ptr(out_tokens), _ptr(out_num_accepted),
+                                       _ptr(ws), ws.numel(), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_greedy_lazy")
+    return out_tokens, out_num_accepted
 
 
 def greedy_tree(nodes: torch.Tensor, cand_tokens: torch.Tensor, cand_rows: torch.Tensor, *,

@@ -83,11 +83,13 @@ struct Workspace {
     void* partials;
     SampleDesc* desc;
     float* chunk_sums;
+    int* lists;                        // early exit: two lists of B sequence ids
+    int* counts;                       // early exit: their two counters
     size_t bytes;
 };
 
-// Layout: [split partials][sample descriptors][chunk totals], each region
-// 256-byte aligned.
+// Layout: [split partials][sample descriptors][chunk totals][work lists]
+// [counters], each region 256-byte aligned.
 Workspace layout(char* base, int B, long long rows, int V)
 {
     Workspace w;
@@ -100,6 +102,10 @@ Workspace layout(char* base, int B, long long rows, int V)
     off += align_up((size_t)B * sizeof(SampleDesc));
     w.chunk_sums = base ? reinterpret_cast<float*>(base + off) : nullptr;
     off += align_up((size_t)B * pp.nchunks * sizeof(float));
+    w.lists = base ? reinterpret_cast<int*>(base + off) : nullptr;
+    off += align_up((size_t)2 * B * sizeof(int));
+    w.counts = base ? reinterpret_cast<int*>(base + off) : nullptr;
+    off += align_up(2 * sizeof(int));
     w.bytes = off;
     return w;
 }
@@ -277,6 +283,8 @@ int sample_impl(const void* target_logits, long long target_row_stride,
     ma.chunk_sums = w.chunk_sums;
     ma.out_tokens = out_tokens;
     ma.out_row = k + 1;
+    ma.n_target_rows = B * (k + 1);
+    ma.n_draft_rows = B * k;
     if (launch_sample(dtype, vec, B, ma, st) != hipSuccess) return SV_EHIP;
     return SV_OK;
 }
@@ -334,6 +342,63 @@ int candidates_impl(const void* target_logits, long long row_stride,
     da.out_argmax = out_argmax;
     if (launch_decide_candidates(da, st) != hipSuccess) return SV_EHIP;
     return SV_OK;
+}
+
+// ---- early exit -------------------------------------------------------------
+// Window bounds 0, 1, 2, 4, 8, ... clipped to k+1: one position at a time while
+// most sequences are still deciding, then doubling.
+int lazy_bounds(int k, int* bounds)
+{
+    int n = 0;
+    bounds[n++] = 0;
+    int next = 1;
+    while (bounds[n - 1] < k + 1) {
+        bounds[n++] = next < k + 1 ? next : k + 1;
+        next = next < 2 ? next + 1 : next * 2;
+    }
+    return n;
+}
+
+constexpr int kLazyGrid = 4096;
+
+LazyArgs lazy_args(const void* target, long long ts, const void* draft, long long ds, int B, int k,
+                   int V, const StatsPlan& sp, float c, const Workspace& w)
+{
+    LazyArgs l;
+    l.target = target;
+    l.t_stride = ts;
+    l.draft = draft;
+    l.d_stride = ds;
+    l.B = B;
+    l.k = k;
+    l.V = V;
+    l.nvec = sp.nvec;
+    l.splits = sp.splits;
+    l.vec_per_split = sp.vec_per_split;
+    l.n_target_rows = B * (k + 1);
+    l.c = c;
+    l.partials = w.partials;
+    return l;
+}
+
+// Point window `p` of the schedule at its input and output work lists.
+void lazy_window(LazyArgs& l, const Workspace& w, const int* bounds, int p, int B)
+{
+    l.w0 = bounds[p];
+    l.w1 = bounds[p + 1];
+    l.list_in = p == 0 ? nullptr : w.lists + (size_t)(p % 2) * B;
+    l.count_in = p == 0 ? nullptr : w.counts + (p % 2);
+    l.list_out = w.lists + (size_t)((p + 1) % 2) * B;
+    l.count_out = w.counts + ((p + 1) % 2);
+    l.count_clear = l.count_out;
+}
+
+int lazy_grid(const LazyArgs& l, bool with_draft)
+{
+    const int nt = l.w1 - l.w0;
+    const int nd = with_draft ? (l.w0 < l.k ? (l.w1 < l.k ? l.w1 : l.k) - l.w0 : 0) : 0;
+    const long long units = (long long)l.B * (nt + nd) * l.splits;
+    return (int)(units < kLazyGrid ? units : kLazyGrid);
 }
 
 }  // namespace
@@ -441,6 +506,123 @@ int spec_verify_greedy_candidates_ext(const void* target_logits, long long row_s
     return candidates_impl(target_logits, row_stride, cand_tokens, nullptr, 0, B, C, L, R, V, dtype,
                            out_tokens, out_num_accepted, out_best_candidate, out_target_argmax,
                            workspace, workspace_bytes, hip_stream);
+}
+
+int spec_verify_sample_lazy(const void* target_logits, long long target_row_stride,
+                            const void* draft_logits, long long draft_row_stride,
+                            const int* draft_tokens, const float* uniforms, float temperature,
+                            int B, int k, int V, int dtype, int* out_tokens, int* out_num_accepted,
+                            void* workspace, size_t workspace_bytes, void* hip_stream)
+{
+    if (!dtype_ok(dtype)) return SV_EDTYPE;
+    if (!target_logits || !draft_logits || !draft_tokens || !uniforms || !out_tokens ||
+        !out_num_accepted)
+        return SV_EINVAL;
+    if (B < 1 || k < 1 || k > SV_MAX_K || V < 1 || V > kMaxV) return SV_EINVAL;
+    if (target_row_stride < V || draft_row_stride < V) return SV_EINVAL;
+    if (!(temperature > 0.f) || !isfinite(temperature)) return SV_EINVAL;
+    const double cd = 1.4426950408889634 / (double)temperature;
+    if (!isfinite(cd) || cd > 3.0e38) return SV_EINVAL;
+    const long long rows = (long long)B * (2 * k + 1);
+    if (!fits_grid(rows, V)) return SV_EINVAL;
+    Workspace w = layout(static_cast<char*>(workspace), B, rows, V);
+    if (!workspace || workspace_bytes < w.bytes) return SV_EWORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    const float c = (float)cd;
+    const bool vec = vec_ok(target_logits, target_row_stride, dtype) &&
+                     vec_ok(draft_logits, draft_row_stride, dtype);
+    const StatsPlan sp = plan_stats(rows, V);
+
+    DecideSampleArgs da;
+    da.target = target_logits;
+    da.t_stride = target_row_stride;
+    da.draft = draft_logits;
+    da.d_stride = draft_row_stride;
+    da.tokens = draft_tokens;
+    da.uniforms = uniforms;
+    da.B = B;
+    da.k = k;
+    da.V = V;
+    da.splits = sp.splits;
+    da.c = c;
+    da.log2_lenience = 0.f;
+    da.partials = static_cast<const SoftPartial*>(w.partials);
+    da.out_tokens = out_tokens;
+    da.out_num_accepted = out_num_accepted;
+    da.out_p_x = nullptr;
+    da.out_q_x = nullptr;
+    da.desc = w.desc;
+
+    LazyArgs l = lazy_args(target_logits, target_row_stride, draft_logits, draft_row_stride, B, k, V,
+                           sp, c, w);
+    int bounds[16];
+    const int nb = lazy_bounds(k, bounds);
+    for (int p = 0; p + 1 < nb; ++p) {
+        lazy_window(l, w, bounds, p, B);
+        if (launch_lazy_stats(dtype, vec, true, lazy_grid(l, true), l, st) != hipSuccess) return SV_EHIP;
+        if (launch_lazy_decide_sample(dtype, l, da, st) != hipSuccess) return SV_EHIP;
+    }
+
+    const SamplePlan pp = plan_sample(B, sp.nvec);
+    SampleArgs ma;
+    ma.target = target_logits;
+    ma.t_stride = target_row_stride;
+    ma.draft = draft_logits;
+    ma.d_stride = draft_row_stride;
+    ma.V = V;
+    ma.nvec = sp.nvec;
+    ma.nchunks = pp.nchunks;
+    ma.vec_per_chunk = pp.vec_per_chunk;
+    ma.chunks_per_block = pp.chunks_per_block;
+    ma.blocks_per_seq = pp.blocks_per_seq;
+    ma.c = c;
+    ma.desc = w.desc;
+    ma.chunk_sums = w.chunk_sums;
+    ma.out_tokens = out_tokens;
+    ma.out_row = k + 1;
+    ma.n_target_rows = B * (k + 1);
+    ma.n_draft_rows = B * k;
+    if (launch_sample(dtype, vec, B, ma, st) != hipSuccess) return SV_EHIP;
+    return SV_OK;
+}
+
+int spec_verify_greedy_lazy(const void* target_logits, long long target_row_stride,
+                            const int* draft_tokens, int B, int k, int V, int dtype,
+                            int* out_tokens, int* out_num_accepted,
+                            void* workspace, size_t workspace_bytes, void* hip_stream)
+{
+    if (!dtype_ok(dtype)) return SV_EDTYPE;
+    if (!target_logits || !draft_tokens || !out_tokens || !out_num_accepted) return SV_EINVAL;
+    if (B < 1 || k < 1 || k > SV_MAX_K || V < 1 || V > kMaxV || target_row_stride < V) return SV_EINVAL;
+    const long long rows = (long long)B * (k + 1);
+    if (!fits_grid(rows, V)) return SV_EINVAL;
+    Workspace w = layout(static_cast<char*>(workspace), B, rows, V);
+    if (!workspace || workspace_bytes < w.bytes) return SV_EWORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    const StatsPlan sp = plan_stats(rows, V);
+
+    DecideGreedyArgs da;
+    da.tokens = draft_tokens;
+    da.B = B;
+    da.k = k;
+    da.splits = sp.splits;
+    da.partials = static_cast<const ArgPartial*>(w.partials);
+    da.out_tokens = out_tokens;
+    da.out_num_accepted = out_num_accepted;
+    da.out_argmax = nullptr;
+    da.out_match_mask = nullptr;
+    da.out_num_match = nullptr;
+
+    LazyArgs l = lazy_args(target_logits, target_row_stride, nullptr, 0, B, k, V, sp, 0.f, w);
+    const bool vec = vec_ok(target_logits, target_row_stride, dtype);
+    int bounds[16];
+    const int nb = lazy_bounds(k, bounds);
+    for (int p = 0; p + 1 < nb; ++p) {
+        lazy_window(l, w, bounds, p, B);
+        if (launch_lazy_stats(dtype, vec, false, lazy_grid(l, false), l, st) != hipSuccess) return SV_EHIP;
+        if (launch_lazy_decide_greedy(l, da, st) != hipSuccess) return SV_EHIP;
+    }
+    return SV_OK;
 }
 
 int spec_verify_profile_begin(int max_calls, int every)

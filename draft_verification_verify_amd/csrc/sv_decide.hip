@@ -56,67 +56,122 @@ __device__ __forceinline__ unsigned long long ballot64(bool pred)
 // log q <= log p + log l (ratio >= 1, and q = 0) or u < exp2(log p + log l -
 // log q).  Lenience l (Cascade Speculative Drafting, review function) is 1
 // for the exact rule, where log l = 0 leaves the test unchanged.
+
+// The statistics of target row (b, pos) and, for pos < k, the decision at pos.
+struct PosSample {
+    float mt, st, md, sd, px, qx;
+    int x;
+    bool reject;
+};
+
+template <int DT>
+__device__ __forceinline__ PosSample sample_position(const DecideSampleArgs& a, int b, int pos)
+{
+    constexpr int ES = DT == DT_F32 ? 4 : 2;
+    const int k = a.k;
+    const float c = a.c;
+    PosSample r;
+    r.md = -INFINITY;
+    r.sd = 0.f;
+    r.px = 0.f;
+    r.qx = 0.f;
+    r.x = -1;
+    r.reject = false;
+    const int tr = b * (k + 1) + pos;
+    merge_soft(a.partials + (long long)tr * a.splits, a.splits, c, r.mt, r.st);
+    if (pos < k) {
+        const int nT = a.B * (k + 1);
+        const int dr = b * k + pos;
+        merge_soft(a.partials + (long long)(nT + dr) * a.splits, a.splits, c, r.md, r.sd);
+        r.x = a.tokens[(long long)b * k + pos];
+        const bool valid = r.x >= 0 && r.x < a.V;
+        if (valid) {
+            const float zx = load_elem<DT>(row_ptr(a.target, tr, a.t_stride, ES), r.x);
+            const float yx = load_elem<DT>(row_ptr(a.draft, dr, a.d_stride, ES), r.x);
+            const float lp = (zx - r.mt) * c - log2f(r.st);
+            const float lq = (yx - r.md) * c - log2f(r.sd);
+            const float u = a.uniforms[(long long)b * (k + 1) + pos];
+            const float lpl = lp + a.log2_lenience;
+            const bool accept = (lq <= lpl) || (u < exp2f(lpl - lq));
+            r.reject = !accept;
+            r.px = exp2f(lp);
+            r.qx = exp2f(lq);
+        } else {
+            r.reject = true;
+        }
+    }
+    return r;
+}
+
+// The round's one draw: the residual against draft row j, or the bonus row k.
+__device__ __forceinline__ void write_desc(const DecideSampleArgs& a, int b, int j, const PosSample& r)
+{
+    const int k = a.k;
+    SampleDesc d;
+    d.t_row = b * (k + 1) + j;
+    d.d_row = j < k ? b * k + j : -1;
+    d.out_pos = j;
+    d.kind = j < k ? 0 : 1;
+    d.off_t = r.mt * a.c + log2f(r.st);
+    d.off_d = j < k ? r.md * a.c + log2f(r.sd) : 0.f;
+    d.u = a.uniforms[(long long)b * (k + 1) + k];
+    d.pad = 0;
+    a.desc[b] = d;
+    a.out_num_accepted[b] = j;
+}
+
 template <int DT>
 __global__ __launch_bounds__(kBlock) void k_decide_sample(DecideSampleArgs a)
 {
-    constexpr int ES = DT == DT_F32 ? 4 : 2;
     const int b = blockIdx.x * kSeqPerBlock + (threadIdx.x >> 6);
     if (b >= a.B) return;
     const int lane = threadIdx.x & 63;
     const int k = a.k;
-    const float c = a.c;
-    const int nT = a.B * (k + 1);
-
-    float mt = -INFINITY, st = 0.f, md = -INFINITY, sd = 0.f;
-    bool reject = false;
-    int x = -1;
-    float px = 0.f, qx = 0.f;
-    if (lane <= k) {
-        const int tr = b * (k + 1) + lane;
-        merge_soft(a.partials + (long long)tr * a.splits, a.splits, c, mt, st);
-    }
-    if (lane < k) {
-        const int dr = b * k + lane;
-        merge_soft(a.partials + (long long)(nT + dr) * a.splits, a.splits, c, md, sd);
-        x = a.tokens[(long long)b * k + lane];
-        const bool valid = x >= 0 && x < a.V;
-        if (valid) {
-            const float zx = load_elem<DT>(row_ptr(a.target, b * (k + 1) + lane, a.t_stride, ES), x);
-            const float yx = load_elem<DT>(row_ptr(a.draft, dr, a.d_stride, ES), x);
-            const float lp = (zx - mt) * c - log2f(st);
-            const float lq = (yx - md) * c - log2f(sd);
-            const float u = a.uniforms[(long long)b * (k + 1) + lane];
-            const float lpl = lp + a.log2_lenience;
-            const bool accept = (lq <= lpl) || (u < exp2f(lpl - lq));
-            reject = !accept;
-            px = exp2f(lp);
-            qx = exp2f(lq);
-        } else {
-            reject = true;
-        }
-    }
-    const unsigned long long rej = ballot64(reject);
+    PosSample r{};
+    if (lane <= k) r = sample_position<DT>(a, b, lane);
+    const unsigned long long rej = ballot64(lane < k && r.reject);
     const int j = rej ? (__ffsll((long long)rej) - 1) : k;
 
     int* out = a.out_tokens + (long long)b * (k + 1);
-    if (lane < j) out[lane] = x;
+    if (lane < j) out[lane] = r.x;
     else if (lane > j && lane <= k) out[lane] = -1;
     if (lane < k) {
-        if (a.out_p_x) a.out_p_x[(long long)b * k + lane] = px;
-        if (a.out_q_x) a.out_q_x[(long long)b * k + lane] = qx;
+        if (a.out_p_x) a.out_p_x[(long long)b * k + lane] = r.px;
+        if (a.out_q_x) a.out_q_x[(long long)b * k + lane] = r.qx;
     }
-    if (lane == j) {
-        SampleDesc d;
-        d.t_row = b * (k + 1) + j;
-        d.d_row = j < k ? b * k + j : -1;
-        d.out_pos = j;
-        d.kind = j < k ? 0 : 1;
-        d.off_t = mt * c + log2f(st);
-        d.off_d = j < k ? md * c + log2f(sd) : 0.f;
-        d.u = a.uniforms[(long long)b * (k + 1) + k];
-        d.pad = 0;
-        a.desc[b] = d;
-        a.out_num_accepted[b] = j;
+    if (lane == j) write_desc(a, b, j, r);
+}
+
+// Early exit: lane i takes position w0 + i of window [w0, w1).  A rejection
+// inside the window (or reaching position k) finishes the sequence exactly as
+// k_decide_sample would; otherwise its accepted drafts are written and it
+// moves on to the next window.
+template <int DT>
+__global__ __launch_bounds__(kBlock) void k_lazy_decide_sample(LazyArgs l, DecideSampleArgs a)
+{
+    const int li = blockIdx.x * kSeqPerBlock + (threadIdx.x >> 6);
+    const int count = l.list_in ? min(*l.count_in, a.B) : a.B;
+    if (li >= count) return;
+    const int b = l.list_in ? l.list_in[li] : li;
+    if (b < 0 || b >= a.B) return;
+    const int lane = threadIdx.x & 63;
+    const int k = a.k;
+    const int pos = l.w0 + lane;
+    const bool in = pos < l.w1;
+    PosSample r{};
+    if (in) r = sample_position<DT>(a, b, pos);
+    const unsigned long long rej = ballot64(in && pos < k && r.reject);
+    int j = -1;
+    if (rej) j = l.w0 + __ffsll((long long)rej) - 1;
+    else if (l.w1 == k + 1) j = k;
+    int* out = a.out_tokens + (long long)b * (k + 1);
+    if (in && pos < k && (j < 0 || pos < j)) out[pos] = r.x;
+    if (j >= 0) {
+        if (pos == j) write_desc(a, b, j, r);
+        if (lane > j && lane <= k) out[lane] = -1;
+    } else if (lane == 0) {
+        const int slot = atomicAdd(l.count_out, 1);
+        l.list_out[slot] = b;
     }
 }
 
@@ -148,6 +203,44 @@ __global__ __launch_bounds__(kBlock) void k_decide_greedy(DecideGreedyArgs a)
         a.out_num_accepted[b] = j;
         if (a.out_match_mask) a.out_match_mask[b] = match;
         if (a.out_num_match) a.out_num_match[b] = __popcll(match);
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void k_lazy_decide_greedy(LazyArgs l, DecideGreedyArgs a)
+{
+    const int li = blockIdx.x * kSeqPerBlock + (threadIdx.x >> 6);
+    const int count = l.list_in ? min(*l.count_in, a.B) : a.B;
+    if (li >= count) return;
+    const int b = l.list_in ? l.list_in[li] : li;
+    if (b < 0 || b >= a.B) return;
+    const int lane = threadIdx.x & 63;
+    const int k = a.k;
+    const int pos = l.w0 + lane;
+    const bool in = pos < l.w1;
+    int amax = 0, x = -1;
+    bool miss = false;
+    if (in) {
+        amax = merge_arg(a.partials + (long long)(b * (k + 1) + pos) * a.splits, a.splits);
+        if (pos < k) {
+            x = a.tokens[(long long)b * k + pos];
+            miss = x != amax;
+        }
+    }
+    const unsigned long long mm = ballot64(in && pos < k && miss);
+    int j = -1;
+    if (mm) j = l.w0 + __ffsll((long long)mm) - 1;
+    else if (l.w1 == k + 1) j = k;
+    int* out = a.out_tokens + (long long)b * (k + 1);
+    if (in && pos < k && (j < 0 || pos < j)) out[pos] = x;
+    if (j >= 0) {
+        if (pos == j) {
+            out[pos] = amax;
+            a.out_num_accepted[b] = j;
+        }
+        if (lane > j && lane <= k) out[lane] = -1;
+    } else if (lane == 0) {
+        const int slot = atomicAdd(l.count_out, 1);
+        l.list_out[slot] = b;
     }
 }
 
@@ -228,6 +321,24 @@ hipError_t launch_decide_sample(int dt, const DecideSampleArgs& a, hipStream_t s
                   : dt == DT_F16 ? reinterpret_cast<const void*>(k_decide_sample<DT_F16>)
                                  : reinterpret_cast<const void*>(k_decide_sample<DT_BF16>);
     return hipLaunchKernel(f, dim3(grid), dim3(kBlock), args, 0, st);
+}
+
+hipError_t launch_lazy_decide_sample(int dt, const LazyArgs& l, const DecideSampleArgs& a, hipStream_t st)
+{
+    void* args[] = {const_cast<LazyArgs*>(&l), const_cast<DecideSampleArgs*>(&a)};
+    const unsigned grid = (unsigned)((a.B + kSeqPerBlock - 1) / kSeqPerBlock);
+    const void* f = dt == DT_F32 ? reinterpret_cast<const void*>(k_lazy_decide_sample<DT_F32>)
+                  : dt == DT_F16 ? reinterpret_cast<const void*>(k_lazy_decide_sample<DT_F16>)
+                                 : reinterpret_cast<const void*>(k_lazy_decide_sample<DT_BF16>);
+    return hipLaunchKernel(f, dim3(grid), dim3(kBlock), args, 0, st);
+}
+
+hipError_t launch_lazy_decide_greedy(const LazyArgs& l, const DecideGreedyArgs& a, hipStream_t st)
+{
+    void* args[] = {const_cast<LazyArgs*>(&l), const_cast<DecideGreedyArgs*>(&a)};
+    const unsigned grid = (unsigned)((a.B + kSeqPerBlock - 1) / kSeqPerBlock);
+    return hipLaunchKernel(reinterpret_cast<const void*>(k_lazy_decide_greedy), dim3(grid), dim3(kBlock),
+                           args, 0, st);
 }
 
 hipError_t launch_decide_greedy(const DecideGreedyArgs& a, hipStream_t st)

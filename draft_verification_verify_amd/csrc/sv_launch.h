@@ -119,9 +119,34 @@ struct SampleArgs {
     float* chunk_sums;                 // [B][nchunks]
     int* out_tokens;                   // [B][out_row]
     int out_row;
+    int n_target_rows, n_draft_rows;   // bounds every descriptor is checked against
 };
 
 constexpr int kMaxChunks = 128;
+
+// Early-exit verification (sv_stats.hip k_lazy_stats, sv_decide.hip
+// k_lazy_decide_*): positions are taken in windows [w0, w1); a window's rows
+// are streamed only for the sequences still undecided after the previous
+// windows (list_in / count_in; null list_in: every sequence, in order).  The
+// decision kernel finishes every sequence that rejects inside the window (or
+// reaches position k) and appends the others to list_out / count_out.  The
+// statistics kernel zeroes count_clear (the next decision's output counter).
+struct LazyArgs {
+    const void* target;
+    long long t_stride;
+    const void* draft;                 // null for greedy
+    long long d_stride;
+    int B, k, V, nvec, splits, vec_per_split;
+    int n_target_rows;                 // B*(k+1); draft rows follow in the partials
+    float c;
+    void* partials;
+    int w0, w1;
+    const int* list_in;
+    const int* count_in;
+    int* list_out;
+    int* count_out;
+    int* count_clear;
+};
 
 hipError_t launch_softmax_stats(int dt, bool vec, const StatsArgs& a, hipStream_t st);
 hipError_t launch_argmax_stats(int dt, bool vec, const StatsArgs& a, hipStream_t st);
@@ -129,5 +154,8 @@ hipError_t launch_decide_sample(int dt, const DecideSampleArgs& a, hipStream_t s
 hipError_t launch_decide_greedy(const DecideGreedyArgs& a, hipStream_t st);
 hipError_t launch_decide_candidates(const DecideCandArgs& a, hipStream_t st);
 hipError_t launch_sample(int dt, bool vec, int B, const SampleArgs& a, hipStream_t st);
+hipError_t launch_lazy_stats(int dt, bool vec, bool soft, int grid, const LazyArgs& a, hipStream_t st);
+hipError_t launch_lazy_decide_sample(int dt, const LazyArgs& l, const DecideSampleArgs& a, hipStream_t st);
+hipError_t launch_lazy_decide_greedy(const LazyArgs& l, const DecideGreedyArgs& a, hipStream_t st);
 
 }  // namespace sv

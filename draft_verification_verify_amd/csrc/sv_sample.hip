@@ -155,6 +155,16 @@ constexpr int kRoundsInFlight = 4;
 // Chunk totals: workgroup (b, g) covers chunks [g * chunks_per_block, ...) of
 // sequence b's sampled row, kRoundsInFlight rounds per step with every load of
 // the step issued before any arithmetic.
+// A descriptor names rows inside the batch and a position inside the output
+// row; anything else (never produced by the decision kernels) is skipped.
+__device__ __forceinline__ bool desc_ok(const SampleArgs& a, const SampleDesc& d)
+{
+    if (d.t_row < 0 || d.t_row >= a.n_target_rows) return false;
+    if (d.out_pos < 0 || d.out_pos >= a.out_row) return false;
+    if (d.kind == 0 && (d.d_row < 0 || d.d_row >= a.n_draft_rows)) return false;
+    return true;
+}
+
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kBlock) void k_sample_chunks(SampleArgs a)
 {
@@ -165,7 +175,7 @@ __global__ __launch_bounds__(kBlock) void k_sample_chunks(SampleArgs a)
     const SampleDesc d = a.desc[b];
     const int ch0 = g * a.chunks_per_block;
     const int ch1 = min(ch0 + a.chunks_per_block, a.nchunks);
-    if (ch0 >= ch1) return;                       // uniform across the workgroup
+    if (ch0 >= ch1 || !desc_ok(a, d)) return;     // uniform across the workgroup
     const char* zr = row_ptr(a.target, d.t_row, a.t_stride, ES);
     const char* yr = d.kind == 0 ? row_ptr(a.draft, d.d_row, a.d_stride, ES) : zr;
     const int v0 = ch0 * a.vec_per_chunk;
@@ -231,6 +241,7 @@ __global__ __launch_bounds__(kBlock) void k_sample_pick(SampleArgs a)
 
     const int b = blockIdx.x;
     const SampleDesc d = a.desc[b];
+    if (!desc_ok(a, d)) return;                   // uniform across the workgroup
     const char* zr = row_ptr(a.target, d.t_row, a.t_stride, ES);
     const char* yr = d.kind == 0 ? row_ptr(a.draft, d.d_row, a.d_stride, ES) : zr;
 

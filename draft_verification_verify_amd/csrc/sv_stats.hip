@@ -64,21 +64,15 @@ __device__ __forceinline__ const char* stats_row(const StatsArgs& a, int row, in
 constexpr int kSB = kStatsBlock;
 constexpr int kSW = kStatsBlock / 64;
 
+// (max, sum of exp2) of logical vectors [v0, v1) of one row, reduced over the
+// 512-thread workgroup in a fixed order; thread 0 holds the result.  Called
+// by every thread of the workgroup.
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kStatsBlock) void k_softmax_stats(StatsArgs a)
+__device__ __forceinline__ SoftPartial slice_softmax(const char* rp, int v0, int v1, int V, float c,
+                                                     float* lds_m, float* lds_s)
 {
-    __shared__ float lds_m[kSW], lds_s[kSW];
-    constexpr int ES = DT == DT_F32 ? 4 : 2;
-    const int unit = blockIdx.x;
-    const int row = unit / a.splits;
-    const int split = unit - row * a.splits;
-    const char* rp = stats_row(a, row, ES);
-    const int v0 = split * a.vec_per_split;
-    const int v1 = min(v0 + a.vec_per_split, a.nvec);
-    const int nfull = a.V >> 3;
+    const int nfull = V >> 3;
     const int vend = min(v1, nfull);
-    const float c = a.c;
-
     float m = -INFINITY, s = 0.f;
     int v = v0 + (int)threadIdx.x;
     for (; v + 3 * kSB < vend; v += 4 * kSB) {
@@ -101,7 +95,7 @@ __global__ __launch_bounds__(kStatsBlock) void k_softmax_stats(StatsArgs a)
     }
     if (v == nfull && nfull < v1) {    // the row's partial last vector
         float e[kVec];
-        load_partial<DT>(rp, nfull, a.V - 8 * nfull, -INFINITY, e);
+        load_partial<DT>(rp, nfull, V - 8 * nfull, -INFINITY, e);
         soft_update<kVec>(e, m, s, c);
     }
 
@@ -117,34 +111,26 @@ __global__ __launch_bounds__(kStatsBlock) void k_softmax_stats(StatsArgs a)
         lds_s[w] = s;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        float M = lds_m[0], S = lds_s[0];
+    float M = lds_m[0], S = lds_s[0];
+    if (threadIdx.x == 0)
         for (int i = 1; i < kSW; ++i) soft_merge(M, S, lds_m[i], lds_s[i], c);
-        reinterpret_cast<SoftPartial*>(a.partials)[unit] = SoftPartial{M, S};
-    }
+    __syncthreads();                   // the LDS slots may be reused by the caller
+    return SoftPartial{M, S};
 }
 
-// Argmax with the lowest index among equal maxima.  Each thread keeps the
-// largest value it has seen and the first group of vectors where it appeared
-// (strictly-greater updates keep the first occurrence, in ascending index
-// order within the thread).  After the block maximum M is known, only the
-// threads holding M reload that one group to locate their first index of M;
-// the block takes the smallest.  -0.0 and +0.0 compare equal throughout.
+// Argmax with the lowest index among equal maxima over logical vectors
+// [v0, v1) of one row.  Each thread keeps the largest value it has seen and
+// the first group of vectors where it appeared (strictly-greater updates keep
+// the first occurrence, in ascending index order within the thread).  After
+// the block maximum M is known, only the threads holding M reload that one
+// group to locate their first index of M; the block takes the smallest.
+// -0.0 and +0.0 compare equal throughout.  Called by every thread.
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kStatsBlock) void k_argmax_stats(StatsArgs a)
+__device__ __forceinline__ ArgPartial slice_argmax(const char* rp, int v0, int v1, int V,
+                                                   float* lds_f, int* lds_i)
 {
-    __shared__ float lds_f[kSW];
-    __shared__ int lds_i[kSW];
-    constexpr int ES = DT == DT_F32 ? 4 : 2;
-    const int unit = blockIdx.x;
-    const int row = unit / a.splits;
-    const int split = unit - row * a.splits;
-    const char* rp = stats_row(a, row, ES);
-    const int v0 = split * a.vec_per_split;
-    const int v1 = min(v0 + a.vec_per_split, a.nvec);
-    const int nfull = a.V >> 3;
+    const int nfull = V >> 3;
     const int vend = min(v1, nfull);
-
     float bv = -INFINITY;
     int bvec = -1, bcnt = 0;
     int v = v0 + (int)threadIdx.x;
@@ -184,7 +170,7 @@ __global__ __launch_bounds__(kStatsBlock) void k_argmax_stats(StatsArgs a)
     }
     if (v == nfull && nfull < v1) {
         float e[kVec];
-        load_partial<DT>(rp, nfull, a.V - 8 * nfull, -INFINITY, e);
+        load_partial<DT>(rp, nfull, V - 8 * nfull, -INFINITY, e);
         float cm = e[0];
 #pragma unroll
         for (int j = 1; j < kVec; ++j) cm = fmaxf(cm, e[j]);
@@ -201,14 +187,106 @@ __global__ __launch_bounds__(kStatsBlock) void k_argmax_stats(StatsArgs a)
         for (int j = 0; j < bcnt && idx == INT32_MAX; ++j) {
             const int vv = bvec + j * kSB;
             float e[kVec];
-            load8<DT, VEC>(rp, vv, nfull, a.V, -INFINITY, e);
+            load8<DT, VEC>(rp, vv, nfull, V, -INFINITY, e);
 #pragma unroll
             for (int t = kVec - 1; t >= 0; --t)
                 if (e[t] == M) idx = 8 * vv + t;
         }
     }
     idx = block_min_int<kSW>(idx, lds_i);
-    if (threadIdx.x == 0) reinterpret_cast<ArgPartial*>(a.partials)[unit] = ArgPartial{M, idx};
+    return ArgPartial{M, idx};
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kStatsBlock) void k_softmax_stats(StatsArgs a)
+{
+    __shared__ float lds_m[kSW], lds_s[kSW];
+    constexpr int ES = DT == DT_F32 ? 4 : 2;
+    const int unit = blockIdx.x;
+    const int row = unit / a.splits;
+    const int split = unit - row * a.splits;
+    const int v0 = split * a.vec_per_split;
+    const int v1 = min(v0 + a.vec_per_split, a.nvec);
+    const SoftPartial r = slice_softmax<DT, VEC>(stats_row(a, row, ES), v0, v1, a.V, a.c, lds_m, lds_s);
+    if (threadIdx.x == 0) reinterpret_cast<SoftPartial*>(a.partials)[unit] = r;
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kStatsBlock) void k_argmax_stats(StatsArgs a)
+{
+    __shared__ float lds_f[kSW];
+    __shared__ int lds_i[kSW];
+    constexpr int ES = DT == DT_F32 ? 4 : 2;
+    const int unit = blockIdx.x;
+    const int row = unit / a.splits;
+    const int split = unit - row * a.splits;
+    const int v0 = split * a.vec_per_split;
+    const int v1 = min(v0 + a.vec_per_split, a.nvec);
+    const ArgPartial r = slice_argmax<DT, VEC>(stats_row(a, row, ES), v0, v1, a.V, lds_f, lds_i);
+    if (threadIdx.x == 0) reinterpret_cast<ArgPartial*>(a.partials)[unit] = r;
+}
+
+// Early-exit statistics: the rows of window [w0, w1) of every listed
+// sequence, one (row, slice) unit at a time in a workgroup-strided loop (the
+// grid is sized for the worst case and workgroups past the live units exit).
+// Row and slice numbering is the full pass's, so partials match it bit for bit.
+template <int DT, bool VEC, bool SOFT>
+__global__ __launch_bounds__(kStatsBlock) void k_lazy_stats(LazyArgs a)
+{
+    __shared__ float lds_f[kSW], lds_s[kSW];
+    __shared__ int lds_i[kSW];
+    constexpr int ES = DT == DT_F32 ? 4 : 2;
+    if (blockIdx.x == 0 && threadIdx.x == 0 && a.count_clear) *a.count_clear = 0;
+    const int count = a.list_in ? min(*a.count_in, a.B) : a.B;
+    const int nt = a.w1 - a.w0;
+    const int nd = a.draft ? max(0, min(a.w1, a.k) - a.w0) : 0;
+    const int per_seq = (nt + nd) * a.splits;
+    const long long n_units = (long long)count * per_seq;
+    for (long long u = blockIdx.x; u < n_units; u += gridDim.x) {
+        const int li = (int)(u / per_seq);
+        const int rem = (int)(u - (long long)li * per_seq);
+        const int r = rem / a.splits;
+        const int split = rem - r * a.splits;
+        const int b = a.list_in ? a.list_in[li] : li;
+        if (b < 0 || b >= a.B) continue;         // uniform across the workgroup
+        long long row;
+        const char* rp;
+        if (r < nt) {
+            row = (long long)b * (a.k + 1) + a.w0 + r;
+            rp = row_ptr(a.target, row, a.t_stride, ES);
+        } else {
+            const long long drow = (long long)b * a.k + a.w0 + (r - nt);
+            row = a.n_target_rows + drow;
+            rp = row_ptr(a.draft, drow, a.d_stride, ES);
+        }
+        const int v0 = split * a.vec_per_split;
+        const int v1 = min(v0 + a.vec_per_split, a.nvec);
+        if constexpr (SOFT) {
+            const SoftPartial p = slice_softmax<DT, VEC>(rp, v0, v1, a.V, a.c, lds_f, lds_s);
+            if (threadIdx.x == 0) reinterpret_cast<SoftPartial*>(a.partials)[row * a.splits + split] = p;
+        } else {
+            const ArgPartial p = slice_argmax<DT, VEC>(rp, v0, v1, a.V, lds_f, lds_i);
+            if (threadIdx.x == 0) reinterpret_cast<ArgPartial*>(a.partials)[row * a.splits + split] = p;
+        }
+    }
+}
+
+template <int DT, bool VEC>
+static hipError_t launch_lazy_dt(bool soft, int grid, const LazyArgs& a, hipStream_t st)
+{
+    void* args[] = {const_cast<LazyArgs*>(&a)};
+    const void* f = soft ? reinterpret_cast<const void*>(k_lazy_stats<DT, VEC, true>)
+                         : reinterpret_cast<const void*>(k_lazy_stats<DT, VEC, false>);
+    return hipLaunchKernel(f, dim3((unsigned)grid), dim3(kStatsBlock), args, 0, st);
+}
+
+hipError_t launch_lazy_stats(int dt, bool vec, bool soft, int grid, const LazyArgs& a, hipStream_t st)
+{
+    switch (dt) {
+    case DT_F32: return vec ? launch_lazy_dt<DT_F32, true>(soft, grid, a, st) : launch_lazy_dt<DT_F32, false>(soft, grid, a, st);
+    case DT_F16: return vec ? launch_lazy_dt<DT_F16, true>(soft, grid, a, st) : launch_lazy_dt<DT_F16, false>(soft, grid, a, st);
+    default:     return vec ? launch_lazy_dt<DT_BF16, true>(soft, grid, a, st) : launch_lazy_dt<DT_BF16, false>(soft, grid, a, st);
+    }
 }
 
 template <typename K>

@@ -200,6 +200,31 @@ int spec_verify_greedy_tree(const void* node_logits, long long row_stride, int N
                             int* out_best_candidate,
                             void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* Early-exit verification: the same results as spec_verify_sample /
+ * spec_verify_greedy, bit for bit, while reading only the rows the rule
+ * looks at.  The rule examines position i only when every earlier draft was
+ * accepted (production blog, "The acceptance rule": left to right, stopping
+ * at the first rejection), so positions are taken in windows [0,1), [1,2),
+ * [2,4), [4,8), ... and a window's rows are streamed only for the sequences
+ * still undecided after the previous windows (a device-side work list; no
+ * host synchronisation).  Rows read per sequence: those up to its first
+ * rejection, rounded up to the end of that window, plus the sampled row.
+ * Worth it when acceptance is low; with high acceptance it reads as much as
+ * the full pass in more launches.  p(x_i) and q(x_i) are not exported (the
+ * rows after the first rejection are not read).
+ * Arguments, outputs, workspace size and errors as spec_verify_sample /
+ * spec_verify_greedy respectively. */
+int spec_verify_sample_lazy(const void* target_logits, long long target_row_stride,
+                            const void* draft_logits, long long draft_row_stride,
+                            const int* draft_tokens, const float* uniforms, float temperature,
+                            int B, int k, int V, int dtype, int* out_tokens, int* out_num_accepted,
+                            void* workspace, size_t workspace_bytes, void* hip_stream);
+
+int spec_verify_greedy_lazy(const void* target_logits, long long target_row_stride,
+                            const int* draft_tokens, int B, int k, int V, int dtype,
+                            int* out_tokens, int* out_num_accepted,
+                            void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* Measurement aid (not thread-safe; for a single profiling thread).  While
  * enabled, every `every`-th verification call (the first, then every
  * `every` calls), up to `max_calls` of them, records a pair of HIP events on

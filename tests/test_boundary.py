@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_header_symbols_exported(sv):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     assert sorted(sv.EXPORTED) == names
     for n in names:
         assert hasattr(sv.lib(), n), n
@@ -212,4 +212,21 @@ def test_lenient_and_ext_reject_bad_arguments(sv):
     assert L.spec_verify_greedy_ext(f, 100, f, 2, 0, 100, 2, po, f, f, f, f, f, 1 << 30, None) == sv.SV_EINVAL
     assert L.spec_verify_greedy_candidates_ext(f, 100, f, 2, 8, 8, 10, 100, 2, po, f, f, f, f, 1 << 30,
                                                None) == sv.SV_EINVAL
+    assert (out == SENT).all()
+
+
+def test_lazy_reject_bad_arguments(sv):
+    L = sv.lib()
+    out, po = host_buf(64)
+    f = fake()[1]
+    assert L.spec_verify_sample_lazy(f, 100, None, 100, f, f, 1.0, 2, 3, 100, 2, po, f, f, 1 << 30,
+                                     None) == sv.SV_EINVAL
+    assert L.spec_verify_sample_lazy(f, 100, f, 100, f, f, 0.0, 2, 3, 100, 2, po, f, f, 1 << 30,
+                                     None) == sv.SV_EINVAL
+    assert L.spec_verify_sample_lazy(f, 100, f, 100, f, f, 1.0, 2, 3, 100, 7, po, f, f, 1 << 30,
+                                     None) == sv.SV_EDTYPE
+    assert L.spec_verify_sample_lazy(f, 100, f, 100, f, f, 1.0, 2, 3, 100, 2, po, f, f, 8,
+                                     None) == sv.SV_EWORKSPACE
+    assert L.spec_verify_greedy_lazy(f, 99, f, 2, 3, 100, 2, po, f, f, 1 << 30, None) == sv.SV_EINVAL
+    assert L.spec_verify_greedy_lazy(f, 100, f, 2, 64, 100, 2, po, f, f, 1 << 30, None) == sv.SV_EINVAL
     assert (out == SENT).all()

@@ -444,6 +444,57 @@ def test_tree_workload4_equals_flat(sv):
 
 
 # ---------------------------------------------------------------------------
+# early exit: the same results, bit for bit, from fewer rows
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("B,k,V", [(1, 1, 1), (5, 4, 1000), (9, 8, 12345), (3, 63, 300), (6, 16, 32000)])
+@pytest.mark.parametrize("noise", [0.3, 3.0])
+def test_lazy_equals_full(sv, dtype, B, k, V, noise):
+    w = synthetic.chain(B, k, V, dtype, var_noise=noise, T=0.8, seed=B * 11 + k + V, device=DEV)
+    g = torch.Generator(device=DEV).manual_seed(B + k)
+    x = corrupt_after_argmax(w.target, k, g, 0.9)
+    a = sv.sample(w.target, w.draft, w.tokens, w.uniforms, w.T)
+    b = sv.sample_lazy(w.target, w.draft, w.tokens, w.uniforms, w.T)
+    c = sv.greedy(w.target, x)
+    d = sv.greedy_lazy(w.target, x)
+    torch.cuda.synchronize()
+    for u, v in zip(a + c, b + d):
+        assert np.array_equal(npi(u), npi(v))
+    bad, _, _ = parity.check_greedy(f32(w.target), npi(x), npi(d[0]), npi(d[1]))
+    assert not bad
+    rep = parity.check_sample(f32(w.target), f32(w.draft), npi(w.tokens), npi(w.uniforms), w.T,
+                              npi(b[0]), npi(b[1]), eps=EPS)
+    assert rep.ok(), (rep.summary(), rep.failures[:3])
+
+
+def test_lazy_full_acceptance_and_masking(sv):
+    """Every draft accepted (p = q): every window runs and the bonus is drawn;
+    invalid tokens stop a sequence mid-window."""
+    w = synthetic.chain(40, 20, 3000, "bf16", T=1.1, seed=41, device=DEV)
+    w.draft.copy_(w.target[:, :20])
+    w.tokens[5, 7] = -3
+    w.tokens[9, 13] = 3000
+    a = sv.sample(w.target, w.draft, w.tokens, w.uniforms, w.T)
+    b = sv.sample_lazy(w.target, w.draft, w.tokens, w.uniforms, w.T)
+    torch.cuda.synchronize()
+    assert np.array_equal(npi(a[0]), npi(b[0])) and np.array_equal(npi(a[1]), npi(b[1]))
+    na = npi(b[1])
+    assert na[5] == 7 and na[9] == 13 and (np.delete(na, [5, 9]) == 20).all()
+
+
+@pytest.mark.parametrize("cid", [3, 5])
+def test_lazy_workloads(sv, cid):
+    w = synthetic.generate(cid, device=DEV)
+    a = sv.sample(w.target, w.draft, w.tokens, w.uniforms, w.T)
+    b = sv.sample_lazy(w.target, w.draft, w.tokens, w.uniforms, w.T)
+    c = sv.greedy(w.target, w.tokens)
+    d = sv.greedy_lazy(w.target, w.tokens)
+    torch.cuda.synchronize()
+    for u, v in zip(a + c, b + d):
+        assert np.array_equal(npi(u), npi(v))
+
+
+# ---------------------------------------------------------------------------
 # streams and the measurement aid
 # ---------------------------------------------------------------------------
 def test_side_stream_and_profile(sv):
