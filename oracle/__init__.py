@@ -79,10 +79,12 @@ def lib():
         L.oracle_greedy_matches.argtypes = [P, LL, P, I, I, I, P, P, P]
         L.oracle_row_argmax.argtypes = [P, LL, LL, I, P]
         L.oracle_greedy_tree.argtypes = [P, LL, I, P, P, I, I, I, I, I, P, P, P]
+        L.oracle_sample_truncated.argtypes = [P, LL, P, LL, P, P, D, I, D, I, I, I, P, P, P, P]
+        L.oracle_truncated_row.argtypes = [P, I, D, I, D, P, P]
         for f in ("oracle_greedy", "oracle_sample", "oracle_greedy_candidates",
                   "oracle_token_probs_seq", "oracle_trace_size", "oracle_draw_interval",
                   "oracle_sample_lenient", "oracle_greedy_matches", "oracle_row_argmax",
-                  "oracle_greedy_tree"):
+                  "oracle_greedy_tree", "oracle_sample_truncated", "oracle_truncated_row"):
             getattr(L, f).restype = I
         if L.oracle_trace_size() != ctypes.sizeof(Trace):
             raise RuntimeError("oracle_trace layout mismatch")
@@ -257,3 +259,41 @@ def greedy_tree(nodes, cand_tokens, cand_rows):
     if rc:
         raise RuntimeError(f"oracle_greedy_tree failed: {rc}")
     return out, na, best
+
+
+def sample_truncated(target, draft, draft_tokens, uniforms, temperature, top_k=0, top_p=1.0,
+                     traces=False):
+    """The rule on top-k / top-p truncated p and q.  Returns (tokens, num_accepted)
+    and, with traces, also (traces, trunc_margin [B])."""
+    z = _f32(target)
+    y = _f32(draft)
+    x = _i32(draft_tokens)
+    u = _f32(uniforms)
+    B, k1, V = z.shape
+    k = k1 - 1
+    out = np.full((B, k + 1), -1, np.int32)
+    na = np.zeros(B, np.int32)
+    tr = (Trace * B)() if traces else None
+    margin = np.ones(B, np.float64)
+    rc = lib().oracle_sample_truncated(_ptr(z), V, _ptr(y), V, _ptr(x), _ptr(u), float(temperature),
+                                       int(top_k), float(top_p), B, k, V, _ptr(out), _ptr(na),
+                                       ctypes.cast(tr, ctypes.c_void_p) if traces else None,
+                                       _ptr(margin))
+    if rc:
+        raise RuntimeError(f"oracle_sample_truncated failed: {rc}")
+    if traces:
+        return out, na, list(tr), margin
+    return out, na
+
+
+def truncated_row(z, temperature, top_k=0, top_p=1.0):
+    """p' of one row and its top-p boundary margin."""
+    zz = _f32(z)
+    V = zz.shape[-1]
+    p = np.zeros(V, np.float64)
+    m = ctypes.c_double()
+    rc = lib().oracle_truncated_row(_ptr(zz), V, float(temperature), int(top_k), float(top_p),
+                                    _ptr(p), ctypes.byref(m))
+    if rc:
+        raise RuntimeError(f"oracle_truncated_row failed: {rc}")
+    return p, m.value

@@ -32,6 +32,78 @@ static int softmax_row(const float* z, int V, double T, double* p)
     return 0;
 }
 
+/* ---- truncation (top-k, then top-p) -------------------------------------
+ * Tokens are ranked by logit; equal logits share a rank group and are kept
+ * or dropped together. */
+typedef struct { double z, p; } zp_pair;
+
+static int cmp_desc(const void* a, const void* b)
+{
+    double x = ((const zp_pair*)a)->z, y = ((const zp_pair*)b)->z;
+    return (x < y) - (x > y);
+}
+
+static int truncate_row(const float* z, int V, double T, int top_k, double top_p, double* p,
+                        double* margin)
+{
+    *margin = 1.0;
+    int rc = softmax_row(z, V, T, p);          /* p: softmax(z / T) */
+    if (rc) return rc;
+    zp_pair* sorted = (zp_pair*)malloc(sizeof(zp_pair) * (size_t)V);
+    if (!sorted) return -2;
+    for (int t = 0; t < V; ++t) {
+        sorted[t].z = (double)z[t];
+        sorted[t].p = p[t];
+    }
+    qsort(sorted, (size_t)V, sizeof(zp_pair), cmp_desc);
+    /* top-k: keep logits >= the top_k-th largest */
+    double zk = -INFINITY;
+    if (top_k >= 1 && top_k < V) zk = sorted[top_k - 1].z;
+    /* top-p over the kept set, groups of equal logits in descending order:
+     * a group is kept iff the kept mass strictly above it is below top_p of
+     * the kept mass; the first group that fails and every later one drop */
+    double zdrop = -INFINITY;                  /* drop logits <= zdrop */
+    int dropped = 0;
+    if (top_p < 1.0) {
+        double M = 0.0;
+        for (int i = 0; i < V && sorted[i].z >= zk; ++i) M += sorted[i].p;
+        const double budget = top_p * M;
+        double greater = 0.0;
+        int i = 0;
+        while (i < V && sorted[i].z >= zk) {
+            const double g = sorted[i].z;
+            if (!(greater < budget)) {
+                zdrop = g;
+                dropped = 1;
+                const double m1 = (greater - budget) / M;
+                if (m1 < *margin) *margin = m1;
+                break;
+            }
+            const double m0 = (budget - greater) / M;
+            if (m0 < *margin) *margin = m0;
+            while (i < V && sorted[i].z == g) greater += sorted[i++].p;
+        }
+    }
+    free(sorted);
+    double S = 0.0;
+    for (int t = 0; t < V; ++t) {
+        const double zt = (double)z[t];
+        const int kept = zt >= zk && !(dropped && zt <= zdrop);
+        if (!kept) p[t] = 0.0;
+        S += p[t];
+    }
+    for (int t = 0; t < V; ++t) p[t] /= S;
+    return 0;
+}
+
+int oracle_truncated_row(const float* z, int V, double T, int top_k, double top_p, double* out_p,
+                         double* margin)
+{
+    if (!z || !out_p || !margin || V < 1 || top_k < 0 || !(top_p > 0.0)) return -1;
+    if (!(T > 0.0) || !isfinite(T)) return -1;
+    return truncate_row(z, V, T, top_k, top_p, out_p, margin);
+}
+
 /* ---- one draw by inverse CDF ------------------------------------------------
  * Draw from the distribution proportional to w using one uniform u: walk the
  * vocabulary in ascending index order, summing weights, and return the first
@@ -116,10 +188,26 @@ int oracle_greedy_seq(const float* target, long long row_stride, const int* draf
  * x_i with probability min(1, p(x_i)/q(x_i)); at the first rejection sample a
  * replacement from the residual proportional to max(0, p - q) and stop; if
  * all k are kept, sample one bonus token from p at position k+1.           */
-static int sample_seq(const float* target, long long ts, const float* draft, long long ds,
-                      const int* x, const float* u, double T, double l, int k, int V,
-                      int* out_tokens, int* out_num_accepted, oracle_trace* tr, int mut)
+/* p (or q) of one row: softmax(z / T), truncated when top-k or top-p is on;
+ * *margin keeps the smallest top-p boundary distance seen. */
+static int row_dist(const float* z, int V, double T, int top_k, double top_p, double* p,
+                    double* margin)
 {
+    if ((top_k <= 0 || top_k >= V) && top_p >= 1.0) return softmax_row(z, V, T, p);
+    double m = 1.0;
+    int rc = truncate_row(z, V, T, top_k, top_p, p, &m);
+    if (m < *margin) *margin = m;
+    return rc;
+}
+
+static int sample_seq(const float* target, long long ts, const float* draft, long long ds,
+                      const int* x, const float* u, double T, double l, int top_k, double top_p,
+                      int k, int V, int* out_tokens, int* out_num_accepted, oracle_trace* tr,
+                      int mut, double* trunc_margin)
+{
+    double margin_local = 1.0;
+    if (!trunc_margin) trunc_margin = &margin_local;
+    *trunc_margin = 1.0;
     if (!target || !draft || !x || !u || !out_tokens || !out_num_accepted) return -1;
     if (k < 1 || k > ORACLE_MAX_K || V < 1 || ts < V || ds < V) return -1;
     if (!(T > 0.0) || !isfinite(T)) return -1;
@@ -138,8 +226,8 @@ static int sample_seq(const float* target, long long ts, const float* draft, lon
     int rc = 0;
     const double u_sample = (double)u[k];
     for (int i = 0; i < k; ++i) {
-        if ((rc = softmax_row(target + (long long)i * ts, V, T, p)) != 0) goto done;
-        if ((rc = softmax_row(draft + (long long)i * ds, V, T, q)) != 0) goto done;
+        if ((rc = row_dist(target + (long long)i * ts, V, T, top_k, top_p, p, trunc_margin)) != 0) goto done;
+        if ((rc = row_dist(draft + (long long)i * ds, V, T, top_k, top_p, q, trunc_margin)) != 0) goto done;
 
         const int tok = x[i];
         const int valid = tok >= 0 && tok < V;
@@ -199,9 +287,9 @@ static int sample_seq(const float* target, long long ts, const float* draft, lon
 
     /* every draft kept: one bonus token from p at position k+1 */
     if (mut == ORACLE_MUT_BONUS_FROM_Q) {
-        if ((rc = softmax_row(draft + (long long)(k - 1) * ds, V, T, p)) != 0) goto done;
+        if ((rc = row_dist(draft + (long long)(k - 1) * ds, V, T, top_k, top_p, p, trunc_margin)) != 0) goto done;
     } else {
-        if ((rc = softmax_row(target + (long long)k * ts, V, T, p)) != 0) goto done;
+        if ((rc = row_dist(target + (long long)k * ts, V, T, top_k, top_p, p, trunc_margin)) != 0) goto done;
     }
     {
         int t_star = inverse_cdf(p, V, u_sample, &tr->sample_total, &tr->sample_lo, &tr->sample_hi);
@@ -232,8 +320,8 @@ int oracle_sample_seq(const float* target, long long target_row_stride,
                       oracle_trace* trace)
 {
     return sample_seq(target, target_row_stride, draft, draft_row_stride, draft_tokens,
-                      uniforms, temperature, 1.0, k, V, out_tokens, out_num_accepted, trace,
-                      ORACLE_MUT_NONE);
+                      uniforms, temperature, 1.0, 0, 1.0, k, V, out_tokens, out_num_accepted, trace,
+                      ORACLE_MUT_NONE, NULL);
 }
 
 int oracle_sample_seq_mutant(const float* target, long long target_row_stride,
@@ -243,8 +331,8 @@ int oracle_sample_seq_mutant(const float* target, long long target_row_stride,
                              oracle_trace* trace, int mutation)
 {
     return sample_seq(target, target_row_stride, draft, draft_row_stride, draft_tokens,
-                      uniforms, temperature, 1.0, k, V, out_tokens, out_num_accepted, trace,
-                      mutation);
+                      uniforms, temperature, 1.0, 0, 1.0, k, V, out_tokens, out_num_accepted, trace,
+                      mutation, NULL);
 }
 
 /* p_i(x_i), q_i(x_i) at every draft position: the quantities whose ratio the
@@ -375,9 +463,9 @@ int oracle_sample(const float* target, long long ts, const float* draft, long lo
     for (int b = 0; b < B; ++b) {
         int rc = sample_seq(target + (long long)b * (k + 1) * ts, ts,
                             draft + (long long)b * k * ds, ds,
-                            x + (long long)b * k, u + (long long)b * (k + 1), T, 1.0, k, V,
+                            x + (long long)b * k, u + (long long)b * (k + 1), T, 1.0, 0, 1.0, k, V,
                             out_tokens + (long long)b * (k + 1), out_num_accepted + b,
-                            traces ? traces + b : NULL, mutation);
+                            traces ? traces + b : NULL, mutation, NULL);
         if (rc) return rc;
     }
     return 0;
@@ -394,9 +482,28 @@ int oracle_sample_lenient(const float* target, long long ts, const float* draft,
     for (int b = 0; b < B; ++b) {
         int rc = sample_seq(target + (long long)b * (k + 1) * ts, ts,
                             draft + (long long)b * k * ds, ds,
-                            x + (long long)b * k, u + (long long)b * (k + 1), T, l, k, V,
+                            x + (long long)b * k, u + (long long)b * (k + 1), T, l, 0, 1.0, k, V,
                             out_tokens + (long long)b * (k + 1), out_num_accepted + b,
-                            traces ? traces + b : NULL, ORACLE_MUT_NONE);
+                            traces ? traces + b : NULL, ORACLE_MUT_NONE, NULL);
+        if (rc) return rc;
+    }
+    return 0;
+}
+
+/* Truncated sampling (top-k then top-p on target and draft alike). */
+int oracle_sample_truncated(const float* target, long long ts, const float* draft, long long ds,
+                            const int* x, const float* u, double T, int top_k, double top_p,
+                            int B, int k, int V, int* out_tokens, int* out_num_accepted,
+                            oracle_trace* traces, double* trunc_margin)
+{
+    if (B < 0 || top_k < 0 || !(top_p > 0.0)) return -1;
+    for (int b = 0; b < B; ++b) {
+        int rc = sample_seq(target + (long long)b * (k + 1) * ts, ts,
+                            draft + (long long)b * k * ds, ds,
+                            x + (long long)b * k, u + (long long)b * (k + 1), T, 1.0, top_k, top_p,
+                            k, V, out_tokens + (long long)b * (k + 1), out_num_accepted + b,
+                            traces ? traces + b : NULL, ORACLE_MUT_NONE,
+                            trunc_margin ? trunc_margin + b : NULL);
         if (rc) return rc;
     }
     return 0;

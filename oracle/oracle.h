@@ -115,6 +115,33 @@ int oracle_sample_lenient(const float* target, long long target_row_stride,
                           double lenience, int B, int k, int V, int* out_tokens,
                           int* out_num_accepted, oracle_trace* traces);
 
+/* Sampling rule on truncated distributions: top-k then top-p applied to the
+ * target's and the draft's rows alike (the production blog, "Integration with
+ * the serving engine" and "Failure modes": a processor applied to one side
+ * and not the other breaks the q the rule relies on; Ouroboros samples with
+ * top-p 0.8).  Per row, with w_t = exp(z_t/T - max):
+ *   top-k (top_k >= 1, top_k < V): keep t iff fewer than top_k tokens have a
+ *     strictly larger logit (ties at the boundary all kept);
+ *   top-p (0 < top_p < 1): among the tokens top-k kept, keep t iff the kept
+ *     tokens with strictly larger logits hold less than top_p of the kept mass
+ *     (the smallest set of top tokens reaching top_p, ties kept together);
+ *   p' = w / (sum of w over kept tokens) on kept tokens, 0 elsewhere.
+ * top_k = 0 and top_p >= 1 switch the respective step off.  The rule then
+ * runs on p' and q'.  trace->sample_* refer to p', q'.  `trunc_margin`, if
+ * not NULL, gets per sequence the smallest distance, over every row the round
+ * read, between top_p and the kept-mass fraction at either side of the top-p
+ * boundary (1 where top-p is off). */
+int oracle_sample_truncated(const float* target, long long target_row_stride,
+                            const float* draft, long long draft_row_stride,
+                            const int* draft_tokens, const float* uniforms, double temperature,
+                            int top_k, double top_p, int B, int k, int V, int* out_tokens,
+                            int* out_num_accepted, oracle_trace* traces, double* trunc_margin);
+
+/* One truncated row: p' as above (out_p[V]); returns 0 or an error. *margin as
+ * above for this row. */
+int oracle_truncated_row(const float* z, int V, double temperature, int top_k, double top_p,
+                         double* out_p, double* margin);
+
 /* Verification by-products of the greedy pass (Ouroboros section 3.4.4,
  * Eq. 10): v_i = argmax of target row i for i <= k (the target's own token at
  * every position, accepted or not), bit i of the match mask = [x_i == v_i]

@@ -618,3 +618,116 @@ def test_tree_invalid_row_index_never_matches():
     t, a, best = oracle.greedy_tree(nodes, cand, rows)
     assert (a == 2).all() and (best == 0).all()
     assert (t[:, 2] == -1).all()                        # correction from an invalid row
+
+
+# ---------------------------------------------------------------------------
+# Consistent top-k / top-p truncation of p and q (Ouroboros samples with
+# top-p 0.8; the blog requires processors to be applied to target and draft
+# alike)
+# ---------------------------------------------------------------------------
+def test_truncation_worked_examples():
+    """Hand-worked cases of the definition (top-k keeps logits >= the k-th
+    largest; top-p keeps a token when the kept mass strictly above it is below
+    top_p of the kept mass)."""
+    P = np.array([0.5, 0.3, 0.15, 0.05])
+    z = np.log(P).astype(np.float32)
+    cases = [
+        (0, 0.8, [0.625, 0.375, 0, 0]),        # 0.5 < 0.8 keeps 0.3; 0.8 is not < 0.8
+        (0, 0.81, [0.5 / 0.95, 0.3 / 0.95, 0.15 / 0.95, 0]),
+        (0, 0.5, [1, 0, 0, 0]),                # 0.5 is not < 0.5
+        (0, 0.49, [1, 0, 0, 0]),
+        (2, 1.0, [0.625, 0.375, 0, 0]),
+        (3, 1.0, [0.5 / 0.95, 0.3 / 0.95, 0.15 / 0.95, 0]),
+        (3, 0.6, [0.625, 0.375, 0, 0]),        # top-p on the top-3 mass: 0.5/0.95 < 0.6
+        (3, 0.5, [1, 0, 0, 0]),
+        (4, 1.0, list(P)),
+        (0, 1.0, list(P)),
+    ]
+    for top_k, top_p, want in cases:
+        got, _ = oracle.truncated_row(z, 1.0, top_k, top_p)
+        np.testing.assert_allclose(got, want, atol=2e-7, err_msg=f"top_k={top_k} top_p={top_p}")
+    # ties at the boundary are kept together
+    zt = np.array([1.0, 1.0, 0.0, 0.0], np.float32)
+    got, _ = oracle.truncated_row(zt, 1.0, 1, 1.0)
+    np.testing.assert_allclose(got, [0.5, 0.5, 0, 0], atol=1e-12)
+    got, _ = oracle.truncated_row(zt, 1.0, 0, 0.3)
+    np.testing.assert_allclose(got, [0.5, 0.5, 0, 0], atol=1e-12)
+    # temperature applies before truncation: T = 0.5 squares and renormalises
+    got, _ = oracle.truncated_row(z, 0.5, 0, 0.9)
+    P2 = P ** 2 / (P ** 2).sum()               # [0.7042, 0.2535, 0.0634, 0.0070]
+    np.testing.assert_allclose(got, [P2[0] / (P2[0] + P2[1]), P2[1] / (P2[0] + P2[1]), 0, 0], atol=1e-6)
+
+
+def np_truncate(P, top_k, top_p):
+    """Independent numpy statement of the truncation for probability rows."""
+    out = np.zeros_like(P)
+    for i, row in enumerate(P):
+        keep = np.ones(len(row), bool)
+        if 0 < top_k < len(row):
+            keep &= row >= np.sort(row)[::-1][top_k - 1]
+        if top_p < 1.0:
+            M = row[keep].sum()
+            above = np.array([row[keep & (row > v)].sum() for v in row])
+            keep &= above < top_p * M
+        out[i] = np.where(keep, row, 0.0) / row[keep].sum()
+    return out
+
+
+@pytest.mark.parametrize("top_k,top_p", [(3, 1.0), (0, 0.7), (5, 0.8)])
+def test_v8_truncated_law(top_k, top_p):
+    """With x drawn from the truncated draft q', every committed token follows
+    the truncated target p' exactly (the rule's guarantee, applied to p', q')."""
+    rng = np.random.default_rng(18)
+    k = 3
+    P = rng.dirichlet(np.ones(8), k + 1)
+    Q = rng.dirichlet(np.ones(8), k)
+    Pt, Qt = np_truncate(P, top_k, top_p), np_truncate(Q, top_k, top_p)
+    pr = Probe(P, Q, 1.0, oracle.MUT_NONE)
+    pr.run = lambda x, U: oracle.sample_truncated(
+        np.broadcast_to(pr.z, (U.shape[0],) + pr.z.shape).copy(),
+        np.broadcast_to(pr.y, (U.shape[0],) + pr.y.shape).copy(),
+        np.broadcast_to(np.asarray(x, np.int32), (U.shape[0], k)).copy(),
+        U.astype(np.float32), 1.0, top_k, top_p)
+    safe = [int(np.argmax(np.minimum(Pt[i], Qt[i]) + 1e-3 * (Pt[i] > 0))) for i in range(k)]
+    for i in range(k):
+        law = np.zeros(8)
+        for xv in range(8):
+            if Qt[i, xv] == 0:
+                continue
+            x = safe.copy()
+            x[i] = xv
+            base = np.zeros(k + 1)
+            a = pr.measure(x, base, i, lambda r: 1 if r is None else (r[1] > i))[0]
+            law[xv] += Qt[i, xv] * a
+            if a < 1.0:
+                base[i] = a
+                cdf = pr.measure(x, base, k, lambda r: 8 if r is None else (r[0][:, i] <= np.arange(8)))
+                law += Qt[i, xv] * (1 - a) * np.diff(np.concatenate([[0.0], cdf]))
+        np.testing.assert_allclose(law, Pt[i], atol=3e-6, err_msg=f"position {i}")
+
+
+def test_top_k_one_is_greedy():
+    rng = np.random.default_rng(19)
+    n, k, V = 300, 4, 50
+    z = rng.normal(0, 1, (n, k + 1, V)).astype(np.float32)
+    y = (z[:, :k] + rng.normal(0, 1, (n, k, V))).astype(np.float32)
+    x = np.argmax(y, axis=2).astype(np.int32)          # the truncated draft's only token
+    u = u24(rng, (n, k + 1))
+    ts, ns = oracle.sample_truncated(z, y, x, u, 1.0, top_k=1)
+    tg, ng = oracle.greedy(z, x)
+    np.testing.assert_array_equal(ns, ng)
+    np.testing.assert_array_equal(ts, tg)
+
+
+def test_truncation_off_is_the_rule():
+    rng = np.random.default_rng(20)
+    n, k, V = 200, 5, 40
+    z = rng.normal(0, 2, (n, k + 1, V)).astype(np.float32)
+    y = (z[:, :k] + rng.normal(0, 1, (n, k, V))).astype(np.float32)
+    x = rng.integers(0, V, (n, k)).astype(np.int32)
+    u = u24(rng, (n, k + 1))
+    t1, n1 = oracle.sample(z, y, x, u, 0.8)
+    for top_k, top_p in ((0, 1.0), (V, 1.0), (V + 5, 2.0)):
+        t2, n2 = oracle.sample_truncated(z, y, x, u, 0.8, top_k, top_p)
+        np.testing.assert_array_equal(t1, t2)
+        np.testing.assert_array_equal(n1, n2)
