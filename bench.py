@@ -60,13 +60,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--mode", default="sample",
                     choices=["sample", "greedy", "candidates", "greedy_ext", "lenient", "candidates_ext",
-                             "tree", "sample_lazy", "greedy_lazy"],
+                             "tree", "sample_lazy", "greedy_lazy", "truncated"],
                     help="sample: workload 5 (the benchmark line); greedy / greedy_ext: workload 5 "
                          "greedy (ext: with the #Match by-products); lenient: workload 5 sampling "
                          "with --lenience; candidates / candidates_ext: workload 4; tree: workload 4 "
                          "with shared rows stored once; sample_lazy / greedy_lazy: workload 5 with "
-                         "early exit")
+                         "early exit; truncated: workload 5 sampling on top-k / top-p truncated "
+                         "rows (--top-k, --top-p)")
     ap.add_argument("--lenience", type=float, default=2.0)
+    ap.add_argument("--top-k", type=int, default=50)
+    ap.add_argument("--top-p", type=float, default=0.8)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU oracle baseline budget (0 disables it)")
     ap.add_argument("--profile-every", type=int, default=5,
@@ -155,6 +158,16 @@ def main():
                                   workspace=ws)
             stats_rows = B * (2 * k + 1)
             workload = f"spec_verify_sample_lenient B={B} k={k} V={V} bf16 T={w.T} l={args.lenience}"
+        elif args.mode == "truncated":
+            ws = torch.empty(sv.workspace_bytes(B, 2 * k + 1, V, w.target.dtype), dtype=torch.uint8,
+                             device=dev)
+
+            def step():
+                sv.sample_truncated(w.target, w.draft, w.tokens, w.uniforms, w.T, args.top_k,
+                                    args.top_p, workspace=ws)
+            stats_rows = B * (2 * k + 1)
+            workload = (f"spec_verify_sample_truncated B={B} k={k} V={V} bf16 T={w.T} "
+                        f"top_k={args.top_k} top_p={args.top_p}")
         elif args.mode == "sample_lazy":
             ws = torch.empty(sv.workspace_bytes(B, 2 * k + 1, V, w.target.dtype), dtype=torch.uint8,
                              device=dev)
@@ -249,9 +262,13 @@ def main():
             "device": torch.cuda.get_device_name(0),
         },
         "roofline": None if lazy else {
-            "kernel": "k_softmax_stats" if args.mode in ("sample", "lenient") else "k_argmax_stats",
-            "note": ("rows counts every scored candidate position (B*C*R); the kernel reads "
-                     "B*N unique node rows") if args.mode == "tree" else None,
+            "kernel": {"sample": "k_softmax_stats", "lenient": "k_softmax_stats",
+                       "truncated": "k_trunc_rows"}.get(args.mode, "k_argmax_stats"),
+            "note": ("algorithmic bytes count one read of every row; the kernel streams each "
+                     "row once per selection pass (the later passes mostly from cache)")
+            if args.mode == "truncated" else (
+                "rows counts every scored candidate position (B*C*R); the kernel reads "
+                "B*N unique node rows") if args.mode == "tree" else None,
             "bound": "hbm",
             "achieved": achieved,
             "peak": PEAK_HBM_GBS,

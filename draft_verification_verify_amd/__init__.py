@@ -64,6 +64,9 @@ def lib():
         L.spec_verify_sample_lazy.restype = I
         L.spec_verify_greedy_lazy.argtypes = [P, LL, P, I, I, I, I, P, P, P, SZ, P]
         L.spec_verify_greedy_lazy.restype = I
+        L.spec_verify_sample_truncated.argtypes = [P, LL, P, LL, P, P, F, I, F, I, I, I, I, P, P, P,
+                                                   P, P, SZ, P]
+        L.spec_verify_sample_truncated.restype = I
         L.spec_verify_profile_begin.argtypes = [I, I]
         L.spec_verify_profile_begin.restype = I
         L.spec_verify_profile_end.argtypes = [P, I]
@@ -77,7 +80,7 @@ EXPORTED = (
     "spec_verify_greedy", "spec_verify_sample", "spec_verify_greedy_candidates",
     "spec_verify_greedy_ext", "spec_verify_sample_lenient", "spec_verify_greedy_candidates_ext",
     "spec_verify_greedy_tree", "spec_verify_sample_lazy", "spec_verify_greedy_lazy",
-    "spec_verify_profile_begin", "spec_verify_profile_end",
+    "spec_verify_profile_begin", "spec_verify_profile_end", "spec_verify_sample_truncated",
 )
 
 
@@ -228,6 +231,32 @@ def sample_lenient(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torc
                                           _stream(stream))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_sample_lenient")
+    if return_probs:
+        return out_tokens, out_na, out_p_x, out_q_x
+    return out_tokens, out_na
+
+
+def sample_truncated(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
+                     uniforms: torch.Tensor, temperature: float, top_k: int = 0, top_p: float = 1.0,
+                     *, return_probs: bool = False, workspace=None, stream=None):
+    """Sampling verification on top-k / top-p truncated target and draft rows
+    (top_k = 0 and top_p >= 1 switch the steps off)."""
+    B, k1, V = target.shape
+    k = k1 - 1
+    dev = target.device
+    out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
+    out_na = torch.empty((B,), dtype=torch.int32, device=dev)
+    out_p_x = torch.empty((B, k), dtype=torch.float32, device=dev) if return_probs else None
+    out_q_x = torch.empty((B, k), dtype=torch.float32, device=dev) if return_probs else None
+    ws = _workspace(workspace, B, 2 * k + 1, V, target.dtype, dev)
+    st = lib().spec_verify_sample_truncated(_ptr(target), _check_rows(target, 2), _ptr(draft),
+                                            _check_rows(draft, 2), _ptr(draft_tokens),
+                                            _ptr(uniforms), float(temperature), int(top_k),
+                                            float(top_p), B, k, V, _DTYPE[target.dtype],
+                                            _ptr(out_tokens), _ptr(out_na), _ptr(out_p_x),
+                                            _ptr(out_q_x), _ptr(ws), ws.numel(), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_sample_truncated")
     if return_probs:
         return out_tokens, out_na, out_p_x, out_q_x
     return out_tokens, out_na

@@ -34,6 +34,7 @@ SOURCES = {
     "sv_stats.hip": ["-fno-honor-nans"],
     "sv_decide.hip": [],
     "sv_sample.hip": [],
+    "sv_trunc.hip": [],
     "sv_api.hip": [],
 }
 

@@ -14,6 +14,7 @@ using namespace sv;
 namespace {
 
 constexpr int kMaxV = 1 << 28;
+constexpr int kMaxTruncV = 1 << 23;    // truncated rows: fixed-point masses of 2^-40 fit 63 bits
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -81,6 +82,7 @@ SamplePlan plan_sample(int B, int nvec)
 
 struct Workspace {
     void* partials;
+    TruncRow* trunc;                   // truncated sampling: one per row
     SampleDesc* desc;
     float* chunk_sums;
     int* lists;                        // early exit: two lists of B sequence ids
@@ -88,8 +90,8 @@ struct Workspace {
     size_t bytes;
 };
 
-// Layout: [split partials][sample descriptors][chunk totals][work lists]
-// [counters], each region 256-byte aligned.
+// Layout: [split partials][truncated rows][sample descriptors][chunk totals]
+// [work lists][counters], each region 256-byte aligned.
 Workspace layout(char* base, int B, long long rows, int V)
 {
     Workspace w;
@@ -98,6 +100,8 @@ Workspace layout(char* base, int B, long long rows, int V)
     size_t off = 0;
     w.partials = base ? base + off : nullptr;
     off += align_up((size_t)rows * sp.splits * 8);
+    w.trunc = base ? reinterpret_cast<TruncRow*>(base + off) : nullptr;
+    off += align_up((size_t)rows * sizeof(TruncRow));
     w.desc = base ? reinterpret_cast<SampleDesc*>(base + off) : nullptr;
     off += align_up((size_t)B * sizeof(SampleDesc));
     w.chunk_sums = base ? reinterpret_cast<float*>(base + off) : nullptr;
@@ -203,7 +207,7 @@ int greedy_impl(const void* target_logits, long long target_row_stride,
 int sample_impl(const void* target_logits, long long target_row_stride,
                 const void* draft_logits, long long draft_row_stride,
                 const int* draft_tokens, const float* uniforms, float temperature,
-                float lenience, int B, int k, int V, int dtype,
+                float lenience, int top_k, float top_p, int B, int k, int V, int dtype,
                 int* out_tokens, int* out_num_accepted,
                 float* out_p_x, float* out_q_x,
                 void* workspace, size_t workspace_bytes, void* hip_stream)
@@ -216,6 +220,9 @@ int sample_impl(const void* target_logits, long long target_row_stride,
     if (target_row_stride < V || draft_row_stride < V) return SV_EINVAL;
     if (!(temperature > 0.f) || !isfinite(temperature)) return SV_EINVAL;
     if (!(lenience >= 1.f) || !isfinite(lenience)) return SV_EINVAL;
+    if (top_k < 0 || !(top_p > 0.f) || isnan(top_p)) return SV_EINVAL;
+    const bool trunc = (top_k >= 1 && top_k < V) || top_p < 1.f;
+    if (trunc && V > kMaxTruncV) return SV_EINVAL;
     const double cd = 1.4426950408889634 / (double)temperature;
     if (!isfinite(cd) || cd > 3.0e38) return SV_EINVAL;
     const long long rows = (long long)B * (2 * k + 1);
@@ -242,7 +249,23 @@ int sample_impl(const void* target_logits, long long target_row_stride,
     sa.c = c;
     sa.partials = w.partials;
     prof_begin(st);
-    if (launch_softmax_stats(dtype, vec, sa, st) != hipSuccess) return SV_EHIP;
+    if (trunc) {
+        TruncArgs ta;
+        ta.target = target_logits;
+        ta.t_stride = target_row_stride;
+        ta.draft = draft_logits;
+        ta.d_stride = draft_row_stride;
+        ta.n_target_rows = B * (k + 1);
+        ta.n_rows = (int)rows;
+        ta.V = V;
+        ta.c = c;
+        ta.top_k = top_k;
+        ta.top_p = top_p;
+        ta.rows = w.trunc;
+        if (launch_trunc_rows(dtype, vec, ta, st) != hipSuccess) return SV_EHIP;
+    } else {
+        if (launch_softmax_stats(dtype, vec, sa, st) != hipSuccess) return SV_EHIP;
+    }
     prof_end(st);
 
     DecideSampleArgs da;
@@ -259,6 +282,7 @@ int sample_impl(const void* target_logits, long long target_row_stride,
     da.c = c;
     da.log2_lenience = (float)log2((double)lenience);
     da.partials = static_cast<const SoftPartial*>(w.partials);
+    da.trunc = trunc ? w.trunc : nullptr;
     da.out_tokens = out_tokens;
     da.out_num_accepted = out_num_accepted;
     da.out_p_x = out_p_x;
@@ -285,7 +309,7 @@ int sample_impl(const void* target_logits, long long target_row_stride,
     ma.out_row = k + 1;
     ma.n_target_rows = B * (k + 1);
     ma.n_draft_rows = B * k;
-    if (launch_sample(dtype, vec, B, ma, st) != hipSuccess) return SV_EHIP;
+    if (launch_sample(dtype, vec, trunc, B, ma, st) != hipSuccess) return SV_EHIP;
     return SV_OK;
 }
 
@@ -457,7 +481,7 @@ int spec_verify_sample(const void* target_logits, long long target_row_stride,
                        void* workspace, size_t workspace_bytes, void* hip_stream)
 {
     return sample_impl(target_logits, target_row_stride, draft_logits, draft_row_stride,
-                       draft_tokens, uniforms, temperature, 1.f, B, k, V, dtype, out_tokens,
+                       draft_tokens, uniforms, temperature, 1.f, 0, 1.f, B, k, V, dtype, out_tokens,
                        out_num_accepted, out_p_x, out_q_x, workspace, workspace_bytes, hip_stream);
 }
 
@@ -470,8 +494,22 @@ int spec_verify_sample_lenient(const void* target_logits, long long target_row_s
                                void* workspace, size_t workspace_bytes, void* hip_stream)
 {
     return sample_impl(target_logits, target_row_stride, draft_logits, draft_row_stride,
-                       draft_tokens, uniforms, temperature, lenience, B, k, V, dtype, out_tokens,
+                       draft_tokens, uniforms, temperature, lenience, 0, 1.f, B, k, V, dtype, out_tokens,
                        out_num_accepted, out_p_x, out_q_x, workspace, workspace_bytes, hip_stream);
+}
+
+int spec_verify_sample_truncated(const void* target_logits, long long target_row_stride,
+                                 const void* draft_logits, long long draft_row_stride,
+                                 const int* draft_tokens, const float* uniforms, float temperature,
+                                 int top_k, float top_p, int B, int k, int V, int dtype,
+                                 int* out_tokens, int* out_num_accepted,
+                                 float* out_p_x, float* out_q_x,
+                                 void* workspace, size_t workspace_bytes, void* hip_stream)
+{
+    return sample_impl(target_logits, target_row_stride, draft_logits, draft_row_stride,
+                       draft_tokens, uniforms, temperature, 1.f, top_k, top_p, B, k, V, dtype,
+                       out_tokens, out_num_accepted, out_p_x, out_q_x, workspace, workspace_bytes,
+                       hip_stream);
 }
 
 int spec_verify_greedy_candidates(const void* target_logits, long long row_stride,
@@ -547,6 +585,7 @@ int spec_verify_sample_lazy(const void* target_logits, long long target_row_stri
     da.c = c;
     da.log2_lenience = 0.f;
     da.partials = static_cast<const SoftPartial*>(w.partials);
+    da.trunc = nullptr;
     da.out_tokens = out_tokens;
     da.out_num_accepted = out_num_accepted;
     da.out_p_x = nullptr;
@@ -582,7 +621,7 @@ int spec_verify_sample_lazy(const void* target_logits, long long target_row_stri
     ma.out_row = k + 1;
     ma.n_target_rows = B * (k + 1);
     ma.n_draft_rows = B * k;
-    if (launch_sample(dtype, vec, B, ma, st) != hipSuccess) return SV_EHIP;
+    if (launch_sample(dtype, vec, false, B, ma, st) != hipSuccess) return SV_EHIP;
     return SV_OK;
 }
 

@@ -12,22 +12,6 @@ namespace sv {
 
 constexpr int kSeqPerBlock = kBlock / 64;
 
-__device__ __forceinline__ void merge_soft(const SoftPartial* p, int splits, float c, float& m, float& s)
-{
-    m = p[0].m;
-    s = p[0].s;
-    for (int i = 1; i < splits; ++i) {
-        const float m2 = p[i].m, s2 = p[i].s;
-        const float mn = fmaxf(m, m2);
-        if (mn == -INFINITY) {
-            s = 0.f;
-        } else {
-            s = s * exp2f((m - mn) * c) + s2 * exp2f((m2 - mn) * c);
-        }
-        m = mn;
-    }
-}
-
 // Larger value wins; equal values keep the smaller index.  An all -inf row
 // has index INT32_MAX in every split and maps to 0.
 __device__ __forceinline__ int merge_arg(const ArgPartial* p, int splits)
@@ -55,11 +39,38 @@ __device__ __forceinline__ unsigned long long ballot64(bool pred)
 // taken in the log domain so that no probability underflows: accept iff
 // log q <= log p + log l (ratio >= 1, and q = 0) or u < exp2(log p + log l -
 // log q).  Lenience l (Cascade Speculative Drafting, review function) is 1
-// for the exact rule, where log l = 0 leaves the test unchanged.
+// for the exact rule, where log l = 0 leaves the test unchanged.  With
+// truncation, s is the kept mass and a token below the row's key threshold
+// has p = 0 (log p = -inf).
+
+// A row's normaliser: max m, l2s = log2 of the (kept) mass relative to
+// exp2(m * c), and the key threshold (0 keeps every token).
+struct RowNorm {
+    float m, l2s;
+    uint32_t tau;
+};
+
+__device__ __forceinline__ RowNorm row_norm(const DecideSampleArgs& a, long long row)
+{
+    RowNorm r;
+    if (a.trunc) {
+        const TruncRow t = a.trunc[row];
+        r.m = t.m;
+        r.l2s = t.l2s;
+        r.tau = t.tau;
+    } else {
+        float s;
+        merge_soft(a.partials + row * a.splits, a.splits, a.c, r.m, s);
+        r.l2s = log2f(s);
+        r.tau = 0u;
+    }
+    return r;
+}
 
 // The statistics of target row (b, pos) and, for pos < k, the decision at pos.
 struct PosSample {
-    float mt, st, md, sd, px, qx;
+    RowNorm t, d;
+    float px, qx;
     int x;
     bool reject;
 };
@@ -71,25 +82,24 @@ __device__ __forceinline__ PosSample sample_position(const DecideSampleArgs& a, 
     const int k = a.k;
     const float c = a.c;
     PosSample r;
-    r.md = -INFINITY;
-    r.sd = 0.f;
+    r.d = RowNorm{-INFINITY, -INFINITY, 0u};
     r.px = 0.f;
     r.qx = 0.f;
     r.x = -1;
     r.reject = false;
     const int tr = b * (k + 1) + pos;
-    merge_soft(a.partials + (long long)tr * a.splits, a.splits, c, r.mt, r.st);
+    r.t = row_norm(a, tr);
     if (pos < k) {
         const int nT = a.B * (k + 1);
         const int dr = b * k + pos;
-        merge_soft(a.partials + (long long)(nT + dr) * a.splits, a.splits, c, r.md, r.sd);
+        r.d = row_norm(a, nT + dr);
         r.x = a.tokens[(long long)b * k + pos];
         const bool valid = r.x >= 0 && r.x < a.V;
         if (valid) {
             const float zx = load_elem<DT>(row_ptr(a.target, tr, a.t_stride, ES), r.x);
             const float yx = load_elem<DT>(row_ptr(a.draft, dr, a.d_stride, ES), r.x);
-            const float lp = (zx - r.mt) * c - log2f(r.st);
-            const float lq = (yx - r.md) * c - log2f(r.sd);
+            const float lp = key_of<DT>(zx) >= r.t.tau ? (zx - r.t.m) * c - r.t.l2s : -INFINITY;
+            const float lq = key_of<DT>(yx) >= r.d.tau ? (yx - r.d.m) * c - r.d.l2s : -INFINITY;
             const float u = a.uniforms[(long long)b * (k + 1) + pos];
             const float lpl = lp + a.log2_lenience;
             const bool accept = (lq <= lpl) || (u < exp2f(lpl - lq));
@@ -112,9 +122,11 @@ __device__ __forceinline__ void write_desc(const DecideSampleArgs& a, int b, int
     d.d_row = j < k ? b * k + j : -1;
     d.out_pos = j;
     d.kind = j < k ? 0 : 1;
-    d.off_t = r.mt * a.c + log2f(r.st);
-    d.off_d = j < k ? r.md * a.c + log2f(r.sd) : 0.f;
+    d.off_t = r.t.m * a.c + r.t.l2s;
+    d.off_d = j < k ? r.d.m * a.c + r.d.l2s : 0.f;
     d.u = a.uniforms[(long long)b * (k + 1) + k];
+    d.tau_t = r.t.tau;
+    d.tau_d = j < k ? r.d.tau : 0u;
     d.pad = 0;
     a.desc[b] = d;
     a.out_num_accepted[b] = j;

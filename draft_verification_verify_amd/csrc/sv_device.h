@@ -70,6 +70,25 @@ __device__ __forceinline__ Raw<DT> load_raw(const char* row, int v)
     return r;
 }
 
+// The same with ordinary (cached) loads, for rows that are read again soon.
+template <int DT, bool VEC>
+__device__ __forceinline__ Raw<DT> load_raw_cached(const char* row, int v)
+{
+    if constexpr (VEC) {
+        Raw<DT> r;
+        if constexpr (DT == DT_F32) {
+            const u32x4* p = reinterpret_cast<const u32x4*>(row) + 2 * v;
+            r.a = p[0];
+            r.b = p[1];
+        } else {
+            r.a = reinterpret_cast<const u32x4*>(row)[v];
+        }
+        return r;
+    } else {
+        return load_raw<DT, false>(row, v);
+    }
+}
+
 template <int DT>
 __device__ __forceinline__ void decode(const Raw<DT>& r, float* e)
 {
@@ -114,6 +133,46 @@ __device__ __forceinline__ void load8(const char* row, int v, int nfull, int V, 
 __device__ __forceinline__ const char* row_ptr(const void* base, long long row, long long stride, int es)
 {
     return reinterpret_cast<const char*>(base) + row * stride * es;
+}
+
+// ---- ordering keys -----------------------------------------------------------
+// An unsigned key that orders like the logit: equal logits share a key
+// (-0.0 is mapped to +0.0), larger logits get larger keys.  16-bit formats
+// use their own 16 bits, fp32 its 32.  NaN is outside the contract.
+template <int DT>
+__device__ __forceinline__ uint32_t key_of(float v)
+{
+    if constexpr (DT == DT_F32) {
+        uint32_t u = __float_as_uint(v);
+        u = (u == 0x80000000u) ? 0u : u;
+        return (u >> 31) ? ~u : (u | 0x80000000u);
+    } else {
+        uint32_t u;
+        if constexpr (DT == DT_BF16) {
+            u = __float_as_uint(v) >> 16;
+        } else {
+            u = __builtin_bit_cast(unsigned short, (_Float16)v);
+        }
+        u = (u == 0x8000u) ? 0u : u;
+        return (u >> 15) ? (~u & 0xffffu) : (u | 0x8000u);
+    }
+}
+
+// The merged (max, sum of exp2) of a row from its slice partials, in slice order.
+__device__ __forceinline__ void merge_soft(const SoftPartial* p, int splits, float c, float& m, float& s)
+{
+    m = p[0].m;
+    s = p[0].s;
+    for (int i = 1; i < splits; ++i) {
+        const float m2 = p[i].m, s2 = p[i].s;
+        const float mn = fmaxf(m, m2);
+        if (mn == -INFINITY) {
+            s = 0.f;
+        } else {
+            s = s * exp2f((m - mn) * c) + s2 * exp2f((m2 - mn) * c);
+        }
+        m = mn;
+    }
 }
 
 // ---- fixed-order workgroup collectives -------------------------------------

@@ -55,7 +55,36 @@ struct SampleDesc {
     float off_t;
     float off_d;
     float u;
+    uint32_t tau_t;                    // truncation: keep z with key >= tau_t (0: keep all)
+    uint32_t tau_d;
     int pad;
+};
+
+// A truncated row (top-k, then top-p): its max m, log2 of the kept mass
+// relative to exp2(m * c), and the smallest kept ordering key (key_of in
+// sv_device.h): token t keeps p'(t) = exp2((z_t - m) * c - l2s) iff
+// key(z_t) >= tau, else 0.
+struct TruncRow {
+    float m;
+    float l2s;
+    uint32_t tau;
+    uint32_t pad;
+};
+
+// Truncation of every row of a batch (sv_trunc.hip), rows numbered as in
+// StatsArgs.  top_k in [1, V) or 0 (off); top_p in (0, 1), or >= 1 (off).
+struct TruncArgs {
+    const void* target;
+    long long t_stride;
+    const void* draft;
+    long long d_stride;
+    int n_target_rows;
+    int n_rows;
+    int V;
+    float c;
+    int top_k;
+    float top_p;
+    TruncRow* rows;
 };
 
 struct DecideSampleArgs {
@@ -69,6 +98,7 @@ struct DecideSampleArgs {
     float c;
     float log2_lenience;               // log2 l, 0 for the exact rule (l = 1)
     const SoftPartial* partials;       // target rows then draft rows
+    const TruncRow* trunc;             // truncated rows (same numbering) or null
     int* out_tokens;                   // [B][k+1]
     int* out_num_accepted;             // [B]
     float* out_p_x;                    // [B][k] or null
@@ -153,7 +183,8 @@ hipError_t launch_argmax_stats(int dt, bool vec, const StatsArgs& a, hipStream_t
 hipError_t launch_decide_sample(int dt, const DecideSampleArgs& a, hipStream_t st);
 hipError_t launch_decide_greedy(const DecideGreedyArgs& a, hipStream_t st);
 hipError_t launch_decide_candidates(const DecideCandArgs& a, hipStream_t st);
-hipError_t launch_sample(int dt, bool vec, int B, const SampleArgs& a, hipStream_t st);
+hipError_t launch_sample(int dt, bool vec, bool mask, int B, const SampleArgs& a, hipStream_t st);
+hipError_t launch_trunc_rows(int dt, bool vec, const TruncArgs& a, hipStream_t st);
 hipError_t launch_lazy_stats(int dt, bool vec, bool soft, int grid, const LazyArgs& a, hipStream_t st);
 hipError_t launch_lazy_decide_sample(int dt, const LazyArgs& l, const DecideSampleArgs& a, hipStream_t st);
 hipError_t launch_lazy_decide_greedy(const LazyArgs& l, const DecideGreedyArgs& a, hipStream_t st);

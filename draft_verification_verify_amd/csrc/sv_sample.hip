@@ -24,25 +24,30 @@ namespace sv {
 
 // The weight arithmetic, shared by every pass: the residual
 // max(0, p - q) (kind 0) or p (otherwise), each exp2(z*c - off) with off the
-// row's log2 normaliser, so both are normalised probabilities.
-__device__ __forceinline__ float weight_of(float ez, float ey, int kind, float c, float off_t, float off_d)
+// row's log2 normaliser, so both are normalised probabilities.  MASK: the
+// rows are truncated, and a logit whose key is below its row's threshold has
+// probability 0.
+template <int DT, bool MASK>
+__device__ __forceinline__ float weight_of(float ez, float ey, int kind, float c, const SampleDesc& d)
 {
-    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(ez, c, -off_t));
+    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(ez, c, -d.off_t));
+    if (MASK && key_of<DT>(ez) < d.tau_t) p = 0.f;
     if (kind != 0) return p;
-    const float q = __builtin_amdgcn_exp2f(__builtin_fmaf(ey, c, -off_d));
+    float q = __builtin_amdgcn_exp2f(__builtin_fmaf(ey, c, -d.off_d));
+    if (MASK && key_of<DT>(ey) < d.tau_d) q = 0.f;
     return fmaxf(p - q, 0.f);
 }
 
 // Weights of logical vector v (0 past the row's end).
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool MASK>
 __device__ __forceinline__ void weights8(const char* zr, const char* yr, int v, int nfull, int V,
-                                         int kind, float c, float off_t, float off_d, float* w)
+                                         int kind, float c, const SampleDesc& d, float* w)
 {
     float ez[kVec], ey[kVec];
     load8<DT, VEC>(zr, v, nfull, V, -INFINITY, ez);
     if (kind == 0) load8<DT, VEC>(yr, v, nfull, V, -INFINITY, ey);
 #pragma unroll
-    for (int j = 0; j < kVec; ++j) w[j] = weight_of(ez[j], kind == 0 ? ey[j] : 0.f, kind, c, off_t, off_d);
+    for (int j = 0; j < kVec; ++j) w[j] = weight_of<DT, MASK>(ez[j], kind == 0 ? ey[j] : 0.f, kind, c, d);
 }
 
 __device__ __forceinline__ float sum8(const float* w)
@@ -54,9 +59,9 @@ __device__ __forceinline__ float sum8(const float* w)
 }
 
 // Total weight of chunk [c0, c1), one round (kBlock vectors) at a time.
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool MASK>
 __device__ float chunk_total(const SampleArgs& a, const char* zr, const char* yr, int kind,
-                             float off_t, float off_d, int c0, int c1, float* lds)
+                             const SampleDesc& d, int c0, int c1, float* lds)
 {
     const int nfull = a.V >> 3;
     float total = 0.f;
@@ -65,7 +70,7 @@ __device__ float chunk_total(const SampleArgs& a, const char* zr, const char* yr
         float ts = 0.f;
         if (v < c1) {
             float w[kVec];
-            weights8<DT, VEC>(zr, yr, v, nfull, a.V, kind, a.c, off_t, off_d, w);
+            weights8<DT, VEC, MASK>(zr, yr, v, nfull, a.V, kind, a.c, d, w);
             ts = sum8(w);
         }
         float ex, rt;
@@ -83,9 +88,9 @@ __device__ float chunk_total(const SampleArgs& a, const char* zr, const char* yr
 // positive token; if the crossing thread holds no positive weight, the
 // nearest positive token of the round before it, else after it.  Returns -1
 // only for a chunk without positive weight.
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool MASK>
 __device__ int chunk_pick(const SampleArgs& a, const char* zr, const char* yr, int kind,
-                          float off_t, float off_d, int c0, int c1, float rem,
+                          const SampleDesc& d, int c0, int c1, float rem,
                           float* lds, int* ilds)
 {
     const int nfull = a.V >> 3;
@@ -97,7 +102,7 @@ __device__ int chunk_pick(const SampleArgs& a, const char* zr, const char* yr, i
         float ts = 0.f;
         int firstpos = -1, lastpos = -1;
         if (v < c1) {
-            weights8<DT, VEC>(zr, yr, v, nfull, a.V, kind, a.c, off_t, off_d, w);
+            weights8<DT, VEC, MASK>(zr, yr, v, nfull, a.V, kind, a.c, d, w);
 #pragma unroll
             for (int j = 0; j < kVec; ++j) {
                 ts += w[j];
@@ -165,7 +170,7 @@ __device__ __forceinline__ bool desc_ok(const SampleArgs& a, const SampleDesc& d
     return true;
 }
 
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool MASK>
 __global__ __launch_bounds__(kBlock) void k_sample_chunks(SampleArgs a)
 {
     __shared__ float lds[kWaves];
@@ -212,7 +217,7 @@ __global__ __launch_bounds__(kBlock) void k_sample_chunks(SampleArgs a)
                 }
 #pragma unroll
                 for (int j = 0; j < kVec; ++j)
-                    w[j] = weight_of(ez[j], kind == 0 ? ey[j] : 0.f, kind, a.c, d.off_t, d.off_d);
+                    w[j] = weight_of<DT, MASK>(ez[j], kind == 0 ? ey[j] : 0.f, kind, a.c, d);
                 ts = sum8(w);
             }
             float ex, rt;
@@ -229,7 +234,7 @@ __global__ __launch_bounds__(kBlock) void k_sample_chunks(SampleArgs a)
 }
 
 // The draw: one workgroup per sequence.
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool MASK>
 __global__ __launch_bounds__(kBlock) void k_sample_pick(SampleArgs a)
 {
     __shared__ float lds[kWaves];
@@ -256,7 +261,7 @@ __global__ __launch_bounds__(kBlock) void k_sample_pick(SampleArgs a)
         for (int i = 0; i < a.nchunks; ++i) {
             const int e0 = i * a.vec_per_chunk;
             const int e1 = min(e0 + a.vec_per_chunk, a.nvec);
-            const float t = chunk_total<DT, VEC>(a, zr, yr, kind, d.off_t, d.off_d, e0, e1, lds);
+            const float t = chunk_total<DT, VEC, MASK>(a, zr, yr, kind, d, e0, e1, lds);
             if (threadIdx.x == 0) s_sums[i] = t;
         }
         __syncthreads();
@@ -288,30 +293,37 @@ __global__ __launch_bounds__(kBlock) void k_sample_pick(SampleArgs a)
     const int cs = s_chunk;
     const int e0 = cs * a.vec_per_chunk;
     const int e1 = min(e0 + a.vec_per_chunk, a.nvec);
-    int tok = chunk_pick<DT, VEC>(a, zr, yr, kind, d.off_t, d.off_d, e0, e1, s_rem, lds, ilds);
+    int tok = chunk_pick<DT, VEC, MASK>(a, zr, yr, kind, d, e0, e1, s_rem, lds, ilds);
     if (threadIdx.x == 0) {
         if (tok < 0 || tok >= a.V) tok = 0;    // only for inputs outside the contract
         a.out_tokens[(long long)b * a.out_row + d.out_pos] = tok;
     }
 }
 
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool MASK>
 static hipError_t launch_pair(int B, const SampleArgs& a, hipStream_t st)
 {
     void* args[] = {const_cast<SampleArgs*>(&a)};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(k_sample_chunks<DT, VEC>),
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(k_sample_chunks<DT, VEC, MASK>),
                                    dim3((unsigned)((long long)B * a.blocks_per_seq)), dim3(kBlock), args, 0, st);
     if (e != hipSuccess) return e;
-    return hipLaunchKernel(reinterpret_cast<const void*>(k_sample_pick<DT, VEC>), dim3((unsigned)B),
+    return hipLaunchKernel(reinterpret_cast<const void*>(k_sample_pick<DT, VEC, MASK>), dim3((unsigned)B),
                            dim3(kBlock), args, 0, st);
 }
 
-hipError_t launch_sample(int dt, bool vec, int B, const SampleArgs& a, hipStream_t st)
+template <int DT>
+static hipError_t launch_dt(bool vec, bool mask, int B, const SampleArgs& a, hipStream_t st)
+{
+    if (mask) return vec ? launch_pair<DT, true, true>(B, a, st) : launch_pair<DT, false, true>(B, a, st);
+    return vec ? launch_pair<DT, true, false>(B, a, st) : launch_pair<DT, false, false>(B, a, st);
+}
+
+hipError_t launch_sample(int dt, bool vec, bool mask, int B, const SampleArgs& a, hipStream_t st)
 {
     switch (dt) {
-    case DT_F32: return vec ? launch_pair<DT_F32, true>(B, a, st) : launch_pair<DT_F32, false>(B, a, st);
-    case DT_F16: return vec ? launch_pair<DT_F16, true>(B, a, st) : launch_pair<DT_F16, false>(B, a, st);
-    default:     return vec ? launch_pair<DT_BF16, true>(B, a, st) : launch_pair<DT_BF16, false>(B, a, st);
+    case DT_F32: return launch_dt<DT_F32>(vec, mask, B, a, st);
+    case DT_F16: return launch_dt<DT_F16>(vec, mask, B, a, st);
+    default:     return launch_dt<DT_BF16>(vec, mask, B, a, st);
     }
 }
 

@@ -152,6 +152,33 @@ int spec_verify_sample_lenient(const void* target_logits, long long target_row_s
                                float* out_p_x, float* out_q_x,
                                void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* Sampling verification on truncated distributions: top-k, then top-p,
+ * applied to every target row and every draft row alike (production blog,
+ * "Integration with the serving engine" and "Failure modes": a sampling
+ * processor applied to one side only breaks the q the rule relies on;
+ * Ouroboros samples with top-p 0.8).  Per row, with w_t = exp((z_t - max)/T):
+ *   top_k in [1, V): keep t iff fewer than top_k tokens have a strictly
+ *     larger logit (equal logits at the boundary all kept);
+ *   top_p in (0, 1): among the tokens top-k kept, keep t iff the kept tokens
+ *     with strictly larger logits hold less than top_p of the kept mass (the
+ *     smallest set of top logits reaching top_p, equal logits kept together);
+ *   p'(t) = w_t / (sum of w over kept tokens) on kept tokens, 0 elsewhere.
+ * The rule (spec_verify_sample) then runs on p' and q': out_p_x / out_q_x are
+ * p'_i(x_i), q'_i(x_i), the residual is max(0, p' - q') and the bonus is drawn
+ * from p'_k.  top_k = 0 or top_k >= V turns top-k off, top_p >= 1 turns top-p
+ * off; with both off the call is spec_verify_sample.  Errors: SV_EINVAL for
+ * top_k < 0, top_p <= 0 or NaN, and V > 2^23 with truncation on (kept masses
+ * are summed as 64-bit fixed-point integers, 2^-40 of the row maximum's
+ * weight, so that they are reproducible bit for bit).  Other arguments,
+ * layouts and errors as spec_verify_sample; the workspace is the same size. */
+int spec_verify_sample_truncated(const void* target_logits, long long target_row_stride,
+                                 const void* draft_logits, long long draft_row_stride,
+                                 const int* draft_tokens, const float* uniforms, float temperature,
+                                 int top_k, float top_p, int B, int k, int V, int dtype,
+                                 int* out_tokens, int* out_num_accepted,
+                                 float* out_p_x, float* out_q_x,
+                                 void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* Multi-candidate greedy verification (see the header comment).
  *   target_logits DEVICE [B][C][R][V]; row (c, i) scores candidate token (c, i).
  *                 R = L (no row after the last token: a fully accepted candidate

@@ -22,7 +22,7 @@ import dataclasses
 import numpy as np
 
 from . import (draw_interval, greedy, greedy_candidates, greedy_matches, row_argmax, sample,
-               sample_lenient, token_probs)
+               sample_lenient, sample_truncated, token_probs, truncated_row)
 
 
 @dataclasses.dataclass
@@ -31,6 +31,7 @@ class SampleReport:
     exact: int = 0
     tie_accept: int = 0
     tie_sample: int = 0
+    tie_trunc: int = 0
     failures: list = dataclasses.field(default_factory=list)
     committed: int = 0
 
@@ -39,7 +40,8 @@ class SampleReport:
 
     def summary(self):
         return (f"rounds={self.rounds} exact={self.exact} tie_accept={self.tie_accept} "
-                f"tie_sample={self.tie_sample} failures={len(self.failures)} "
+                f"tie_sample={self.tie_sample} tie_trunc={self.tie_trunc} "
+                f"failures={len(self.failures)} "
                 f"mean_committed={self.committed / max(1, self.rounds):.4f}")
 
 
@@ -128,3 +130,85 @@ def check_greedy_matches(z, x, gpu_v, gpu_mask, gpu_count):
 def check_row_argmax(z, gpu_v):
     ref = row_argmax(z)
     return np.argwhere(ref != gpu_v).tolist()
+
+
+def _truncated_interval(zrow, yrow, T, top_k, top_p, token):
+    """(lo, hi, weight) of `token` in the cumulative distribution drawn from on
+    truncated rows: max(0, p' - q') against `yrow`, or p' if yrow is None."""
+    p, _ = truncated_row(zrow, T, top_k, top_p)
+    w = p
+    if yrow is not None:
+        q, _ = truncated_row(yrow, T, top_k, top_p)
+        w = np.maximum(p - q, 0.0)
+        if not w.sum() > 0:
+            w = p
+    cum = np.cumsum(w)
+    S = cum[-1]
+    lo = (cum[token] - w[token]) / S
+    return lo, cum[token] / S, w[token]
+
+
+def check_sample_truncated(z, y, x, u, T, top_k, top_p, gpu_tokens, gpu_nacc, eps=1e-5,
+                           eps_trunc=1e-5, report=None) -> SampleReport:
+    """As check_sample, on top-k / top-p truncated rows.  A round in which some
+    row's top-p boundary lies within eps_trunc of top_p (the oracle's
+    trunc_margin) may keep a different set on the GPU: it is counted as
+    tie_trunc and checked for validity only (accepted drafts, padding)."""
+    rep = report or SampleReport()
+    ot, on, tr, margin = sample_truncated(z, y, x, u, T, top_k, top_p, traces=True)
+    B, k1 = ot.shape
+    k = k1 - 1
+    for b in range(B):
+        rep.rounds += 1
+        rep.committed += int(gpu_nacc[b]) + 1
+        gt, gn = gpu_tokens[b], int(gpu_nacc[b])
+        if gn == on[b] and (gt == ot[b]).all():
+            rep.exact += 1
+            continue
+        if not (0 <= gn <= k) or (gt[gn + 1:] != -1).any() or not (gt[:gn] == x[b, :gn]).all():
+            rep.failures.append((b, "invalid round", gt.tolist(), ot[b].tolist()))
+            continue
+        if margin[b] < eps_trunc:
+            rep.tie_trunc += 1
+            continue
+        t = tr[b]
+        first = min(gn, int(on[b]))
+        if gn != on[b]:
+            if first < t.evaluated and t.accept_margin[first] < eps:
+                rep.tie_accept += 1
+            else:
+                rep.failures.append((b, f"accepted length {gn} vs {on[b]}", gt.tolist(),
+                                     ot[b].tolist(), t.accept_margin[first]))
+            continue
+        j = gn
+        if t.sample_margin < eps and 0 <= gt[j] < z.shape[2]:
+            lo, hi, w = _truncated_interval(z[b, j], y[b, j] if j < k else None, T, top_k, top_p,
+                                            int(gt[j]))
+            if w > 0 and lo - eps <= u[b, k] <= hi + eps:
+                rep.tie_sample += 1
+                continue
+        rep.failures.append((b, f"drawn token {gt[j]} vs {ot[b, j]}", float(u[b, k]),
+                             t.sample_lo, t.sample_hi, t.sample_margin))
+    return rep
+
+
+def check_probs_truncated(z, y, x, T, top_k, top_p, gpu_px, gpu_qx, eps_trunc=1e-5):
+    """Largest relative error of the exported p'_i(x_i), q'_i(x_i) over the
+    positions whose rows have a top-p margin of at least eps_trunc (the others
+    may legitimately keep a different set); returns (worst, skipped rows)."""
+    worst, skipped = 0.0, 0
+    B, k = x.shape
+    for b in range(B):
+        for i in range(k):
+            for row, got in ((z[b, i], gpu_px[b, i]), (y[b, i], gpu_qx[b, i])):
+                p, m = truncated_row(row, T, top_k, top_p)
+                if m < eps_trunc:
+                    skipped += 1
+                    continue
+                ref = p[x[b, i]] if 0 <= x[b, i] < p.shape[0] else 0.0
+                if ref == 0.0:
+                    if got != 0.0:
+                        return float("inf"), skipped
+                    continue
+                worst = max(worst, abs(float(got) - ref) / ref)
+    return worst, skipped

@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_header_symbols_exported(sv):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     assert sorted(sv.EXPORTED) == names
     for n in names:
         assert hasattr(sv.lib(), n), n
@@ -229,4 +229,30 @@ def test_lazy_reject_bad_arguments(sv):
                                      None) == sv.SV_EWORKSPACE
     assert L.spec_verify_greedy_lazy(f, 99, f, 2, 3, 100, 2, po, f, f, 1 << 30, None) == sv.SV_EINVAL
     assert L.spec_verify_greedy_lazy(f, 100, f, 2, 64, 100, 2, po, f, f, 1 << 30, None) == sv.SV_EINVAL
+    assert (out == SENT).all()
+
+
+def test_truncated_reject_bad_arguments(sv):
+    L = sv.lib()
+    out, po = host_buf(64)
+    f = fake()[1]
+
+    def call(top_k, top_p, **kw):
+        a = dict(target=f, ts=100, draft=f, ds=100, tokens=f, u=f, T=1.0, B=2, k=3, V=100, dt=2,
+                 out=po, nacc=f, ws=f, wsb=1 << 30)
+        a.update(kw)
+        return L.spec_verify_sample_truncated(a["target"], a["ts"], a["draft"], a["ds"], a["tokens"],
+                                              a["u"], a["T"], top_k, top_p, a["B"], a["k"], a["V"],
+                                              a["dt"], a["out"], a["nacc"], None, None, a["ws"],
+                                              a["wsb"], None)
+
+    for tk, tp in ((-1, 1.0), (0, 0.0), (0, -0.5), (5, float("nan")), (-3, 0.9)):
+        assert call(tk, tp) == sv.SV_EINVAL, (tk, tp)
+    # the fixed-point kept mass bounds V when truncation is on, not when it is off
+    assert call(50, 1.0, V=(1 << 23) + 1, ts=(1 << 23) + 1, ds=(1 << 23) + 1) == sv.SV_EINVAL
+    assert call(0, 0.9, V=(1 << 23) + 1, ts=(1 << 23) + 1, ds=(1 << 23) + 1) == sv.SV_EINVAL
+    assert call(50, 0.9, T=0.0) == sv.SV_EINVAL
+    assert call(50, 0.9, dt=4) == sv.SV_EDTYPE
+    assert call(50, 0.9, wsb=8) == sv.SV_EWORKSPACE
+    assert call(0, 1.0, wsb=8) == sv.SV_EWORKSPACE
     assert (out == SENT).all()

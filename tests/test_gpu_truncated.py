@@ -1,0 +1,206 @@
+"""Parity of truncated sampling verification (top-k, then top-p, on target and
+draft rows alike) with the CPU oracle, on the GPU, through the C ABI.
+
+Exact except in rounds the oracle marks as boundary cases: an acceptance or a
+draw within 1e-5 of its threshold, or a row whose kept-mass fraction lies
+within 1e-5 of top_p at the top-p boundary (the GPU's fixed-point masses may
+then keep the neighbouring set); such rounds are counted and checked for
+validity (oracle/parity.py).  Exported p'(x), q'(x) within 1e-5 relative.
+The proposer's drafts are drawn from the truncated q' itself, as a serving
+engine that applies the same processor to the draft would.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from oracle import parity
+
+pytestmark = pytest.mark.gpu
+
+EPS = 1e-5
+PROB_RTOL = 1e-5
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def sv():
+    assert torch.cuda.is_available(), "GPU tests need the MI355X"
+    if not os.path.exists(oracle.LIB_PATH):
+        oracle.build()
+    import draft_verification_verify_amd as m
+    return m
+
+
+def f32(t):
+    return t.float().cpu().numpy()
+
+
+def npi(t):
+    return t.cpu().numpy()
+
+
+def truncated_drafts(y, T, top_k, top_p, seed):
+    """Draft tokens drawn from q' = the truncated draft rows (the proposer's
+    side of a consistent processor), one per row of y [B, k, V]."""
+    rng = np.random.default_rng(seed)
+    B, k, V = y.shape
+    x = np.zeros((B, k), np.int32)
+    for b in range(B):
+        for i in range(k):
+            q, _ = oracle.truncated_row(y[b, i], T, top_k, top_p)
+            x[b, i] = rng.choice(V, p=q / q.sum())
+    return x
+
+
+def workload(B, k, V, dtype, seed, top_k, top_p, T=None):
+    w = synthetic.chain(B, k, V, dtype, seed=seed, device=DEV)
+    T = w.T if T is None else T
+    y = f32(w.draft)
+    x = truncated_drafts(y, T, top_k, top_p, seed)
+    return w, T, torch.from_numpy(x).to(DEV)
+
+
+def check(sv, w, T, x, top_k, top_p, tgt=None, dft=None):
+    tgt = w.target if tgt is None else tgt
+    dft = w.draft if dft is None else dft
+    toks, na, px, qx = sv.sample_truncated(tgt, dft, x, w.uniforms, T, top_k, top_p,
+                                           return_probs=True)
+    torch.cuda.synchronize()
+    z, y = f32(w.target), f32(w.draft)
+    xx, u = npi(x), npi(w.uniforms)
+    rep = parity.check_sample_truncated(z, y, xx, u, T, top_k, top_p, npi(toks), npi(na), eps=EPS)
+    assert rep.ok(), (rep.summary(), rep.failures[:3])
+    print(rep.summary())
+    worst, skipped = parity.check_probs_truncated(z, y, xx, T, top_k, top_p, npi(px), npi(qx))
+    assert worst <= PROB_RTOL, worst
+    return rep, npi(toks), npi(na)
+
+
+SETTINGS = [(50, 1.0), (0, 0.8), (50, 0.9), (5, 0.95), (0, 0.3), (1000, 0.99)]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("top_k,top_p", SETTINGS)
+def test_truncated_parity(sv, dtype, top_k, top_p):
+    B, k, V = 24, 5, 32000
+    w, T, x = workload(B, k, V, dtype, 11 + top_k, top_k, top_p)
+    rep, _, _ = check(sv, w, T, x, top_k, top_p)
+    assert rep.exact >= rep.rounds - 2
+
+
+@pytest.mark.parametrize("B,k,V", [(8, 3, 4097), (4, 8, 1000), (3, 2, 7), (2, 4, 9), (5, 1, 100)])
+@pytest.mark.parametrize("top_k,top_p", [(3, 1.0), (0, 0.7), (4, 0.6)])
+def test_truncated_ragged_shapes(sv, B, k, V, top_k, top_p):
+    w, T, x = workload(B, k, V, "bf16", B + k + V, top_k, top_p)
+    check(sv, w, T, x, top_k, top_p)
+
+
+@pytest.mark.parametrize("layout", ["padded", "offset"])
+def test_truncated_unaligned_rows(sv, layout):
+    """Rows that are not 16-byte aligned take the element-load path."""
+    B, k, V = 12, 4, 5003
+    w, T, x = workload(B, k, V, "fp16", 77, 40, 0.9)
+    g = torch.Generator(device=DEV).manual_seed(3)
+
+    def lay(t):
+        *lead, V_ = t.shape
+        pad = 1 if layout == "padded" else 9
+        big = torch.randn((*lead, V_ + pad), generator=g, device=DEV).to(t.dtype)
+        off = 0 if layout == "padded" else 1
+        big[..., off:off + V_] = t
+        return big[..., off:off + V_]
+
+    check(sv, w, T, x, 40, 0.9, tgt=lay(w.target), dft=lay(w.draft))
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+def test_truncated_ties_and_masked_tokens(sv, dtype):
+    """Integer logits (large tie groups straddle the top-k and top-p
+    boundaries, which keep or drop a group whole), -0.0 beside +0.0, and
+    -inf (masked) tokens."""
+    g = torch.Generator(device=DEV).manual_seed(21)
+    B, k, V = 16, 4, 3001
+    tdt = synthetic.DTYPES[dtype]
+    z = torch.randint(-4, 4, (B, k + 1, V), generator=g, device=DEV).to(tdt)
+    y = torch.randint(-4, 4, (B, k, V), generator=g, device=DEV).to(tdt)
+    neg = torch.rand(z.shape, generator=g, device=DEV) < 0.5
+    z = torch.where((z == 0) & neg, torch.tensor(-0.0, dtype=tdt, device=DEV), z)
+    mask = torch.rand(z.shape, generator=g, device=DEV) < 0.2
+    z = z.masked_fill(mask, -float("inf"))
+    y = y.masked_fill(mask[:, :k], -float("inf"))
+    u = synthetic.uniforms24((B, k + 1), g, DEV)
+    w = synthetic.Workload(synthetic.CONFIGS[1], z, y, None, u, 1.0)
+    for top_k, top_p in ((7, 1.0), (400, 1.0), (0, 0.83), (400, 0.61)):
+        x = torch.from_numpy(truncated_drafts(f32(y), 1.0, top_k, top_p, 5)).to(DEV)
+        check(sv, w, 1.0, x, top_k, top_p)
+
+
+def test_top_k_one_is_greedy(sv):
+    """top_k = 1 keeps only the row maximum on both sides: with the draft's
+    argmax as its token, the rule commits exactly the greedy tokens."""
+    B, k, V = 64, 6, 32000
+    w = synthetic.chain(B, k, V, "fp32", seed=9, device=DEV)
+    x = torch.argmax(w.draft.float(), dim=2).to(torch.int32)
+    toks, na = sv.sample_truncated(w.target, w.draft, x, w.uniforms, w.T, 1, 1.0)
+    gt, gn = sv.greedy(w.target, x)
+    torch.cuda.synchronize()
+    assert torch.equal(toks, gt) and torch.equal(na, gn)
+    check(sv, w, w.T, x, 1, 1.0)
+
+
+def test_truncation_off_is_plain_sampling(sv):
+    w = synthetic.chain(32, 5, 32000, "bf16", seed=4, device=DEV)
+    a = sv.sample_truncated(w.target, w.draft, w.tokens, w.uniforms, w.T, 0, 1.0, return_probs=True)
+    b = sv.sample(w.target, w.draft, w.tokens, w.uniforms, w.T, return_probs=True)
+    c = sv.sample_truncated(w.target, w.draft, w.tokens, w.uniforms, w.T, 32000, 1.5,
+                            return_probs=True)
+    torch.cuda.synchronize()
+    for ta, tb, tc in zip(a, b, c):
+        assert torch.equal(ta, tb) and torch.equal(tc, tb)
+
+
+def test_truncated_deterministic(sv):
+    w, T, x = workload(48, 6, 32000, "bf16", 31, 50, 0.9)
+    r1 = sv.sample_truncated(w.target, w.draft, x, w.uniforms, T, 50, 0.9, return_probs=True)
+    r2 = sv.sample_truncated(w.target, w.draft, x, w.uniforms, T, 50, 0.9, return_probs=True)
+    torch.cuda.synchronize()
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("cid,top_k,top_p", [(3, 0, 0.8), (5, 50, 0.9), (5, 0, 0.8), (2, 20, 1.0)])
+def test_truncated_workload_subsets(sv, cid, top_k, top_p):
+    """The workloads' own rows (vocabulary, dtype, temperature, spikes), a few
+    sequences each."""
+    cfg = synthetic.CONFIGS[cid]
+    B = 6
+    w = synthetic.generate(cid, device=DEV, B=B)
+    y = f32(w.draft)
+    x = torch.from_numpy(truncated_drafts(y, w.T, top_k, top_p, cid)).to(DEV)
+    rep, _, _ = check(sv, w, w.T, x, top_k, top_p)
+    assert rep.rounds == B and cfg.V == w.target.shape[2]
+
+
+def test_truncated_full_size_sampled(sv):
+    """The 512 x 16 x 128256 bf16 workload at full size, top-p 0.8: every
+    sequence's round is run, and a sample of sequences is checked against the
+    oracle one by one."""
+    w = synthetic.generate(5, device=DEV)
+    B, k = w.tokens.shape
+    idx = np.array([0, 1, 137, 255, 256, 400, 511])
+    x = w.tokens.clone()
+    x[torch.from_numpy(idx).to(DEV)] = torch.from_numpy(
+        truncated_drafts(f32(w.draft[idx]), w.T, 0, 0.8, 55)).to(DEV)
+    toks, na = sv.sample_truncated(w.target, w.draft, x, w.uniforms, w.T, 0, 0.8)
+    torch.cuda.synchronize()
+    toks, na = npi(toks), npi(na)
+    assert ((na >= 0) & (na <= k)).all()
+    rep = parity.check_sample_truncated(f32(w.target[idx]), f32(w.draft[idx]), npi(x)[idx],
+                                        npi(w.uniforms[idx]), w.T, 0, 0.8, toks[idx], na[idx],
+                                        eps=EPS)
+    assert rep.ok(), (rep.summary(), rep.failures[:3])
+    print(rep.summary())
