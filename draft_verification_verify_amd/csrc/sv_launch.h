@@ -63,7 +63,8 @@ struct SampleDesc {
 // A truncated row (top-k, then top-p): its max m, log2 of the kept mass
 // relative to exp2(m * c), and the smallest kept ordering key (key_of in
 // sv_device.h): token t keeps p'(t) = exp2((z_t - m) * c - l2s) iff
-// key(z_t) >= tau, else 0.
+// key(z_t) >= tau, else 0.  pad = 1 marks a row the one-pass 16-bit kernel
+// left to the radix kernel.
 struct TruncRow {
     float m;
     float l2s;
@@ -85,6 +86,7 @@ struct TruncArgs {
     int top_k;
     float top_p;
     TruncRow* rows;
+    int only_marked;                   // radix kernel: only rows whose pad the exact kernel set to 1
 };
 
 struct DecideSampleArgs {

@@ -231,13 +231,10 @@ __device__ void hist_pass(const char* rp, int V, int L, uint32_t prefix, uint32_
 }
 
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kTB) void k_trunc_rows(TruncArgs a)
+__device__ void trunc_row_radix(const TruncArgs& a, int row, Shared& sh)
 {
     using D = Digits<DT>;
     constexpr int ES = DT == DT_F32 ? 4 : 2;
-    __shared__ Shared sh;
-    const int row = blockIdx.x;
-    if (row >= a.n_rows) return;
     const char* rp = row < a.n_target_rows ? row_ptr(a.target, row, a.t_stride, ES)
                                            : row_ptr(a.draft, row - a.n_target_rows, a.d_stride, ES);
     const int V = a.V;
@@ -261,6 +258,7 @@ __global__ __launch_bounds__(kTB) void k_trunc_rows(TruncArgs a)
     const float m = block_max<kTW>(mx, sh.redf);
     if (m == -INFINITY) {              // nothing to keep; the rule never reads such a row
         if (threadIdx.x == 0) a.rows[row] = TruncRow{m, -INFINITY, 0u, 0u};
+        __syncthreads();
         return;
     }
 
@@ -314,15 +312,454 @@ __global__ __launch_bounds__(kTB) void k_trunc_rows(TruncArgs a)
         const float l2s = (float)(log2((double)kept) - (double)kFixBits);
         a.rows[row] = TruncRow{m, l2s, tau, 0u};
     }
+    __syncthreads();                   // the shared state is reused by the next row
+}
+
+// Rows blockIdx.x, blockIdx.x + gridDim.x, ...; with only_marked, just the
+// rows the one-pass kernel marked (pad = 1).
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kTB) void k_trunc_rows(TruncArgs a)
+{
+    __shared__ Shared sh;
+    for (int row = blockIdx.x; row < a.n_rows; row += gridDim.x) {
+        if (a.only_marked && a.rows[row].pad != 1u) continue;    // uniform across the workgroup
+        trunc_row_radix<DT, VEC>(a, row, sh);
+    }
+}
+
+// ---- one pass for 16-bit logits ---------------------------------------------
+// A 16-bit logit has one of 65536 bit patterns, so one streaming pass can
+// count every value exactly: 32768 LDS words, each holding the counts of two
+// adjacent patterns in its 16-bit halves (four integer ops and one ds_add
+// per element, no exp in the stream).  The max, the top-k threshold, the
+// top-p threshold and the kept mass are then read off the histogram: a
+// value's mass is its count times the fixed-point weight of that one value,
+// the same integer the radix passes sum element by element.
+//
+// Special patterns: +-inf are even and their odd neighbours are NaNs, so
+// their words count them as plain 32-bit integers (a masked row can hold any
+// number of -inf); -0.0 is merged into +0.0.  A half that reached 65536 (that
+// many equal finite logits) would carry into its neighbour: the total no
+// longer matches the row length, and the row is marked for the radix kernel.
+//
+// Analysis runs in position order: position d = 65535 - key is 0 for the
+// largest value, and the patterns map to it as d < 32768: 32767 - d
+// (positive values, descending), d >= 32768: d (negative values).  The 1024
+// chunks of 64 positions are summed by thread (16 * lane + wave) so that the
+// dense middle of the range is shared by every wave; a thread reads its 32
+// words rotated by its lane, which puts the wave's reads in 32 different LDS
+// banks.  The chunk where a threshold is crossed is resolved by one wave, a
+// lane per position.
+
+constexpr int kT16 = 1024;
+constexpr int kW16 = kT16 / 64;
+constexpr int kWords = 32768;          // 65536 patterns, two per word
+constexpr int kChunks = 1024;
+
+template <int DT>
+__device__ __forceinline__ uint32_t ninf_bits()
+{
+    return DT == DT_BF16 ? 0xFF80u : 0xFC00u;
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t pinf_bits()
+{
+    return DT == DT_BF16 ? 0x7F80u : 0x7C00u;
+}
+
+__device__ __forceinline__ uint32_t bits_at(uint32_t d)
+{
+    return d < 32768u ? 32767u - d : d;
+}
+
+template <int DT>
+__device__ __forceinline__ float value_of_bits(uint32_t bits)
+{
+    if constexpr (DT == DT_BF16) return __uint_as_float(bits << 16);
+    else return (float)__builtin_bit_cast(_Float16, (unsigned short)bits);
+}
+
+// Count the two 16-bit logits packed in w.
+__device__ __forceinline__ void count_word(uint32_t* hist, uint32_t w)
+{
+    char* base = reinterpret_cast<char*>(hist);
+    const uint32_t a0 = (w << 1) & 0x1FFFCu;               // byte offset of word (w & 0xFFFF) >> 1
+    const uint32_t i0 = (w & 1u) * 0xFFFFu + 1u;           // 1 (low half) or 0x10000 (high half)
+    const uint32_t a1 = (w >> 15) & 0x1FFFCu;
+    const uint32_t i1 = ((w >> 16) & 1u) * 0xFFFFu + 1u;
+    atomicAdd(reinterpret_cast<uint32_t*>(base + a0), i0);
+    atomicAdd(reinterpret_cast<uint32_t*>(base + a1), i1);
+}
+
+// The count of pattern `bits` (-0.0 merged into +0.0; +-inf whole words).
+template <int DT>
+__device__ __forceinline__ uint32_t count_bits(const uint32_t* hist, uint32_t bits, uint32_t negzero)
+{
+    const uint32_t w = hist[bits >> 1];
+    const uint32_t even = bits & ~1u;
+    if (even == ninf_bits<DT>() || even == pinf_bits<DT>()) return (bits & 1u) ? 0u : w;
+    if (bits == 0x8000u) return 0u;
+    const uint32_t c = (w >> ((bits & 1u) * 16u)) & 0xFFFFu;
+    return bits == 0u ? c + negzero : c;
+}
+
+struct Scratch16 {
+    uint32_t cnt[kChunks];             // chunk counts, by chunk position
+    u64 mass[kChunks];                 // chunk masses, by chunk position
+    u64 gmass[kW16];                   // masses of 64-chunk groups
+    uint32_t wcnt[kW16];
+    int wmin[kW16];
+    uint32_t d;
+    uint32_t dk;
+    u64 incl;
+};
+
+// ---- wave scans in DPP (row shifts, then row broadcasts), no LDS ----------
+template <int CTRL, int ROWS, bool BC>
+__device__ __forceinline__ uint32_t dpp32(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROWS, 0xf, BC);
+}
+
+template <int CTRL, int ROWS, bool BC>
+__device__ __forceinline__ u64 dpp64(u64 x)
+{
+    const uint32_t lo = dpp32<CTRL, ROWS, BC>((uint32_t)x);
+    const uint32_t hi = dpp32<CTRL, ROWS, BC>((uint32_t)(x >> 32));
+    return ((u64)hi << 32) | lo;
+}
+
+// Inclusive scan over the wave in lane order.
+__device__ __forceinline__ uint32_t wave_scan_u32(uint32_t x)
+{
+    x += dpp32<0x111, 0xf, true>(x);   // row_shr:1
+    x += dpp32<0x112, 0xf, true>(x);   // row_shr:2
+    x += dpp32<0x114, 0xf, true>(x);   // row_shr:4
+    x += dpp32<0x118, 0xf, true>(x);   // row_shr:8
+    x += dpp32<0x142, 0xa, false>(x);  // row_bcast:15 into rows 1 and 3
+    x += dpp32<0x143, 0xc, false>(x);  // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
+__device__ __forceinline__ u64 wave_scan_u64(u64 x)
+{
+    x += dpp64<0x111, 0xf, true>(x);
+    x += dpp64<0x112, 0xf, true>(x);
+    x += dpp64<0x114, 0xf, true>(x);
+    x += dpp64<0x118, 0xf, true>(x);
+    x += dpp64<0x142, 0xa, false>(x);
+    x += dpp64<0x143, 0xc, false>(x);
+    return x;
+}
+
+__device__ __forceinline__ uint32_t lane63_u32(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+// x of lane `l` (uniform), to every lane
+__device__ __forceinline__ u64 readlane_u64(u64 x, int l)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l);
+    return ((u64)hi << 32) | lo;
+}
+
+__device__ __forceinline__ u64 lane63_u64(u64 x)
+{
+    return readlane_u64(x, 63);
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// lo half + hi half + acc, in one instruction
+__device__ __forceinline__ uint32_t add_halves(uint32_t w, uint32_t acc)
+{
+    return __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, w), u16x2{1, 1}, acc, false);
+}
+
+// Persistent: workgroup g takes rows g, g + gridDim.x, ...  While it
+// analyses one row, the first round of its next row is already loading.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kT16) void k_trunc16(TruncArgs a)
+{
+    constexpr int ES = 2;
+    constexpr int kAhead = 4;          // vectors per thread loaded ahead
+    __shared__ __attribute__((aligned(16))) uint32_t hist[kWords];
+    __shared__ __attribute__((aligned(16))) Scratch16 sc;
+    const int V = a.V;
+    const int t = (int)threadIdx.x;
+    const int lane = t & 63, wv = t >> 6;
+    const int nfull = V >> 3;
+    u32x4* h4 = reinterpret_cast<u32x4*>(hist);
+    auto row_of = [&](int r) -> const char* {
+        return r < a.n_target_rows ? row_ptr(a.target, r, a.t_stride, ES)
+                                   : row_ptr(a.draft, r - a.n_target_rows, a.d_stride, ES);
+    };
+
+    Raw<DT> ahead[kAhead];
+    int row = blockIdx.x;
+    if (row < a.n_rows) {
+        const char* rp = row_of(row);
+#pragma unroll
+        for (int u = 0; u < kAhead; ++u)
+            if (t + u * kT16 < nfull) ahead[u] = load_raw<DT, VEC>(rp, t + u * kT16);
+    }
+    for (; row < a.n_rows; row += gridDim.x) {
+    const char* rp = row_of(row);
+    for (int i = t; i < kWords / 4; i += kT16) h4[i] = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+
+    // the pass: count every pattern (the first kAhead vectors are already here)
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) {
+        if (t + u * kT16 < nfull) {
+            count_word(hist, ahead[u].a.x);
+            count_word(hist, ahead[u].a.y);
+            count_word(hist, ahead[u].a.z);
+            count_word(hist, ahead[u].a.w);
+        }
+    }
+    int v = t + kAhead * kT16;
+    for (; v + 3 * kT16 < nfull; v += 4 * kT16) {
+        Raw<DT> r[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) r[u] = load_raw<DT, VEC>(rp, v + u * kT16);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            count_word(hist, r[u].a.x);
+            count_word(hist, r[u].a.y);
+            count_word(hist, r[u].a.z);
+            count_word(hist, r[u].a.w);
+        }
+    }
+    for (; v < nfull; v += kT16) {
+        const Raw<DT> r = load_raw<DT, VEC>(rp, v);
+        count_word(hist, r.a.x);
+        count_word(hist, r.a.y);
+        count_word(hist, r.a.z);
+        count_word(hist, r.a.w);
+    }
+    if (t == nfull % kT16 && 8 * nfull < V) {   // the partial last vector: one thread
+        const unsigned short* e = reinterpret_cast<const unsigned short*>(rp) + 8LL * nfull;
+        for (int j = 0; j < V - 8 * nfull; ++j) {
+            const uint32_t b = e[j];
+            atomicAdd(&hist[b >> 1], (b & 1u) * 0xFFFFu + 1u);
+        }
+    }
+    // the next row's first vectors load during the analysis
+    {
+        const int nrow = row + (int)gridDim.x;
+        if (nrow < a.n_rows) {
+            const char* np = row_of(nrow);
+#pragma unroll
+            for (int u = 0; u < kAhead; ++u)
+                if (t + u * kT16 < nfull) ahead[u] = load_raw<DT, VEC>(np, t + u * kT16);
+        }
+    }
+    __syncthreads();
+    const uint32_t negzero = hist[0x8000u >> 1] & 0xFFFFu;     // -0.0
+    const uint32_t ninf = hist[ninf_bits<DT>() >> 1];
+
+    // chunk sums: thread (lane, wave) sums chunk position 16 * lane + wave,
+    // reading its 8 groups of 4 words rotated by lane
+    const int cp = 16 * lane + wv;
+    const int bc = cp < 512 ? 511 - cp : cp;                  // its pattern chunk
+    uint32_t my_cnt = 0;
+    {
+        const u32x4* cw = h4 + 8 * bc;
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            const u32x4 q = cw[(g + lane) & 7];
+            my_cnt = add_halves(q.x, my_cnt);
+            my_cnt = add_halves(q.y, my_cnt);
+            my_cnt = add_halves(q.z, my_cnt);
+            my_cnt = add_halves(q.w, my_cnt);
+        }
+        // whole-word counters and the -0.0 / +0.0 merge
+        if (bc == (int)(ninf_bits<DT>() >> 6)) my_cnt += ninf - add_halves(ninf, 0u);
+        if (bc == (int)(pinf_bits<DT>() >> 6)) {
+            const uint32_t w = hist[pinf_bits<DT>() >> 1];
+            my_cnt += w - add_halves(w, 0u);
+        }
+        if (bc == 512) my_cnt -= negzero;
+        if (bc == 0) my_cnt += negzero;
+    }
+    sc.cnt[cp] = my_cnt;
+    const uint32_t fin_cnt = bc == (int)(ninf_bits<DT>() >> 6) ? my_cnt - ninf : my_cnt;
+    {
+        const uint32_t wt = lane63_u32(wave_scan_u32(my_cnt));
+        const unsigned long long ne = __ballot(fin_cnt != 0u);
+        if (lane == 0) {
+            sc.wcnt[wv] = wt;
+            sc.wmin[wv] = ne ? 16 * (__ffsll((long long)ne) - 1) + wv : INT32_MAX;
+        }
+    }
+    __syncthreads();
+    uint32_t total = 0;
+    int cmax = INT32_MAX;
+#pragma unroll
+    for (int i = 0; i < kW16; ++i) {
+        total += sc.wcnt[i];
+        cmax = min(cmax, sc.wmin[i]);
+    }
+    if (total != (uint32_t)V) {        // a half overflowed: leave the row to the radix kernel
+        if (t == 0) a.rows[row] = TruncRow{0.f, 0.f, 0u, 1u};
+        __syncthreads();
+        continue;
+    }
+    const uint32_t finite = total - ninf;
+    if (finite == 0) {                 // every logit is -inf
+        if (t == 0) a.rows[row] = TruncRow{-INFINITY, -INFINITY, 0u, 0u};
+        __syncthreads();
+        continue;
+    }
+
+    // wave 0: the max (first nonempty position of chunk cmax), then top-k
+    if (wv == 0) {
+        {
+            const uint32_t d = 64u * cmax + lane;
+            const uint32_t b = bits_at(d);
+            const bool nz = b != ninf_bits<DT>() && count_bits<DT>(hist, b, negzero) != 0u;
+            const unsigned long long hit = __ballot(nz);
+            if (lane == 0) sc.d = 64u * cmax + (uint32_t)(__ffsll((long long)hit) - 1);
+        }
+        uint32_t dk = 65535u;          // positions <= dk survive top-k
+        if (a.top_k >= 1 && (uint32_t)a.top_k < finite) {
+            const uint32_t need = (uint32_t)a.top_k;
+            uint32_t base = 0;
+            int ch = -1;
+            for (int g = 0; g < kChunks / 64 && ch < 0; ++g) {   // uniform across the wave
+                const uint32_t x = sc.cnt[64 * g + lane];
+                const uint32_t incl = base + wave_scan_u32(x);
+                const unsigned long long hit = __ballot(incl >= need);
+                if (hit) {
+                    const int f = __ffsll((long long)hit) - 1;
+                    ch = 64 * g + f;
+                    base = (uint32_t)__builtin_amdgcn_readlane((int)(incl - x), f);
+                } else {
+                    base = lane63_u32(incl);
+                }
+            }
+            if (ch < 0) ch = kChunks - 1;                 // unreachable: top_k < finite
+            const uint32_t d = 64u * ch + lane;
+            const uint32_t incl = base + wave_scan_u32(count_bits<DT>(hist, bits_at(d), negzero));
+            const unsigned long long hit = __ballot(incl >= need);
+            dk = 64u * ch + (uint32_t)(__ffsll((long long)hit) - 1);
+        }
+        if (lane == 0) sc.dk = dk;
+    }
+    __syncthreads();
+    const float m = value_of_bits<DT>(bits_at(sc.d));
+    const float c = a.c;
+    const uint32_t dk = sc.dk;
+
+    // masses of the chunks (positions <= dk), one wave per chunk, each wave
+    // taking the nonempty chunks its own threads summed
+    auto mass_at = [=](uint32_t d) -> u64 {
+        if (d > dk) return 0;
+        const uint32_t b = bits_at(d);
+        const uint32_t n = count_bits<DT>(hist, b, negzero);
+        return n ? (u64)n * fixed40(weight(value_of_bits<DT>(b), m, c)) : 0;
+    };
+    {
+        sc.mass[cp] = 0;
+        unsigned long long todo = __ballot(fin_cnt != 0 && (uint32_t)cp <= (dk >> 6));
+        while (todo) {
+            const int bit = __ffsll((long long)todo) - 1;
+            todo &= todo - 1;
+            const int ch = 16 * bit + wv;
+            const u64 mk = lane63_u64(wave_scan_u64(mass_at(64u * ch + lane)));
+            if (lane == 0) sc.mass[ch] = mk;
+        }
+    }
+    __syncthreads();
+    // group totals: wave w sums chunk positions 64w .. 64w + 63
+    {
+        const u64 gt = lane63_u64(wave_scan_u64(sc.mass[64 * wv + lane]));
+        if (lane == 0) sc.gmass[wv] = gt;
+    }
+    __syncthreads();
+    // every wave: the group totals as a scan over lanes 0..15
+    const u64 gm = lane < kW16 ? sc.gmass[lane] : 0;
+    const u64 ginc = wave_scan_u64(gm);
+    const u64 M = lane63_u64(ginc);
+    u64 kept = M;
+    uint32_t dtau = dk;
+    if (a.top_p < 1.f) {
+        const double budget = (double)a.top_p * (double)M;
+        // the group, then the chunk, then the position where budget is reached
+        const unsigned long long ghit = __ballot(lane < kW16 && (double)ginc >= budget);
+        const int G = ghit ? __ffsll((long long)ghit) - 1 : kW16 - 1;
+        const u64 gbase = readlane_u64(ginc - gm, G);
+        if (wv == G) {
+            const u64 x = sc.mass[64 * G + lane];
+            const u64 incl = gbase + wave_scan_u64(x);
+            const unsigned long long hit = __ballot((double)incl >= budget);
+            const int f = hit ? __ffsll((long long)hit) - 1 : 63;
+            const int ch = 64 * G + f;
+            const u64 excl_f = readlane_u64(incl - x, f);
+            const uint32_t d = 64u * ch + lane;
+            const u64 mk = mass_at(d);
+            const u64 incl2 = excl_f + wave_scan_u64(mk);
+            const unsigned long long hit2 = __ballot((double)incl2 >= budget);
+            const int f2 = hit2 ? __ffsll((long long)hit2) - 1 : 63;
+            if (lane == f2) {
+                sc.d = d;
+                sc.incl = incl2;
+            }
+        }
+        __syncthreads();
+        dtau = sc.d;
+        kept = sc.incl;
+    }
+    if (t == 0) {
+        const float l2s = (float)(log2((double)kept) - (double)kFixBits);
+        a.rows[row] = TruncRow{m, l2s, 65535u - dtau, 0u};
+    }
+    __syncthreads();                   // LDS is cleared for the next row
+    }
+}
+
+// The current device's compute units (queried once per device).
+int compute_units()
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
 }
 
 template <int DT>
 hipError_t launch_dt(bool vec, const TruncArgs& a, hipStream_t st)
 {
-    void* args[] = {const_cast<TruncArgs*>(&a)};
-    const void* f = vec ? reinterpret_cast<const void*>(k_trunc_rows<DT, true>)
-                        : reinterpret_cast<const void*>(k_trunc_rows<DT, false>);
-    return hipLaunchKernel(f, dim3((unsigned)a.n_rows), dim3(kTB), args, 0, st);
+    TruncArgs b = a;
+    b.only_marked = 0;
+    void* args[] = {&b};
+    if constexpr (DT == DT_F32) {
+        const void* f = vec ? reinterpret_cast<const void*>(k_trunc_rows<DT, true>)
+                            : reinterpret_cast<const void*>(k_trunc_rows<DT, false>);
+        return hipLaunchKernel(f, dim3((unsigned)a.n_rows), dim3(kTB), args, 0, st);
+    } else {
+        const void* f = vec ? reinterpret_cast<const void*>(k_trunc16<DT, true>)
+                            : reinterpret_cast<const void*>(k_trunc16<DT, false>);
+        const int cus = compute_units();
+        const unsigned g16 = (unsigned)(a.n_rows < cus ? a.n_rows : cus);   // one workgroup fills a CU's LDS
+        hipError_t e = hipLaunchKernel(f, dim3(g16), dim3(kT16), args, 0, st);
+        if (e != hipSuccess) return e;
+        // rows with 65536 or more equal finite logits
+        b.only_marked = 1;
+        const void* g = vec ? reinterpret_cast<const void*>(k_trunc_rows<DT, true>)
+                            : reinterpret_cast<const void*>(k_trunc_rows<DT, false>);
+        const unsigned grid = (unsigned)(a.n_rows < 512 ? a.n_rows : 512);
+        return hipLaunchKernel(g, dim3(grid), dim3(kTB), args, 0, st);
+    }
 }
 
 }  // namespace

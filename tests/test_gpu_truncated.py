@@ -204,3 +204,28 @@ def test_truncated_full_size_sampled(sv):
                                         eps=EPS)
     assert rep.ok(), (rep.summary(), rep.failures[:3])
     print(rep.summary())
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_truncated_many_equal_logits(sv, dtype):
+    """16-bit rows with 65536 or more equal finite logits (the one-pass key
+    histogram cannot hold that count and hands the row to the radix passes),
+    +0.0 and -0.0 together past 65535, and rows with more than 65535 masked
+    (-inf) tokens."""
+    g = torch.Generator(device=DEV).manual_seed(8)
+    B, k, V = 3, 2, 70001
+    tdt = synthetic.DTYPES[dtype]
+    z = torch.randn((B, k + 1, V), generator=g, device=DEV).to(tdt)
+    y = torch.randn((B, k, V), generator=g, device=DEV).to(tdt)
+    z[0, :, :66000] = 0.5                          # one value 66000 times
+    y[0, :, 1000:67500] = -1.25
+    zero = torch.rand((V,), generator=g, device=DEV) < 0.5
+    z[1, :, :68000] = torch.where(zero[:68000], torch.tensor(0.0, dtype=tdt, device=DEV),
+                                  torch.tensor(-0.0, dtype=tdt, device=DEV))
+    z[2, :, 2:68002] = -float("inf")               # a masked row: 68000 -inf
+    y[2, :, 5:68005] = -float("inf")
+    u = synthetic.uniforms24((B, k + 1), g, DEV)
+    w = synthetic.Workload(synthetic.CONFIGS[1], z, y, None, u, 1.0)
+    for top_k, top_p in ((100, 1.0), (0, 0.9), (70000, 0.5), (3, 0.99)):
+        x = torch.from_numpy(truncated_drafts(f32(y), 1.0, top_k, top_p, 9)).to(DEV)
+        check(sv, w, 1.0, x, top_k, top_p)
