@@ -263,9 +263,10 @@ def main():
         },
         "roofline": None if lazy else {
             "kernel": {"sample": "k_softmax_stats", "lenient": "k_softmax_stats",
-                       "truncated": "k_trunc_rows"}.get(args.mode, "k_argmax_stats"),
-            "note": ("algorithmic bytes count one read of every row; the kernel streams each "
-                     "row once per selection pass (the later passes mostly from cache)")
+                       "truncated": "k_trunc16"}.get(args.mode, "k_argmax_stats"),
+            "note": ("the timed launch is k_trunc16 (one pass per 16-bit row: an exact LDS "
+                     "histogram of all 65536 bit patterns) and k_trunc_rows over the rows it "
+                     "marked (none here); algorithmic bytes: every row read once")
             if args.mode == "truncated" else (
                 "rows counts every scored candidate position (B*C*R); the kernel reads "
                 "B*N unique node rows") if args.mode == "tree" else None,

@@ -11,14 +11,20 @@
 //   together.  Both keep a set {t : key(z_t) >= tau} for an ordering key
 //   (key_of), so a row is summarised by (m, tau, kept mass).
 //
-// One 512-thread workgroup per row finds tau by radix selection on the key,
-// most significant digit first (11 bits, then 5 for 16-bit keys; 11, 11 and
-// 10 bits for fp32 keys).  Each pass streams the row once (the first from
-// HBM, the rest mostly from cache) and histograms the next digit of the keys
-// that share the prefix chosen so far: counts for top-k, masses for top-p.
+// Two kernels find tau and the kept mass:
+//  - k_trunc16 (fp16 / bf16 rows): one pass per row, an exact count of all
+//    65536 bit patterns in LDS, the thresholds read off the histogram;
+//  - k_trunc_rows (fp32 rows, and the rare 16-bit row the histogram cannot
+//    hold): radix selection on the key, most significant digit first (11, 11
+//    and 10 bits for fp32 keys; 11 then 5 for 16-bit keys), one 512-thread
+//    workgroup per row streaming the row once per digit (the first pass from
+//    HBM, the rest mostly from cache) and histogramming the next digit of the
+//    keys that share the prefix chosen so far: counts for top-k, masses for
+//    top-p.
 // Masses are fixed-point integers (w * 2^40, truncated), summed with integer
 // atomics and integer reductions, so every result is independent of
-// scheduling and bitwise reproducible.
+// scheduling and bitwise reproducible, and both kernels give the same
+// integers for the same row.
 
 #include "sv_device.h"
 
@@ -316,14 +322,29 @@ __device__ void trunc_row_radix(const TruncArgs& a, int row, Shared& sh)
 }
 
 // Rows blockIdx.x, blockIdx.x + gridDim.x, ...; with only_marked, just the
-// rows the one-pass kernel marked (pad = 1).
+// rows the one-pass kernel marked (pad = 1): the workgroup reads the marks of
+// kTB rows at once (rows blockIdx.x * kTB + i, then gridDim.x * kTB further)
+// and runs the marked ones.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kTB) void k_trunc_rows(TruncArgs a)
 {
     __shared__ Shared sh;
-    for (int row = blockIdx.x; row < a.n_rows; row += gridDim.x) {
-        if (a.only_marked && a.rows[row].pad != 1u) continue;    // uniform across the workgroup
-        trunc_row_radix<DT, VEC>(a, row, sh);
+    __shared__ int marked[kTB];
+    __shared__ int n_marked;
+    if (!a.only_marked) {
+        for (int row = blockIdx.x; row < a.n_rows; row += gridDim.x) trunc_row_radix<DT, VEC>(a, row, sh);
+        return;
+    }
+    for (int base = blockIdx.x * kTB; base < a.n_rows; base += gridDim.x * kTB) {
+        if (threadIdx.x == 0) n_marked = 0;
+        __syncthreads();
+        const int row = base + (int)threadIdx.x;
+        if (row < a.n_rows && a.rows[row].pad == 1u) marked[atomicAdd(&n_marked, 1)] = row;
+        __syncthreads();
+        const int n = n_marked;
+        // each row's result depends on that row alone, so the order is free
+        for (int i = 0; i < n; ++i) trunc_row_radix<DT, VEC>(a, marked[i], sh);
+        __syncthreads();
     }
 }
 
@@ -757,7 +778,8 @@ hipError_t launch_dt(bool vec, const TruncArgs& a, hipStream_t st)
         b.only_marked = 1;
         const void* g = vec ? reinterpret_cast<const void*>(k_trunc_rows<DT, true>)
                             : reinterpret_cast<const void*>(k_trunc_rows<DT, false>);
-        const unsigned grid = (unsigned)(a.n_rows < 512 ? a.n_rows : 512);
+        const int blocks = (a.n_rows + kTB - 1) / kTB;
+        const unsigned grid = (unsigned)(blocks < 1024 ? blocks : 1024);
         return hipLaunchKernel(g, dim3(grid), dim3(kTB), args, 0, st);
     }
 }
