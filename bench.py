@@ -3,7 +3,9 @@
 
 A step is one spec_verify_sample call over workload 5: B = 512 sequences,
 k = 16 drafts, V = 128256, bf16 logits, T = 1.0 (the largest workload; all
-inputs already resident in HBM).  One call runs the whole hot path: the
+inputs already resident in HBM).  --workload / --mode measure the other
+workloads and entry points; workloads smaller than 1 GiB rotate over several
+input sets, call by call, so that no call reads its rows from the MALL.  One call runs the whole hot path: the
 vocabulary-streaming statistics pass over every target and draft row, the
 per-sequence decisions, and the residual/bonus draw.  The metric counts
 verified positions: B * (k+1) rows per call.
@@ -53,27 +55,33 @@ def measured_traffic(bytes_algo: float):
     return t.get("bytes_per_launch")
 
 
+CHAIN_MODES = ("sample", "greedy", "greedy_ext", "lenient", "sample_lazy", "greedy_lazy", "truncated")
+CAND_MODES = ("candidates", "candidates_ext", "tree")
+MALL_DEFEAT_BYTES = 1 << 30            # inputs rotated over at least this many bytes (MALL: 256 MB)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--mode", default="sample",
-                    choices=["sample", "greedy", "candidates", "greedy_ext", "lenient", "candidates_ext",
-                             "tree", "sample_lazy", "greedy_lazy", "truncated"],
-                    help="sample: workload 5 (the benchmark line); greedy / greedy_ext: workload 5 "
-                         "greedy (ext: with the #Match by-products); lenient: workload 5 sampling "
-                         "with --lenience; candidates / candidates_ext: workload 4; tree: workload 4 "
-                         "with shared rows stored once; sample_lazy / greedy_lazy: workload 5 with "
-                         "early exit; truncated: workload 5 sampling on top-k / top-p truncated "
-                         "rows (--top-k, --top-p)")
+    ap.add_argument("--mode", default="sample", choices=list(CHAIN_MODES + CAND_MODES),
+                    help="sample (default, the benchmark line), greedy / greedy_ext (with the "
+                         "#Match by-products), lenient (--lenience), sample_lazy / greedy_lazy "
+                         "(early exit), truncated (--top-k, --top-p): chain workloads; "
+                         "candidates / candidates_ext / tree (shared rows stored once): workload 4")
+    ap.add_argument("--workload", type=int, default=None, choices=[1, 2, 3, 4, 5],
+                    help="default: 5 for chain modes, 4 for candidate modes")
+    ap.add_argument("--sets", type=int, default=0,
+                    help="input sets rotated over, call by call (0: enough to span 1 GiB, so "
+                         "that no call finds its rows in the 256 MB MALL)")
     ap.add_argument("--lenience", type=float, default=2.0)
     ap.add_argument("--top-k", type=int, default=50)
     ap.add_argument("--top-p", type=float, default=0.8)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="CPU oracle baseline budget (0 disables it)")
+                    help="CPU oracle baseline budget (sample mode; 0 disables it)")
     ap.add_argument("--profile-every", type=int, default=5,
-                    help="time the statistics kernel on every N-th timed call")
+                    help="time the streaming kernel on every N-th timed call")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (scale for the rocprofv3 byte counters)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -89,6 +97,11 @@ def main():
               "shard over GPUs with no exchange, so one GPU's rate is its share); run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
+    cand = args.mode in CAND_MODES
+    cid = args.workload or (4 if cand else 5)
+    if cand != (cid == 4):
+        print(f"mode {args.mode} does not run on workload {cid}", file=sys.stderr)
+        sys.exit(2)
 
     import torch
 
@@ -97,28 +110,45 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    cid = 4 if args.mode.startswith("candidates") or args.mode == "tree" else 5
+    cfg0 = synthetic.CONFIGS[cid]
+    es = {"fp32": 4, "fp16": 2, "bf16": 2}[cfg0.dtype]
+    if cand:
+        stream_rows = cfg0.C * cfg0.R
+    else:
+        stream_rows = 2 * cfg0.k + 1 if args.mode in ("sample", "lenient", "sample_lazy", "truncated") \
+            else cfg0.k + 1
+    set_bytes = cfg0.B * stream_rows * cfg0.V * es
+    sets = args.sets or max(1, min(1000, -(-MALL_DEFEAT_BYTES // set_bytes)))
+    if sets > 1 and set_bytes * sets > (6 << 30):
+        sets = max(1, (6 << 30) // set_bytes)
     t0 = time.perf_counter()
-    w = synthetic.generate(cid, device=dev)
+    wall = synthetic.generate(cid, device=dev, B=cfg0.B * sets)
     torch.cuda.synchronize()
     gen_s = time.perf_counter() - t0
-    cfg = w.cfg
-    es = w.target.element_size()
+    B = cfg0.B
+
+    def part(t, s):
+        return None if t is None else t[s * B:(s + 1) * B]
+
+    slices = [synthetic.Workload(cfg0, part(wall.target, s), part(wall.draft, s), part(wall.tokens, s),
+                                 part(wall.uniforms, s), wall.T) for s in range(sets)]
+    w = slices[0]
 
     if args.mode == "tree":
-        nodes, cand_rows = synthetic.as_tree(w)
-        B, C, R, V = w.target.shape
+        trees = [synthetic.as_tree(x) for x in slices]
+        _, C, R, V = w.target.shape
         L = w.tokens.shape[2]
-        N = nodes.shape[1]
+        N = trees[0][0].shape[1]
         rows = B * C * R
-        ws = torch.empty(sv.workspace_bytes(B, N, V, nodes.dtype), dtype=torch.uint8, device=dev)
+        ws = torch.empty(sv.workspace_bytes(B, N, V, trees[0][0].dtype), dtype=torch.uint8, device=dev)
 
-        def step():
-            sv.greedy_tree(nodes, w.tokens, cand_rows, workspace=ws)
+        def call(i):
+            nodes, cand_rows = trees[i % sets]
+            sv.greedy_tree(nodes, slices[i % sets].tokens, cand_rows, workspace=ws)
         stats_rows = B * N
-        workload = f"spec_verify_greedy_tree B={B} C={C} L={L} R={R} N={N} V={V} bf16"
-    elif args.mode.startswith("candidates"):
-        B, C, R, V = w.target.shape
+        workload = f"workload {cid}: spec_verify_greedy_tree B={B} C={C} L={L} R={R} N={N} V={V} {cfg0.dtype}"
+    elif cand:
+        _, C, R, V = w.target.shape
         L = w.tokens.shape[2]
         rows = B * C * R
         out = (torch.empty((B, L + 1), dtype=torch.int32, device=dev),
@@ -126,93 +156,67 @@ def main():
         ws = torch.empty(sv.workspace_bytes(B, C * R, V, w.target.dtype), dtype=torch.uint8, device=dev)
 
         if args.mode == "candidates":
-            def step():
-                sv.greedy_candidates(w.target, w.tokens, out_tokens=out[0], out_num_accepted=out[1],
+            def call(i):
+                x = slices[i % sets]
+                sv.greedy_candidates(x.target, x.tokens, out_tokens=out[0], out_num_accepted=out[1],
                                      out_best=out[2], workspace=ws)
         else:
-            def step():
-                sv.greedy_candidates_ext(w.target, w.tokens, workspace=ws)
+            def call(i):
+                x = slices[i % sets]
+                sv.greedy_candidates_ext(x.target, x.tokens, workspace=ws)
         stats_rows = rows
-        workload = f"spec_verify_greedy_{args.mode} B={B} C={C} L={L} R={R} V={V} bf16"
+        workload = f"workload {cid}: spec_verify_greedy_{args.mode} B={B} C={C} L={L} R={R} V={V} {cfg0.dtype}"
     else:
-        B, k1, V = w.target.shape
+        _, k1, V = w.target.shape
         k = k1 - 1
         rows = B * k1
         out_t = torch.empty((B, k1), dtype=torch.int32, device=dev)
         out_n = torch.empty(B, dtype=torch.int32, device=dev)
-        if args.mode == "sample":
-            ws = torch.empty(sv.workspace_bytes(B, 2 * k + 1, V, w.target.dtype), dtype=torch.uint8,
-                             device=dev)
+        sampling = stream_rows == 2 * k + 1
+        ws = torch.empty(sv.workspace_bytes(B, 2 * k + 1 if sampling else k + 1, V, w.target.dtype),
+                         dtype=torch.uint8, device=dev)
+        name = {"sample": "spec_verify_sample", "lenient": "spec_verify_sample_lenient",
+                "sample_lazy": "spec_verify_sample_lazy", "truncated": "spec_verify_sample_truncated",
+                "greedy": "spec_verify_greedy", "greedy_ext": "spec_verify_greedy_ext",
+                "greedy_lazy": "spec_verify_greedy_lazy"}[args.mode]
+        extra = {"lenient": f" l={args.lenience}",
+                 "truncated": f" top_k={args.top_k} top_p={args.top_p}"}.get(args.mode, "")
+        workload = (f"workload {cid}: {name} B={B} k={k} V={V} {cfg0.dtype}"
+                    f"{' T=' + str(w.T) if sampling else ''}{extra}")
+        stats_rows = B * stream_rows
 
-            def step():
-                sv.sample(w.target, w.draft, w.tokens, w.uniforms, w.T, out_tokens=out_t,
+        def call(i):
+            x = slices[i % sets]
+            if args.mode == "sample":
+                sv.sample(x.target, x.draft, x.tokens, x.uniforms, x.T, out_tokens=out_t,
                           out_num_accepted=out_n, workspace=ws)
-            stats_rows = B * (2 * k + 1)
-            workload = f"spec_verify_sample B={B} k={k} V={V} bf16 T={w.T}"
-        elif args.mode == "lenient":
-            ws = torch.empty(sv.workspace_bytes(B, 2 * k + 1, V, w.target.dtype), dtype=torch.uint8,
-                             device=dev)
-
-            def step():
-                sv.sample_lenient(w.target, w.draft, w.tokens, w.uniforms, w.T, args.lenience,
+            elif args.mode == "lenient":
+                sv.sample_lenient(x.target, x.draft, x.tokens, x.uniforms, x.T, args.lenience,
                                   workspace=ws)
-            stats_rows = B * (2 * k + 1)
-            workload = f"spec_verify_sample_lenient B={B} k={k} V={V} bf16 T={w.T} l={args.lenience}"
-        elif args.mode == "truncated":
-            ws = torch.empty(sv.workspace_bytes(B, 2 * k + 1, V, w.target.dtype), dtype=torch.uint8,
-                             device=dev)
-
-            def step():
-                sv.sample_truncated(w.target, w.draft, w.tokens, w.uniforms, w.T, args.top_k,
-                                    args.top_p, workspace=ws)
-            stats_rows = B * (2 * k + 1)
-            workload = (f"spec_verify_sample_truncated B={B} k={k} V={V} bf16 T={w.T} "
-                        f"top_k={args.top_k} top_p={args.top_p}")
-        elif args.mode == "sample_lazy":
-            ws = torch.empty(sv.workspace_bytes(B, 2 * k + 1, V, w.target.dtype), dtype=torch.uint8,
-                             device=dev)
-
-            def step():
-                sv.sample_lazy(w.target, w.draft, w.tokens, w.uniforms, w.T, out_tokens=out_t,
+            elif args.mode == "sample_lazy":
+                sv.sample_lazy(x.target, x.draft, x.tokens, x.uniforms, x.T, out_tokens=out_t,
                                out_num_accepted=out_n, workspace=ws)
-            stats_rows = B * (2 * k + 1)
-            workload = f"spec_verify_sample_lazy B={B} k={k} V={V} bf16 T={w.T}"
-        elif args.mode == "greedy_lazy":
-            ws = torch.empty(sv.workspace_bytes(B, k + 1, V, w.target.dtype), dtype=torch.uint8,
-                             device=dev)
-
-            def step():
-                sv.greedy_lazy(w.target, w.tokens, out_tokens=out_t, out_num_accepted=out_n,
+            elif args.mode == "truncated":
+                sv.sample_truncated(x.target, x.draft, x.tokens, x.uniforms, x.T, args.top_k,
+                                    args.top_p, workspace=ws)
+            elif args.mode == "greedy_lazy":
+                sv.greedy_lazy(x.target, x.tokens, out_tokens=out_t, out_num_accepted=out_n,
                                workspace=ws)
-            stats_rows = rows
-            workload = f"spec_verify_greedy_lazy B={B} k={k} V={V} bf16"
-        elif args.mode == "greedy_ext":
-            ws = torch.empty(sv.workspace_bytes(B, k + 1, V, w.target.dtype), dtype=torch.uint8,
-                             device=dev)
+            elif args.mode == "greedy_ext":
+                sv.greedy_ext(x.target, x.tokens, workspace=ws)
+            else:
+                sv.greedy(x.target, x.tokens, out_tokens=out_t, out_num_accepted=out_n, workspace=ws)
 
-            def step():
-                sv.greedy_ext(w.target, w.tokens, workspace=ws)
-            stats_rows = rows
-            workload = f"spec_verify_greedy_ext B={B} k={k} V={V} bf16"
-        else:
-            ws = torch.empty(sv.workspace_bytes(B, k + 1, V, w.target.dtype), dtype=torch.uint8,
-                             device=dev)
-
-            def step():
-                sv.greedy(w.target, w.tokens, out_tokens=out_t, out_num_accepted=out_n, workspace=ws)
-            stats_rows = rows
-            workload = f"spec_verify_greedy B={B} k={k} V={V} bf16"
-
-    # algorithmic bytes of the statistics kernel: every logit row read once
+    # algorithmic bytes of the streaming kernel: every logit row read once
     # (V * element size) plus its 8-byte partial written
     bytes_per_row = V * es + 8
     stats_bytes = stats_rows * bytes_per_row
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        call(i)
     torch.cuda.synchronize()
 
-    # the statistics kernel is timed by events around it on every
+    # the streaming kernel is timed by events around it on every
     # `profile_every`-th call of the timed region (each event pair adds a few
     # microseconds of queue time to the call it brackets)
     sv.profile_begin(args.steps, args.profile_every)
@@ -221,8 +225,8 @@ def main():
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     start.record()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        call(args.warmup + i)
     end.record()
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - w0
@@ -231,12 +235,26 @@ def main():
     ms_per_step = total_ms / args.steps
     value = rows * args.steps / (total_ms / 1e3)
 
+    # after the timed region: each call on its own between two events, for
+    # the spread of single-call times
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i, (e0, e1) in enumerate(evs):
+        e0.record()
+        call(i)
+        e1.record()
+    torch.cuda.synchronize()
+    per_call = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+
+    def pct(q):
+        return per_call[min(len(per_call) - 1, int(q * (len(per_call) - 1) + 0.5))]
+
     lazy = args.mode.endswith("_lazy")
     if lazy:                           # early exit: no single streaming kernel per call
         kernel_ms = []
     k_avg_ms = statistics.fmean(kernel_ms) if kernel_ms else None
     achieved = stats_bytes / (k_avg_ms / 1e3) / 1e9 if kernel_ms else None
-    traffic = measured_traffic(stats_bytes) if args.mode == "sample" else None
+    traffic = measured_traffic(stats_bytes) if (args.mode == "sample" and cid == 5) else None
 
     line = {
         "metric": METRIC,
@@ -253,17 +271,20 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": workload,
-            "input_dtype": "bf16",
+            "input_dtype": cfg0.dtype,
             "rows_per_call": rows,
             "logit_bytes_per_call": stats_rows * V * es,
             "call_effective_GBps": stats_rows * V * es / (ms_per_step / 1e3) / 1e9,
+            "input_sets_rotated": sets,
+            "single_call_ms_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
             "wall_s_timed_region": wall_s,
             "input_generation_s": gen_s,
             "device": torch.cuda.get_device_name(0),
         },
         "roofline": None if lazy else {
             "kernel": {"sample": "k_softmax_stats", "lenient": "k_softmax_stats",
-                       "truncated": "k_trunc16"}.get(args.mode, "k_argmax_stats"),
+                       "truncated": "k_trunc16" if es == 2 else "k_trunc_rows"}.get(
+                           args.mode, "k_argmax_stats"),
             "note": ("the timed launch is k_trunc16 (one pass per 16-bit row: an exact LDS "
                      "histogram of all 65536 bit patterns) and k_trunc_rows over the rows it "
                      "marked (none here); algorithmic bytes: every row read once")
@@ -285,6 +306,8 @@ def main():
     }
 
     if args.cpu_seconds > 0 and args.mode == "sample":
+        call(0)                        # slice 0 again, for the parity comparison
+        torch.cuda.synchronize()
         line["cpu_baseline"] = cpu_baseline(w, out_t, out_n, args.cpu_seconds)
     if args.calibrate_copy:
         calibrate_copy()
