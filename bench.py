@@ -315,11 +315,16 @@ def main():
 
 
 def cpu_baseline(w, out_t, out_n, budget_s):
-    """The CPU oracle, as written (one thread, double precision), timed on the
-    sequences of the same workload, in order, passing over the batch again if
-    needed, until `budget_s` of oracle time is spent.  Host copies are outside
-    the timed part.  The oracle's results on the first pass are compared with
-    the GPU's last call."""
+    """The CPU oracle, as written (double precision, one sequence after
+    another), timed on a bounded sample of the same workload: the first
+    sequences of the batch, copied to host memory outside the timed part, run
+    repeatedly until the budget is spent.  First on one thread (a quarter of
+    the budget), then on every host core the process may use (the oracle is
+    a C library; ctypes releases the interpreter lock around each call, so
+    the threads run in parallel).  The oracle's results on the sample are also
+    compared with the GPU's call on the same sequences."""
+    import threading
+
     import numpy as np
 
     import oracle
@@ -327,38 +332,58 @@ def cpu_baseline(w, out_t, out_n, budget_s):
     if not os.path.exists(oracle.LIB_PATH):
         oracle.build()
     B, k1, V = w.target.shape
-    chunk = 16
-    done, spent, passes = 0, 0.0, 0
-    gt = out_t.cpu().numpy()
-    gn = out_n.cpu().numpy()
-    rep = parity.SampleReport()
-    while spent < budget_s:
-        for b0 in range(0, B, chunk):
-            b1 = min(B, b0 + chunk)
-            z = w.target[b0:b1].float().cpu().numpy()
-            y = w.draft[b0:b1].float().cpu().numpy()
-            x = w.tokens[b0:b1].cpu().numpy()
-            u = w.uniforms[b0:b1].cpu().numpy()
-            t0 = time.perf_counter()
-            oracle.sample(z, y, x, u, w.T)
-            spent += time.perf_counter() - t0
-            done += b1 - b0
-            if passes == 0:
-                parity.check_sample(z, y, x, u, w.T, gt[b0:b1], gn[b0:b1], report=rep,
-                                    seq_ids=np.arange(b0, b1))
-            if spent >= budget_s:
-                break
-        passes += 1
+    nseq = min(B, 64)
+    z = w.target[:nseq].float().cpu().numpy()
+    y = w.draft[:nseq].float().cpu().numpy()
+    x = w.tokens[:nseq].cpu().numpy()
+    u = w.uniforms[:nseq].cpu().numpy()
+    rep = parity.check_sample(z, y, x, u, w.T, out_t[:nseq].cpu().numpy(), out_n[:nseq].cpu().numpy(),
+                              seq_ids=np.arange(nseq))
+    chunk = 4
+    starts = list(range(0, nseq, chunk))
+
+    def run(threads, seconds):
+        lock = threading.Lock()
+        state = {"next": 0, "seqs": 0}
+        stop = time.perf_counter() + seconds
+
+        def worker():
+            while time.perf_counter() < stop:
+                with lock:
+                    i = state["next"]
+                    state["next"] += 1
+                b0 = starts[i % len(starts)]
+                b1 = min(nseq, b0 + chunk)
+                oracle.sample(z[b0:b1], y[b0:b1], x[b0:b1], u[b0:b1], w.T)
+                with lock:
+                    state["seqs"] += b1 - b0
+        t0 = time.perf_counter()
+        ts = [threading.Thread(target=worker) for _ in range(threads)]
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join()
+        return state["seqs"], time.perf_counter() - t0
+
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(16, cores))
+    s1, t1 = run(1, budget_s / 4)
+    sn, tn = run(cores, budget_s * 3 / 4)
     return {
-        "value": done * k1 / spent,
+        "value": sn * k1 / tn,
         "unit": "rows/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
-        "sample": (f"{done} sequences ({done * k1} rows) of the same workload, in batch order"
-                   f"{' over ' + str(passes) + ' passes' if passes > 1 else ''}; single-threaded "
-                   f"C oracle in double precision, {spent:.1f} s; it stops at each sequence's "
-                   f"first rejection, so it reads fewer rows than it counts"),
-        "parity_vs_gpu_first_pass": rep.summary(),
+        "value_1_core": s1 * k1 / t1,
+        "sample": (f"the first {nseq} sequences of the same workload ({nseq * k1} rows), run "
+                   f"repeatedly in chunks of {chunk}: {s1} sequences on 1 thread in {t1:.1f} s, "
+                   f"then {sn} sequences on {cores} threads in {tn:.1f} s; C oracle in double "
+                   f"precision, unchanged; it stops at each sequence's first rejection, so it "
+                   f"reads fewer rows than it counts"),
+        "parity_vs_gpu": rep.summary(),
     }
 
 
