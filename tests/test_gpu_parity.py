@@ -519,3 +519,34 @@ def test_side_stream_and_profile(sv):
         sv.greedy(w.target, w.tokens)
     ms = sv.profile_end()
     assert len(ms) == 2 and all(m > 0 for m in ms)
+
+
+# ---------------------------------------------------------------------------
+# extremes of the shape space
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("V", [262144, 262147])
+def test_large_vocabulary(sv, V):
+    """Vocabularies past the workloads' (262144 is the largest in common use):
+    more slices per row and a ragged tail at the odd size."""
+    g = torch.Generator(device=DEV).manual_seed(V)
+    w = synthetic.chain(4, 3, V, "bf16", var_target=3.0, var_noise=2.0, spike=8.0, seed=V, device=DEV)
+    rep = assert_sample_parity(w, *run_sample(sv, w))
+    assert rep.rounds == 4
+    x = corrupt_after_argmax(w.target, 3, g)
+    toks, na = sv.greedy(w.target, x)
+    torch.cuda.synchronize()
+    bad, _, _ = parity.check_greedy(f32(w.target), npi(x), npi(toks), npi(na))
+    assert not bad
+
+
+def test_many_short_rows(sv):
+    """4096 sequences of 300-token rows: far more sequences than workgroups
+    per sequence, one slice per row."""
+    g = torch.Generator(device=DEV).manual_seed(4096)
+    w = synthetic.chain(4096, 2, 300, "fp16", seed=4096, device=DEV)
+    assert_sample_parity(w, *run_sample(sv, w))
+    x = corrupt_after_argmax(w.target, 2, g)
+    toks, na = sv.greedy(w.target, x)
+    torch.cuda.synchronize()
+    bad, _, _ = parity.check_greedy(f32(w.target), npi(x), npi(toks), npi(na))
+    assert not bad

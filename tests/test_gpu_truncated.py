@@ -229,3 +229,18 @@ def test_truncated_many_equal_logits(sv, dtype):
     for top_k, top_p in ((100, 1.0), (0, 0.9), (70000, 0.5), (3, 0.99)):
         x = torch.from_numpy(truncated_drafts(f32(y), 1.0, top_k, top_p, 9)).to(DEV)
         check(sv, w, 1.0, x, top_k, top_p)
+
+
+def test_truncated_fp32_large_vocabulary(sv):
+    """fp32 rows take the radix passes (three digits); at V = 128256."""
+    w, T, x = workload(2, 2, 128256, "fp32", 61, 50, 0.8)
+    check(sv, w, T, x, 50, 0.8)
+    w, T, x = workload(2, 2, 128256, "fp32", 62, 0, 0.95)
+    check(sv, w, T, x, 0, 0.95)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_truncated_k63(sv, dtype):
+    """The longest draft one wave decides (k = 63)."""
+    w, T, x = workload(3, 63, 1000, dtype, 63, 10, 0.9)
+    check(sv, w, T, x, 10, 0.9)
