@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "sv_launch.h"
 
 namespace sv {
@@ -176,25 +178,62 @@ __device__ __forceinline__ void merge_soft(const SoftPartial* p, int splits, flo
 }
 
 // ---- fixed-order workgroup collectives -------------------------------------
+// Wave reductions in DPP: rotations by 1, 2, 4 and 8 lanes inside each row of
+// 16 leave every lane holding its row's result; the four rows' results are
+// then read as scalars and combined in row order, the same on every lane.
+// No LDS round trip.
+template <int N>
+__device__ __forceinline__ uint32_t row_ror(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x120 + N, 0xf, 0xf, false);
+}
+
+__device__ __forceinline__ float row_ror_f(float x, int n)
+{
+    switch (n) {
+    case 1: return __uint_as_float(row_ror<1>(__float_as_uint(x)));
+    case 2: return __uint_as_float(row_ror<2>(__float_as_uint(x)));
+    case 4: return __uint_as_float(row_ror<4>(__float_as_uint(x)));
+    default: return __uint_as_float(row_ror<8>(__float_as_uint(x)));
+    }
+}
+
+__device__ __forceinline__ int row_ror_i(int x, int n)
+{
+    switch (n) {
+    case 1: return (int)row_ror<1>((uint32_t)x);
+    case 2: return (int)row_ror<2>((uint32_t)x);
+    case 4: return (int)row_ror<4>((uint32_t)x);
+    default: return (int)row_ror<8>((uint32_t)x);
+    }
+}
+
+__device__ __forceinline__ float lane_f(float x, int l)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
 __device__ __forceinline__ float wave_max(float v)
 {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+    for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, row_ror_f(v, o));
+    return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
 __device__ __forceinline__ int wave_min_int(int v)
 {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
-    return v;
+    for (int o = 1; o < 16; o <<= 1) v = min(v, row_ror_i(v, o));
+    return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+               min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
 
 __device__ __forceinline__ int wave_max_int(int v)
 {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
-    return v;
+    for (int o = 1; o < 16; o <<= 1) v = max(v, row_ror_i(v, o));
+    return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+               max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
 
 // Block-wide reductions over a workgroup of NW wave64s; `lds` holds at least
@@ -244,17 +283,26 @@ __device__ __forceinline__ int block_max_int(int v, int* lds)
 // block total, bitwise equal to the last thread's inclusive value.
 __device__ __forceinline__ float block_scan(float x, float* excl, float* total, float* lds)
 {
-    const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
+    // inclusive scan of the wave in DPP: row shifts, then row broadcasts
+    // (disabled lanes and rows add +0.0)
+    auto dpp = [](float v, auto ctrl, auto rows, auto bc) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value,
+                                                          decltype(rows)::value, 0xf, decltype(bc)::value));
+    };
+    using B1 = std::integral_constant<bool, true>;
+    using B0 = std::integral_constant<bool, false>;
+    using RA = std::integral_constant<int, 0xf>;
     float incl = x;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        float y = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += y;
-    }
-    float wex = __shfl_up(incl, 1, 64);
-    if (lane == 0) wex = 0.f;
-    if (lane == 63) lds[w] = incl;
+    incl += dpp(incl, std::integral_constant<int, 0x111>{}, RA{}, B1{});   // row_shr:1
+    incl += dpp(incl, std::integral_constant<int, 0x112>{}, RA{}, B1{});   // row_shr:2
+    incl += dpp(incl, std::integral_constant<int, 0x114>{}, RA{}, B1{});   // row_shr:4
+    incl += dpp(incl, std::integral_constant<int, 0x118>{}, RA{}, B1{});   // row_shr:8
+    incl += dpp(incl, std::integral_constant<int, 0x142>{}, std::integral_constant<int, 0xa>{}, B0{});  // row_bcast:15
+    incl += dpp(incl, std::integral_constant<int, 0x143>{}, std::integral_constant<int, 0xc>{}, B0{});  // row_bcast:31
+    // the previous lane's inclusive value (0 for lane 0): wave_shr:1
+    const float wex = dpp(incl, std::integral_constant<int, 0x138>{}, RA{}, B1{});
+    if ((threadIdx.x & 63) == 63) lds[w] = incl;
     __syncthreads();
     float pre = 0.f;
     for (int i = 0; i < w; ++i) pre += lds[i];

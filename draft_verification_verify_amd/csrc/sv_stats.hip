@@ -99,11 +99,15 @@ __device__ __forceinline__ SoftPartial slice_softmax(const char* rp, int v0, int
         soft_update<kVec>(e, m, s, c);
     }
 
+    // the wave: DPP rotations inside each row of 16, then the four rows in order
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        float m2 = __shfl_xor(m, o, 64);
-        float s2 = __shfl_xor(s, o, 64);
-        soft_merge(m, s, m2, s2, c);
+    for (int o = 1; o < 16; o <<= 1) soft_merge(m, s, row_ror_f(m, o), row_ror_f(s, o), c);
+    {
+        float wm = lane_f(m, 0), ws = lane_f(s, 0);
+#pragma unroll
+        for (int r = 1; r < 4; ++r) soft_merge(wm, ws, lane_f(m, 16 * r), lane_f(s, 16 * r), c);
+        m = wm;
+        s = ws;
     }
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     if (lane == 0) {
