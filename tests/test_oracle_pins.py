@@ -731,3 +731,66 @@ def test_truncation_off_is_the_rule():
         t2, n2 = oracle.sample_truncated(z, y, x, u, 0.8, top_k, top_p)
         np.testing.assert_array_equal(t1, t2)
         np.testing.assert_array_equal(n1, n2)
+
+
+# ---------------------------------------------------------------------------
+# The exported probabilities and the draw's CDF intervals (used by the parity
+# checks), pinned outside the functions themselves
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T", [0.7, 1.0, 1.3])
+def test_token_probs_are_softmax_entries(T):
+    """p_i(x_i), q_i(x_i) are softmax(z_i / T)[x_i] and softmax(y_i / T)[x_i]
+    (scipy's softmax); an invalid token reports 0 for both."""
+    import scipy.special
+    rng = np.random.default_rng(31)
+    k, V = 5, 257
+    z = rng.normal(0, 2, (k + 1, V)).astype(np.float32)
+    y = (z[:k] + rng.normal(0, 1, (k, V))).astype(np.float32)
+    x = rng.integers(0, V, k).astype(np.int32)
+    x[3] = V + 4                                   # outside the vocabulary
+    px, qx = oracle.token_probs(z, y, x, T)
+    for i in range(k):
+        if i == 3:
+            assert px[i] == 0.0 and qx[i] == 0.0
+            continue
+        ref_p = scipy.special.softmax(z[i].astype(np.float64) / T)[x[i]]
+        ref_q = scipy.special.softmax(y[i].astype(np.float64) / T)[x[i]]
+        np.testing.assert_allclose(px[i], ref_p, rtol=1e-12)
+        np.testing.assert_allclose(qx[i], ref_q, rtol=1e-12)
+
+
+def test_draw_intervals_tile_and_match_the_draws():
+    """The intervals of all tokens tile [0, 1) in index order (zero-weight
+    tokens get empty ones), and a uniform at an interval's midpoint makes the
+    rule's own draw (pinned by the V = 8 law) pick that token: after a forced
+    rejection (residual against the draft row) and for the bonus (target row)."""
+    rng = np.random.default_rng(32)
+    V, T = 8, 1.0
+    P = rng.dirichlet(np.ones(V))
+    P[2] = 0.0
+    P /= P.sum()
+    Q = rng.dirichlet(np.ones(V))
+    with np.errstate(divide="ignore"):         # token 2 has p = 0: logit -inf
+        z = np.log(np.stack([P, rng.dirichlet(np.ones(V))])).astype(np.float32)   # rows 0 and 1 (bonus)
+    y = np.log(Q)[None].astype(np.float32)
+    x0 = int(np.argmax(Q / np.maximum(P, 1e-30)))  # a token with q > p: rejectable
+    for row, drow in ((0, y[0]), (1, None)):
+        iv = [oracle.draw_interval(z[row], drow, T, t) for t in range(V)]
+        lo = np.array([a for a, _, _ in iv])
+        hi = np.array([b for _, b, _ in iv])
+        w = np.array([c for _, _, c in iv])
+        assert lo[0] == 0.0 and abs(hi[-1] - 1.0) < 1e-12
+        np.testing.assert_allclose(lo[1:], hi[:-1], atol=1e-15)
+        assert ((hi - lo > 0) == (w > 0)).all()
+        for t in range(V):
+            if w[t] <= 0:
+                continue
+            um = np.float32((lo[t] + hi[t]) / 2)
+            if row == 0:       # reject x0 (u0 just below 1), then draw with um
+                u = np.array([[np.float32(1 - 2 ** -24), um]], np.float32)
+            else:              # accept x0 (u0 = 0 and p(x0) > 0 needed), bonus with um
+                u = np.array([[0.0, um]], np.float32)
+            xs = np.array([[x0 if row == 0 else int(np.argmax(P))]], np.int32)
+            toks, na = oracle.sample(z[None], y[None], xs, u, T)
+            assert na[0] == (0 if row == 0 else 1)
+            assert toks[0, na[0]] == t, (row, t, toks)
