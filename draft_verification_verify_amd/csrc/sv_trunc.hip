@@ -527,9 +527,11 @@ __global__ __launch_bounds__(kT16) void k_trunc16(TruncArgs a)
         for (int u = 0; u < kAhead; ++u)
             if (t + u * kT16 < nfull) ahead[u] = load_raw<DT, VEC>(rp, t + u * kT16);
     }
+    // The histogram is zeroed once here; after each row, only the chunks that
+    // row touched are zeroed again, each by the thread that summed it.
+    for (int i = t; i < kWords / 4; i += kT16) h4[i] = u32x4{0u, 0u, 0u, 0u};
     for (; row < a.n_rows; row += gridDim.x) {
     const char* rp = row_of(row);
-    for (int i = t; i < kWords / 4; i += kT16) h4[i] = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
 
     // the pass: count every pattern (the first kAhead vectors are already here)
@@ -588,8 +590,9 @@ __global__ __launch_bounds__(kT16) void k_trunc16(TruncArgs a)
     const int cp = 16 * lane + wv;
     const int bc = cp < 512 ? 511 - cp : cp;                  // its pattern chunk
     uint32_t my_cnt = 0;
+    u32x4* const cw = h4 + 8 * bc;
+    bool dirty;
     {
-        const u32x4* cw = h4 + 8 * bc;
 #pragma unroll
         for (int g = 0; g < 8; ++g) {
             const u32x4 q = cw[(g + lane) & 7];
@@ -598,6 +601,7 @@ __global__ __launch_bounds__(kT16) void k_trunc16(TruncArgs a)
             my_cnt = add_halves(q.z, my_cnt);
             my_cnt = add_halves(q.w, my_cnt);
         }
+        dirty = my_cnt != 0u;          // a nonzero word has a nonzero half
         // whole-word counters and the -0.0 / +0.0 merge
         if (bc == (int)(ninf_bits<DT>() >> 6)) my_cnt += ninf - add_halves(ninf, 0u);
         if (bc == (int)(pinf_bits<DT>() >> 6)) {
@@ -625,15 +629,23 @@ __global__ __launch_bounds__(kT16) void k_trunc16(TruncArgs a)
         total += sc.wcnt[i];
         cmax = min(cmax, sc.wmin[i]);
     }
+    // after every reader of the row's histogram is done: zero this thread's chunk
+    auto clear_chunk = [&]() {
+        __syncthreads();
+        if (dirty) {
+#pragma unroll
+            for (int g = 0; g < 8; ++g) cw[(g + lane) & 7] = u32x4{0u, 0u, 0u, 0u};
+        }
+    };
     if (total != (uint32_t)V) {        // a half overflowed: leave the row to the radix kernel
         if (t == 0) a.rows[row] = TruncRow{0.f, 0.f, 0u, 1u};
-        __syncthreads();
+        clear_chunk();
         continue;
     }
     const uint32_t finite = total - ninf;
     if (finite == 0) {                 // every logit is -inf
         if (t == 0) a.rows[row] = TruncRow{-INFINITY, -INFINITY, 0u, 0u};
-        __syncthreads();
+        clear_chunk();
         continue;
     }
 
@@ -739,7 +751,7 @@ __global__ __launch_bounds__(kT16) void k_trunc16(TruncArgs a)
         const float l2s = (float)(log2((double)kept) - (double)kFixBits);
         a.rows[row] = TruncRow{m, l2s, 65535u - dtau, 0u};
     }
-    __syncthreads();                   // LDS is cleared for the next row
+    clear_chunk();
     }
 }
 
