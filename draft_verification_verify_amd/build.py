@@ -63,5 +63,26 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+CLIENT_SRC = os.path.join(ROOT, "tests", "c_client", "sv_client.c")
+CLIENT_BIN = os.path.join(ROOT, "tests", "c_client", "sv_client")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
+def build_client(verbose: bool = False) -> str:
+    """The plain C client of the boundary (tests/c_client): gcc, C99, linked
+    against libspecverify.so and the HIP runtime, no Python or torch."""
+    cmd = ["gcc", "-std=c99", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__", f"-I{INCLUDE}",
+           f"-I{ROCM}/include", CLIENT_SRC, "-o", CLIENT_BIN, f"-L{HERE}", "-lspecverify",
+           f"-L{ROCM}/lib", "-lamdhip64", f"-Wl,-rpath,$ORIGIN/../../draft_verification_verify_amd",
+           f"-Wl,-rpath,{ROCM}/lib"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"client build failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print("built", CLIENT_BIN)
+    return CLIENT_BIN
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    build_client(verbose=True)

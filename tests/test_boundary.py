@@ -256,3 +256,19 @@ def test_truncated_reject_bad_arguments(sv):
     assert call(50, 0.9, wsb=8) == sv.SV_EWORKSPACE
     assert call(0, 1.0, wsb=8) == sv.SV_EWORKSPACE
     assert (out == SENT).all()
+
+
+def test_c_client_host_side():
+    """A plain C99 program (no Python, no torch) links the library and checks
+    the host side of the boundary through include/spec_verify.h alone."""
+    import importlib.util
+    import subprocess
+    spec = importlib.util.spec_from_file_location(
+        "_sv_build", os.path.join(ROOT, "draft_verification_verify_amd", "build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    if not os.path.exists(b.CLIENT_BIN):
+        b.build_client()
+    r = subprocess.run([b.CLIENT_BIN], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stderr
+    assert "all checks passed" in r.stdout

@@ -2,7 +2,8 @@
 sets memory with a memset, or synchronises, so a caller can capture a call
 into a graph and replay it on new inputs.  Each replay here runs on inputs
 copied into the captured buffers, with eager work and synchronisations in
-between, and must equal an eager call on the same inputs bit for bit."""
+between, and must equal an eager call on the same inputs bit for bit.  Calls
+on several streams with their own workspaces may also overlap."""
 import os
 
 import pytest
@@ -127,3 +128,33 @@ def test_candidates_replay(sv):
 
     g, outs = capture(run)
     replay_and_compare(g, outs, load, eager, len(sets))
+
+
+def test_calls_on_concurrent_streams(sv):
+    """Calls on different streams with their own workspaces may overlap: four
+    streams, each with its own inputs, launched back to back with no
+    synchronisation in between, equal the same calls made one at a time."""
+    B, k, V = 96, 8, 32000
+    sets = chain_sets(4, B, k, V, "bf16")
+    streams = [torch.cuda.Stream() for _ in sets]
+    wss = [torch.empty(sv.workspace_bytes(B, 2 * k + 1, V, torch.bfloat16), dtype=torch.uint8, device=DEV)
+           for _ in sets]
+    ref = []
+    for w in sets:
+        ref.append(sv.sample(w.target, w.draft, w.tokens, w.uniforms, w.T, return_probs=True))
+        ref.append(sv.greedy(w.target, w.tokens))
+    torch.cuda.synchronize()
+    got = [None] * len(ref)
+    for rep in range(3):
+        for i, (w, s, ws) in enumerate(zip(sets, streams, wss)):
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                got[2 * i] = sv.sample(w.target, w.draft, w.tokens, w.uniforms, w.T, return_probs=True,
+                                       workspace=ws, stream=s)
+        for i, (w, s, ws) in enumerate(zip(sets, streams, wss)):
+            with torch.cuda.stream(s):
+                got[2 * i + 1] = sv.greedy(w.target, w.tokens, workspace=ws, stream=s)
+        torch.cuda.synchronize()
+        for a, b in zip(got, ref):
+            for x, y in zip(a, b):
+                assert torch.equal(x, y), rep
