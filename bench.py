@@ -285,9 +285,12 @@ def main():
             "kernel": {"sample": "k_softmax_stats", "lenient": "k_softmax_stats",
                        "truncated": "k_trunc16" if es == 2 else "k_trunc_rows"}.get(
                            args.mode, "k_argmax_stats"),
-            "note": ("the timed launch is k_trunc16 (one pass per 16-bit row: an exact LDS "
-                     "histogram of all 65536 bit patterns) and k_trunc_rows over the rows it "
-                     "marked (none here); algorithmic bytes: every row read once")
+            "note": (("the timed launch is k_trunc16 (one pass per 16-bit row: an exact LDS "
+                      "histogram of all 65536 bit patterns) followed by k_trunc_rows over the "
+                      "rows it marked; algorithmic bytes: every row read once") if es == 2 else
+                     ("the timed launch is k_trunc_rows (radix selection, one workgroup per "
+                      "row; the first digit's pass reads the row from HBM, later ones mostly "
+                      "from cache); algorithmic bytes: every row read once"))
             if args.mode == "truncated" else (
                 "rows counts every scored candidate position (B*C*R); the kernel reads "
                 "B*N unique node rows") if args.mode == "tree" else None,

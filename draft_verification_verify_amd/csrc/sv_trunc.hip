@@ -425,15 +425,24 @@ __device__ __forceinline__ uint32_t count_bits(const uint32_t* hist, uint32_t bi
     return bits == 0u ? c + negzero : c;
 }
 
+// Per-chunk counts and masses are stored owner-major: chunk position
+// p = 16 * lane + wave sits at slot(p) = 68 * (p % 16) + p / 16, so a wave's
+// own 64 chunks are 64 consecutive slots, and 64 consecutive positions
+// (p = 64 g + lane) fall in 64 different banks (68 = 4 mod 64).
+constexpr int kSlotStride = 68;
+__device__ __forceinline__ int slot_of(int p)
+{
+    return kSlotStride * (p & 15) + (p >> 4);
+}
+
 struct Scratch16 {
-    uint32_t cnt[kChunks];             // chunk counts, by chunk position
-    u64 mass[kChunks];                 // chunk masses, by chunk position
-    u64 gmass[kW16];                   // masses of 64-chunk groups
+    uint32_t cnt[kSlotStride * 16];    // chunk counts, by slot
+    u64 mass[kSlotStride * 16];        // chunk masses, by slot
     uint32_t wcnt[kW16];
     int wmin[kW16];
+    int state;                         // 0: analyse; 1: overflowed half; 2: every logit -inf
     uint32_t d;
     uint32_t dk;
-    u64 incl;
 };
 
 // ---- wave scans in DPP (row shifts, then row broadcasts), no LDS ----------
@@ -500,85 +509,120 @@ __device__ __forceinline__ uint32_t add_halves(uint32_t w, uint32_t acc)
     return __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, w), u16x2{1, 1}, acc, false);
 }
 
-// Persistent: workgroup g takes rows g, g + gridDim.x, ...  While it
-// analyses one row, the first round of its next row is already loading.
+// floor(w * 2^40) for w in [0, 1] without branches, equal to fixed40(w):
+// f = w * 2^40 is exact, and so are its high part floor(f / 2^32) and the
+// remainder f - high * 2^32 (a multiple of f's last place, below 2^32).
+__device__ __forceinline__ u64 fixed40_nb(float w)
+{
+    const float f = w * 1099511627776.0f;                     // 2^40
+    const float hf = truncf(f * 2.3283064365386963e-10f);     // 2^-32
+    const uint32_t hi = (uint32_t)hf;
+    const uint32_t lo = (uint32_t)(f - hf * 4294967296.0f);
+    return ((u64)hi << 32) | lo;
+}
+
+// The sum over each row of 16 lanes, in every lane of the row.
+__device__ __forceinline__ u64 row_sum_u64(u64 x)
+{
+    x += dpp64<0x121, 0xf, false>(x);  // row_ror:1
+    x += dpp64<0x122, 0xf, false>(x);  // row_ror:2
+    x += dpp64<0x124, 0xf, false>(x);  // row_ror:4
+    x += dpp64<0x128, 0xf, false>(x);  // row_ror:8
+    return x;
+}
+
+// Persistent: workgroup g takes rows g, g + gridDim.x, ...  Its rows form
+// one stream of rounds (four vectors per thread each, a row padded to an even
+// number of rounds); two round buffers in registers alternate, and a buffer
+// reloads the round two ahead as soon as it has been counted, so loads stay
+// in flight across row ends: the next row's first two rounds arrive while the
+// current row is analysed.  Every load is issued unconditionally (indices past
+// a row's end, and rounds past the last row, read the row's first vector
+// again, and only counting is predicated), which keeps the loads countable:
+// each count waits for its own round's loads only.  Needs V >= 8.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kT16) void k_trunc16(TruncArgs a)
 {
     constexpr int ES = 2;
-    constexpr int kAhead = 4;          // vectors per thread loaded ahead
+    constexpr int kRound = 4 * kT16;   // vectors per round
     __shared__ __attribute__((aligned(16))) uint32_t hist[kWords];
     __shared__ __attribute__((aligned(16))) Scratch16 sc;
     const int V = a.V;
     const int t = (int)threadIdx.x;
     const int lane = t & 63, wv = t >> 6;
     const int nfull = V >> 3;
+    const int R2 = 2 * ((nfull + 2 * kRound - 1) / (2 * kRound));   // rounds per row, even
     u32x4* h4 = reinterpret_cast<u32x4*>(hist);
     auto row_of = [&](int r) -> const char* {
         return r < a.n_target_rows ? row_ptr(a.target, r, a.t_stride, ES)
                                    : row_ptr(a.draft, r - a.n_target_rows, a.d_stride, ES);
     };
 
-    Raw<DT> ahead[kAhead];
-    int row = blockIdx.x;
-    if (row < a.n_rows) {
-        const char* rp = row_of(row);
+    // issue cursor: round ir of row irow
+    int irow = blockIdx.x, ir = 0;
+    auto issue = [&](Raw<DT> (&buf)[4]) {
+        const bool live = irow < a.n_rows;
+        const char* p = row_of(live ? irow : (int)blockIdx.x);
+        const int v0 = ir * kRound + t;
 #pragma unroll
-        for (int u = 0; u < kAhead; ++u)
-            if (t + u * kT16 < nfull) ahead[u] = load_raw<DT, VEC>(rp, t + u * kT16);
-    }
+        for (int u = 0; u < 4; ++u) {
+            const int v = v0 + u * kT16;
+            buf[u] = load_raw<DT, VEC>(p, live && v < nfull ? v : 0);
+        }
+        if (++ir == R2) {
+            ir = 0;
+            irow += (int)gridDim.x;
+        }
+    };
+    auto count = [&](const Raw<DT> (&buf)[4], int ri) {
+        const int v0 = ri * kRound + t;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (v0 + u * kT16 < nfull) {
+                count_word(hist, buf[u].a.x);
+                count_word(hist, buf[u].a.y);
+                count_word(hist, buf[u].a.z);
+                count_word(hist, buf[u].a.w);
+            }
+        }
+    };
+
+    Raw<DT> bufA[4], bufB[4];
+    issue(bufA);
+    issue(bufB);
     // The histogram is zeroed once here; after each row, only the chunks that
     // row touched are zeroed again, each by the thread that summed it.
     for (int i = t; i < kWords / 4; i += kT16) h4[i] = u32x4{0u, 0u, 0u, 0u};
-    for (; row < a.n_rows; row += gridDim.x) {
+    // thread 0's finished row, whose summary (with its fp64 log) is written
+    // while the next row streams rather than inside the analysis
+    int pend_row = -1;
+    float pend_m = 0.f;
+    u64 pend_kept = 0;
+    uint32_t pend_tau = 0;
+    auto flush = [&]() {
+        if (t == 0 && pend_row >= 0) {
+            const float l2s = (float)(log2((double)pend_kept) - (double)kFixBits);
+            a.rows[pend_row] = TruncRow{pend_m, l2s, pend_tau, 0u};
+            pend_row = -1;
+        }
+    };
+    for (int row = blockIdx.x; row < a.n_rows; row += gridDim.x) {
     const char* rp = row_of(row);
     __syncthreads();
+    flush();
 
-    // the pass: count every pattern (the first kAhead vectors are already here)
-#pragma unroll
-    for (int u = 0; u < kAhead; ++u) {
-        if (t + u * kT16 < nfull) {
-            count_word(hist, ahead[u].a.x);
-            count_word(hist, ahead[u].a.y);
-            count_word(hist, ahead[u].a.z);
-            count_word(hist, ahead[u].a.w);
-        }
-    }
-    int v = t + kAhead * kT16;
-    for (; v + 3 * kT16 < nfull; v += 4 * kT16) {
-        Raw<DT> r[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) r[u] = load_raw<DT, VEC>(rp, v + u * kT16);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            count_word(hist, r[u].a.x);
-            count_word(hist, r[u].a.y);
-            count_word(hist, r[u].a.z);
-            count_word(hist, r[u].a.w);
-        }
-    }
-    for (; v < nfull; v += kT16) {
-        const Raw<DT> r = load_raw<DT, VEC>(rp, v);
-        count_word(hist, r.a.x);
-        count_word(hist, r.a.y);
-        count_word(hist, r.a.z);
-        count_word(hist, r.a.w);
+    // the pass: count every pattern
+    for (int ri = 0; ri < R2; ri += 2) {
+        count(bufA, ri);
+        issue(bufA);
+        count(bufB, ri + 1);
+        issue(bufB);
     }
     if (t == nfull % kT16 && 8 * nfull < V) {   // the partial last vector: one thread
         const unsigned short* e = reinterpret_cast<const unsigned short*>(rp) + 8LL * nfull;
         for (int j = 0; j < V - 8 * nfull; ++j) {
             const uint32_t b = e[j];
             atomicAdd(&hist[b >> 1], (b & 1u) * 0xFFFFu + 1u);
-        }
-    }
-    // the next row's first vectors load during the analysis
-    {
-        const int nrow = row + (int)gridDim.x;
-        if (nrow < a.n_rows) {
-            const char* np = row_of(nrow);
-#pragma unroll
-            for (int u = 0; u < kAhead; ++u)
-                if (t + u * kT16 < nfull) ahead[u] = load_raw<DT, VEC>(np, t + u * kT16);
         }
     }
     __syncthreads();
@@ -611,7 +655,8 @@ __global__ __launch_bounds__(kT16) void k_trunc16(TruncArgs a)
         if (bc == 512) my_cnt -= negzero;
         if (bc == 0) my_cnt += negzero;
     }
-    sc.cnt[cp] = my_cnt;
+    const int own = kSlotStride * wv + lane;                  // slot_of(cp)
+    sc.cnt[own] = my_cnt;
     const uint32_t fin_cnt = bc == (int)(ninf_bits<DT>() >> 6) ? my_cnt - ninf : my_cnt;
     {
         const uint32_t wt = lane63_u32(wave_scan_u32(my_cnt));
@@ -621,14 +666,6 @@ __global__ __launch_bounds__(kT16) void k_trunc16(TruncArgs a)
             sc.wmin[wv] = ne ? 16 * (__ffsll((long long)ne) - 1) + wv : INT32_MAX;
         }
     }
-    __syncthreads();
-    uint32_t total = 0;
-    int cmax = INT32_MAX;
-#pragma unroll
-    for (int i = 0; i < kW16; ++i) {
-        total += sc.wcnt[i];
-        cmax = min(cmax, sc.wmin[i]);
-    }
     // after every reader of the row's histogram is done: zero this thread's chunk
     auto clear_chunk = [&]() {
         __syncthreads();
@@ -637,122 +674,154 @@ __global__ __launch_bounds__(kT16) void k_trunc16(TruncArgs a)
             for (int g = 0; g < 8; ++g) cw[(g + lane) & 7] = u32x4{0u, 0u, 0u, 0u};
         }
     };
-    if (total != (uint32_t)V) {        // a half overflowed: leave the row to the radix kernel
-        if (t == 0) a.rows[row] = TruncRow{0.f, 0.f, 0u, 1u};
-        clear_chunk();
-        continue;
-    }
-    const uint32_t finite = total - ninf;
-    if (finite == 0) {                 // every logit is -inf
-        if (t == 0) a.rows[row] = TruncRow{-INFINITY, -INFINITY, 0u, 0u};
-        clear_chunk();
-        continue;
-    }
+    __syncthreads();
 
-    // wave 0: the max (first nonempty position of chunk cmax), then top-k
+    // wave 0: the row's count, the max (first nonempty position of the first
+    // nonempty chunk), then top-k
     if (wv == 0) {
-        {
-            const uint32_t d = 64u * cmax + lane;
-            const uint32_t b = bits_at(d);
-            const bool nz = b != ninf_bits<DT>() && count_bits<DT>(hist, b, negzero) != 0u;
-            const unsigned long long hit = __ballot(nz);
-            if (lane == 0) sc.d = 64u * cmax + (uint32_t)(__ffsll((long long)hit) - 1);
-        }
-        uint32_t dk = 65535u;          // positions <= dk survive top-k
-        if (a.top_k >= 1 && (uint32_t)a.top_k < finite) {
-            const uint32_t need = (uint32_t)a.top_k;
-            uint32_t base = 0;
-            int ch = -1;
-            for (int g = 0; g < kChunks / 64 && ch < 0; ++g) {   // uniform across the wave
-                const uint32_t x = sc.cnt[64 * g + lane];
-                const uint32_t incl = base + wave_scan_u32(x);
-                const unsigned long long hit = __ballot(incl >= need);
-                if (hit) {
-                    const int f = __ffsll((long long)hit) - 1;
-                    ch = 64 * g + f;
-                    base = (uint32_t)__builtin_amdgcn_readlane((int)(incl - x), f);
-                } else {
-                    base = lane63_u32(incl);
-                }
+        const uint32_t total = lane63_u32(wave_scan_u32(lane < kW16 ? sc.wcnt[lane] : 0u));
+        const int cmax = wave_min_int(lane < kW16 ? sc.wmin[lane] : INT32_MAX);
+        const uint32_t finite = total - ninf;
+        // a half overflowed: the row goes to the radix kernel
+        const int state = total != (uint32_t)V ? 1 : finite == 0 ? 2 : 0;
+        uint32_t d = 0, dk = 65535u;   // positions <= dk survive top-k
+        if (state == 0) {
+            {
+                const uint32_t dd = 64u * cmax + lane;
+                const uint32_t bb = bits_at(dd);
+                const bool nz = bb != ninf_bits<DT>() && count_bits<DT>(hist, bb, negzero) != 0u;
+                const unsigned long long hit = __ballot(nz);
+                d = 64u * cmax + (uint32_t)(__ffsll((long long)hit) - 1);
             }
-            if (ch < 0) ch = kChunks - 1;                 // unreachable: top_k < finite
-            const uint32_t d = 64u * ch + lane;
-            const uint32_t incl = base + wave_scan_u32(count_bits<DT>(hist, bits_at(d), negzero));
-            const unsigned long long hit = __ballot(incl >= need);
-            dk = 64u * ch + (uint32_t)(__ffsll((long long)hit) - 1);
+            if (a.top_k >= 1 && (uint32_t)a.top_k < finite) {
+                const uint32_t need = (uint32_t)a.top_k;
+                uint32_t base = 0;
+                int ch = -1;
+                for (int g = cmax >> 6; g < kChunks / 64 && ch < 0; ++g) {   // uniform; earlier chunks are empty
+                    const uint32_t x = sc.cnt[slot_of(64 * g + lane)];
+                    const uint32_t incl = base + wave_scan_u32(x);
+                    const unsigned long long hit = __ballot(incl >= need);
+                    if (hit) {
+                        const int f = __ffsll((long long)hit) - 1;
+                        ch = 64 * g + f;
+                        base = (uint32_t)__builtin_amdgcn_readlane((int)(incl - x), f);
+                    } else {
+                        base = lane63_u32(incl);
+                    }
+                }
+                if (ch < 0) ch = kChunks - 1;             // unreachable: top_k < finite
+                const uint32_t dd = 64u * ch + lane;
+                const uint32_t incl = base + wave_scan_u32(count_bits<DT>(hist, bits_at(dd), negzero));
+                const unsigned long long hit = __ballot(incl >= need);
+                dk = 64u * ch + (uint32_t)(__ffsll((long long)hit) - 1);
+            }
         }
-        if (lane == 0) sc.dk = dk;
+        if (lane == 0) {
+            sc.state = state;
+            sc.d = d;
+            sc.dk = dk;
+        }
     }
     __syncthreads();
+    {
+        const int state = sc.state;
+        if (state != 0) {
+            if (t == 0) a.rows[row] = state == 1 ? TruncRow{0.f, 0.f, 0u, 1u}
+                                                 : TruncRow{-INFINITY, -INFINITY, 0u, 0u};
+            clear_chunk();
+            continue;
+        }
+    }
     const float m = value_of_bits<DT>(bits_at(sc.d));
     const float c = a.c;
     const uint32_t dk = sc.dk;
 
-    // masses of the chunks (positions <= dk), one wave per chunk, each wave
-    // taking the nonempty chunks its own threads summed
-    auto mass_at = [=](uint32_t d) -> u64 {
-        if (d > dk) return 0;
-        const uint32_t b = bits_at(d);
-        const uint32_t n = count_bits<DT>(hist, b, negzero);
-        return n ? (u64)n * fixed40(weight(value_of_bits<DT>(b), m, c)) : 0;
-    };
+    // masses of the chunks (positions <= dk): each wave takes the nonempty
+    // chunks its own threads summed, four at a time, a row of 16 lanes per
+    // chunk and four adjacent patterns (one 8-byte read) per lane; no
+    // branches, so the four weights of a lane overlap
     {
-        sc.mass[cp] = 0;
+        sc.mass[own] = 0;
         unsigned long long todo = __ballot(fin_cnt != 0 && (uint32_t)cp <= (dk >> 6));
+        const int r = lane >> 4;
+        const uint32_t q = (uint32_t)(lane & 15);
         while (todo) {
-            const int bit = __ffsll((long long)todo) - 1;
-            todo &= todo - 1;
-            const int ch = 16 * bit + wv;
-            const u64 mk = lane63_u64(wave_scan_u64(mass_at(64u * ch + lane)));
-            if (lane == 0) sc.mass[ch] = mk;
+            int pick[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pick[i] = todo ? __ffsll((long long)todo) - 1 : -1;
+                todo &= todo - 1;
+            }
+            const int bit = r == 0 ? pick[0] : r == 1 ? pick[1] : r == 2 ? pick[2] : pick[3];
+            const bool live = bit >= 0;                    // rows without a chunk add zero
+            const uint32_t d0 = 64u * (uint32_t)(16 * (live ? bit : 0) + wv) + 4u * q;
+            const bool pos = d0 < 32768u;
+            const uint32_t pb = pos ? 32764u - d0 : d0;    // the lowest of the four patterns
+            const uint2 hw = *reinterpret_cast<const uint2*>(hist + (pb >> 1));
+            uint32_t n[4] = {hw.x & 0xFFFFu, hw.x >> 16, hw.y & 0xFFFFu, hw.y >> 16};
+            n[0] = pb == 0u ? n[0] + negzero : n[0];       // +0.0 takes -0.0's count
+            n[0] = pb == 0x8000u ? 0u : n[0];
+            const bool ni = pb == ninf_bits<DT>();          // -inf and its 32-bit counter
+            n[0] = ni ? 0u : n[0];
+            n[1] = ni ? 0u : n[1];
+            u64 mk = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t d = pos ? d0 + 3u - (uint32_t)i : d0 + (uint32_t)i;
+                const uint32_t ni_ = live && d <= dk ? n[i] : 0u;
+                mk += (u64)ni_ * fixed40_nb(weight(value_of_bits<DT>(pb + (uint32_t)i), m, c));
+            }
+            mk = row_sum_u64(mk);
+            if (q == 0 && live) sc.mass[kSlotStride * wv + bit] = mk;
         }
     }
     __syncthreads();
-    // group totals: wave w sums chunk positions 64w .. 64w + 63
-    {
-        const u64 gt = lane63_u64(wave_scan_u64(sc.mass[64 * wv + lane]));
-        if (lane == 0) sc.gmass[wv] = gt;
-    }
-    __syncthreads();
-    // every wave: the group totals as a scan over lanes 0..15
-    const u64 gm = lane < kW16 ? sc.gmass[lane] : 0;
-    const u64 ginc = wave_scan_u64(gm);
-    const u64 M = lane63_u64(ginc);
-    u64 kept = M;
-    uint32_t dtau = dk;
-    if (a.top_p < 1.f) {
-        const double budget = (double)a.top_p * (double)M;
-        // the group, then the chunk, then the position where budget is reached
-        const unsigned long long ghit = __ballot(lane < kW16 && (double)ginc >= budget);
-        const int G = ghit ? __ffsll((long long)ghit) - 1 : kW16 - 1;
-        const u64 gbase = readlane_u64(ginc - gm, G);
-        if (wv == G) {
-            const u64 x = sc.mass[64 * G + lane];
-            const u64 incl = gbase + wave_scan_u64(x);
+
+    // wave 0: the kept mass M, then the top-p boundary: the lane, the chunk
+    // and the position where the running mass first reaches top_p * M
+    if (wv == 0) {
+        u64 lsum = 0;                  // lane l: chunk positions 16 l .. 16 l + 15
+#pragma unroll
+        for (int j = 0; j < 16; ++j) lsum += sc.mass[kSlotStride * j + lane];
+        const u64 incl = wave_scan_u64(lsum);
+        const u64 M = lane63_u64(incl);
+        u64 kept = M;
+        uint32_t dtau = dk;
+        if (a.top_p < 1.f) {
+            const double budget = (double)a.top_p * (double)M;
             const unsigned long long hit = __ballot((double)incl >= budget);
-            const int f = hit ? __ffsll((long long)hit) - 1 : 63;
-            const int ch = 64 * G + f;
-            const u64 excl_f = readlane_u64(incl - x, f);
+            const int L = hit ? __ffsll((long long)hit) - 1 : 63;
+            const u64 base = readlane_u64(incl - lsum, L);
+            // lane j < 16: chunk position 16 L + j
+            const u64 x = lane < 16 ? sc.mass[kSlotStride * lane + L] : 0;
+            const u64 incl1 = base + wave_scan_u64(x);
+            const unsigned long long hit1 = __ballot(lane < 16 && (double)incl1 >= budget);
+            const int f = hit1 ? __ffsll((long long)hit1) - 1 : 15;
+            const int ch = 16 * L + f;
+            const u64 excl_f = readlane_u64(incl1 - x, f);
             const uint32_t d = 64u * ch + lane;
-            const u64 mk = mass_at(d);
+            u64 mk = 0;
+            if (d <= dk) {
+                const uint32_t b = bits_at(d);
+                const uint32_t n = count_bits<DT>(hist, b, negzero);
+                mk = (u64)n * fixed40_nb(weight(value_of_bits<DT>(b), m, c));
+            }
             const u64 incl2 = excl_f + wave_scan_u64(mk);
             const unsigned long long hit2 = __ballot((double)incl2 >= budget);
             const int f2 = hit2 ? __ffsll((long long)hit2) - 1 : 63;
-            if (lane == f2) {
-                sc.d = d;
-                sc.incl = incl2;
-            }
+            dtau = 64u * ch + (uint32_t)f2;
+            kept = readlane_u64(incl2, f2);
         }
-        __syncthreads();
-        dtau = sc.d;
-        kept = sc.incl;
-    }
-    if (t == 0) {
-        const float l2s = (float)(log2((double)kept) - (double)kFixBits);
-        a.rows[row] = TruncRow{m, l2s, 65535u - dtau, 0u};
+        if (lane == 0) {               // thread 0: written during the next row's pass
+            pend_row = row;
+            pend_m = m;
+            pend_kept = kept;
+            pend_tau = 65535u - dtau;
+        }
     }
     clear_chunk();
     }
+    flush();
 }
 
 // The current device's compute units (queried once per device).
@@ -780,6 +849,11 @@ hipError_t launch_dt(bool vec, const TruncArgs& a, hipStream_t st)
                             : reinterpret_cast<const void*>(k_trunc_rows<DT, false>);
         return hipLaunchKernel(f, dim3((unsigned)a.n_rows), dim3(kTB), args, 0, st);
     } else {
+        if (a.V < 8) {                 // no whole vector: the radix kernel takes every row
+            const void* g = vec ? reinterpret_cast<const void*>(k_trunc_rows<DT, true>)
+                                : reinterpret_cast<const void*>(k_trunc_rows<DT, false>);
+            return hipLaunchKernel(g, dim3((unsigned)a.n_rows), dim3(kTB), args, 0, st);
+        }
         const void* f = vec ? reinterpret_cast<const void*>(k_trunc16<DT, true>)
                             : reinterpret_cast<const void*>(k_trunc16<DT, false>);
         const int cus = compute_units();

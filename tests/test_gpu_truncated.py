@@ -92,11 +92,36 @@ def test_truncated_parity(sv, dtype, top_k, top_p):
     assert rep.exact >= rep.rounds - 2
 
 
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("B,k,V", [(8, 3, 4097), (4, 8, 1000), (3, 2, 7), (2, 4, 9), (5, 1, 100)])
 @pytest.mark.parametrize("top_k,top_p", [(3, 1.0), (0, 0.7), (4, 0.6)])
-def test_truncated_ragged_shapes(sv, B, k, V, top_k, top_p):
-    w, T, x = workload(B, k, V, "bf16", B + k + V, top_k, top_p)
+def test_truncated_ragged_shapes(sv, dtype, B, k, V, top_k, top_p):
+    w, T, x = workload(B, k, V, dtype, B + k + V, top_k, top_p)
     check(sv, w, T, x, top_k, top_p)
+
+
+def test_truncated_many_rows_per_workgroup(sv):
+    """More rows than workgroups, at a vocabulary whose last round of loads
+    is partly past the row end (V = 152064): each workgroup streams several
+    rows, target and draft rows in turn."""
+    w, T, x = workload(64, 4, 152064, "fp16", 152, 50, 0.9)
+    check(sv, w, T, x, 50, 0.9)
+
+
+@pytest.mark.parametrize("top_k,top_p", [(50, 0.9), (0, 0.8)])
+def test_truncated_16bit_equals_fp32_at_full_size(sv, top_k, top_p):
+    """At the full 512 x 16 x 128256 bf16 size, every row: the same rows
+    upcast to fp32 (exact) go through the radix passes instead of the 16-bit
+    histogram, and the two must agree bit for bit (same keep set, same
+    fixed-point masses, so the same tokens and the same p'(x), q'(x))."""
+    w = synthetic.generate(5, device=DEV)
+    a = sv.sample_truncated(w.target, w.draft, w.tokens, w.uniforms, w.T, top_k, top_p,
+                            return_probs=True)
+    b = sv.sample_truncated(w.target.float(), w.draft.float(), w.tokens, w.uniforms, w.T, top_k,
+                            top_p, return_probs=True)
+    torch.cuda.synchronize()
+    for ta, tb in zip(a, b):
+        assert torch.equal(ta, tb)
 
 
 @pytest.mark.parametrize("layout", ["padded", "offset"])
