@@ -110,52 +110,108 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _sv_dtype(dtype: torch.dtype) -> int:
+    try:
+        return _DTYPE[dtype]
+    except KeyError:
+        raise TypeError(f"logits must be float32, float16 or bfloat16, not {dtype}") from None
+
+
 def workspace_bytes(B: int, rows_per_seq: int, V: int, dtype: torch.dtype) -> int:
-    return int(lib().spec_verify_workspace_bytes(B, rows_per_seq, V, _DTYPE[dtype]))
+    return int(lib().spec_verify_workspace_bytes(B, rows_per_seq, V, _sv_dtype(dtype)))
 
 
-def _workspace(ws, B, rows_per_seq, V, dtype, device):
-    need = workspace_bytes(B, rows_per_seq, V, dtype)
-    if ws is None:
-        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
-    return ws
+# The C ABI takes plain device pointers and cannot see buffer sizes, so every
+# tensor is checked here before its pointer is passed: device, dtype, shape
+# and layout.  A mismatch raises ValueError / TypeError and launches nothing.
+
+def _describe(t) -> str:
+    if not isinstance(t, torch.Tensor):
+        return type(t).__name__
+    return f"{t.dtype} {tuple(t.shape)} on {t.device}{'' if t.is_contiguous() else ', not contiguous'}"
 
 
-def _row_stride(t: torch.Tensor) -> int:
+def _need(t, name: str, shape: tuple, dtype: torch.dtype, device: torch.device):
+    """A contiguous tensor of exactly this shape and dtype on the logits' device."""
+    if (not isinstance(t, torch.Tensor) or t.device != device or t.dtype is not dtype
+            or t.shape != shape or not t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} on "
+                         f"{device}; got {_describe(t)}")
+    return t
+
+
+def _logits(t, name: str, ndim: int, lead: Optional[tuple] = None, dtype=None) -> int:
+    """Logits on the GPU, `ndim` dims, rows contiguous along V and evenly
+    spaced over the leading dims; returns the row stride in elements."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a tensor on the GPU; got {_describe(t)}")
+    if t.dim() != ndim or (lead is not None and tuple(t.shape[:-1]) != lead):
+        want = f"[{', '.join(map(str, lead))}, V]" if lead is not None else f"{ndim} dims"
+        raise ValueError(f"{name} must have shape {want}; got {tuple(t.shape)}")
+    if dtype is not None and t.dtype is not dtype:
+        raise TypeError(f"{name} must have the target's dtype {dtype}; got {t.dtype}")
+    _sv_dtype(t.dtype)
     if t.stride(-1) != 1:
-        raise ValueError("logit rows must be contiguous along the vocabulary")
-    return t.stride(-2)
-
-
-def _check_rows(t: torch.Tensor, ndim_lead: int):
-    """Rows of the leading dims must be evenly spaced by the row stride."""
-    rs = _row_stride(t)
+        raise ValueError(f"{name}: rows must be contiguous along the vocabulary")
+    rs = t.stride(-2)
     expect = rs
     for d in range(t.dim() - 2, -1, -1):
         if t.size(d) > 1 and t.stride(d) != expect:
-            raise ValueError("logits must be a [.., V] tensor whose rows are evenly spaced")
+            raise ValueError(f"{name} must be a [.., V] tensor whose rows are evenly spaced")
         expect *= t.size(d)
     return rs
+
+
+def _out(t, name: str, shape: tuple, dtype: torch.dtype, device: torch.device):
+    """A caller's output tensor, checked, or a new one."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    return _need(t, name, shape, dtype, device)
+
+
+def _workspace(ws, B, rows_per_seq, V, dtype, device):
+    """(tensor, size in bytes): the caller's contiguous device buffer, or a new one."""
+    if ws is None:
+        need = workspace_bytes(B, rows_per_seq, V, dtype)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    elif not isinstance(ws, torch.Tensor) or ws.device != device or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}; got {_describe(ws)}")
+    return ws, ws.numel() * ws.element_size()
 
 
 def greedy(target: torch.Tensor, draft_tokens: torch.Tensor, *, out_tokens=None,
            out_num_accepted=None, workspace=None, stream=None):
     """Greedy verification.  target [B, k+1, V] (fp32/fp16/bf16, rows contiguous
     along V), draft_tokens [B, k] int32.  Returns (tokens [B, k+1], num_accepted [B])."""
+    ts = _logits(target, "target", 3)
     B, k1, V = target.shape
     k = k1 - 1
     dev = target.device
-    if out_tokens is None:
-        out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
-    if out_num_accepted is None:
-        out_num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
-    ws = _workspace(workspace, B, k + 1, V, target.dtype, dev)
-    st = lib().spec_verify_greedy(_ptr(target), _check_rows(target, 2), _ptr(draft_tokens), B, k, V,
-                                  _DTYPE[target.dtype], _ptr(out_tokens), _ptr(out_num_accepted),
-                                  _ptr(ws), ws.numel(), _stream(stream))
+    _need(draft_tokens, "draft_tokens", (B, k), torch.int32, dev)
+    out_tokens = _out(out_tokens, "out_tokens", (B, k + 1), torch.int32, dev)
+    out_num_accepted = _out(out_num_accepted, "out_num_accepted", (B,), torch.int32, dev)
+    ws, wsb = _workspace(workspace, B, k + 1, V, target.dtype, dev)
+    st = lib().spec_verify_greedy(_ptr(target), ts, _ptr(draft_tokens), B, k, V,
+                                  _sv_dtype(target.dtype), _ptr(out_tokens), _ptr(out_num_accepted),
+                                  _ptr(ws), wsb, _stream(stream))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_greedy")
     return out_tokens, out_num_accepted
+
+
+def _sample_inputs(target, draft, draft_tokens, uniforms):
+    """Checks the sampling entry points' inputs; returns (B, k, V, target
+    row stride, draft row stride)."""
+    ts = _logits(target, "target", 3)
+    B, k1, V = target.shape
+    k = k1 - 1
+    dev = target.device
+    if isinstance(draft, torch.Tensor) and draft.device != dev:
+        raise ValueError(f"draft must be on the target's device {dev}; got {_describe(draft)}")
+    ds = _logits(draft, "draft", 3, (B, k), target.dtype)
+    _need(draft_tokens, "draft_tokens", (B, k), torch.int32, dev)
+    _need(uniforms, "uniforms", (B, k + 1), torch.float32, dev)
+    return B, k, V, ts, ds
 
 
 def sample(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
@@ -166,23 +222,21 @@ def sample(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor
     draft_tokens [B, k] int32, uniforms [B, k+1] float32 in [0, 1).
     Returns (tokens [B, k+1], num_accepted [B]) and, with return_probs,
     also (p_x [B, k], q_x [B, k])."""
-    B, k1, V = target.shape
-    k = k1 - 1
+    B, k, V, ts, ds = _sample_inputs(target, draft, draft_tokens, uniforms)
     dev = target.device
-    if out_tokens is None:
-        out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
-    if out_num_accepted is None:
-        out_num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    out_tokens = _out(out_tokens, "out_tokens", (B, k + 1), torch.int32, dev)
+    out_num_accepted = _out(out_num_accepted, "out_num_accepted", (B,), torch.int32, dev)
     if return_probs:
-        if out_p_x is None:
-            out_p_x = torch.empty((B, k), dtype=torch.float32, device=dev)
-        if out_q_x is None:
-            out_q_x = torch.empty((B, k), dtype=torch.float32, device=dev)
-    ws = _workspace(workspace, B, 2 * k + 1, V, target.dtype, dev)
-    st = lib().spec_verify_sample(_ptr(target), _check_rows(target, 2), _ptr(draft), _check_rows(draft, 2),
+        out_p_x = _out(out_p_x, "out_p_x", (B, k), torch.float32, dev)
+        out_q_x = _out(out_q_x, "out_q_x", (B, k), torch.float32, dev)
+    else:
+        out_p_x = None if out_p_x is None else _need(out_p_x, "out_p_x", (B, k), torch.float32, dev)
+        out_q_x = None if out_q_x is None else _need(out_q_x, "out_q_x", (B, k), torch.float32, dev)
+    ws, wsb = _workspace(workspace, B, 2 * k + 1, V, target.dtype, dev)
+    st = lib().spec_verify_sample(_ptr(target), ts, _ptr(draft), ds,
                                   _ptr(draft_tokens), _ptr(uniforms), float(temperature), B, k, V,
-                                  _DTYPE[target.dtype], _ptr(out_tokens), _ptr(out_num_accepted),
-                                  _ptr(out_p_x), _ptr(out_q_x), _ptr(ws), ws.numel(), _stream(stream))
+                                  _sv_dtype(target.dtype), _ptr(out_tokens), _ptr(out_num_accepted),
+                                  _ptr(out_p_x), _ptr(out_q_x), _ptr(ws), wsb, _stream(stream))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_sample")
     if return_probs:
@@ -194,18 +248,20 @@ def greedy_ext(target: torch.Tensor, draft_tokens: torch.Tensor, *, workspace=No
     """Greedy verification plus its phrase-harvesting by-products.  Returns
     (tokens [B, k+1], num_accepted [B], target_argmax [B, k+1],
     match_mask [B] (int64 bit pattern of the uint64 mask), num_match [B])."""
+    ts = _logits(target, "target", 3)
     B, k1, V = target.shape
     k = k1 - 1
     dev = target.device
+    _need(draft_tokens, "draft_tokens", (B, k), torch.int32, dev)
     out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
     out_na = torch.empty((B,), dtype=torch.int32, device=dev)
     out_v = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
     out_mask = torch.empty((B,), dtype=torch.int64, device=dev)
     out_cnt = torch.empty((B,), dtype=torch.int32, device=dev)
-    ws = _workspace(workspace, B, k + 1, V, target.dtype, dev)
-    st = lib().spec_verify_greedy_ext(_ptr(target), _check_rows(target, 2), _ptr(draft_tokens), B, k, V,
-                                      _DTYPE[target.dtype], _ptr(out_tokens), _ptr(out_na), _ptr(out_v),
-                                      _ptr(out_mask), _ptr(out_cnt), _ptr(ws), ws.numel(), _stream(stream))
+    ws, wsb = _workspace(workspace, B, k + 1, V, target.dtype, dev)
+    st = lib().spec_verify_greedy_ext(_ptr(target), ts, _ptr(draft_tokens), B, k, V,
+                                      _sv_dtype(target.dtype), _ptr(out_tokens), _ptr(out_na), _ptr(out_v),
+                                      _ptr(out_mask), _ptr(out_cnt), _ptr(ws), wsb, _stream(stream))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_greedy_ext")
     return out_tokens, out_na, out_v, out_mask, out_cnt
@@ -215,19 +271,17 @@ def sample_lenient(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torc
                    uniforms: torch.Tensor, temperature: float, lenience: float, *,
                    return_probs: bool = False, workspace=None, stream=None):
     """Sampling verification with lenience l >= 1 (l = 1: `sample`)."""
-    B, k1, V = target.shape
-    k = k1 - 1
+    B, k, V, ts, ds = _sample_inputs(target, draft, draft_tokens, uniforms)
     dev = target.device
     out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
     out_na = torch.empty((B,), dtype=torch.int32, device=dev)
     out_p_x = torch.empty((B, k), dtype=torch.float32, device=dev) if return_probs else None
     out_q_x = torch.empty((B, k), dtype=torch.float32, device=dev) if return_probs else None
-    ws = _workspace(workspace, B, 2 * k + 1, V, target.dtype, dev)
-    st = lib().spec_verify_sample_lenient(_ptr(target), _check_rows(target, 2), _ptr(draft),
-                                          _check_rows(draft, 2), _ptr(draft_tokens), _ptr(uniforms),
-                                          float(temperature), float(lenience), B, k, V,
-                                          _DTYPE[target.dtype], _ptr(out_tokens), _ptr(out_na),
-                                          _ptr(out_p_x), _ptr(out_q_x), _ptr(ws), ws.numel(),
+    ws, wsb = _workspace(workspace, B, 2 * k + 1, V, target.dtype, dev)
+    st = lib().spec_verify_sample_lenient(_ptr(target), ts, _ptr(draft), ds, _ptr(draft_tokens),
+                                          _ptr(uniforms), float(temperature), float(lenience), B, k, V,
+                                          _sv_dtype(target.dtype), _ptr(out_tokens), _ptr(out_na),
+                                          _ptr(out_p_x), _ptr(out_q_x), _ptr(ws), wsb,
                                           _stream(stream))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_sample_lenient")
@@ -241,20 +295,18 @@ def sample_truncated(target: torch.Tensor, draft: torch.Tensor, draft_tokens: to
                      *, return_probs: bool = False, workspace=None, stream=None):
     """Sampling verification on top-k / top-p truncated target and draft rows
     (top_k = 0 and top_p >= 1 switch the steps off)."""
-    B, k1, V = target.shape
-    k = k1 - 1
+    B, k, V, ts, ds = _sample_inputs(target, draft, draft_tokens, uniforms)
     dev = target.device
     out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
     out_na = torch.empty((B,), dtype=torch.int32, device=dev)
     out_p_x = torch.empty((B, k), dtype=torch.float32, device=dev) if return_probs else None
     out_q_x = torch.empty((B, k), dtype=torch.float32, device=dev) if return_probs else None
-    ws = _workspace(workspace, B, 2 * k + 1, V, target.dtype, dev)
-    st = lib().spec_verify_sample_truncated(_ptr(target), _check_rows(target, 2), _ptr(draft),
-                                            _check_rows(draft, 2), _ptr(draft_tokens),
+    ws, wsb = _workspace(workspace, B, 2 * k + 1, V, target.dtype, dev)
+    st = lib().spec_verify_sample_truncated(_ptr(target), ts, _ptr(draft), ds, _ptr(draft_tokens),
                                             _ptr(uniforms), float(temperature), int(top_k),
-                                            float(top_p), B, k, V, _DTYPE[target.dtype],
+                                            float(top_p), B, k, V, _sv_dtype(target.dtype),
                                             _ptr(out_tokens), _ptr(out_na), _ptr(out_p_x),
-                                            _ptr(out_q_x), _ptr(ws), ws.numel(), _stream(stream))
+                                            _ptr(out_q_x), _ptr(ws), wsb, _stream(stream))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_sample_truncated")
     if return_probs:
@@ -262,22 +314,33 @@ def sample_truncated(target: torch.Tensor, draft: torch.Tensor, draft_tokens: to
     return out_tokens, out_na
 
 
+def _candidate_inputs(target, cand_tokens):
+    """Checks the candidate entry points' inputs; returns (B, C, R, V, L,
+    target row stride)."""
+    ts = _logits(target, "target", 4)
+    B, C, R, V = target.shape
+    if not isinstance(cand_tokens, torch.Tensor) or cand_tokens.dim() != 3:
+        raise ValueError(f"cand_tokens must be a [B, C, L] int32 tensor; got {_describe(cand_tokens)}")
+    L = cand_tokens.shape[2]
+    _need(cand_tokens, "cand_tokens", (B, C, L), torch.int32, target.device)
+    return B, C, R, V, L, ts
+
+
 def greedy_candidates_ext(target: torch.Tensor, cand_tokens: torch.Tensor, *, workspace=None,
                           stream=None):
     """Multi-candidate greedy verification plus the argmax of every scored row.
     Returns (tokens [B, L+1], A [B], best [B], target_argmax [B, C, R])."""
-    B, C, R, V = target.shape
-    L = cand_tokens.shape[2]
+    B, C, R, V, L, ts = _candidate_inputs(target, cand_tokens)
     dev = target.device
     out_tokens = torch.empty((B, L + 1), dtype=torch.int32, device=dev)
     out_na = torch.empty((B,), dtype=torch.int32, device=dev)
     out_best = torch.empty((B,), dtype=torch.int32, device=dev)
     out_v = torch.empty((B, C, R), dtype=torch.int32, device=dev)
-    ws = _workspace(workspace, B, C * R, V, target.dtype, dev)
-    st = lib().spec_verify_greedy_candidates_ext(_ptr(target), _check_rows(target, 3), _ptr(cand_tokens),
-                                                 B, C, L, R, V, _DTYPE[target.dtype], _ptr(out_tokens),
+    ws, wsb = _workspace(workspace, B, C * R, V, target.dtype, dev)
+    st = lib().spec_verify_greedy_candidates_ext(_ptr(target), ts, _ptr(cand_tokens),
+                                                 B, C, L, R, V, _sv_dtype(target.dtype), _ptr(out_tokens),
                                                  _ptr(out_na), _ptr(out_best), _ptr(out_v), _ptr(ws),
-                                                 ws.numel(), _stream(stream))
+                                                 wsb, _stream(stream))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_greedy_candidates_ext")
     return out_tokens, out_na, out_best, out_v
@@ -288,19 +351,15 @@ def sample_lazy(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.T
                 workspace=None, stream=None):
     """Early-exit sampling verification: `sample`'s results, reading only the rows
     the rule looks at.  Returns (tokens [B, k+1], num_accepted [B])."""
-    B, k1, V = target.shape
-    k = k1 - 1
+    B, k, V, ts, ds = _sample_inputs(target, draft, draft_tokens, uniforms)
     dev = target.device
-    if out_tokens is None:
-        out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
-    if out_num_accepted is None:
-        out_num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
-    ws = _workspace(workspace, B, 2 * k + 1, V, target.dtype, dev)
-    st = lib().spec_verify_sample_lazy(_ptr(target), _check_rows(target, 2), _ptr(draft),
-                                       _check_rows(draft, 2), _ptr(draft_tokens), _ptr(uniforms),
-                                       float(temperature), B, k, V, _DTYPE[target.dtype],
-                                       _ptr(out_tokens), _ptr(out_num_accepted), _ptr(ws), ws.numel(),
-                                       _stream(stream))
+    out_tokens = _out(out_tokens, "out_tokens", (B, k + 1), torch.int32, dev)
+    out_num_accepted = _out(out_num_accepted, "out_num_accepted", (B,), torch.int32, dev)
+    ws, wsb = _workspace(workspace, B, 2 * k + 1, V, target.dtype, dev)
+    st = lib().spec_verify_sample_lazy(_ptr(target), ts, _ptr(draft), ds, _ptr(draft_tokens),
+                                       _ptr(uniforms), float(temperature), B, k, V,
+                                       _sv_dtype(target.dtype), _ptr(out_tokens), _ptr(out_num_accepted),
+                                       _ptr(ws), wsb, _stream(stream))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_sample_lazy")
     return out_tokens, out_num_accepted
@@ -310,17 +369,17 @@ def greedy_lazy(target: torch.Tensor, draft_tokens: torch.Tensor, *, out_tokens=
                 out_num_accepted=None, workspace=None, stream=None):
     """Early-exit greedy verification: `greedy`'s results, reading only the rows
     the rule looks at.  Returns (tokens [B, k+1], num_accepted [B])."""
+    ts = _logits(target, "target", 3)
     B, k1, V = target.shape
     k = k1 - 1
     dev = target.device
-    if out_tokens is None:
-        out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
-    if out_num_accepted is None:
-        out_num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
-    ws = _workspace(workspace, B, k + 1, V, target.dtype, dev)
-    st = lib().spec_verify_greedy_lazy(_ptr(target), _check_rows(target, 2), _ptr(draft_tokens), B, k, V,
-                                       _DTYPE[target.dtype], _ptr(out_tokens), _ptr(out_num_accepted),
-                                       _ptr(ws), ws.numel(), _stream(stream))
+    _need(draft_tokens, "draft_tokens", (B, k), torch.int32, dev)
+    out_tokens = _out(out_tokens, "out_tokens", (B, k + 1), torch.int32, dev)
+    out_num_accepted = _out(out_num_accepted, "out_num_accepted", (B,), torch.int32, dev)
+    ws, wsb = _workspace(workspace, B, k + 1, V, target.dtype, dev)
+    st = lib().spec_verify_greedy_lazy(_ptr(target), ts, _ptr(draft_tokens), B, k, V,
+                                       _sv_dtype(target.dtype), _ptr(out_tokens), _ptr(out_num_accepted),
+                                       _ptr(ws), wsb, _stream(stream))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_greedy_lazy")
     return out_tokens, out_num_accepted
@@ -331,18 +390,24 @@ def greedy_tree(nodes: torch.Tensor, cand_tokens: torch.Tensor, cand_rows: torch
     """Multi-candidate greedy verification over a token tree.  nodes [B, N, V],
     cand_tokens [B, C, L] int32, cand_rows [B, C, R] int32 (node row per
     candidate position).  Returns (tokens [B, L+1], A [B], best [B])."""
+    ns = _logits(nodes, "nodes", 3)
     B, N, V = nodes.shape
+    dev = nodes.device
+    for t, name in ((cand_tokens, "cand_tokens"), (cand_rows, "cand_rows")):
+        if not isinstance(t, torch.Tensor) or t.dim() != 3 or t.shape[0] != B:
+            raise ValueError(f"{name} must be a [B, C, *] int32 tensor; got {_describe(t)}")
     _, C, L = cand_tokens.shape
     R = cand_rows.shape[2]
-    dev = nodes.device
+    _need(cand_tokens, "cand_tokens", (B, C, L), torch.int32, dev)
+    _need(cand_rows, "cand_rows", (B, C, R), torch.int32, dev)
     out_tokens = torch.empty((B, L + 1), dtype=torch.int32, device=dev)
     out_na = torch.empty((B,), dtype=torch.int32, device=dev)
     out_best = torch.empty((B,), dtype=torch.int32, device=dev)
-    ws = _workspace(workspace, B, N, V, nodes.dtype, dev)
-    st = lib().spec_verify_greedy_tree(_ptr(nodes), _check_rows(nodes, 2), N, _ptr(cand_tokens),
-                                       _ptr(cand_rows), B, C, L, R, V, _DTYPE[nodes.dtype],
+    ws, wsb = _workspace(workspace, B, N, V, nodes.dtype, dev)
+    st = lib().spec_verify_greedy_tree(_ptr(nodes), ns, N, _ptr(cand_tokens),
+                                       _ptr(cand_rows), B, C, L, R, V, _sv_dtype(nodes.dtype),
                                        _ptr(out_tokens), _ptr(out_na), _ptr(out_best), _ptr(ws),
-                                       ws.numel(), _stream(stream))
+                                       wsb, _stream(stream))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_greedy_tree")
     return out_tokens, out_na, out_best
@@ -352,20 +417,16 @@ def greedy_candidates(target: torch.Tensor, cand_tokens: torch.Tensor, *, out_to
                       out_num_accepted=None, out_best=None, workspace=None, stream=None):
     """Multi-candidate greedy verification.  target [B, C, R, V] with R = L or L+1,
     cand_tokens [B, C, L] int32.  Returns (tokens [B, L+1], A [B], best [B])."""
-    B, C, R, V = target.shape
-    L = cand_tokens.shape[2]
+    B, C, R, V, L, ts = _candidate_inputs(target, cand_tokens)
     dev = target.device
-    if out_tokens is None:
-        out_tokens = torch.empty((B, L + 1), dtype=torch.int32, device=dev)
-    if out_num_accepted is None:
-        out_num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
-    if out_best is None:
-        out_best = torch.empty((B,), dtype=torch.int32, device=dev)
-    ws = _workspace(workspace, B, C * R, V, target.dtype, dev)
-    st = lib().spec_verify_greedy_candidates(_ptr(target), _check_rows(target, 3), _ptr(cand_tokens),
-                                             B, C, L, R, V, _DTYPE[target.dtype], _ptr(out_tokens),
+    out_tokens = _out(out_tokens, "out_tokens", (B, L + 1), torch.int32, dev)
+    out_num_accepted = _out(out_num_accepted, "out_num_accepted", (B,), torch.int32, dev)
+    out_best = _out(out_best, "out_best", (B,), torch.int32, dev)
+    ws, wsb = _workspace(workspace, B, C * R, V, target.dtype, dev)
+    st = lib().spec_verify_greedy_candidates(_ptr(target), ts, _ptr(cand_tokens),
+                                             B, C, L, R, V, _sv_dtype(target.dtype), _ptr(out_tokens),
                                              _ptr(out_num_accepted), _ptr(out_best), _ptr(ws),
-                                             ws.numel(), _stream(stream))
+                                             wsb, _stream(stream))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_greedy_candidates")
     return out_tokens, out_num_accepted, out_best

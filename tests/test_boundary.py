@@ -272,3 +272,28 @@ def test_c_client_host_side():
     r = subprocess.run([b.CLIENT_BIN], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stderr
     assert "all checks passed" in r.stdout
+
+
+def test_binding_checks_tensors_before_any_launch(sv):
+    """The binding checks every tensor (device, dtype, shape, layout) before
+    it passes a pointer to the C ABI, which cannot see buffer sizes."""
+    import torch
+    cpu = torch.device("cpu")
+    t = torch.zeros((2, 3), dtype=torch.int32)
+    assert sv._need(t, "x", (2, 3), torch.int32, cpu) is t
+    for bad in (torch.zeros((2, 4), dtype=torch.int32),            # shape
+                torch.zeros((2, 3), dtype=torch.int64),            # dtype
+                torch.zeros((3, 2), dtype=torch.int32).t(),        # layout
+                [[0, 0, 0], [0, 0, 0]]):                           # not a tensor
+        with pytest.raises(ValueError):
+            sv._need(bad, "x", (2, 3), torch.int32, cpu)
+    with pytest.raises(TypeError):
+        sv._sv_dtype(torch.float64)
+    # logits must live on the GPU: CPU tensors are refused before the library is called
+    z = torch.zeros((2, 5, 16))
+    with pytest.raises(ValueError, match="GPU"):
+        sv.sample(z, z[:, :4], torch.zeros((2, 4), dtype=torch.int32), torch.zeros((2, 5)), 1.0)
+    with pytest.raises(ValueError, match="GPU"):
+        sv.greedy(z, torch.zeros((2, 4), dtype=torch.int32))
+    with pytest.raises(ValueError, match="GPU"):
+        sv.greedy_candidates(torch.zeros((2, 2, 3, 16)), torch.zeros((2, 2, 3), dtype=torch.int32))
