@@ -323,7 +323,8 @@ int candidates_impl(const void* target_logits, long long row_stride,
     if (!dtype_ok(dtype)) return SV_EDTYPE;
     if (!target_logits || !cand_tokens || !out_tokens || !out_num_accepted || !out_best_candidate)
         return SV_EINVAL;
-    if (B < 1 || C < 1 || L < 1 || L > SV_MAX_K || C * L > SV_MAX_CANDIDATE_TOKENS) return SV_EINVAL;
+    if (B < 1 || C < 1 || L < 1 || L > SV_MAX_K || (long long)C * L > SV_MAX_CANDIDATE_TOKENS)
+        return SV_EINVAL;
     if ((R != L && R != L + 1) || V < 1 || V > kMaxV || row_stride < V) return SV_EINVAL;
     if (cand_rows && N < 1) return SV_EINVAL;
     const long long rows = (long long)B * (cand_rows ? (long long)N : (long long)C * R);

@@ -158,6 +158,7 @@ def test_candidates_rejects_bad_arguments(sv):
         (dict(R=10), sv.SV_EINVAL), (dict(C=1, L=64, R=64), sv.SV_EINVAL), (dict(best=None), sv.SV_EINVAL),
         (dict(cand=None), sv.SV_EINVAL), (dict(stride=10), sv.SV_EINVAL), (dict(dt=5), sv.SV_EDTYPE),
         (dict(ws=None), sv.SV_EWORKSPACE),
+        (dict(C=1 << 30, L=4, R=4), sv.SV_EINVAL),      # C * L overflows an int
     ]
     for kw, want in cases:
         assert call(**kw) == want, kw
