@@ -14,6 +14,9 @@ Prints one JSON line.  Also reports, for the dominant kernel (the statistics
 pass), its average duration from HIP events recorded on the launch stream
 during the timed region and its achieved HBM bandwidth against the 8 TB/s
 peak, and the CPU oracle timed on a bounded sample of the same workload.
+After the timed region it replays the same calls captured in one HIP graph
+(config.graph_replay_ms_per_call: the per-call time without host and launch
+overhead, which bounds the small, launch-bound workloads).
 """
 from __future__ import annotations
 
@@ -80,6 +83,9 @@ def main():
     ap.add_argument("--top-p", type=float, default=0.8)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU oracle baseline budget (sample mode; 0 disables it)")
+    ap.add_argument("--graph-calls", type=int, default=100,
+                    help="calls captured in one HIP graph and replayed after the timed region "
+                         "(0: skip); reported as config.graph_replay_ms_per_call")
     ap.add_argument("--profile-every", type=int, default=5,
                     help="time the streaming kernel on every N-th timed call")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -249,6 +255,30 @@ def main():
     def pct(q):
         return per_call[min(len(per_call) - 1, int(q * (len(per_call) - 1) + 0.5))]
 
+    # the same calls captured in one HIP graph and replayed: the per-call time
+    # without host and launch overhead (a call enqueues no allocation, memset
+    # or synchronisation, so it can be captured); each captured call reads the
+    # input set it would read in the timed region
+    graph_ms, graph_n = None, 0
+    if args.graph_calls > 0:
+        graph_n = args.graph_calls
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(graph_n):
+                call(i)
+        g.replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        reps = 3
+        g0.record()
+        for _ in range(reps):
+            g.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / (reps * graph_n)
+        del g
+
     lazy = args.mode.endswith("_lazy")
     if lazy:                           # early exit: no single streaming kernel per call
         kernel_ms = []
@@ -277,6 +307,8 @@ def main():
             "call_effective_GBps": stats_rows * V * es / (ms_per_step / 1e3) / 1e9,
             "input_sets_rotated": sets,
             "single_call_ms_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
+            "graph_replay_ms_per_call": graph_ms,
+            "graph_calls": graph_n,
             "wall_s_timed_region": wall_s,
             "input_generation_s": gen_s,
             "device": torch.cuda.get_device_name(0),

@@ -101,13 +101,20 @@ def check_single_hip_runtime():
 
 
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
 
 
-def _stream(stream) -> ctypes.c_void_p:
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+# the current stream's raw handle without building a Stream object (about
+# 0.1 us instead of 3 us per call)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(stream, device: torch.device):
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None:
+        return _raw_stream(device.index)
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def _sv_dtype(dtype: torch.dtype) -> int:
@@ -151,14 +158,15 @@ def _logits(t, name: str, ndim: int, lead: Optional[tuple] = None, dtype=None) -
     if dtype is not None and t.dtype is not dtype:
         raise TypeError(f"{name} must have the target's dtype {dtype}; got {t.dtype}")
     _sv_dtype(t.dtype)
-    if t.stride(-1) != 1:
+    shape, strides = t.shape, t.stride()
+    if strides[-1] != 1:
         raise ValueError(f"{name}: rows must be contiguous along the vocabulary")
-    rs = t.stride(-2)
+    rs = strides[-2]
     expect = rs
-    for d in range(t.dim() - 2, -1, -1):
-        if t.size(d) > 1 and t.stride(d) != expect:
+    for d in range(ndim - 2, -1, -1):
+        if shape[d] > 1 and strides[d] != expect:
             raise ValueError(f"{name} must be a [.., V] tensor whose rows are evenly spaced")
-        expect *= t.size(d)
+        expect *= shape[d]
     return rs
 
 
@@ -193,7 +201,7 @@ def greedy(target: torch.Tensor, draft_tokens: torch.Tensor, *, out_tokens=None,
     ws, wsb = _workspace(workspace, B, k + 1, V, target.dtype, dev)
     st = lib().spec_verify_greedy(_ptr(target), ts, _ptr(draft_tokens), B, k, V,
                                   _sv_dtype(target.dtype), _ptr(out_tokens), _ptr(out_num_accepted),
-                                  _ptr(ws), wsb, _stream(stream))
+                                  _ptr(ws), wsb, _stream(stream, dev))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_greedy")
     return out_tokens, out_num_accepted
@@ -236,7 +244,7 @@ def sample(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor
     st = lib().spec_verify_sample(_ptr(target), ts, _ptr(draft), ds,
                                   _ptr(draft_tokens), _ptr(uniforms), float(temperature), B, k, V,
                                   _sv_dtype(target.dtype), _ptr(out_tokens), _ptr(out_num_accepted),
-                                  _ptr(out_p_x), _ptr(out_q_x), _ptr(ws), wsb, _stream(stream))
+                                  _ptr(out_p_x), _ptr(out_q_x), _ptr(ws), wsb, _stream(stream, dev))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_sample")
     if return_probs:
@@ -261,7 +269,7 @@ def greedy_ext(target: torch.Tensor, draft_tokens: torch.Tensor, *, workspace=No
     ws, wsb = _workspace(workspace, B, k + 1, V, target.dtype, dev)
     st = lib().spec_verify_greedy_ext(_ptr(target), ts, _ptr(draft_tokens), B, k, V,
                                       _sv_dtype(target.dtype), _ptr(out_tokens), _ptr(out_na), _ptr(out_v),
-                                      _ptr(out_mask), _ptr(out_cnt), _ptr(ws), wsb, _stream(stream))
+                                      _ptr(out_mask), _ptr(out_cnt), _ptr(ws), wsb, _stream(stream, dev))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_greedy_ext")
     return out_tokens, out_na, out_v, out_mask, out_cnt
@@ -282,7 +290,7 @@ def sample_lenient(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torc
                                           _ptr(uniforms), float(temperature), float(lenience), B, k, V,
                                           _sv_dtype(target.dtype), _ptr(out_tokens), _ptr(out_na),
                                           _ptr(out_p_x), _ptr(out_q_x), _ptr(ws), wsb,
-                                          _stream(stream))
+                                          _stream(stream, dev))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_sample_lenient")
     if return_probs:
@@ -306,7 +314,7 @@ def sample_truncated(target: torch.Tensor, draft: torch.Tensor, draft_tokens: to
                                             _ptr(uniforms), float(temperature), int(top_k),
                                             float(top_p), B, k, V, _sv_dtype(target.dtype),
                                             _ptr(out_tokens), _ptr(out_na), _ptr(out_p_x),
-                                            _ptr(out_q_x), _ptr(ws), wsb, _stream(stream))
+                                            _ptr(out_q_x), _ptr(ws), wsb, _stream(stream, dev))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_sample_truncated")
     if return_probs:
@@ -340,7 +348,7 @@ def greedy_candidates_ext(target: torch.Tensor, cand_tokens: torch.Tensor, *, wo
     st = lib().spec_verify_greedy_candidates_ext(_ptr(target), ts, _ptr(cand_tokens),
                                                  B, C, L, R, V, _sv_dtype(target.dtype), _ptr(out_tokens),
                                                  _ptr(out_na), _ptr(out_best), _ptr(out_v), _ptr(ws),
-                                                 wsb, _stream(stream))
+                                                 wsb, _stream(stream, dev))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_greedy_candidates_ext")
     return out_tokens, out_na, out_best, out_v
@@ -359,7 +367,7 @@ def sample_lazy(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.T
     st = lib().spec_verify_sample_lazy(_ptr(target), ts, _ptr(draft), ds, _ptr(draft_tokens),
                                        _ptr(uniforms), float(temperature), B, k, V,
                                        _sv_dtype(target.dtype), _ptr(out_tokens), _ptr(out_num_accepted),
-                                       _ptr(ws), wsb, _stream(stream))
+                                       _ptr(ws), wsb, _stream(stream, dev))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_sample_lazy")
     return out_tokens, out_num_accepted
@@ -379,7 +387,7 @@ def greedy_lazy(target: torch.Tensor, draft_tokens: torch.Tensor, *, out_tokens=
     ws, wsb = _workspace(workspace, B, k + 1, V, target.dtype, dev)
     st = lib().spec_verify_greedy_lazy(_ptr(target), ts, _ptr(draft_tokens), B, k, V,
                                        _sv_dtype(target.dtype), _ptr(out_tokens), _ptr(out_num_accepted),
-                                       _ptr(ws), wsb, _stream(stream))
+                                       _ptr(ws), wsb, _stream(stream, dev))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_greedy_lazy")
     return out_tokens, out_num_accepted
@@ -407,7 +415,7 @@ def greedy_tree(nodes: torch.Tensor, cand_tokens: torch.Tensor, cand_rows: torch
     st = lib().spec_verify_greedy_tree(_ptr(nodes), ns, N, _ptr(cand_tokens),
                                        _ptr(cand_rows), B, C, L, R, V, _sv_dtype(nodes.dtype),
                                        _ptr(out_tokens), _ptr(out_na), _ptr(out_best), _ptr(ws),
-                                       wsb, _stream(stream))
+                                       wsb, _stream(stream, dev))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_greedy_tree")
     return out_tokens, out_na, out_best
@@ -426,7 +434,7 @@ def greedy_candidates(target: torch.Tensor, cand_tokens: torch.Tensor, *, out_to
     st = lib().spec_verify_greedy_candidates(_ptr(target), ts, _ptr(cand_tokens),
                                              B, C, L, R, V, _sv_dtype(target.dtype), _ptr(out_tokens),
                                              _ptr(out_num_accepted), _ptr(out_best), _ptr(ws),
-                                             wsb, _stream(stream))
+                                             wsb, _stream(stream, dev))
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_greedy_candidates")
     return out_tokens, out_num_accepted, out_best
