@@ -33,15 +33,27 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 METRIC = "verified positions/sec (B·(k+1) rows/s) and achieved HBM GB/s vs peak"
-STATS_SOURCES = ["sv_stats.hip", "sv_device.h", "sv_launch.h", "sv_api.hip"]
+STATS_SOURCES = ["sv_stats.hip", "sv_device.h", "sv_launch.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_softmax_stats_workload5_traffic.json")
 
 
+def _plan_source() -> bytes:
+    """The launch plan of the statistics kernel (plan_stats in sv_api.hip),
+    from its signature to its closing brace."""
+    with open(os.path.join(ROOT, "draft_verification_verify_amd", "csrc", "sv_api.hip"), "rb") as fh:
+        src = fh.read()
+    a = src.index(b"StatsPlan plan_stats(")
+    return src[a:src.index(b"\n}\n", a) + 3]
+
+
 def stats_kernel_digest() -> str:
+    """What the statistics kernel's counters depend on: its source, the
+    headers it includes, its launch plan and the build flags."""
     h = hashlib.sha256()
     for f in STATS_SOURCES:
         with open(os.path.join(ROOT, "draft_verification_verify_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
+    h.update(_plan_source())
     h.update(open(os.path.join(ROOT, "draft_verification_verify_amd", "build.py"), "rb").read())
     return h.hexdigest()[:16]
 
