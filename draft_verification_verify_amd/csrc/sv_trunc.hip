@@ -20,7 +20,8 @@
 //    workgroup per row streaming the row once per digit (the first pass from
 //    HBM, the rest mostly from cache) and histogramming the next digit of the
 //    keys that share the prefix chosen so far: counts for top-k, masses for
-//    top-p.
+//    top-p.  k_trunc_rows_lds runs the same passes on fp32 rows of at most
+//    32768 logits held in LDS, read from memory once.
 // Masses are fixed-point integers (w * 2^40, truncated), summed with integer
 // atomics and integer reductions, so every result is independent of
 // scheduling and bitwise reproducible, and both kernels give the same
@@ -102,6 +103,74 @@ __device__ __forceinline__ void for_each_elem(const char* rp, int V, F&& f)
         const int n = V - 8 * nfull;   // the partial last vector, if any
         for (int j = 0; j < n; ++j) f(load_elem<DT>(rp, 8LL * nfull + j));
     }
+}
+
+// Where a radix pass finds the row: streamed from memory on every pass
+// (StreamRow), or held in LDS (LdsRow).  Both visit every element exactly
+// once per pass, in any order; every pass's result (counts, integer masses,
+// the max) is independent of that order.
+template <int DT, bool VEC>
+struct StreamRow {
+    const char* rp;
+    int V;
+    template <typename F>
+    __device__ __forceinline__ void each(F&& f) const { for_each_elem<DT, VEC>(rp, V, f); }
+};
+
+// An fp32 row of at most kLdsRowMax logits held in LDS: loaded from memory
+// once (four vectors per thread in flight), then every pass reads LDS.
+constexpr int kLdsRowMax = 32768;
+
+struct LdsRow {
+    const float* buf;                  // LDS, V floats
+    int V;
+    template <typename F>
+    __device__ __forceinline__ void each(F&& f) const
+    {
+        const int nfull = V >> 3;
+        for (int v = (int)threadIdx.x; v < nfull; v += kTB) {
+            const float4 x = *reinterpret_cast<const float4*>(buf + 8 * v);
+            const float4 y = *reinterpret_cast<const float4*>(buf + 8 * v + 4);
+            f(x.x);
+            f(x.y);
+            f(x.z);
+            f(x.w);
+            f(y.x);
+            f(y.y);
+            f(y.z);
+            f(y.w);
+        }
+        if ((int)threadIdx.x == nfull % kTB) {   // the partial last vector, if any
+            for (int j = 8 * nfull; j < V; ++j) f(buf[j]);
+        }
+    }
+};
+
+template <bool VEC>
+__device__ __forceinline__ void load_row_lds(float* buf, const char* rp, int V)
+{
+    const int nfull = V >> 3;
+    for (int v0 = 0; v0 < nfull; v0 += 4 * kTB) {
+        Raw<DT_F32> r[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int v = v0 + u * kTB + (int)threadIdx.x;
+            if (v < nfull) r[u] = load_raw<DT_F32, VEC>(rp, v);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int v = v0 + u * kTB + (int)threadIdx.x;
+            if (v < nfull) {
+                float e[kVec];
+                decode<DT_F32>(r[u], e);
+                *reinterpret_cast<float4*>(buf + 8 * v) = float4{e[0], e[1], e[2], e[3]};
+                *reinterpret_cast<float4*>(buf + 8 * v + 4) = float4{e[4], e[5], e[6], e[7]};
+            }
+        }
+    }
+    const int n = V - 8 * nfull;
+    if ((int)threadIdx.x < n) buf[8 * nfull + threadIdx.x] = load_elem<DT_F32>(rp, 8LL * nfull + threadIdx.x);
+    __syncthreads();
 }
 
 __device__ __forceinline__ u64 wave_sum_u64(u64 x)
@@ -196,8 +265,8 @@ __device__ void select_desc(const T* val, int nb, u64 base, double thr, Shared& 
 // digits above L equal `prefix` are binned by digit L (counts if CNT, masses
 // if MASS); those with a larger prefix are summed into *above_cnt /
 // *above_mass.  Level 0 has no prefix: every key >= lo is binned.
-template <int DT, bool VEC, bool CNT, bool MASS>
-__device__ void hist_pass(const char* rp, int V, int L, uint32_t prefix, uint32_t lo, float m,
+template <int DT, bool CNT, bool MASS, typename Src>
+__device__ __forceinline__ void hist_pass(const Src& src, int L, uint32_t prefix, uint32_t lo, float m,
                           float c, Shared& sh, u64* above_cnt, u64* above_mass)
 {
     using D = Digits<DT>;
@@ -211,7 +280,7 @@ __device__ void hist_pass(const char* rp, int V, int L, uint32_t prefix, uint32_
     const int sh_hi = L == 0 ? 0 : D::shift(L - 1);
     uint32_t ac = 0;
     u64 am = 0;
-    for_each_elem<DT, VEC>(rp, V, [&](float z) {
+    src.each([&](float z) {
         const uint32_t key = key_of<DT>(z);
         if (key < lo) return;
         if (L > 0) {
@@ -236,13 +305,18 @@ __device__ void hist_pass(const char* rp, int V, int L, uint32_t prefix, uint32_
     *above_mass = MASS ? block_sum_u64(am, sh.red) : 0;
 }
 
-template <int DT, bool VEC>
-__device__ void trunc_row_radix(const TruncArgs& a, int row, Shared& sh)
+template <int DT>
+__device__ __forceinline__ const char* trunc_row_ptr(const TruncArgs& a, int row)
+{
+    constexpr int ES = DT == DT_F32 ? 4 : 2;
+    return row < a.n_target_rows ? row_ptr(a.target, row, a.t_stride, ES)
+                                 : row_ptr(a.draft, row - a.n_target_rows, a.d_stride, ES);
+}
+
+template <int DT, typename Src>
+__device__ __forceinline__ void trunc_row_radix(const TruncArgs& a, int row, Shared& sh, const Src& src)
 {
     using D = Digits<DT>;
-    constexpr int ES = DT == DT_F32 ? 4 : 2;
-    const char* rp = row < a.n_target_rows ? row_ptr(a.target, row, a.t_stride, ES)
-                                           : row_ptr(a.draft, row - a.n_target_rows, a.d_stride, ES);
     const int V = a.V;
     const float c = a.c;
     const bool topk = a.top_k >= 1 && a.top_k < V;
@@ -254,12 +328,12 @@ __device__ void trunc_row_radix(const TruncArgs& a, int row, Shared& sh)
         for (int i = (int)threadIdx.x; i < kBins; i += kTB) sh.cnt[i] = 0;
         __syncthreads();
         const int s0 = D::shift(0);
-        for_each_elem<DT, VEC>(rp, V, [&](float z) {
+        src.each([&](float z) {
             mx = fmaxf(mx, z);
             atomicAdd(&sh.cnt[key_of<DT>(z) >> s0], 1u);
         });
     } else {
-        for_each_elem<DT, VEC>(rp, V, [&](float z) { mx = fmaxf(mx, z); });
+        src.each([&](float z) { mx = fmaxf(mx, z); });
     }
     const float m = block_max<kTW>(mx, sh.redf);
     if (m == -INFINITY) {              // nothing to keep; the rule never reads such a row
@@ -277,9 +351,9 @@ __device__ void trunc_row_radix(const TruncArgs& a, int row, Shared& sh)
             const bool last = L == D::levels - 1;
             if (L > 0) {
                 if (last && !topp)
-                    hist_pass<DT, VEC, true, true>(rp, V, L, prefix, 0u, m, c, sh, &above_c, &above_m);
+                    hist_pass<DT, true, true>(src, L, prefix, 0u, m, c, sh, &above_c, &above_m);
                 else
-                    hist_pass<DT, VEC, true, false>(rp, V, L, prefix, 0u, m, c, sh, &above_c, &above_m);
+                    hist_pass<DT, true, false>(src, L, prefix, 0u, m, c, sh, &above_c, &above_m);
             }
             select_desc(sh.cnt, 1 << D::bits(L), above_c, (double)a.top_k, sh);
             const int d = sh.sel < 0 ? 0 : sh.sel;
@@ -300,7 +374,7 @@ __device__ void trunc_row_radix(const TruncArgs& a, int row, Shared& sh)
         double budget = 0.0;
         for (int L = 0; L < D::levels; ++L) {
             u64 above_c = 0, above_m = 0;
-            hist_pass<DT, VEC, false, true>(rp, V, L, prefix, lo, m, c, sh, &above_c, &above_m);
+            hist_pass<DT, false, true>(src, L, prefix, lo, m, c, sh, &above_c, &above_m);
             if (L == 0) {
                 u64 mine = 0;
                 for (int i = (int)threadIdx.x; i < kBins; i += kTB) mine += sh.mass[i];
@@ -321,6 +395,21 @@ __device__ void trunc_row_radix(const TruncArgs& a, int row, Shared& sh)
     __syncthreads();                   // the shared state is reused by the next row
 }
 
+// fp32 rows of at most kLdsRowMax logits: each workgroup loads its row into
+// LDS once and runs the radix passes on the LDS copy, instead of streaming
+// the row again for every digit.  The copy and the radix state fill most of
+// a CU's LDS, so one workgroup per CU.
+template <bool VEC>
+__global__ __launch_bounds__(kTB) void k_trunc_rows_lds(TruncArgs a)
+{
+    __shared__ Shared sh;
+    __shared__ __attribute__((aligned(16))) float buf[kLdsRowMax];
+    for (int row = blockIdx.x; row < a.n_rows; row += gridDim.x) {
+        load_row_lds<VEC>(buf, trunc_row_ptr<DT_F32>(a, row), a.V);
+        trunc_row_radix<DT_F32>(a, row, sh, LdsRow{buf, a.V});
+    }
+}
+
 // Rows blockIdx.x, blockIdx.x + gridDim.x, ...; with only_marked, just the
 // rows the one-pass kernel marked (pad = 1): the workgroup reads the marks of
 // kTB rows at once (rows blockIdx.x * kTB + i, then gridDim.x * kTB further)
@@ -332,7 +421,8 @@ __global__ __launch_bounds__(kTB) void k_trunc_rows(TruncArgs a)
     __shared__ int marked[kTB];
     __shared__ int n_marked;
     if (!a.only_marked) {
-        for (int row = blockIdx.x; row < a.n_rows; row += gridDim.x) trunc_row_radix<DT, VEC>(a, row, sh);
+        for (int row = blockIdx.x; row < a.n_rows; row += gridDim.x)
+            trunc_row_radix<DT>(a, row, sh, StreamRow<DT, VEC>{trunc_row_ptr<DT>(a, row), a.V});
         return;
     }
     for (int base = blockIdx.x * kTB; base < a.n_rows; base += gridDim.x * kTB) {
@@ -343,7 +433,8 @@ __global__ __launch_bounds__(kTB) void k_trunc_rows(TruncArgs a)
         __syncthreads();
         const int n = n_marked;
         // each row's result depends on that row alone, so the order is free
-        for (int i = 0; i < n; ++i) trunc_row_radix<DT, VEC>(a, marked[i], sh);
+        for (int i = 0; i < n; ++i)
+            trunc_row_radix<DT>(a, marked[i], sh, StreamRow<DT, VEC>{trunc_row_ptr<DT>(a, marked[i]), a.V});
         __syncthreads();
     }
 }
@@ -845,8 +936,11 @@ hipError_t launch_dt(bool vec, const TruncArgs& a, hipStream_t st)
     b.only_marked = 0;
     void* args[] = {&b};
     if constexpr (DT == DT_F32) {
-        const void* f = vec ? reinterpret_cast<const void*>(k_trunc_rows<DT, true>)
-                            : reinterpret_cast<const void*>(k_trunc_rows<DT, false>);
+        const bool in_lds = a.V <= kLdsRowMax;
+        const void* f = in_lds ? (vec ? reinterpret_cast<const void*>(k_trunc_rows_lds<true>)
+                                      : reinterpret_cast<const void*>(k_trunc_rows_lds<false>))
+                               : (vec ? reinterpret_cast<const void*>(k_trunc_rows<DT, true>)
+                                      : reinterpret_cast<const void*>(k_trunc_rows<DT, false>));
         return hipLaunchKernel(f, dim3((unsigned)a.n_rows), dim3(kTB), args, 0, st);
     } else {
         if (a.V < 8) {                 // no whole vector: the radix kernel takes every row

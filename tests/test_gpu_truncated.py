@@ -92,7 +92,7 @@ def test_truncated_parity(sv, dtype, top_k, top_p):
     assert rep.exact >= rep.rounds - 2
 
 
-@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
 @pytest.mark.parametrize("B,k,V", [(8, 3, 4097), (4, 8, 1000), (3, 2, 7), (2, 4, 9), (5, 1, 100)])
 @pytest.mark.parametrize("top_k,top_p", [(3, 1.0), (0, 0.7), (4, 0.6)])
 def test_truncated_ragged_shapes(sv, dtype, B, k, V, top_k, top_p):
@@ -254,6 +254,14 @@ def test_truncated_many_equal_logits(sv, dtype):
     for top_k, top_p in ((100, 1.0), (0, 0.9), (70000, 0.5), (3, 0.99)):
         x = torch.from_numpy(truncated_drafts(f32(y), 1.0, top_k, top_p, 9)).to(DEV)
         check(sv, w, 1.0, x, top_k, top_p)
+
+
+@pytest.mark.parametrize("V", [32767, 32768, 32769])
+def test_truncated_fp32_lds_boundary(sv, V):
+    """fp32 rows of up to 32768 logits run the radix passes on an LDS copy,
+    longer ones stream the row for every pass: both sides of the switch."""
+    w, T, x = workload(3, 3, V, "fp32", V, 40, 0.9)
+    check(sv, w, T, x, 40, 0.9)
 
 
 def test_truncated_fp32_large_vocabulary(sv):
