@@ -54,9 +54,15 @@ StatsPlan plan_stats(long long rows, int V)
 }
 
 // The sampled row (pair) is cut into chunks of whole rounds (kBlock logical
-// vectors each), at most kMaxChunks of them; a workgroup of the chunk pass
-// takes up to 4 rounds (with all their loads in flight together), as many as
-// keep the pass near 8192 workgroups.
+// vectors each), at most kMaxChunks of them, one chunk per workgroup of the
+// chunk pass; chunks are lengthened until the pass has at most
+// kSampleBlocks workgroups (a sweep on 512 row pairs of 128256 bf16 logits:
+// 63 one-round chunks per row, 32256 workgroups, 49.5 us; 32 two-round
+// chunks, 16384 workgroups, 42.6 us; four rounds per workgroup as four
+// one-round chunks, 51.9 us).  Fewer rounds per chunk keep the draw's
+// rescan of one chunk short.
+constexpr long long kSampleBlocks = 16384;
+
 struct SamplePlan {
     int nchunks;
     int vec_per_chunk;
@@ -68,16 +74,12 @@ SamplePlan plan_sample(int B, int nvec)
 {
     SamplePlan p;
     const int rounds = (nvec + kBlock - 1) / kBlock;
-    const int rounds_per_chunk = (rounds + kMaxChunks - 1) / kMaxChunks;
-    p.vec_per_chunk = rounds_per_chunk * kBlock;
+    int rpc = (rounds + kMaxChunks - 1) / kMaxChunks;
+    while (rpc < rounds && (long long)B * ((rounds + rpc - 1) / rpc) > kSampleBlocks) ++rpc;
+    p.vec_per_chunk = rpc * kBlock;
     p.nchunks = (nvec + p.vec_per_chunk - 1) / p.vec_per_chunk;
-    const long long want = (long long)B * p.nchunks;
-    int cpb = (int)((want + 8191) / 8192);
-    if (cpb < 1) cpb = 1;
-    const int max_cpb = rounds_per_chunk >= 4 ? 1 : 4 / rounds_per_chunk;
-    if (cpb > max_cpb) cpb = max_cpb;
-    p.chunks_per_block = cpb;
-    p.blocks_per_seq = (p.nchunks + cpb - 1) / cpb;
+    p.chunks_per_block = 1;
+    p.blocks_per_seq = p.nchunks;
     return p;
 }
 
