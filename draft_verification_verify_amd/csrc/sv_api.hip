@@ -142,19 +142,19 @@ struct Profile {
 };
 Profile g_prof;
 
+// A call is counted only when both of its events were recorded.
 void prof_begin(hipStream_t st)
 {
     if (!g_prof.on) return;
     g_prof.armed = (g_prof.seen % g_prof.every == 0) && g_prof.count < g_prof.max_calls;
     g_prof.seen++;
-    if (g_prof.armed) hipEventRecord(g_prof.ev[2 * g_prof.count], st);
+    if (g_prof.armed && hipEventRecord(g_prof.ev[2 * g_prof.count], st) != hipSuccess) g_prof.armed = false;
 }
 
 void prof_end(hipStream_t st)
 {
     if (!g_prof.armed) return;
-    hipEventRecord(g_prof.ev[2 * g_prof.count + 1], st);
-    g_prof.count++;
+    if (hipEventRecord(g_prof.ev[2 * g_prof.count + 1], st) == hipSuccess) g_prof.count++;
     g_prof.armed = false;
 }
 
@@ -675,7 +675,7 @@ int spec_verify_profile_begin(int max_calls, int every)
     if (!g_prof.ev) return SV_EINVAL;
     for (int i = 0; i < 2 * max_calls; ++i) {
         if (hipEventCreate(&g_prof.ev[i]) != hipSuccess) {
-            for (int j = 0; j < i; ++j) hipEventDestroy(g_prof.ev[j]);
+            for (int j = 0; j < i; ++j) (void)hipEventDestroy(g_prof.ev[j]);
             free(g_prof.ev);
             g_prof.ev = nullptr;
             return SV_EHIP;
@@ -700,7 +700,7 @@ int spec_verify_profile_end(float* out_ms, int max_out)
         if (hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]) != hipSuccess) { rc = -2; break; }
         if (out_ms && i < max_out) out_ms[i] = ms;
     }
-    for (int i = 0; i < 2 * g_prof.max_calls; ++i) hipEventDestroy(g_prof.ev[i]);
+    for (int i = 0; i < 2 * g_prof.max_calls; ++i) (void)hipEventDestroy(g_prof.ev[i]);
     free(g_prof.ev);
     g_prof = Profile();
     return rc;
