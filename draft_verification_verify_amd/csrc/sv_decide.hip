@@ -35,7 +35,7 @@ __device__ __forceinline__ unsigned long long ballot64(bool pred)
 }
 
 // ---- sampling --------------------------------------------------------------
-// log2 p_i(x) = (z_x - m) * c - log2 s with c = log2(e)/T.  The ratio test is
+// log2 p_i(x) = (z_x - m) * c - log2 s with c = log2(e)/T (log2_prob).  The ratio test is
 // taken in the log domain so that no probability underflows: accept iff
 // log q <= log p + log l (ratio >= 1, and q = 0) or u < exp2(log p + log l -
 // log q).  Lenience l (Cascade Speculative Drafting, review function) is 1
@@ -65,6 +65,15 @@ __device__ __forceinline__ RowNorm row_norm(const DecideSampleArgs& a, long long
         r.tau = 0u;
     }
     return r;
+}
+
+// log2 of a token's probability, in the form its row's mass was summed in:
+// exp2((z - m) c) on truncated rows (the truncation kernel's weights),
+// exp2(z c - h) with h = stab_of(m, c) on softmax rows (the statistics
+// kernel's terms), so that the rounding of h cancels against the mass's.
+__device__ __forceinline__ float log2_prob(float z, const RowNorm& r, float c, bool trunc)
+{
+    return (trunc ? (z - r.m) * c : __builtin_fmaf(z, c, -stab_of(r.m, c))) - r.l2s;
 }
 
 // The statistics of target row (b, pos) and, for pos < k, the decision at pos.
@@ -98,8 +107,9 @@ __device__ __forceinline__ PosSample sample_position(const DecideSampleArgs& a, 
         if (valid) {
             const float zx = load_elem<DT>(row_ptr(a.target, tr, a.t_stride, ES), r.x);
             const float yx = load_elem<DT>(row_ptr(a.draft, dr, a.d_stride, ES), r.x);
-            const float lp = key_of<DT>(zx) >= r.t.tau ? (zx - r.t.m) * c - r.t.l2s : -INFINITY;
-            const float lq = key_of<DT>(yx) >= r.d.tau ? (yx - r.d.m) * c - r.d.l2s : -INFINITY;
+            const bool tr = a.trunc != nullptr;
+            const float lp = key_of<DT>(zx) >= r.t.tau ? log2_prob(zx, r.t, c, tr) : -INFINITY;
+            const float lq = key_of<DT>(yx) >= r.d.tau ? log2_prob(yx, r.d, c, tr) : -INFINITY;
             const float u = a.uniforms[(long long)b * (k + 1) + pos];
             const float lpl = lp + a.log2_lenience;
             const bool accept = (lq <= lpl) || (u < exp2f(lpl - lq));
@@ -122,12 +132,12 @@ __device__ __forceinline__ void write_desc(const DecideSampleArgs& a, int b, int
     d.d_row = j < k ? b * k + j : -1;
     d.out_pos = j;
     d.kind = j < k ? 0 : 1;
-    d.off_t = r.t.m * a.c + r.t.l2s;
-    d.off_d = j < k ? r.d.m * a.c + r.d.l2s : 0.f;
+    d.m_t = r.t.m;
+    d.m_d = j < k ? r.d.m : 0.f;
+    d.kq = j < k ? exp2f(r.t.l2s - r.d.l2s) : 0.f;
     d.u = a.uniforms[(long long)b * (k + 1) + k];
     d.tau_t = r.t.tau;
     d.tau_d = j < k ? r.d.tau : 0u;
-    d.pad = 0;
     a.desc[b] = d;
     a.out_num_accepted[b] = j;
 }

@@ -160,7 +160,17 @@ __device__ __forceinline__ uint32_t key_of(float v)
     }
 }
 
-// The merged (max, sum of exp2) of a row from its slice partials, in slice order.
+// The stabiliser of softmax statistics with max m: h = m * c, rounded once
+// and never contracted into a neighbouring operation, so that every kernel
+// forms the same h from the same m.  A softmax row's mass is
+// s = sum_t exp2(z_t c - h) and its probabilities are exp2(fma(z, c, -h) - log2 s).
+__device__ __forceinline__ float stab_of(float m, float c)
+{
+    return __fmul_rn(m, c);
+}
+
+// The merged (max, sum of exp2(z c - h)) of a row from its slice partials, in
+// slice order; each partial's sum is relative to its own stabiliser.
 __device__ __forceinline__ void merge_soft(const SoftPartial* p, int splits, float c, float& m, float& s)
 {
     m = p[0].m;
@@ -171,7 +181,8 @@ __device__ __forceinline__ void merge_soft(const SoftPartial* p, int splits, flo
         if (mn == -INFINITY) {
             s = 0.f;
         } else {
-            s = s * exp2f((m - mn) * c) + s2 * exp2f((m2 - mn) * c);
+            const float hn = stab_of(mn, c);
+            s = s * exp2f(stab_of(m, c) - hn) + s2 * exp2f(stab_of(m2, c) - hn);
         }
         m = mn;
     }

@@ -17,7 +17,7 @@ enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 inline int elem_size(int dt) { return dt == DT_F32 ? 4 : 2; }
 
 // Per-(row, split) partial of the softmax statistics: running max m (raw
-// logit units) and s = sum exp2((z - m) * c), c = log2(e) / T.
+// logit units) and s = sum exp2(z c - stab_of(m, c)), c = log2(e) / T.
 struct SoftPartial { float m; float s; };
 // Per-(row, split) partial of the argmax: value and lowest index (INT32_MAX
 // when the split holds nothing above -inf).
@@ -44,20 +44,24 @@ struct StatsArgs {
 };
 
 // One sampling step per sequence, prepared by the decision kernel: draw from
-// target row t_row (weights exp2(z*c - off_t)) or, for kind 0, from the
-// residual max(0, exp2(z*c - off_t) - exp2(y*c - off_d)) against draft row
-// d_row; write the token at out_pos of the sequence's output row.
+// target row t_row or, for kind 0, from the residual max(0, p - q) against
+// draft row d_row; write the token at out_pos of the sequence's output row.
+// The sampler weighs each token by s_t times its normalised weight (the draw
+// divides by the total, so a common factor does not change it):
+// p~ = exp2(z c - h_t) and the residual max(0, p~ - kq q~) with
+// q~ = exp2(y c - h_d), h = stab_of(m, c); on truncated rows exp2((z - m) c),
+// masked by the key threshold.
 struct SampleDesc {
     int t_row;
     int d_row;
     int out_pos;
     int kind;                          // 0 residual, 1 target row (bonus)
-    float off_t;
-    float off_d;
+    float m_t;                         // target row max
+    float m_d;                         // draft row max (kind 0)
+    float kq;                          // s_t / s_d, the rows' (kept) masses (kind 0)
     float u;
     uint32_t tau_t;                    // truncation: keep z with key >= tau_t (0: keep all)
     uint32_t tau_d;
-    int pad;
 };
 
 // A truncated row (top-k, then top-p): its max m, log2 of the kept mass

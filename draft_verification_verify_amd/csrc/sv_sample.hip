@@ -22,20 +22,22 @@
 
 namespace sv {
 
-// The weight arithmetic, shared by every pass: the residual
-// max(0, p - q) (kind 0) or p (otherwise), each exp2(z*c - off) with off the
-// row's log2 normaliser, so both are normalised probabilities.  MASK: the
-// rows are truncated, and a logit whose key is below its row's threshold has
-// probability 0.
+// The weight arithmetic, shared by every pass, in units of the target row's
+// mass s_t (the draw divides by the total): p~ = s_t p, and for kind 0 the
+// residual max(0, p~ - kq q~) = s_t max(0, p - q), with each exponent in the
+// form its row's mass was summed in (h = stab_of(m, c) on softmax rows,
+// z - m on truncated rows).  MASK: the rows are truncated, and a logit whose
+// key is below its row's threshold has probability 0.
 template <int DT, bool MASK>
-__device__ __forceinline__ float weight_of(float ez, float ey, int kind, float c, const SampleDesc& d)
+__device__ __forceinline__ float weight_of(float ez, float ey, int kind, float c, float h_t, float h_d,
+                                           const SampleDesc& d)
 {
-    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(ez, c, -d.off_t));
+    float p = __builtin_amdgcn_exp2f(MASK ? (ez - d.m_t) * c : __builtin_fmaf(ez, c, -h_t));
     if (MASK && key_of<DT>(ez) < d.tau_t) p = 0.f;
     if (kind != 0) return p;
-    float q = __builtin_amdgcn_exp2f(__builtin_fmaf(ey, c, -d.off_d));
+    float q = __builtin_amdgcn_exp2f(MASK ? (ey - d.m_d) * c : __builtin_fmaf(ey, c, -h_d));
     if (MASK && key_of<DT>(ey) < d.tau_d) q = 0.f;
-    return fmaxf(p - q, 0.f);
+    return fmaxf(__builtin_fmaf(-d.kq, q, p), 0.f);
 }
 
 // Weights of logical vector v (0 past the row's end).
@@ -47,7 +49,9 @@ __device__ __forceinline__ void weights8(const char* zr, const char* yr, int v, 
     load8<DT, VEC>(zr, v, nfull, V, -INFINITY, ez);
     if (kind == 0) load8<DT, VEC>(yr, v, nfull, V, -INFINITY, ey);
 #pragma unroll
-    for (int j = 0; j < kVec; ++j) w[j] = weight_of<DT, MASK>(ez[j], kind == 0 ? ey[j] : 0.f, kind, c, d);
+    for (int j = 0; j < kVec; ++j)
+        w[j] = weight_of<DT, MASK>(ez[j], kind == 0 ? ey[j] : 0.f, kind, c, stab_of(d.m_t, c),
+                                   stab_of(d.m_d, c), d);
 }
 
 __device__ __forceinline__ float sum8(const float* w)
@@ -188,6 +192,7 @@ __global__ __launch_bounds__(kBlock) void k_sample_chunks(SampleArgs a)
     const int nfull = a.V >> 3;
     const int vfull = min(v1, nfull);
     const int kind = d.kind;
+    const float h_t = stab_of(d.m_t, a.c), h_d = stab_of(d.m_d, a.c);
 
     float acc = 0.f;
     for (int r0 = v0; r0 < v1; r0 += kRoundsInFlight * kBlock) {
@@ -217,7 +222,7 @@ __global__ __launch_bounds__(kBlock) void k_sample_chunks(SampleArgs a)
                 }
 #pragma unroll
                 for (int j = 0; j < kVec; ++j)
-                    w[j] = weight_of<DT, MASK>(ez[j], kind == 0 ? ey[j] : 0.f, kind, a.c, d);
+                    w[j] = weight_of<DT, MASK>(ez[j], kind == 0 ? ey[j] : 0.f, kind, a.c, h_t, h_d, d);
                 ts = sum8(w);
             }
             float ex, rt;

@@ -16,7 +16,15 @@
 
 namespace sv {
 
-// Online softmax statistics in base 2: s = sum exp2(z*c - m*c), m = max z.
+// Online softmax statistics in base 2, relative to the stabiliser h = m c
+// with m the running max and the product rounded once (stab_of):
+// s = sum exp2(z c - h).  Each term is exp2(fma(z, c, -h)); a new max
+// rescales s by exp2(h_old - h_new), both rounded as the terms saw them.  So
+// every term of s carries the one rounding error of h, as does a
+// probability formed later as exp2(fma(z, c, -h) - log2 s), and the two
+// cancel: no error grows with |m c| (large logits, low temperatures), and
+// each element costs one fma.  The rescale's own rounding is exact for
+// nearby maxima and otherwise applies to terms scaled down by 2^-|h_old - h_new|.
 // Rescales s once per group of N elements (one exp2), not per element.
 template <int N>
 __device__ __forceinline__ void soft_update(const float* e, float& m, float& s, float c)
@@ -28,8 +36,9 @@ __device__ __forceinline__ void soft_update(const float* e, float& m, float& s, 
         cm1 = fmaxf(cm1, e[j + 1]);
     }
     const float mn = fmaxf(m, fmaxf(cm0, cm1));
-    const float scale = (m == mn) ? 1.f : __builtin_amdgcn_exp2f((m - mn) * c);
-    const float off = (mn == -INFINITY) ? 0.f : -mn * c;
+    const float hn = stab_of(mn, c);
+    const float scale = (m == mn) ? 1.f : __builtin_amdgcn_exp2f(stab_of(m, c) - hn);
+    const float off = (mn == -INFINITY) ? 0.f : -hn;   // an all -inf group adds exp2(-inf) = 0
     float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll
     for (int j = 0; j < N; j += 4) {
@@ -50,7 +59,8 @@ __device__ __forceinline__ void soft_merge(float& m, float& s, float m2, float s
         s = 0.f;
         return;
     }
-    s = s * __builtin_amdgcn_exp2f((m - mn) * c) + s2 * __builtin_amdgcn_exp2f((m2 - mn) * c);
+    const float hn = stab_of(mn, c);
+    s = s * __builtin_amdgcn_exp2f(stab_of(m, c) - hn) + s2 * __builtin_amdgcn_exp2f(stab_of(m2, c) - hn);
     m = mn;
 }
 

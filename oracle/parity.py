@@ -91,8 +91,24 @@ def check_sample(z, y, x, u, T, gpu_tokens, gpu_nacc, eps=1e-5, report=None,
     return rep
 
 
+# The exported p(x), q(x) are float32: below float32's smallest normal number
+# a value cannot carry relative precision (and underflows to 0 below 2^-149),
+# so there the error is measured against that number instead of the value.
+FP32_MIN_NORMAL = 2.0 ** -126
+
+
+def prob_error(got, ref):
+    """Relative error of float32 probabilities, with float32's smallest normal
+    number as the floor of the denominator."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return np.abs(got - ref) / np.maximum(ref, FP32_MIN_NORMAL)
+
+
 def check_probs(z, y, x, T, gpu_px, gpu_qx, rtol=1e-5):
-    """Largest relative error of the exported p_i(x_i), q_i(x_i) over all positions."""
+    """Largest error of the exported p_i(x_i), q_i(x_i) over all positions
+    (relative, and absolute below float32's normal range: prob_error).  A
+    token the oracle gives probability 0 must be exported as exactly 0."""
     worst = 0.0
     for b in range(z.shape[0]):
         px, qx = token_probs(z[b], y[b], x[b], T)
@@ -101,8 +117,7 @@ def check_probs(z, y, x, T, gpu_px, gpu_qx, rtol=1e-5):
             if (got[zero] != 0).any():
                 return float("inf")
             if (~zero).any():
-                rel = np.abs(got[~zero].astype(np.float64) - ref[~zero]) / ref[~zero]
-                worst = max(worst, float(rel.max()))
+                worst = max(worst, float(prob_error(got[~zero], ref[~zero]).max()))
     return worst
 
 
@@ -210,5 +225,5 @@ def check_probs_truncated(z, y, x, T, top_k, top_p, gpu_px, gpu_qx, eps_trunc=1e
                     if got != 0.0:
                         return float("inf"), skipped
                     continue
-                worst = max(worst, abs(float(got) - ref) / ref)
+                worst = max(worst, float(prob_error(got, ref)))
     return worst, skipped

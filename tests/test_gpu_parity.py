@@ -150,6 +150,22 @@ def test_sample_parity(sv, dtype, B, k, V, T):
     assert_sample_parity(w, toks, na, px, qx)
 
 
+@pytest.mark.parametrize("dtype,var_target,T", [
+    ("fp32", 400.0, 0.1),      # LLM-sized logits (sd 20) at a low temperature: |m c| ~ 900
+    ("bf16", 400.0, 0.1),
+    ("fp16", 400.0, 0.3),
+    ("fp32", 2.0, 25.0),       # a high temperature: near-uniform p and q
+    ("bf16", 1e4, 1.0),        # logits of order 100-400
+])
+def test_sample_parity_extreme_scales(sv, dtype, var_target, T):
+    """Large logits and low temperatures make z * c large; the acceptance
+    ratios, draws and exported p(x), q(x) must still meet the same bar."""
+    w = synthetic.chain(32, 6, 5003, dtype, var_target=var_target, var_noise=0.05 * var_target,
+                        T=T, seed=int(var_target) + 7, device=DEV)
+    toks, na, px, qx = run_sample(sv, w)
+    assert_sample_parity(w, toks, na, px, qx)
+
+
 @pytest.mark.parametrize("layout", ["padded", "offset"])
 @pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
 def test_sample_parity_unaligned(sv, dtype, layout):

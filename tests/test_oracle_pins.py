@@ -794,3 +794,18 @@ def test_draw_intervals_tile_and_match_the_draws():
             toks, na = oracle.sample(z[None], y[None], xs, u, T)
             assert na[0] == (0 if row == 0 else 1)
             assert toks[0, na[0]] == t, (row, t, toks)
+
+
+def test_probability_error_floor():
+    """The exported probabilities are float32: relative error above float32's
+    smallest normal number, absolute (against that number) below it."""
+    from oracle.parity import FP32_MIN_NORMAL, prob_error
+    assert prob_error(np.float32(0.5), 0.5) == 0.0
+    assert abs(prob_error(np.float32(1.0 + 2 ** -20), 1.0) - 2 ** -20) < 1e-12
+    # a true value deep below the float32 range, exported as 0: error = value / 2^-126
+    assert prob_error(np.float32(0.0), 1e-60) < 1e-20
+    # a denormal exported one unit off is still tiny against the floor
+    assert prob_error(np.float32(2 ** -140), 2 ** -140 + 2 ** -149) < 2 ** -22
+    # a normal value off by 1e-4 relative stays 1e-4
+    assert abs(prob_error(np.float32(1e-10 * (1 + 1e-4)), 1e-10) - 1e-4) < 1e-6
+    assert FP32_MIN_NORMAL == 2.0 ** -126
