@@ -74,6 +74,41 @@ __device__ __forceinline__ const char* stats_row(const StatsArgs& a, int row, in
 constexpr int kSB = kStatsBlock;
 constexpr int kSW = kStatsBlock / 64;
 
+// A thread's last round of a slice: its vectors v + j kSB (j < 4) below
+// vend, loaded together like a full round, so that no wave trails the
+// others by a chain of single loads.  The loads past vend are clamped to
+// vend - 1 (v < vend) and their elements read as -inf.  Returns the number
+// of vectors below vend (a prefix of the four).
+template <int DT, bool VEC>
+__device__ __forceinline__ int last_round(const char* rp, int v, int vend, float* e)
+{
+    const int last = vend - 1;
+    const Raw<DT> r0 = load_raw<DT, VEC>(rp, v);
+    const Raw<DT> r1 = load_raw<DT, VEC>(rp, min(v + kSB, last));
+    const Raw<DT> r2 = load_raw<DT, VEC>(rp, min(v + 2 * kSB, last));
+    const Raw<DT> r3 = load_raw<DT, VEC>(rp, min(v + 3 * kSB, last));
+    decode<DT>(r0, e);
+    decode<DT>(r1, e + 8);
+    decode<DT>(r2, e + 16);
+    decode<DT>(r3, e + 24);
+    int n = 1;
+#pragma unroll
+    for (int j = 1; j < 4; ++j) {
+        const bool ok = v + j * kSB < vend;
+        n += ok ? 1 : 0;
+#pragma unroll
+        for (int t = 0; t < kVec; ++t) e[kVec * j + t] = ok ? e[kVec * j + t] : -INFINITY;
+    }
+    return n;
+}
+
+// The thread that takes a row's partial last vector (V not a multiple of 8)
+// when it falls in slice [v0, v1): the one whose vectors v0 + tid + n kSB reach it.
+__device__ __forceinline__ bool takes_partial(int v0, int v1, int nfull)
+{
+    return nfull < v1 && (nfull - v0) % kSB == (int)threadIdx.x;
+}
+
 // (max, sum of exp2) of logical vectors [v0, v1) of one row, reduced over the
 // 512-thread workgroup in a fixed order; thread 0 holds the result.  Called
 // by every thread of the workgroup.
@@ -97,13 +132,12 @@ __device__ __forceinline__ SoftPartial slice_softmax(const char* rp, int v0, int
         decode<DT>(r3, e + 24);
         soft_update<4 * kVec>(e, m, s, c);
     }
-    for (; v < vend; v += kSB) {
-        Raw<DT> r0 = load_raw<DT, VEC>(rp, v);
-        float e[kVec];
-        decode<DT>(r0, e);
-        soft_update<kVec>(e, m, s, c);
+    if (v < vend) {
+        float e[4 * kVec];
+        last_round<DT, VEC>(rp, v, vend, e);
+        soft_update<4 * kVec>(e, m, s, c);
     }
-    if (v == nfull && nfull < v1) {    // the row's partial last vector
+    if (takes_partial(v0, v1, nfull)) {    // the row's partial last vector
         float e[kVec];
         load_partial<DT>(rp, nfull, V - 8 * nfull, -INFINITY, e);
         soft_update<kVec>(e, m, s, c);
@@ -170,19 +204,22 @@ __device__ __forceinline__ ArgPartial slice_argmax(const char* rp, int v0, int v
         bvec = up ? v : bvec;
         bcnt = up ? 4 : bcnt;
     }
-    for (; v < vend; v += kSB) {
-        Raw<DT> r0 = load_raw<DT, VEC>(rp, v);
-        float e[kVec];
-        decode<DT>(r0, e);
-        float cm = e[0];
+    if (v < vend) {
+        float e[4 * kVec];
+        const int n = last_round<DT, VEC>(rp, v, vend, e);
+        float cm0 = e[0], cm1 = e[1];
 #pragma unroll
-        for (int j = 1; j < kVec; ++j) cm = fmaxf(cm, e[j]);
+        for (int j = 2; j < 4 * kVec; j += 2) {
+            cm0 = fmaxf(cm0, e[j]);
+            cm1 = fmaxf(cm1, e[j + 1]);
+        }
+        const float cm = fmaxf(cm0, cm1);
         const bool up = cm > bv;
         bv = up ? cm : bv;
         bvec = up ? v : bvec;
-        bcnt = up ? 1 : bcnt;
+        bcnt = up ? n : bcnt;
     }
-    if (v == nfull && nfull < v1) {
+    if (takes_partial(v0, v1, nfull)) {
         float e[kVec];
         load_partial<DT>(rp, nfull, V - 8 * nfull, -INFINITY, e);
         float cm = e[0];
