@@ -128,7 +128,7 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    cfg0 = synthetic.CONFIGS[cid]
+    cfg0 = synthetic.WORKLOADS[cid]
     es = {"fp32": 4, "fp16": 2, "bf16": 2}[cfg0.dtype]
     if cand:
         stream_rows = cfg0.C * cfg0.R

@@ -73,7 +73,7 @@ class Config:
         return self.k + 1
 
 
-CONFIGS = {
+WORKLOADS = {
     1: Config(1, B=1, k=4, V=32000, dtype="fp32", var_target=2.0, var_noise=1.0, spike=0.0,
               T=1.0, modes=("greedy", "sample")),
     2: Config(2, B=64, k=5, V=32000, dtype="fp16", var_target=3.0, var_noise=1.5, spike=0.0,
@@ -136,7 +136,7 @@ def generate(cid: int, device="cpu", set_index: int = 0, B: Optional[int] = None
              chunk_seqs: Optional[int] = None) -> Workload:
     """Materialise workload `cid` (optionally with B, V or k overridden for
     reduced-size cases) on `device`."""
-    cfg = CONFIGS[cid]
+    cfg = WORKLOADS[cid]
     if B is not None or V is not None or k is not None:
         cfg = dataclasses.replace(cfg, B=B or cfg.B, V=V or cfg.V, k=k or cfg.k)
     if seed is None:

@@ -158,7 +158,7 @@ def test_truncated_ties_and_masked_tokens(sv, dtype):
     z = z.masked_fill(mask, -float("inf"))
     y = y.masked_fill(mask[:, :k], -float("inf"))
     u = synthetic.uniforms24((B, k + 1), g, DEV)
-    w = synthetic.Workload(synthetic.CONFIGS[1], z, y, None, u, 1.0)
+    w = synthetic.Workload(synthetic.WORKLOADS[1], z, y, None, u, 1.0)
     for top_k, top_p in ((7, 1.0), (400, 1.0), (0, 0.83), (400, 0.61)):
         x = torch.from_numpy(truncated_drafts(f32(y), 1.0, top_k, top_p, 5)).to(DEV)
         check(sv, w, 1.0, x, top_k, top_p)
@@ -201,7 +201,7 @@ def test_truncated_deterministic(sv):
 def test_truncated_workload_subsets(sv, cid, top_k, top_p):
     """The workloads' own rows (vocabulary, dtype, temperature, spikes), a few
     sequences each."""
-    cfg = synthetic.CONFIGS[cid]
+    cfg = synthetic.WORKLOADS[cid]
     B = 6
     w = synthetic.generate(cid, device=DEV, B=B)
     y = f32(w.draft)
@@ -250,7 +250,7 @@ def test_truncated_many_equal_logits(sv, dtype):
     z[2, :, 2:68002] = -float("inf")               # a masked row: 68000 -inf
     y[2, :, 5:68005] = -float("inf")
     u = synthetic.uniforms24((B, k + 1), g, DEV)
-    w = synthetic.Workload(synthetic.CONFIGS[1], z, y, None, u, 1.0)
+    w = synthetic.Workload(synthetic.WORKLOADS[1], z, y, None, u, 1.0)
     for top_k, top_p in ((100, 1.0), (0, 0.9), (70000, 0.5), (3, 0.99)):
         x = torch.from_numpy(truncated_drafts(f32(y), 1.0, top_k, top_p, 9)).to(DEV)
         check(sv, w, 1.0, x, top_k, top_p)
