@@ -4,7 +4,8 @@ verification library.
 Argument marshalling only: every step of the verification runs in the HIP
 kernels behind the C ABI declared in ``include/spec_verify.h``.  PyTorch
 provides device memory (tensors) and streams.  There is no fallback: if the
-library is not built, importing this package raises.
+library is not built, importing this package raises.  An empty batch (B = 0)
+has nothing to verify: its (empty) outputs are returned without a call.
 """
 from __future__ import annotations
 
@@ -111,6 +112,8 @@ _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 def _stream(stream, device: torch.device):
     if stream is not None:
+        if stream.device != device:
+            raise ValueError(f"stream is on {stream.device}, the logits on {device}")
         return stream.cuda_stream
     if _raw_stream is not None:
         return _raw_stream(device.index)
@@ -198,6 +201,8 @@ def greedy(target: torch.Tensor, draft_tokens: torch.Tensor, *, out_tokens=None,
     _need(draft_tokens, "draft_tokens", (B, k), torch.int32, dev)
     out_tokens = _out(out_tokens, "out_tokens", (B, k + 1), torch.int32, dev)
     out_num_accepted = _out(out_num_accepted, "out_num_accepted", (B,), torch.int32, dev)
+    if B == 0:
+        return out_tokens, out_num_accepted
     ws, wsb = _workspace(workspace, B, k + 1, V, target.dtype, dev)
     st = lib().spec_verify_greedy(_ptr(target), ts, _ptr(draft_tokens), B, k, V,
                                   _sv_dtype(target.dtype), _ptr(out_tokens), _ptr(out_num_accepted),
@@ -240,6 +245,8 @@ def sample(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor
     else:
         out_p_x = None if out_p_x is None else _need(out_p_x, "out_p_x", (B, k), torch.float32, dev)
         out_q_x = None if out_q_x is None else _need(out_q_x, "out_q_x", (B, k), torch.float32, dev)
+    if B == 0:
+        return (out_tokens, out_num_accepted, out_p_x, out_q_x) if return_probs else (out_tokens, out_num_accepted)
     ws, wsb = _workspace(workspace, B, 2 * k + 1, V, target.dtype, dev)
     st = lib().spec_verify_sample(_ptr(target), ts, _ptr(draft), ds,
                                   _ptr(draft_tokens), _ptr(uniforms), float(temperature), B, k, V,
@@ -266,6 +273,8 @@ def greedy_ext(target: torch.Tensor, draft_tokens: torch.Tensor, *, workspace=No
     out_v = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
     out_mask = torch.empty((B,), dtype=torch.int64, device=dev)
     out_cnt = torch.empty((B,), dtype=torch.int32, device=dev)
+    if B == 0:
+        return out_tokens, out_na, out_v, out_mask, out_cnt
     ws, wsb = _workspace(workspace, B, k + 1, V, target.dtype, dev)
     st = lib().spec_verify_greedy_ext(_ptr(target), ts, _ptr(draft_tokens), B, k, V,
                                       _sv_dtype(target.dtype), _ptr(out_tokens), _ptr(out_na), _ptr(out_v),
@@ -285,6 +294,8 @@ def sample_lenient(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torc
     out_na = torch.empty((B,), dtype=torch.int32, device=dev)
     out_p_x = torch.empty((B, k), dtype=torch.float32, device=dev) if return_probs else None
     out_q_x = torch.empty((B, k), dtype=torch.float32, device=dev) if return_probs else None
+    if B == 0:
+        return (out_tokens, out_na, out_p_x, out_q_x) if return_probs else (out_tokens, out_na)
     ws, wsb = _workspace(workspace, B, 2 * k + 1, V, target.dtype, dev)
     st = lib().spec_verify_sample_lenient(_ptr(target), ts, _ptr(draft), ds, _ptr(draft_tokens),
                                           _ptr(uniforms), float(temperature), float(lenience), B, k, V,
@@ -309,6 +320,8 @@ def sample_truncated(target: torch.Tensor, draft: torch.Tensor, draft_tokens: to
     out_na = torch.empty((B,), dtype=torch.int32, device=dev)
     out_p_x = torch.empty((B, k), dtype=torch.float32, device=dev) if return_probs else None
     out_q_x = torch.empty((B, k), dtype=torch.float32, device=dev) if return_probs else None
+    if B == 0:
+        return (out_tokens, out_na, out_p_x, out_q_x) if return_probs else (out_tokens, out_na)
     ws, wsb = _workspace(workspace, B, 2 * k + 1, V, target.dtype, dev)
     st = lib().spec_verify_sample_truncated(_ptr(target), ts, _ptr(draft), ds, _ptr(draft_tokens),
                                             _ptr(uniforms), float(temperature), int(top_k),
@@ -344,6 +357,8 @@ def greedy_candidates_ext(target: torch.Tensor, cand_tokens: torch.Tensor, *, wo
     out_na = torch.empty((B,), dtype=torch.int32, device=dev)
     out_best = torch.empty((B,), dtype=torch.int32, device=dev)
     out_v = torch.empty((B, C, R), dtype=torch.int32, device=dev)
+    if B == 0:
+        return out_tokens, out_na, out_best, out_v
     ws, wsb = _workspace(workspace, B, C * R, V, target.dtype, dev)
     st = lib().spec_verify_greedy_candidates_ext(_ptr(target), ts, _ptr(cand_tokens),
                                                  B, C, L, R, V, _sv_dtype(target.dtype), _ptr(out_tokens),
@@ -363,6 +378,8 @@ def sample_lazy(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.T
     dev = target.device
     out_tokens = _out(out_tokens, "out_tokens", (B, k + 1), torch.int32, dev)
     out_num_accepted = _out(out_num_accepted, "out_num_accepted", (B,), torch.int32, dev)
+    if B == 0:
+        return out_tokens, out_num_accepted
     ws, wsb = _workspace(workspace, B, 2 * k + 1, V, target.dtype, dev)
     st = lib().spec_verify_sample_lazy(_ptr(target), ts, _ptr(draft), ds, _ptr(draft_tokens),
                                        _ptr(uniforms), float(temperature), B, k, V,
@@ -384,6 +401,8 @@ def greedy_lazy(target: torch.Tensor, draft_tokens: torch.Tensor, *, out_tokens=
     _need(draft_tokens, "draft_tokens", (B, k), torch.int32, dev)
     out_tokens = _out(out_tokens, "out_tokens", (B, k + 1), torch.int32, dev)
     out_num_accepted = _out(out_num_accepted, "out_num_accepted", (B,), torch.int32, dev)
+    if B == 0:
+        return out_tokens, out_num_accepted
     ws, wsb = _workspace(workspace, B, k + 1, V, target.dtype, dev)
     st = lib().spec_verify_greedy_lazy(_ptr(target), ts, _ptr(draft_tokens), B, k, V,
                                        _sv_dtype(target.dtype), _ptr(out_tokens), _ptr(out_num_accepted),
@@ -411,6 +430,8 @@ def greedy_tree(nodes: torch.Tensor, cand_tokens: torch.Tensor, cand_rows: torch
     out_tokens = torch.empty((B, L + 1), dtype=torch.int32, device=dev)
     out_na = torch.empty((B,), dtype=torch.int32, device=dev)
     out_best = torch.empty((B,), dtype=torch.int32, device=dev)
+    if B == 0:
+        return out_tokens, out_na, out_best
     ws, wsb = _workspace(workspace, B, N, V, nodes.dtype, dev)
     st = lib().spec_verify_greedy_tree(_ptr(nodes), ns, N, _ptr(cand_tokens),
                                        _ptr(cand_rows), B, C, L, R, V, _sv_dtype(nodes.dtype),
@@ -430,6 +451,8 @@ def greedy_candidates(target: torch.Tensor, cand_tokens: torch.Tensor, *, out_to
     out_tokens = _out(out_tokens, "out_tokens", (B, L + 1), torch.int32, dev)
     out_num_accepted = _out(out_num_accepted, "out_num_accepted", (B,), torch.int32, dev)
     out_best = _out(out_best, "out_best", (B,), torch.int32, dev)
+    if B == 0:
+        return out_tokens, out_num_accepted, out_best
     ws, wsb = _workspace(workspace, B, C * R, V, target.dtype, dev)
     st = lib().spec_verify_greedy_candidates(_ptr(target), ts, _ptr(cand_tokens),
                                              B, C, L, R, V, _sv_dtype(target.dtype), _ptr(out_tokens),

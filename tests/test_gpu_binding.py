@@ -87,3 +87,42 @@ def test_a_float_workspace_counts_its_bytes(sv, w):
     b = sv.sample(w.target, w.draft, w.tokens, w.uniforms, w.T)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_empty_batch_returns_empty_outputs(sv):
+    """B = 0: nothing to verify, so every entry point returns empty outputs
+    of the right shapes (the C ABI itself rejects B = 0)."""
+    k, V = 3, 1000
+    z = torch.zeros((0, k + 1, V), dtype=torch.bfloat16, device=DEV)
+    y = torch.zeros((0, k, V), dtype=torch.bfloat16, device=DEV)
+    x = torch.zeros((0, k), dtype=torch.int32, device=DEV)
+    u = torch.zeros((0, k + 1), dtype=torch.float32, device=DEV)
+    shapes = lambda outs: [tuple(o.shape) for o in outs]
+    assert shapes(sv.greedy(z, x)) == [(0, k + 1), (0,)]
+    assert shapes(sv.greedy_lazy(z, x)) == [(0, k + 1), (0,)]
+    assert shapes(sv.greedy_ext(z, x)) == [(0, k + 1), (0,), (0, k + 1), (0,), (0,)]
+    assert shapes(sv.sample(z, y, x, u, 1.0)) == [(0, k + 1), (0,)]
+    assert shapes(sv.sample(z, y, x, u, 1.0, return_probs=True)) == [(0, k + 1), (0,), (0, k), (0, k)]
+    assert shapes(sv.sample_lazy(z, y, x, u, 1.0)) == [(0, k + 1), (0,)]
+    assert shapes(sv.sample_lenient(z, y, x, u, 1.0, 2.0)) == [(0, k + 1), (0,)]
+    assert shapes(sv.sample_truncated(z, y, x, u, 1.0, 5, 0.9, return_probs=True)) == \
+        [(0, k + 1), (0,), (0, k), (0, k)]
+    C, L, R = 2, 4, 5
+    t = torch.zeros((0, C, R, V), dtype=torch.bfloat16, device=DEV)
+    ct = torch.zeros((0, C, L), dtype=torch.int32, device=DEV)
+    assert shapes(sv.greedy_candidates(t, ct)) == [(0, L + 1), (0,), (0,)]
+    assert shapes(sv.greedy_candidates_ext(t, ct)) == [(0, L + 1), (0,), (0,), (0, C, R)]
+    n = torch.zeros((0, 7, V), dtype=torch.bfloat16, device=DEV)
+    cr = torch.zeros((0, C, R), dtype=torch.int32, device=DEV)
+    assert shapes(sv.greedy_tree(n, ct, cr)) == [(0, L + 1), (0,), (0,)]
+
+
+def test_explicit_stream(sv, w):
+    """A caller's stream on the logits' device is used as given."""
+    s = torch.cuda.Stream(device=DEV)
+    s.wait_stream(torch.cuda.current_stream())     # the inputs were written on the default stream
+    a = sv.sample(w.target, w.draft, w.tokens, w.uniforms, w.T, stream=s)
+    s.synchronize()
+    b = sv.sample(w.target, w.draft, w.tokens, w.uniforms, w.T)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
