@@ -231,6 +231,15 @@ __device__ __forceinline__ float wave_max(float v)
     return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
+// The wave's sum in a fixed order: each row of 16 by DPP rotations, then the
+// four row sums in row order (the same result on every lane).
+__device__ __forceinline__ float wave_sum_f(float v)
+{
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) v += row_ror_f(v, o);
+    return ((lane_f(v, 0) + lane_f(v, 16)) + lane_f(v, 32)) + lane_f(v, 48);
+}
+
 __device__ __forceinline__ int wave_min_int(int v)
 {
 #pragma unroll

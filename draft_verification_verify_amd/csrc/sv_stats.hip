@@ -51,19 +51,6 @@ __device__ __forceinline__ void soft_update(const float* e, float& m, float& s, 
     m = mn;
 }
 
-__device__ __forceinline__ void soft_merge(float& m, float& s, float m2, float s2, float c)
-{
-    const float mn = fmaxf(m, m2);
-    if (mn == -INFINITY) {
-        m = mn;
-        s = 0.f;
-        return;
-    }
-    const float hn = stab_of(mn, c);
-    s = s * __builtin_amdgcn_exp2f(stab_of(m, c) - hn) + s2 * __builtin_amdgcn_exp2f(stab_of(m2, c) - hn);
-    m = mn;
-}
-
 __device__ __forceinline__ const char* stats_row(const StatsArgs& a, int row, int es)
 {
     return row < a.n_target_rows
@@ -143,25 +130,29 @@ __device__ __forceinline__ SoftPartial slice_softmax(const char* rp, int v0, int
         soft_update<kVec>(e, m, s, c);
     }
 
-    // the wave: DPP rotations inside each row of 16, then the four rows in order
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) soft_merge(m, s, row_ror_f(m, o), row_ror_f(s, o), c);
-    {
-        float wm = lane_f(m, 0), ws = lane_f(s, 0);
-#pragma unroll
-        for (int r = 1; r < 4; ++r) soft_merge(wm, ws, lane_f(m, 16 * r), lane_f(s, 16 * r), c);
-        m = wm;
-        s = ws;
-    }
+    // Merging: the wave's max first (exact in any order), then every lane's
+    // sum rescaled to it, exp2(stab(m) - stab(max)) with the same rounded
+    // stabilisers as the terms, and summed in a fixed order; the workgroup's
+    // eight wave results the same way.  One exp2 per lane instead of one per
+    // pairwise merge.  A lane or wave without a finite element holds s = 0.
+    const float wm = wave_max(m);
+    const float ws = wave_sum_f(wm == -INFINITY ? 0.f : s * __builtin_amdgcn_exp2f(stab_of(m, c) - stab_of(wm, c)));
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     if (lane == 0) {
-        lds_m[w] = m;
-        lds_s[w] = s;
+        lds_m[w] = wm;
+        lds_s[w] = ws;
     }
     __syncthreads();
-    float M = lds_m[0], S = lds_s[0];
-    if (threadIdx.x == 0)
-        for (int i = 1; i < kSW; ++i) soft_merge(M, S, lds_m[i], lds_s[i], c);
+    float M = -INFINITY, S = 0.f;
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int i = 0; i < kSW; ++i) M = fmaxf(M, lds_m[i]);
+        if (M != -INFINITY) {
+            const float hM = stab_of(M, c);
+#pragma unroll
+            for (int i = 0; i < kSW; ++i) S += lds_s[i] * __builtin_amdgcn_exp2f(stab_of(lds_m[i], c) - hM);
+        }
+    }
     __syncthreads();                   // the LDS slots may be reused by the caller
     return SoftPartial{M, S};
 }
