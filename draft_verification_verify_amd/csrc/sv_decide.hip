@@ -43,8 +43,9 @@ __device__ __forceinline__ unsigned long long ballot64(bool pred)
 // truncation, s is the kept mass and a token below the row's key threshold
 // has p = 0 (log p = -inf).
 
-// A row's normaliser: max m, l2s = log2 of the (kept) mass relative to
-// exp2(m * c), and the key threshold (0 keeps every token).
+// A row's normaliser: max m, l2s = log2 of the (kept) mass relative to the
+// max's weight (exp2(stab_of(m, c)) on softmax rows, exp2(m c) on truncated
+// rows, as log2_prob reads it), and the key threshold (0 keeps every token).
 struct RowNorm {
     float m, l2s;
     uint32_t tau;
