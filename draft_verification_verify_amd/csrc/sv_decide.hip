@@ -13,17 +13,29 @@ namespace sv {
 constexpr int kSeqPerBlock = kBlock / 64;
 
 // Larger value wins; equal values keep the smaller index.  An all -inf row
-// has index INT32_MAX in every split and maps to 0.
+// has index INT32_MAX in every split and maps to 0.  The partials are read
+// eight at a time (none past `splits`), so each batch's loads overlap.
 __device__ __forceinline__ int merge_arg(const ArgPartial* p, int splits)
 {
-    float v = p[0].v;
-    int idx = p[0].i;
-    for (int i = 1; i < splits; ++i) {
-        const float v2 = p[i].v;
-        const int i2 = p[i].i;
-        if (v2 > v || (v2 == v && i2 < idx)) {
-            v = v2;
-            idx = i2;
+    float v = -INFINITY;
+    int idx = INT32_MAX;
+    for (int i0 = 0; i0 < splits; i0 += 8) {
+        ArgPartial q[8];
+        const unsigned long long* p8 = reinterpret_cast<const unsigned long long*>(p);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {                  // one 8-byte load per partial
+            q[u] = ArgPartial{-INFINITY, INT32_MAX};
+            if (i0 + u < splits) {
+                const unsigned long long w = p8[i0 + u];
+                q[u] = ArgPartial{__uint_as_float((uint32_t)w), (int)(uint32_t)(w >> 32)};
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (i0 + u < splits && (q[u].v > v || (q[u].v == v && q[u].i < idx))) {
+                v = q[u].v;
+                idx = q[u].i;
+            }
         }
     }
     return idx == INT32_MAX ? 0 : idx;
@@ -51,21 +63,37 @@ struct RowNorm {
     uint32_t tau;
 };
 
-__device__ __forceinline__ RowNorm row_norm(const DecideSampleArgs& a, long long row)
+// The normalisers of target row rt and, when has_d, draft row rd, with the
+// two rows' loads issued together: their truncation summaries (TRUNC), or
+// each batch of their slice partials.  Without has_d, d is left as no row.
+// TRUNC is a template parameter so that neither form's loads share a branch
+// join with the other's (which would make the compiler wait for both).
+template <bool TRUNC>
+__device__ __forceinline__ void row_norms(const DecideSampleArgs& a, long long rt, long long rd, bool has_d,
+                                          RowNorm& t, RowNorm& d)
 {
-    RowNorm r;
-    if (a.trunc) {
-        const TruncRow t = a.trunc[row];
-        r.m = t.m;
-        r.l2s = t.l2s;
-        r.tau = t.tau;
-    } else {
-        float s;
-        merge_soft(a.partials + row * a.splits, a.splits, a.c, r.m, s);
-        r.l2s = log2f(s);
-        r.tau = 0u;
+    const long long rd_ = has_d ? rd : rt;         // a valid row either way
+    d = RowNorm{-INFINITY, -INFINITY, 0u};
+    if constexpr (TRUNC) {
+        const TruncRow tt = a.trunc[rt];
+        const TruncRow td = a.trunc[rd_];
+        t = RowNorm{tt.m, tt.l2s, tt.tau};
+        if (has_d) d = RowNorm{td.m, td.l2s, td.tau};
+        return;
     }
-    return r;
+    const SoftPartial* pt = a.partials + rt * a.splits;
+    const SoftPartial* pd = a.partials + rd_ * a.splits;
+    float mt = -INFINITY, st = 0.f, md = -INFINITY, sd = 0.f;
+    for (int i0 = 0; i0 < a.splits; i0 += kSoftBatch) {
+        SoftPartial qt[kSoftBatch], qd[kSoftBatch];
+        load_soft_batch(pt, i0, a.splits, qt);
+        load_soft_batch(pd, i0, a.splits, qd);
+        const int n = min(kSoftBatch, a.splits - i0);
+        merge_soft_batch(qt, n, a.c, mt, st);
+        merge_soft_batch(qd, n, a.c, md, sd);
+    }
+    t = RowNorm{mt, log2f(st), 0u};
+    if (has_d) d = RowNorm{md, log2f(sd), 0u};
 }
 
 // log2 of a token's probability, in the form its row's mass was summed in:
@@ -85,7 +113,7 @@ struct PosSample {
     bool reject;
 };
 
-template <int DT>
+template <int DT, bool TRUNC>
 __device__ __forceinline__ PosSample sample_position(const DecideSampleArgs& a, int b, int pos)
 {
     constexpr int ES = DT == DT_F32 ? 4 : 2;
@@ -98,20 +126,23 @@ __device__ __forceinline__ PosSample sample_position(const DecideSampleArgs& a, 
     r.x = -1;
     r.reject = false;
     const int tr = b * (k + 1) + pos;
-    r.t = row_norm(a, tr);
-    if (pos < k) {
-        const int nT = a.B * (k + 1);
-        const int dr = b * k + pos;
-        r.d = row_norm(a, nT + dr);
-        r.x = a.tokens[(long long)b * k + pos];
+    const int dr = b * k + pos;
+    const bool has_d = pos < k;
+    // the loads that depend on nothing go first: the draft token and its
+    // uniform, then both rows' statistics; only the gathers wait for them
+    const int pc = has_d ? pos : k - 1;            // unconditional loads (no branch to join)
+    const int xl = a.tokens[(long long)b * k + pc];
+    const float u = a.uniforms[(long long)b * (k + 1) + pc];
+    const int x = has_d ? xl : -1;
+    row_norms<TRUNC>(a, tr, (long long)a.B * (k + 1) + dr, has_d, r.t, r.d);
+    if (has_d) {
+        r.x = x;
         const bool valid = r.x >= 0 && r.x < a.V;
         if (valid) {
             const float zx = load_elem<DT>(row_ptr(a.target, tr, a.t_stride, ES), r.x);
             const float yx = load_elem<DT>(row_ptr(a.draft, dr, a.d_stride, ES), r.x);
-            const bool tr = a.trunc != nullptr;
-            const float lp = key_of<DT>(zx) >= r.t.tau ? log2_prob(zx, r.t, c, tr) : -INFINITY;
-            const float lq = key_of<DT>(yx) >= r.d.tau ? log2_prob(yx, r.d, c, tr) : -INFINITY;
-            const float u = a.uniforms[(long long)b * (k + 1) + pos];
+            const float lp = key_of<DT>(zx) >= r.t.tau ? log2_prob(zx, r.t, c, TRUNC) : -INFINITY;
+            const float lq = key_of<DT>(yx) >= r.d.tau ? log2_prob(yx, r.d, c, TRUNC) : -INFINITY;
             const float lpl = lp + a.log2_lenience;
             const bool accept = (lq <= lpl) || (u < exp2f(lpl - lq));
             r.reject = !accept;
@@ -143,7 +174,7 @@ __device__ __forceinline__ void write_desc(const DecideSampleArgs& a, int b, int
     a.out_num_accepted[b] = j;
 }
 
-template <int DT>
+template <int DT, bool TRUNC>
 __global__ __launch_bounds__(kBlock) void k_decide_sample(DecideSampleArgs a)
 {
     const int b = blockIdx.x * kSeqPerBlock + (threadIdx.x >> 6);
@@ -151,7 +182,7 @@ __global__ __launch_bounds__(kBlock) void k_decide_sample(DecideSampleArgs a)
     const int lane = threadIdx.x & 63;
     const int k = a.k;
     PosSample r{};
-    if (lane <= k) r = sample_position<DT>(a, b, lane);
+    if (lane <= k) r = sample_position<DT, TRUNC>(a, b, lane);
     const unsigned long long rej = ballot64(lane < k && r.reject);
     const int j = rej ? (__ffsll((long long)rej) - 1) : k;
 
@@ -182,7 +213,7 @@ __global__ __launch_bounds__(kBlock) void k_lazy_decide_sample(LazyArgs l, Decid
     const int pos = l.w0 + lane;
     const bool in = pos < l.w1;
     PosSample r{};
-    if (in) r = sample_position<DT>(a, b, pos);
+    if (in) r = sample_position<DT, false>(a, b, pos);      // early exit runs without truncation
     const unsigned long long rej = ballot64(in && pos < k && r.reject);
     int j = -1;
     if (rej) j = l.w0 + __ffsll((long long)rej) - 1;
@@ -205,11 +236,13 @@ __global__ __launch_bounds__(kBlock) void k_decide_greedy(DecideGreedyArgs a)
     if (b >= a.B) return;
     const int lane = threadIdx.x & 63;
     const int k = a.k;
+    // the token's load first (clamped, unconditional), so it overlaps the partials'
+    const int xl = a.tokens[(long long)b * k + min(lane, k - 1)];
     int amax = 0, x = -1;
     bool miss = false;
     if (lane <= k) amax = merge_arg(a.partials + (long long)(b * (k + 1) + lane) * a.splits, a.splits);
     if (lane < k) {
-        x = a.tokens[(long long)b * k + lane];
+        x = xl;
         miss = x != amax;
     }
     const unsigned long long mm = ballot64(miss);
@@ -240,12 +273,13 @@ __global__ __launch_bounds__(kBlock) void k_lazy_decide_greedy(LazyArgs l, Decid
     const int k = a.k;
     const int pos = l.w0 + lane;
     const bool in = pos < l.w1;
+    const int xl = a.tokens[(long long)b * k + min(pos, k - 1)];   // overlaps the partials' loads
     int amax = 0, x = -1;
     bool miss = false;
     if (in) {
         amax = merge_arg(a.partials + (long long)(b * (k + 1) + pos) * a.splits, a.splits);
         if (pos < k) {
-            x = a.tokens[(long long)b * k + pos];
+            x = xl;
             miss = x != amax;
         }
     }
@@ -340,14 +374,19 @@ hipError_t launch_decide_sample(int dt, const DecideSampleArgs& a, hipStream_t s
 {
     void* args[] = {const_cast<DecideSampleArgs*>(&a)};
     const unsigned grid = (unsigned)((a.B + kSeqPerBlock - 1) / kSeqPerBlock);
-    const void* f = dt == DT_F32 ? reinterpret_cast<const void*>(k_decide_sample<DT_F32>)
-                  : dt == DT_F16 ? reinterpret_cast<const void*>(k_decide_sample<DT_F16>)
-                                 : reinterpret_cast<const void*>(k_decide_sample<DT_BF16>);
+    const bool t = a.trunc != nullptr;
+    const void* f = dt == DT_F32 ? (t ? reinterpret_cast<const void*>(k_decide_sample<DT_F32, true>)
+                                      : reinterpret_cast<const void*>(k_decide_sample<DT_F32, false>))
+                  : dt == DT_F16 ? (t ? reinterpret_cast<const void*>(k_decide_sample<DT_F16, true>)
+                                      : reinterpret_cast<const void*>(k_decide_sample<DT_F16, false>))
+                                 : (t ? reinterpret_cast<const void*>(k_decide_sample<DT_BF16, true>)
+                                      : reinterpret_cast<const void*>(k_decide_sample<DT_BF16, false>));
     return hipLaunchKernel(f, dim3(grid), dim3(kBlock), args, 0, st);
 }
 
 hipError_t launch_lazy_decide_sample(int dt, const LazyArgs& l, const DecideSampleArgs& a, hipStream_t st)
 {
+    if (a.trunc) return hipErrorInvalidValue;     // early exit has no truncated form
     void* args[] = {const_cast<LazyArgs*>(&l), const_cast<DecideSampleArgs*>(&a)};
     const unsigned grid = (unsigned)((a.B + kSeqPerBlock - 1) / kSeqPerBlock);
     const void* f = dt == DT_F32 ? reinterpret_cast<const void*>(k_lazy_decide_sample<DT_F32>)

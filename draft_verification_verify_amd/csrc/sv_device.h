@@ -169,22 +169,69 @@ __device__ __forceinline__ float stab_of(float m, float c)
     return __fmul_rn(m, c);
 }
 
-// The merged (max, sum of exp2(z c - h)) of a row from its slice partials, in
-// slice order; each partial's sum is relative to its own stabiliser.
+// Slice partials are read kSoftBatch at a time, the batch's loads issued
+// together (one round trip per batch).  Partials past `splits` are not read
+// (the condition is uniform, so it costs a scalar branch, not a wait).
+constexpr int kSoftBatch = 8;
+
+__device__ __forceinline__ void load_soft_batch(const SoftPartial* p, int i0, int splits, SoftPartial* q)
+{
+    // one 8-byte load per partial, so (m, s) arrive together
+    const unsigned long long* p8 = reinterpret_cast<const unsigned long long*>(p);
+#pragma unroll
+    for (int u = 0; u < kSoftBatch; ++u) {
+        q[u] = SoftPartial{-INFINITY, 0.f};
+        if (i0 + u < splits) {
+            const unsigned long long w = p8[i0 + u];
+            q[u] = SoftPartial{__uint_as_float((uint32_t)w), __uint_as_float((uint32_t)(w >> 32))};
+        }
+    }
+}
+
+// Adds partials q[0..N) to (m, s): the new max first, then every sum
+// rescaled to it, exp2(stab(m_i) - stab(max)), and added in slice order.
+// s stays 0 while every max is -inf.
+template <int N>
+__device__ __forceinline__ void merge_soft_n(const SoftPartial* q, float c, float& m, float& s)
+{
+    float mn = m;
+#pragma unroll
+    for (int u = 0; u < N; ++u) mn = fmaxf(mn, q[u].m);
+    if (mn == -INFINITY) return;
+    const float hn = stab_of(mn, c);
+    float sn = m == -INFINITY ? 0.f : s * exp2f(stab_of(m, c) - hn);
+#pragma unroll
+    for (int u = 0; u < N; ++u) sn += q[u].s * exp2f(stab_of(q[u].m, c) - hn);
+    m = mn;
+    s = sn;
+}
+
+// The same for a uniform count n in [1, kSoftBatch]: one straight-line body
+// per count, so no merge is computed and then discarded.
+__device__ __forceinline__ void merge_soft_batch(const SoftPartial* q, int n, float c, float& m, float& s)
+{
+    switch (n) {
+    case 1: merge_soft_n<1>(q, c, m, s); break;
+    case 2: merge_soft_n<2>(q, c, m, s); break;
+    case 3: merge_soft_n<3>(q, c, m, s); break;
+    case 4: merge_soft_n<4>(q, c, m, s); break;
+    case 5: merge_soft_n<5>(q, c, m, s); break;
+    case 6: merge_soft_n<6>(q, c, m, s); break;
+    case 7: merge_soft_n<7>(q, c, m, s); break;
+    default: merge_soft_n<kSoftBatch>(q, c, m, s); break;
+    }
+}
+
+// The merged (max, sum of exp2(z c - h)) of a row from its slice partials;
+// each partial's sum is relative to its own stabiliser.
 __device__ __forceinline__ void merge_soft(const SoftPartial* p, int splits, float c, float& m, float& s)
 {
-    m = p[0].m;
-    s = p[0].s;
-    for (int i = 1; i < splits; ++i) {
-        const float m2 = p[i].m, s2 = p[i].s;
-        const float mn = fmaxf(m, m2);
-        if (mn == -INFINITY) {
-            s = 0.f;
-        } else {
-            const float hn = stab_of(mn, c);
-            s = s * exp2f(stab_of(m, c) - hn) + s2 * exp2f(stab_of(m2, c) - hn);
-        }
-        m = mn;
+    m = -INFINITY;
+    s = 0.f;
+    for (int i0 = 0; i0 < splits; i0 += kSoftBatch) {
+        SoftPartial q[kSoftBatch];
+        load_soft_batch(p, i0, splits, q);
+        merge_soft_batch(q, min(kSoftBatch, splits - i0), c, m, s);
     }
 }
 
