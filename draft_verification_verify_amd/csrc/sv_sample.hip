@@ -250,12 +250,15 @@ __global__ __launch_bounds__(kBlock) void k_sample_pick(SampleArgs a)
     constexpr int ES = DT == DT_F32 ? 4 : 2;
 
     const int b = blockIdx.x;
+    // the chunk totals do not depend on the descriptor: both loads go out together
+    const int ct = min((int)threadIdx.x, a.nchunks - 1);
+    const float my_sum = a.chunk_sums[(long long)b * a.nchunks + ct];
     const SampleDesc d = a.desc[b];
     if (!desc_ok(a, d)) return;                   // uniform across the workgroup
     const char* zr = row_ptr(a.target, d.t_row, a.t_stride, ES);
     const char* yr = d.kind == 0 ? row_ptr(a.draft, d.d_row, a.d_stride, ES) : zr;
 
-    if ((int)threadIdx.x < a.nchunks) s_sums[threadIdx.x] = a.chunk_sums[(long long)b * a.nchunks + threadIdx.x];
+    if ((int)threadIdx.x < a.nchunks) s_sums[threadIdx.x] = my_sum;
     __syncthreads();
     int kind = d.kind;
     double S = 0.0;
