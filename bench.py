@@ -425,6 +425,7 @@ def cpu_baseline(w, out_t, out_n, budget_s):
         "cores": cores,
         "kind": "oracle",
         "value_1_core": s1 * k1 / t1,
+        "cpu_model": _cpu_model(),
         "sample": (f"the first {nseq} sequences of the same workload ({nseq * k1} rows), run "
                    f"repeatedly in chunks of {chunk}: {s1} sequences on 1 thread in {t1:.1f} s, "
                    f"then {sn} sequences on {cores} threads in {tn:.1f} s; C oracle in double "
@@ -432,6 +433,18 @@ def cpu_baseline(w, out_t, out_n, budget_s):
                    f"reads fewer rows than it counts"),
         "parity_vs_gpu": rep.summary(),
     }
+
+
+def _cpu_model() -> str:
+    """The host CPU's model name, as /proc/cpuinfo reports it (or "unknown")."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def calibrate_copy(nbytes=1 << 30):
