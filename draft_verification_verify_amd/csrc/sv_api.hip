@@ -387,7 +387,12 @@ int lazy_bounds(int k, int* bounds)
     return n;
 }
 
-constexpr int kLazyGrid = 4096;
+// Workgroups of an early-exit statistics launch, which loop over the window's
+// (row, slice) units.  A late window is often nearly empty, and every one of
+// its workgroups is still dispatched to find no work: 2048 (8 per CU) kept
+// the full first window's rate and made greedy early exit about 4% faster
+// than 4096 on a 512-sequence batch; 1024 slowed the sampling form.
+constexpr int kLazyGrid = 2048;
 
 LazyArgs lazy_args(const void* target, long long ts, const void* draft, long long ds, int B, int k,
                    int V, const StatsPlan& sp, float c, const Workspace& w)
