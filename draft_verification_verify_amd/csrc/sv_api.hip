@@ -384,6 +384,12 @@ int lazy_bounds(int k, int* bounds)
         bounds[n++] = next < k + 1 ? next : k + 1;
         next = next < 2 ? next + 1 : next * 2;
     }
+    // a last window [k, k+1) would hold only the bonus row and cost two
+    // launches that are nearly always empty: the window before takes it
+    if (n >= 3 && bounds[n - 2] == k) {
+        bounds[n - 2] = k + 1;
+        --n;
+    }
     return n;
 }
 

@@ -232,7 +232,8 @@ int spec_verify_greedy_tree(const void* node_logits, long long row_stride, int N
  * looks at.  The rule examines position i only when every earlier draft was
  * accepted (production blog, "The acceptance rule": left to right, stopping
  * at the first rejection), so positions are taken in windows [0,1), [1,2),
- * [2,4), [4,8), ... and a window's rows are streamed only for the sequences
+ * [2,4), [4,8), ... (the bonus row k joins the last window rather than
+ * forming one of its own) and a window's rows are streamed only for the sequences
  * still undecided after the previous windows (a device-side work list; no
  * host synchronisation).  Rows read per sequence: those up to its first
  * rejection, rounded up to the end of that window, plus the sampled row.
