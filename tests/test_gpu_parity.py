@@ -567,3 +567,50 @@ def test_many_short_rows(sv):
     torch.cuda.synchronize()
     bad, _, _ = parity.check_greedy(f32(w.target), npi(x), npi(toks), npi(na))
     assert not bad
+
+
+# ---------------------------------------------------------------------------
+# a seeded sweep over random shapes, dtypes, temperatures, scales and layouts
+# ---------------------------------------------------------------------------
+def random_case(i):
+    """Case i of the sweep: log-uniform V in [1, 70000] (ragged tails), k up
+    to 63, temperatures 0.05-5, logit variances 0.5-100, three layouts; the
+    oracle's work is capped at 6e6 elements per case."""
+    r = np.random.default_rng(9000 + i)
+    dtype = ["fp32", "fp16", "bf16"][int(r.integers(3))]
+    k = int(r.choice([1, 2, 3, 5, 8, 16, 31, 63]))
+    V = max(1, int(np.exp(r.uniform(0.0, np.log(70000.0)))))
+    B = int(r.integers(1, 41))
+    while B > 1 and B * (2 * k + 1) * V > 6_000_000:
+        B //= 2
+    V = min(V, max(1, 6_000_000 // (B * (2 * k + 1))))
+    T = float(np.exp(r.uniform(np.log(0.05), np.log(5.0))))
+    var_t = float(r.choice([0.5, 2.0, 9.0, 100.0]))
+    layout = ["dense", "padded", "offset"][int(r.integers(3))]
+    return dtype, B, k, V, T, var_t, layout
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_cases(sv, i):
+    dtype, B, k, V, T, var_t, layout = random_case(i)
+    print(f"case {i}: {dtype} B={B} k={k} V={V} T={T:.3f} var={var_t} {layout}", flush=True)
+    w = synthetic.chain(B, k, V, dtype, var_target=var_t, var_noise=0.3 * var_t, T=T, seed=7000 + i,
+                        device=DEV)
+    gen = torch.Generator(device=DEV).manual_seed(i)
+    toks, na, px, qx = run_sample(sv, w, layout, gen)
+    assert_sample_parity(w, toks, na, px, qx)
+    # the layout changes only how rows are loaded: the dense call agrees bit for
+    # bit, and so does early exit
+    a = sv.sample(w.target, w.draft, w.tokens, w.uniforms, w.T)
+    lz = sv.sample_lazy(w.target, w.draft, w.tokens, w.uniforms, w.T)
+    torch.cuda.synchronize()
+    assert np.array_equal(toks, npi(a[0])) and np.array_equal(na, npi(a[1]))
+    assert np.array_equal(npi(lz[0]), npi(a[0])) and np.array_equal(npi(lz[1]), npi(a[1]))
+    # greedy on drafts that follow the argmax for a while
+    x = corrupt_after_argmax(w.target, k, gen)
+    g = sv.greedy(with_layout(w.target, layout, gen), x)
+    gl = sv.greedy_lazy(w.target, x)
+    torch.cuda.synchronize()
+    bad, _, _ = parity.check_greedy(f32(w.target), npi(x), npi(g[0]), npi(g[1]))
+    assert not bad
+    assert np.array_equal(npi(gl[0]), npi(g[0])) and np.array_equal(npi(gl[1]), npi(g[1]))
