@@ -277,3 +277,36 @@ def test_truncated_k63(sv, dtype):
     """The longest draft one wave decides (k = 63)."""
     w, T, x = workload(3, 63, 1000, dtype, 63, 10, 0.9)
     check(sv, w, T, x, 10, 0.9)
+
+
+# ---------------------------------------------------------------------------
+# a seeded sweep over random shapes, dtypes, scales and truncation settings
+# ---------------------------------------------------------------------------
+def random_trunc_case(i):
+    """Case i: log-uniform V in [1, 70000], k up to 31, temperatures 0.1-3,
+    logit variances 0.5-100, top-k from off to V-1 and top-p from off to
+    1e-6; the oracle's work is capped at 2e6 elements per case."""
+    r = np.random.default_rng(5000 + i)
+    dtype = ["fp32", "fp16", "bf16"][int(r.integers(3))]
+    k = int(r.choice([1, 2, 4, 8, 16, 31]))
+    V = max(1, int(np.exp(r.uniform(0.0, np.log(70000.0)))))
+    B = int(r.integers(1, 17))
+    while B > 1 and B * (2 * k + 1) * V > 2_000_000:
+        B //= 2
+    V = min(V, max(1, 2_000_000 // (B * (2 * k + 1))))
+    T = float(np.exp(r.uniform(np.log(0.1), np.log(3.0))))
+    var_t = float(r.choice([0.5, 2.0, 9.0, 100.0]))
+    top_k = int(r.choice([0, 1, 2, 5, 50, 1000, max(1, V - 1)]))
+    top_p = float(r.choice([1.0, 0.999, 0.9, 0.5, 0.1, 1e-6]))
+    return dtype, B, k, V, T, var_t, top_k, top_p
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_truncated_cases(sv, i):
+    dtype, B, k, V, T, var_t, top_k, top_p = random_trunc_case(i)
+    print(f"case {i}: {dtype} B={B} k={k} V={V} T={T:.3f} var={var_t} top_k={top_k} top_p={top_p}",
+          flush=True)
+    w = synthetic.chain(B, k, V, dtype, var_target=var_t, var_noise=0.3 * var_t, T=T, seed=6000 + i,
+                        device=DEV)
+    x = torch.from_numpy(truncated_drafts(f32(w.draft), T, top_k, top_p, 6000 + i)).to(DEV)
+    check(sv, w, T, x, top_k, top_p)
