@@ -614,3 +614,41 @@ def test_random_cases(sv, i):
     bad, _, _ = parity.check_greedy(f32(w.target), npi(x), npi(g[0]), npi(g[1]))
     assert not bad
     assert np.array_equal(npi(gl[0]), npi(g[0])) and np.array_equal(npi(gl[1]), npi(g[1]))
+
+
+def random_candidate_case(i):
+    """Case i: C x L up to 64 scored tokens, R = L or L+1, log-uniform V in
+    [1, 60000], all three dtypes; the oracle's work capped at 8e6 elements."""
+    r = np.random.default_rng(8000 + i)
+    dtype = ["fp32", "fp16", "bf16"][int(r.integers(3))]
+    C = int(r.integers(1, 9))
+    L = int(r.integers(1, min(63, 64 // C) + 1))
+    R = L + int(r.integers(2))
+    V = max(1, int(np.exp(r.uniform(0.0, np.log(60000.0)))))
+    B = int(r.integers(1, 25))
+    while B > 1 and B * C * R * V > 8_000_000:
+        B //= 2
+    V = min(V, max(1, 8_000_000 // (B * C * R)))
+    return dtype, B, C, L, R, V
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_candidate_cases(sv, i):
+    dtype, B, C, L, R, V = random_candidate_case(i)
+    print(f"case {i}: {dtype} B={B} C={C} L={L} R={R} V={V}", flush=True)
+    w = synthetic.candidates(B, C, L, R, V, dtype, spike=8.0, seed=8000 + i, device=DEV)
+    toks, A, best = sv.greedy_candidates(w.target, w.tokens)
+    et, ea, eb, ev = sv.greedy_candidates_ext(w.target, w.tokens)
+    # the same rows as a token tree: node rows in a shuffled order, mapped back
+    g = torch.Generator(device=DEV).manual_seed(i)
+    perm = torch.randperm(C * R, generator=g, device=DEV)
+    nodes = w.target.reshape(B, C * R, V)[:, perm].contiguous()
+    inv = torch.argsort(perm).to(torch.int32)
+    rows = inv.reshape(1, C, R).expand(B, C, R).contiguous()
+    tt, ta, tb = sv.greedy_tree(nodes, w.tokens, rows)
+    torch.cuda.synchronize()
+    bad, _, _, _ = parity.check_candidates(f32(w.target), npi(w.tokens), npi(toks), npi(A), npi(best))
+    assert not bad, bad[:5]
+    for u, v in ((et, toks), (ea, A), (eb, best), (tt, toks), (ta, A), (tb, best)):
+        assert np.array_equal(npi(u), npi(v))
+    assert not parity.check_row_argmax(f32(w.target).reshape(B * C * R, V), npi(ev).reshape(-1))
