@@ -614,6 +614,13 @@ def test_random_cases(sv, i):
     bad, _, _ = parity.check_greedy(f32(w.target), npi(x), npi(g[0]), npi(g[1]))
     assert not bad
     assert np.array_equal(npi(gl[0]), npi(g[0])) and np.array_equal(npi(gl[1]), npi(g[1]))
+    # the lenient rule with a random l >= 1
+    lenience = 1.0 + float(np.random.default_rng(i).exponential(2.0))
+    lt, ln = sv.sample_lenient(w.target, w.draft, w.tokens, w.uniforms, w.T, lenience)
+    torch.cuda.synchronize()
+    rep = parity.check_sample(f32(w.target), f32(w.draft), npi(w.tokens), npi(w.uniforms), w.T,
+                              npi(lt), npi(ln), eps=EPS, lenience=lenience)
+    assert rep.ok(), (lenience, rep.summary(), rep.failures[:3])
 
 
 def random_candidate_case(i):
