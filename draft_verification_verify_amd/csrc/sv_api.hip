@@ -207,13 +207,25 @@ int greedy_impl(const void* target_logits, long long target_row_stride,
     return SV_OK;
 }
 
-int sample_impl(const void* target_logits, long long target_row_stride,
-                const void* draft_logits, long long draft_row_stride,
-                const int* draft_tokens, const float* uniforms, float temperature,
-                float lenience, int top_k, float top_p, int B, int k, int V, int dtype,
-                int* out_tokens, int* out_num_accepted,
-                float* out_p_x, float* out_q_x,
-                void* workspace, size_t workspace_bytes, void* hip_stream)
+// What every sampling entry point checks and derives before its first
+// launch, in this order: arguments, the workspace, the statistics plan, the
+// stream and c = log2(e) / T.
+struct SampleCall {
+    Workspace w;
+    StatsPlan sp;
+    long long rows;
+    float c;
+    bool vec;
+    bool trunc;                        // top-k or top-p is on
+    hipStream_t st;
+};
+
+int prepare_sample(const void* target_logits, long long target_row_stride,
+                   const void* draft_logits, long long draft_row_stride,
+                   const int* draft_tokens, const float* uniforms, float temperature,
+                   float lenience, int top_k, float top_p, int B, int k, int V, int dtype,
+                   const int* out_tokens, const int* out_num_accepted,
+                   void* workspace, size_t workspace_bytes, void* hip_stream, SampleCall& sc)
 {
     if (!dtype_ok(dtype)) return SV_EDTYPE;
     if (!target_logits || !draft_logits || !draft_tokens || !uniforms || !out_tokens ||
@@ -224,53 +236,30 @@ int sample_impl(const void* target_logits, long long target_row_stride,
     if (!(temperature > 0.f) || !isfinite(temperature)) return SV_EINVAL;
     if (!(lenience >= 1.f) || !isfinite(lenience)) return SV_EINVAL;
     if (top_k < 0 || !(top_p > 0.f) || isnan(top_p)) return SV_EINVAL;
-    const bool trunc = (top_k >= 1 && top_k < V) || top_p < 1.f;
-    if (trunc && V > kMaxTruncV) return SV_EINVAL;
+    sc.trunc = (top_k >= 1 && top_k < V) || top_p < 1.f;
+    if (sc.trunc && V > kMaxTruncV) return SV_EINVAL;
     const double cd = 1.4426950408889634 / (double)temperature;
     if (!isfinite(cd) || cd > 3.0e38) return SV_EINVAL;
-    const long long rows = (long long)B * (2 * k + 1);
-    if (!fits_grid(rows, V)) return SV_EINVAL;
-    Workspace w = layout(static_cast<char*>(workspace), B, rows, V);
-    if (!workspace || workspace_bytes < w.bytes) return SV_EWORKSPACE;
-    hipStream_t st = static_cast<hipStream_t>(hip_stream);
-    const float c = (float)cd;
-    const bool vec = vec_ok(target_logits, target_row_stride, dtype) &&
-                     vec_ok(draft_logits, draft_row_stride, dtype);
+    sc.rows = (long long)B * (2 * k + 1);
+    if (!fits_grid(sc.rows, V)) return SV_EINVAL;
+    sc.w = layout(static_cast<char*>(workspace), B, sc.rows, V);
+    if (!workspace || workspace_bytes < sc.w.bytes) return SV_EWORKSPACE;
+    sc.st = static_cast<hipStream_t>(hip_stream);
+    sc.c = (float)cd;
+    sc.vec = vec_ok(target_logits, target_row_stride, dtype) && vec_ok(draft_logits, draft_row_stride, dtype);
+    sc.sp = plan_stats(sc.rows, V);
+    return SV_OK;
+}
 
-    const StatsPlan sp = plan_stats(rows, V);
-    StatsArgs sa;
-    sa.target = target_logits;
-    sa.t_stride = target_row_stride;
-    sa.draft = draft_logits;
-    sa.d_stride = draft_row_stride;
-    sa.n_target_rows = B * (k + 1);
-    sa.n_rows = (int)rows;
-    sa.V = V;
-    sa.nvec = sp.nvec;
-    sa.splits = sp.splits;
-    sa.vec_per_split = sp.vec_per_split;
-    sa.c = c;
-    sa.partials = w.partials;
-    prof_begin(st);
-    if (trunc) {
-        TruncArgs ta;
-        ta.target = target_logits;
-        ta.t_stride = target_row_stride;
-        ta.draft = draft_logits;
-        ta.d_stride = draft_row_stride;
-        ta.n_target_rows = B * (k + 1);
-        ta.n_rows = (int)rows;
-        ta.V = V;
-        ta.c = c;
-        ta.top_k = top_k;
-        ta.top_p = top_p;
-        ta.rows = w.trunc;
-        if (launch_trunc_rows(dtype, vec, ta, st) != hipSuccess) return SV_EHIP;
-    } else {
-        if (launch_softmax_stats(dtype, vec, sa, st) != hipSuccess) return SV_EHIP;
-    }
-    prof_end(st);
-
+// The decision kernel's arguments: the rows' slice partials, or with
+// truncation the truncated rows' summaries.
+DecideSampleArgs decide_sample_args(const void* target_logits, long long target_row_stride,
+                                    const void* draft_logits, long long draft_row_stride,
+                                    const int* draft_tokens, const float* uniforms, float lenience,
+                                    int B, int k, int V, const SampleCall& sc,
+                                    int* out_tokens, int* out_num_accepted,
+                                    float* out_p_x, float* out_q_x)
+{
     DecideSampleArgs da;
     da.target = target_logits;
     da.t_stride = target_row_stride;
@@ -281,38 +270,101 @@ int sample_impl(const void* target_logits, long long target_row_stride,
     da.B = B;
     da.k = k;
     da.V = V;
-    da.splits = sp.splits;
-    da.c = c;
+    da.splits = sc.sp.splits;
+    da.c = sc.c;
     da.log2_lenience = (float)log2((double)lenience);
-    da.partials = static_cast<const SoftPartial*>(w.partials);
-    da.trunc = trunc ? w.trunc : nullptr;
+    da.partials = static_cast<const SoftPartial*>(sc.w.partials);
+    da.trunc = sc.trunc ? sc.w.trunc : nullptr;
     da.out_tokens = out_tokens;
     da.out_num_accepted = out_num_accepted;
     da.out_p_x = out_p_x;
     da.out_q_x = out_q_x;
-    da.desc = w.desc;
-    if (launch_decide_sample(dtype, da, st) != hipSuccess) return SV_EHIP;
+    da.desc = sc.w.desc;
+    return da;
+}
 
-    const SamplePlan pp = plan_sample(B, sp.nvec);
+// The sampler's arguments: the round's one draw per sequence.
+SampleArgs sampler_args(const void* target_logits, long long target_row_stride,
+                        const void* draft_logits, long long draft_row_stride,
+                        int B, int k, int V, const SampleCall& sc, int* out_tokens)
+{
+    const SamplePlan pp = plan_sample(B, sc.sp.nvec);
     SampleArgs ma;
     ma.target = target_logits;
     ma.t_stride = target_row_stride;
     ma.draft = draft_logits;
     ma.d_stride = draft_row_stride;
     ma.V = V;
-    ma.nvec = sp.nvec;
+    ma.nvec = sc.sp.nvec;
     ma.nchunks = pp.nchunks;
     ma.vec_per_chunk = pp.vec_per_chunk;
     ma.chunks_per_block = pp.chunks_per_block;
     ma.blocks_per_seq = pp.blocks_per_seq;
-    ma.c = c;
-    ma.desc = w.desc;
-    ma.chunk_sums = w.chunk_sums;
+    ma.c = sc.c;
+    ma.desc = sc.w.desc;
+    ma.chunk_sums = sc.w.chunk_sums;
     ma.out_tokens = out_tokens;
     ma.out_row = k + 1;
     ma.n_target_rows = B * (k + 1);
     ma.n_draft_rows = B * k;
-    if (launch_sample(dtype, vec, trunc, B, ma, st) != hipSuccess) return SV_EHIP;
+    return ma;
+}
+
+int sample_impl(const void* target_logits, long long target_row_stride,
+                const void* draft_logits, long long draft_row_stride,
+                const int* draft_tokens, const float* uniforms, float temperature,
+                float lenience, int top_k, float top_p, int B, int k, int V, int dtype,
+                int* out_tokens, int* out_num_accepted,
+                float* out_p_x, float* out_q_x,
+                void* workspace, size_t workspace_bytes, void* hip_stream)
+{
+    SampleCall sc;
+    const int status = prepare_sample(target_logits, target_row_stride, draft_logits, draft_row_stride,
+                                      draft_tokens, uniforms, temperature, lenience, top_k, top_p, B, k, V,
+                                      dtype, out_tokens, out_num_accepted, workspace, workspace_bytes,
+                                      hip_stream, sc);
+    if (status != SV_OK) return status;
+
+    prof_begin(sc.st);
+    if (sc.trunc) {
+        TruncArgs ta;
+        ta.target = target_logits;
+        ta.t_stride = target_row_stride;
+        ta.draft = draft_logits;
+        ta.d_stride = draft_row_stride;
+        ta.n_target_rows = B * (k + 1);
+        ta.n_rows = (int)sc.rows;
+        ta.V = V;
+        ta.c = sc.c;
+        ta.top_k = top_k;
+        ta.top_p = top_p;
+        ta.rows = sc.w.trunc;
+        if (launch_trunc_rows(dtype, sc.vec, ta, sc.st) != hipSuccess) return SV_EHIP;
+    } else {
+        StatsArgs sa;
+        sa.target = target_logits;
+        sa.t_stride = target_row_stride;
+        sa.draft = draft_logits;
+        sa.d_stride = draft_row_stride;
+        sa.n_target_rows = B * (k + 1);
+        sa.n_rows = (int)sc.rows;
+        sa.V = V;
+        sa.nvec = sc.sp.nvec;
+        sa.splits = sc.sp.splits;
+        sa.vec_per_split = sc.sp.vec_per_split;
+        sa.c = sc.c;
+        sa.partials = sc.w.partials;
+        if (launch_softmax_stats(dtype, sc.vec, sa, sc.st) != hipSuccess) return SV_EHIP;
+    }
+    prof_end(sc.st);
+
+    const DecideSampleArgs da =
+        decide_sample_args(target_logits, target_row_stride, draft_logits, draft_row_stride, draft_tokens,
+                           uniforms, lenience, B, k, V, sc, out_tokens, out_num_accepted, out_p_x, out_q_x);
+    if (launch_decide_sample(dtype, da, sc.st) != hipSuccess) return SV_EHIP;
+    const SampleArgs ma =
+        sampler_args(target_logits, target_row_stride, draft_logits, draft_row_stride, B, k, V, sc, out_tokens);
+    if (launch_sample(dtype, sc.vec, sc.trunc, B, ma, sc.st) != hipSuccess) return SV_EHIP;
     return SV_OK;
 }
 
@@ -567,76 +619,28 @@ int spec_verify_sample_lazy(const void* target_logits, long long target_row_stri
                             int B, int k, int V, int dtype, int* out_tokens, int* out_num_accepted,
                             void* workspace, size_t workspace_bytes, void* hip_stream)
 {
-    if (!dtype_ok(dtype)) return SV_EDTYPE;
-    if (!target_logits || !draft_logits || !draft_tokens || !uniforms || !out_tokens ||
-        !out_num_accepted)
-        return SV_EINVAL;
-    if (B < 1 || k < 1 || k > SV_MAX_K || V < 1 || V > kMaxV) return SV_EINVAL;
-    if (target_row_stride < V || draft_row_stride < V) return SV_EINVAL;
-    if (!(temperature > 0.f) || !isfinite(temperature)) return SV_EINVAL;
-    const double cd = 1.4426950408889634 / (double)temperature;
-    if (!isfinite(cd) || cd > 3.0e38) return SV_EINVAL;
-    const long long rows = (long long)B * (2 * k + 1);
-    if (!fits_grid(rows, V)) return SV_EINVAL;
-    Workspace w = layout(static_cast<char*>(workspace), B, rows, V);
-    if (!workspace || workspace_bytes < w.bytes) return SV_EWORKSPACE;
-    hipStream_t st = static_cast<hipStream_t>(hip_stream);
-    const float c = (float)cd;
-    const bool vec = vec_ok(target_logits, target_row_stride, dtype) &&
-                     vec_ok(draft_logits, draft_row_stride, dtype);
-    const StatsPlan sp = plan_stats(rows, V);
+    SampleCall sc;
+    const int status = prepare_sample(target_logits, target_row_stride, draft_logits, draft_row_stride,
+                                      draft_tokens, uniforms, temperature, 1.f, 0, 1.f, B, k, V, dtype,
+                                      out_tokens, out_num_accepted, workspace, workspace_bytes, hip_stream,
+                                      sc);
+    if (status != SV_OK) return status;
 
-    DecideSampleArgs da;
-    da.target = target_logits;
-    da.t_stride = target_row_stride;
-    da.draft = draft_logits;
-    da.d_stride = draft_row_stride;
-    da.tokens = draft_tokens;
-    da.uniforms = uniforms;
-    da.B = B;
-    da.k = k;
-    da.V = V;
-    da.splits = sp.splits;
-    da.c = c;
-    da.log2_lenience = 0.f;
-    da.partials = static_cast<const SoftPartial*>(w.partials);
-    da.trunc = nullptr;
-    da.out_tokens = out_tokens;
-    da.out_num_accepted = out_num_accepted;
-    da.out_p_x = nullptr;
-    da.out_q_x = nullptr;
-    da.desc = w.desc;
-
+    const DecideSampleArgs da =
+        decide_sample_args(target_logits, target_row_stride, draft_logits, draft_row_stride, draft_tokens,
+                           uniforms, 1.f, B, k, V, sc, out_tokens, out_num_accepted, nullptr, nullptr);
     LazyArgs l = lazy_args(target_logits, target_row_stride, draft_logits, draft_row_stride, B, k, V,
-                           sp, c, w);
+                           sc.sp, sc.c, sc.w);
     int bounds[16];
     const int nb = lazy_bounds(k, bounds);
     for (int p = 0; p + 1 < nb; ++p) {
-        lazy_window(l, w, bounds, p, B);
-        if (launch_lazy_stats(dtype, vec, true, lazy_grid(l, true), l, st) != hipSuccess) return SV_EHIP;
-        if (launch_lazy_decide_sample(dtype, l, da, st) != hipSuccess) return SV_EHIP;
+        lazy_window(l, sc.w, bounds, p, B);
+        if (launch_lazy_stats(dtype, sc.vec, true, lazy_grid(l, true), l, sc.st) != hipSuccess) return SV_EHIP;
+        if (launch_lazy_decide_sample(dtype, l, da, sc.st) != hipSuccess) return SV_EHIP;
     }
-
-    const SamplePlan pp = plan_sample(B, sp.nvec);
-    SampleArgs ma;
-    ma.target = target_logits;
-    ma.t_stride = target_row_stride;
-    ma.draft = draft_logits;
-    ma.d_stride = draft_row_stride;
-    ma.V = V;
-    ma.nvec = sp.nvec;
-    ma.nchunks = pp.nchunks;
-    ma.vec_per_chunk = pp.vec_per_chunk;
-    ma.chunks_per_block = pp.chunks_per_block;
-    ma.blocks_per_seq = pp.blocks_per_seq;
-    ma.c = c;
-    ma.desc = w.desc;
-    ma.chunk_sums = w.chunk_sums;
-    ma.out_tokens = out_tokens;
-    ma.out_row = k + 1;
-    ma.n_target_rows = B * (k + 1);
-    ma.n_draft_rows = B * k;
-    if (launch_sample(dtype, vec, false, B, ma, st) != hipSuccess) return SV_EHIP;
+    const SampleArgs ma =
+        sampler_args(target_logits, target_row_stride, draft_logits, draft_row_stride, B, k, V, sc, out_tokens);
+    if (launch_sample(dtype, sc.vec, false, B, ma, sc.st) != hipSuccess) return SV_EHIP;
     return SV_OK;
 }
 
