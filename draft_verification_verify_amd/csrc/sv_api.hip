@@ -158,52 +158,81 @@ void prof_end(hipStream_t st)
     g_prof.armed = false;
 }
 
+// What every greedy entry point checks and derives before its first launch.
+struct GreedyCall {
+    Workspace w;
+    StatsPlan sp;
+    long long rows;
+    bool vec;
+    hipStream_t st;
+};
+
+int prepare_greedy(const void* target_logits, long long target_row_stride, const int* draft_tokens,
+                   int B, int k, int V, int dtype, const int* out_tokens, const int* out_num_accepted,
+                   void* workspace, size_t workspace_bytes, void* hip_stream, GreedyCall& gc)
+{
+    if (!dtype_ok(dtype)) return SV_EDTYPE;
+    if (!target_logits || !draft_tokens || !out_tokens || !out_num_accepted) return SV_EINVAL;
+    if (B < 1 || k < 1 || k > SV_MAX_K || V < 1 || V > kMaxV || target_row_stride < V) return SV_EINVAL;
+    gc.rows = (long long)B * (k + 1);
+    if (!fits_grid(gc.rows, V)) return SV_EINVAL;
+    gc.w = layout(static_cast<char*>(workspace), B, gc.rows, V);
+    if (!workspace || workspace_bytes < gc.w.bytes) return SV_EWORKSPACE;
+    gc.st = static_cast<hipStream_t>(hip_stream);
+    gc.vec = vec_ok(target_logits, target_row_stride, dtype);
+    gc.sp = plan_stats(gc.rows, V);
+    return SV_OK;
+}
+
+DecideGreedyArgs decide_greedy_args(const int* draft_tokens, int B, int k, const GreedyCall& gc,
+                                    int* out_tokens, int* out_num_accepted, int* out_argmax,
+                                    unsigned long long* out_match_mask, int* out_num_match)
+{
+    DecideGreedyArgs da;
+    da.tokens = draft_tokens;
+    da.B = B;
+    da.k = k;
+    da.splits = gc.sp.splits;
+    da.partials = static_cast<const ArgPartial*>(gc.w.partials);
+    da.out_tokens = out_tokens;
+    da.out_num_accepted = out_num_accepted;
+    da.out_argmax = out_argmax;
+    da.out_match_mask = out_match_mask;
+    da.out_num_match = out_num_match;
+    return da;
+}
+
 int greedy_impl(const void* target_logits, long long target_row_stride,
                 const int* draft_tokens, int B, int k, int V, int dtype,
                 int* out_tokens, int* out_num_accepted, int* out_argmax,
                 unsigned long long* out_match_mask, int* out_num_match,
                 void* workspace, size_t workspace_bytes, void* hip_stream)
 {
-    if (!dtype_ok(dtype)) return SV_EDTYPE;
-    if (!target_logits || !draft_tokens || !out_tokens || !out_num_accepted) return SV_EINVAL;
-    if (B < 1 || k < 1 || k > SV_MAX_K || V < 1 || V > kMaxV || target_row_stride < V) return SV_EINVAL;
-    const long long rows = (long long)B * (k + 1);
-    if (!fits_grid(rows, V)) return SV_EINVAL;
-    Workspace w = layout(static_cast<char*>(workspace), B, rows, V);
-    if (!workspace || workspace_bytes < w.bytes) return SV_EWORKSPACE;
-    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    GreedyCall gc;
+    const int status = prepare_greedy(target_logits, target_row_stride, draft_tokens, B, k, V, dtype,
+                                      out_tokens, out_num_accepted, workspace, workspace_bytes, hip_stream, gc);
+    if (status != SV_OK) return status;
 
-    const StatsPlan sp = plan_stats(rows, V);
     StatsArgs sa;
     sa.target = target_logits;
     sa.t_stride = target_row_stride;
     sa.draft = nullptr;
     sa.d_stride = 0;
-    sa.n_target_rows = (int)rows;
-    sa.n_rows = (int)rows;
+    sa.n_target_rows = (int)gc.rows;
+    sa.n_rows = (int)gc.rows;
     sa.V = V;
-    sa.nvec = sp.nvec;
-    sa.splits = sp.splits;
-    sa.vec_per_split = sp.vec_per_split;
+    sa.nvec = gc.sp.nvec;
+    sa.splits = gc.sp.splits;
+    sa.vec_per_split = gc.sp.vec_per_split;
     sa.c = 0.f;
-    sa.partials = w.partials;
-    prof_begin(st);
-    if (launch_argmax_stats(dtype, vec_ok(target_logits, target_row_stride, dtype), sa, st) != hipSuccess)
-        return SV_EHIP;
-    prof_end(st);
+    sa.partials = gc.w.partials;
+    prof_begin(gc.st);
+    if (launch_argmax_stats(dtype, gc.vec, sa, gc.st) != hipSuccess) return SV_EHIP;
+    prof_end(gc.st);
 
-    DecideGreedyArgs da;
-    da.tokens = draft_tokens;
-    da.B = B;
-    da.k = k;
-    da.splits = sp.splits;
-    da.partials = static_cast<const ArgPartial*>(w.partials);
-    da.out_tokens = out_tokens;
-    da.out_num_accepted = out_num_accepted;
-    da.out_argmax = out_argmax;
-    da.out_match_mask = out_match_mask;
-    da.out_num_match = out_num_match;
-    if (launch_decide_greedy(da, st) != hipSuccess) return SV_EHIP;
+    const DecideGreedyArgs da = decide_greedy_args(draft_tokens, B, k, gc, out_tokens, out_num_accepted,
+                                                   out_argmax, out_match_mask, out_num_match);
+    if (launch_decide_greedy(da, gc.st) != hipSuccess) return SV_EHIP;
     return SV_OK;
 }
 
@@ -649,36 +678,20 @@ int spec_verify_greedy_lazy(const void* target_logits, long long target_row_stri
                             int* out_tokens, int* out_num_accepted,
                             void* workspace, size_t workspace_bytes, void* hip_stream)
 {
-    if (!dtype_ok(dtype)) return SV_EDTYPE;
-    if (!target_logits || !draft_tokens || !out_tokens || !out_num_accepted) return SV_EINVAL;
-    if (B < 1 || k < 1 || k > SV_MAX_K || V < 1 || V > kMaxV || target_row_stride < V) return SV_EINVAL;
-    const long long rows = (long long)B * (k + 1);
-    if (!fits_grid(rows, V)) return SV_EINVAL;
-    Workspace w = layout(static_cast<char*>(workspace), B, rows, V);
-    if (!workspace || workspace_bytes < w.bytes) return SV_EWORKSPACE;
-    hipStream_t st = static_cast<hipStream_t>(hip_stream);
-    const StatsPlan sp = plan_stats(rows, V);
+    GreedyCall gc;
+    const int status = prepare_greedy(target_logits, target_row_stride, draft_tokens, B, k, V, dtype,
+                                      out_tokens, out_num_accepted, workspace, workspace_bytes, hip_stream, gc);
+    if (status != SV_OK) return status;
 
-    DecideGreedyArgs da;
-    da.tokens = draft_tokens;
-    da.B = B;
-    da.k = k;
-    da.splits = sp.splits;
-    da.partials = static_cast<const ArgPartial*>(w.partials);
-    da.out_tokens = out_tokens;
-    da.out_num_accepted = out_num_accepted;
-    da.out_argmax = nullptr;
-    da.out_match_mask = nullptr;
-    da.out_num_match = nullptr;
-
-    LazyArgs l = lazy_args(target_logits, target_row_stride, nullptr, 0, B, k, V, sp, 0.f, w);
-    const bool vec = vec_ok(target_logits, target_row_stride, dtype);
+    const DecideGreedyArgs da =
+        decide_greedy_args(draft_tokens, B, k, gc, out_tokens, out_num_accepted, nullptr, nullptr, nullptr);
+    LazyArgs l = lazy_args(target_logits, target_row_stride, nullptr, 0, B, k, V, gc.sp, 0.f, gc.w);
     int bounds[16];
     const int nb = lazy_bounds(k, bounds);
     for (int p = 0; p + 1 < nb; ++p) {
-        lazy_window(l, w, bounds, p, B);
-        if (launch_lazy_stats(dtype, vec, false, lazy_grid(l, false), l, st) != hipSuccess) return SV_EHIP;
-        if (launch_lazy_decide_greedy(l, da, st) != hipSuccess) return SV_EHIP;
+        lazy_window(l, gc.w, bounds, p, B);
+        if (launch_lazy_stats(dtype, gc.vec, false, lazy_grid(l, false), l, gc.st) != hipSuccess) return SV_EHIP;
+        if (launch_lazy_decide_greedy(l, da, gc.st) != hipSuccess) return SV_EHIP;
     }
     return SV_OK;
 }
