@@ -5,10 +5,10 @@ A step is one spec_verify_sample call over workload 5: B = 512 sequences,
 k = 16 drafts, V = 128256, bf16 logits, T = 1.0 (the largest workload; all
 inputs already resident in HBM).  --workload / --mode measure the other
 workloads and entry points; workloads smaller than 1 GiB rotate over several
-input sets, call by call, so that no call reads its rows from the MALL.  One call runs the whole hot path: the
-vocabulary-streaming statistics pass over every target and draft row, the
-per-sequence decisions, and the residual/bonus draw.  The metric counts
-verified positions: B * (k+1) rows per call.
+input sets, call by call, so that no call reads its rows from the MALL.  One
+call runs the whole hot path: the vocabulary-streaming statistics pass over
+every target and draft row, the per-sequence decisions, and the residual or
+bonus draw.  The metric counts verified positions: B * (k+1) rows per call.
 
 Prints one JSON line.  Also reports, for the dominant kernel (the statistics
 pass), its average duration from HIP events recorded on the launch stream
