@@ -17,11 +17,11 @@ constexpr int kSeqPerBlock = kBlock / 64;
 // eight at a time (none past `splits`), so each batch's loads overlap.
 __device__ __forceinline__ int merge_arg(const ArgPartial* p, int splits)
 {
+    const unsigned long long* p8 = reinterpret_cast<const unsigned long long*>(p);
     float v = -INFINITY;
     int idx = INT32_MAX;
     for (int i0 = 0; i0 < splits; i0 += 8) {
         ArgPartial q[8];
-        const unsigned long long* p8 = reinterpret_cast<const unsigned long long*>(p);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {                  // one 8-byte load per partial
             q[u] = ArgPartial{-INFINITY, INT32_MAX};
@@ -47,8 +47,8 @@ __device__ __forceinline__ unsigned long long ballot64(bool pred)
 }
 
 // ---- sampling --------------------------------------------------------------
-// log2 p_i(x) = (z_x - m) * c - log2 s with c = log2(e)/T (log2_prob).  The ratio test is
-// taken in the log domain so that no probability underflows: accept iff
+// log2 p_i(x) = (z_x - m) * c - log2 s with c = log2(e)/T (log2_prob).  The
+// ratio test is taken in the log domain so that no probability underflows: accept iff
 // log q <= log p + log l (ratio >= 1, and q = 0) or u < exp2(log p + log l -
 // log q).  Lenience l (Cascade Speculative Drafting, review function) is 1
 // for the exact rule, where log l = 0 leaves the test unchanged.  With
