@@ -10,7 +10,10 @@
  *     positions, then differ: the accepted count is that prefix and the
  *     correction is the first maximum (the rule, Blog "The acceptance rule");
  *   - sampling with draft rows equal to the target rows: every ratio is 1, so
- *     every draft is accepted (u < 1), and the bonus is a token of p_k.
+ *     every draft is accepted (u < 1), and the bonus is a token of p_k;
+ *   - the greedy by-products (every row's first maximum, the match mask and
+ *     #Match) against its own scan, and the early-exit entry points against
+ *     the full-pass calls, bit for bit.
  * Exit status 0 when every check holds. */
 #include <stdio.h>
 #include <stdlib.h>
@@ -116,6 +119,53 @@ static void gpu_checks(void)
         for (int i = j + 1; i <= K; ++i) CHECK(out[b * (K + 1) + i] == -1, "greedy padding %d.%d", b, i);
     }
 
+    /* greedy by-products and early-exit greedy on the same inputs */
+    {
+        int *dv = NULL, *dcnt = NULL, *dout2 = NULL, *dna2 = NULL;
+        unsigned long long* dmask = NULL;
+        CHECK(hipMalloc((void**)&dv, sizeof(int) * rows) == hipSuccess, "hipMalloc");
+        CHECK(hipMalloc((void**)&dcnt, sizeof(int) * B) == hipSuccess, "hipMalloc");
+        CHECK(hipMalloc((void**)&dmask, sizeof(unsigned long long) * B) == hipSuccess, "hipMalloc");
+        CHECK(hipMalloc((void**)&dout2, sizeof(int) * B * (K + 1)) == hipSuccess, "hipMalloc");
+        CHECK(hipMalloc((void**)&dna2, sizeof(int) * B) == hipSuccess, "hipMalloc");
+        if (failures) return;
+        CHECK(spec_verify_greedy_ext(dz, V, dx, B, K, V, SV_F32, dout2, dna2, dv, dmask, dcnt, ws, wsb, NULL) ==
+                  SV_OK,
+              "greedy_ext call");
+        hipDeviceSynchronize();
+        int v[rows], cnt[B], out2[B * (K + 1)], na2[B];
+        unsigned long long mask[B];
+        hipMemcpy(v, dv, sizeof(v), hipMemcpyDeviceToHost);
+        hipMemcpy(cnt, dcnt, sizeof(cnt), hipMemcpyDeviceToHost);
+        hipMemcpy(mask, dmask, sizeof(mask), hipMemcpyDeviceToHost);
+        hipMemcpy(out2, dout2, sizeof(out2), hipMemcpyDeviceToHost);
+        hipMemcpy(na2, dna2, sizeof(na2), hipMemcpyDeviceToHost);
+        for (int b = 0; b < B; ++b) {
+            unsigned long long want = 0;
+            for (int i = 0; i <= K; ++i) {
+                const int amax = first_max(z + (size_t)(b * (K + 1) + i) * V, V);
+                CHECK(v[b * (K + 1) + i] == amax, "argmax of row %d.%d", b, i);
+                if (i < K && x[b * K + i] == amax) want |= 1ull << i;
+            }
+            CHECK(mask[b] == want, "match mask of sequence %d", b);
+            CHECK(cnt[b] == __builtin_popcountll(want), "#Match of sequence %d", b);
+            CHECK(na2[b] == na[b], "greedy_ext accepted count of sequence %d", b);
+            for (int i = 0; i <= K; ++i) CHECK(out2[b * (K + 1) + i] == out[b * (K + 1) + i], "greedy_ext token");
+        }
+        CHECK(spec_verify_greedy_lazy(dz, V, dx, B, K, V, SV_F32, dout2, dna2, ws, wsb, NULL) == SV_OK,
+              "greedy_lazy call");
+        hipDeviceSynchronize();
+        hipMemcpy(out2, dout2, sizeof(out2), hipMemcpyDeviceToHost);
+        hipMemcpy(na2, dna2, sizeof(na2), hipMemcpyDeviceToHost);
+        CHECK(memcmp(out2, out, sizeof(out)) == 0 && memcmp(na2, na, sizeof(na)) == 0,
+              "early-exit greedy equals greedy");
+        hipFree(dv);
+        hipFree(dcnt);
+        hipFree(dmask);
+        hipFree(dout2);
+        hipFree(dna2);
+    }
+
     /* sampling with the draft rows equal to the target rows: target rows
      * b*(K+1)+i, i < K, double as draft rows with stride (K+1)*V per sequence
      * is not expressible, so copy them into a [B][K][V] buffer */
@@ -144,6 +194,18 @@ static void gpu_checks(void)
         }
         const int bonus = out[b * (K + 1) + K];
         CHECK(bonus >= 0 && bonus < V, "bonus token of sequence %d in range", b);
+    }
+    /* early-exit sampling on the same inputs: the same tokens, bit for bit */
+    {
+        int out2[B * (K + 1)], na2[B];
+        CHECK(spec_verify_sample_lazy(dz, V, dy, V, dx, du, 1.0f, B, K, V, SV_F32, dout, dna, ws, wsb, NULL) ==
+                  SV_OK,
+              "sample_lazy call");
+        hipDeviceSynchronize();
+        hipMemcpy(out2, dout, sizeof(out2), hipMemcpyDeviceToHost);
+        hipMemcpy(na2, dna, sizeof(na2), hipMemcpyDeviceToHost);
+        CHECK(memcmp(out2, out, sizeof(out2)) == 0 && memcmp(na2, na, sizeof(na2)) == 0,
+              "early-exit sampling equals sampling");
     }
     hipFree(dz);
     hipFree(dy);
