@@ -556,6 +556,50 @@ def test_large_vocabulary(sv, V):
     assert not bad
 
 
+# 1100 x 16 x 131072 target and 1100 x 15 x 131072 draft logits: both
+# tensors hold more than 2^31 elements (4.6 and 4.3 GB in bf16). Target rows
+# of sequences 1024.. and draft rows of sequences 1093.. start past element
+# 2^31, so a 32-bit element offset anywhere in the path would read the wrong
+# rows there.
+HUGE = dict(B=1100, k=15, V=131072)
+HUGE_IDX = np.array([0, 1, 700, 1023, 1024, 1092, 1093, 1099])
+
+
+def huge_workload():
+    w = synthetic.chain(HUGE["B"], HUGE["k"], HUGE["V"], "bf16", var_target=3.0, var_noise=1.0,
+                        seed=2 ** 31, device=DEV)
+    assert w.target.numel() > 2 ** 31 and w.draft.numel() > 2 ** 31
+    return w
+
+
+def test_tensors_past_2_31_elements(sv):
+    """Sampling, greedy and early exit on logit tensors of more than 2^31
+    elements; the sequences on either side of element 2^31 are checked
+    against the oracle, early exit against the full pass on every sequence."""
+    w, idx = huge_workload(), HUGE_IDX
+    B, k = HUGE["B"], HUGE["k"]
+    ti = torch.as_tensor(idx, device=DEV)
+    toks, na, px, qx = run_sample(sv, w)
+    x, u = npi(w.tokens), npi(w.uniforms)
+    z, y = f32(w.target[ti]), f32(w.draft[ti])
+    rep = parity.check_sample(z, y, x[idx], u[idx], w.T, toks[idx], na[idx], eps=EPS, seq_ids=idx)
+    assert rep.ok(), (rep.summary(), rep.failures[:3])
+    assert parity.check_probs(z, y, x[idx], w.T, px[idx], qx[idx]) <= PROB_RTOL
+    lz = sv.sample_lazy(w.target, w.draft, w.tokens, w.uniforms, w.T)
+    g = torch.Generator(device=DEV).manual_seed(B)
+    xg = corrupt_after_argmax(w.target, k, g, 0.9)
+    gt, gn = sv.greedy(w.target, xg)
+    gl = sv.greedy_lazy(w.target, xg)
+    torch.cuda.synchronize()
+    assert np.array_equal(npi(lz[0]), toks) and np.array_equal(npi(lz[1]), na)
+    assert np.array_equal(npi(gl[0]), npi(gt)) and np.array_equal(npi(gl[1]), npi(gn))
+    bad, _, _ = parity.check_greedy(z, npi(xg)[idx], npi(gt)[idx], npi(gn)[idx])
+    assert not bad
+    print("past 2^31 elements:", rep.summary(), "greedy accepted", npi(gn)[idx])
+    del w, lz, gt, gn, gl
+    torch.cuda.empty_cache()
+
+
 def test_many_short_rows(sv):
     """4096 sequences of 300-token rows: far more sequences than workgroups
     per sequence, one slice per row."""

@@ -231,6 +231,31 @@ def test_truncated_full_size_sampled(sv):
     print(rep.summary())
 
 
+def test_truncated_past_2_31_elements(sv):
+    """Top-k 50 + top-p 0.8 on 1100 x 16 x 131072 target and 1100 x 15 x
+    131072 draft logits (bf16), each tensor past 2^31 elements: target rows of
+    sequences 1024.. and draft rows of sequences 1093.. start beyond element
+    2^31; the sequences on either side are checked against the oracle."""
+    B, k, V = 1100, 15, 131072
+    w = synthetic.chain(B, k, V, "bf16", var_target=3.0, var_noise=1.0, seed=2 ** 31 + 1, device=DEV)
+    assert w.target.numel() > 2 ** 31 and w.draft.numel() > 2 ** 31
+    idx = np.array([0, 1, 1023, 1024, 1092, 1093, 1099])
+    ti = torch.from_numpy(idx).to(DEV)
+    x = w.tokens.clone()
+    x[ti] = torch.from_numpy(truncated_drafts(f32(w.draft[ti]), w.T, 50, 0.8, 77)).to(DEV)
+    toks, na = sv.sample_truncated(w.target, w.draft, x, w.uniforms, w.T, 50, 0.8)
+    torch.cuda.synchronize()
+    toks, na = npi(toks), npi(na)
+    assert ((na >= 0) & (na <= k)).all()
+    rep = parity.check_sample_truncated(f32(w.target[ti]), f32(w.draft[ti]), npi(x)[idx],
+                                        npi(w.uniforms[ti]), w.T, 50, 0.8, toks[idx], na[idx],
+                                        eps=EPS)
+    assert rep.ok(), (rep.summary(), rep.failures[:3])
+    print(rep.summary())
+    del w, x
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 def test_truncated_many_equal_logits(sv, dtype):
     """16-bit rows with 65536 or more equal finite logits (the one-pass key
