@@ -21,6 +21,7 @@ overhead, which bounds the small, launch-bound workloads).
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -90,6 +91,10 @@ def main():
     ap.add_argument("--sets", type=int, default=0,
                     help="input sets rotated over, call by call (0: enough to span 1 GiB, so "
                          "that no call finds its rows in the 256 MB MALL)")
+    ap.add_argument("--vocab-shard", type=int, default=1, metavar="G",
+                    help="one GPU's share of a vocabulary-parallel LM head over G GPUs: every "
+                         "row holds ceil(V/G) logits (the exchange of row partials between "
+                         "the GPUs is not part of the measurement)")
     ap.add_argument("--lenience", type=float, default=2.0)
     ap.add_argument("--top-k", type=int, default=50)
     ap.add_argument("--top-p", type=float, default=0.8)
@@ -115,6 +120,9 @@ def main():
               "shard over GPUs with no exchange, so one GPU's rate is its share); run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
+    if args.vocab_shard < 1:
+        print("--vocab-shard must be at least 1", file=sys.stderr)
+        sys.exit(2)
     cand = args.mode in CAND_MODES
     cid = args.workload or (4 if cand else 5)
     if cand != (cid == 4):
@@ -129,6 +137,9 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     cfg0 = synthetic.WORKLOADS[cid]
+    v_full = cfg0.V
+    if args.vocab_shard > 1:
+        cfg0 = dataclasses.replace(cfg0, V=-(-v_full // args.vocab_shard))
     es = {"fp32": 4, "fp16": 2, "bf16": 2}[cfg0.dtype]
     if cand:
         stream_rows = cfg0.C * cfg0.R
@@ -140,7 +151,7 @@ def main():
     if sets > 1 and set_bytes * sets > (6 << 30):
         sets = max(1, (6 << 30) // set_bytes)
     t0 = time.perf_counter()
-    wall = synthetic.generate(cid, device=dev, B=cfg0.B * sets)
+    wall = synthetic.generate(cid, device=dev, B=cfg0.B * sets, V=cfg0.V)
     torch.cuda.synchronize()
     gen_s = time.perf_counter() - t0
     B = cfg0.B
@@ -225,6 +236,9 @@ def main():
             else:
                 sv.greedy(x.target, x.tokens, out_tokens=out_t, out_num_accepted=out_n, workspace=ws)
 
+    if args.vocab_shard > 1:
+        workload += f" (one of {args.vocab_shard} vocabulary shards of V={v_full})"
+
     # algorithmic bytes of the streaming kernel: every logit row read once
     # (V * element size) plus its 8-byte partial written
     bytes_per_row = V * es + 8
@@ -296,7 +310,8 @@ def main():
         kernel_ms = []
     k_avg_ms = statistics.fmean(kernel_ms) if kernel_ms else None
     achieved = stats_bytes / (k_avg_ms / 1e3) / 1e9 if kernel_ms else None
-    traffic = measured_traffic(stats_bytes) if (args.mode == "sample" and cid == 5) else None
+    traffic = measured_traffic(stats_bytes) \
+        if (args.mode == "sample" and cid == 5 and args.vocab_shard == 1) else None
 
     line = {
         "metric": METRIC,

@@ -341,6 +341,26 @@ def test_workload5_sample(sv, w5):
     print("workload 5 sample:", rep.summary())
 
 
+def test_workload5_vocabulary_shard(sv):
+    """Workload 5 as one of 8 vocabulary shards (V = 16032 per row, the shape
+    bench.py --vocab-shard 8 times): a sample of sequences against the oracle,
+    sampling and greedy."""
+    w = synthetic.generate(5, device=DEV, V=16032)
+    toks, na, px, qx = run_sample(sv, w)
+    idx = np.arange(0, 512, 4)
+    ti = torch.as_tensor(idx, device=DEV)
+    z, y = f32(w.target[ti]), f32(w.draft[ti])
+    x, u = npi(w.tokens), npi(w.uniforms)
+    rep = parity.check_sample(z, y, x[idx], u[idx], w.T, toks[idx], na[idx], eps=EPS, seq_ids=idx)
+    assert rep.ok(), (rep.summary(), rep.failures[:3])
+    assert parity.check_probs(z, y, x[idx], w.T, px[idx], qx[idx]) <= PROB_RTOL
+    gt, gn = sv.greedy(w.target, w.tokens)
+    torch.cuda.synchronize()
+    bad, _, _ = parity.check_greedy(z, x[idx], npi(gt)[idx], npi(gn)[idx])
+    assert not bad
+    print("workload 5, one of 8 vocabulary shards:", rep.summary())
+
+
 def test_workload5_greedy(sv, w5):
     toks, na = sv.greedy(w5.target, w5.tokens)
     torch.cuda.synchronize()
