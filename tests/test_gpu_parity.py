@@ -211,6 +211,22 @@ def test_sample_invalid_tokens(sv):
     assert_sample_parity(w, toks, na, px, qx)
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("u", [0.0, 1.0 - 2.0 ** -24])
+def test_sample_extreme_uniforms(sv, dtype, u):
+    """Uniforms at the ends of [0, 1): u = 0 accepts every draft of positive
+    probability and draws the first token of positive weight; the largest
+    float below 1 accepts only where p >= q (up to the counted tie band) and
+    draws from the end of the CDF."""
+    w = synthetic.chain(64, 6, 5000, dtype, var_noise=2.0, T=0.9, seed=31, device=DEV)
+    w.uniforms.fill_(u)
+    toks, na, px, qx = run_sample(sv, w)
+    rep = assert_sample_parity(w, toks, na, px, qx)
+    if u == 0.0:
+        assert (na == 6).all()
+    assert rep.rounds == 64
+
+
 def test_sample_low_temperature_matches_greedy(sv):
     """Low temperature: the sampling path reproduces the greedy path's tokens
     (the greedy collapse), both through the library."""
