@@ -100,6 +100,18 @@ def test_truncated_ragged_shapes(sv, dtype, B, k, V, top_k, top_p):
     check(sv, w, T, x, top_k, top_p)
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("u", [0.0, 1.0 - 2.0 ** -24])
+def test_truncated_extreme_uniforms(sv, dtype, u):
+    """Uniforms at the ends of [0, 1) on truncated rows: u = 0 draws the
+    lowest-index token of the kept set, the largest float below 1 the
+    highest; every draw must avoid the truncated-away tokens."""
+    w, T, x = workload(32, 4, 6000, dtype, 33, 50, 0.9)
+    w.uniforms.fill_(u)
+    rep, _, _ = check(sv, w, T, x, 50, 0.9)
+    assert rep.rounds == 32
+
+
 def test_truncated_many_rows_per_workgroup(sv):
     """More rows than workgroups, at a vocabulary whose last round of loads
     is partly past the row end (V = 152064): each workgroup streams several
