@@ -500,7 +500,8 @@ def test_tree_workload4_equals_flat(sv):
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
 @pytest.mark.parametrize("B,k,V", [(1, 1, 1), (5, 4, 1000), (9, 8, 12345), (3, 63, 300), (6, 16, 32000),
-                                   (2, 3, 100003)])   # the last: 24 slices per row, merged in three batches
+                                   (2, 3, 100003),    # 24 slices per row, merged in three batches
+                                   (129, 8, 9001)])   # 2193 short rows, one slice each
 @pytest.mark.parametrize("noise", [0.3, 3.0])
 def test_lazy_equals_full(sv, dtype, B, k, V, noise):
     w = synthetic.chain(B, k, V, dtype, var_noise=noise, T=0.8, seed=B * 11 + k + V, device=DEV)
