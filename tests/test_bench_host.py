@@ -1,0 +1,110 @@
+"""Host-side logic of bench.py, on the CPU: the refusals that need no GPU,
+the traffic figure from two rocprofv3 counter files, and the check that
+keeps a traffic figure from being reported for a changed kernel."""
+import csv
+import io
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def run_bench(*args):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args],
+                          capture_output=True, text=True, timeout=120)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = run_bench("--gpus", "2")
+    assert r.returncode == 2 and "one GPU only" in r.stderr
+
+
+def test_rank_environment_is_refused():
+    env = dict(os.environ, WORLD_SIZE="2")
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")], capture_output=True,
+                       text=True, timeout=120, env=env)
+    assert r.returncode == 2 and "one GPU only" in r.stderr
+
+
+@pytest.mark.parametrize("args,msg", [(["--vocab-shard", "0"], "at least 1"),
+                                      (["--mode", "tree", "--workload", "5"], "does not run"),
+                                      (["--mode", "sample", "--workload", "4"], "does not run")])
+def test_bad_arguments_are_refused(args, msg):
+    r = run_bench(*args)
+    assert r.returncode == 2 and msg in r.stderr
+
+
+def write_counters(path, counter, rows):
+    """A counter_collection.csv as rocprofv3 writes it: one row per dispatch."""
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for i, (name, kib) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": name, "Counter_Name": counter,
+                        "Counter_Value": kib})
+
+
+STATS = "void sv::k_softmax_stats<2, true>(sv::StatsArgs)"
+COPY = "void at::native::elementwise_kernel<...copy...>"
+
+
+def test_traffic_scales_each_counter_by_the_calibration_copy(tmp_path):
+    """A copy of 2^30 bytes reads 1.25x and writes 0.5x its size on these
+    counters: the kernel's figures are divided by the same factors."""
+    gib = 1 << 30
+    fetch = tmp_path / "fetch.csv"
+    write = tmp_path / "write.csv"
+    write_counters(fetch, "FETCH_SIZE", [(STATS, 1000.0), ("other", 5.0), (STATS, 1200.0),
+                                         (COPY, 1.25 * gib / 1024)])
+    write_counters(write, "WRITE_SIZE", [(STATS, 10.0), (STATS, 30.0), (COPY, 0.5 * gib / 1024)])
+    out = tmp_path / "traffic.json"
+    bench.traffic_from_pmc(str(fetch), str(write), out_path=str(out), copy_bytes=gib)
+    t = json.loads(out.read_text())
+    assert t["fetch_scale"] == pytest.approx(1.25) and t["write_scale"] == pytest.approx(0.5)
+    assert t["bytes_per_launch"] == pytest.approx(1100.0 * 1024 / 1.25 + 20.0 * 1024 / 0.5)
+    assert t["kernel"] == STATS and t["kernel_digest"] == bench.stats_kernel_digest()
+
+
+def test_traffic_needs_the_copy_last(tmp_path):
+    fetch = tmp_path / "fetch.csv"
+    write = tmp_path / "write.csv"
+    write_counters(fetch, "FETCH_SIZE", [(COPY, 1.0), (STATS, 2.0)])
+    write_counters(write, "WRITE_SIZE", [(COPY, 1.0), (STATS, 2.0)])
+    with pytest.raises(SystemExit):
+        bench.traffic_from_pmc(str(fetch), str(write), out_path=str(tmp_path / "t.json"))
+
+
+def test_traffic_is_reported_only_for_the_kernel_it_was_taken_on(tmp_path, monkeypatch):
+    f = tmp_path / "traffic.json"
+    f.write_text(json.dumps({"kernel_digest": bench.stats_kernel_digest(), "bytes_per_launch": 123.0}))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    assert bench.measured_traffic(0.0) == 123.0
+    f.write_text(json.dumps({"kernel_digest": "0" * 16, "bytes_per_launch": 123.0}))
+    assert bench.measured_traffic(0.0) is None
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "absent.json"))
+    assert bench.measured_traffic(0.0) is None
+
+
+def test_digest_follows_the_kernel_source(monkeypatch):
+    """Any change to a source the statistics kernel's counters depend on
+    changes the digest."""
+    d0 = bench.stats_kernel_digest()
+    src = os.path.join(ROOT, "draft_verification_verify_amd", "csrc", "sv_stats.hip")
+    real_open = open
+
+    def fake_open(path, mode="r", *a, **k):
+        fh = real_open(path, mode, *a, **k)
+        if os.path.abspath(path) == src and "b" in mode:
+            data = fh.read() + b"\n// changed\n"
+            fh.close()
+            return io.BytesIO(data)
+        return fh
+    monkeypatch.setattr("builtins.open", fake_open)
+    assert bench.stats_kernel_digest() != d0
