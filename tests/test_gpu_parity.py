@@ -285,11 +285,19 @@ def test_workload1_rounds(sv):
 
 
 def test_workload2(sv):
+    """Sampling on three input sets; greedy on the same target logits as an
+    extra check, with drafts that follow the argmax for a random prefix."""
     for s in range(3):
         w = synthetic.generate(2, device=DEV, set_index=s)
         toks, na, px, qx = run_sample(sv, w)
         rep = assert_sample_parity(w, toks, na, px, qx)
         print(f"workload 2 set {s}:", rep.summary())
+        g = torch.Generator(device=DEV).manual_seed(200 + s)
+        x = corrupt_after_argmax(w.target, w.tokens.shape[1], g, 0.8)
+        gt, gn = sv.greedy(w.target, x)
+        torch.cuda.synchronize()
+        bad, _, _ = parity.check_greedy(f32(w.target), npi(x), npi(gt), npi(gn))
+        assert not bad
 
 
 @pytest.fixture(scope="module")
