@@ -329,6 +329,23 @@ def test_workload3_deterministic(sv, w3):
     assert all(np.array_equal(u, v) for u, v in zip(g1, g2))
 
 
+@pytest.mark.parametrize("cid", [1, 2, 4, 5])
+def test_workloads_deterministic(sv, cid, request):
+    """Every workload's entry points called twice on the same stream give
+    bit-identical outputs (no floating-point atomics, fixed reduction
+    order)."""
+    w = request.getfixturevalue("w5") if cid == 5 else synthetic.generate(cid, device=DEV)
+    if cid == 4:
+        calls = [lambda: sv.greedy_candidates(w.target, w.tokens)]
+    else:
+        calls = [lambda: sv.sample(w.target, w.draft, w.tokens, w.uniforms, w.T, return_probs=True),
+                 lambda: sv.greedy(w.target, w.tokens)]
+    for f in calls:
+        a = [npi(t) for t in f()]
+        b = [npi(t) for t in f()]
+        assert all(np.array_equal(u, v) for u, v in zip(a, b))
+
+
 def test_workload4(sv):
     w = synthetic.generate(4, device=DEV)
     toks, A, best = sv.greedy_candidates(w.target, w.tokens)
