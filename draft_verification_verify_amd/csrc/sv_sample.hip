@@ -98,15 +98,39 @@ __device__ int chunk_pick(const SampleArgs& a, const char* zr, const char* yr, i
                           float* lds, int* ilds)
 {
     const int nfull = a.V >> 3;
+    const int vfull = min(c1, nfull);
     float R = 0.f;
     int last_tok = -1;
+    // a round's full vectors are loaded while the round before it is scanned
+    Raw<DT> nz, ny;
+    auto issue = [&](int r0) {
+        const int v = r0 + (int)threadIdx.x;
+        if (v < vfull) {
+            nz = load_raw<DT, VEC>(zr, v);
+            if (kind == 0) ny = load_raw<DT, VEC>(yr, v);
+        }
+    };
+    issue(c0);
     for (int r0 = c0; r0 < c1; r0 += kBlock) {
         const int v = r0 + (int)threadIdx.x;
+        const Raw<DT> cz = nz, cy = ny;
+        if (r0 + kBlock < c1) issue(r0 + kBlock);
         float w[kVec];
         float ts = 0.f;
         int firstpos = -1, lastpos = -1;
         if (v < c1) {
-            weights8<DT, VEC, MASK>(zr, yr, v, nfull, a.V, kind, a.c, d, w);
+            float ez[kVec], ey[kVec];
+            if (v < nfull) {
+                decode<DT>(cz, ez);
+                if (kind == 0) decode<DT>(cy, ey);
+            } else {
+                load_partial<DT>(zr, v, a.V - 8 * v, -INFINITY, ez);
+                if (kind == 0) load_partial<DT>(yr, v, a.V - 8 * v, -INFINITY, ey);
+            }
+#pragma unroll
+            for (int j = 0; j < kVec; ++j)
+                w[j] = weight_of<DT, MASK>(ez[j], kind == 0 ? ey[j] : 0.f, kind, a.c, stab_of(d.m_t, a.c),
+                                           stab_of(d.m_d, a.c), d);
 #pragma unroll
             for (int j = 0; j < kVec; ++j) {
                 ts += w[j];
