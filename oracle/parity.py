@@ -3,16 +3,23 @@
 TEST INFRASTRUCTURE ONLY (tests, smoke check).  Receives plain arrays; never
 imports or calls the GPU library.
 
-Greedy and candidate results must be bit-exact.  Sampling results must match
-exactly, except in rounds where the oracle's own decision lies within `eps`
-of its boundary, where float32 rounding on the GPU may legitimately go the
-other way:
-  - an acceptance decision with |u_i - min(1, p/q)| < eps: the rounds may
-    then diverge from that position on (the accepted drafts before it must
-    still agree);
+Greedy and candidate results must be bit-exact.  A sampling round must match
+the oracle's round exactly, except where one of the oracle's own decisions
+lies within `eps` of its boundary, where float32 rounding on the GPU may
+legitimately go the other way.  Such a decision excuses that decision alone,
+never the rest of the round:
+  - an acceptance with |u_i - min(1, p/q)| < eps taken the other way: the
+    oracle is run again on that sequence with u_i moved to the GPU's side
+    (0 if the GPU accepted, the largest float32 below 1 if it rejected), and
+    the GPU's round must match that run, by the same rules (so a later tie is
+    handled the same way);
   - the round's draw with u_k within eps of a boundary of the drawn token's
-    CDF interval: the GPU's token must then be a token of positive weight
-    whose own interval lies within eps of u_k.
+    CDF interval: the GPU's token must be a token of positive weight whose own
+    interval lies within eps of u_k;
+  - truncated rows whose top-p boundary lies within eps_trunc of top_p (the
+    oracle's trunc_margin): the GPU may keep the neighbouring set, so the
+    round must match, by the rules above, the oracle run at top_p or at
+    top_p -/+ eps_trunc, which keeps the neighbouring set of every such row.
 Such rounds are counted, not hidden.
 """
 from __future__ import annotations
@@ -24,6 +31,9 @@ import numpy as np
 from . import (draw_interval, greedy, greedy_candidates, greedy_matches, row_argmax, sample,
                sample_lenient, sample_truncated, token_probs, truncated_row)
 
+# the largest float32 below 1: a uniform that rejects every ratio below 1
+U_BELOW_ONE = float(np.nextafter(np.float32(1.0), np.float32(0.0)))
+
 
 @dataclasses.dataclass
 class SampleReport:
@@ -32,17 +42,85 @@ class SampleReport:
     tie_accept: int = 0
     tie_sample: int = 0
     tie_trunc: int = 0
+    forced: int = 0                    # tied acceptance decisions forced the GPU's way
     failures: list = dataclasses.field(default_factory=list)
     committed: int = 0
 
     def ok(self):
         return not self.failures
 
+    def count(self, kinds):
+        """Counts a passing round by the first band it passed through."""
+        if not kinds:
+            self.exact += 1
+        elif kinds[0] == "trunc":
+            self.tie_trunc += 1
+        elif kinds[0] == "accept":
+            self.tie_accept += 1
+        else:
+            self.tie_sample += 1
+        self.forced += kinds.count("accept")
+
     def summary(self):
         return (f"rounds={self.rounds} exact={self.exact} tie_accept={self.tie_accept} "
-                f"tie_sample={self.tie_sample} tie_trunc={self.tie_trunc} "
+                f"tie_sample={self.tie_sample} tie_trunc={self.tie_trunc} forced={self.forced} "
                 f"failures={len(self.failures)} "
                 f"mean_committed={self.committed / max(1, self.rounds):.4f}")
+
+
+def _draw_within(interval, j, token, u, eps, V):
+    """The drawn `token` at row j has positive weight and its CDF interval
+    lies within eps of u."""
+    if not 0 <= token < V:
+        return False
+    lo, hi, w = interval(j, int(token))
+    return w > 0 and lo - eps <= u <= hi + eps
+
+
+def check_round(run, interval, u, gt, gn, V, eps):
+    """One GPU round (tokens gt, accepted count gn) against the oracle on its
+    sequence.  run(u) -> (tokens, num_accepted, trace) runs the oracle with
+    the uniforms u [k+1]; interval(j, token) -> (lo, hi, weight) places a
+    token in the distribution the round draws from at row j.  Returns
+    (kinds, failure): the tie bands the round passed through, in order
+    ("accept", "sample"), and None or a description of the mismatch."""
+    ot, on, t = run(u)
+    on = int(on)
+    k = len(ot) - 1
+    if gn == on and (gt == ot).all():
+        return [], None
+    first = min(gn, on)
+    if not (0 <= gn <= k) or not (gt[:first] == ot[:first]).all():
+        return [], ("accepted prefix differs", gt.tolist(), ot.tolist())
+    if (gt[gn + 1:] != -1).any():
+        return [], ("padding", gt.tolist(), ot.tolist())
+    if gn != on:
+        if not (first < t.evaluated and t.accept_margin[first] < eps):
+            return [], (f"accepted length {gn} vs {on}", gt.tolist(), ot.tolist(),
+                        t.accept_margin[first] if first < t.evaluated else None)
+        gpu_accepts = gn > first
+        u2 = np.array(u, dtype=np.float32, copy=True)
+        u2[first] = 0.0 if gpu_accepts else U_BELOW_ONE
+        _, on2, _ = run(u2)
+        if (int(on2) > first) == gpu_accepts:
+            kinds, fail = check_round(run, interval, u2, gt, gn, V, eps)
+            return ["accept"] + kinds, fail
+        # no uniform takes the oracle the GPU's way: its ratio is exactly 1
+        # (the GPU rejected) or exactly 0 (the GPU accepted)
+        if gpu_accepts:
+            return [], (f"accepted at {first} where the oracle's ratio is 0", gt.tolist(), ot.tolist())
+        # the GPU's round ends at `first` with a draw from that row's residual
+        if _draw_within(interval, first, gt[first], float(u[k]), eps, V):
+            return ["accept"], None
+        return [], (f"draw at {first} after a forced rejection", gt.tolist(), float(u[k]))
+    if t.sample_margin < eps and _draw_within(interval, gn, gt[gn], float(u[k]), eps, V):
+        return ["sample"], None
+    return [], (f"drawn token {gt[gn]} vs {ot[gn]}", float(u[k]), t.sample_lo, t.sample_hi,
+                t.sample_margin)
+
+
+def _one(a, b):
+    return a[b:b + 1]
 
 
 def check_sample(z, y, x, u, T, gpu_tokens, gpu_nacc, eps=1e-5, report=None,
@@ -51,43 +129,37 @@ def check_sample(z, y, x, u, T, gpu_tokens, gpu_nacc, eps=1e-5, report=None,
     `lenience` (l >= 1) compares against the lenient rule instead."""
     rep = report or SampleReport()
     if lenience is None:
-        ot, on, tr = sample(z, y, x, u, T, traces=True)
+        ot, on, _ = sample(z, y, x, u, T, traces=True)
     else:
-        ot, on, tr = sample_lenient(z, y, x, u, T, lenience, traces=True)
+        ot, on, _ = sample_lenient(z, y, x, u, T, lenience, traces=True)
     B, k1 = ot.shape
     k = k1 - 1
+    V = z.shape[2]
     for b in range(B):
         sid = b if seq_ids is None else seq_ids[b]
         rep.rounds += 1
         rep.committed += int(gpu_nacc[b]) + 1
-        gt, gn = gpu_tokens[b], int(gpu_nacc[b])
+        gt, gn = np.asarray(gpu_tokens[b]), int(gpu_nacc[b])
         if gn == on[b] and (gt == ot[b]).all():
             rep.exact += 1
             continue
-        t = tr[b]
-        first = min(gn, int(on[b]))
-        if not (0 <= gn <= k) or not (gt[:first] == ot[b, :first]).all():
-            rep.failures.append((sid, "accepted prefix differs", gt.tolist(), ot[b].tolist()))
-            continue
-        if (gt[gn + 1:] != -1).any():
-            rep.failures.append((sid, "padding", gt.tolist(), ot[b].tolist()))
-            continue
-        if gn != on[b]:
-            if first < t.evaluated and t.accept_margin[first] < eps:
-                rep.tie_accept += 1
+
+        def run(uu, b=b):
+            if lenience is None:
+                a, n, tr = sample(_one(z, b), _one(y, b), _one(x, b), uu[None], T, traces=True)
             else:
-                rep.failures.append((sid, f"accepted length {gn} vs {on[b]}", gt.tolist(),
-                                     ot[b].tolist(), t.accept_margin[first]))
-            continue
-        j = gn
-        if t.sample_margin < eps:
-            lo, hi, w = draw_interval(z[b, j], y[b, j] if j < k else None, T, int(gt[j])) \
-                if 0 <= gt[j] < z.shape[2] else (0.0, 0.0, 0.0)
-            if w > 0 and lo - eps <= u[b, k] <= hi + eps:
-                rep.tie_sample += 1
-                continue
-        rep.failures.append((sid, f"drawn token {gt[j]} vs {ot[b, j]}", float(u[b, k]),
-                             t.sample_lo, t.sample_hi, t.sample_margin))
+                a, n, tr = sample_lenient(_one(z, b), _one(y, b), _one(x, b), uu[None], T, lenience,
+                                          traces=True)
+            return a[0], n[0], tr[0]
+
+        def interval(j, tok, b=b):
+            return draw_interval(z[b, j], y[b, j] if j < k else None, T, tok)
+
+        kinds, fail = check_round(run, interval, u[b], gt, gn, V, eps)
+        if fail is not None:
+            rep.failures.append((sid,) + tuple(fail))
+        else:
+            rep.count(kinds)
     return rep
 
 
@@ -164,46 +236,49 @@ def _truncated_interval(zrow, yrow, T, top_k, top_p, token):
 
 
 def check_sample_truncated(z, y, x, u, T, top_k, top_p, gpu_tokens, gpu_nacc, eps=1e-5,
-                           eps_trunc=1e-5, report=None) -> SampleReport:
+                           eps_trunc=1e-5, report=None, seq_ids=None) -> SampleReport:
     """As check_sample, on top-k / top-p truncated rows.  A round in which some
     row's top-p boundary lies within eps_trunc of top_p (the oracle's
-    trunc_margin) may keep a different set on the GPU: it is counted as
-    tie_trunc and checked for validity only (accepted drafts, padding)."""
+    trunc_margin) may keep a neighbouring set on the GPU: it must then match
+    the oracle run at top_p - eps_trunc or top_p + eps_trunc, which keeps the
+    neighbouring set of every such row (counted as tie_trunc)."""
     rep = report or SampleReport()
-    ot, on, tr, margin = sample_truncated(z, y, x, u, T, top_k, top_p, traces=True)
+    ot, on, _, margin = sample_truncated(z, y, x, u, T, top_k, top_p, traces=True)
     B, k1 = ot.shape
     k = k1 - 1
+    V = z.shape[2]
     for b in range(B):
+        sid = b if seq_ids is None else seq_ids[b]
         rep.rounds += 1
         rep.committed += int(gpu_nacc[b]) + 1
-        gt, gn = gpu_tokens[b], int(gpu_nacc[b])
+        gt, gn = np.asarray(gpu_tokens[b]), int(gpu_nacc[b])
         if gn == on[b] and (gt == ot[b]).all():
             rep.exact += 1
             continue
-        if not (0 <= gn <= k) or (gt[gn + 1:] != -1).any() or not (gt[:gn] == x[b, :gn]).all():
-            rep.failures.append((b, "invalid round", gt.tolist(), ot[b].tolist()))
-            continue
-        if margin[b] < eps_trunc:
-            rep.tie_trunc += 1
-            continue
-        t = tr[b]
-        first = min(gn, int(on[b]))
-        if gn != on[b]:
-            if first < t.evaluated and t.accept_margin[first] < eps:
-                rep.tie_accept += 1
-            else:
-                rep.failures.append((b, f"accepted length {gn} vs {on[b]}", gt.tolist(),
-                                     ot[b].tolist(), t.accept_margin[first]))
-            continue
-        j = gn
-        if t.sample_margin < eps and 0 <= gt[j] < z.shape[2]:
-            lo, hi, w = _truncated_interval(z[b, j], y[b, j] if j < k else None, T, top_k, top_p,
-                                            int(gt[j]))
-            if w > 0 and lo - eps <= u[b, k] <= hi + eps:
-                rep.tie_sample += 1
-                continue
-        rep.failures.append((b, f"drawn token {gt[j]} vs {ot[b, j]}", float(u[b, k]),
-                             t.sample_lo, t.sample_hi, t.sample_margin))
+
+        def against(tp, b=b):
+            def run(uu):
+                a, n, tr, _ = sample_truncated(_one(z, b), _one(y, b), _one(x, b), uu[None], T, top_k,
+                                               tp, traces=True)
+                return a[0], n[0], tr[0]
+
+            def interval(j, tok):
+                return _truncated_interval(z[b, j], y[b, j] if j < k else None, T, top_k, tp, tok)
+            return check_round(run, interval, u[b], gt, gn, V, eps)
+
+        kinds, fail = against(top_p)
+        if fail is not None and margin[b] < eps_trunc:
+            for tp in (top_p - eps_trunc, top_p + eps_trunc):
+                if not tp > 0.0:
+                    continue
+                kinds2, fail2 = against(tp)
+                if fail2 is None:
+                    kinds, fail = ["trunc"] + kinds2, None
+                    break
+        if fail is not None:
+            rep.failures.append((sid,) + tuple(fail))
+        else:
+            rep.count(kinds)
     return rep
 
 

@@ -224,22 +224,31 @@ def test_truncated_workload_subsets(sv, cid, top_k, top_p):
 
 def test_truncated_full_size_sampled(sv):
     """The 512 x 16 x 128256 bf16 workload at full size, top-p 0.8: every
-    sequence's round is run, and a sample of sequences is checked against the
-    oracle one by one."""
+    sequence's round is run and checked for the rule's invariants, and 64
+    evenly spaced sequences (their drafts drawn from the truncated q') are
+    checked against the oracle one by one."""
     w = synthetic.generate(5, device=DEV)
     B, k = w.tokens.shape
-    idx = np.array([0, 1, 137, 255, 256, 400, 511])
+    idx = np.arange(0, B, 8)
+    ti = torch.from_numpy(idx).to(DEV)
     x = w.tokens.clone()
-    x[torch.from_numpy(idx).to(DEV)] = torch.from_numpy(
-        truncated_drafts(f32(w.draft[idx]), w.T, 0, 0.8, 55)).to(DEV)
+    x[ti] = torch.from_numpy(truncated_drafts(f32(w.draft[ti]), w.T, 0, 0.8, 55)).to(DEV)
     toks, na = sv.sample_truncated(w.target, w.draft, x, w.uniforms, w.T, 0, 0.8)
     torch.cuda.synchronize()
-    toks, na = npi(toks), npi(na)
+    toks, na, xx = npi(toks), npi(na), npi(x)
     assert ((na >= 0) & (na <= k)).all()
-    rep = parity.check_sample_truncated(f32(w.target[idx]), f32(w.draft[idx]), npi(x)[idx],
-                                        npi(w.uniforms[idx]), w.T, 0, 0.8, toks[idx], na[idx],
-                                        eps=EPS)
+    for b in range(B):
+        assert (toks[b, :na[b]] == xx[b, :na[b]]).all()
+        assert 0 <= toks[b, na[b]] < w.target.shape[2]
+        assert (toks[b, na[b] + 1:] == -1).all()
+    rep = parity.SampleReport()
+    for c0 in range(0, idx.size, 16):
+        sel = idx[c0:c0 + 16]
+        ts = torch.from_numpy(sel).to(DEV)
+        parity.check_sample_truncated(f32(w.target[ts]), f32(w.draft[ts]), xx[sel], npi(w.uniforms)[sel],
+                                      w.T, 0, 0.8, toks[sel], na[sel], eps=EPS, report=rep, seq_ids=sel)
     assert rep.ok(), (rep.summary(), rep.failures[:3])
+    assert rep.rounds == 64
     print(rep.summary())
 
 
