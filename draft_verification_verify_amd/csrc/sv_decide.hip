@@ -307,7 +307,9 @@ __global__ __launch_bounds__(kBlock) void k_lazy_decide_greedy(LazyArgs l, Decid
 // ties to the lowest c (Ouroboros 3.4.3, "Selecting the accepted tokens").
 // Flat layout: row (c, i) of sequence b is row (b*C + c)*R + i.  Tree layout
 // (Ouroboros Figure 3, each node scored once): the row is b*N + cand_rows[b][c][i];
-// an index outside [0, N) never matches and gives the correction -1.
+// an index outside [0, N) is never read: cand_argmax gives -1 for it, which the
+// decision counts as a mismatch whatever the token (a -1 padding token included),
+// and -1 is also its correction.
 __device__ __forceinline__ int cand_argmax(const DecideCandArgs& a, int b, int c, int i)
 {
     long long row;
@@ -335,7 +337,7 @@ __global__ __launch_bounds__(kBlock) void k_decide_candidates(DecideCandArgs a)
     if (active) {
         amax = cand_argmax(a, b, c, i);
         tok = a.cand[((long long)b * C + c) * L + i];
-        miss = tok != amax;
+        miss = amax < 0 || tok != amax;
     }
     const unsigned long long mm = ballot64(miss);
     int acc = 0;

@@ -556,8 +556,9 @@ int oracle_greedy_tree(const float* nodes, long long row_stride, int N, const in
             int a = L;
             for (int i = 0; i < L; ++i) {
                 int r = rows[c * R + i];
-                int v = (r >= 0 && r < N) ? argmax_row(seq + (long long)r * row_stride, V) : -1;
-                if (cb[c * L + i] != v) { a = i; break; }
+                /* a row outside [0, N) scores nothing: a mismatch whatever the token */
+                if (r < 0 || r >= N) { a = i; break; }
+                if (cb[c * L + i] != argmax_row(seq + (long long)r * row_stride, V)) { a = i; break; }
             }
             if (a > best_a) { best_a = a; best_c = c; }
         }

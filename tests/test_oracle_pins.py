@@ -620,6 +620,26 @@ def test_tree_invalid_row_index_never_matches():
     assert (t[:, 2] == -1).all()                        # correction from an invalid row
 
 
+def test_tree_padding_slots_never_match():
+    """A tree builder that pads a short candidate with token -1 at row -1 gets
+    nothing from the padding: a row outside [0, N) scores nothing, so its
+    position is a mismatch whatever the token (the -1 token included)."""
+    rng = np.random.default_rng(19)
+    B, C, L, V, N = 40, 3, 4, 11, 7
+    nodes = rng.normal(size=(B, N, V)).astype(np.float32)
+    rows = rng.integers(0, N, (B, C, L)).astype(np.int32)
+    ref = np.argmax(np.take_along_axis(nodes[:, None], rows[..., None].astype(np.int64), axis=2), axis=3)
+    cand = ref.astype(np.int32)
+    cand[:, 0, 1] = (ref[:, 0, 1] + 1) % V              # candidate 0 runs 1 token
+    cand[:, 1, 2:] = -1                                 # candidate 1: 2 real tokens, then padding
+    rows[:, 1, 2:] = -1
+    cand[:, 2, 0] = (ref[:, 2, 0] + 1) % V              # candidate 2 runs 0 tokens
+    t, a, best = oracle.greedy_tree(nodes, cand, rows)
+    assert (a == 2).all() and (best == 1).all()
+    np.testing.assert_array_equal(t[:, :2], cand[:, 1, :2])
+    assert (t[:, 2:] == -1).all()                       # correction from the padded row, then padding
+
+
 # ---------------------------------------------------------------------------
 # Consistent top-k / top-p truncation of p and q (Ouroboros samples with
 # top-p 0.8; the blog requires processors to be applied to target and draft
