@@ -68,10 +68,14 @@ def lib():
         L.spec_verify_sample_truncated.argtypes = [P, LL, P, LL, P, P, F, I, F, I, I, I, I, P, P, P,
                                                    P, P, SZ, P]
         L.spec_verify_sample_truncated.restype = I
-        L.spec_verify_profile_begin.argtypes = [I, I]
-        L.spec_verify_profile_begin.restype = I
-        L.spec_verify_profile_end.argtypes = [P, I]
-        L.spec_verify_profile_end.restype = I
+        L.spec_verify_sample_timed.argtypes = [P, LL, P, LL, P, P, F, F, I, F, I, I, I, I, P, P, P, P,
+                                               P, SZ, P, P, P]
+        L.spec_verify_sample_timed.restype = I
+        L.spec_verify_greedy_timed.argtypes = [P, LL, P, I, I, I, I, P, P, P, P, P, P, SZ, P, P, P]
+        L.spec_verify_greedy_timed.restype = I
+        L.spec_verify_candidates_timed.argtypes = [P, LL, P, P, I, I, I, I, I, I, I, P, P, P, P, P, SZ,
+                                                   P, P, P]
+        L.spec_verify_candidates_timed.restype = I
         _lib = L
     return _lib
 
@@ -81,7 +85,8 @@ EXPORTED = (
     "spec_verify_greedy", "spec_verify_sample", "spec_verify_greedy_candidates",
     "spec_verify_greedy_ext", "spec_verify_sample_lenient", "spec_verify_greedy_candidates_ext",
     "spec_verify_greedy_tree", "spec_verify_sample_lazy", "spec_verify_greedy_lazy",
-    "spec_verify_profile_begin", "spec_verify_profile_end", "spec_verify_sample_truncated",
+    "spec_verify_sample_truncated", "spec_verify_sample_timed", "spec_verify_greedy_timed",
+    "spec_verify_candidates_timed",
 )
 
 
@@ -173,40 +178,88 @@ def _logits(t, name: str, ndim: int, lead: Optional[tuple] = None, dtype=None) -
     return rs
 
 
-def _out(t, name: str, shape: tuple, dtype: torch.dtype, device: torch.device):
-    """A caller's output tensor, checked, or a new one."""
+def _new(shape, dtype, device, owned: list):
+    """A tensor the binding allocates for this call (listed in `owned`)."""
+    t = torch.empty(shape, dtype=dtype, device=device)
+    owned.append(t)
+    return t
+
+
+def _out(t, name: str, shape: tuple, dtype: torch.dtype, device: torch.device, owned: list):
+    """A caller's output tensor, checked, or a new one (listed in `owned`)."""
     if t is None:
-        return torch.empty(shape, dtype=dtype, device=device)
+        return _new(shape, dtype, device, owned)
     return _need(t, name, shape, dtype, device)
 
 
-def _workspace(ws, B, rows_per_seq, V, dtype, device):
-    """(tensor, size in bytes): the caller's contiguous device buffer, or a new one."""
+def _workspace(ws, B, rows_per_seq, V, dtype, device, owned: list):
+    """(tensor, size in bytes): the caller's contiguous device buffer, or a new
+    one (listed in `owned`)."""
     if ws is None:
         need = workspace_bytes(B, rows_per_seq, V, dtype)
-        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+        ws = _new(max(need, 1), torch.uint8, device, owned)
     elif not isinstance(ws, torch.Tensor) or ws.device != device or not ws.is_contiguous():
         raise ValueError(f"workspace must be a contiguous tensor on {device}; got {_describe(ws)}")
     return ws, ws.numel() * ws.element_size()
 
 
+def _launched(stream, owned: list):
+    """After a launch on a caller's `stream`: the tensors the binding allocated
+    came from the current stream's pool, and the kernels on `stream` may still
+    use them after this call returns (the workspace is even released at once).
+    Recording them on `stream` keeps the caching allocator from handing their
+    memory to other work before that stream's work is done."""
+    if stream is None or not owned:
+        return
+    if stream == torch.cuda.current_stream(stream.device):
+        return
+    for t in owned:
+        t.record_stream(stream)
+
+
+def _event_handles(events, stream, device):
+    """The raw HIP handles of a caller's pair of torch.cuda.Event objects
+    (enable_timing=True), which the library records around the streaming
+    kernel.  torch creates an event's handle at its first record, so an event
+    never recorded is recorded once on the call's stream first."""
+    if events is None:
+        return None
+    if len(events) != 2 or not all(isinstance(e, torch.cuda.Event) for e in events):
+        raise ValueError("events must be a pair of torch.cuda.Event objects")
+    st = stream if stream is not None else torch.cuda.current_stream(device)
+    out = []
+    for e in events:
+        if not e.cuda_event:
+            e.record(st)
+        out.append(e.cuda_event)
+    return out
+
+
 def greedy(target: torch.Tensor, draft_tokens: torch.Tensor, *, out_tokens=None,
-           out_num_accepted=None, workspace=None, stream=None):
+           out_num_accepted=None, workspace=None, stream=None, events=None):
     """Greedy verification.  target [B, k+1, V] (fp32/fp16/bf16, rows contiguous
     along V), draft_tokens [B, k] int32.  Returns (tokens [B, k+1], num_accepted [B])."""
     ts = _logits(target, "target", 3)
     B, k1, V = target.shape
     k = k1 - 1
     dev = target.device
+    owned = []
     _need(draft_tokens, "draft_tokens", (B, k), torch.int32, dev)
-    out_tokens = _out(out_tokens, "out_tokens", (B, k + 1), torch.int32, dev)
-    out_num_accepted = _out(out_num_accepted, "out_num_accepted", (B,), torch.int32, dev)
+    out_tokens = _out(out_tokens, "out_tokens", (B, k + 1), torch.int32, dev, owned)
+    out_num_accepted = _out(out_num_accepted, "out_num_accepted", (B,), torch.int32, dev, owned)
     if B == 0:
         return out_tokens, out_num_accepted
-    ws, wsb = _workspace(workspace, B, k + 1, V, target.dtype, dev)
-    st = lib().spec_verify_greedy(_ptr(target), ts, _ptr(draft_tokens), B, k, V,
-                                  _sv_dtype(target.dtype), _ptr(out_tokens), _ptr(out_num_accepted),
-                                  _ptr(ws), wsb, _stream(stream, dev))
+    ws, wsb = _workspace(workspace, B, k + 1, V, target.dtype, dev, owned)
+    ev = _event_handles(events, stream, dev)
+    if ev is None:
+        st = lib().spec_verify_greedy(_ptr(target), ts, _ptr(draft_tokens), B, k, V,
+                                      _sv_dtype(target.dtype), _ptr(out_tokens), _ptr(out_num_accepted),
+                                      _ptr(ws), wsb, _stream(stream, dev))
+    else:
+        st = lib().spec_verify_greedy_timed(_ptr(target), ts, _ptr(draft_tokens), B, k, V,
+                                            _sv_dtype(target.dtype), _ptr(out_tokens), _ptr(out_num_accepted),
+                                            None, None, None, _ptr(ws), wsb, _stream(stream, dev), *ev)
+    _launched(stream, owned)
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_greedy")
     return out_tokens, out_num_accepted
@@ -230,28 +283,38 @@ def _sample_inputs(target, draft, draft_tokens, uniforms):
 def sample(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
            uniforms: torch.Tensor, temperature: float, *, return_probs: bool = False,
            out_tokens=None, out_num_accepted=None, out_p_x=None, out_q_x=None,
-           workspace=None, stream=None):
+           workspace=None, stream=None, events=None):
     """Sampling verification.  target [B, k+1, V], draft [B, k, V] (same dtype),
     draft_tokens [B, k] int32, uniforms [B, k+1] float32 in [0, 1).
     Returns (tokens [B, k+1], num_accepted [B]) and, with return_probs,
     also (p_x [B, k], q_x [B, k])."""
     B, k, V, ts, ds = _sample_inputs(target, draft, draft_tokens, uniforms)
     dev = target.device
-    out_tokens = _out(out_tokens, "out_tokens", (B, k + 1), torch.int32, dev)
-    out_num_accepted = _out(out_num_accepted, "out_num_accepted", (B,), torch.int32, dev)
+    owned = []
+    out_tokens = _out(out_tokens, "out_tokens", (B, k + 1), torch.int32, dev, owned)
+    out_num_accepted = _out(out_num_accepted, "out_num_accepted", (B,), torch.int32, dev, owned)
     if return_probs:
-        out_p_x = _out(out_p_x, "out_p_x", (B, k), torch.float32, dev)
-        out_q_x = _out(out_q_x, "out_q_x", (B, k), torch.float32, dev)
+        out_p_x = _out(out_p_x, "out_p_x", (B, k), torch.float32, dev, owned)
+        out_q_x = _out(out_q_x, "out_q_x", (B, k), torch.float32, dev, owned)
     else:
         out_p_x = None if out_p_x is None else _need(out_p_x, "out_p_x", (B, k), torch.float32, dev)
         out_q_x = None if out_q_x is None else _need(out_q_x, "out_q_x", (B, k), torch.float32, dev)
     if B == 0:
         return (out_tokens, out_num_accepted, out_p_x, out_q_x) if return_probs else (out_tokens, out_num_accepted)
-    ws, wsb = _workspace(workspace, B, 2 * k + 1, V, target.dtype, dev)
-    st = lib().spec_verify_sample(_ptr(target), ts, _ptr(draft), ds,
-                                  _ptr(draft_tokens), _ptr(uniforms), float(temperature), B, k, V,
-                                  _sv_dtype(target.dtype), _ptr(out_tokens), _ptr(out_num_accepted),
-                                  _ptr(out_p_x), _ptr(out_q_x), _ptr(ws), wsb, _stream(stream, dev))
+    ws, wsb = _workspace(workspace, B, 2 * k + 1, V, target.dtype, dev, owned)
+    ev = _event_handles(events, stream, dev)
+    if ev is None:
+        st = lib().spec_verify_sample(_ptr(target), ts, _ptr(draft), ds,
+                                      _ptr(draft_tokens), _ptr(uniforms), float(temperature), B, k, V,
+                                      _sv_dtype(target.dtype), _ptr(out_tokens), _ptr(out_num_accepted),
+                                      _ptr(out_p_x), _ptr(out_q_x), _ptr(ws), wsb, _stream(stream, dev))
+    else:
+        st = lib().spec_verify_sample_timed(_ptr(target), ts, _ptr(draft), ds, _ptr(draft_tokens),
+                                            _ptr(uniforms), float(temperature), 1.0, 0, 1.0, B, k, V,
+                                            _sv_dtype(target.dtype), _ptr(out_tokens), _ptr(out_num_accepted),
+                                            _ptr(out_p_x), _ptr(out_q_x), _ptr(ws), wsb, _stream(stream, dev),
+                                            *ev)
+    _launched(stream, owned)
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_sample")
     if return_probs:
@@ -259,7 +322,7 @@ def sample(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor
     return out_tokens, out_num_accepted
 
 
-def greedy_ext(target: torch.Tensor, draft_tokens: torch.Tensor, *, workspace=None, stream=None):
+def greedy_ext(target: torch.Tensor, draft_tokens: torch.Tensor, *, workspace=None, stream=None, events=None):
     """Greedy verification plus its phrase-harvesting by-products.  Returns
     (tokens [B, k+1], num_accepted [B], target_argmax [B, k+1],
     match_mask [B] (int64 bit pattern of the uint64 mask), num_match [B])."""
@@ -267,18 +330,27 @@ def greedy_ext(target: torch.Tensor, draft_tokens: torch.Tensor, *, workspace=No
     B, k1, V = target.shape
     k = k1 - 1
     dev = target.device
+    owned = []
     _need(draft_tokens, "draft_tokens", (B, k), torch.int32, dev)
-    out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
-    out_na = torch.empty((B,), dtype=torch.int32, device=dev)
-    out_v = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
-    out_mask = torch.empty((B,), dtype=torch.int64, device=dev)
-    out_cnt = torch.empty((B,), dtype=torch.int32, device=dev)
+    out_tokens = _new((B, k + 1), torch.int32, dev, owned)
+    out_na = _new((B,), torch.int32, dev, owned)
+    out_v = _new((B, k + 1), torch.int32, dev, owned)
+    out_mask = _new((B,), torch.int64, dev, owned)
+    out_cnt = _new((B,), torch.int32, dev, owned)
     if B == 0:
         return out_tokens, out_na, out_v, out_mask, out_cnt
-    ws, wsb = _workspace(workspace, B, k + 1, V, target.dtype, dev)
-    st = lib().spec_verify_greedy_ext(_ptr(target), ts, _ptr(draft_tokens), B, k, V,
-                                      _sv_dtype(target.dtype), _ptr(out_tokens), _ptr(out_na), _ptr(out_v),
-                                      _ptr(out_mask), _ptr(out_cnt), _ptr(ws), wsb, _stream(stream, dev))
+    ws, wsb = _workspace(workspace, B, k + 1, V, target.dtype, dev, owned)
+    ev = _event_handles(events, stream, dev)
+    if ev is None:
+        st = lib().spec_verify_greedy_ext(_ptr(target), ts, _ptr(draft_tokens), B, k, V,
+                                          _sv_dtype(target.dtype), _ptr(out_tokens), _ptr(out_na), _ptr(out_v),
+                                          _ptr(out_mask), _ptr(out_cnt), _ptr(ws), wsb, _stream(stream, dev))
+    else:
+        st = lib().spec_verify_greedy_timed(_ptr(target), ts, _ptr(draft_tokens), B, k, V,
+                                            _sv_dtype(target.dtype), _ptr(out_tokens), _ptr(out_na),
+                                            _ptr(out_v), _ptr(out_mask), _ptr(out_cnt), _ptr(ws), wsb,
+                                            _stream(stream, dev), *ev)
+    _launched(stream, owned)
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_greedy_ext")
     return out_tokens, out_na, out_v, out_mask, out_cnt
@@ -286,22 +358,32 @@ def greedy_ext(target: torch.Tensor, draft_tokens: torch.Tensor, *, workspace=No
 
 def sample_lenient(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
                    uniforms: torch.Tensor, temperature: float, lenience: float, *,
-                   return_probs: bool = False, workspace=None, stream=None):
+                   return_probs: bool = False, workspace=None, stream=None, events=None):
     """Sampling verification with lenience l >= 1 (l = 1: `sample`)."""
     B, k, V, ts, ds = _sample_inputs(target, draft, draft_tokens, uniforms)
     dev = target.device
-    out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
-    out_na = torch.empty((B,), dtype=torch.int32, device=dev)
-    out_p_x = torch.empty((B, k), dtype=torch.float32, device=dev) if return_probs else None
-    out_q_x = torch.empty((B, k), dtype=torch.float32, device=dev) if return_probs else None
+    owned = []
+    out_tokens = _new((B, k + 1), torch.int32, dev, owned)
+    out_na = _new((B,), torch.int32, dev, owned)
+    out_p_x = _new((B, k), torch.float32, dev, owned) if return_probs else None
+    out_q_x = _new((B, k), torch.float32, dev, owned) if return_probs else None
     if B == 0:
         return (out_tokens, out_na, out_p_x, out_q_x) if return_probs else (out_tokens, out_na)
-    ws, wsb = _workspace(workspace, B, 2 * k + 1, V, target.dtype, dev)
-    st = lib().spec_verify_sample_lenient(_ptr(target), ts, _ptr(draft), ds, _ptr(draft_tokens),
-                                          _ptr(uniforms), float(temperature), float(lenience), B, k, V,
-                                          _sv_dtype(target.dtype), _ptr(out_tokens), _ptr(out_na),
-                                          _ptr(out_p_x), _ptr(out_q_x), _ptr(ws), wsb,
-                                          _stream(stream, dev))
+    ws, wsb = _workspace(workspace, B, 2 * k + 1, V, target.dtype, dev, owned)
+    ev = _event_handles(events, stream, dev)
+    if ev is None:
+        st = lib().spec_verify_sample_lenient(_ptr(target), ts, _ptr(draft), ds, _ptr(draft_tokens),
+                                              _ptr(uniforms), float(temperature), float(lenience), B, k, V,
+                                              _sv_dtype(target.dtype), _ptr(out_tokens), _ptr(out_na),
+                                              _ptr(out_p_x), _ptr(out_q_x), _ptr(ws), wsb,
+                                              _stream(stream, dev))
+    else:
+        st = lib().spec_verify_sample_timed(_ptr(target), ts, _ptr(draft), ds, _ptr(draft_tokens),
+                                            _ptr(uniforms), float(temperature), float(lenience), 0, 1.0, B, k,
+                                            V, _sv_dtype(target.dtype), _ptr(out_tokens), _ptr(out_na),
+                                            _ptr(out_p_x), _ptr(out_q_x), _ptr(ws), wsb, _stream(stream, dev),
+                                            *ev)
+    _launched(stream, owned)
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_sample_lenient")
     if return_probs:
@@ -311,23 +393,33 @@ def sample_lenient(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torc
 
 def sample_truncated(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
                      uniforms: torch.Tensor, temperature: float, top_k: int = 0, top_p: float = 1.0,
-                     *, return_probs: bool = False, workspace=None, stream=None):
+                     *, return_probs: bool = False, workspace=None, stream=None, events=None):
     """Sampling verification on top-k / top-p truncated target and draft rows
     (top_k = 0 and top_p >= 1 switch the steps off)."""
     B, k, V, ts, ds = _sample_inputs(target, draft, draft_tokens, uniforms)
     dev = target.device
-    out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
-    out_na = torch.empty((B,), dtype=torch.int32, device=dev)
-    out_p_x = torch.empty((B, k), dtype=torch.float32, device=dev) if return_probs else None
-    out_q_x = torch.empty((B, k), dtype=torch.float32, device=dev) if return_probs else None
+    owned = []
+    out_tokens = _new((B, k + 1), torch.int32, dev, owned)
+    out_na = _new((B,), torch.int32, dev, owned)
+    out_p_x = _new((B, k), torch.float32, dev, owned) if return_probs else None
+    out_q_x = _new((B, k), torch.float32, dev, owned) if return_probs else None
     if B == 0:
         return (out_tokens, out_na, out_p_x, out_q_x) if return_probs else (out_tokens, out_na)
-    ws, wsb = _workspace(workspace, B, 2 * k + 1, V, target.dtype, dev)
-    st = lib().spec_verify_sample_truncated(_ptr(target), ts, _ptr(draft), ds, _ptr(draft_tokens),
-                                            _ptr(uniforms), float(temperature), int(top_k),
-                                            float(top_p), B, k, V, _sv_dtype(target.dtype),
-                                            _ptr(out_tokens), _ptr(out_na), _ptr(out_p_x),
-                                            _ptr(out_q_x), _ptr(ws), wsb, _stream(stream, dev))
+    ws, wsb = _workspace(workspace, B, 2 * k + 1, V, target.dtype, dev, owned)
+    ev = _event_handles(events, stream, dev)
+    if ev is None:
+        st = lib().spec_verify_sample_truncated(_ptr(target), ts, _ptr(draft), ds, _ptr(draft_tokens),
+                                                _ptr(uniforms), float(temperature), int(top_k),
+                                                float(top_p), B, k, V, _sv_dtype(target.dtype),
+                                                _ptr(out_tokens), _ptr(out_na), _ptr(out_p_x),
+                                                _ptr(out_q_x), _ptr(ws), wsb, _stream(stream, dev))
+    else:
+        st = lib().spec_verify_sample_timed(_ptr(target), ts, _ptr(draft), ds, _ptr(draft_tokens),
+                                            _ptr(uniforms), float(temperature), 1.0, int(top_k), float(top_p),
+                                            B, k, V, _sv_dtype(target.dtype), _ptr(out_tokens), _ptr(out_na),
+                                            _ptr(out_p_x), _ptr(out_q_x), _ptr(ws), wsb, _stream(stream, dev),
+                                            *ev)
+    _launched(stream, owned)
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_sample_truncated")
     if return_probs:
@@ -348,22 +440,31 @@ def _candidate_inputs(target, cand_tokens):
 
 
 def greedy_candidates_ext(target: torch.Tensor, cand_tokens: torch.Tensor, *, workspace=None,
-                          stream=None):
+                          stream=None, events=None):
     """Multi-candidate greedy verification plus the argmax of every scored row.
     Returns (tokens [B, L+1], A [B], best [B], target_argmax [B, C, R])."""
     B, C, R, V, L, ts = _candidate_inputs(target, cand_tokens)
     dev = target.device
-    out_tokens = torch.empty((B, L + 1), dtype=torch.int32, device=dev)
-    out_na = torch.empty((B,), dtype=torch.int32, device=dev)
-    out_best = torch.empty((B,), dtype=torch.int32, device=dev)
-    out_v = torch.empty((B, C, R), dtype=torch.int32, device=dev)
+    owned = []
+    out_tokens = _new((B, L + 1), torch.int32, dev, owned)
+    out_na = _new((B,), torch.int32, dev, owned)
+    out_best = _new((B,), torch.int32, dev, owned)
+    out_v = _new((B, C, R), torch.int32, dev, owned)
     if B == 0:
         return out_tokens, out_na, out_best, out_v
-    ws, wsb = _workspace(workspace, B, C * R, V, target.dtype, dev)
-    st = lib().spec_verify_greedy_candidates_ext(_ptr(target), ts, _ptr(cand_tokens),
-                                                 B, C, L, R, V, _sv_dtype(target.dtype), _ptr(out_tokens),
-                                                 _ptr(out_na), _ptr(out_best), _ptr(out_v), _ptr(ws),
-                                                 wsb, _stream(stream, dev))
+    ws, wsb = _workspace(workspace, B, C * R, V, target.dtype, dev, owned)
+    ev = _event_handles(events, stream, dev)
+    if ev is None:
+        st = lib().spec_verify_greedy_candidates_ext(_ptr(target), ts, _ptr(cand_tokens),
+                                                     B, C, L, R, V, _sv_dtype(target.dtype), _ptr(out_tokens),
+                                                     _ptr(out_na), _ptr(out_best), _ptr(out_v), _ptr(ws),
+                                                     wsb, _stream(stream, dev))
+    else:
+        st = lib().spec_verify_candidates_timed(_ptr(target), ts, _ptr(cand_tokens), None, 0, B, C, L, R, V,
+                                                _sv_dtype(target.dtype), _ptr(out_tokens), _ptr(out_na),
+                                                _ptr(out_best), _ptr(out_v), _ptr(ws), wsb, _stream(stream,
+                                                dev), *ev)
+    _launched(stream, owned)
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_greedy_candidates_ext")
     return out_tokens, out_na, out_best, out_v
@@ -376,15 +477,17 @@ def sample_lazy(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.T
     the rule looks at.  Returns (tokens [B, k+1], num_accepted [B])."""
     B, k, V, ts, ds = _sample_inputs(target, draft, draft_tokens, uniforms)
     dev = target.device
-    out_tokens = _out(out_tokens, "out_tokens", (B, k + 1), torch.int32, dev)
-    out_num_accepted = _out(out_num_accepted, "out_num_accepted", (B,), torch.int32, dev)
+    owned = []
+    out_tokens = _out(out_tokens, "out_tokens", (B, k + 1), torch.int32, dev, owned)
+    out_num_accepted = _out(out_num_accepted, "out_num_accepted", (B,), torch.int32, dev, owned)
     if B == 0:
         return out_tokens, out_num_accepted
-    ws, wsb = _workspace(workspace, B, 2 * k + 1, V, target.dtype, dev)
+    ws, wsb = _workspace(workspace, B, 2 * k + 1, V, target.dtype, dev, owned)
     st = lib().spec_verify_sample_lazy(_ptr(target), ts, _ptr(draft), ds, _ptr(draft_tokens),
                                        _ptr(uniforms), float(temperature), B, k, V,
                                        _sv_dtype(target.dtype), _ptr(out_tokens), _ptr(out_num_accepted),
                                        _ptr(ws), wsb, _stream(stream, dev))
+    _launched(stream, owned)
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_sample_lazy")
     return out_tokens, out_num_accepted
@@ -398,28 +501,31 @@ def greedy_lazy(target: torch.Tensor, draft_tokens: torch.Tensor, *, out_tokens=
     B, k1, V = target.shape
     k = k1 - 1
     dev = target.device
+    owned = []
     _need(draft_tokens, "draft_tokens", (B, k), torch.int32, dev)
-    out_tokens = _out(out_tokens, "out_tokens", (B, k + 1), torch.int32, dev)
-    out_num_accepted = _out(out_num_accepted, "out_num_accepted", (B,), torch.int32, dev)
+    out_tokens = _out(out_tokens, "out_tokens", (B, k + 1), torch.int32, dev, owned)
+    out_num_accepted = _out(out_num_accepted, "out_num_accepted", (B,), torch.int32, dev, owned)
     if B == 0:
         return out_tokens, out_num_accepted
-    ws, wsb = _workspace(workspace, B, k + 1, V, target.dtype, dev)
+    ws, wsb = _workspace(workspace, B, k + 1, V, target.dtype, dev, owned)
     st = lib().spec_verify_greedy_lazy(_ptr(target), ts, _ptr(draft_tokens), B, k, V,
                                        _sv_dtype(target.dtype), _ptr(out_tokens), _ptr(out_num_accepted),
                                        _ptr(ws), wsb, _stream(stream, dev))
+    _launched(stream, owned)
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_greedy_lazy")
     return out_tokens, out_num_accepted
 
 
 def greedy_tree(nodes: torch.Tensor, cand_tokens: torch.Tensor, cand_rows: torch.Tensor, *,
-                workspace=None, stream=None):
+                workspace=None, stream=None, events=None):
     """Multi-candidate greedy verification over a token tree.  nodes [B, N, V],
     cand_tokens [B, C, L] int32, cand_rows [B, C, R] int32 (node row per
     candidate position).  Returns (tokens [B, L+1], A [B], best [B])."""
     ns = _logits(nodes, "nodes", 3)
     B, N, V = nodes.shape
     dev = nodes.device
+    owned = []
     for t, name in ((cand_tokens, "cand_tokens"), (cand_rows, "cand_rows")):
         if not isinstance(t, torch.Tensor) or t.dim() != 3 or t.shape[0] != B:
             raise ValueError(f"{name} must be a [B, C, *] int32 tensor; got {_describe(t)}")
@@ -427,55 +533,57 @@ def greedy_tree(nodes: torch.Tensor, cand_tokens: torch.Tensor, cand_rows: torch
     R = cand_rows.shape[2]
     _need(cand_tokens, "cand_tokens", (B, C, L), torch.int32, dev)
     _need(cand_rows, "cand_rows", (B, C, R), torch.int32, dev)
-    out_tokens = torch.empty((B, L + 1), dtype=torch.int32, device=dev)
-    out_na = torch.empty((B,), dtype=torch.int32, device=dev)
-    out_best = torch.empty((B,), dtype=torch.int32, device=dev)
+    out_tokens = _new((B, L + 1), torch.int32, dev, owned)
+    out_na = _new((B,), torch.int32, dev, owned)
+    out_best = _new((B,), torch.int32, dev, owned)
     if B == 0:
         return out_tokens, out_na, out_best
-    ws, wsb = _workspace(workspace, B, N, V, nodes.dtype, dev)
-    st = lib().spec_verify_greedy_tree(_ptr(nodes), ns, N, _ptr(cand_tokens),
-                                       _ptr(cand_rows), B, C, L, R, V, _sv_dtype(nodes.dtype),
-                                       _ptr(out_tokens), _ptr(out_na), _ptr(out_best), _ptr(ws),
-                                       wsb, _stream(stream, dev))
+    ws, wsb = _workspace(workspace, B, N, V, nodes.dtype, dev, owned)
+    ev = _event_handles(events, stream, dev)
+    if ev is None:
+        st = lib().spec_verify_greedy_tree(_ptr(nodes), ns, N, _ptr(cand_tokens),
+                                           _ptr(cand_rows), B, C, L, R, V, _sv_dtype(nodes.dtype),
+                                           _ptr(out_tokens), _ptr(out_na), _ptr(out_best), _ptr(ws),
+                                           wsb, _stream(stream, dev))
+    else:
+        st = lib().spec_verify_candidates_timed(_ptr(nodes), ns, _ptr(cand_tokens), _ptr(cand_rows), N, B, C,
+                                                L, R, V, _sv_dtype(nodes.dtype), _ptr(out_tokens),
+                                                _ptr(out_na), _ptr(out_best), None, _ptr(ws), wsb,
+                                                _stream(stream, dev), *ev)
+    _launched(stream, owned)
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_greedy_tree")
     return out_tokens, out_na, out_best
 
 
 def greedy_candidates(target: torch.Tensor, cand_tokens: torch.Tensor, *, out_tokens=None,
-                      out_num_accepted=None, out_best=None, workspace=None, stream=None):
+                      out_num_accepted=None, out_best=None, workspace=None, stream=None, events=None):
     """Multi-candidate greedy verification.  target [B, C, R, V] with R = L or L+1,
     cand_tokens [B, C, L] int32.  Returns (tokens [B, L+1], A [B], best [B])."""
     B, C, R, V, L, ts = _candidate_inputs(target, cand_tokens)
     dev = target.device
-    out_tokens = _out(out_tokens, "out_tokens", (B, L + 1), torch.int32, dev)
-    out_num_accepted = _out(out_num_accepted, "out_num_accepted", (B,), torch.int32, dev)
-    out_best = _out(out_best, "out_best", (B,), torch.int32, dev)
+    owned = []
+    out_tokens = _out(out_tokens, "out_tokens", (B, L + 1), torch.int32, dev, owned)
+    out_num_accepted = _out(out_num_accepted, "out_num_accepted", (B,), torch.int32, dev, owned)
+    out_best = _out(out_best, "out_best", (B,), torch.int32, dev, owned)
     if B == 0:
         return out_tokens, out_num_accepted, out_best
-    ws, wsb = _workspace(workspace, B, C * R, V, target.dtype, dev)
-    st = lib().spec_verify_greedy_candidates(_ptr(target), ts, _ptr(cand_tokens),
-                                             B, C, L, R, V, _sv_dtype(target.dtype), _ptr(out_tokens),
-                                             _ptr(out_num_accepted), _ptr(out_best), _ptr(ws),
-                                             wsb, _stream(stream, dev))
+    ws, wsb = _workspace(workspace, B, C * R, V, target.dtype, dev, owned)
+    ev = _event_handles(events, stream, dev)
+    if ev is None:
+        st = lib().spec_verify_greedy_candidates(_ptr(target), ts, _ptr(cand_tokens),
+                                                 B, C, L, R, V, _sv_dtype(target.dtype), _ptr(out_tokens),
+                                                 _ptr(out_num_accepted), _ptr(out_best), _ptr(ws),
+                                                 wsb, _stream(stream, dev))
+    else:
+        st = lib().spec_verify_candidates_timed(_ptr(target), ts, _ptr(cand_tokens), None, 0, B, C, L, R, V,
+                                                _sv_dtype(target.dtype), _ptr(out_tokens),
+                                                _ptr(out_num_accepted), _ptr(out_best), None, _ptr(ws), wsb,
+                                                _stream(stream, dev), *ev)
+    _launched(stream, owned)
     if st != SV_OK:
         raise SpecVerifyError(st, "spec_verify_greedy_candidates")
     return out_tokens, out_num_accepted, out_best
-
-
-def profile_begin(max_calls: int, every: int = 1):
-    """Record the statistics kernel's duration on every `every`-th call."""
-    st = lib().spec_verify_profile_begin(int(max_calls), int(every))
-    if st != SV_OK:
-        raise SpecVerifyError(st, "spec_verify_profile_begin")
-
-
-def profile_end(max_out: int = 1 << 16):
-    buf = (ctypes.c_float * max_out)()
-    n = lib().spec_verify_profile_end(buf, max_out)
-    if n < 0:
-        raise RuntimeError(f"spec_verify_profile_end failed: {n}")
-    return [buf[i] for i in range(min(n, max_out))]
 
 
 lib()

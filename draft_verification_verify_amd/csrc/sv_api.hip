@@ -134,33 +134,17 @@ bool vec_ok(const void* p, long long stride, int dt)
     return ((uintptr_t)p % 16 == 0) && ((stride * es) % 16 == 0);
 }
 
-// ---- measurement aid: events around the statistics kernel of every
-// `every`-th call, up to max_calls recorded calls ----------------------------
-struct Profile {
-    hipEvent_t* ev = nullptr;
-    int max_calls = 0;
-    int every = 1;
-    int count = 0;
-    long long seen = 0;
-    bool armed = false;
-    bool on = false;
+// ---- measurement variants: the caller's two events (hipEvent_t, or null for
+// none) recorded on the call's stream right before and right after the
+// vocabulary-streaming kernel.  The library keeps no state of its own.
+struct Timing {
+    hipEvent_t begin = nullptr;
+    hipEvent_t end = nullptr;
 };
-Profile g_prof;
 
-// A call is counted only when both of its events were recorded.
-void prof_begin(hipStream_t st)
+hipError_t mark(hipEvent_t ev, hipStream_t st)
 {
-    if (!g_prof.on) return;
-    g_prof.armed = (g_prof.seen % g_prof.every == 0) && g_prof.count < g_prof.max_calls;
-    g_prof.seen++;
-    if (g_prof.armed && hipEventRecord(g_prof.ev[2 * g_prof.count], st) != hipSuccess) g_prof.armed = false;
-}
-
-void prof_end(hipStream_t st)
-{
-    if (!g_prof.armed) return;
-    if (hipEventRecord(g_prof.ev[2 * g_prof.count + 1], st) == hipSuccess) g_prof.count++;
-    g_prof.armed = false;
+    return ev ? hipEventRecord(ev, st) : hipSuccess;
 }
 
 // What every greedy entry point checks and derives before its first launch.
@@ -211,7 +195,7 @@ int greedy_impl(const void* target_logits, long long target_row_stride,
                 const int* draft_tokens, int B, int k, int V, int dtype,
                 int* out_tokens, int* out_num_accepted, int* out_argmax,
                 unsigned long long* out_match_mask, int* out_num_match,
-                void* workspace, size_t workspace_bytes, void* hip_stream)
+                void* workspace, size_t workspace_bytes, void* hip_stream, const Timing& tm = Timing())
 {
     GreedyCall gc;
     const int status = prepare_greedy(target_logits, target_row_stride, draft_tokens, B, k, V, dtype,
@@ -231,9 +215,9 @@ int greedy_impl(const void* target_logits, long long target_row_stride,
     sa.vec_per_split = gc.sp.vec_per_split;
     sa.c = 0.f;
     sa.partials = gc.w.partials;
-    prof_begin(gc.st);
+    if (mark(tm.begin, gc.st) != hipSuccess) return SV_EHIP;
     if (launch_argmax_stats(dtype, gc.vec, sa, gc.st) != hipSuccess) return SV_EHIP;
-    prof_end(gc.st);
+    if (mark(tm.end, gc.st) != hipSuccess) return SV_EHIP;
 
     const DecideGreedyArgs da = decide_greedy_args(draft_tokens, B, k, gc, out_tokens, out_num_accepted,
                                                    out_argmax, out_match_mask, out_num_match);
@@ -350,7 +334,7 @@ int sample_impl(const void* target_logits, long long target_row_stride,
                 float lenience, int top_k, float top_p, int B, int k, int V, int dtype,
                 int* out_tokens, int* out_num_accepted,
                 float* out_p_x, float* out_q_x,
-                void* workspace, size_t workspace_bytes, void* hip_stream)
+                void* workspace, size_t workspace_bytes, void* hip_stream, const Timing& tm = Timing())
 {
     SampleCall sc;
     const int status = prepare_sample(target_logits, target_row_stride, draft_logits, draft_row_stride,
@@ -359,7 +343,7 @@ int sample_impl(const void* target_logits, long long target_row_stride,
                                       hip_stream, sc);
     if (status != SV_OK) return status;
 
-    prof_begin(sc.st);
+    if (mark(tm.begin, sc.st) != hipSuccess) return SV_EHIP;
     if (sc.trunc) {
         TruncArgs ta;
         ta.target = target_logits;
@@ -390,7 +374,7 @@ int sample_impl(const void* target_logits, long long target_row_stride,
         sa.partials = sc.w.partials;
         if (launch_softmax_stats(dtype, sc.vec, sa, sc.st) != hipSuccess) return SV_EHIP;
     }
-    prof_end(sc.st);
+    if (mark(tm.end, sc.st) != hipSuccess) return SV_EHIP;
 
     const DecideSampleArgs da =
         decide_sample_args(target_logits, target_row_stride, draft_logits, draft_row_stride, draft_tokens,
@@ -406,7 +390,7 @@ int candidates_impl(const void* target_logits, long long row_stride,
                     const int* cand_tokens, const int* cand_rows, int N, int B, int C, int L, int R,
                     int V, int dtype, int* out_tokens, int* out_num_accepted,
                     int* out_best_candidate, int* out_argmax,
-                    void* workspace, size_t workspace_bytes, void* hip_stream)
+                    void* workspace, size_t workspace_bytes, void* hip_stream, const Timing& tm = Timing())
 {
     if (!dtype_ok(dtype)) return SV_EDTYPE;
     if (!target_logits || !cand_tokens || !out_tokens || !out_num_accepted || !out_best_candidate)
@@ -435,10 +419,10 @@ int candidates_impl(const void* target_logits, long long row_stride,
     sa.vec_per_split = sp.vec_per_split;
     sa.c = 0.f;
     sa.partials = w.partials;
-    prof_begin(st);
+    if (mark(tm.begin, st) != hipSuccess) return SV_EHIP;
     if (launch_argmax_stats(dtype, vec_ok(target_logits, row_stride, dtype), sa, st) != hipSuccess)
         return SV_EHIP;
-    prof_end(st);
+    if (mark(tm.end, st) != hipSuccess) return SV_EHIP;
 
     DecideCandArgs da;
     da.cand = cand_tokens;
@@ -701,42 +685,55 @@ int spec_verify_greedy_lazy(const void* target_logits, long long target_row_stri
     return SV_OK;
 }
 
-int spec_verify_profile_begin(int max_calls, int every)
+int spec_verify_sample_timed(const void* target_logits, long long target_row_stride,
+                             const void* draft_logits, long long draft_row_stride,
+                             const int* draft_tokens, const float* uniforms, float temperature,
+                             float lenience, int top_k, float top_p, int B, int k, int V, int dtype,
+                             int* out_tokens, int* out_num_accepted, float* out_p_x, float* out_q_x,
+                             void* workspace, size_t workspace_bytes, void* hip_stream,
+                             void* event_begin, void* event_end)
 {
-    if (max_calls < 1 || every < 1 || g_prof.on) return SV_EINVAL;
-    g_prof.ev = static_cast<hipEvent_t*>(calloc((size_t)2 * max_calls, sizeof(hipEvent_t)));
-    if (!g_prof.ev) return SV_EINVAL;
-    for (int i = 0; i < 2 * max_calls; ++i) {
-        if (hipEventCreate(&g_prof.ev[i]) != hipSuccess) {
-            for (int j = 0; j < i; ++j) (void)hipEventDestroy(g_prof.ev[j]);
-            free(g_prof.ev);
-            g_prof.ev = nullptr;
-            return SV_EHIP;
-        }
-    }
-    g_prof.max_calls = max_calls;
-    g_prof.every = every;
-    g_prof.count = 0;
-    g_prof.seen = 0;
-    g_prof.armed = false;
-    g_prof.on = true;
-    return SV_OK;
+    if (!event_begin || !event_end) return SV_EINVAL;
+    Timing tm;
+    tm.begin = static_cast<hipEvent_t>(event_begin);
+    tm.end = static_cast<hipEvent_t>(event_end);
+    return sample_impl(target_logits, target_row_stride, draft_logits, draft_row_stride,
+                       draft_tokens, uniforms, temperature, lenience, top_k, top_p, B, k, V, dtype,
+                       out_tokens, out_num_accepted, out_p_x, out_q_x, workspace, workspace_bytes,
+                       hip_stream, tm);
 }
 
-int spec_verify_profile_end(float* out_ms, int max_out)
+int spec_verify_greedy_timed(const void* target_logits, long long target_row_stride,
+                             const int* draft_tokens, int B, int k, int V, int dtype,
+                             int* out_tokens, int* out_num_accepted, int* out_target_argmax,
+                             unsigned long long* out_match_mask, int* out_num_match,
+                             void* workspace, size_t workspace_bytes, void* hip_stream,
+                             void* event_begin, void* event_end)
 {
-    if (!g_prof.on) return -1;
-    int rc = g_prof.count;
-    for (int i = 0; i < g_prof.count; ++i) {
-        if (hipEventSynchronize(g_prof.ev[2 * i + 1]) != hipSuccess) { rc = -2; break; }
-        float ms = 0.f;
-        if (hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]) != hipSuccess) { rc = -2; break; }
-        if (out_ms && i < max_out) out_ms[i] = ms;
-    }
-    for (int i = 0; i < 2 * g_prof.max_calls; ++i) (void)hipEventDestroy(g_prof.ev[i]);
-    free(g_prof.ev);
-    g_prof = Profile();
-    return rc;
+    if (!event_begin || !event_end) return SV_EINVAL;
+    Timing tm;
+    tm.begin = static_cast<hipEvent_t>(event_begin);
+    tm.end = static_cast<hipEvent_t>(event_end);
+    return greedy_impl(target_logits, target_row_stride, draft_tokens, B, k, V, dtype, out_tokens,
+                       out_num_accepted, out_target_argmax, out_match_mask, out_num_match,
+                       workspace, workspace_bytes, hip_stream, tm);
+}
+
+int spec_verify_candidates_timed(const void* target_logits, long long row_stride,
+                                 const int* cand_tokens, const int* cand_rows, int N,
+                                 int B, int C, int L, int R, int V, int dtype,
+                                 int* out_tokens, int* out_num_accepted, int* out_best_candidate,
+                                 int* out_target_argmax,
+                                 void* workspace, size_t workspace_bytes, void* hip_stream,
+                                 void* event_begin, void* event_end)
+{
+    if (!event_begin || !event_end) return SV_EINVAL;
+    Timing tm;
+    tm.begin = static_cast<hipEvent_t>(event_begin);
+    tm.end = static_cast<hipEvent_t>(event_end);
+    return candidates_impl(target_logits, row_stride, cand_tokens, cand_rows, N, B, C, L, R, V, dtype,
+                           out_tokens, out_num_accepted, out_best_candidate, out_target_argmax,
+                           workspace, workspace_bytes, hip_stream, tm);
 }
 
 }  // extern "C"

@@ -253,18 +253,52 @@ int spec_verify_greedy_lazy(const void* target_logits, long long target_row_stri
                             int* out_tokens, int* out_num_accepted,
                             void* workspace, size_t workspace_bytes, void* hip_stream);
 
-/* Measurement aid (not thread-safe; for a single profiling thread).  While
- * enabled, every `every`-th verification call (the first, then every
- * `every` calls), up to `max_calls` of them, records a pair of HIP events on
- * its stream around its vocabulary-streaming statistics kernel (the kernel
- * that reads every logit).  Each pair costs a few microseconds of queue time.
- * spec_verify_profile_end waits for the recorded events, writes up to
- * `max_out` durations in milliseconds, frees the events, disables recording
- * and returns the number of recorded calls (or a negative value: -1 if not
- * enabled, -2 on a HIP error).  spec_verify_profile_begin returns a status
- * (SV_EINVAL for max_calls < 1, every < 1 or when already enabled). */
-int spec_verify_profile_begin(int max_calls, int every);
-int spec_verify_profile_end(float* out_ms, int max_out);
+/* Measurement variants, for callers that time the vocabulary-streaming kernel
+ * (the one launch that reads every logit) inside their own timed region.
+ * Each does exactly what the entry points named below do, and in addition
+ * records the caller's two HIP events on `hip_stream`: `event_begin` right
+ * before that kernel and `event_end` right after it.  The events are
+ * hipEvent_t handles created and owned by the caller (passed as void*); the
+ * library keeps no state, so concurrent calls on different streams with
+ * their own events and workspaces do not interact.  Both events are
+ * required (SV_EINVAL if either is NULL, nothing launched); a failed event
+ * record returns SV_EHIP.  An event pair costs a few microseconds of queue
+ * time on the stream.
+ *  - spec_verify_sample_timed: spec_verify_sample_truncated's arguments plus
+ *    spec_verify_sample_lenient's lenience (>= 1; 1 is the exact rule);
+ *    top_k = 0 and top_p >= 1 with lenience 1 is spec_verify_sample.  The
+ *    timed kernel is the statistics pass, or the truncation pass when top-k
+ *    or top-p is on.
+ *  - spec_verify_greedy_timed: spec_verify_greedy_ext's arguments, whose
+ *    three by-product outputs may each be NULL (all NULL: spec_verify_greedy).
+ *  - spec_verify_candidates_timed: spec_verify_greedy_tree's arguments, where
+ *    cand_rows = NULL selects the flat layout of
+ *    spec_verify_greedy_candidates (N is then ignored), plus
+ *    spec_verify_greedy_candidates_ext's out_target_argmax (NULL = none):
+ *    [B][C][R], the argmax of the row that scores each candidate position
+ *    (-1 where a tree row is outside [0, N)). */
+int spec_verify_sample_timed(const void* target_logits, long long target_row_stride,
+                             const void* draft_logits, long long draft_row_stride,
+                             const int* draft_tokens, const float* uniforms, float temperature,
+                             float lenience, int top_k, float top_p, int B, int k, int V, int dtype,
+                             int* out_tokens, int* out_num_accepted, float* out_p_x, float* out_q_x,
+                             void* workspace, size_t workspace_bytes, void* hip_stream,
+                             void* event_begin, void* event_end);
+
+int spec_verify_greedy_timed(const void* target_logits, long long target_row_stride,
+                             const int* draft_tokens, int B, int k, int V, int dtype,
+                             int* out_tokens, int* out_num_accepted, int* out_target_argmax,
+                             unsigned long long* out_match_mask, int* out_num_match,
+                             void* workspace, size_t workspace_bytes, void* hip_stream,
+                             void* event_begin, void* event_end);
+
+int spec_verify_candidates_timed(const void* target_logits, long long row_stride,
+                                 const int* cand_tokens, const int* cand_rows, int N,
+                                 int B, int C, int L, int R, int V, int dtype,
+                                 int* out_tokens, int* out_num_accepted, int* out_best_candidate,
+                                 int* out_target_argmax,
+                                 void* workspace, size_t workspace_bytes, void* hip_stream,
+                                 void* event_begin, void* event_end);
 
 #ifdef __cplusplus
 }

@@ -20,7 +20,8 @@ The second parameter of N(., .) is read as a variance.  "Spike": +8 added to
 one uniformly chosen index per target row; the draft rows inherit it through
 "draft = target + noise".  Draft tokens are sampled from softmax(draft / T) of
 the dtype-rounded draft logits (Gumbel-max: the index of the largest
-draft/T + Gumbel noise), and the same tokens serve greedy mode.  Uniforms are
+draft/T + Gumbel noise), and the same tokens serve greedy mode; for greedy
+drafting, greedy_drafts() gives the draft's own argmax at each position.  Uniforms are
 24-bit floats k / 2^24 in [0, 1 - 2^-24]: one per draft position plus one for
 the round's single sampling step.
 
@@ -115,6 +116,19 @@ def gumbel_max_sample(logits: torch.Tensor, T: float, gen: torch.Generator,
         g = -torch.log(-torch.log(uu))
         out[r0:r1] = torch.argmax(logits[r0:r1].to(torch.float32) / T + g, dim=1).to(torch.int32)
     return out
+
+
+def greedy_drafts(draft: torch.Tensor, chunk_rows: int = 1024) -> torch.Tensor:
+    """Greedy drafting (a draft model decoding at temperature 0): at every
+    position the draft's own most likely token, the argmax of its logits.
+    draft: [B, k, V]; returns int32 [B, k].  This plays the proposer's part."""
+    B, k, V = draft.shape
+    flat = draft.reshape(B * k, V)
+    out = torch.empty(B * k, dtype=torch.int32, device=draft.device)
+    for r0 in range(0, B * k, chunk_rows):
+        r1 = min(B * k, r0 + chunk_rows)
+        out[r0:r1] = torch.argmax(flat[r0:r1].to(torch.float32), dim=1).to(torch.int32)
+    return out.reshape(B, k)
 
 
 @dataclasses.dataclass

@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_header_symbols_exported(sv):
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     assert sorted(sv.EXPORTED) == names
     for n in names:
         assert hasattr(sv.lib(), n), n
@@ -173,11 +173,21 @@ def test_candidates_rejects_bad_arguments(sv):
     assert (out == SENT).all()
 
 
-def test_profile_api_without_calls(sv):
+def test_timed_variants_need_both_events(sv):
+    """The measurement variants take the caller's two events; a missing one is
+    SV_EINVAL before anything else happens (no HIP call, outputs untouched)."""
     L = sv.lib()
-    assert L.spec_verify_profile_begin(0, 1) == sv.SV_EINVAL
-    assert L.spec_verify_profile_begin(4, 0) == sv.SV_EINVAL
-    assert L.spec_verify_profile_end(None, 0) == -1      # not enabled
+    f = ctypes.c_void_p(64)
+    out = np.full(8, SENT, np.int32)
+    po = out.ctypes.data_as(ctypes.c_void_p)
+    for e0, e1 in ((None, f), (f, None), (None, None)):
+        assert L.spec_verify_sample_timed(f, 100, f, 100, f, f, 1.0, 1.0, 0, 1.0, 2, 3, 100, 2, po, po,
+                                          None, None, f, 1 << 30, None, e0, e1) == sv.SV_EINVAL
+        assert L.spec_verify_greedy_timed(f, 100, f, 2, 3, 100, 2, po, po, None, None, None, f, 1 << 30,
+                                          None, e0, e1) == sv.SV_EINVAL
+        assert L.spec_verify_candidates_timed(f, 100, f, None, 0, 2, 2, 3, 3, 100, 2, po, po, po, None, f,
+                                              1 << 30, None, e0, e1) == sv.SV_EINVAL
+    assert (out == SENT).all()
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

@@ -126,3 +126,49 @@ def test_explicit_stream(sv, w):
     b = sv.sample(w.target, w.draft, w.tokens, w.uniforms, w.T)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("entry", ["sample", "greedy"])
+def test_stream_keeps_binding_buffers_alive(sv, w, entry):
+    """With stream=s other than the current stream, the buffers the binding
+    allocates (workspace, outputs) come from the current stream's pool while
+    the kernels run on s.  They are recorded on s, so while s's work is still
+    pending the caching allocator hands none of their memory to new
+    allocations on the current stream, which are written at once with no
+    synchronisation; the results equal a plain call's."""
+    L = sv.lib()
+    name = "spec_verify_" + entry
+    orig = getattr(L, name)
+    seen = {}
+
+    def spy(*args):
+        seen["ws"], seen["wsb"] = args[-3], args[-2]
+        return orig(*args)
+
+    def call(**kw):
+        if entry == "sample":
+            return sv.sample(w.target, w.draft, w.tokens, w.uniforms, w.T, **kw)
+        return sv.greedy(w.target, w.tokens, **kw)
+
+    ref = [t.clone() for t in call()]
+    torch.cuda.synchronize()
+    a = torch.randn(8192, 8192, device=DEV)
+    b = torch.empty_like(a)
+    s = torch.cuda.Stream(device=DEV)
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                     # keeps s busy for tens of milliseconds
+        for _ in range(6):
+            torch.mm(a, a, out=b)
+    setattr(L, name, spy)
+    try:
+        got = call(stream=s)
+    finally:
+        setattr(L, name, orig)
+    live = {t.data_ptr() for t in got} | {seen["ws"]}
+    junk = [torch.full((seen["wsb"],), 255, dtype=torch.uint8, device=DEV) for _ in range(4)]
+    junk += [torch.full(t.shape, -7, dtype=t.dtype, device=DEV) for t in got]
+    assert not live & {j.data_ptr() for j in junk}
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for r, g in zip(ref, got):
+        assert torch.equal(r, g)

@@ -311,12 +311,17 @@ def test_workload3_sample(sv, w3):
     print("workload 3 sample:", rep.summary())
 
 
-def test_workload3_greedy(sv, w3):
-    toks, na = sv.greedy(w3.target, w3.tokens)
+@pytest.mark.parametrize("drafts", ["argmax", "sampled"])
+def test_workload3_greedy(sv, w3, drafts):
+    """Greedy verification of workload 3 with greedy drafting (the draft's own
+    argmax at each position, a draft model decoding at temperature 0) and
+    with the sampled drafts."""
+    x = synthetic.greedy_drafts(w3.draft) if drafts == "argmax" else w3.tokens
+    toks, na = sv.greedy(w3.target, x)
     torch.cuda.synchronize()
-    bad, _, on = parity.check_greedy(f32(w3.target), npi(w3.tokens), npi(toks), npi(na))
+    bad, _, on = parity.check_greedy(f32(w3.target), npi(x), npi(toks), npi(na))
     assert not bad
-    print("workload 3 greedy: mean committed", on.mean() + 1)
+    print(f"workload 3 greedy, {drafts} drafts: mean committed", on.mean() + 1)
 
 
 def test_workload3_deterministic(sv, w3):
@@ -361,9 +366,41 @@ def w5():
     return synthetic.generate(5, device=DEV)
 
 
+def check_sample_all(w, toks, na, chunk=64, probs_every=8, px=None, qx=None):
+    """Every sequence of a large batch against the oracle, `chunk` sequences
+    at a time (host copies stay near 1 GB); the exported p(x), q(x) on every
+    `probs_every`-th sequence."""
+    B = w.target.shape[0]
+    x, u = npi(w.tokens), npi(w.uniforms)
+    rep = parity.SampleReport()
+    worst = 0.0
+    for b0 in range(0, B, chunk):
+        b1 = min(B, b0 + chunk)
+        z, y = f32(w.target[b0:b1]), f32(w.draft[b0:b1])
+        parity.check_sample(z, y, x[b0:b1], u[b0:b1], w.T, toks[b0:b1], na[b0:b1], eps=EPS,
+                            report=rep, seq_ids=np.arange(b0, b1))
+        if px is not None:
+            sel = np.arange(b0, b1)
+            sel = sel[sel % probs_every == 0] - b0
+            worst = max(worst, parity.check_probs(z[sel], y[sel], x[b0:b1][sel], w.T, px[b0:b1][sel],
+                                                  qx[b0:b1][sel]))
+    return rep, worst
+
+
+def check_greedy_all(w, x, toks, na, chunk=64):
+    """Every sequence of a large batch, bit-exact; returns the mismatching ids."""
+    B = w.target.shape[0]
+    bad = []
+    for b0 in range(0, B, chunk):
+        b1 = min(B, b0 + chunk)
+        bb, _, _ = parity.check_greedy(f32(w.target[b0:b1]), x[b0:b1], toks[b0:b1], na[b0:b1])
+        bad += [b0 + i for i in bb]
+    return bad
+
+
 def test_workload5_sample(sv, w5):
-    """Full B=512, k=16, V=128256 bf16 call; every sequence checked for the
-    rule's invariants, 64 evenly spaced sequences against the oracle."""
+    """Full B=512, k=16, V=128256 bf16 call: every sequence checked for the
+    rule's invariants and against the oracle; p(x), q(x) on every 8th."""
     toks, na, px, qx = run_sample(sv, w5)
     x = npi(w5.tokens)
     assert ((na >= 0) & (na <= 16)).all()
@@ -371,45 +408,37 @@ def test_workload5_sample(sv, w5):
         assert (toks[b, : na[b]] == x[b, : na[b]]).all()
         assert 0 <= toks[b, na[b]] < 128256
         assert (toks[b, na[b] + 1:] == -1).all()
-    idx = np.arange(0, 512, 8)
-    ti = torch.as_tensor(idx, device=DEV)
-    z, y = f32(w5.target[ti]), f32(w5.draft[ti])
-    u = npi(w5.uniforms)[idx]
-    rep = parity.check_sample(z, y, x[idx], u, w5.T, toks[idx], na[idx], eps=EPS, seq_ids=idx)
+    rep, worst = check_sample_all(w5, toks, na, px=px, qx=qx)
     assert rep.ok(), (rep.summary(), rep.failures[:3])
-    worst = parity.check_probs(z, y, x[idx], w5.T, px[idx], qx[idx])
+    assert rep.rounds == 512
     assert worst <= PROB_RTOL, worst
     print("workload 5 sample:", rep.summary())
 
 
 def test_workload5_vocabulary_shard(sv):
     """Workload 5 as one of 8 vocabulary shards (V = 16032 per row, the shape
-    bench.py --vocab-shard 8 times): a sample of sequences against the oracle,
+    bench.py --vocab-shard 8 times): every sequence against the oracle,
     sampling and greedy."""
     w = synthetic.generate(5, device=DEV, V=16032)
     toks, na, px, qx = run_sample(sv, w)
-    idx = np.arange(0, 512, 4)
-    ti = torch.as_tensor(idx, device=DEV)
-    z, y = f32(w.target[ti]), f32(w.draft[ti])
-    x, u = npi(w.tokens), npi(w.uniforms)
-    rep = parity.check_sample(z, y, x[idx], u[idx], w.T, toks[idx], na[idx], eps=EPS, seq_ids=idx)
+    rep, worst = check_sample_all(w, toks, na, px=px, qx=qx, probs_every=2)
     assert rep.ok(), (rep.summary(), rep.failures[:3])
-    assert parity.check_probs(z, y, x[idx], w.T, px[idx], qx[idx]) <= PROB_RTOL
+    assert rep.rounds == 512
+    assert worst <= PROB_RTOL, worst
     gt, gn = sv.greedy(w.target, w.tokens)
     torch.cuda.synchronize()
-    bad, _, _ = parity.check_greedy(z, x[idx], npi(gt)[idx], npi(gn)[idx])
-    assert not bad
+    assert not check_greedy_all(w, npi(w.tokens), npi(gt), npi(gn))
     print("workload 5, one of 8 vocabulary shards:", rep.summary())
 
 
 def test_workload5_greedy(sv, w5):
-    toks, na = sv.greedy(w5.target, w5.tokens)
-    torch.cuda.synchronize()
-    idx = np.arange(0, 512, 4)
-    ti = torch.as_tensor(idx, device=DEV)
-    bad, _, _ = parity.check_greedy(f32(w5.target[ti]), npi(w5.tokens)[idx], npi(toks)[idx],
-                                    npi(na)[idx])
-    assert not bad
+    """Every sequence, bit-exact, with the sampled drafts and with drafts that
+    follow the argmax for a random prefix (longer accepted runs)."""
+    g = torch.Generator(device=DEV).manual_seed(505)
+    for x in (w5.tokens, corrupt_after_argmax(w5.target, 16, g, 0.85)):
+        toks, na = sv.greedy(w5.target, x)
+        torch.cuda.synchronize()
+        assert not check_greedy_all(w5, npi(x), npi(toks), npi(na))
 
 
 # ---------------------------------------------------------------------------
@@ -434,11 +463,13 @@ def test_greedy_ext_parity(sv, dtype, B, k, V):
 
 
 def test_greedy_ext_workload3(sv, w3):
-    toks, na, v, mask, cnt = sv.greedy_ext(w3.target, w3.tokens)
+    """The #Match by-products on workload 3 with greedy drafting."""
+    x = synthetic.greedy_drafts(w3.draft)
+    toks, na, v, mask, cnt = sv.greedy_ext(w3.target, x)
     torch.cuda.synchronize()
     z = f32(w3.target)
-    assert not parity.check_greedy(z, npi(w3.tokens), npi(toks), npi(na))[0]
-    assert not parity.check_greedy_matches(z, npi(w3.tokens), npi(v), npi(mask), npi(cnt))
+    assert not parity.check_greedy(z, npi(x), npi(toks), npi(na))[0]
+    assert not parity.check_greedy_matches(z, npi(x), npi(v), npi(mask), npi(cnt))
     print("workload 3 greedy: mean #Match", npi(cnt).mean(), "mean accepted", npi(na).mean())
 
 
@@ -505,6 +536,30 @@ def test_tree_parity(sv, B, N, C, L, R, V):
     torch.cuda.synchronize()
     ot, oa, ob = oracle.greedy_tree(f32(nodes), npi(cand), npi(rows))
     assert np.array_equal(ot, npi(toks)) and np.array_equal(oa, npi(A)) and np.array_equal(ob, npi(best))
+
+
+def test_tree_padding_slots(sv):
+    """Short candidates padded with token -1 at row -1 (a tree builder's
+    padding): the padded positions never match, so no -1 is ever committed
+    as an accepted token, and the GPU equals the oracle."""
+    B, N, C, L, V = 24, 9, 4, 6, 3001
+    g = torch.Generator(device=DEV).manual_seed(2024)
+    nodes = (torch.randn((B, N, V), generator=g, device=DEV) * 2).to(torch.bfloat16)
+    rows = torch.randint(0, N, (B, C, L), generator=g, device=DEV, dtype=torch.int32)
+    ref = torch.gather(torch.argmax(nodes.float(), dim=2), 1, rows.long().reshape(B, -1)).reshape(B, C, L)
+    cand = ref.to(torch.int32)
+    lens = torch.randint(0, L + 1, (B, C), generator=g, device=DEV)
+    pad = torch.arange(L, device=DEV)[None, None, :] >= lens[:, :, None]
+    cand[pad] = -1
+    rows[pad] = -1
+    toks, A, best = sv.greedy_tree(nodes, cand, rows)
+    torch.cuda.synchronize()
+    ot, oa, ob = oracle.greedy_tree(f32(nodes), npi(cand), npi(rows))
+    assert np.array_equal(ot, npi(toks)) and np.array_equal(oa, npi(A)) and np.array_equal(ob, npi(best))
+    assert np.array_equal(npi(A), npi(lens).max(axis=1))
+    t, a = npi(toks), npi(A)
+    for b in range(B):
+        assert (t[b, :a[b]] >= 0).all()
 
 
 def test_tree_workload4_equals_flat(sv):
@@ -574,30 +629,47 @@ def test_lazy_workloads(sv, cid):
 
 
 # ---------------------------------------------------------------------------
-# streams and the measurement aid
+# streams and the measurement variants
 # ---------------------------------------------------------------------------
-def test_side_stream_and_profile(sv):
+def test_side_stream_and_timed_variants(sv):
+    """Calls on a side stream equal calls on the current one; with a pair of
+    the caller's events every entry point family records them around its
+    streaming kernel (a positive duration) and computes the same result."""
     w = synthetic.chain(16, 4, 20000, "bf16", seed=31, device=DEV)
     ref = run_sample(sv, w)
+    ref_g = [npi(t) for t in sv.greedy_ext(w.target, w.tokens)]
+    c = synthetic.candidates(4, 3, 5, 5, 7001, "bf16", seed=9, device=DEV)
+    ref_c = [npi(t) for t in sv.greedy_candidates_ext(c.target, c.tokens)]
+    nodes, rows = synthetic.as_tree(c)
+    ref_t = [npi(t) for t in sv.greedy_tree(nodes, c.tokens, rows)]
+    ref_tr = [npi(t) for t in sv.sample_truncated(w.target, w.draft, w.tokens, w.uniforms, w.T, 20, 0.9)]
+    ref_l = [npi(t) for t in sv.sample_lenient(w.target, w.draft, w.tokens, w.uniforms, w.T, 2.0)]
+    torch.cuda.synchronize()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
-    sv.profile_begin(4)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(9)]
     with torch.cuda.stream(s):
-        out = sv.sample(w.target, w.draft, w.tokens, w.uniforms, w.T, return_probs=True)
-        out2 = sv.greedy(w.target, w.tokens)
-    ms = sv.profile_end()
+        out = sv.sample(w.target, w.draft, w.tokens, w.uniforms, w.T, return_probs=True, events=evs[0])
+        got = [
+            (ref_g[:2], sv.greedy(w.target, w.tokens, events=evs[1])),
+            (ref_g, sv.greedy_ext(w.target, w.tokens, events=evs[2])),
+            (ref_c[:3], sv.greedy_candidates(c.target, c.tokens, events=evs[3])),
+            (ref_c, sv.greedy_candidates_ext(c.target, c.tokens, events=evs[4])),
+            (ref_t, sv.greedy_tree(nodes, c.tokens, rows, events=evs[5])),
+            (ref_tr, sv.sample_truncated(w.target, w.draft, w.tokens, w.uniforms, w.T, 20, 0.9,
+                                         events=evs[6])),
+            (ref_l, sv.sample_lenient(w.target, w.draft, w.tokens, w.uniforms, w.T, 2.0, events=evs[7])),
+            (ref[:2], sv.sample(w.target, w.draft, w.tokens, w.uniforms, w.T, events=evs[8])),
+        ]
     torch.cuda.synchronize()
-    assert len(ms) == 2 and all(m > 0 for m in ms)
     for a, b in zip(ref, out):
         assert np.array_equal(a, npi(b))
-    bad, _, _ = parity.check_greedy(f32(w.target), npi(w.tokens), npi(out2[0]), npi(out2[1]))
-    assert not bad
-    # every third call, at most two of them
-    sv.profile_begin(2, 3)
-    for _ in range(9):
-        sv.greedy(w.target, w.tokens)
-    ms = sv.profile_end()
-    assert len(ms) == 2 and all(m > 0 for m in ms)
+    for want, have in got:
+        for a, b in zip(want, have):
+            assert np.array_equal(a, npi(b))
+    ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    assert all(m > 0 for m in ms), ms
 
 
 # ---------------------------------------------------------------------------
