@@ -74,6 +74,7 @@ def measured_traffic(bytes_algo: float):
 CHAIN_MODES = ("sample", "greedy", "greedy_ext", "lenient", "sample_lazy", "greedy_lazy", "truncated")
 CAND_MODES = ("candidates", "candidates_ext", "tree")
 MALL_DEFEAT_BYTES = 1 << 30            # inputs rotated over at least this many bytes (MALL: 256 MB)
+CPU_SHARE = 16                         # host CPUs the GPU machine gives one GPU's job
 
 
 def main():
@@ -104,7 +105,15 @@ def main():
                     help="calls captured in one HIP graph and replayed after the timed region "
                          "(0: skip); reported as config.graph_replay_ms_per_call")
     ap.add_argument("--profile-every", type=int, default=5,
-                    help="time the streaming kernel on every N-th timed call")
+                    help="time the streaming kernel on every N-th timed call (a pair of events "
+                         "the library records around it)")
+    ap.add_argument("--drafts", default="auto", choices=["auto", "sampled", "argmax"],
+                    help="draft tokens of chain workloads: sampled from the draft rows, or the "
+                         "draft's argmax (greedy drafting); auto: argmax for greedy modes on "
+                         "workload 3, sampled otherwise")
+    ap.add_argument("--ceiling-vec", type=int, default=4096,
+                    help="16-byte vectors per workgroup of the plain streaming read that gives "
+                         "the device's achievable read rate (roofline.ceiling); 0 skips it")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (scale for the rocprofv3 byte counters)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -159,6 +168,12 @@ def main():
     def part(t, s):
         return None if t is None else t[s * B:(s + 1) * B]
 
+    greedy_mode = args.mode in ("greedy", "greedy_ext", "greedy_lazy")
+    drafts = args.drafts
+    if drafts == "auto":
+        drafts = "argmax" if (greedy_mode and cid == 3) else "sampled"
+    if drafts == "argmax" and not cand:
+        wall.tokens = synthetic.greedy_drafts(wall.draft)
     slices = [synthetic.Workload(cfg0, part(wall.target, s), part(wall.draft, s), part(wall.tokens, s),
                                  part(wall.uniforms, s), wall.T) for s in range(sets)]
     w = slices[0]
@@ -171,9 +186,9 @@ def main():
         rows = B * C * R
         ws = torch.empty(sv.workspace_bytes(B, N, V, trees[0][0].dtype), dtype=torch.uint8, device=dev)
 
-        def call(i):
+        def call(i, ev=None):
             nodes, cand_rows = trees[i % sets]
-            sv.greedy_tree(nodes, slices[i % sets].tokens, cand_rows, workspace=ws)
+            sv.greedy_tree(nodes, slices[i % sets].tokens, cand_rows, workspace=ws, events=ev)
         stats_rows = B * N
         workload = f"workload {cid}: spec_verify_greedy_tree B={B} C={C} L={L} R={R} N={N} V={V} {cfg0.dtype}"
     elif cand:
@@ -185,14 +200,14 @@ def main():
         ws = torch.empty(sv.workspace_bytes(B, C * R, V, w.target.dtype), dtype=torch.uint8, device=dev)
 
         if args.mode == "candidates":
-            def call(i):
+            def call(i, ev=None):
                 x = slices[i % sets]
                 sv.greedy_candidates(x.target, x.tokens, out_tokens=out[0], out_num_accepted=out[1],
-                                     out_best=out[2], workspace=ws)
+                                     out_best=out[2], workspace=ws, events=ev)
         else:
-            def call(i):
+            def call(i, ev=None):
                 x = slices[i % sets]
-                sv.greedy_candidates_ext(x.target, x.tokens, workspace=ws)
+                sv.greedy_candidates_ext(x.target, x.tokens, workspace=ws, events=ev)
         stats_rows = rows
         workload = f"workload {cid}: spec_verify_greedy_{args.mode} B={B} C={C} L={L} R={R} V={V} {cfg0.dtype}"
     else:
@@ -214,27 +229,29 @@ def main():
                     f"{' T=' + str(w.T) if sampling else ''}{extra}")
         stats_rows = B * stream_rows
 
-        def call(i):
+        def call(i, ev=None):
+            # the early-exit modes have no single streaming kernel to time: `ev` is unused there
             x = slices[i % sets]
             if args.mode == "sample":
                 sv.sample(x.target, x.draft, x.tokens, x.uniforms, x.T, out_tokens=out_t,
-                          out_num_accepted=out_n, workspace=ws)
+                          out_num_accepted=out_n, workspace=ws, events=ev)
             elif args.mode == "lenient":
                 sv.sample_lenient(x.target, x.draft, x.tokens, x.uniforms, x.T, args.lenience,
-                                  workspace=ws)
+                                  workspace=ws, events=ev)
             elif args.mode == "sample_lazy":
                 sv.sample_lazy(x.target, x.draft, x.tokens, x.uniforms, x.T, out_tokens=out_t,
                                out_num_accepted=out_n, workspace=ws)
             elif args.mode == "truncated":
                 sv.sample_truncated(x.target, x.draft, x.tokens, x.uniforms, x.T, args.top_k,
-                                    args.top_p, workspace=ws)
+                                    args.top_p, workspace=ws, events=ev)
             elif args.mode == "greedy_lazy":
                 sv.greedy_lazy(x.target, x.tokens, out_tokens=out_t, out_num_accepted=out_n,
                                workspace=ws)
             elif args.mode == "greedy_ext":
-                sv.greedy_ext(x.target, x.tokens, workspace=ws)
+                sv.greedy_ext(x.target, x.tokens, workspace=ws, events=ev)
             else:
-                sv.greedy(x.target, x.tokens, out_tokens=out_t, out_num_accepted=out_n, workspace=ws)
+                sv.greedy(x.target, x.tokens, out_tokens=out_t, out_num_accepted=out_n, workspace=ws,
+                          events=ev)
 
     if args.vocab_shard > 1:
         workload += f" (one of {args.vocab_shard} vocabulary shards of V={v_full})"
@@ -248,21 +265,27 @@ def main():
         call(i)
     torch.cuda.synchronize()
 
-    # the streaming kernel is timed by events around it on every
-    # `profile_every`-th call of the timed region (each event pair adds a few
-    # microseconds of queue time to the call it brackets)
-    sv.profile_begin(args.steps, args.profile_every)
+    # the streaming kernel is timed by a pair of events the library records
+    # around it, on every `profile_every`-th call of the timed region (each
+    # pair adds a few microseconds of queue time to the call it brackets)
+    lazy = args.mode.endswith("_lazy")
+    timed_ids = [] if lazy else list(range(0, args.steps, max(1, args.profile_every)))
+    kev = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for i in timed_ids}
+    for e0, e1 in kev.values():                    # creates the events' handles before the timed region
+        e0.record()
+        e1.record()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     start.record()
     for i in range(args.steps):
-        call(args.warmup + i)
+        call(args.warmup + i, kev.get(i))
     end.record()
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - w0
-    kernel_ms = sv.profile_end()
+    kernel_ms = [e0.elapsed_time(e1) for e0, e1 in kev.values()]
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
     value = rows * args.steps / (total_ms / 1e3)
@@ -305,11 +328,35 @@ def main():
         graph_ms = g0.elapsed_time(g1) / (reps * graph_n)
         del g
 
-    lazy = args.mode.endswith("_lazy")
-    if lazy:                           # early exit: no single streaming kernel per call
-        kernel_ms = []
     k_avg_ms = statistics.fmean(kernel_ms) if kernel_ms else None
     achieved = stats_bytes / (k_avg_ms / 1e3) / 1e9 if kernel_ms else None
+
+    # early exit: the bytes a call actually streams follow from each
+    # sequence's accepted count (the windows it stayed undecided through, and
+    # the draw's re-read), worked out per input set
+    lazy_bytes = None
+    if lazy:
+        per_set = []
+        for si in range(sets):
+            call(si)
+            torch.cuda.synchronize()
+            r_stats, r_draw = lazy_streamed_rows(out_n.cpu().tolist(), k, args.mode == "sample_lazy")
+            per_set.append(r_stats * bytes_per_row + r_draw * V * es)
+        lazy_bytes = statistics.fmean(per_set[(args.warmup + i) % sets] for i in range(args.steps))
+        achieved = lazy_bytes / (ms_per_step / 1e3) / 1e9
+
+    # the device's achievable read rate: a plain 16-byte streaming read of the
+    # same buffers (the same input sets, rotated the same way), one launch
+    # over each call's logits
+    ceiling = None
+    if args.ceiling_vec > 0:
+        if args.mode == "tree":
+            bufs = [(nodes, None) for nodes, _ in trees]
+        elif cand or stream_rows != 2 * cfg0.k + 1:
+            bufs = [(x.target, None) for x in slices]
+        else:
+            bufs = [(x.target, x.draft) for x in slices]
+        ceiling = stream_ceiling(bufs, max(args.steps, 20), args.ceiling_vec)
     traffic = measured_traffic(stats_bytes) \
         if (args.mode == "sample" and cid == 5 and args.vocab_shard == 1) else None
 
@@ -333,6 +380,8 @@ def main():
             "logit_bytes_per_call": stats_rows * V * es,
             "call_effective_GBps": stats_rows * V * es / (ms_per_step / 1e3) / 1e9,
             "input_sets_rotated": sets,
+            "draft_tokens": "argmax of the draft rows (greedy drafting)" if (drafts == "argmax" and not cand)
+            else None if cand else "sampled from softmax(draft / T)",
             "single_call_ms_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
             "graph_replay_ms_per_call": graph_ms,
             "graph_calls": graph_n,
@@ -340,7 +389,23 @@ def main():
             "input_generation_s": gen_s,
             "device": torch.cuda.get_device_name(0),
         },
-        "roofline": None if lazy else {
+        "roofline": {
+            "kernel": "the whole call (windows of k_lazy_stats, their decisions, the draw)",
+            "note": ("early exit has no single streaming kernel: achieved = the bytes the call "
+                     "streams (every row of each window a sequence is still undecided at, plus "
+                     "the draw's re-read; from the calls' accepted counts) / ms_per_step"),
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS,
+            "ceiling": ceiling["GBps"] if ceiling else None,
+            "frac_of_ceiling": achieved / ceiling["GBps"] if ceiling else None,
+            "ceiling_run": ceiling,
+            "traffic": None,
+            "streamed_bytes_per_call": lazy_bytes,
+            "full_pass_bytes_per_call": stats_bytes,
+        } if lazy else {
             "kernel": {"sample": "k_softmax_stats", "lenient": "k_softmax_stats",
                        "truncated": "k_trunc16" if es == 2 else "k_trunc_rows"}.get(
                            args.mode, "k_argmax_stats"),
@@ -358,6 +423,9 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBS if achieved else None,
+            "ceiling": ceiling["GBps"] if ceiling else None,
+            "frac_of_ceiling": achieved / ceiling["GBps"] if (ceiling and achieved) else None,
+            "ceiling_run": ceiling,
             "traffic": traffic,
             "kernel_ms_avg": k_avg_ms,
             "kernel_ms_min": min(kernel_ms) if kernel_ms else None,
@@ -374,6 +442,89 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
     print(json.dumps(line), flush=True)
+
+
+def lazy_bounds(k):
+    """Window bounds of the early-exit entry points: 0, 1, 2, 4, 8, ...
+    clipped to k+1, a last window that would hold only the bonus row joining
+    the window before it (the schedule the library launches)."""
+    b = [0]
+    nxt = 1
+    while b[-1] < k + 1:
+        b.append(min(nxt, k + 1))
+        nxt = nxt + 1 if nxt < 2 else nxt * 2
+    if len(b) >= 3 and b[-2] == k:
+        b[-2] = k + 1
+        b.pop()
+    return b
+
+
+def lazy_streamed_rows(num_accepted, k, sampling):
+    """(rows streamed by the statistics windows, rows re-read by the draw) of
+    one early-exit call: a sequence with j accepted drafts is undecided at
+    every window that starts at or before position j and is streamed there
+    (the window's target rows, and when sampling its draft rows below k);
+    the draw re-reads the rejected row pair, or the bonus row."""
+    b = lazy_bounds(k)
+    stats = draw = 0
+    for j in num_accepted:
+        for w0, w1 in zip(b[:-1], b[1:]):
+            if j < w0:
+                break
+            stats += w1 - w0
+            if sampling:
+                stats += max(0, min(w1, k) - w0)
+        if sampling:
+            draw += 2 if j < k else 1
+    return stats, draw
+
+
+def stream_ceiling(bufs, calls, vec_per_block):
+    """GB/s of a plain 16-byte non-temporal streaming read (libsvceiling.so)
+    over `bufs` [(a, b or None), ...] device tensors, one launch per entry,
+    rotated like the calls; averaged over `calls` launches between two
+    events, after a few untimed ones."""
+    import ctypes
+
+    import torch
+    path = os.path.join(ROOT, "draft_verification_verify_amd", "libsvceiling.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is not built (run __graft_entry__.build())")
+    L = ctypes.CDLL(path)
+    P, LL, I = ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int
+    L.sv_stream_read_blocks.argtypes = [LL, LL, I]
+    L.sv_stream_read_blocks.restype = LL
+    L.sv_stream_read.argtypes = [P, LL, P, LL, I, P, LL, P]
+    L.sv_stream_read.restype = I
+
+    def nbytes(t):
+        return 0 if t is None else t.numel() * t.element_size()
+
+    blocks = max(L.sv_stream_read_blocks(nbytes(a), nbytes(b), vec_per_block) for a, b in bufs)
+    sink = torch.zeros(blocks, dtype=torch.int32, device="cuda:0")
+    st = torch.cuda.current_stream().cuda_stream
+
+    def launch(i):
+        a, b = bufs[i % len(bufs)]
+        rc = L.sv_stream_read(a.data_ptr(), nbytes(a), None if b is None else b.data_ptr(), nbytes(b),
+                              vec_per_block, sink.data_ptr(), blocks, st)
+        if rc != 0:
+            raise RuntimeError(f"sv_stream_read failed: {rc}")
+
+    for i in range(5):
+        launch(i)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(calls):
+        launch(5 + i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / calls
+    per = statistics.fmean(nbytes(a) + nbytes(b) for a, b in bufs)
+    return {"GBps": per / (ms / 1e3) / 1e9, "ms_per_launch": ms, "bytes_per_launch": per,
+            "launches": calls, "vec_per_block": vec_per_block, "kernel": "k_stream_read"}
 
 
 def cpu_baseline(w, out_t, out_n, budget_s):
@@ -428,10 +579,12 @@ def cpu_baseline(w, out_t, out_n, budget_s):
         return state["seqs"], time.perf_counter() - t0
 
     try:
-        cores = len(os.sched_getaffinity(0))
+        affinity = len(os.sched_getaffinity(0))
     except AttributeError:
-        cores = os.cpu_count() or 1
-    cores = max(1, min(16, cores))
+        affinity = os.cpu_count() or 1
+    # the GPU machine gives one GPU's job a share of 16 of its host's CPUs (its
+    # worker pools are sized to that share, whatever the host has in all)
+    cores = max(1, min(CPU_SHARE, affinity))
     s1, t1 = run(1, budget_s / 4)
     sn, tn = run(cores, budget_s * 3 / 4)
     return {
@@ -440,6 +593,9 @@ def cpu_baseline(w, out_t, out_n, budget_s):
         "cores": cores,
         "kind": "oracle",
         "value_1_core": s1 * k1 / t1,
+        "host_nproc": os.cpu_count(),
+        "host_affinity_cpus": affinity,
+        "cpu_share": CPU_SHARE,
         "cpu_model": _cpu_model(),
         "sample": (f"the first {nseq} sequences of the same workload ({nseq * k1} rows), run "
                    f"repeatedly in chunks of {chunk}: {s1} sequences on 1 thread in {t1:.1f} s, "
@@ -451,7 +607,16 @@ def cpu_baseline(w, out_t, out_n, budget_s):
 
 
 def _cpu_model() -> str:
-    """The host CPU's model name, as /proc/cpuinfo reports it (or "unknown")."""
+    """The host CPU's model name, as lscpu reports it, else /proc/cpuinfo (or
+    "unknown")."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.strip().startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:

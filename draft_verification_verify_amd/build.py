@@ -63,6 +63,25 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+CEILING_SRC = os.path.join(CSRC, "sv_ceiling.hip")
+CEILING_LIB = os.path.join(HERE, "libsvceiling.so")
+
+
+def build_ceiling(verbose: bool = False) -> str:
+    """libsvceiling.so: the plain streaming-read kernel bench.py measures the
+    device's achievable read rate with (a measurement tool, not part of the
+    verification library)."""
+    tmp = CEILING_LIB + ".tmp"
+    cmd = [HIPCC, *COMMON, "-shared", CEILING_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for sv_ceiling.hip:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, CEILING_LIB)
+    if verbose:
+        print("built", CEILING_LIB)
+    return CEILING_LIB
+
+
 CLIENT_SRC = os.path.join(ROOT, "tests", "c_client", "sv_client.c")
 CLIENT_BIN = os.path.join(ROOT, "tests", "c_client", "sv_client")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
@@ -85,4 +104,5 @@ def build_client(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     build(verbose=True)
+    build_ceiling(verbose=True)
     build_client(verbose=True)

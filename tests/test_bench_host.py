@@ -108,3 +108,25 @@ def test_digest_follows_the_kernel_source(monkeypatch):
         return fh
     monkeypatch.setattr("builtins.open", fake_open)
     assert bench.stats_kernel_digest() != d0
+
+
+@pytest.mark.parametrize("k,bounds", [(16, [0, 1, 2, 4, 8, 17]), (8, [0, 1, 2, 4, 9]), (4, [0, 1, 2, 5]),
+                                      (1, [0, 2]), (5, [0, 1, 2, 4, 6]), (63, [0, 1, 2, 4, 8, 16, 32, 64])])
+def test_lazy_window_schedule(k, bounds):
+    """The early-exit windows 0, 1, 2, 4, 8, ... clipped to k+1, where a last
+    window holding only the bonus row joins the window before it."""
+    assert bench.lazy_bounds(k) == bounds
+
+
+def test_lazy_streamed_rows():
+    """Rows an early-exit call streams, worked by hand for k = 4 (windows
+    [0,1), [1,2), [2,5)): a sequence rejecting at 0 streams window 0's target
+    and draft row and the draw re-reads the pair; one accepting everything
+    streams 1+1, 1+1 and 3+2 rows and re-reads the bonus row."""
+    assert bench.lazy_streamed_rows([0], 4, True) == (2, 2)
+    assert bench.lazy_streamed_rows([1], 4, True) == (4, 2)
+    assert bench.lazy_streamed_rows([2], 4, True) == (9, 2)
+    assert bench.lazy_streamed_rows([3], 4, True) == (9, 2)
+    assert bench.lazy_streamed_rows([4], 4, True) == (9, 1)
+    assert bench.lazy_streamed_rows([0, 4, 1], 4, True) == (15, 5)
+    assert bench.lazy_streamed_rows([0, 2, 4], 4, False) == (1 + 5 + 5, 0)
