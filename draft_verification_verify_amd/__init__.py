@@ -18,7 +18,8 @@ import torch  # loads torch's HIP runtime first, so the library binds to the sam
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 
-SV_OK, SV_EINVAL, SV_EDTYPE, SV_EWORKSPACE, SV_EHIP = 0, 1, 2, 3, 4
+SV_OK, SV_EINVAL, SV_EDTYPE, SV_EWORKSPACE, SV_EHIP, SV_ESCRATCH = 0, 1, 2, 3, 4, 5
+NOALLOC_SCRATCH_BYTES = 4 << 20        # SV_NOALLOC_SCRATCH_BYTES
 SV_F32, SV_F16, SV_BF16 = 0, 1, 2
 MAX_K = 63
 
@@ -68,6 +69,8 @@ def lib():
         L.spec_verify_sample_truncated.argtypes = [P, LL, P, LL, P, P, F, I, F, I, I, I, I, P, P, P,
                                                    P, P, SZ, P]
         L.spec_verify_sample_truncated.restype = I
+        L.spec_verify_sample_noalloc.argtypes = [P, LL, P, LL, P, P, F, I, I, I, I, P, P, P, P, P]
+        L.spec_verify_sample_noalloc.restype = I
         L.spec_verify_sample_timed.argtypes = [P, LL, P, LL, P, P, F, F, I, F, I, I, I, I, P, P, P, P,
                                                P, SZ, P, P, P]
         L.spec_verify_sample_timed.restype = I
@@ -86,7 +89,7 @@ EXPORTED = (
     "spec_verify_greedy_ext", "spec_verify_sample_lenient", "spec_verify_greedy_candidates_ext",
     "spec_verify_greedy_tree", "spec_verify_sample_lazy", "spec_verify_greedy_lazy",
     "spec_verify_sample_truncated", "spec_verify_sample_timed", "spec_verify_greedy_timed",
-    "spec_verify_candidates_timed",
+    "spec_verify_candidates_timed", "spec_verify_sample_noalloc",
 )
 
 
@@ -319,6 +322,32 @@ def sample(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor
         raise SpecVerifyError(st, "spec_verify_sample")
     if return_probs:
         return out_tokens, out_num_accepted, out_p_x, out_q_x
+    return out_tokens, out_num_accepted
+
+
+def sample_noalloc(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
+                   uniforms: torch.Tensor, temperature: float, *, out_tokens, out_num_accepted,
+                   out_p_x=None, out_q_x=None, stream=None):
+    """`sample` for callers that cannot allocate: the outputs are the caller's
+    (required), and the library's static scratch of NOALLOC_SCRATCH_BYTES per
+    device replaces the workspace.  Calls that overlap on one device race on
+    that scratch.  Returns (tokens, num_accepted)."""
+    B, k, V, ts, ds = _sample_inputs(target, draft, draft_tokens, uniforms)
+    dev = target.device
+    _need(out_tokens, "out_tokens", (B, k + 1), torch.int32, dev)
+    _need(out_num_accepted, "out_num_accepted", (B,), torch.int32, dev)
+    for t, name in ((out_p_x, "out_p_x"), (out_q_x, "out_q_x")):
+        if t is not None:
+            _need(t, name, (B, k), torch.float32, dev)
+    if B == 0:
+        return out_tokens, out_num_accepted
+    st = lib().spec_verify_sample_noalloc(_ptr(target), ts, _ptr(draft), ds, _ptr(draft_tokens),
+                                          _ptr(uniforms), float(temperature), B, k, V,
+                                          _sv_dtype(target.dtype), _ptr(out_tokens),
+                                          _ptr(out_num_accepted), _ptr(out_p_x), _ptr(out_q_x),
+                                          _stream(stream, dev))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "spec_verify_sample_noalloc")
     return out_tokens, out_num_accepted
 
 

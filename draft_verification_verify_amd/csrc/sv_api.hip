@@ -6,10 +6,19 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "spec_verify.h"
 #include "sv_launch.h"
 
 using namespace sv;
+
+// The scratch of spec_verify_sample_noalloc: one copy per device, held until
+// the process ends.  Host code never passes this name to a kernel (on the host
+// it is a stand-in, not a device address): it uses the address that
+// hipGetSymbolAddress gives for the current device (scratch_address below).
+static __device__ __align__(256) unsigned char scratch[SV_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -510,6 +519,29 @@ int lazy_grid(const LazyArgs& l, bool with_draft)
     return (int)(units < kLazyGrid ? units : kLazyGrid);
 }
 
+// The device address of the current device's copy of `scratch`, looked up
+// with hipGetSymbolAddress on the first call on that device (with that device
+// current) and kept per device; null if the lookup fails.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+void* scratch_address(int dev)
+{
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        void* q = nullptr;
+        if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+        g_scratch[dev].store(q, std::memory_order_release);
+        p = q;
+    }
+    return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -524,6 +556,7 @@ const char* spec_verify_status_string(int s)
     case SV_EDTYPE: return "SV_EDTYPE: unknown dtype";
     case SV_EWORKSPACE: return "SV_EWORKSPACE: workspace missing or too small";
     case SV_EHIP: return "SV_EHIP: HIP launch error";
+    case SV_ESCRATCH: return "SV_ESCRATCH: the call needs more scratch than SV_NOALLOC_SCRATCH_BYTES";
     default: return "unknown status";
     }
 }
@@ -683,6 +716,35 @@ int spec_verify_greedy_lazy(const void* target_logits, long long target_row_stri
         if (launch_lazy_decide_greedy(l, da, gc.st) != hipSuccess) return SV_EHIP;
     }
     return SV_OK;
+}
+
+int spec_verify_sample_noalloc(const void* target_logits, long long target_row_stride,
+                               const void* draft_logits, long long draft_row_stride,
+                               const int* draft_tokens, const float* uniforms, float temperature,
+                               int B, int k, int V, int dtype,
+                               int* out_tokens, int* out_num_accepted,
+                               float* out_p_x, float* out_q_x, void* hip_stream)
+{
+    // a call whose shape needs more scratch than the static buffer is refused
+    // before anything else (shapes any call rejects are left to the checks of
+    // spec_verify_sample, which follow)
+    if (B >= 1 && k >= 1 && k <= SV_MAX_K && V >= 1 && V <= kMaxV && dtype_ok(dtype)) {
+        const long long rows = (long long)B * (2 * k + 1);
+        if (fits_grid(rows, V) && layout(nullptr, B, rows, V).bytes > SV_NOALLOC_SCRATCH_BYTES)
+            return SV_ESCRATCH;
+    }
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return SV_EHIP;
+    if (hip_stream) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(static_cast<hipStream_t>(hip_stream), &sdev) != hipSuccess) return SV_EHIP;
+        if (sdev != dev) return SV_EINVAL;
+    }
+    void* ws = scratch_address(dev);
+    if (!ws) return SV_EHIP;
+    return sample_impl(target_logits, target_row_stride, draft_logits, draft_row_stride,
+                       draft_tokens, uniforms, temperature, 1.f, 0, 1.f, B, k, V, dtype, out_tokens,
+                       out_num_accepted, out_p_x, out_q_x, ws, SV_NOALLOC_SCRATCH_BYTES, hip_stream);
 }
 
 int spec_verify_sample_timed(const void* target_logits, long long target_row_stride,

@@ -60,9 +60,11 @@
  *    required pointer or a size/stride/temperature out of range; SV_EDTYPE:
  *    an unknown dtype; SV_EWORKSPACE: workspace NULL or smaller than
  *    spec_verify_workspace_bytes(); SV_EHIP: a launch failed (the HIP error
- *    is reported by the runtime's error state).
+ *    is reported by the runtime's error state); SV_ESCRATCH: a call of
+ *    spec_verify_sample_noalloc that needs more than its static scratch.
  *  - Re-entrancy: calls keep no state between them; concurrent calls must use
- *    distinct workspaces.  Results are deterministic: the same inputs and
+ *    distinct workspaces (spec_verify_sample_noalloc, which has no workspace
+ *    argument, shares one static buffer per device).  Results are deterministic: the same inputs and
  *    shapes give bit-identical outputs (no floating-point atomics).
  */
 #ifndef SPEC_VERIFY_H
@@ -74,11 +76,13 @@
 extern "C" {
 #endif
 
-enum { SV_OK = 0, SV_EINVAL = 1, SV_EDTYPE = 2, SV_EWORKSPACE = 3, SV_EHIP = 4 };
+enum { SV_OK = 0, SV_EINVAL = 1, SV_EDTYPE = 2, SV_EWORKSPACE = 3, SV_EHIP = 4, SV_ESCRATCH = 5 };
 enum { SV_F32 = 0, SV_F16 = 1, SV_BF16 = 2 };
 
 #define SV_MAX_K 63
 #define SV_MAX_CANDIDATE_TOKENS 64
+/* Size of the static scratch of spec_verify_sample_noalloc (per device). */
+#define SV_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
 
 /* Library version, major * 10000 + minor * 100 + patch. */
 int spec_verify_version(void);
@@ -252,6 +256,31 @@ int spec_verify_greedy_lazy(const void* target_logits, long long target_row_stri
                             const int* draft_tokens, int B, int k, int V, int dtype,
                             int* out_tokens, int* out_num_accepted,
                             void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.
+ * spec_verify_sample without the workspace arguments: the same kernels and
+ * the same results, bit for bit, with the scratch taken from a static device
+ * buffer of SV_NOALLOC_SCRATCH_BYTES (4 MiB) that the library holds on each
+ * device it runs on until the process ends.  The call allocates and frees
+ * nothing (no hipMalloc / hipFree, no allocating library routine).
+ *  - Limit: shapes whose spec_verify_workspace_bytes(B, 2k+1, V, dtype)
+ *    exceeds SV_NOALLOC_SCRATCH_BYTES are refused with SV_ESCRATCH before
+ *    anything is launched (B = 512, k = 16, V = 128256 needs 0.86 MiB).
+ *  - One buffer per device, shared by every call on it: the buffer keeps
+ *    the last call's contents (nothing in it needs clearing), and calls that
+ *    overlap on one device race on it, even on different streams.  Issue
+ *    them on one stream, or order them.
+ *  - The device is the current one; hip_stream (NULL: the null stream) must
+ *    belong to it (SV_EINVAL otherwise).  The buffer's address is looked up
+ *    on the first call on each device.
+ *  Other arguments, outputs and errors as spec_verify_sample. */
+int spec_verify_sample_noalloc(const void* target_logits, long long target_row_stride,
+                               const void* draft_logits, long long draft_row_stride,
+                               const int* draft_tokens, const float* uniforms, float temperature,
+                               int B, int k, int V, int dtype,
+                               int* out_tokens, int* out_num_accepted,
+                               float* out_p_x, float* out_q_x, void* hip_stream);
 
 /* Measurement variants, for callers that time the vocabulary-streaming kernel
  * (the one launch that reads every logit) inside their own timed region.

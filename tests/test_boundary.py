@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_header_symbols_exported(sv):
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     assert sorted(sv.EXPORTED) == names
     for n in names:
         assert hasattr(sv.lib(), n), n
@@ -49,7 +49,7 @@ def test_single_hip_runtime(sv):
 def test_status_strings_and_version(sv):
     L = sv.lib()
     assert L.spec_verify_version() >= 200
-    for s in range(5):
+    for s in range(6):
         assert L.spec_verify_status_string(s).startswith(b"SV_")
     assert L.spec_verify_status_string(99) == b"unknown status"
 
@@ -170,6 +170,26 @@ def test_candidates_rejects_bad_arguments(sv):
                                      None) == sv.SV_EINVAL
     assert L.spec_verify_greedy_tree(f, 100, 5, f, f, 2, 2, 3, 5, 100, 2, po, f, f, f, 1 << 30,
                                      None) == sv.SV_EINVAL
+    assert (out == SENT).all()
+
+
+def test_noalloc_refuses_shapes_beyond_its_scratch(sv):
+    """spec_verify_sample_noalloc refuses, before any HIP call, a shape whose
+    workspace exceeds its static scratch, and names the limit; the header's
+    limit is the binding's."""
+    L = sv.lib()
+    text = open(HEADER).read()
+    m = re.search(r"#define SV_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == sv.NOALLOC_SCRATCH_BYTES
+    f = ctypes.c_void_p(64)
+    out = np.full(8, SENT, np.int32)
+    po = out.ctypes.data_as(ctypes.c_void_p)
+    need = L.spec_verify_workspace_bytes(4096, 33, 128256, 2)
+    assert need > sv.NOALLOC_SCRATCH_BYTES
+    assert L.spec_verify_sample_noalloc(f, 128256, f, 128256, f, f, 1.0, 4096, 16, 128256, 2, po, po,
+                                        None, None, None) == sv.SV_ESCRATCH
+    assert b"SV_NOALLOC_SCRATCH_BYTES" in L.spec_verify_status_string(sv.SV_ESCRATCH)
+    assert L.spec_verify_workspace_bytes(512, 33, 128256, 2) <= sv.NOALLOC_SCRATCH_BYTES
     assert (out == SENT).all()
 
 
