@@ -35,7 +35,12 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 METRIC = "verified positions/sec (B·(k+1) rows/s) and achieved HBM GB/s vs peak"
 STATS_SOURCES = ["sv_stats.hip", "sv_device.h", "sv_launch.h"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_softmax_stats_workload5_traffic.json")
+STREAM_KERNELS = ("k_softmax_stats", "k_argmax_stats")
+
+
+def traffic_file(kernel: str, cid: int) -> str:
+    """Where the committed counter figures of a streaming kernel on a workload live."""
+    return os.path.join(ROOT, "profiles", f"{kernel}_workload{cid}_traffic.json")
 
 
 def _plan_source() -> bytes:
@@ -47,24 +52,38 @@ def _plan_source() -> bytes:
     return src[a:src.index(b"\n}\n", a) + 3]
 
 
+def _build_flags() -> bytes:
+    """The compiler flags the streaming kernels are built with (build.py's
+    common flags and those of sv_stats.hip)."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_sv_build_flags", os.path.join(ROOT, "draft_verification_verify_amd", "build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    common = [f for f in b.COMMON if not f.startswith("-I")]
+    return repr((b.HIPCC.split("/")[-1], common, b.SOURCES["sv_stats.hip"])).encode()
+
+
 def stats_kernel_digest() -> str:
-    """What the statistics kernel's counters depend on: its source, the
-    headers it includes, its launch plan and the build flags."""
+    """What the streaming kernels' counters depend on: their source, the
+    headers it includes, their launch plan and the build flags."""
     h = hashlib.sha256()
     for f in STATS_SOURCES:
         with open(os.path.join(ROOT, "draft_verification_verify_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     h.update(_plan_source())
-    h.update(open(os.path.join(ROOT, "draft_verification_verify_amd", "build.py"), "rb").read())
+    h.update(_build_flags())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(bytes_algo: float):
-    """HBM bytes per launch of the statistics kernel from the committed
-    rocprofv3 counter runs, if they were taken on the current kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def measured_traffic(kernel: str, cid: int):
+    """HBM bytes per launch of a streaming kernel on a workload from the
+    committed rocprofv3 counter runs, if they were taken on the current
+    kernel source."""
+    path = traffic_file(kernel, cid)
+    if not os.path.exists(path):
         return None
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         t = json.load(f)
     if t.get("kernel_digest") != stats_kernel_digest():
         return None
@@ -117,11 +136,13 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (scale for the rocprofv3 byte counters)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write the statistics kernel's measured HBM traffic from two "
+                    help="write a streaming kernel's measured HBM traffic on --workload from two "
                          "rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) and exit")
+    ap.add_argument("--traffic-kernel", default="k_softmax_stats", choices=list(STREAM_KERNELS))
     args = ap.parse_args()
     if args.traffic_from:
-        traffic_from_pmc(*args.traffic_from)
+        traffic_from_pmc(*args.traffic_from, kernel=args.traffic_kernel,
+                         out_path=traffic_file(args.traffic_kernel, args.workload or 5))
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -357,8 +378,11 @@ def main():
         else:
             bufs = [(x.target, x.draft) for x in slices]
         ceiling = stream_ceiling(bufs, max(args.steps, 20), args.ceiling_vec)
-    traffic = measured_traffic(stats_bytes) \
-        if (args.mode == "sample" and cid == 5 and args.vocab_shard == 1) else None
+    kernel_name = {"sample": "k_softmax_stats", "lenient": "k_softmax_stats",
+                   "truncated": "k_trunc16" if es == 2 else "k_trunc_rows"}.get(args.mode, "k_argmax_stats")
+    traffic = measured_traffic(kernel_name, cid) \
+        if (kernel_name in STREAM_KERNELS and args.vocab_shard == 1 and args.mode != "tree"
+            and not lazy) else None
 
     line = {
         "metric": METRIC,
@@ -406,9 +430,7 @@ def main():
             "streamed_bytes_per_call": lazy_bytes,
             "full_pass_bytes_per_call": stats_bytes,
         } if lazy else {
-            "kernel": {"sample": "k_softmax_stats", "lenient": "k_softmax_stats",
-                       "truncated": "k_trunc16" if es == 2 else "k_trunc_rows"}.get(
-                           args.mode, "k_argmax_stats"),
+            "kernel": kernel_name,
             "note": (("the timed launch is k_trunc16 (one pass per 16-bit row: an exact LDS "
                       "histogram of all 65536 bit patterns) followed by k_trunc_rows over the "
                       "rows it marked; algorithmic bytes: every row read once") if es == 2 else
@@ -640,11 +662,12 @@ def calibrate_copy(nbytes=1 << 30):
     print(json.dumps({"calibration_copy_bytes": nbytes}), flush=True)
 
 
-def traffic_from_pmc(fetch_csv, write_csv, out_path=TRAFFIC_FILE, copy_bytes=1 << 30):
+def traffic_from_pmc(fetch_csv, write_csv, kernel="k_softmax_stats", out_path=None, copy_bytes=1 << 30):
     """Turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, then
-    WRITE_SIZE, in KiB per dispatch) into HBM bytes per launch of the
-    statistics kernel, each counter scaled by what it reads for the
+    WRITE_SIZE, in KiB per dispatch) into HBM bytes per launch of a
+    streaming kernel, each counter scaled by what it reads for the
     calibration copy of `copy_bytes`."""
+    out_path = out_path or traffic_file(kernel, 5)
     import csv
 
     def dispatches(path, counter):
@@ -652,10 +675,10 @@ def traffic_from_pmc(fetch_csv, write_csv, out_path=TRAFFIC_FILE, copy_bytes=1 <
         return sorted(rows, key=lambda r: int(r["Dispatch_Id"]))
 
     def stats_mean(rows):
-        v = [float(r["Counter_Value"]) for r in rows if "k_softmax_stats" in r["Kernel_Name"]]
+        v = [float(r["Counter_Value"]) for r in rows if kernel in r["Kernel_Name"]]
         if not v:
-            raise SystemExit("no k_softmax_stats dispatch in the counter file")
-        return statistics.fmean(v), next(r["Kernel_Name"] for r in rows if "k_softmax_stats" in r["Kernel_Name"])
+            raise SystemExit(f"no {kernel} dispatch in the counter file")
+        return statistics.fmean(v), next(r["Kernel_Name"] for r in rows if kernel in r["Kernel_Name"])
 
     def last_copy(rows):
         # the calibration copy is the process's last dispatch

@@ -82,14 +82,22 @@ def test_traffic_needs_the_copy_last(tmp_path):
 
 
 def test_traffic_is_reported_only_for_the_kernel_it_was_taken_on(tmp_path, monkeypatch):
-    f = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "traffic_file", lambda kernel, cid: str(tmp_path / f"{kernel}_{cid}.json"))
+    f = tmp_path / "k_argmax_stats_4.json"
     f.write_text(json.dumps({"kernel_digest": bench.stats_kernel_digest(), "bytes_per_launch": 123.0}))
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
-    assert bench.measured_traffic(0.0) == 123.0
+    assert bench.measured_traffic("k_argmax_stats", 4) == 123.0
+    assert bench.measured_traffic("k_argmax_stats", 5) is None          # another workload: no file
+    assert bench.measured_traffic("k_softmax_stats", 4) is None         # another kernel: no file
     f.write_text(json.dumps({"kernel_digest": "0" * 16, "bytes_per_launch": 123.0}))
-    assert bench.measured_traffic(0.0) is None
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "absent.json"))
-    assert bench.measured_traffic(0.0) is None
+    assert bench.measured_traffic("k_argmax_stats", 4) is None
+
+
+def test_digest_follows_the_build_flags(monkeypatch):
+    """The streaming kernels' build flags are part of the digest; other
+    build.py changes are not."""
+    d0 = bench.stats_kernel_digest()
+    monkeypatch.setattr(bench, "_build_flags", lambda: b"other flags")
+    assert bench.stats_kernel_digest() != d0
 
 
 def test_digest_follows_the_kernel_source(monkeypatch):
