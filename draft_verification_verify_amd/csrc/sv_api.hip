@@ -72,6 +72,12 @@ StatsPlan plan_stats(long long rows, int V)
 // rescan of one chunk short.
 constexpr long long kSampleBlocks = 16384;
 
+// Chunk passes of at most this many workgroups also decide the round (the
+// fused pass); measured: workload 1 (16 workgroups) 18.0 -> 15.9 us and
+// workload 2 (1024) 25.3 -> 22.6 us per call, while workload 3 (8192)
+// went from 200 to 210 us and workload 5 (16384) from 666 to 691 us.
+constexpr long long kFuseDecideBlocks = 2048;
+
 struct SamplePlan {
     int nchunks;
     int vec_per_chunk;
@@ -388,10 +394,18 @@ int sample_impl(const void* target_logits, long long target_row_stride,
     const DecideSampleArgs da =
         decide_sample_args(target_logits, target_row_stride, draft_logits, draft_row_stride, draft_tokens,
                            uniforms, lenience, B, k, V, sc, out_tokens, out_num_accepted, out_p_x, out_q_x);
-    if (launch_decide_sample(dtype, da, sc.st) != hipSuccess) return SV_EHIP;
     const SampleArgs ma =
         sampler_args(target_logits, target_row_stride, draft_logits, draft_row_stride, B, k, V, sc, out_tokens);
-    if (launch_sample(dtype, sc.vec, sc.trunc, B, ma, sc.st) != hipSuccess) return SV_EHIP;
+    // Small passes decide in the chunk pass's own launch (one dependent
+    // launch fewer); large ones decide in a kernel of their own, since every
+    // chunk workgroup would repeat its sequence's decision and scattered
+    // gathers (workload 5: 71 us for the fused pass against 5 + 42 us).
+    if ((long long)B * ma.blocks_per_seq > kFuseDecideBlocks) {
+        if (launch_decide_sample(dtype, da, sc.st) != hipSuccess) return SV_EHIP;
+        if (launch_sample(dtype, sc.vec, sc.trunc, B, nullptr, ma, sc.st) != hipSuccess) return SV_EHIP;
+    } else {
+        if (launch_sample(dtype, sc.vec, sc.trunc, B, &da, ma, sc.st) != hipSuccess) return SV_EHIP;
+    }
     return SV_OK;
 }
 
@@ -691,7 +705,7 @@ int spec_verify_sample_lazy(const void* target_logits, long long target_row_stri
     }
     const SampleArgs ma =
         sampler_args(target_logits, target_row_stride, draft_logits, draft_row_stride, B, k, V, sc, out_tokens);
-    if (launch_sample(dtype, sc.vec, false, B, ma, sc.st) != hipSuccess) return SV_EHIP;
+    if (launch_sample(dtype, sc.vec, false, B, nullptr, ma, sc.st) != hipSuccess) return SV_EHIP;
     return SV_OK;
 }
 

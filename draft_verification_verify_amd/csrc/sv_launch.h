@@ -186,10 +186,13 @@ struct LazyArgs {
 
 hipError_t launch_softmax_stats(int dt, bool vec, const StatsArgs& a, hipStream_t st);
 hipError_t launch_argmax_stats(int dt, bool vec, const StatsArgs& a, hipStream_t st);
-hipError_t launch_decide_sample(int dt, const DecideSampleArgs& a, hipStream_t st);
 hipError_t launch_decide_greedy(const DecideGreedyArgs& a, hipStream_t st);
 hipError_t launch_decide_candidates(const DecideCandArgs& a, hipStream_t st);
-hipError_t launch_sample(int dt, bool vec, bool mask, int B, const SampleArgs& a, hipStream_t st);
+hipError_t launch_decide_sample(int dt, const DecideSampleArgs& a, hipStream_t st);
+// The round's draw, after a decision kernel (da null) or deciding the round
+// in the same launch as the chunk pass (da given).
+hipError_t launch_sample(int dt, bool vec, bool mask, int B, const DecideSampleArgs* da, const SampleArgs& a,
+                         hipStream_t st);
 hipError_t launch_trunc_rows(int dt, bool vec, const TruncArgs& a, hipStream_t st);
 hipError_t launch_lazy_stats(int dt, bool vec, bool soft, int grid, const LazyArgs& a, hipStream_t st);
 hipError_t launch_lazy_decide_sample(int dt, const LazyArgs& l, const DecideSampleArgs& a, hipStream_t st);

@@ -7,10 +7,13 @@
 // in ascending index order: the smallest token whose cumulative weight
 // exceeds u times the total.
 //
-// Two kernels, so that no workgroup waits on another inside a launch:
-//  - k_sample_chunks streams the sampled row (pair) of every sequence once and
-//    writes the total weight of each chunk (a whole number of rounds of kBlock
-//    logical vectors), several rounds' loads in flight per thread;
+// Two launches, so that no workgroup waits on another inside a launch:
+//  - k_decide_chunks decides the round (every workgroup of a sequence decides
+//    it alike) and streams the sampled row (pair) of every sequence once,
+//    writing the total weight of each chunk (a whole number of rounds of
+//    kBlock logical vectors), several rounds' loads in flight per thread;
+//    after the early-exit decision kernels, k_sample_chunks does the same
+//    from their descriptors;
 //  - k_sample_pick, one workgroup per sequence, accumulates the chunk totals
 //    in chunk order, finds the chunk where u * total is crossed, rescans only
 //    that chunk and resolves the token with a workgroup prefix scan.
@@ -18,7 +21,7 @@
 // is the sequential sum of its rounds' totals, so the two kernels agree bit
 // for bit; every reduction runs in a fixed order, so draws are deterministic.
 
-#include "sv_device.h"
+#include "sv_rule.h"
 
 namespace sv {
 
@@ -198,14 +201,14 @@ __device__ __forceinline__ bool desc_ok(const SampleArgs& a, const SampleDesc& d
     return true;
 }
 
+// Chunk totals of workgroup (b, g), which covers chunks [g * chunks_per_block,
+// ...) of sequence b's sampled row (pair) as descriptor d names it.  Called by
+// every thread of the workgroup.
 template <int DT, bool VEC, bool MASK>
-__global__ __launch_bounds__(kBlock) void k_sample_chunks(SampleArgs a)
+__device__ __forceinline__ void chunk_totals(const SampleArgs& a, int b, int g, const SampleDesc d,
+                                             float* lds)
 {
-    __shared__ float lds[kWaves];
     constexpr int ES = DT == DT_F32 ? 4 : 2;
-    const int b = blockIdx.x / a.blocks_per_seq;
-    const int g = blockIdx.x - b * a.blocks_per_seq;
-    const SampleDesc d = a.desc[b];
     const int ch0 = g * a.chunks_per_block;
     const int ch1 = min(ch0 + a.chunks_per_block, a.nchunks);
     if (ch0 >= ch1 || !desc_ok(a, d)) return;     // uniform across the workgroup
@@ -260,6 +263,42 @@ __global__ __launch_bounds__(kBlock) void k_sample_chunks(SampleArgs a)
             }
         }
     }
+}
+
+// The chunk pass after a separate decision (early exit): the descriptor
+// comes from the decision kernels.
+template <int DT, bool VEC, bool MASK>
+__global__ __launch_bounds__(kBlock) void k_sample_chunks(SampleArgs a)
+{
+    __shared__ float lds[kWaves];
+    const int b = blockIdx.x / a.blocks_per_seq;
+    const int g = blockIdx.x - b * a.blocks_per_seq;
+    const SampleDesc d = a.desc[b];               // once, into registers
+    chunk_totals<DT, VEC, MASK>(a, b, g, d, lds);
+}
+
+// The decision and the chunk pass in one launch: wave 0 of every workgroup
+// of sequence b decides the whole round (decide_sequence), the same
+// computation on the same inputs in each, so all agree bit for bit on the
+// draw's row and weights; workgroup 0 also writes the round's outputs and
+// the descriptor the draw reads.  Removes a dependent launch, for the price
+// of reading the sequence's row statistics (a few hundred bytes) once per
+// workgroup.  MASK: truncated rows.
+template <int DT, bool VEC, bool MASK>
+__global__ __launch_bounds__(kBlock) void k_decide_chunks(DecideSampleArgs da, SampleArgs a)
+{
+    __shared__ float lds[kWaves];
+    __shared__ SampleDesc s_desc;
+    const int b = blockIdx.x / a.blocks_per_seq;
+    const int g = blockIdx.x - b * a.blocks_per_seq;
+    if (threadIdx.x < 64) {
+        SampleDesc d;
+        const int j = decide_sequence<DT, MASK>(da, b, g == 0, &d);
+        if ((int)threadIdx.x == j) s_desc = d;
+    }
+    __syncthreads();
+    const SampleDesc d = s_desc;
+    chunk_totals<DT, VEC, MASK>(a, b, g, d, lds);
 }
 
 // The draw: one workgroup per sequence.
@@ -332,30 +371,44 @@ __global__ __launch_bounds__(kBlock) void k_sample_pick(SampleArgs a)
     }
 }
 
+// The chunk pass, by k_decide_chunks when `da` is given (and then deciding
+// the round too) or by k_sample_chunks after a separate decision, then the
+// draw.
 template <int DT, bool VEC, bool MASK>
-static hipError_t launch_pair(int B, const SampleArgs& a, hipStream_t st)
+static hipError_t launch_pair(int B, const DecideSampleArgs* da, const SampleArgs& a, hipStream_t st)
 {
-    void* args[] = {const_cast<SampleArgs*>(&a)};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(k_sample_chunks<DT, VEC, MASK>),
-                                   dim3((unsigned)((long long)B * a.blocks_per_seq)), dim3(kBlock), args, 0, st);
+    const dim3 grid((unsigned)((long long)B * a.blocks_per_seq));
+    hipError_t e;
+    if (da) {
+        void* args[] = {const_cast<DecideSampleArgs*>(da), const_cast<SampleArgs*>(&a)};
+        e = hipLaunchKernel(reinterpret_cast<const void*>(k_decide_chunks<DT, VEC, MASK>), grid, dim3(kBlock),
+                            args, 0, st);
+    } else {
+        void* args[] = {const_cast<SampleArgs*>(&a)};
+        e = hipLaunchKernel(reinterpret_cast<const void*>(k_sample_chunks<DT, VEC, MASK>), grid, dim3(kBlock),
+                            args, 0, st);
+    }
     if (e != hipSuccess) return e;
+    void* args[] = {const_cast<SampleArgs*>(&a)};
     return hipLaunchKernel(reinterpret_cast<const void*>(k_sample_pick<DT, VEC, MASK>), dim3((unsigned)B),
                            dim3(kBlock), args, 0, st);
 }
 
 template <int DT>
-static hipError_t launch_dt(bool vec, bool mask, int B, const SampleArgs& a, hipStream_t st)
+static hipError_t launch_dt(bool vec, bool mask, int B, const DecideSampleArgs* da, const SampleArgs& a,
+                            hipStream_t st)
 {
-    if (mask) return vec ? launch_pair<DT, true, true>(B, a, st) : launch_pair<DT, false, true>(B, a, st);
-    return vec ? launch_pair<DT, true, false>(B, a, st) : launch_pair<DT, false, false>(B, a, st);
+    if (mask) return vec ? launch_pair<DT, true, true>(B, da, a, st) : launch_pair<DT, false, true>(B, da, a, st);
+    return vec ? launch_pair<DT, true, false>(B, da, a, st) : launch_pair<DT, false, false>(B, da, a, st);
 }
 
-hipError_t launch_sample(int dt, bool vec, bool mask, int B, const SampleArgs& a, hipStream_t st)
+hipError_t launch_sample(int dt, bool vec, bool mask, int B, const DecideSampleArgs* da, const SampleArgs& a,
+                         hipStream_t st)
 {
     switch (dt) {
-    case DT_F32: return launch_dt<DT_F32>(vec, mask, B, a, st);
-    case DT_F16: return launch_dt<DT_F16>(vec, mask, B, a, st);
-    default:     return launch_dt<DT_BF16>(vec, mask, B, a, st);
+    case DT_F32: return launch_dt<DT_F32>(vec, mask, B, da, a, st);
+    case DT_F16: return launch_dt<DT_F16>(vec, mask, B, da, a, st);
+    default:     return launch_dt<DT_BF16>(vec, mask, B, da, a, st);
     }
 }
 

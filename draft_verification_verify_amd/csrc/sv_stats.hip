@@ -89,6 +89,36 @@ __device__ __forceinline__ int last_round(const char* rp, int v, int vend, float
     return n;
 }
 
+// A thread's last (at most eight) vectors of a slice, v + j kSB (j < 8) below
+// vend, all loaded before any is reduced, so that a slice of two rounds per
+// thread costs one memory round trip rather than two.  They are reduced in
+// two groups of four, as two rounds would be (the same groups, so the same
+// result bit for bit); loads past vend are clamped to vend - 1 and read as
+// -inf.  A group with nothing below vend leaves (m, s) exactly as they were
+// (s * 1 + 0), so the second group is reduced without a branch, which would
+// let the compiler issue its loads only after the first group's arithmetic.
+template <int DT, bool VEC>
+__device__ __forceinline__ void last_rounds_soft(const char* rp, int v, int vend, float c, float& m, float& s)
+{
+    const int last = vend - 1;
+    Raw<DT> r[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = load_raw<DT, VEC>(rp, min(v + j * kSB, last));
+    __builtin_amdgcn_sched_barrier(0);             // all eight loads issue before the arithmetic
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float e[4 * kVec];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            decode<DT>(r[4 * h + q], e + kVec * q);
+            const bool ok = v + (4 * h + q) * kSB < vend;
+#pragma unroll
+            for (int t = 0; t < kVec; ++t) e[kVec * q + t] = ok ? e[kVec * q + t] : -INFINITY;
+        }
+        soft_update<4 * kVec>(e, m, s, c);
+    }
+}
+
 // The thread that takes a row's partial last vector (V not a multiple of 8)
 // when it falls in slice [v0, v1): the one whose vectors v0 + tid + n kSB reach it.
 __device__ __forceinline__ bool takes_partial(int v0, int v1, int nfull)
@@ -107,7 +137,7 @@ __device__ __forceinline__ SoftPartial slice_softmax(const char* rp, int v0, int
     const int vend = min(v1, nfull);
     float m = -INFINITY, s = 0.f;
     int v = v0 + (int)threadIdx.x;
-    for (; v + 3 * kSB < vend; v += 4 * kSB) {
+    for (; v + 8 * kSB < vend; v += 4 * kSB) {   // while more than eight vectors remain per thread
         Raw<DT> r0 = load_raw<DT, VEC>(rp, v);
         Raw<DT> r1 = load_raw<DT, VEC>(rp, v + kSB);
         Raw<DT> r2 = load_raw<DT, VEC>(rp, v + 2 * kSB);
@@ -119,7 +149,11 @@ __device__ __forceinline__ SoftPartial slice_softmax(const char* rp, int v0, int
         decode<DT>(r3, e + 24);
         soft_update<4 * kVec>(e, m, s, c);
     }
-    if (v < vend) {
+    // at most eight vectors left per thread: more than four (for thread 0,
+    // which has the most) are loaded together; four or fewer as one round
+    if (vend - (v - (int)threadIdx.x) > 4 * kSB) {
+        last_rounds_soft<DT, VEC>(rp, v, vend, c, m, s);
+    } else if (v < vend) {
         float e[4 * kVec];
         last_round<DT, VEC>(rp, v, vend, e);
         soft_update<4 * kVec>(e, m, s, c);
