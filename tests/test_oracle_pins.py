@@ -323,6 +323,89 @@ def test_histogram_catches_planted_mistakes(mutation):
     assert min(pvals) < 1e-6, pvals
 
 
+def softmax64(v, T=1.0):
+    a = np.asarray(v, np.float64) / T
+    e = np.exp(a - a.max())
+    return e / e.sum()
+
+
+def merged_gof_pvalue(tokens, p, min_expected=20.0):
+    """Chi-square goodness of fit of `tokens` against the distribution p, the
+    tokens taken in descending order of p and merged into bins whose expected
+    count reaches `min_expected` (the rest joins the last bin)."""
+    n = tokens.size
+    counts = np.bincount(tokens, minlength=p.size).astype(np.float64)
+    order = np.argsort(-p, kind="stable")
+    obs, exp_ = [], []
+    o = e = 0.0
+    for t in order:
+        o += counts[t]
+        e += n * p[t]
+        if e >= min_expected:
+            obs.append(o)
+            exp_.append(e)
+            o = e = 0.0
+    obs[-1] += o
+    exp_[-1] += e
+    obs, exp_ = np.array(obs), np.array(exp_)
+    stat = ((obs - exp_) ** 2 / exp_).sum()
+    return scipy.stats.chi2.sf(stat, obs.size - 1)
+
+
+def histogram_experiment_workload1_shape(mutation, n, seed=31, chunk=128):
+    """Rounds at workload 1's shape (k = 4, V = 32000, target logits N(0, var
+    2), draft = target + N(0, var 1), T = 1): the draft tokens drawn from q
+    (numpy's sampler), uniforms on the 2^-24 grid, the oracle run on 8
+    threads.  Returns the p-values, at positions 0, 1 and k, of the
+    committed tokens (rounds that reach the position) against direct draws
+    from p (two-sample) and against p itself (goodness of fit), and the
+    accepted counts."""
+    import concurrent.futures
+    V, k, T = 32000, 4, 1.0
+    rng = np.random.default_rng(seed)
+    z = rng.normal(0.0, np.sqrt(2.0), (k + 1, V)).astype(np.float32)
+    y = (z[:k] + rng.normal(0.0, 1.0, (k, V))).astype(np.float32)
+    p = [softmax64(z[i], T) for i in range(k + 1)]
+    q = [softmax64(y[i], T) for i in range(k)]
+    x = np.stack([rng.choice(V, size=n, p=q[i]) for i in range(k)], axis=1).astype(np.int32)
+    u = u24(rng, (n, k + 1))
+
+    def run(s0):
+        m = min(chunk, n - s0)
+        return oracle.sample(np.broadcast_to(z, (m, k + 1, V)).copy(), np.broadcast_to(y, (m, k, V)).copy(),
+                             x[s0:s0 + m], u[s0:s0 + m], T, mutation=mutation)
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        parts = list(ex.map(run, range(0, n, chunk)))
+    toks = np.concatenate([t for t, _ in parts])
+    nas = np.concatenate([a for _, a in parts])
+    pvals = []
+    for i in (0, 1, k):
+        got = toks[nas >= i, i]
+        direct = rng.choice(V, size=got.size, p=p[i])      # without speculation
+        pvals.append(merged_two_sample_pvalue(got, direct, V))
+        pvals.append(merged_gof_pvalue(got, p[i]))
+    return pvals, nas
+
+
+def test_histogram_at_the_workload_1_shape():
+    """The Blog's advice (compare token histograms with and without
+    speculation) at workload 1's vocabulary of 32000: 32000 rounds, the
+    committed token at positions 0, 1 and k against direct draws from the
+    target's p and against p itself, bins merged to expected counts of at
+    least 20."""
+    pvals, nas = histogram_experiment_workload1_shape(oracle.MUT_NONE, n=32_000)
+    assert (nas == 4).sum() > 3000          # the bonus position is reached often enough
+    assert min(pvals) > 1e-4, pvals
+
+
+@pytest.mark.parametrize("mutation", [oracle.MUT_RESIDUAL_IS_P, oracle.MUT_RESIDUAL_IS_Q,
+                                      oracle.MUT_BONUS_FROM_Q, oracle.MUT_RESIDUAL_SIGN])
+def test_histogram_at_the_workload_1_shape_catches_planted_mistakes(mutation):
+    pvals, _ = histogram_experiment_workload1_shape(mutation, n=12_000)
+    assert min(pvals) < 1e-6, pvals
+
+
 # ---------------------------------------------------------------------------
 # Special cases
 # ---------------------------------------------------------------------------
