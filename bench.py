@@ -94,6 +94,7 @@ CHAIN_MODES = ("sample", "greedy", "greedy_ext", "lenient", "sample_lazy", "gree
 CAND_MODES = ("candidates", "candidates_ext", "tree")
 MALL_DEFEAT_BYTES = 1 << 30            # inputs rotated over at least this many bytes (MALL: 256 MB)
 CPU_SHARE = 16                         # host CPUs the GPU machine gives one GPU's job
+CEILING_VECS = (1024, 2048, 4096, 8192)  # workgroup sizes (16-byte vectors) of the plain streaming read
 
 
 def main():
@@ -130,9 +131,10 @@ def main():
                     help="draft tokens of chain workloads: sampled from the draft rows, or the "
                          "draft's argmax (greedy drafting); auto: argmax for greedy modes on "
                          "workload 3, sampled otherwise")
-    ap.add_argument("--ceiling-vec", type=int, default=4096,
+    ap.add_argument("--ceiling-vec", type=int, default=-1,
                     help="16-byte vectors per workgroup of the plain streaming read that gives "
-                         "the device's achievable read rate (roofline.ceiling); 0 skips it")
+                         "the device's achievable read rate (roofline.ceiling): -1 takes the best "
+                         "of 1024, 2048, 4096 and 8192, 0 skips it")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (scale for the rocprofv3 byte counters)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -370,14 +372,15 @@ def main():
     # same buffers (the same input sets, rotated the same way), one launch
     # over each call's logits
     ceiling = None
-    if args.ceiling_vec > 0:
+    if args.ceiling_vec != 0:
         if args.mode == "tree":
             bufs = [(nodes, None) for nodes, _ in trees]
         elif cand or stream_rows != 2 * cfg0.k + 1:
             bufs = [(x.target, None) for x in slices]
         else:
             bufs = [(x.target, x.draft) for x in slices]
-        ceiling = stream_ceiling(bufs, max(args.steps, 20), args.ceiling_vec)
+        vecs = CEILING_VECS if args.ceiling_vec < 0 else (args.ceiling_vec,)
+        ceiling = stream_ceiling(bufs, max(args.steps, 20), vecs)
     kernel_name = {"sample": "k_softmax_stats", "lenient": "k_softmax_stats",
                    "truncated": "k_trunc16" if es == 2 else "k_trunc_rows"}.get(args.mode, "k_argmax_stats")
     traffic = measured_traffic(kernel_name, cid) \
@@ -501,11 +504,12 @@ def lazy_streamed_rows(num_accepted, k, sampling):
     return stats, draw
 
 
-def stream_ceiling(bufs, calls, vec_per_block):
+def stream_ceiling(bufs, calls, vecs):
     """GB/s of a plain 16-byte non-temporal streaming read (libsvceiling.so)
     over `bufs` [(a, b or None), ...] device tensors, one launch per entry,
-    rotated like the calls; averaged over `calls` launches between two
-    events, after a few untimed ones."""
+    rotated like the calls: for each workgroup size in `vecs` (16-byte
+    vectors per workgroup), `calls` launches between two events after a few
+    untimed ones; the best size gives the ceiling."""
     import ctypes
 
     import torch
@@ -522,31 +526,36 @@ def stream_ceiling(bufs, calls, vec_per_block):
     def nbytes(t):
         return 0 if t is None else t.numel() * t.element_size()
 
-    blocks = max(L.sv_stream_read_blocks(nbytes(a), nbytes(b), vec_per_block) for a, b in bufs)
+    blocks = max(L.sv_stream_read_blocks(nbytes(a), nbytes(b), v) for a, b in bufs for v in vecs)
     sink = torch.zeros(blocks, dtype=torch.int32, device="cuda:0")
     st = torch.cuda.current_stream().cuda_stream
+    per = statistics.fmean(nbytes(a) + nbytes(b) for a, b in bufs)
 
-    def launch(i):
+    def launch(i, vec):
         a, b = bufs[i % len(bufs)]
         rc = L.sv_stream_read(a.data_ptr(), nbytes(a), None if b is None else b.data_ptr(), nbytes(b),
-                              vec_per_block, sink.data_ptr(), blocks, st)
+                              vec, sink.data_ptr(), blocks, st)
         if rc != 0:
             raise RuntimeError(f"sv_stream_read failed: {rc}")
 
-    for i in range(5):
-        launch(i)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for i in range(calls):
-        launch(5 + i)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / calls
-    per = statistics.fmean(nbytes(a) + nbytes(b) for a, b in bufs)
-    return {"GBps": per / (ms / 1e3) / 1e9, "ms_per_launch": ms, "bytes_per_launch": per,
-            "launches": calls, "vec_per_block": vec_per_block, "kernel": "k_stream_read"}
+    runs = {}
+    for vec in vecs:
+        for i in range(5):
+            launch(i, vec)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(calls):
+            launch(5 + i, vec)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / calls
+        runs[vec] = {"GBps": per / (ms / 1e3) / 1e9, "ms_per_launch": ms}
+    best = max(runs, key=lambda v: runs[v]["GBps"])
+    return {"GBps": runs[best]["GBps"], "ms_per_launch": runs[best]["ms_per_launch"], "bytes_per_launch": per,
+            "launches": calls, "vec_per_block": best, "kernel": "k_stream_read",
+            "GBps_by_vec_per_block": {str(v): runs[v]["GBps"] for v in vecs}}
 
 
 def cpu_baseline(w, out_t, out_n, budget_s):
