@@ -36,6 +36,9 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "verified positions/sec (B·(k+1) rows/s) and achieved HBM GB/s vs peak"
 STATS_SOURCES = ["sv_stats.hip", "sv_device.h", "sv_launch.h"]
 STREAM_KERNELS = ("k_softmax_stats", "k_argmax_stats")
+# 16-bit rows under a top-k of at most this take the candidate-list pass
+# (k_topk16); larger or no top-k, the 65536-bin histogram pass (k_trunc16)
+TOPK_ONE_PASS_MAX = 256
 
 
 def traffic_file(kernel: str, cid: int) -> str:
@@ -381,8 +384,9 @@ def main():
             bufs = [(x.target, x.draft) for x in slices]
         vecs = CEILING_VECS if args.ceiling_vec < 0 else (args.ceiling_vec,)
         ceiling = stream_ceiling(bufs, max(args.steps, 20), vecs)
+    one_pass = "k_topk16" if 1 <= args.top_k <= TOPK_ONE_PASS_MAX and args.top_k < V else "k_trunc16"
     kernel_name = {"sample": "k_softmax_stats", "lenient": "k_softmax_stats",
-                   "truncated": "k_trunc16" if es == 2 else "k_trunc_rows"}.get(args.mode, "k_argmax_stats")
+                   "truncated": one_pass if es == 2 else "k_trunc_rows"}.get(args.mode, "k_argmax_stats")
     traffic = measured_traffic(kernel_name, cid) \
         if (kernel_name in STREAM_KERNELS and args.vocab_shard == 1 and args.mode != "tree"
             and not lazy) else None
@@ -434,7 +438,11 @@ def main():
             "full_pass_bytes_per_call": stats_bytes,
         } if lazy else {
             "kernel": kernel_name,
-            "note": (("the timed launch is k_trunc16 (one pass per 16-bit row: an exact LDS "
+            "note": (("the timed launch is k_topk16 (one pass per 16-bit row: per-wave lists "
+                      "of the candidates above a rising floor) followed by k_trunc_rows over "
+                      "the rows it marked; algorithmic bytes: every row read once")
+                     if es == 2 and one_pass == "k_topk16" else
+                     ("the timed launch is k_trunc16 (one pass per 16-bit row: an exact LDS "
                       "histogram of all 65536 bit patterns) followed by k_trunc_rows over the "
                       "rows it marked; algorithmic bytes: every row read once") if es == 2 else
                      ("the timed launch is k_trunc_rows (radix selection, one workgroup per "

@@ -915,6 +915,438 @@ __global__ __launch_bounds__(kT16) void k_trunc16(TruncArgs a)
     flush();
 }
 
+// ---- one pass for 16-bit logits under a small top-k -------------------------
+// With top-k on, only the top_k largest logits (with the ties at the
+// boundary) can be kept, so for top_k <= kTopkMax a row needs no histogram of
+// every pattern.  One 256-thread workgroup takes one row; each wave keeps, in
+// LDS, a list of the 32-bit words (two logits each) it has streamed that may
+// still hold a kept logit, and a floor F: the list holds every word with a
+// logit whose key is at least F.  When a lane's part of the list fills up, the
+// wave raises F to the (top_k + 1)-th largest key at or above F in its list
+// (that many logits of the row are at least as large, so F never passes the
+// row's top_k-th largest key, and the row has more than top_k finite logits)
+// and drops the words with nothing left above it.  F starts just above -inf,
+// so an -inf logit never counts.
+//
+// After the stream the workgroup merges its waves' lists above the largest
+// floor Fg: the top_k-th largest key among them is the row's; if no wave
+// raised its floor the lists hold every finite logit and top-k is off when
+// they number at most top_k (as in k_trunc16).  The row max is the largest
+// key.  The kept keys (at most kKeptMax, else the row goes to the radix
+// kernel) are gathered, and top-p runs on their fixed-point masses.  Both
+// searches are radix selections on the 16-bit key, high byte then low byte,
+// over a 256-bin histogram, and every count, mass and threshold equals
+// k_trunc16's.  A wave whose list still overflows after raising F (more than
+// 64 * (kSlots - 8) words tied at the floor) marks the row for the radix
+// kernel too.
+//
+// Keys here are key_of's with -0.0 merged into +0.0 and every negative value
+// one higher (word_keys: both halves of a word in four operations); tau is
+// converted back when written.  The stream compares raw bits: per half,
+// s ^ ((s >> 15) & 0x7FFF) of the 16-bit pattern s, read as a signed
+// integer, is the key minus 0x8000 (minus one more for negative values), and
+// both halves of a word are compared at once as 32-bit integers.
+
+constexpr int kTK = 256;               // threads per workgroup
+constexpr int kTKW = kTK / 64;
+constexpr int kSlots = 16;             // list words per lane
+constexpr int kTopkMax = 256;
+constexpr int kKeptMax = 512;          // kept keys gathered after top-k
+
+struct TopkShared {
+    uint32_t list[kTKW * kSlots * 64];  // wave w, lane l, word j: [w][j * 64 + l]
+    uint32_t whist[kTKW * 256];         // each wave's radix histogram; after the stream, the kept keys
+    u64 hist[256];                      // the workgroup's: counts (low 1 KB) or masses
+    u64 red[kTKW];
+    uint32_t mx[kTKW];
+    uint32_t F[kTKW];
+    uint32_t over[kTKW];
+    uint32_t nk;
+    uint32_t sel;
+    uint32_t total;
+    u64 above;
+    u64 incl;
+};
+
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// The keys of the two logits of a word, low half in the low 16 bits: key_of,
+// -0.0 merged into +0.0 and negative values one up (an order-preserving map).
+__device__ __forceinline__ uint32_t word_keys(uint32_t x)
+{
+    const uint32_t m = __builtin_bit_cast(uint32_t, __builtin_bit_cast(s16x2, x) >> (short)15);
+    const uint32_t v = x ^ (m | 0x80008000u);
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, v) + __builtin_bit_cast(u16x2, m & 0x00010001u));
+}
+
+// word_keys' key back to key_of's, and to the value
+__device__ __forceinline__ uint32_t std_key(uint32_t k)
+{
+    return k >= 0x8000u ? k : k - 1u;
+}
+
+template <int DT>
+__device__ __forceinline__ float value_of_key(uint32_t k)
+{
+    return value_of_bits<DT>(k >= 0x8000u ? (k & 0x7FFFu) : (~(k - 1u) & 0xFFFFu));
+}
+
+// Orders this wave's LDS accesses: the hardware runs a wave's LDS
+// instructions in order; this keeps the compiler from moving them.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ uint32_t lane_prefix(unsigned long long bal)
+{
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+}
+
+// A 256-bin count histogram read from the top: its total, the bin at which
+// the count first reaches `need` (if the total does) and the count in the
+// bins above it, in every lane.  Lane l holds bins 255 - 4l down to 252 - 4l.
+__device__ __forceinline__ uint32_t find_desc_count(const uint32_t* h, uint32_t need, uint32_t& bin,
+                                                    uint32_t& above)
+{
+    const int lane = (int)threadIdx.x & 63;
+    const u32x4 q = reinterpret_cast<const u32x4*>(h)[63 - lane];
+    const uint32_t s = q.x + q.y + q.z + q.w;
+    const uint32_t incl = wave_scan_u32(s);
+    const unsigned long long hit = __ballot(incl >= need);
+    const int L = hit ? __ffsll((long long)hit) - 1 : 63;
+    const uint32_t acc = incl - s;
+    uint32_t b = 3u, a = acc + q.w + q.z + q.y;
+    if (acc + q.w >= need) { b = 0u; a = acc; }
+    else if (acc + q.w + q.z >= need) { b = 1u; a = acc + q.w; }
+    else if (acc + q.w + q.z + q.y >= need) { b = 2u; a = acc + q.w + q.z; }
+    bin = 255u - 4u * (uint32_t)L - (uint32_t)__builtin_amdgcn_readlane((int)b, L);
+    above = (uint32_t)__builtin_amdgcn_readlane((int)a, L);
+    return lane63_u32(incl);
+}
+
+// The same for a 256-bin mass histogram: the bin at which base plus the mass
+// from the top, as a double, first reaches `budget` (the total reaches it).
+__device__ __forceinline__ void find_desc_mass(const u64* h, u64 base, double budget, uint32_t& bin, u64& above)
+{
+    const int lane = (int)threadIdx.x & 63;
+    const u64 m0 = h[255 - 4 * lane], m1 = h[254 - 4 * lane], m2 = h[253 - 4 * lane], m3 = h[252 - 4 * lane];
+    const u64 s = m0 + m1 + m2 + m3;
+    const u64 incl = base + wave_scan_u64(s);
+    const unsigned long long hit = __ballot((double)incl >= budget);
+    const int L = hit ? __ffsll((long long)hit) - 1 : 63;
+    const u64 acc = incl - s;
+    uint32_t b = 3u;
+    u64 a = acc + m0 + m1 + m2;
+    if ((double)(acc + m0) >= budget) { b = 0u; a = acc; }
+    else if ((double)(acc + m0 + m1) >= budget) { b = 1u; a = acc + m0; }
+    else if ((double)(acc + m0 + m1 + m2) >= budget) { b = 2u; a = acc + m0 + m1; }
+    bin = 255u - 4u * (uint32_t)L - (uint32_t)__builtin_amdgcn_readlane((int)b, L);
+    above = readlane_u64(a, L);
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kTK) void k_topk16(TruncArgs a)
+{
+    __shared__ __attribute__((aligned(16))) TopkShared sh;
+    const int row = (int)blockIdx.x;
+    const int t = (int)threadIdx.x;
+    const int lane = t & 63, wv = t >> 6;
+    const char* rp = trunc_row_ptr<DT>(a, row);
+    const int V = a.V;
+    const int nfull = V >> 3;                                  // >= 1
+    const uint32_t K1 = (uint32_t)a.top_k + 1u;
+    const uint32_t f0 = (~ninf_bits<DT>() & 0xFFFFu) + 2u;      // just above -inf
+    uint32_t* const lst = sh.list + wv * (kSlots * 64);
+    uint32_t* const wh = sh.whist + wv * 256;
+    uint32_t* const hc = reinterpret_cast<uint32_t*>(sh.hist);
+    uint32_t F = f0;                   // the wave's floor (uniform)
+    // the stream's test: the signed form of each half shifted to the top of a
+    // 32-bit integer, against F's (one lower: negative values sit one lower
+    // there, and a positive one just below F entering is harmless)
+    auto test_of = [](uint32_t f) -> int {
+        return f > 0xFFFFu ? INT32_MAX : (int)((uint32_t)((int)f - 0x8001) << 16);
+    };
+    int T = test_of(F);
+    int c = 0;                         // this lane's words
+
+    // raise the floor and drop the words with nothing above it; all lanes, uniform
+    auto compact = [&]() {
+        const int cmax = wave_max_int(c);
+        uint32_t total = 0, b1 = 0, above = 0;
+#pragma unroll
+        for (int level = 0; level < 2; ++level) {
+            reinterpret_cast<u32x4*>(wh)[lane] = u32x4{0u, 0u, 0u, 0u};
+            wave_lds_sync();
+            for (int j = 0; j < c; ++j) {
+                const uint32_t u = word_keys(lst[j * 64 + lane]);
+                const uint32_t k0 = u & 0xFFFFu, k1 = u >> 16;
+                if (level == 0) {
+                    if (k0 >= F) atomicAdd(&wh[k0 >> 8], 1u);
+                    if (k1 >= F) atomicAdd(&wh[k1 >> 8], 1u);
+                } else {
+                    if (k0 >= F && (k0 >> 8) == b1) atomicAdd(&wh[k0 & 255u], 1u);
+                    if (k1 >= F && (k1 >> 8) == b1) atomicAdd(&wh[k1 & 255u], 1u);
+                }
+            }
+            wave_lds_sync();
+            uint32_t bin, ab;
+            const uint32_t tot = find_desc_count(wh, level == 0 ? K1 : K1 - above, bin, ab);
+            wave_lds_sync();
+            if (level == 0) {
+                total = tot;
+                if (total < K1) break; // uniform: too few keys to raise the floor
+                b1 = bin;
+                above = ab;
+            } else {
+                const uint32_t B = (b1 << 8) | bin;
+                F = B > F ? B : F;
+            }
+        }
+        uint32_t base = 0;
+        for (int j = 0; j < cmax; ++j) {
+            const uint32_t x = j < c ? lst[j * 64 + lane] : 0u;
+            const uint32_t u = word_keys(x);
+            const bool keep = j < c && ((u & 0xFFFFu) >= F || (u >> 16) >= F);
+            const unsigned long long bal = __ballot(keep);
+            if (keep) lst[base + lane_prefix(bal)] = x;   // at or below every unread word
+            base += (uint32_t)__popcll(bal);
+        }
+        wave_lds_sync();
+        if (base > 64u * (kSlots - 8)) {                  // tied at the floor: the radix kernel
+            if (lane == 0) sh.over[wv] = 1u;
+            F = 0x10000u;
+            c = 0;
+        } else {
+            c = base > (uint32_t)lane ? (int)((base - (uint32_t)lane + 63u) >> 6) : 0;
+        }
+        T = test_of(F);
+    };
+    auto take = [&](uint32_t x, bool ok) {                // a word: two 16-bit logits
+        const uint32_t sg = __builtin_bit_cast(uint32_t, __builtin_bit_cast(s16x2, x) >> (short)15);
+        const uint32_t sk = x ^ (sg & 0x7FFF7FFFu);
+        const bool in = ((int)sk >= T) || ((int)(sk << 16) >= T);
+        if (ok && in) {
+            lst[c * 64 + lane] = x;
+            ++c;
+        }
+    };
+    if (lane == 0) sh.over[wv] = 0u;
+    hc[t] = 0u;                        // the merge's first histogram (kTK == 256 bins)
+    if (t == 0) sh.nk = 0u;
+
+    // the stream: vector t + i * kTK at step i, in groups of four steps; two
+    // register buffers alternate, each reloading the group two ahead as soon
+    // as it is taken, so a group's loads are in flight while the one before
+    // it is taken.  Loads past the row (the last two groups' reloads among
+    // them) read its last full vector again and are not taken.
+    const int ngroups = 2 * ((nfull + 8 * kTK - 1) / (8 * kTK));   // even
+    auto issue = [&](Raw<DT> (&buf)[4], int g) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int v = t + (4 * g + u) * kTK;
+            buf[u] = load_raw<DT, VEC>(rp, v < nfull ? v : nfull - 1);
+        }
+    };
+    auto take_group = [&](const Raw<DT> (&buf)[4], int g) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if ((u & 1) == 0 && __ballot(c > kSlots - 8)) compact();   // room for two vectors
+            const bool ok = t + (4 * g + u) * kTK < nfull;
+            take(buf[u].a.x, ok);
+            take(buf[u].a.y, ok);
+            take(buf[u].a.z, ok);
+            take(buf[u].a.w, ok);
+        }
+    };
+    Raw<DT> bufA[4], bufB[4];
+    issue(bufA, 0);
+    issue(bufB, 1);
+    for (int g = 0; g < ngroups; g += 2) {
+        take_group(bufA, g);
+        issue(bufA, g + 2);            // unconditional: each group waits for its own loads only
+        take_group(bufB, g + 1);
+        issue(bufB, g + 3);
+    }
+    if (__ballot(c > kSlots - 8)) compact();
+    if (t == 0) {                      // the partial last vector: a word per logit, -inf above it
+        const unsigned short* e = reinterpret_cast<const unsigned short*>(rp) + 8LL * nfull;
+        for (int j = 0; j < V - 8 * nfull; ++j) take((uint32_t)e[j] | (ninf_bits<DT>() << 16), true);
+    }
+    if (lane == 0) sh.F[wv] = F;
+    __syncthreads();
+
+    uint32_t Fg = sh.F[0];
+    uint32_t over = sh.over[0];
+#pragma unroll
+    for (int w = 1; w < kTKW; ++w) {
+        Fg = sh.F[w] > Fg ? sh.F[w] : Fg;
+        over |= sh.over[w];
+    }
+    if (over) {
+        if (t == 0) a.rows[row] = TruncRow{0.f, 0.f, 0u, 1u};
+        return;
+    }
+
+    // the keys at or above Fg: a histogram of their high bytes (its total is
+    // their number) and the largest
+    {
+        uint32_t mx_t = 0;
+        const int cmax = wave_max_int(c);
+        for (int j = 0; j < cmax; ++j) {
+            const uint32_t u = j < c ? word_keys(lst[j * 64 + lane]) : 0u;
+            const uint32_t k0 = u & 0xFFFFu, k1 = u >> 16;
+            if (k0 >= Fg) atomicAdd(&hc[k0 >> 8], 1u);
+            if (k1 >= Fg) atomicAdd(&hc[k1 >> 8], 1u);
+            mx_t = k0 >= Fg && k0 > mx_t ? k0 : mx_t;
+            mx_t = k1 >= Fg && k1 > mx_t ? k1 : mx_t;
+        }
+        const uint32_t mx = (uint32_t)wave_max_int((int)mx_t);
+        if (lane == 0) sh.mx[wv] = mx;
+    }
+    __syncthreads();
+    if (wv == 0) {
+        uint32_t bin, above;
+        const uint32_t total = find_desc_count(hc, (uint32_t)a.top_k, bin, above);
+        if (lane == 0) {
+            sh.total = total;
+            sh.sel = bin;
+            sh.above = above;
+        }
+    }
+    __syncthreads();
+    const uint32_t nU = sh.total;
+    if (nU == 0u) {                    // every logit -inf
+        if (t == 0) a.rows[row] = TruncRow{-INFINITY, -INFINITY, 0u, 0u};
+        return;
+    }
+    uint32_t mxk = sh.mx[0];
+#pragma unroll
+    for (int w = 1; w < kTKW; ++w) mxk = sh.mx[w] > mxk ? sh.mx[w] : mxk;
+
+    // top-k: the top_k-th largest key at or above Fg, its low byte from a
+    // second histogram over the keys with its high byte
+    uint32_t lo = Fg;                  // keys >= lo survive top-k
+    bool topk_on = Fg > f0 || (uint32_t)a.top_k < nU;
+    if (topk_on) {
+        const uint32_t b1 = sh.sel;
+        const uint32_t need = (uint32_t)a.top_k - (uint32_t)sh.above;
+        hc[t] = 0u;
+        __syncthreads();
+        for (int j = 0; j < c; ++j) {
+            const uint32_t u = word_keys(lst[j * 64 + lane]);
+            const uint32_t k0 = u & 0xFFFFu, k1 = u >> 16;
+            if (k0 >= Fg && (k0 >> 8) == b1) atomicAdd(&hc[k0 & 255u], 1u);
+            if (k1 >= Fg && (k1 >> 8) == b1) atomicAdd(&hc[k1 & 255u], 1u);
+        }
+        __syncthreads();
+        if (wv == 0) {
+            uint32_t bin, above;
+            find_desc_count(hc, need, bin, above);
+            if (lane == 0) sh.sel = bin;
+        }
+        __syncthreads();
+        lo = (b1 << 8) | sh.sel;
+    }
+
+    // gather the kept keys
+    uint32_t* const kk = sh.whist;
+    {
+        const int cmax = wave_max_int(c);
+        for (int j = 0; j < cmax; ++j) {
+            const uint32_t u = j < c ? word_keys(lst[j * 64 + lane]) : 0u;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t k = h == 0 ? (u & 0xFFFFu) : (u >> 16);
+                const bool keep = k >= lo;     // lo >= f0 > 0: empty slots never kept
+                const unsigned long long bal = __ballot(keep);
+                if (bal) {
+                    const int first = __ffsll((long long)bal) - 1;
+                    uint32_t base = 0;
+                    if (lane == first) base = atomicAdd(&sh.nk, (uint32_t)__popcll(bal));
+                    base = (uint32_t)__builtin_amdgcn_readlane((int)base, first);
+                    const uint32_t i = base + lane_prefix(bal);
+                    if (keep && i < (uint32_t)kKeptMax) kk[i] = k;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    const uint32_t nk = sh.nk;
+    if (nk > (uint32_t)kKeptMax) {     // a tie group too large to gather: the radix kernel
+        if (t == 0) a.rows[row] = TruncRow{0.f, 0.f, 0u, 1u};
+        return;
+    }
+
+    // the kept logits' masses, two keys per thread at most
+    const float m = value_of_key<DT>(mxk);
+    const float cc = a.c;
+    u64 f[2] = {0, 0};
+    uint32_t kt[2] = {0u, 0u};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int i = t + h * kTK;
+        if (i < (int)nk) {
+            kt[h] = kk[i];
+            f[h] = fixed40_nb(weight(value_of_key<DT>(kt[h]), m, cc));
+        }
+    }
+    {
+        const u64 s = lane63_u64(wave_scan_u64(f[0] + f[1]));
+        if (lane == 0) sh.red[wv] = s;
+    }
+    __syncthreads();
+    u64 M = 0;
+#pragma unroll
+    for (int w = 0; w < kTKW; ++w) M += sh.red[w];
+    u64 kept = M;
+    uint32_t tau = topk_on ? std_key(lo) : 0u;    // top-k off: every key
+
+    // top-p: the key at which the mass from the top first reaches top_p * M
+    if (a.top_p < 1.f) {
+        const double budget = (double)a.top_p * (double)M;
+        uint32_t hi = 0u;
+        u64 base = 0;
+#pragma unroll
+        for (int level = 0; level < 2; ++level) {
+            sh.hist[t] = 0;
+            __syncthreads();
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                if (f[h] && (level == 0 || (kt[h] >> 8) == hi))
+                    atomicAdd(&sh.hist[level == 0 ? kt[h] >> 8 : kt[h] & 255u], f[h]);
+            }
+            __syncthreads();
+            if (wv == 0) {
+                uint32_t bin;
+                u64 above;
+                find_desc_mass(sh.hist, base, budget, bin, above);
+                if (lane == 0) {
+                    sh.sel = bin;
+                    sh.above = above;                  // the mass of every larger key
+                    sh.incl = above + sh.hist[bin];    // and the bin's own
+                }
+            }
+            __syncthreads();
+            if (level == 0) {
+                hi = sh.sel;
+                base = sh.above;
+            } else {
+                hi = (hi << 8) | sh.sel;
+                kept = sh.incl;
+            }
+            __syncthreads();
+        }
+        tau = std_key(hi);
+    }
+    if (t == 0) {
+        const float l2s = (float)(log2((double)kept) - (double)kFixBits);
+        a.rows[row] = TruncRow{m, l2s, tau, 0u};
+    }
+}
+
 // The current device's compute units (queried once per device).
 int compute_units()
 {
@@ -948,13 +1380,21 @@ hipError_t launch_dt(bool vec, const TruncArgs& a, hipStream_t st)
                                 : reinterpret_cast<const void*>(k_trunc_rows<DT, false>);
             return hipLaunchKernel(g, dim3((unsigned)a.n_rows), dim3(kTB), args, 0, st);
         }
-        const void* f = vec ? reinterpret_cast<const void*>(k_trunc16<DT, true>)
-                            : reinterpret_cast<const void*>(k_trunc16<DT, false>);
-        const int cus = compute_units();
-        const unsigned g16 = (unsigned)(a.n_rows < cus ? a.n_rows : cus);   // one workgroup fills a CU's LDS
-        hipError_t e = hipLaunchKernel(f, dim3(g16), dim3(kT16), args, 0, st);
+        hipError_t e;
+        if (a.top_k >= 1 && a.top_k <= kTopkMax && a.top_k < a.V) {
+            const void* f = vec ? reinterpret_cast<const void*>(k_topk16<DT, true>)
+                                : reinterpret_cast<const void*>(k_topk16<DT, false>);
+            e = hipLaunchKernel(f, dim3((unsigned)a.n_rows), dim3(kTK), args, 0, st);
+        } else {
+            const void* f = vec ? reinterpret_cast<const void*>(k_trunc16<DT, true>)
+                                : reinterpret_cast<const void*>(k_trunc16<DT, false>);
+            const int cus = compute_units();
+            const unsigned g16 = (unsigned)(a.n_rows < cus ? a.n_rows : cus);   // one workgroup fills a CU's LDS
+            e = hipLaunchKernel(f, dim3(g16), dim3(kT16), args, 0, st);
+        }
         if (e != hipSuccess) return e;
-        // rows with 65536 or more equal finite logits
+        // rows with 65536 or more equal finite logits (k_trunc16), or too many
+        // tied at a list's floor (k_topk16)
         b.only_marked = 1;
         const void* g = vec ? reinterpret_cast<const void*>(k_trunc_rows<DT, true>)
                             : reinterpret_cast<const void*>(k_trunc_rows<DT, false>);

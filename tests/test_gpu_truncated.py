@@ -302,6 +302,77 @@ def test_truncated_many_equal_logits(sv, dtype):
         check(sv, w, 1.0, x, top_k, top_p)
 
 
+def small_top_k_rows(n, V, tdt, g):
+    """n rows of V logits, one pattern per row (row i: pattern i % 12): plain
+    normal; ascending and descending order (each new logit beats or trails
+    every earlier one, the worst and best order for a streamed floor); all
+    negative; 40 or 3 finite logits among -inf; 300 equal logits above the
+    rest; one constant; a boundary among +0.0 and -0.0; logits near the
+    format's largest magnitudes; every logit in a dozen values (ties
+    everywhere); normal with one far spike."""
+    big = 60000.0 if tdt == torch.float16 else 3.0e38
+    rows = []
+    for i in range(n):
+        p = i % 12
+        r = torch.randn((V,), generator=g, device=DEV)
+        if p == 1:
+            r = torch.sort(r).values
+        elif p == 2:
+            r = torch.sort(r, descending=True).values
+        elif p == 3:
+            r = r - 20.0
+        elif p in (4, 5):
+            keep = torch.randperm(V, generator=g, device=DEV)[:40 if p == 4 else 3]
+            r = torch.full((V,), -float("inf"), device=DEV).index_put((keep,), r[keep])
+        elif p == 6:
+            r[torch.randperm(V, generator=g, device=DEV)[:300]] = 9.0
+        elif p == 7:
+            r = torch.full((V,), 1.5, device=DEV)
+        elif p == 8:
+            r = -torch.rand((V,), generator=g, device=DEV) - 0.5
+            pos = torch.randperm(V, generator=g, device=DEV)
+            r[pos[:20]] = torch.rand((20,), generator=g, device=DEV) + 1.0
+            z = pos[20:20 + V // 3]
+            r[z] = torch.where(torch.rand(z.shape, generator=g, device=DEV) < 0.5, 0.0, -0.0)
+        elif p == 9:
+            r = torch.sign(r) * big * (1.0 - 0.01 * torch.rand((V,), generator=g, device=DEV))
+        elif p == 10:
+            r = torch.randint(-6, 6, (V,), generator=g, device=DEV).float() * 0.5
+        elif p == 11:
+            r[int(torch.randint(V, (1,), generator=g, device=DEV))] = 25.0
+        rows.append(r)
+    return torch.stack(rows).to(tdt)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("V", [3001, 32000])
+def test_truncated_small_top_k_equals_fp32(sv, dtype, V):
+    """Top-k up to 256 on 16-bit rows takes the one-pass candidate lists: on
+    rows built to stress them (small_top_k_rows), at every top-k from 1 to
+    256 (and 257, the histogram pass) and top-p from off to 1e-6, the result
+    must equal, bit for bit, that of the same rows upcast to fp32, which take
+    the radix passes; some settings are checked against the oracle too."""
+    g = torch.Generator(device=DEV).manual_seed(V)
+    tdt = synthetic.DTYPES[dtype]
+    B, k = 12, 3
+    z = small_top_k_rows(B * (k + 1), V, tdt, g).view(B, k + 1, V)
+    y = small_top_k_rows(B * k + 5, V, tdt, g)[5:].view(B, k, V)   # other patterns than z's rows
+    u = synthetic.uniforms24((B, k + 1), g, DEV)
+    tok = torch.randint(0, V, (B, k), generator=g, device=DEV, dtype=torch.int32)
+    for top_k in (1, 2, 5, 39, 40, 41, 50, 63, 64, 65, 255, 256, 257):
+        for top_p in (1.0, 0.9, 0.5, 1e-6):
+            a = sv.sample_truncated(z, y, tok, u, 0.8, top_k, top_p, return_probs=True)
+            b = sv.sample_truncated(z.float(), y.float(), tok, u, 0.8, top_k, top_p,
+                                    return_probs=True)
+            torch.cuda.synchronize()
+            for ta, tb in zip(a, b):
+                assert torch.equal(ta, tb), (top_k, top_p)
+    w = synthetic.Workload(synthetic.WORKLOADS[1], z, y, None, u, 0.8)
+    for top_k, top_p in ((3, 1.0), (40, 0.9), (256, 0.5)):
+        x = torch.from_numpy(truncated_drafts(f32(y), 0.8, top_k, top_p, 13)).to(DEV)
+        check(sv, w, 0.8, x, top_k, top_p)
+
+
 @pytest.mark.parametrize("V", [32767, 32768, 32769])
 def test_truncated_fp32_lds_boundary(sv, V):
     """fp32 rows of up to 32768 logits run the radix passes on an LDS copy,
