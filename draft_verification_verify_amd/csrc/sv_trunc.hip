@@ -11,9 +11,12 @@
 //   together.  Both keep a set {t : key(z_t) >= tau} for an ordering key
 //   (key_of), so a row is summarised by (m, tau, kept mass).
 //
-// Two kernels find tau and the kept mass:
-//  - k_trunc16 (fp16 / bf16 rows): one pass per row, an exact count of all
-//    65536 bit patterns in LDS, the thresholds read off the histogram;
+// Three kernels find tau and the kept mass:
+//  - k_topk16 (fp16 / bf16 rows under a top-k of at most 256): one pass per
+//    row keeping only the logits that can still be among the top_k largest,
+//    the thresholds found among those;
+//  - k_trunc16 (other fp16 / bf16 rows): one pass per row, an exact count of
+//    all 65536 bit patterns in LDS, the thresholds read off the histogram;
 //  - k_trunc_rows (fp32 rows, and the rare 16-bit row the histogram cannot
 //    hold): radix selection on the key, most significant digit first (11, 11
 //    and 10 bits for fp32 keys; 11 then 5 for 16-bit keys), one 512-thread
@@ -25,7 +28,8 @@
 // Masses are fixed-point integers (w * 2^40, truncated), summed with integer
 // atomics and integer reductions, so every result is independent of
 // scheduling and bitwise reproducible, and both kernels give the same
-// integers for the same row.
+// integers for the same row.  The three kernels agree bit for bit on every
+// row summary.
 
 #include "sv_device.h"
 
@@ -918,15 +922,18 @@ __global__ __launch_bounds__(kT16) void k_trunc16(TruncArgs a)
 // ---- one pass for 16-bit logits under a small top-k -------------------------
 // With top-k on, only the top_k largest logits (with the ties at the
 // boundary) can be kept, so for top_k <= kTopkMax a row needs no histogram of
-// every pattern.  One 256-thread workgroup takes one row; each wave keeps, in
-// LDS, a list of the 32-bit words (two logits each) it has streamed that may
-// still hold a kept logit, and a floor F: the list holds every word with a
-// logit whose key is at least F.  When a lane's part of the list fills up, the
-// wave raises F to the (top_k + 1)-th largest key at or above F in its list
-// (that many logits of the row are at least as large, so F never passes the
-// row's top_k-th largest key, and the row has more than top_k finite logits)
-// and drops the words with nothing left above it.  F starts just above -inf,
-// so an -inf logit never counts.
+// every pattern.  One 256-thread workgroup takes one row, eight to a CU (the
+// analysis of one row overlaps the streaming of the others); each wave keeps,
+// in LDS, a list of the 32-bit words (two logits each) it has streamed that
+// may still hold a kept logit, and a floor F: the list holds every word with
+// a logit whose key is at least F.  When a lane's part of the list fills up,
+// the wave raises F to the (top_k + 1)-th largest key at or above F in its
+// list (that many logits of the row are at least as large, so F never passes
+// the row's top_k-th largest key, and the row has more than top_k finite
+// logits) and drops the words with nothing left above it.  F starts just
+// above -inf, so an -inf logit never counts, or, for top_k < 64, at the
+// smallest of the wave's 64 lane maxima over its first vectors if positive
+// (64 different logits are at least that large).
 //
 // After the stream the workgroup merges its waves' lists above the largest
 // floor Fg: the top_k-th largest key among them is the row's; if no wave
@@ -937,19 +944,22 @@ __global__ __launch_bounds__(kT16) void k_trunc16(TruncArgs a)
 // searches are radix selections on the 16-bit key, high byte then low byte,
 // over a 256-bin histogram, and every count, mass and threshold equals
 // k_trunc16's.  A wave whose list still overflows after raising F (more than
-// 64 * (kSlots - 8) words tied at the floor) marks the row for the radix
+// 64 * (kSlots - 4) words tied at the floor) marks the row for the radix
 // kernel too.
 //
 // Keys here are key_of's with -0.0 merged into +0.0 and every negative value
 // one higher (word_keys: both halves of a word in four operations); tau is
-// converted back when written.  The stream compares raw bits: per half,
-// s ^ ((s >> 15) & 0x7FFF) of the 16-bit pattern s, read as a signed
-// integer, is the key minus 0x8000 (minus one more for negative values), and
-// both halves of a word are compared at once as 32-bit integers.
+// converted back when written.  The stream tests raw bits, two operations a
+// word: above a positive floor F only positive logits can count, and their
+// 16-bit patterns, read as signed integers, are their keys minus 0x8000, so
+// a word may hold one iff the larger of its halves is at least F - 0x8000;
+// at or below +0.0, every positive logit counts and a negative pattern's key
+// falls as the pattern, read unsigned, grows, so a word may hold one iff the
+// smaller of its halves, read unsigned, is at most 0x10000 - F.
 
 constexpr int kTK = 256;               // threads per workgroup
 constexpr int kTKW = kTK / 64;
-constexpr int kSlots = 16;             // list words per lane
+constexpr int kSlots = 12;             // list words per lane
 constexpr int kTopkMax = 256;
 constexpr int kKeptMax = 512;          // kept keys gathered after top-k
 
@@ -1048,7 +1058,7 @@ __device__ __forceinline__ void find_desc_mass(const u64* h, u64 base, double bu
 }
 
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kTK) void k_topk16(TruncArgs a)
+__global__ __launch_bounds__(kTK) __attribute__((amdgpu_waves_per_eu(8))) void k_topk16(TruncArgs a)
 {
     __shared__ __attribute__((aligned(16))) TopkShared sh;
     const int row = (int)blockIdx.x;
@@ -1063,17 +1073,14 @@ __global__ __launch_bounds__(kTK) void k_topk16(TruncArgs a)
     uint32_t* const wh = sh.whist + wv * 256;
     uint32_t* const hc = reinterpret_cast<uint32_t*>(sh.hist);
     uint32_t F = f0;                   // the wave's floor (uniform)
-    // the stream's test: the signed form of each half shifted to the top of a
-    // 32-bit integer, against F's (one lower: negative values sit one lower
-    // there, and a positive one just below F entering is harmless)
-    auto test_of = [](uint32_t f) -> int {
-        return f > 0xFFFFu ? INT32_MAX : (int)((uint32_t)((int)f - 0x8001) << 16);
-    };
-    int T = test_of(F);
-    int c = 0;                         // this lane's words
+    uint32_t* const lane_list = lst + lane;
+    uint32_t* wp = lane_list;          // this lane's next word
+    uint32_t* const room = lane_list + 64 * (kSlots - 4);   // beyond: no room for a vector
+    int c = 0;                         // this lane's words (while compacting)
 
     // raise the floor and drop the words with nothing above it; all lanes, uniform
     auto compact = [&]() {
+        c = (int)((wp - lane_list) >> 6);
         const int cmax = wave_max_int(c);
         uint32_t total = 0, b1 = 0, above = 0;
 #pragma unroll
@@ -1115,22 +1122,31 @@ __global__ __launch_bounds__(kTK) void k_topk16(TruncArgs a)
             base += (uint32_t)__popcll(bal);
         }
         wave_lds_sync();
-        if (base > 64u * (kSlots - 8)) {                  // tied at the floor: the radix kernel
+        if (base > 64u * (kSlots - 4)) {                  // tied at the floor: the radix kernel
             if (lane == 0) sh.over[wv] = 1u;
-            F = 0x10000u;
+            F = 0xFFFFu + 0x8000u;                         // no pattern reaches it
             c = 0;
         } else {
             c = base > (uint32_t)lane ? (int)((base - (uint32_t)lane + 63u) >> 6) : 0;
         }
-        T = test_of(F);
+        wp = lane_list + 64 * c;
     };
-    auto take = [&](uint32_t x, bool ok) {                // a word: two 16-bit logits
-        const uint32_t sg = __builtin_bit_cast(uint32_t, __builtin_bit_cast(s16x2, x) >> (short)15);
-        const uint32_t sk = x ^ (sg & 0x7FFF7FFFu);
-        const bool in = ((int)sk >= T) || ((int)(sk << 16) >= T);
-        if (ok && in) {
-            lst[c * 64 + lane] = x;
-            ++c;
+    // a word (two 16-bit logits) that may hold a key >= F: above +0.0 ...
+    auto take_pos = [&](uint32_t x, bool ok, int tp) {
+        const s16x2 h = __builtin_bit_cast(s16x2, x);
+        const int mx = h.x > h.y ? h.x : h.y;
+        if (ok && mx >= tp) {
+            *wp = x;
+            wp += 64;
+        }
+    };
+    // ... and at or below it
+    auto take_neg = [&](uint32_t x, bool ok, uint32_t un) {
+        const uint32_t lo = x & 0xFFFFu, hi = x >> 16;
+        const uint32_t mn = lo < hi ? lo : hi;
+        if (ok && mn <= un) {
+            *wp = x;
+            wp += 64;
         }
     };
     if (lane == 0) sh.over[wv] = 0u;
@@ -1151,14 +1167,48 @@ __global__ __launch_bounds__(kTK) void k_topk16(TruncArgs a)
         }
     };
     auto take_group = [&](const Raw<DT> (&buf)[4], int g) {
+        if (g == 0 && K1 <= 64u) {     // uniform: a first floor from the first group
+            // each lane's largest logit among its first four vectors: 64
+            // different logits of the row at least as large as the smallest
+            // of them, so (for top_k < 64) it may start the floor if positive
+            int lm = -32768;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if ((u & 1) == 0 && __ballot(c > kSlots - 8)) compact();   // room for two vectors
-            const bool ok = t + (4 * g + u) * kTK < nfull;
-            take(buf[u].a.x, ok);
-            take(buf[u].a.y, ok);
-            take(buf[u].a.z, ok);
-            take(buf[u].a.w, ok);
+            for (int u = 0; u < 4; ++u) {
+                if (t + u * kTK < nfull) {
+                    const u32x4 q = buf[u].a;
+                    const s16x2 h0 = __builtin_bit_cast(s16x2, q.x), h1 = __builtin_bit_cast(s16x2, q.y);
+                    const s16x2 h2 = __builtin_bit_cast(s16x2, q.z), h3 = __builtin_bit_cast(s16x2, q.w);
+                    lm = max(lm, max(max((int)h0.x, (int)h0.y), max((int)h1.x, (int)h1.y)));
+                    lm = max(lm, max(max((int)h2.x, (int)h2.y), max((int)h3.x, (int)h3.y)));
+                }
+            }
+            const int mn = wave_min_int(lm);
+            if (mn > 0) F = 0x8000u + (uint32_t)mn;
+        }
+#pragma unroll
+        for (int u0 = 0; u0 < 4; u0 += 1) {
+            if (__ballot(wp > room)) compact();           // room for a vector
+            if (F > 0x8000u) {                            // uniform
+                const int tp = (int)F - 0x8000;
+#pragma unroll
+                for (int u = u0; u < u0 + 1; ++u) {
+                    const bool ok = t + (4 * g + u) * kTK < nfull;
+                    take_pos(buf[u].a.x, ok, tp);
+                    take_pos(buf[u].a.y, ok, tp);
+                    take_pos(buf[u].a.z, ok, tp);
+                    take_pos(buf[u].a.w, ok, tp);
+                }
+            } else {
+                const uint32_t un = 0x10000u - F;
+#pragma unroll
+                for (int u = u0; u < u0 + 1; ++u) {
+                    const bool ok = t + (4 * g + u) * kTK < nfull;
+                    take_neg(buf[u].a.x, ok, un);
+                    take_neg(buf[u].a.y, ok, un);
+                    take_neg(buf[u].a.z, ok, un);
+                    take_neg(buf[u].a.w, ok, un);
+                }
+            }
         }
     };
     Raw<DT> bufA[4], bufB[4];
@@ -1170,11 +1220,16 @@ __global__ __launch_bounds__(kTK) void k_topk16(TruncArgs a)
         take_group(bufB, g + 1);
         issue(bufB, g + 3);
     }
-    if (__ballot(c > kSlots - 8)) compact();
+    if (__ballot(wp > room)) compact();
     if (t == 0) {                      // the partial last vector: a word per logit, -inf above it
         const unsigned short* e = reinterpret_cast<const unsigned short*>(rp) + 8LL * nfull;
-        for (int j = 0; j < V - 8 * nfull; ++j) take((uint32_t)e[j] | (ninf_bits<DT>() << 16), true);
+        for (int j = 0; j < V - 8 * nfull; ++j) {
+            const uint32_t x = (uint32_t)e[j] | (ninf_bits<DT>() << 16);
+            if (F > 0x8000u) take_pos(x, true, (int)F - 0x8000);
+            else take_neg(x, true, 0x10000u - F);
+        }
     }
+    c = (int)((wp - lane_list) >> 6);
     if (lane == 0) sh.F[wv] = F;
     __syncthreads();
 
