@@ -1221,10 +1221,12 @@ __global__ __launch_bounds__(kTK) __attribute__((amdgpu_waves_per_eu(8))) void k
         issue(bufB, g + 3);
     }
     if (__ballot(wp > room)) compact();
-    if (t == 0) {                      // the partial last vector: a word per logit, -inf above it
+    if (t == 0) {                      // the partial last vector: at most four words, like a vector,
         const unsigned short* e = reinterpret_cast<const unsigned short*>(rp) + 8LL * nfull;
-        for (int j = 0; j < V - 8 * nfull; ++j) {
-            const uint32_t x = (uint32_t)e[j] | (ninf_bits<DT>() << 16);
+        const int n = V - 8 * nfull;   // -inf past its end
+        for (int j = 0; j < n; j += 2) {
+            const uint32_t hi = j + 1 < n ? (uint32_t)e[j + 1] : ninf_bits<DT>();
+            const uint32_t x = (uint32_t)e[j] | (hi << 16);
             if (F > 0x8000u) take_pos(x, true, (int)F - 0x8000);
             else take_neg(x, true, 0x10000u - F);
         }
