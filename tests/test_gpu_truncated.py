@@ -345,15 +345,16 @@ def small_top_k_rows(n, V, tdt, g):
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
-@pytest.mark.parametrize("V", [3001, 3007, 32000])
+@pytest.mark.parametrize("V", [3001, 3004, 3005, 3007, 32000])
 def test_truncated_small_top_k_equals_fp32(sv, dtype, V):
     """Top-k up to 256 on 16-bit rows takes the one-pass candidate lists: on
     rows built to stress them (small_top_k_rows), at every top-k from 1 to
     256 (and 257, the histogram pass) and top-p from off to 1e-6, the result
     must equal, bit for bit, that of the same rows upcast to fp32, which take
     the radix passes; some settings are checked against the oracle too.
-    V = 3007 ends each row with a partial vector of 7 logits, taken after the
-    stream by a lane whose list may be nearly full (ascending rows)."""
+    V = 3001, 3004, 3005 and 3007 end each row with a partial vector of 1,
+    4, 5 and 7 logits, taken after the stream by a lane whose list may be
+    nearly full (ascending rows)."""
     g = torch.Generator(device=DEV).manual_seed(V)
     tdt = synthetic.DTYPES[dtype]
     B, k = 12, 3
