@@ -138,3 +138,12 @@ def test_lazy_streamed_rows():
     assert bench.lazy_streamed_rows([4], 4, True) == (9, 1)
     assert bench.lazy_streamed_rows([0, 4, 1], 4, True) == (15, 5)
     assert bench.lazy_streamed_rows([0, 2, 4], 4, False) == (1 + 5 + 5, 0)
+
+
+def test_one_pass_top_k_limit_matches_the_library():
+    """bench.py names the truncation kernel from the library's dispatch rule:
+    its top-k limit for the candidate-list pass must be the library's."""
+    import re
+    src = open(os.path.join(ROOT, "draft_verification_verify_amd", "csrc", "sv_trunc.hip")).read()
+    m = re.search(r"constexpr int kTopkMax = (\d+);", src)
+    assert m and int(m.group(1)) == bench.TOPK_ONE_PASS_MAX
