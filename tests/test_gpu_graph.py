@@ -59,7 +59,7 @@ def replay_and_compare(g, outs, load, eager, n):
 
 
 @pytest.mark.parametrize("mode", ["sample", "greedy", "sample_lazy", "greedy_lazy", "truncated",
-                                  "lenient"])
+                                  "truncated_top_p", "lenient"])
 def test_chain_entry_points_replay(sv, mode):
     B, k, V = 48, 6, 32000
     sets = chain_sets(4, B, k, V, "bf16")
@@ -82,13 +82,15 @@ def test_chain_entry_points_replay(sv, mode):
                                   workspace=workspace)
         if mode == "greedy_lazy":
             return sv.greedy_lazy(t, xx, out_tokens=ot, out_num_accepted=on, workspace=workspace)
-        if mode == "truncated":
+        if mode == "truncated":        # the candidate-list pass
             return sv.sample_truncated(t, d, xx, uu, T, 20, 0.9, workspace=workspace)
+        if mode == "truncated_top_p":  # the pattern-histogram pass
+            return sv.sample_truncated(t, d, xx, uu, T, 0, 0.9, workspace=workspace)
         return sv.sample_lenient(t, d, xx, uu, T, 2.0, workspace=workspace)
 
     def run():
         r = call(tgt, dft, x, u, ws, out_t, out_n)
-        return r if mode in ("truncated", "lenient") else (out_t, out_n)
+        return r if mode in ("truncated", "truncated_top_p", "lenient") else (out_t, out_n)
 
     def load(i):
         tgt.copy_(sets[i].target)
