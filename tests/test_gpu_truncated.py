@@ -430,3 +430,56 @@ def test_random_truncated_cases(sv, i):
                         device=DEV)
     x = torch.from_numpy(truncated_drafts(f32(w.draft), T, top_k, top_p, 6000 + i)).to(DEV)
     check(sv, w, T, x, top_k, top_p)
+
+
+def random_small_top_k_case(i):
+    """Case i of the candidate-list sweep: fp16 or bf16, V in [8, 200000]
+    (log-uniform, so every partial-vector length occurs), top-k uniform in
+    [1, 256], top-p from off to 1e-6, and one of four value laws: Gaussian
+    logits of variance 0.5-100, a dozen distinct values (ties everywhere),
+    Gaussian logits with a quarter masked to -inf, or a shuffled ramp (every
+    logit distinct, a flat distribution)."""
+    r = np.random.default_rng(7000 + i)
+    dtype = ["fp16", "bf16"][int(r.integers(2))]
+    V = int(np.exp(r.uniform(np.log(8.0), np.log(200000.0))))
+    rows = int(max(1, min(24, 3_000_000 // V)))
+    top_k = int(r.integers(1, 257))
+    top_p = float(r.choice([1.0, 0.999, 0.9, 0.5, 0.1, 1e-6]))
+    law = int(r.integers(4))
+    scale = float(np.sqrt(r.choice([0.5, 2.0, 9.0, 100.0])))
+    return dtype, V, rows, top_k, top_p, law, scale
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_small_top_k_equals_fp32(sv, i):
+    """The candidate-list pass (16-bit rows, top-k <= 256) against the fp32
+    radix passes on the same (upcast) rows, bit for bit, over a seeded sweep
+    of shapes, settings and value laws (random_small_top_k_case)."""
+    dtype, V, rows, top_k, top_p, law, scale = random_small_top_k_case(i)
+    print(f"case {i}: {dtype} V={V} rows={rows} top_k={top_k} top_p={top_p} law={law} scale={scale:.2f}",
+          flush=True)
+    g = torch.Generator(device=DEV).manual_seed(7000 + i)
+    tdt = synthetic.DTYPES[dtype]
+    B, k = max(1, rows // 3), 1                    # rows = B * (2k + 1)
+    n = B * (2 * k + 1)
+    if law == 0:
+        z = torch.randn((n, V), generator=g, device=DEV) * scale
+    elif law == 1:
+        z = torch.randint(-6, 6, (n, V), generator=g, device=DEV).float() * 0.5
+    elif law == 2:
+        z = torch.randn((n, V), generator=g, device=DEV) * scale
+        z = z.masked_fill(torch.rand((n, V), generator=g, device=DEV) < 0.25, -float("inf"))
+        z[:, 0] = 0.0                                 # at least one finite logit per row
+    else:
+        ramp = torch.linspace(-4.0, 4.0, V, device=DEV)
+        z = torch.stack([ramp[torch.randperm(V, generator=g, device=DEV)] for _ in range(n)])
+    z = z.to(tdt)
+    tgt = z[:B * (k + 1)].view(B, k + 1, V)
+    dft = z[B * (k + 1):].view(B, k, V)
+    u = synthetic.uniforms24((B, k + 1), g, DEV)
+    tok = torch.randint(0, V, (B, k), generator=g, device=DEV, dtype=torch.int32)
+    a = sv.sample_truncated(tgt, dft, tok, u, 1.0, top_k, top_p, return_probs=True)
+    b = sv.sample_truncated(tgt.float(), dft.float(), tok, u, 1.0, top_k, top_p, return_probs=True)
+    torch.cuda.synchronize()
+    for ta, tb in zip(a, b):
+        assert torch.equal(ta, tb)
