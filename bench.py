@@ -36,9 +36,33 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "verified positions/sec (B·(k+1) rows/s) and achieved HBM GB/s vs peak"
 STATS_SOURCES = ["sv_stats.hip", "sv_device.h", "sv_launch.h"]
 STREAM_KERNELS = ("k_softmax_stats", "k_argmax_stats")
-# 16-bit rows under a top-k of at most this take the candidate-list pass
-# (k_topk16); larger or no top-k, the 65536-bin histogram pass (k_trunc16)
+# Rows under a top-k of at most this take a candidate-list pass (k_topk16 for
+# 16-bit rows, k_topk32 for fp32); larger or no top-k, 16-bit rows take the
+# 65536-bin histogram pass (k_trunc16) and fp32 rows the radix passes
 TOPK_ONE_PASS_MAX = 256
+LDS_ROW_MAX = 32768                    # fp32 rows up to this run the radix passes from LDS
+TRUNC_NOTES = {
+    "k_topk16": "k_topk16 (one pass per 16-bit row: per-wave lists of the candidates above a "
+                "rising floor) followed by k_trunc_rows over the rows it marked",
+    "k_topk32": "k_topk32 (one pass per fp32 row: per-wave lists of the candidates above a "
+                "rising floor) followed by k_trunc_rows over the rows it marked",
+    "k_trunc16": "k_trunc16 (one pass per 16-bit row: an exact LDS histogram of all 65536 bit "
+                 "patterns) followed by k_trunc_rows over the rows it marked",
+    "k_trunc_rows_lds": "k_trunc_rows_lds (radix selection on an LDS copy of each fp32 row, "
+                        "read from HBM once)",
+    "k_trunc_rows": "k_trunc_rows (radix selection, one workgroup per row; the first digit's "
+                    "pass reads the row from HBM, later ones mostly from cache)",
+}
+
+
+def truncation_kernel(es: int, V: int, top_k: int) -> str:
+    """The launch that summarises every row for truncated sampling."""
+    small_topk = 1 <= top_k <= TOPK_ONE_PASS_MAX and top_k < V
+    if es == 2:
+        return "k_topk16" if small_topk and V >= 8 else ("k_trunc16" if V >= 8 else "k_trunc_rows")
+    if small_topk and V >= 8:
+        return "k_topk32"
+    return "k_trunc_rows_lds" if V <= LDS_ROW_MAX else "k_trunc_rows"
 
 
 def traffic_file(kernel: str, cid: int) -> str:
@@ -384,9 +408,8 @@ def main():
             bufs = [(x.target, x.draft) for x in slices]
         vecs = CEILING_VECS if args.ceiling_vec < 0 else (args.ceiling_vec,)
         ceiling = stream_ceiling(bufs, max(args.steps, 20), vecs)
-    one_pass = "k_topk16" if 1 <= args.top_k <= TOPK_ONE_PASS_MAX and args.top_k < V else "k_trunc16"
     kernel_name = {"sample": "k_softmax_stats", "lenient": "k_softmax_stats",
-                   "truncated": one_pass if es == 2 else "k_trunc_rows"}.get(args.mode, "k_argmax_stats")
+                   "truncated": truncation_kernel(es, V, args.top_k)}.get(args.mode, "k_argmax_stats")
     traffic = measured_traffic(kernel_name, cid) \
         if (kernel_name in STREAM_KERNELS and args.vocab_shard == 1 and args.mode != "tree"
             and not lazy) else None
@@ -438,16 +461,8 @@ def main():
             "full_pass_bytes_per_call": stats_bytes,
         } if lazy else {
             "kernel": kernel_name,
-            "note": (("the timed launch is k_topk16 (one pass per 16-bit row: per-wave lists "
-                      "of the candidates above a rising floor) followed by k_trunc_rows over "
-                      "the rows it marked; algorithmic bytes: every row read once")
-                     if es == 2 and one_pass == "k_topk16" else
-                     ("the timed launch is k_trunc16 (one pass per 16-bit row: an exact LDS "
-                      "histogram of all 65536 bit patterns) followed by k_trunc_rows over the "
-                      "rows it marked; algorithmic bytes: every row read once") if es == 2 else
-                     ("the timed launch is k_trunc_rows (radix selection, one workgroup per "
-                      "row; the first digit's pass reads the row from HBM, later ones mostly "
-                      "from cache); algorithmic bytes: every row read once"))
+            "note": ("the timed launch is " + TRUNC_NOTES[kernel_name]
+                     + "; algorithmic bytes: every row read once")
             if args.mode == "truncated" else (
                 "rows counts every scored candidate position (B*C*R); the kernel reads "
                 "B*N unique node rows") if args.mode == "tree" else None,

@@ -11,14 +11,14 @@
 //   together.  Both keep a set {t : key(z_t) >= tau} for an ordering key
 //   (key_of), so a row is summarised by (m, tau, kept mass).
 //
-// Three kernels find tau and the kept mass:
-//  - k_topk16 (fp16 / bf16 rows under a top-k of at most 256): one pass per
-//    row keeping only the logits that can still be among the top_k largest,
-//    the thresholds found among those;
+// Four kernels find tau and the kept mass:
+//  - k_topk16 and k_topk32 (16-bit and fp32 rows under a top-k of at most
+//    256): one pass per row keeping only the logits that can still be among
+//    the top_k largest, the thresholds found among those;
 //  - k_trunc16 (other fp16 / bf16 rows): one pass per row, an exact count of
 //    all 65536 bit patterns in LDS, the thresholds read off the histogram;
-//  - k_trunc_rows (fp32 rows, and the rare 16-bit row the histogram cannot
-//    hold): radix selection on the key, most significant digit first (11, 11
+//  - k_trunc_rows (other fp32 rows, and the rare row the one-pass kernels
+//    cannot summarise): radix selection on the key, most significant digit first (11, 11
 //    and 10 bits for fp32 keys; 11 then 5 for 16-bit keys), one 512-thread
 //    workgroup per row streaming the row once per digit (the first pass from
 //    HBM, the rest mostly from cache) and histogramming the next digit of the
@@ -27,9 +27,9 @@
 //    32768 logits held in LDS, read from memory once.
 // Masses are fixed-point integers (w * 2^40, truncated), summed with integer
 // atomics and integer reductions, so every result is independent of
-// scheduling and bitwise reproducible, and both kernels give the same
-// integers for the same row.  The three kernels agree bit for bit on every
-// row summary.
+// scheduling and bitwise reproducible, and every kernel gives the same
+// integers for the same row.  The kernels agree bit for bit on every row
+// summary.
 
 #include "sv_device.h"
 
@@ -1404,6 +1404,424 @@ __global__ __launch_bounds__(kTK) __attribute__((amdgpu_waves_per_eu(8))) void k
     }
 }
 
+// ---- one pass for fp32 logits under a small top-k ---------------------------
+// k_topk16's design on 32-bit keys, with these differences:
+//  - a list entry is one logit (its bits) and the stream test one float
+//    comparison against the floor's value;
+//  - radix digits are taken from a key's offset above a base (the floor),
+//    starting at the top bit of the range the keys span (OffDigits): the high
+//    bits of an fp32 key are mostly its exponent, and digits of the key itself
+//    would put nearly every candidate in one or two bins, whose LDS atomics
+//    then serialise;
+//  - a wave raises its floor to the 16-bit offset prefix of the (top_k + 1)-th
+//    largest key in its list (the keys with that prefix or a larger one stay:
+//    at least top_k + 1 of them), also once more after the stream, so that few
+//    keys are above the largest floor;
+//  - for top_k < 64 the first floor is the (top_k + 1)-th largest of the
+//    wave's 64 lane maxima over its first vectors (that many different
+//    logits are at least as large), found one bit at a time with ballots;
+//  - after the stream the keys at or above the largest floor are gathered,
+//    and one wave finds the top_k-th largest of them and then top-p on the
+//    kept masses, with no workgroup barrier.
+// Every count, mass and threshold equals the radix passes'.  NT threads take
+// one row: 256 (eight workgroups to a CU) when the rows outnumber the compute
+// units, else 1024, so that few rows still keep many loads in flight (a
+// 32000-logit row is one load per 16 bytes of the workgroup's first round).
+
+// list entries per lane: 16 with 1024 threads (one workgroup to a CU), 12
+// with 256 (eight to a CU)
+template <int NT>
+constexpr int kS32 = NT == 1024 ? 16 : 12;
+
+template <int NT>
+struct Topk32Shared {
+    static constexpr int NW = NT / 64;
+    uint32_t list[NW * kS32<NT> * 64]; // wave w, lane l, entry j: [w][j * 64 + l]; then the keys >= the floor
+    uint32_t whist[NW * 256];           // each wave's histogram while compacting; then wave 0's and the kept keys
+    u64 mh[256];                        // wave 0's mass histogram
+    uint32_t mx[NW];
+    uint32_t F[NW];
+    uint32_t over[NW];
+    uint32_t nk;
+};
+
+// key_of's fp32 key back to the value (+0.0 for the merged zero)
+__device__ __forceinline__ float value_of_key32(uint32_t k)
+{
+    return __uint_as_float(k >= 0x80000000u ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+__device__ __forceinline__ uint32_t key32(uint32_t x)
+{
+    return key_of<DT_F32>(__uint_as_float(x));
+}
+
+// Radix digits of a key's offset o from a base, for keys spanning [base,
+// base + range]: the first level takes the top (up to) 8 of the bits the
+// range needs, each later one the next 8; level l's digit is o's bits
+// [ls, hs) (level 0: every bit from ls up), ls = shift(l), hs = shift(l - 1).
+struct OffDigits {
+    int top;                           // bits the range needs (0: a single key)
+    __device__ explicit OffDigits(uint32_t range) : top(range ? 32 - __clz((int)range) : 0) {}
+    __device__ int shift(int l) const
+    {
+        const int s = top - 8 * (l + 1);
+        return s > 0 ? s : 0;
+    }
+    __device__ static uint32_t digit(uint32_t o, int level, int hs, int ls)
+    {
+        return level == 0 ? o >> ls : (o >> ls) & ((1u << (hs - ls)) - 1u);
+    }
+};
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    return (uint32_t)wave_max_int((int)(v ^ 0x80000000u)) ^ 0x80000000u;
+}
+
+template <bool VEC, int NT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 256 ? 8 : 4)))
+void k_topk32(TruncArgs a)
+{
+    constexpr int NW = NT / 64;
+    constexpr int KS = kS32<NT>;
+    static_assert(NW >= 3, "wave 0's histogram and the kept keys fit in the wave histograms");
+    __shared__ __attribute__((aligned(16))) Topk32Shared<NT> sh;
+    const int row = (int)blockIdx.x;
+    const int t = (int)threadIdx.x;
+    const int lane = t & 63, wv = t >> 6;
+    const char* rp = trunc_row_ptr<DT_F32>(a, row);
+    const int V = a.V;
+    const int nfull = V >> 3;                                  // >= 1
+    const uint32_t K1 = (uint32_t)a.top_k + 1u;
+    const uint32_t f0 = key32(0xFF800000u) + 1u;               // just above -inf
+    uint32_t* const lst = sh.list + wv * (KS * 64);
+    uint32_t* const wh = sh.whist + wv * 256;
+    uint32_t F = f0;                   // the wave's floor (uniform) and its value
+    float fF = value_of_key32(F);
+    uint32_t* const lane_list = lst + lane;
+    uint32_t* wp = lane_list;          // this lane's next entry
+    uint32_t* const room = lane_list + 64 * (KS - 4);   // beyond: no room for four more
+    int c = 0;
+
+    // Raise the floor F to the 16-bit offset prefix of the K1-th largest of
+    // the wave's keys at or above it (at least K1 of them stay at or above
+    // it), or leave it when they are fewer; key(j) is this lane's j-th key
+    // (j < n).  All lanes, uniform.
+    auto raise_floor = [&](auto&& key, int n) {
+        uint32_t mk = F;
+        for (int j = 0; j < n; ++j) {
+            const uint32_t k = key(j);
+            mk = k > mk ? k : mk;
+        }
+        const OffDigits od(wave_max_u32(mk) - F);
+        uint32_t prefix = 0, need = K1;
+        int hs = od.top, ls = od.shift(0);   // level 0 has no prefix
+#pragma unroll
+        for (int level = 0; level < 2; ++level) {
+            reinterpret_cast<u32x4*>(wh)[lane] = u32x4{0u, 0u, 0u, 0u};
+            wave_lds_sync();
+            for (int j = 0; j < n; ++j) {
+                const uint32_t k = key(j), o = k - F;
+                if (k >= F && (level == 0 || (o >> hs) == prefix)) atomicAdd(&wh[od.digit(o, level, hs, ls)], 1u);
+            }
+            wave_lds_sync();
+            uint32_t bin, ab;
+            const uint32_t tot = find_desc_count(wh, need, bin, ab);
+            wave_lds_sync();
+            if (level == 0 && tot < K1) break;   // uniform: too few keys to raise the floor
+            prefix = (prefix << (hs - ls)) | bin;
+            need -= ab;
+            if (level == 1 || ls == 0) {
+                F += prefix << ls;
+                break;
+            }
+            hs = ls;
+            ls = od.shift(1);
+        }
+    };
+    // raise the floor and drop the entries below it; all lanes, uniform
+    auto compact = [&]() {
+        c = (int)((wp - lane_list) >> 6);
+        const int cmax = wave_max_int(c);
+        raise_floor([&](int j) { return key32(lst[j * 64 + lane]); }, c);
+        uint32_t base = 0;
+        for (int j = 0; j < cmax; ++j) {
+            const uint32_t x = j < c ? lst[j * 64 + lane] : 0u;
+            const bool keep = j < c && key32(x) >= F;
+            const unsigned long long bal = __ballot(keep);
+            if (keep) lst[base + lane_prefix(bal)] = x;   // at or below every unread entry
+            base += (uint32_t)__popcll(bal);
+        }
+        wave_lds_sync();
+        if (base > 64u * (KS - 4)) {                    // tied at the floor: the radix kernel
+            if (lane == 0) sh.over[wv] = 1u;
+            F = 0xFFFFFFFFu;                               // its value is a NaN: nothing passes
+            c = 0;
+        } else {
+            c = base > (uint32_t)lane ? (int)((base - (uint32_t)lane + 63u) >> 6) : 0;
+        }
+        wp = lane_list + 64 * c;
+        fF = value_of_key32(F);
+    };
+    // a logit whose key may be >= F: its value is >= F's (-0.0 and +0.0 alike)
+    auto take = [&](uint32_t x, bool ok) {
+        if (ok && __uint_as_float(x) >= fF) {
+            *wp = x;
+            wp += 64;
+        }
+    };
+    auto take4 = [&](const u32x4& q, bool ok) {
+        if (__ballot(wp > room)) compact();
+        take(q.x, ok);
+        take(q.y, ok);
+        take(q.z, ok);
+        take(q.w, ok);
+    };
+    if (lane == 0) sh.over[wv] = 0u;
+    if (t == 0) sh.nk = 0u;
+
+    // the stream: vector t + i * NT at step i, in groups of two steps; two
+    // register buffers alternate as in k_topk16.  With 1024 threads the last
+    // two groups are taken after the loop, so that no load is issued past them
+    // (the registers they would fill are reused, so the merge would wait for
+    // them); with 256 the loop reloads past the row.  A lane's vectors past
+    // the row read its last full vector again and are not taken.
+    const int ngroups = 2 * ((nfull + 4 * NT - 1) / (4 * NT));   // even
+    auto issue = [&](Raw<DT_F32> (&buf)[2], int g) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int v = t + (2 * g + u) * NT;
+            buf[u] = load_raw<DT_F32, VEC>(rp, v < nfull ? v : nfull - 1);
+        }
+    };
+    auto take_group = [&](const Raw<DT_F32> (&buf)[2], int g) {
+        if (g == 0 && K1 <= 64u) {     // uniform: a first floor from the first group
+            // each lane's largest logit among its first two vectors: K1
+            // different logits of the row are at least as large as the K1-th
+            // largest of the 64, found one bit at a time
+            float lm = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                if (t + u * NT < nfull) {
+                    const u32x4 p = buf[u].a, q = buf[u].b;
+                    lm = fmaxf(lm, fmaxf(fmaxf(__uint_as_float(p.x), __uint_as_float(p.y)),
+                                         fmaxf(__uint_as_float(p.z), __uint_as_float(p.w))));
+                    lm = fmaxf(lm, fmaxf(fmaxf(__uint_as_float(q.x), __uint_as_float(q.y)),
+                                         fmaxf(__uint_as_float(q.z), __uint_as_float(q.w))));
+                }
+            }
+            const uint32_t lk = lm > -INFINITY ? key_of<DT_F32>(lm) : 0u;   // 0: below every key
+            uint32_t s = 0u;
+            for (int b = 31; b >= 0; --b) {
+                const uint32_t cand = s | (1u << b);
+                if ((uint32_t)__popcll(__ballot(lk >= cand)) >= K1) s = cand;
+            }
+            if (s > F) {
+                F = s;
+                fF = value_of_key32(F);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const bool ok = t + (2 * g + u) * NT < nfull;
+            take4(buf[u].a, ok);
+            take4(buf[u].b, ok);
+        }
+    };
+    Raw<DT_F32> bufA[2], bufB[2];
+    issue(bufA, 0);
+    issue(bufB, 1);
+    if constexpr (NT == 1024) {
+        for (int g = 0; g + 2 < ngroups; g += 2) {
+            take_group(bufA, g);
+            issue(bufA, g + 2);        // unconditional: each group waits for its own loads only
+            take_group(bufB, g + 1);
+            issue(bufB, g + 3);
+        }
+        take_group(bufA, ngroups - 2);
+        take_group(bufB, ngroups - 1);
+    } else {                           // in 64 registers: one copy of the groups, reloads past the row
+        for (int g = 0; g < ngroups; g += 2) {
+            take_group(bufA, g);
+            issue(bufA, g + 2);
+            take_group(bufB, g + 1);
+            issue(bufB, g + 3);
+        }
+    }
+    if (__ballot(wp > room)) compact();
+    if (t < 2) {                       // the partial last vector: up to four logits on each of two lanes
+        const float* e = reinterpret_cast<const float*>(rp) + 8LL * nfull;
+        const int n = V - 8 * nfull;
+        for (int j = 4 * t; j < n && j < 4 * t + 4; ++j) take(__float_as_uint(e[j]), true);
+    }
+    c = (int)((wp - lane_list) >> 6);
+    uint32_t kr[KS];                 // this lane's keys (0 past its list: below every floor)
+#pragma unroll
+    for (int j = 0; j < KS; ++j) kr[j] = j < c ? key32(lst[j * 64 + lane]) : 0u;
+    // the wave's last floor, raised on its final list: few keys above the
+    // largest floor are left for the merge
+    if (F != 0xFFFFFFFFu) raise_floor([&](int j) { return kr[j]; }, KS);
+    {
+        uint32_t mx_t = 0;             // the largest key in the lists is the row's
+#pragma unroll
+        for (int j = 0; j < KS; ++j) mx_t = kr[j] > mx_t ? kr[j] : mx_t;
+        const uint32_t mx = wave_max_u32(mx_t);
+        if (lane == 0) {
+            sh.F[wv] = F;
+            sh.mx[wv] = mx;
+        }
+    }
+    __syncthreads();
+
+    uint32_t Fg = sh.F[0], mxk = sh.mx[0];
+    uint32_t over = sh.over[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+        Fg = sh.F[w] > Fg ? sh.F[w] : Fg;
+        mxk = sh.mx[w] > mxk ? sh.mx[w] : mxk;
+        over |= sh.over[w];
+    }
+    if (over) {
+        if (t == 0) a.rows[row] = TruncRow{0.f, 0.f, 0u, 1u};
+        return;
+    }
+    if (mxk < Fg) {                    // no key at or above the floor: every logit -inf
+        if (t == 0) a.rows[row] = TruncRow{-INFINITY, -INFINITY, 0u, 0u};
+        return;
+    }
+
+    // gather the keys at or above Fg into the list area (free: every key is
+    // in registers); wave 0 then finds both thresholds alone
+    uint32_t* const gk = sh.list;
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+        const bool keep = kr[j] >= Fg;     // Fg >= f0 > 0: empty slots never kept
+        const unsigned long long bal = __ballot(keep);
+        if (bal) {
+            const int first = __ffsll((long long)bal) - 1;
+            uint32_t base = 0;
+            if (lane == first) base = atomicAdd(&sh.nk, (uint32_t)__popcll(bal));
+            base = (uint32_t)__builtin_amdgcn_readlane((int)base, first);
+            if (keep) gk[base + lane_prefix(bal)] = kr[j];
+        }
+    }
+    __syncthreads();
+    if (wv != 0) return;
+    const uint32_t n = sh.nk;          // >= 1: the row max is among them
+
+    // top-k: the top_k-th largest of the n keys, one digit of its offset from
+    // Fg per level; with every finite logit among them (no floor raised) top-k
+    // is off for at most top_k of them
+    const bool topk_on = Fg > f0 || (uint32_t)a.top_k < n;
+    uint32_t lo = Fg;                  // keys >= lo survive top-k
+    if (topk_on) {
+        const OffDigits od(mxk - Fg);
+        uint32_t prefix = 0, need = (uint32_t)a.top_k;
+        int hs = od.top, ls = od.shift(0);   // level 0 has no prefix
+        for (int level = 0;; ++level) {
+            reinterpret_cast<u32x4*>(wh)[lane] = u32x4{0u, 0u, 0u, 0u};
+            wave_lds_sync();
+            for (uint32_t i0 = 0; i0 < n; i0 += 256) {   // four reads in flight per lane
+                uint32_t q[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint32_t i = i0 + (uint32_t)(lane + 64 * u);
+                    q[u] = i < n ? gk[i] : 0u;
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint32_t o = q[u] - Fg;
+                    if (q[u] >= Fg && (level == 0 || (o >> hs) == prefix))
+                        atomicAdd(&wh[od.digit(o, level, hs, ls)], 1u);
+                }
+            }
+            wave_lds_sync();
+            uint32_t bin, above;
+            find_desc_count(wh, need, bin, above);
+            wave_lds_sync();
+            prefix = (prefix << (hs - ls)) | bin;
+            need -= above;
+            if (ls == 0) break;
+            hs = ls;
+            ls = od.shift(level + 1);
+        }
+        lo = Fg + prefix;
+    }
+
+    // the kept keys (at most kKeptMax, else the row goes to the radix kernel)
+    uint32_t* const kk = sh.whist + 256;
+    uint32_t nk = 0;
+    for (uint32_t i0 = 0; i0 < n; i0 += 64) {
+        const uint32_t i = i0 + (uint32_t)lane;
+        const uint32_t k = i < n ? gk[i] : 0u;
+        const bool keep = k >= lo;     // lo >= f0 > 0
+        const unsigned long long bal = __ballot(keep);
+        const uint32_t pos = nk + lane_prefix(bal);
+        if (keep && pos < (uint32_t)kKeptMax) kk[pos] = k;
+        nk += (uint32_t)__popcll(bal);
+    }
+    if (nk > (uint32_t)kKeptMax) {     // a tie group too large to gather
+        if (t == 0) a.rows[row] = TruncRow{0.f, 0.f, 0u, 1u};
+        return;
+    }
+    wave_lds_sync();
+
+    // the kept logits' masses, eight keys per lane at most, and the kept
+    // mass; top-p: the key at which the mass from the top first reaches top_p
+    // of it, one digit of its offset from lo per level
+    constexpr int H = kKeptMax / 64;
+    const float m = value_of_key32(mxk);
+    const float cc = a.c;
+    u64 f[H];
+    uint32_t kt[H];
+    u64 fs = 0;
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+        const uint32_t i = (uint32_t)(lane + 64 * h);
+        kt[h] = i < nk ? kk[i] : 0u;
+        f[h] = i < nk ? fixed40_nb(weight(value_of_key32(kt[h]), m, cc)) : 0;
+        fs += f[h];
+    }
+    u64 kept = lane63_u64(wave_scan_u64(fs));
+    uint32_t tau = topk_on ? lo : 0u;  // top-k off: every key
+    if (a.top_p < 1.f) {
+        const double budget = (double)a.top_p * (double)kept;
+        u64* const hm = sh.mh;
+        const OffDigits od(mxk - lo);  // the kept keys: lo .. mxk
+        uint32_t prefix = 0u;
+        u64 base = 0;
+        int hs = od.top, ls = od.shift(0);   // level 0 has no prefix
+        for (int level = 0;; ++level) {
+            reinterpret_cast<u32x4*>(hm)[2 * lane] = u32x4{0u, 0u, 0u, 0u};
+            reinterpret_cast<u32x4*>(hm)[2 * lane + 1] = u32x4{0u, 0u, 0u, 0u};
+            wave_lds_sync();
+#pragma unroll
+            for (int h = 0; h < H; ++h) {
+                const uint32_t o = kt[h] - lo;
+                if (f[h] && (level == 0 || (o >> hs) == prefix))
+                    atomicAdd(&hm[od.digit(o, level, hs, ls)], f[h]);
+            }
+            wave_lds_sync();
+            uint32_t bin;
+            u64 above;
+            find_desc_mass(hm, base, budget, bin, above);
+            kept = above + hm[bin];    // the mass of every larger key and the bin's own
+            base = above;
+            prefix = (prefix << (hs - ls)) | bin;
+            wave_lds_sync();
+            if (ls == 0) break;
+            hs = ls;
+            ls = od.shift(level + 1);
+        }
+        tau = lo + prefix;
+    }
+    if (t == 0) {
+        const float l2s = (float)(log2((double)kept) - (double)kFixBits);
+        a.rows[row] = TruncRow{m, l2s, tau, 0u};
+    }
+}
+
 // The current device's compute units (queried once per device).
 int compute_units()
 {
@@ -1424,7 +1842,28 @@ hipError_t launch_dt(bool vec, const TruncArgs& a, hipStream_t st)
     TruncArgs b = a;
     b.only_marked = 0;
     void* args[] = {&b};
+    const void* marked = vec ? reinterpret_cast<const void*>(k_trunc_rows<DT, true>)
+                             : reinterpret_cast<const void*>(k_trunc_rows<DT, false>);
+    // rows the one-pass kernels could not summarise (pad = 1): 65536 or more
+    // equal finite 16-bit logits (k_trunc16), or too many tied at a list's
+    // floor (k_topk16, k_topk32)
+    auto run_marked = [&]() {
+        b.only_marked = 1;
+        const int blocks = (a.n_rows + kTB - 1) / kTB;
+        const unsigned grid = (unsigned)(blocks < 1024 ? blocks : 1024);
+        return hipLaunchKernel(marked, dim3(grid), dim3(kTB), args, 0, st);
+    };
+    const bool small_topk = a.top_k >= 1 && a.top_k <= kTopkMax && a.top_k < a.V;
     if constexpr (DT == DT_F32) {
+        if (small_topk && a.V >= 8) {
+            const bool wide = a.n_rows <= compute_units();   // few rows: 1024 threads each
+            const void* f = wide ? (vec ? reinterpret_cast<const void*>(k_topk32<true, 1024>)
+                                        : reinterpret_cast<const void*>(k_topk32<false, 1024>))
+                                 : (vec ? reinterpret_cast<const void*>(k_topk32<true, 256>)
+                                        : reinterpret_cast<const void*>(k_topk32<false, 256>));
+            const hipError_t e = hipLaunchKernel(f, dim3((unsigned)a.n_rows), dim3(wide ? 1024 : 256), args, 0, st);
+            return e != hipSuccess ? e : run_marked();
+        }
         const bool in_lds = a.V <= kLdsRowMax;
         const void* f = in_lds ? (vec ? reinterpret_cast<const void*>(k_trunc_rows_lds<true>)
                                       : reinterpret_cast<const void*>(k_trunc_rows_lds<false>))
@@ -1432,13 +1871,10 @@ hipError_t launch_dt(bool vec, const TruncArgs& a, hipStream_t st)
                                       : reinterpret_cast<const void*>(k_trunc_rows<DT, false>));
         return hipLaunchKernel(f, dim3((unsigned)a.n_rows), dim3(kTB), args, 0, st);
     } else {
-        if (a.V < 8) {                 // no whole vector: the radix kernel takes every row
-            const void* g = vec ? reinterpret_cast<const void*>(k_trunc_rows<DT, true>)
-                                : reinterpret_cast<const void*>(k_trunc_rows<DT, false>);
-            return hipLaunchKernel(g, dim3((unsigned)a.n_rows), dim3(kTB), args, 0, st);
-        }
+        if (a.V < 8)                   // no whole vector: the radix kernel takes every row
+            return hipLaunchKernel(marked, dim3((unsigned)a.n_rows), dim3(kTB), args, 0, st);
         hipError_t e;
-        if (a.top_k >= 1 && a.top_k <= kTopkMax && a.top_k < a.V) {
+        if (small_topk) {
             const void* f = vec ? reinterpret_cast<const void*>(k_topk16<DT, true>)
                                 : reinterpret_cast<const void*>(k_topk16<DT, false>);
             e = hipLaunchKernel(f, dim3((unsigned)a.n_rows), dim3(kTK), args, 0, st);
@@ -1449,15 +1885,7 @@ hipError_t launch_dt(bool vec, const TruncArgs& a, hipStream_t st)
             const unsigned g16 = (unsigned)(a.n_rows < cus ? a.n_rows : cus);   // one workgroup fills a CU's LDS
             e = hipLaunchKernel(f, dim3(g16), dim3(kT16), args, 0, st);
         }
-        if (e != hipSuccess) return e;
-        // rows with 65536 or more equal finite logits (k_trunc16), or too many
-        // tied at a list's floor (k_topk16)
-        b.only_marked = 1;
-        const void* g = vec ? reinterpret_cast<const void*>(k_trunc_rows<DT, true>)
-                            : reinterpret_cast<const void*>(k_trunc_rows<DT, false>);
-        const int blocks = (a.n_rows + kTB - 1) / kTB;
-        const unsigned grid = (unsigned)(blocks < 1024 ? blocks : 1024);
-        return hipLaunchKernel(g, dim3(grid), dim3(kTB), args, 0, st);
+        return e != hipSuccess ? e : run_marked();
     }
 }
 

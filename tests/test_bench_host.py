@@ -147,3 +147,22 @@ def test_one_pass_top_k_limit_matches_the_library():
     src = open(os.path.join(ROOT, "draft_verification_verify_amd", "csrc", "sv_trunc.hip")).read()
     m = re.search(r"constexpr int kTopkMax = (\d+);", src)
     assert m and int(m.group(1)) == bench.TOPK_ONE_PASS_MAX
+    m = re.search(r"constexpr int kLdsRowMax = (\d+);", src)
+    assert m and int(m.group(1)) == bench.LDS_ROW_MAX
+
+
+def test_truncation_kernel_names():
+    """The launch bench.py times for truncated sampling, by element size,
+    vocabulary and top-k, as the library dispatches it."""
+    tk = bench.truncation_kernel
+    assert tk(2, 128256, 50) == "k_topk16"
+    assert tk(2, 128256, 256) == "k_topk16"
+    assert tk(2, 128256, 257) == "k_trunc16"
+    assert tk(2, 128256, 0) == "k_trunc16"
+    assert tk(2, 100, 100) == "k_trunc16"          # top-k >= V is off
+    assert tk(2, 7, 3) == "k_trunc_rows"          # no whole vector
+    assert tk(4, 32000, 50) == "k_topk32"
+    assert tk(4, 32000, 0) == "k_trunc_rows_lds"
+    assert tk(4, 32768, 300) == "k_trunc_rows_lds"
+    assert tk(4, 32769, 0) == "k_trunc_rows"
+    assert tk(4, 7, 3) == "k_trunc_rows_lds"

@@ -123,9 +123,11 @@ def test_truncated_many_rows_per_workgroup(sv):
 @pytest.mark.parametrize("top_k,top_p", [(50, 0.9), (0, 0.8)])
 def test_truncated_16bit_equals_fp32_at_full_size(sv, top_k, top_p):
     """At the full 512 x 16 x 128256 bf16 size, every row: the same rows
-    upcast to fp32 (exact) go through the radix passes instead of the 16-bit
-    histogram, and the two must agree bit for bit (same keep set, same
-    fixed-point masses, so the same tokens and the same p'(x), q'(x))."""
+    upcast to fp32 (exact) go through the fp32 kernels (top-k 50: the fp32
+    candidate lists, 256 threads per row; top-p alone: the radix passes)
+    instead of the 16-bit ones, and the two must agree bit for bit (same keep
+    set, same fixed-point masses, so the same tokens and the same p'(x),
+    q'(x))."""
     w = synthetic.generate(5, device=DEV)
     a = sv.sample_truncated(w.target, w.draft, w.tokens, w.uniforms, w.T, top_k, top_p,
                             return_probs=True)
@@ -346,18 +348,21 @@ def small_top_k_rows(n, V, tdt, g):
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("V", [3001, 3004, 3005, 3007, 32000])
-def test_truncated_small_top_k_equals_fp32(sv, dtype, V):
-    """Top-k up to 256 on 16-bit rows takes the one-pass candidate lists: on
-    rows built to stress them (small_top_k_rows), at every top-k from 1 to
-    256 (and 257, the histogram pass) and top-p from off to 1e-6, the result
-    must equal, bit for bit, that of the same rows upcast to fp32, which take
-    the radix passes; some settings are checked against the oracle too.
-    V = 3001, 3004, 3005 and 3007 end each row with a partial vector of 1,
-    4, 5 and 7 logits, taken after the stream by a lane whose list may be
-    nearly full (ascending rows)."""
-    g = torch.Generator(device=DEV).manual_seed(V)
+@pytest.mark.parametrize("B", [12, 40])
+def test_truncated_small_top_k_equals_fp32(sv, dtype, V, B):
+    """Top-k up to 256 takes the one-pass candidate lists, 16-bit rows
+    k_topk16 and fp32 rows k_topk32: on rows built to stress them
+    (small_top_k_rows), at every top-k from 1 to 256 (and 257: the histogram
+    pass against the radix passes) and top-p from off to 1e-6, the 16-bit
+    result must equal, bit for bit, that of the same rows upcast to fp32;
+    some settings are checked against the oracle too.  B = 12 gives 84 rows
+    (1024 threads per fp32 row), B = 40 gives 280 rows, more than the compute
+    units (256 threads per row).  V = 3001, 3004, 3005 and 3007 end each row
+    with a partial vector of 1, 4, 5 and 7 logits, taken after the stream by
+    lanes whose lists may be nearly full (ascending rows)."""
+    g = torch.Generator(device=DEV).manual_seed(V + B)
     tdt = synthetic.DTYPES[dtype]
-    B, k = 12, 3
+    k = 3
     z = small_top_k_rows(B * (k + 1), V, tdt, g).view(B, k + 1, V)
     y = small_top_k_rows(B * k + 5, V, tdt, g)[5:].view(B, k, V)   # other patterns than z's rows
     u = synthetic.uniforms24((B, k + 1), g, DEV)
@@ -376,16 +381,38 @@ def test_truncated_small_top_k_equals_fp32(sv, dtype, V):
         check(sv, w, 0.8, x, top_k, top_p)
 
 
+@pytest.mark.parametrize("V", [3001, 3007, 32000])
+@pytest.mark.parametrize("B", [12, 40])
+def test_truncated_small_top_k_fp32(sv, V, B):
+    """The fp32 candidate-list pass on fp32 values that no 16-bit format
+    holds (small_top_k_rows in fp32: ties, -inf masks, +-0, magnitudes near
+    3e38, ascending rows), against the oracle, with 1024 (B = 12) and 256
+    (B = 40) threads per row; constant rows overflow the lists and take the
+    radix passes."""
+    g = torch.Generator(device=DEV).manual_seed(3 * V + B)
+    k = 3
+    z = small_top_k_rows(B * (k + 1), V, torch.float32, g).view(B, k + 1, V)
+    y = small_top_k_rows(B * k + 5, V, torch.float32, g)[5:].view(B, k, V)
+    u = synthetic.uniforms24((B, k + 1), g, DEV)
+    w = synthetic.Workload(synthetic.WORKLOADS[1], z, y, None, u, 0.8)
+    for top_k, top_p in ((1, 1.0), (5, 0.9), (50, 0.8), (63, 1.0), (64, 0.5), (256, 0.99)):
+        x = torch.from_numpy(truncated_drafts(f32(y), 0.8, top_k, top_p, 17)).to(DEV)
+        check(sv, w, 0.8, x, top_k, top_p)
+
+
 @pytest.mark.parametrize("V", [32767, 32768, 32769])
-def test_truncated_fp32_lds_boundary(sv, V):
-    """fp32 rows of up to 32768 logits run the radix passes on an LDS copy,
-    longer ones stream the row for every pass: both sides of the switch."""
-    w, T, x = workload(3, 3, V, "fp32", V, 40, 0.9)
-    check(sv, w, T, x, 40, 0.9)
+@pytest.mark.parametrize("top_k,top_p", [(0, 0.9), (300, 0.9), (40, 0.9)])
+def test_truncated_fp32_lds_boundary(sv, V, top_k, top_p):
+    """Without a top-k of at most 256, fp32 rows of up to 32768 logits run the
+    radix passes on an LDS copy and longer ones stream the row for every
+    pass: both sides of the switch (top-k 40 takes the candidate lists)."""
+    w, T, x = workload(3, 3, V, "fp32", V, top_k, top_p)
+    check(sv, w, T, x, top_k, top_p)
 
 
 def test_truncated_fp32_large_vocabulary(sv):
-    """fp32 rows take the radix passes (three digits); at V = 128256."""
+    """fp32 rows at V = 128256: top-k 50 takes the candidate lists, top-p
+    alone the radix passes (three digits, the row streamed for each)."""
     w, T, x = workload(2, 2, 128256, "fp32", 61, 50, 0.8)
     check(sv, w, T, x, 50, 0.8)
     w, T, x = workload(2, 2, 128256, "fp32", 62, 0, 0.95)
@@ -452,9 +479,9 @@ def random_small_top_k_case(i):
 
 @pytest.mark.parametrize("i", range(24))
 def test_random_small_top_k_equals_fp32(sv, i):
-    """The candidate-list pass (16-bit rows, top-k <= 256) against the fp32
-    radix passes on the same (upcast) rows, bit for bit, over a seeded sweep
-    of shapes, settings and value laws (random_small_top_k_case)."""
+    """The candidate-list pass for 16-bit rows against the one for fp32 rows
+    on the same (upcast) rows, bit for bit, over a seeded sweep of shapes,
+    settings and value laws (random_small_top_k_case)."""
     dtype, V, rows, top_k, top_p, law, scale = random_small_top_k_case(i)
     print(f"case {i}: {dtype} V={V} rows={rows} top_k={top_k} top_p={top_p} law={law} scale={scale:.2f}",
           flush=True)
