@@ -78,6 +78,12 @@ constexpr long long kSampleBlocks = 16384;
 // went from 200 to 210 us and workload 5 (16384) from 666 to 691 us.
 constexpr long long kFuseDecideBlocks = 2048;
 
+// Fused passes of at most this many workgroups also make the draw, in each
+// sequence's last workgroup (one dependent launch fewer; every workgroup
+// then pays an agent-scope release, an L2 write-back on this chip).
+constexpr long long kFusePickBlocks = 64;
+static_assert(kFusePickBlocks <= kBlock, "the first kernel's workgroup 0 zeroes one counter per thread");
+
 struct SamplePlan {
     int nchunks;
     int vec_per_chunk;
@@ -110,11 +116,12 @@ struct Workspace {
     float* chunk_sums;
     int* lists;                        // early exit: two lists of B sequence ids
     int* counts;                       // early exit: their two counters
+    int* done;                         // the draw in the chunk pass: B counters
     size_t bytes;
 };
 
 // Layout: [split partials][truncated rows][sample descriptors][chunk totals]
-// [work lists][counters], each region 256-byte aligned.
+// [work lists][counters][draw counters], each region 256-byte aligned.
 Workspace layout(char* base, int B, long long rows, int V)
 {
     Workspace w;
@@ -133,6 +140,8 @@ Workspace layout(char* base, int B, long long rows, int V)
     off += align_up((size_t)2 * B * sizeof(int));
     w.counts = base ? reinterpret_cast<int*>(base + off) : nullptr;
     off += align_up(2 * sizeof(int));
+    w.done = base ? reinterpret_cast<int*>(base + off) : nullptr;
+    off += align_up((size_t)B * sizeof(int));
     w.bytes = off;
     return w;
 }
@@ -217,7 +226,7 @@ int greedy_impl(const void* target_logits, long long target_row_stride,
                                       out_tokens, out_num_accepted, workspace, workspace_bytes, hip_stream, gc);
     if (status != SV_OK) return status;
 
-    StatsArgs sa;
+    StatsArgs sa{};
     sa.target = target_logits;
     sa.t_stride = target_row_stride;
     sa.draft = nullptr;
@@ -316,13 +325,14 @@ DecideSampleArgs decide_sample_args(const void* target_logits, long long target_
     return da;
 }
 
-// The sampler's arguments: the round's one draw per sequence.
+// The sampler's arguments: the round's one draw per sequence (in the chunk
+// pass when `pick_in_pass`).
 SampleArgs sampler_args(const void* target_logits, long long target_row_stride,
                         const void* draft_logits, long long draft_row_stride,
-                        int B, int k, int V, const SampleCall& sc, int* out_tokens)
+                        int B, int k, int V, const SampleCall& sc, int* out_tokens, bool pick_in_pass = false)
 {
     const SamplePlan pp = plan_sample(B, sc.sp.nvec);
-    SampleArgs ma;
+    SampleArgs ma{};
     ma.target = target_logits;
     ma.t_stride = target_row_stride;
     ma.draft = draft_logits;
@@ -340,6 +350,7 @@ SampleArgs sampler_args(const void* target_logits, long long target_row_stride,
     ma.out_row = k + 1;
     ma.n_target_rows = B * (k + 1);
     ma.n_draft_rows = B * k;
+    ma.done = pick_in_pass ? sc.w.done : nullptr;
     return ma;
 }
 
@@ -357,10 +368,14 @@ int sample_impl(const void* target_logits, long long target_row_stride,
                                       dtype, out_tokens, out_num_accepted, workspace, workspace_bytes,
                                       hip_stream, sc);
     if (status != SV_OK) return status;
+    // small passes decide the round and make the draw in the chunk pass's
+    // launch, its counters zeroed by the first kernel
+    const SamplePlan pp = plan_sample(B, sc.sp.nvec);
+    const bool pick_in_pass = (long long)B * pp.blocks_per_seq <= kFusePickBlocks;
 
     if (mark(tm.begin, sc.st) != hipSuccess) return SV_EHIP;
     if (sc.trunc) {
-        TruncArgs ta;
+        TruncArgs ta{};
         ta.target = target_logits;
         ta.t_stride = target_row_stride;
         ta.draft = draft_logits;
@@ -372,9 +387,11 @@ int sample_impl(const void* target_logits, long long target_row_stride,
         ta.top_k = top_k;
         ta.top_p = top_p;
         ta.rows = sc.w.trunc;
+        ta.zero = pick_in_pass ? sc.w.done : nullptr;
+        ta.n_zero = pick_in_pass ? B : 0;
         if (launch_trunc_rows(dtype, sc.vec, ta, sc.st) != hipSuccess) return SV_EHIP;
     } else {
-        StatsArgs sa;
+        StatsArgs sa{};
         sa.target = target_logits;
         sa.t_stride = target_row_stride;
         sa.draft = draft_logits;
@@ -387,6 +404,8 @@ int sample_impl(const void* target_logits, long long target_row_stride,
         sa.vec_per_split = sc.sp.vec_per_split;
         sa.c = sc.c;
         sa.partials = sc.w.partials;
+        sa.zero = pick_in_pass ? sc.w.done : nullptr;
+        sa.n_zero = pick_in_pass ? B : 0;
         if (launch_softmax_stats(dtype, sc.vec, sa, sc.st) != hipSuccess) return SV_EHIP;
     }
     if (mark(tm.end, sc.st) != hipSuccess) return SV_EHIP;
@@ -394,8 +413,8 @@ int sample_impl(const void* target_logits, long long target_row_stride,
     const DecideSampleArgs da =
         decide_sample_args(target_logits, target_row_stride, draft_logits, draft_row_stride, draft_tokens,
                            uniforms, lenience, B, k, V, sc, out_tokens, out_num_accepted, out_p_x, out_q_x);
-    const SampleArgs ma =
-        sampler_args(target_logits, target_row_stride, draft_logits, draft_row_stride, B, k, V, sc, out_tokens);
+    const SampleArgs ma = sampler_args(target_logits, target_row_stride, draft_logits, draft_row_stride, B, k, V,
+                                       sc, out_tokens, pick_in_pass);
     // Small passes decide in the chunk pass's own launch (one dependent
     // launch fewer); large ones decide in a kernel of their own, since every
     // chunk workgroup would repeat its sequence's decision and scattered
@@ -429,7 +448,7 @@ int candidates_impl(const void* target_logits, long long row_stride,
     hipStream_t st = static_cast<hipStream_t>(hip_stream);
 
     const StatsPlan sp = plan_stats(rows, V);
-    StatsArgs sa;
+    StatsArgs sa{};
     sa.target = target_logits;
     sa.t_stride = row_stride;
     sa.draft = nullptr;

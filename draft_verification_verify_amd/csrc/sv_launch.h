@@ -41,6 +41,8 @@ struct StatsArgs {
     int vec_per_split;
     float c;                           // log2(e) / T (softmax statistics only)
     void* partials;                    // [n_rows][splits] SoftPartial or ArgPartial
+    int* zero;                         // softmax statistics: n_zero counters that a later
+    int n_zero;                        // kernel of the call needs at 0 (<= kBlock; else null, 0)
 };
 
 // One sampling step per sequence, prepared by the decision kernel: draw from
@@ -91,6 +93,8 @@ struct TruncArgs {
     float top_p;
     TruncRow* rows;
     int only_marked;                   // radix kernel: only rows whose pad the exact kernel set to 1
+    int* zero;                         // n_zero counters zeroed by the first launch, as in
+    int n_zero;                        // StatsArgs (null, 0: none)
 };
 
 struct DecideSampleArgs {
@@ -156,6 +160,8 @@ struct SampleArgs {
     int* out_tokens;                   // [B][out_row]
     int out_row;
     int n_target_rows, n_draft_rows;   // bounds every descriptor is checked against
+    int* done;                         // [B] the draw in the chunk pass: workgroups finished per
+                                       // sequence, zeroed by the call's first kernel (else null)
 };
 
 constexpr int kMaxChunks = 128;

@@ -17,6 +17,8 @@
 //  - k_sample_pick, one workgroup per sequence, accumulates the chunk totals
 //    in chunk order, finds the chunk where u * total is crossed, rescans only
 //    that chunk and resolves the token with a workgroup prefix scan.
+// A chunk pass of a few dozen workgroups makes the draw itself instead, in
+// the last workgroup of each sequence to finish (k_decide_chunks, PICK).
 // A round's total is the same block scan in both kernels and a chunk's total
 // is the sequential sum of its rounds' totals, so the two kernels agree bit
 // for bit; every reduction runs in a fixed order, so draws are deterministic.
@@ -265,6 +267,76 @@ __device__ __forceinline__ void chunk_totals(const SampleArgs& a, int b, int g, 
     }
 }
 
+// The draw of sequence b from its chunk totals and descriptor d: accumulate
+// the totals in chunk order, find the chunk where u * total is crossed,
+// rescan only that chunk.  Called by every thread of one workgroup.
+struct PickShared {
+    float lds[kWaves];
+    int ilds[kWaves];
+    float sums[kMaxChunks];
+    int chunk;
+    float rem;
+};
+
+template <int DT, bool VEC, bool MASK>
+__device__ __forceinline__ void pick_sequence(const SampleArgs& a, int b, const SampleDesc& d, float my_sum,
+                                              PickShared& ps)
+{
+    constexpr int ES = DT == DT_F32 ? 4 : 2;
+    if (!desc_ok(a, d)) return;                   // uniform across the workgroup
+    const char* zr = row_ptr(a.target, d.t_row, a.t_stride, ES);
+    const char* yr = d.kind == 0 ? row_ptr(a.draft, d.d_row, a.d_stride, ES) : zr;
+
+    if ((int)threadIdx.x < a.nchunks) ps.sums[threadIdx.x] = my_sum;
+    __syncthreads();
+    int kind = d.kind;
+    double S = 0.0;
+    for (int i = 0; i < a.nchunks; ++i) S += (double)ps.sums[i];
+    if (!(S > 0.0) && kind == 0) {
+        // no residual mass (p = q after rounding): draw from p instead
+        kind = 1;
+        for (int i = 0; i < a.nchunks; ++i) {
+            const int e0 = i * a.vec_per_chunk;
+            const int e1 = min(e0 + a.vec_per_chunk, a.nvec);
+            const float t = chunk_total<DT, VEC, MASK>(a, zr, yr, kind, d, e0, e1, ps.lds);
+            if (threadIdx.x == 0) ps.sums[i] = t;
+        }
+        __syncthreads();
+        S = 0.0;
+        for (int i = 0; i < a.nchunks; ++i) S += (double)ps.sums[i];
+    }
+    if (threadIdx.x == 0) {
+        const double thr = (double)d.u * S;
+        double pre = 0.0;
+        int cs = -1, lastpos = -1;
+        float rem = 0.f;
+        for (int i = 0; i < a.nchunks; ++i) {
+            const double nx = pre + (double)ps.sums[i];
+            if (ps.sums[i] > 0.f) lastpos = i;
+            if (cs < 0 && nx > thr) {
+                cs = i;
+                rem = (float)(thr - pre);
+            }
+            pre = nx;
+        }
+        if (cs < 0) {                  // rounding left no crossing: the last positive chunk, its end
+            cs = lastpos < 0 ? 0 : lastpos;
+            rem = ps.sums[cs];
+        }
+        ps.chunk = cs;
+        ps.rem = fmaxf(rem, 0.f);
+    }
+    __syncthreads();
+    const int cs = ps.chunk;
+    const int e0 = cs * a.vec_per_chunk;
+    const int e1 = min(e0 + a.vec_per_chunk, a.nvec);
+    int tok = chunk_pick<DT, VEC, MASK>(a, zr, yr, kind, d, e0, e1, ps.rem, ps.lds, ps.ilds);
+    if (threadIdx.x == 0) {
+        if (tok < 0 || tok >= a.V) tok = 0;    // only for inputs outside the contract
+        a.out_tokens[(long long)b * a.out_row + d.out_pos] = tok;
+    }
+}
+
 // The chunk pass after a separate decision (early exit): the descriptor
 // comes from the decision kernels.
 template <int DT, bool VEC, bool MASK>
@@ -284,11 +356,20 @@ __global__ __launch_bounds__(kBlock) void k_sample_chunks(SampleArgs a)
 // the descriptor the draw reads.  Removes a dependent launch, for the price
 // of reading the sequence's row statistics (a few hundred bytes) once per
 // workgroup.  MASK: truncated rows.
-template <int DT, bool VEC, bool MASK>
+//
+// PICK (small passes): the sequence's last workgroup to finish also makes the
+// draw, found with a per-sequence counter (a.done, zeroed by the call's first
+// kernel): each workgroup's thread 0, which wrote its chunk totals, adds 1 with
+// agent-scope release and acquire, and the workgroup that sees
+// blocks_per_seq - 1 reads every total after an agent-scope acquire.  On this
+// chip each such release writes back the XCD's L2 and each acquire
+// invalidates it: cheap for a few dozen workgroups, ruinous for thousands.
+template <int DT, bool VEC, bool MASK, bool PICK>
 __global__ __launch_bounds__(kBlock) void k_decide_chunks(DecideSampleArgs da, SampleArgs a)
 {
     __shared__ float lds[kWaves];
     __shared__ SampleDesc s_desc;
+    __shared__ int s_last;
     const int b = blockIdx.x / a.blocks_per_seq;
     const int g = blockIdx.x - b * a.blocks_per_seq;
     if (threadIdx.x < 64) {
@@ -299,76 +380,32 @@ __global__ __launch_bounds__(kBlock) void k_decide_chunks(DecideSampleArgs da, S
     __syncthreads();
     const SampleDesc d = s_desc;
     chunk_totals<DT, VEC, MASK>(a, b, g, d, lds);
+    if constexpr (PICK) {
+        if (threadIdx.x == 0) {
+            const int before = __hip_atomic_fetch_add(a.done + b, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            s_last = before == a.blocks_per_seq - 1;
+        }
+        __syncthreads();
+        if (!s_last) return;                      // uniform across the workgroup
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __shared__ PickShared ps;
+        const int ct = min((int)threadIdx.x, a.nchunks - 1);
+        const float my_sum = a.chunk_sums[(long long)b * a.nchunks + ct];
+        pick_sequence<DT, VEC, MASK>(a, b, d, my_sum, ps);
+    }
 }
 
 // The draw: one workgroup per sequence.
 template <int DT, bool VEC, bool MASK>
 __global__ __launch_bounds__(kBlock) void k_sample_pick(SampleArgs a)
 {
-    __shared__ float lds[kWaves];
-    __shared__ int ilds[kWaves];
-    __shared__ float s_sums[kMaxChunks];
-    __shared__ int s_chunk;
-    __shared__ float s_rem;
-    constexpr int ES = DT == DT_F32 ? 4 : 2;
-
+    __shared__ PickShared ps;
     const int b = blockIdx.x;
     // the chunk totals do not depend on the descriptor: both loads go out together
     const int ct = min((int)threadIdx.x, a.nchunks - 1);
     const float my_sum = a.chunk_sums[(long long)b * a.nchunks + ct];
     const SampleDesc d = a.desc[b];
-    if (!desc_ok(a, d)) return;                   // uniform across the workgroup
-    const char* zr = row_ptr(a.target, d.t_row, a.t_stride, ES);
-    const char* yr = d.kind == 0 ? row_ptr(a.draft, d.d_row, a.d_stride, ES) : zr;
-
-    if ((int)threadIdx.x < a.nchunks) s_sums[threadIdx.x] = my_sum;
-    __syncthreads();
-    int kind = d.kind;
-    double S = 0.0;
-    for (int i = 0; i < a.nchunks; ++i) S += (double)s_sums[i];
-    if (!(S > 0.0) && kind == 0) {
-        // no residual mass (p = q after rounding): draw from p instead
-        kind = 1;
-        for (int i = 0; i < a.nchunks; ++i) {
-            const int e0 = i * a.vec_per_chunk;
-            const int e1 = min(e0 + a.vec_per_chunk, a.nvec);
-            const float t = chunk_total<DT, VEC, MASK>(a, zr, yr, kind, d, e0, e1, lds);
-            if (threadIdx.x == 0) s_sums[i] = t;
-        }
-        __syncthreads();
-        S = 0.0;
-        for (int i = 0; i < a.nchunks; ++i) S += (double)s_sums[i];
-    }
-    if (threadIdx.x == 0) {
-        const double thr = (double)d.u * S;
-        double pre = 0.0;
-        int cs = -1, lastpos = -1;
-        float rem = 0.f;
-        for (int i = 0; i < a.nchunks; ++i) {
-            const double nx = pre + (double)s_sums[i];
-            if (s_sums[i] > 0.f) lastpos = i;
-            if (cs < 0 && nx > thr) {
-                cs = i;
-                rem = (float)(thr - pre);
-            }
-            pre = nx;
-        }
-        if (cs < 0) {                  // rounding left no crossing: the last positive chunk, its end
-            cs = lastpos < 0 ? 0 : lastpos;
-            rem = s_sums[cs];
-        }
-        s_chunk = cs;
-        s_rem = fmaxf(rem, 0.f);
-    }
-    __syncthreads();
-    const int cs = s_chunk;
-    const int e0 = cs * a.vec_per_chunk;
-    const int e1 = min(e0 + a.vec_per_chunk, a.nvec);
-    int tok = chunk_pick<DT, VEC, MASK>(a, zr, yr, kind, d, e0, e1, s_rem, lds, ilds);
-    if (threadIdx.x == 0) {
-        if (tok < 0 || tok >= a.V) tok = 0;    // only for inputs outside the contract
-        a.out_tokens[(long long)b * a.out_row + d.out_pos] = tok;
-    }
+    pick_sequence<DT, VEC, MASK>(a, b, d, my_sum, ps);
 }
 
 // The chunk pass, by k_decide_chunks when `da` is given (and then deciding
@@ -379,10 +416,15 @@ static hipError_t launch_pair(int B, const DecideSampleArgs* da, const SampleArg
 {
     const dim3 grid((unsigned)((long long)B * a.blocks_per_seq));
     hipError_t e;
+    if (da && a.done) {                           // the draw in the same launch
+        void* args[] = {const_cast<DecideSampleArgs*>(da), const_cast<SampleArgs*>(&a)};
+        return hipLaunchKernel(reinterpret_cast<const void*>(k_decide_chunks<DT, VEC, MASK, true>), grid,
+                               dim3(kBlock), args, 0, st);
+    }
     if (da) {
         void* args[] = {const_cast<DecideSampleArgs*>(da), const_cast<SampleArgs*>(&a)};
-        e = hipLaunchKernel(reinterpret_cast<const void*>(k_decide_chunks<DT, VEC, MASK>), grid, dim3(kBlock),
-                            args, 0, st);
+        e = hipLaunchKernel(reinterpret_cast<const void*>(k_decide_chunks<DT, VEC, MASK, false>), grid,
+                            dim3(kBlock), args, 0, st);
     } else {
         void* args[] = {const_cast<SampleArgs*>(&a)};
         e = hipLaunchKernel(reinterpret_cast<const void*>(k_sample_chunks<DT, VEC, MASK>), grid, dim3(kBlock),

@@ -309,6 +309,13 @@ __device__ __forceinline__ void hist_pass(const Src& src, int L, uint32_t prefix
     *above_mass = MASS ? block_sum_u64(am, sh.red) : 0;
 }
 
+// The counters a later kernel of the call needs at zero, by the first
+// launch's workgroup 0.
+__device__ __forceinline__ void zero_counters(const TruncArgs& a)
+{
+    if (blockIdx.x == 0 && (int)threadIdx.x < a.n_zero) a.zero[threadIdx.x] = 0;
+}
+
 template <int DT>
 __device__ __forceinline__ const char* trunc_row_ptr(const TruncArgs& a, int row)
 {
@@ -408,6 +415,7 @@ __global__ __launch_bounds__(kTB) void k_trunc_rows_lds(TruncArgs a)
 {
     __shared__ Shared sh;
     __shared__ __attribute__((aligned(16))) float buf[kLdsRowMax];
+    zero_counters(a);
     for (int row = blockIdx.x; row < a.n_rows; row += gridDim.x) {
         load_row_lds<VEC>(buf, trunc_row_ptr<DT_F32>(a, row), a.V);
         trunc_row_radix<DT_F32>(a, row, sh, LdsRow{buf, a.V});
@@ -425,6 +433,7 @@ __global__ __launch_bounds__(kTB) void k_trunc_rows(TruncArgs a)
     __shared__ int marked[kTB];
     __shared__ int n_marked;
     if (!a.only_marked) {
+        zero_counters(a);
         for (int row = blockIdx.x; row < a.n_rows; row += gridDim.x)
             trunc_row_radix<DT>(a, row, sh, StreamRow<DT, VEC>{trunc_row_ptr<DT>(a, row), a.V});
         return;
@@ -648,6 +657,7 @@ __global__ __launch_bounds__(kT16) void k_trunc16(TruncArgs a)
     const int nfull = V >> 3;
     const int R2 = 2 * ((nfull + 2 * kRound - 1) / (2 * kRound));   // rounds per row, even
     u32x4* h4 = reinterpret_cast<u32x4*>(hist);
+    zero_counters(a);
     auto row_of = [&](int r) -> const char* {
         return r < a.n_target_rows ? row_ptr(a.target, r, a.t_stride, ES)
                                    : row_ptr(a.draft, r - a.n_target_rows, a.d_stride, ES);
@@ -1150,6 +1160,7 @@ __global__ __launch_bounds__(kTK) __attribute__((amdgpu_waves_per_eu(8))) void k
         }
     };
     if (lane == 0) sh.over[wv] = 0u;
+    zero_counters(a);
     hc[t] = 0u;                        // the merge's first histogram (kTK == 256 bins)
     if (t == 0) sh.nk = 0u;
 
@@ -1579,6 +1590,7 @@ void k_topk32(TruncArgs a)
         take(q.w, ok);
     };
     if (lane == 0) sh.over[wv] = 0u;
+    zero_counters(a);
     if (t == 0) sh.nk = 0u;
 
     // the stream: vector t + i * NT at step i, in groups of two steps; two
