@@ -60,9 +60,14 @@ def replay_and_compare(g, outs, load, eager, n):
 
 @pytest.mark.parametrize("mode", ["sample", "greedy", "sample_lazy", "greedy_lazy", "truncated",
                                   "truncated_top_p", "lenient"])
-def test_chain_entry_points_replay(sv, mode):
-    B, k, V = 48, 6, 32000
-    sets = chain_sets(4, B, k, V, "bf16")
+@pytest.mark.parametrize("B,k,V,dtype", [(48, 6, 32000, "bf16"), (4, 4, 32000, "fp32")])
+def test_chain_entry_points_replay(sv, mode, B, k, V, dtype):
+    """B = 48: the draw in a kernel of its own; B = 4 (64 chunk workgroups, the
+    most for which the chunk pass makes the draw itself): the per-sequence
+    counters must start every replay at zero, cleared by the first kernel
+    (no memset is captured); fp32 truncation takes the 1024-thread candidate
+    lists and the radix passes from LDS."""
+    sets = chain_sets(4, B, k, V, dtype)
     tgt = sets[0].target.clone()
     dft = sets[0].draft.clone()
     x = sets[0].tokens.clone()
