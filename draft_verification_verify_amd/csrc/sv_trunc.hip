@@ -933,8 +933,10 @@ __global__ __launch_bounds__(kT16) void k_trunc16(TruncArgs a)
 // With top-k on, only the top_k largest logits (with the ties at the
 // boundary) can be kept, so for top_k <= kTopkMax a row needs no histogram of
 // every pattern.  One 256-thread workgroup takes one row, eight to a CU (the
-// analysis of one row overlaps the streaming of the others); each wave keeps,
-// in LDS, a list of the 32-bit words (two logits each) it has streamed that
+// analysis of one row overlaps the streaming of the others), or, when the
+// rows do not outnumber the compute units, one 1024-thread workgroup with 16
+// list words per lane, so that few rows keep many loads in flight.  Each wave
+// keeps, in LDS, a list of the 32-bit words (two logits each) it has streamed that
 // may still hold a kept logit, and a floor F: the list holds every word with
 // a logit whose key is at least F.  When a lane's part of the list fills up,
 // the wave raises F to the (top_k + 1)-th largest key at or above F in its
@@ -942,8 +944,9 @@ __global__ __launch_bounds__(kT16) void k_trunc16(TruncArgs a)
 // the row's top_k-th largest key, and the row has more than top_k finite
 // logits) and drops the words with nothing left above it.  F starts just
 // above -inf, so an -inf logit never counts, or, for top_k < 64, at the
-// smallest of the wave's 64 lane maxima over its first vectors if positive
-// (64 different logits are at least that large).
+// (top_k + 1)-th largest of the wave's 64 lane maxima over its first vectors
+// if positive (that many different logits are at least that large; found bit
+// by bit with ballots).
 //
 // After the stream the workgroup merges its waves' lists above the largest
 // floor Fg: the top_k-th largest key among them is the row's; if no wave
@@ -967,20 +970,24 @@ __global__ __launch_bounds__(kT16) void k_trunc16(TruncArgs a)
 // falls as the pattern, read unsigned, grows, so a word may hold one iff the
 // smaller of its halves, read unsigned, is at most 0x10000 - F.
 
-constexpr int kTK = 256;               // threads per workgroup
-constexpr int kTKW = kTK / 64;
-constexpr int kSlots = 12;             // list words per lane
 constexpr int kTopkMax = 256;
 constexpr int kKeptMax = 512;          // kept keys gathered after top-k
 
+// list words per lane: 16 with 1024 threads (one workgroup to a CU), 12 with
+// 256 (eight to a CU)
+template <int NT>
+constexpr int kSlots = NT == 1024 ? 16 : 12;
+
+template <int NT>
 struct TopkShared {
-    uint32_t list[kTKW * kSlots * 64];  // wave w, lane l, word j: [w][j * 64 + l]
-    uint32_t whist[kTKW * 256];         // each wave's radix histogram; after the stream, the kept keys
+    static constexpr int NW = NT / 64;
+    uint32_t list[NW * kSlots<NT> * 64];  // wave w, lane l, word j: [w][j * 64 + l]
+    uint32_t whist[NW * 256];           // each wave's radix histogram; after the stream, the kept keys
     u64 hist[256];                      // the workgroup's: counts (low 1 KB) or masses
-    u64 red[kTKW];
-    uint32_t mx[kTKW];
-    uint32_t F[kTKW];
-    uint32_t over[kTKW];
+    u64 red[NW];
+    uint32_t mx[NW];
+    uint32_t F[NW];
+    uint32_t over[NW];
     uint32_t nk;
     uint32_t sel;
     uint32_t total;
@@ -1067,10 +1074,14 @@ __device__ __forceinline__ void find_desc_mass(const u64* h, u64 base, double bu
     above = readlane_u64(a, L);
 }
 
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kTK) __attribute__((amdgpu_waves_per_eu(8))) void k_topk16(TruncArgs a)
+template <int DT, bool VEC, int NT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 256 ? 8 : 4))) void k_topk16(TruncArgs a)
 {
-    __shared__ __attribute__((aligned(16))) TopkShared sh;
+    constexpr int kTK = NT;
+    constexpr int kTKW = NT / 64;
+    constexpr int KS = kSlots<NT>;
+    static_assert(kTKW * 256 >= kKeptMax, "the kept keys reuse the wave histograms");
+    __shared__ __attribute__((aligned(16))) TopkShared<NT> sh;
     const int row = (int)blockIdx.x;
     const int t = (int)threadIdx.x;
     const int lane = t & 63, wv = t >> 6;
@@ -1079,13 +1090,13 @@ __global__ __launch_bounds__(kTK) __attribute__((amdgpu_waves_per_eu(8))) void k
     const int nfull = V >> 3;                                  // >= 1
     const uint32_t K1 = (uint32_t)a.top_k + 1u;
     const uint32_t f0 = (~ninf_bits<DT>() & 0xFFFFu) + 2u;      // just above -inf
-    uint32_t* const lst = sh.list + wv * (kSlots * 64);
+    uint32_t* const lst = sh.list + wv * (KS * 64);
     uint32_t* const wh = sh.whist + wv * 256;
     uint32_t* const hc = reinterpret_cast<uint32_t*>(sh.hist);
     uint32_t F = f0;                   // the wave's floor (uniform)
     uint32_t* const lane_list = lst + lane;
     uint32_t* wp = lane_list;          // this lane's next word
-    uint32_t* const room = lane_list + 64 * (kSlots - 4);   // beyond: no room for a vector
+    uint32_t* const room = lane_list + 64 * (KS - 4);   // beyond: no room for a vector
     int c = 0;                         // this lane's words (while compacting)
 
     // raise the floor and drop the words with nothing above it; all lanes, uniform
@@ -1132,7 +1143,7 @@ __global__ __launch_bounds__(kTK) __attribute__((amdgpu_waves_per_eu(8))) void k
             base += (uint32_t)__popcll(bal);
         }
         wave_lds_sync();
-        if (base > 64u * (kSlots - 4)) {                  // tied at the floor: the radix kernel
+        if (base > 64u * (KS - 4)) {                  // tied at the floor: the radix kernel
             if (lane == 0) sh.over[wv] = 1u;
             F = 0xFFFFu + 0x8000u;                         // no pattern reaches it
             c = 0;
@@ -1161,7 +1172,7 @@ __global__ __launch_bounds__(kTK) __attribute__((amdgpu_waves_per_eu(8))) void k
     };
     if (lane == 0) sh.over[wv] = 0u;
     zero_counters(a);
-    hc[t] = 0u;                        // the merge's first histogram (kTK == 256 bins)
+    if (t < 256) hc[t] = 0u;           // the merge's first histogram
     if (t == 0) sh.nk = 0u;
 
     // the stream: vector t + i * kTK at step i, in groups of four steps; two
@@ -1179,9 +1190,9 @@ __global__ __launch_bounds__(kTK) __attribute__((amdgpu_waves_per_eu(8))) void k
     };
     auto take_group = [&](const Raw<DT> (&buf)[4], int g) {
         if (g == 0 && K1 <= 64u) {     // uniform: a first floor from the first group
-            // each lane's largest logit among its first four vectors: 64
-            // different logits of the row at least as large as the smallest
-            // of them, so (for top_k < 64) it may start the floor if positive
+            // each lane's largest logit among its first four vectors; if
+            // positive, the (top_k + 1)-th largest of the 64 may start the
+            // floor (for top_k < 64)
             int lm = -32768;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -1193,7 +1204,15 @@ __global__ __launch_bounds__(kTK) __attribute__((amdgpu_waves_per_eu(8))) void k
                     lm = max(lm, max(max((int)h2.x, (int)h2.y), max((int)h3.x, (int)h3.y)));
                 }
             }
-            const int mn = wave_min_int(lm);
+            // the K1-th largest of the 64 lane maxima, bit by bit: K1 different
+            // logits are at least that large
+            const uint32_t lu = (uint32_t)(lm + 32768);
+            uint32_t sel = 0u;
+            for (int b = 15; b >= 0; --b) {
+                const uint32_t cand = sel | (1u << b);
+                if ((uint32_t)__popcll(__ballot(lu >= cand)) >= K1) sel = cand;
+            }
+            const int mn = (int)sel - 32768;
             if (mn > 0) F = 0x8000u + (uint32_t)mn;
         }
 #pragma unroll
@@ -1225,11 +1244,22 @@ __global__ __launch_bounds__(kTK) __attribute__((amdgpu_waves_per_eu(8))) void k
     Raw<DT> bufA[4], bufB[4];
     issue(bufA, 0);
     issue(bufB, 1);
-    for (int g = 0; g < ngroups; g += 2) {
-        take_group(bufA, g);
-        issue(bufA, g + 2);            // unconditional: each group waits for its own loads only
-        take_group(bufB, g + 1);
-        issue(bufB, g + 3);
+    if constexpr (NT == 1024) {        // the last two groups after the loop: no load past them
+        for (int g = 0; g + 2 < ngroups; g += 2) {
+            take_group(bufA, g);
+            issue(bufA, g + 2);        // unconditional: each group waits for its own loads only
+            take_group(bufB, g + 1);
+            issue(bufB, g + 3);
+        }
+        take_group(bufA, ngroups - 2);
+        take_group(bufB, ngroups - 1);
+    } else {
+        for (int g = 0; g < ngroups; g += 2) {
+            take_group(bufA, g);
+            issue(bufA, g + 2);        // unconditional: each group waits for its own loads only
+            take_group(bufB, g + 1);
+            issue(bufB, g + 3);
+        }
     }
     if (__ballot(wp > room)) compact();
     if (t == 0) {                      // the partial last vector: at most four words, like a vector,
@@ -1301,7 +1331,7 @@ __global__ __launch_bounds__(kTK) __attribute__((amdgpu_waves_per_eu(8))) void k
     if (topk_on) {
         const uint32_t b1 = sh.sel;
         const uint32_t need = (uint32_t)a.top_k - (uint32_t)sh.above;
-        hc[t] = 0u;
+        if (t < 256) hc[t] = 0u;
         __syncthreads();
         for (int j = 0; j < c; ++j) {
             const uint32_t u = word_keys(lst[j * 64 + lane]);
@@ -1348,7 +1378,7 @@ __global__ __launch_bounds__(kTK) __attribute__((amdgpu_waves_per_eu(8))) void k
         return;
     }
 
-    // the kept logits' masses, two keys per thread at most
+    // the kept logits' masses, two keys per thread at most (one with 1024 threads)
     const float m = value_of_key<DT>(mxk);
     const float cc = a.c;
     u64 f[2] = {0, 0};
@@ -1379,7 +1409,7 @@ __global__ __launch_bounds__(kTK) __attribute__((amdgpu_waves_per_eu(8))) void k
         u64 base = 0;
 #pragma unroll
         for (int level = 0; level < 2; ++level) {
-            sh.hist[t] = 0;
+            if (t < 256) sh.hist[t] = 0;
             __syncthreads();
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -1887,9 +1917,12 @@ hipError_t launch_dt(bool vec, const TruncArgs& a, hipStream_t st)
             return hipLaunchKernel(marked, dim3((unsigned)a.n_rows), dim3(kTB), args, 0, st);
         hipError_t e;
         if (small_topk) {
-            const void* f = vec ? reinterpret_cast<const void*>(k_topk16<DT, true>)
-                                : reinterpret_cast<const void*>(k_topk16<DT, false>);
-            e = hipLaunchKernel(f, dim3((unsigned)a.n_rows), dim3(kTK), args, 0, st);
+            const bool wide = a.n_rows <= compute_units();   // few rows: 1024 threads each
+            const void* f = wide ? (vec ? reinterpret_cast<const void*>(k_topk16<DT, true, 1024>)
+                                        : reinterpret_cast<const void*>(k_topk16<DT, false, 1024>))
+                                 : (vec ? reinterpret_cast<const void*>(k_topk16<DT, true, 256>)
+                                        : reinterpret_cast<const void*>(k_topk16<DT, false, 256>));
+            e = hipLaunchKernel(f, dim3((unsigned)a.n_rows), dim3(wide ? 1024 : 256), args, 0, st);
         } else {
             const void* f = vec ? reinterpret_cast<const void*>(k_trunc16<DT, true>)
                                 : reinterpret_cast<const void*>(k_trunc16<DT, false>);
