@@ -41,11 +41,21 @@ STREAM_KERNELS = ("k_softmax_stats", "k_argmax_stats")
 # 65536-bin histogram pass (k_trunc16) and fp32 rows the radix passes
 TOPK_ONE_PASS_MAX = 256
 LDS_ROW_MAX = 32768                    # fp32 rows up to this run the radix passes from LDS
+# Few rows under such a top-k are cut into slices of at least SPLIT_MIN_BYTES
+# of whole 8-logit vectors, about SPLIT_TARGET workgroups in all, at most
+# SPLIT_MAX per row; each slice's candidates go to k_trunc_merge
+SPLIT_TARGET, SPLIT_MIN_BYTES, SPLIT_MAX = 1024, 16384, 32
 TRUNC_NOTES = {
     "k_topk16": "k_topk16 (one pass per 16-bit row: per-wave lists of the candidates above a "
                 "rising floor) followed by k_trunc_rows over the rows it marked",
     "k_topk32": "k_topk32 (one pass per fp32 row: per-wave lists of the candidates above a "
                 "rising floor) followed by k_trunc_rows over the rows it marked",
+    "k_topk16_sliced": "k_topk16 on row slices (each slice's candidates above its own rising "
+                       "floor) followed by k_trunc_merge (one workgroup per row merges them; "
+                       "the radix passes for rows the slices could not summarise)",
+    "k_topk32_sliced": "k_topk32 on row slices (each slice's candidates above its own rising "
+                       "floor) followed by k_trunc_merge (one workgroup per row merges them; "
+                       "the radix passes for rows the slices could not summarise)",
     "k_trunc16": "k_trunc16 (one pass per 16-bit row: an exact LDS histogram of all 65536 bit "
                  "patterns) followed by k_trunc_rows over the rows it marked",
     "k_trunc_rows_lds": "k_trunc_rows_lds (radix selection on an LDS copy of each fp32 row, "
@@ -55,9 +65,19 @@ TRUNC_NOTES = {
 }
 
 
-def truncation_kernel(es: int, V: int, top_k: int) -> str:
-    """The launch that summarises every row for truncated sampling."""
+def split_slices(n_rows: int, V: int, es: int) -> int:
+    """Slices per row for the candidate-list pass (1: rows whole), for rows
+    of V logits of es bytes."""
+    s = min(SPLIT_TARGET // max(n_rows, 1), (V // 8) // (SPLIT_MIN_BYTES // (8 * es)), SPLIT_MAX)
+    return s if s >= 2 else 1
+
+
+def truncation_kernel(es: int, V: int, top_k: int, n_rows: int) -> str:
+    """The launch that summarises every row for truncated sampling, for
+    n_rows rows of V logits of es bytes."""
     small_topk = 1 <= top_k <= TOPK_ONE_PASS_MAX and top_k < V
+    if small_topk and V >= 8 and split_slices(n_rows, V, es) > 1:
+        return "k_topk16_sliced" if es == 2 else "k_topk32_sliced"
     if es == 2:
         return "k_topk16" if small_topk and V >= 8 else ("k_trunc16" if V >= 8 else "k_trunc_rows")
     if small_topk and V >= 8:
@@ -409,7 +429,7 @@ def main():
         vecs = CEILING_VECS if args.ceiling_vec < 0 else (args.ceiling_vec,)
         ceiling = stream_ceiling(bufs, max(args.steps, 20), vecs)
     kernel_name = {"sample": "k_softmax_stats", "lenient": "k_softmax_stats",
-                   "truncated": truncation_kernel(es, V, args.top_k)}.get(args.mode, "k_argmax_stats")
+                   "truncated": truncation_kernel(es, V, args.top_k, cfg0.B * stream_rows)}.get(args.mode, "k_argmax_stats")
     traffic = measured_traffic(kernel_name, cid) \
         if (kernel_name in STREAM_KERNELS and args.vocab_shard == 1 and args.mode != "tree"
             and not lazy) else None

@@ -117,12 +117,16 @@ struct Workspace {
     int* lists;                        // early exit: two lists of B sequence ids
     int* counts;                       // early exit: their two counters
     int* done;                         // the draw in the chunk pass: B counters
+    uint32_t* cand;                    // truncation of few rows: candidate keys per row slice
+    uint32_t* cand_hdr;                // and each slice's floor, largest key, count, overflow
     size_t bytes;
 };
 
 // Layout: [split partials][truncated rows][sample descriptors][chunk totals]
-// [work lists][counters][draw counters], each region 256-byte aligned.
-Workspace layout(char* base, int B, long long rows, int V)
+// [work lists][counters][draw counters][slice candidates][slice headers],
+// each region 256-byte aligned; the last two only for a call that cuts its
+// rows into `slices` > 1 (a truncated call with a small top-k, few rows).
+Workspace layout(char* base, int B, long long rows, int V, int slices)
 {
     Workspace w;
     const StatsPlan sp = plan_stats(rows, V);
@@ -142,6 +146,15 @@ Workspace layout(char* base, int B, long long rows, int V)
     off += align_up(2 * sizeof(int));
     w.done = base ? reinterpret_cast<int*>(base + off) : nullptr;
     off += align_up((size_t)B * sizeof(int));
+    const int sl = slices;
+    w.cand = nullptr;
+    w.cand_hdr = nullptr;
+    if (sl > 1) {
+        w.cand = base ? reinterpret_cast<uint32_t*>(base + off) : nullptr;
+        off += align_up((size_t)rows * sl * kCandMax * sizeof(uint32_t));
+        w.cand_hdr = base ? reinterpret_cast<uint32_t*>(base + off) : nullptr;
+        off += align_up((size_t)rows * sl * 4 * sizeof(uint32_t));
+    }
     w.bytes = off;
     return w;
 }
@@ -189,7 +202,7 @@ int prepare_greedy(const void* target_logits, long long target_row_stride, const
     if (B < 1 || k < 1 || k > SV_MAX_K || V < 1 || V > kMaxV || target_row_stride < V) return SV_EINVAL;
     gc.rows = (long long)B * (k + 1);
     if (!fits_grid(gc.rows, V)) return SV_EINVAL;
-    gc.w = layout(static_cast<char*>(workspace), B, gc.rows, V);
+    gc.w = layout(static_cast<char*>(workspace), B, gc.rows, V, 1);
     if (!workspace || workspace_bytes < gc.w.bytes) return SV_EWORKSPACE;
     gc.st = static_cast<hipStream_t>(hip_stream);
     gc.vec = vec_ok(target_logits, target_row_stride, dtype);
@@ -259,6 +272,7 @@ struct SampleCall {
     float c;
     bool vec;
     bool trunc;                        // top-k or top-p is on
+    int slices;                        // truncation: slices per row (1: none)
     hipStream_t st;
 };
 
@@ -284,7 +298,8 @@ int prepare_sample(const void* target_logits, long long target_row_stride,
     if (!isfinite(cd) || cd > 3.0e38) return SV_EINVAL;
     sc.rows = (long long)B * (2 * k + 1);
     if (!fits_grid(sc.rows, V)) return SV_EINVAL;
-    sc.w = layout(static_cast<char*>(workspace), B, sc.rows, V);
+    sc.slices = sc.trunc ? trunc_slices(sc.rows, V, elem_size(dtype), top_k) : 1;
+    sc.w = layout(static_cast<char*>(workspace), B, sc.rows, V, sc.slices);
     if (!workspace || workspace_bytes < sc.w.bytes) return SV_EWORKSPACE;
     sc.st = static_cast<hipStream_t>(hip_stream);
     sc.c = (float)cd;
@@ -389,6 +404,9 @@ int sample_impl(const void* target_logits, long long target_row_stride,
         ta.rows = sc.w.trunc;
         ta.zero = pick_in_pass ? sc.w.done : nullptr;
         ta.n_zero = pick_in_pass ? B : 0;
+        ta.slices = sc.slices;
+        ta.cand = sc.w.cand;
+        ta.cand_hdr = sc.w.cand_hdr;
         if (launch_trunc_rows(dtype, sc.vec, ta, sc.st) != hipSuccess) return SV_EHIP;
     } else {
         StatsArgs sa{};
@@ -443,7 +461,7 @@ int candidates_impl(const void* target_logits, long long row_stride,
     if (cand_rows && N < 1) return SV_EINVAL;
     const long long rows = (long long)B * (cand_rows ? (long long)N : (long long)C * R);
     if (!fits_grid(rows, V)) return SV_EINVAL;
-    Workspace w = layout(static_cast<char*>(workspace), B, rows, V);
+    Workspace w = layout(static_cast<char*>(workspace), B, rows, V, 1);
     if (!workspace || workspace_bytes < w.bytes) return SV_EWORKSPACE;
     hipStream_t st = static_cast<hipStream_t>(hip_stream);
 
@@ -599,7 +617,7 @@ size_t spec_verify_workspace_bytes(int B, int rows_per_seq, int V, int dtype)
     if (B < 1 || rows_per_seq < 1 || V < 1 || V > kMaxV || !dtype_ok(dtype)) return 0;
     const long long rows = (long long)B * rows_per_seq;
     if (!fits_grid(rows, V)) return 0;
-    return layout(nullptr, B, rows, V).bytes;
+    return layout(nullptr, B, rows, V, split_slices(rows, V, elem_size(dtype))).bytes;   // enough for any call
 }
 
 int spec_verify_greedy(const void* target_logits, long long target_row_stride,
@@ -763,7 +781,7 @@ int spec_verify_sample_noalloc(const void* target_logits, long long target_row_s
     // spec_verify_sample, which follow)
     if (B >= 1 && k >= 1 && k <= SV_MAX_K && V >= 1 && V <= kMaxV && dtype_ok(dtype)) {
         const long long rows = (long long)B * (2 * k + 1);
-        if (fits_grid(rows, V) && layout(nullptr, B, rows, V).bytes > SV_NOALLOC_SCRATCH_BYTES)
+        if (fits_grid(rows, V) && layout(nullptr, B, rows, V, 1).bytes > SV_NOALLOC_SCRATCH_BYTES)
             return SV_ESCRATCH;
     }
     int dev = -1;

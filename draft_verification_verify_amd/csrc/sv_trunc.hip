@@ -970,7 +970,6 @@ __global__ __launch_bounds__(kT16) void k_trunc16(TruncArgs a)
 // falls as the pattern, read unsigned, grows, so a word may hold one iff the
 // smaller of its halves, read unsigned, is at most 0x10000 - F.
 
-constexpr int kTopkMax = 256;
 constexpr int kKeptMax = 512;          // kept keys gathered after top-k
 
 // list words per lane: 16 with 1024 threads (one workgroup to a CU), 12 with
@@ -1074,7 +1073,144 @@ __device__ __forceinline__ void find_desc_mass(const u64* h, u64 base, double bu
     above = readlane_u64(a, L);
 }
 
-template <int DT, bool VEC, int NT>
+// Radix digits of a key's offset o from a base, for keys spanning [base,
+// base + range]: the first level takes the top (up to) 8 of the bits the
+// range needs, each later one the next 8; level l's digit is o's bits
+// [ls, hs) (level 0: every bit from ls up), ls = shift(l), hs = shift(l - 1).
+struct OffDigits {
+    int top;                           // bits the range needs (0: a single key)
+    __device__ explicit OffDigits(uint32_t range) : top(range ? 32 - __clz((int)range) : 0) {}
+    __device__ int shift(int l) const
+    {
+        const int s = top - 8 * (l + 1);
+        return s > 0 ? s : 0;
+    }
+    __device__ static uint32_t digit(uint32_t o, int level, int hs, int ls)
+    {
+        return level == 0 ? o >> ls : (o >> ls) & ((1u << (hs - ls)) - 1u);
+    }
+};
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    return (uint32_t)wave_max_int((int)(v ^ 0x80000000u)) ^ 0x80000000u;
+}
+
+// A slice's candidates, when rows are cut into slices: the keys at or above
+// the slice's floor Fs, the largest floor Fg of its waves when at most
+// kCandMax keys are at or above it, else the K1-th largest key of the lists
+// at or above Fg.  Either way K1 different logits of the row are at least Fs
+// (a wave raises its floor only under K1 of its own keys), so Fs never passes
+// the row's top_k-th largest key, and every key at or above the largest floor
+// of a row's slices is among the row's candidates.  kr: this lane's keys (0 for
+// none; keys below the wave's floor are skipped), F: its wave's floor.  Wave
+// 0 writes the keys and a header (Fs, the largest key, their number, and an
+// overflow flag, set when a wave's list overflowed, when more than CAP keys
+// are at or above the largest floor (the list area's words; two 16-bit keys
+// share a word), or when the keys at or above Fs outnumber kCandMax).  Called
+// by every thread of the workgroup.
+template <int NT, int J, int CAP>
+__device__ __forceinline__ void slice_candidates(const uint32_t (&kr)[J], uint32_t F, uint32_t K1, uint32_t* list, uint32_t* wh0, uint32_t* sF, uint32_t* smx,
+                                                 const uint32_t* sover, uint32_t* snk, uint32_t* cand, uint32_t* hdr)
+{
+    constexpr int NW = NT / 64;
+    const int t = (int)threadIdx.x, lane = t & 63, wv = t >> 6;
+    {
+        uint32_t mx_t = 0;
+#pragma unroll
+        for (int j = 0; j < J; ++j) mx_t = kr[j] > mx_t ? kr[j] : mx_t;
+        const uint32_t mx = wave_max_u32(mx_t);
+        if (lane == 0) {
+            sF[wv] = F;
+            smx[wv] = mx;
+        }
+    }
+    __syncthreads();
+    uint32_t Fg = sF[0], mxk = smx[0], over = sover[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+        Fg = sF[w] > Fg ? sF[w] : Fg;
+        mxk = smx[w] > mxk ? smx[w] : mxk;
+        over |= sover[w];
+    }
+    if (over) {
+        if (t == 0) {
+            hdr[0] = 0u;
+            hdr[1] = 0u;
+            hdr[2] = 0u;
+            hdr[3] = 1u;
+        }
+        return;
+    }
+    // the keys at or above Fg, gathered into the list area (every key is in registers)
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const bool keep = kr[j] >= Fg;     // Fg >= f0 > 0: empty slots never kept
+        const unsigned long long bal = __ballot(keep);
+        if (bal) {
+            const int first = __ffsll((long long)bal) - 1;
+            uint32_t base = 0;
+            if (lane == first) base = atomicAdd(snk, (uint32_t)__popcll(bal));
+            base = (uint32_t)__builtin_amdgcn_readlane((int)base, first);
+            const uint32_t pos = base + lane_prefix(bal);
+            if (keep && pos < (uint32_t)CAP) list[pos] = kr[j];
+        }
+    }
+    __syncthreads();
+    if (wv != 0) return;
+    const uint32_t n = *snk;
+    if (n > (uint32_t)CAP) {           // uniform: more than the list area holds
+        if (lane == 0) {
+            hdr[0] = 0u;
+            hdr[1] = 0u;
+            hdr[2] = 0u;
+            hdr[3] = 1u;
+        }
+        return;
+    }
+    uint32_t Fs = Fg;
+    if (n > (uint32_t)kCandMax) {      // uniform: the K1-th largest (n > K1), one offset digit per level
+        const OffDigits od(mxk - Fg);
+        uint32_t prefix = 0, need = K1;
+        int hs = od.top, ls = od.shift(0);   // level 0 has no prefix
+        for (int level = 0;; ++level) {
+            reinterpret_cast<u32x4*>(wh0)[lane] = u32x4{0u, 0u, 0u, 0u};
+            wave_lds_sync();
+            for (uint32_t i = (uint32_t)lane; i < n; i += 64) {
+                const uint32_t o = list[i] - Fg;
+                if (level == 0 || (o >> hs) == prefix) atomicAdd(&wh0[od.digit(o, level, hs, ls)], 1u);
+            }
+            wave_lds_sync();
+            uint32_t bin, above;
+            find_desc_count(wh0, need, bin, above);
+            wave_lds_sync();
+            prefix = (prefix << (hs - ls)) | bin;
+            need -= above;
+            if (ls == 0) break;
+            hs = ls;
+            ls = od.shift(level + 1);
+        }
+        Fs = Fg + prefix;
+    }
+    uint32_t cnt = 0;
+    for (uint32_t i0 = 0; i0 < n; i0 += 64) {
+        const uint32_t i = i0 + (uint32_t)lane;
+        const uint32_t k = i < n ? list[i] : 0u;
+        const bool keep = k >= Fs;
+        const unsigned long long bal = __ballot(keep);
+        const uint32_t pos = cnt + lane_prefix(bal);
+        if (keep && pos < (uint32_t)kCandMax) cand[pos] = k;
+        cnt += (uint32_t)__popcll(bal);
+    }
+    if (lane == 0) {
+        hdr[0] = Fs;
+        hdr[1] = mxk;
+        hdr[2] = cnt < (uint32_t)kCandMax ? cnt : (uint32_t)kCandMax;
+        hdr[3] = cnt > (uint32_t)kCandMax ? 1u : 0u;
+    }
+}
+
+template <int DT, bool VEC, int NT, bool SPLIT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 256 ? 8 : 4))) void k_topk16(TruncArgs a)
 {
     constexpr int kTK = NT;
@@ -1082,12 +1218,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 256 ? 
     constexpr int KS = kSlots<NT>;
     static_assert(kTKW * 256 >= kKeptMax, "the kept keys reuse the wave histograms");
     __shared__ __attribute__((aligned(16))) TopkShared<NT> sh;
-    const int row = (int)blockIdx.x;
+    // SPLIT: workgroup (row, slice) streams the slice's whole vectors only
+    const int S = SPLIT ? a.slices : 1;
+    const int row = SPLIT ? (int)blockIdx.x / S : (int)blockIdx.x;
+    const int slice = (int)blockIdx.x - row * S;
     const int t = (int)threadIdx.x;
     const int lane = t & 63, wv = t >> 6;
-    const char* rp = trunc_row_ptr<DT>(a, row);
+    const char* const rrow = trunc_row_ptr<DT>(a, row);
     const int V = a.V;
-    const int nfull = V >> 3;                                  // >= 1
+    const int nall = V >> 3;                                   // >= 1
+    const int vps = (nall + S - 1) / S;
+    const int vb = slice * vps;
+    const char* rp = rrow + 16LL * vb;                         // 16 bytes per logical vector
+    const int nfull = (vb + vps < nall ? vb + vps : nall) - vb; // >= 1
+    const bool last_slice = slice == S - 1;
     const uint32_t K1 = (uint32_t)a.top_k + 1u;
     const uint32_t f0 = (~ninf_bits<DT>() & 0xFFFFu) + 2u;      // just above -inf
     uint32_t* const lst = sh.list + wv * (KS * 64);
@@ -1262,9 +1406,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 256 ? 
         }
     }
     if (__ballot(wp > room)) compact();
-    if (t == 0) {                      // the partial last vector: at most four words, like a vector,
-        const unsigned short* e = reinterpret_cast<const unsigned short*>(rp) + 8LL * nfull;
-        const int n = V - 8 * nfull;   // -inf past its end
+    if (last_slice && t == 0) {        // the partial last vector: at most four words, like a vector,
+        const unsigned short* e = reinterpret_cast<const unsigned short*>(rrow) + 8LL * nall;
+        const int n = V - 8 * nall;    // -inf past its end
         for (int j = 0; j < n; j += 2) {
             const uint32_t hi = j + 1 < n ? (uint32_t)e[j + 1] : ninf_bits<DT>();
             const uint32_t x = (uint32_t)e[j] | (hi << 16);
@@ -1273,6 +1417,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 256 ? 
         }
     }
     c = (int)((wp - lane_list) >> 6);
+    if constexpr (SPLIT) {             // both keys of every word, 0 past the list
+        uint32_t kr[2 * KS];
+#pragma unroll
+        for (int j = 0; j < KS; ++j) {
+            const uint32_t u = j < c ? word_keys(lst[j * 64 + lane]) : 0u;
+            kr[2 * j] = u & 0xFFFFu;
+            kr[2 * j + 1] = u >> 16;
+        }
+        const long long sl = (long long)row * S + slice;
+        slice_candidates<NT, 2 * KS, NT * KS>(kr, F, K1, sh.list, sh.whist, sh.F, sh.mx, sh.over, &sh.nk,
+                                     a.cand + sl * kCandMax, a.cand_hdr + sl * 4);
+        return;
+    }
     if (lane == 0) sh.F[wv] = F;
     __syncthreads();
 
@@ -1497,30 +1654,7 @@ __device__ __forceinline__ uint32_t key32(uint32_t x)
     return key_of<DT_F32>(__uint_as_float(x));
 }
 
-// Radix digits of a key's offset o from a base, for keys spanning [base,
-// base + range]: the first level takes the top (up to) 8 of the bits the
-// range needs, each later one the next 8; level l's digit is o's bits
-// [ls, hs) (level 0: every bit from ls up), ls = shift(l), hs = shift(l - 1).
-struct OffDigits {
-    int top;                           // bits the range needs (0: a single key)
-    __device__ explicit OffDigits(uint32_t range) : top(range ? 32 - __clz((int)range) : 0) {}
-    __device__ int shift(int l) const
-    {
-        const int s = top - 8 * (l + 1);
-        return s > 0 ? s : 0;
-    }
-    __device__ static uint32_t digit(uint32_t o, int level, int hs, int ls)
-    {
-        return level == 0 ? o >> ls : (o >> ls) & ((1u << (hs - ls)) - 1u);
-    }
-};
-
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
-{
-    return (uint32_t)wave_max_int((int)(v ^ 0x80000000u)) ^ 0x80000000u;
-}
-
-template <bool VEC, int NT>
+template <bool VEC, int NT, bool SPLIT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 256 ? 8 : 4)))
 void k_topk32(TruncArgs a)
 {
@@ -1528,12 +1662,20 @@ void k_topk32(TruncArgs a)
     constexpr int KS = kS32<NT>;
     static_assert(NW >= 3, "wave 0's histogram and the kept keys fit in the wave histograms");
     __shared__ __attribute__((aligned(16))) Topk32Shared<NT> sh;
-    const int row = (int)blockIdx.x;
+    // SPLIT: workgroup (row, slice) streams the slice's whole vectors only
+    const int S = SPLIT ? a.slices : 1;
+    const int row = SPLIT ? (int)blockIdx.x / S : (int)blockIdx.x;
+    const int slice = (int)blockIdx.x - row * S;
     const int t = (int)threadIdx.x;
     const int lane = t & 63, wv = t >> 6;
-    const char* rp = trunc_row_ptr<DT_F32>(a, row);
+    const char* const rrow = trunc_row_ptr<DT_F32>(a, row);
     const int V = a.V;
-    const int nfull = V >> 3;                                  // >= 1
+    const int nall = V >> 3;                                   // >= 1
+    const int vps = (nall + S - 1) / S;
+    const int vb = slice * vps;
+    const char* rp = rrow + 32LL * vb;                         // 32 bytes per logical vector
+    const int nfull = (vb + vps < nall ? vb + vps : nall) - vb; // >= 1
+    const bool last_slice = slice == S - 1;
     const uint32_t K1 = (uint32_t)a.top_k + 1u;
     const uint32_t f0 = key32(0xFF800000u) + 1u;               // just above -inf
     uint32_t* const lst = sh.list + wv * (KS * 64);
@@ -1692,9 +1834,9 @@ void k_topk32(TruncArgs a)
         }
     }
     if (__ballot(wp > room)) compact();
-    if (t < 2) {                       // the partial last vector: up to four logits on each of two lanes
-        const float* e = reinterpret_cast<const float*>(rp) + 8LL * nfull;
-        const int n = V - 8 * nfull;
+    if (last_slice && t < 2) {         // the partial last vector: up to four logits on each of two lanes
+        const float* e = reinterpret_cast<const float*>(rrow) + 8LL * nall;
+        const int n = V - 8 * nall;
         for (int j = 4 * t; j < n && j < 4 * t + 4; ++j) take(__float_as_uint(e[j]), true);
     }
     c = (int)((wp - lane_list) >> 6);
@@ -1704,6 +1846,12 @@ void k_topk32(TruncArgs a)
     // the wave's last floor, raised on its final list: few keys above the
     // largest floor are left for the merge
     if (F != 0xFFFFFFFFu) raise_floor([&](int j) { return kr[j]; }, KS);
+    if constexpr (SPLIT) {
+        const long long sl = (long long)row * S + slice;
+        slice_candidates<NT, KS, NT * KS>(kr, F, K1, sh.list, sh.whist, sh.F, sh.mx, sh.over, &sh.nk,
+                                 a.cand + sl * kCandMax, a.cand_hdr + sl * 4);
+        return;
+    }
     {
         uint32_t mx_t = 0;             // the largest key in the lists is the row's
 #pragma unroll
@@ -1864,6 +2012,239 @@ void k_topk32(TruncArgs a)
     }
 }
 
+// ---- the merge of a row's slices ---------------------------------------------
+// Rows cut into slices (split_slices > 1, top-k of at most 256): every key of
+// a row at or above the largest floor Fr of its slices is among the slices'
+// candidates, and Fr never passes the row's top_k-th largest key.  One
+// 512-thread workgroup per row gathers them and finds the top_k-th largest,
+// the kept keys' fixed-point masses and the top-p boundary as the one-pass
+// kernels do (the same integers, so the same summary); a row whose slices
+// overflowed, or with more candidates or kept keys than it can gather, takes
+// the radix passes in the same workgroup.  Keys are the slice kernels' own:
+// key_of for fp32, word_keys' form for the 16-bit formats.
+constexpr int kMergeMax = 4096;        // candidates gathered per row
+
+struct MergeShared {
+    uint32_t hdr[kSplitMax][4];
+    uint32_t pre[kSplitMax];           // the slices' candidate counts, exclusive prefix
+    uint32_t total;
+    uint32_t keys[kMergeMax];
+    uint32_t kk[kKeptMax];
+    uint32_t hc[256];
+    u64 hm[256];
+    u64 red[kTW];
+    uint32_t nk;
+    uint32_t nkept;
+    uint32_t sel;
+    uint32_t above;
+    u64 mabove;
+    u64 incl;
+};
+
+template <int DT>
+__device__ __forceinline__ float cand_value(uint32_t k)
+{
+    if constexpr (DT == DT_F32) return value_of_key32(k);
+    else return value_of_key<DT>(k);
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t cand_tau(uint32_t k)
+{
+    if constexpr (DT == DT_F32) return k;
+    else return std_key(k);
+}
+
+// One row's summary from its slices' candidates at or above Fr; false (uniform
+// over the workgroup) when there are more candidates or kept keys than it
+// gathers.
+template <int DT>
+__device__ __forceinline__ bool merge_row(const TruncArgs& a, int row, uint32_t Fr, uint32_t mxk,
+                                          const uint32_t* cand, MergeShared& ms)
+{
+    const int t = (int)threadIdx.x;
+    const int lane = t & 63, wv = t >> 6;
+    const int S = a.slices;
+    const uint32_t f0 = DT == DT_F32 ? key32(0xFF800000u) + 1u : (~ninf_bits<DT>() & 0xFFFFu) + 2u;
+    if (mxk < Fr) {                    // no finite logit
+        if (t == 0) a.rows[row] = TruncRow{-INFINITY, -INFINITY, 0u, 0u};
+        return true;
+    }
+
+    // the candidates at or above Fr: candidate i of the row is entry i - pre[s]
+    // of slice s, the last slice with pre[s] <= i; every load of a round is
+    // issued before the first is used
+    if (wv == 0) {
+        const uint32_t c = lane < S ? ms.hdr[lane][2] : 0u;
+        const uint32_t inc = (uint32_t)wave_scan_u64(c);
+        if (lane < S) ms.pre[lane] = inc - c;
+        if (lane == 63) ms.total = inc;
+    }
+    __syncthreads();
+    const uint32_t total = ms.total;   // at most kSplitMax * kCandMax
+    constexpr int R = 8;
+    for (uint32_t i0 = 0; i0 < total; i0 += R * kTB) {
+        uint32_t q[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint32_t i = i0 + (uint32_t)(t + r * kTB);
+            int s0 = 0, s1 = S - 1;    // pre[0] = 0 <= i
+            while (s0 < s1) {
+                const int mid = (s0 + s1 + 1) >> 1;
+                if (ms.pre[mid] <= i) s0 = mid;
+                else s1 = mid - 1;
+            }
+            q[r] = i < total ? cand[(long long)s0 * kCandMax + (i - ms.pre[s0])] : 0u;
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const bool keep = q[r] >= Fr;   // Fr >= f0 > 0: past the end never kept
+            const unsigned long long bal = __ballot(keep);
+            if (bal) {
+                const int first = __ffsll((long long)bal) - 1;
+                uint32_t base = 0;
+                if (lane == first) base = atomicAdd(&ms.nk, (uint32_t)__popcll(bal));
+                base = (uint32_t)__builtin_amdgcn_readlane((int)base, first);
+                const uint32_t pos = base + lane_prefix(bal);
+                if (keep && pos < (uint32_t)kMergeMax) ms.keys[pos] = q[r];
+            }
+        }
+    }
+    __syncthreads();
+    const uint32_t n = ms.nk;
+    if (n > (uint32_t)kMergeMax) return false;
+
+    // top-k: the top_k-th largest of the n keys, one offset digit per level;
+    // with every finite logit among them (no floor raised) top-k is off for
+    // at most top_k of them
+    const bool topk_on = Fr > f0 || (uint32_t)a.top_k < n;
+    uint32_t lo = Fr;                  // keys >= lo survive top-k
+    if (topk_on) {
+        const OffDigits od(mxk - Fr);
+        uint32_t prefix = 0, need = (uint32_t)a.top_k;
+        int hs = od.top, ls = od.shift(0);   // level 0 has no prefix
+        for (int level = 0;; ++level) {
+            if (t < 256) ms.hc[t] = 0u;      // read by the last find, before the last barrier
+            __syncthreads();
+            for (uint32_t i = (uint32_t)t; i < n; i += kTB) {
+                const uint32_t o = ms.keys[i] - Fr;
+                if (level == 0 || (o >> hs) == prefix) atomicAdd(&ms.hc[od.digit(o, level, hs, ls)], 1u);
+            }
+            __syncthreads();
+            if (wv == 0) {
+                uint32_t bin, above;
+                find_desc_count(ms.hc, need, bin, above);
+                if (lane == 0) {
+                    ms.sel = bin;
+                    ms.above = above;
+                }
+            }
+            __syncthreads();
+            prefix = (prefix << (hs - ls)) | ms.sel;   // rewritten two barriers later
+            need -= ms.above;
+            if (ls == 0) break;
+            hs = ls;
+            ls = od.shift(level + 1);
+        }
+        lo = Fr + prefix;
+    }
+
+    // the kept keys
+    for (uint32_t i0 = 0; i0 < n; i0 += kTB) {
+        const uint32_t i = i0 + (uint32_t)t;
+        const uint32_t k = i < n ? ms.keys[i] : 0u;
+        const bool keep = k >= lo;     // lo >= f0 > 0
+        const unsigned long long bal = __ballot(keep);
+        if (bal) {
+            const int first = __ffsll((long long)bal) - 1;
+            uint32_t base = 0;
+            if (lane == first) base = atomicAdd(&ms.nkept, (uint32_t)__popcll(bal));
+            base = (uint32_t)__builtin_amdgcn_readlane((int)base, first);
+            const uint32_t pos = base + lane_prefix(bal);
+            if (keep && pos < (uint32_t)kKeptMax) ms.kk[pos] = k;
+        }
+    }
+    __syncthreads();
+    const uint32_t nk = ms.nkept;
+    if (nk > (uint32_t)kKeptMax) return false;
+
+    // the kept logits' masses, one per thread
+    const float m = cand_value<DT>(mxk);
+    const uint32_t kt = t < (int)nk ? ms.kk[t] : 0u;
+    const u64 f = t < (int)nk ? fixed40_nb(weight(cand_value<DT>(kt), m, a.c)) : 0;
+    u64 kept = block_sum_u64(f, ms.red);
+    const u64 M = kept;
+    uint32_t tau = topk_on ? cand_tau<DT>(lo) : 0u;   // top-k off: every key
+
+    // top-p: the key at which the mass from the top first reaches top_p * M
+    if (a.top_p < 1.f) {
+        const double budget = (double)a.top_p * (double)M;
+        const OffDigits od(mxk - lo);  // the kept keys: lo .. mxk
+        uint32_t prefix = 0u;
+        u64 base = 0;
+        int hs = od.top, ls = od.shift(0);   // level 0 has no prefix
+        for (int level = 0;; ++level) {
+            if (t < 256) ms.hm[t] = 0;
+            __syncthreads();
+            const uint32_t o = kt - lo;
+            if (f && (level == 0 || (o >> hs) == prefix)) atomicAdd(&ms.hm[od.digit(o, level, hs, ls)], f);
+            __syncthreads();
+            if (wv == 0) {
+                uint32_t bin;
+                u64 above;
+                find_desc_mass(ms.hm, base, budget, bin, above);
+                if (lane == 0) {
+                    ms.sel = bin;
+                    ms.mabove = above;                 // the mass of every larger key
+                    ms.incl = above + ms.hm[bin];      // and the bin's own
+                }
+            }
+            __syncthreads();
+            prefix = (prefix << (hs - ls)) | ms.sel;   // rewritten two barriers later
+            base = ms.mabove;
+            kept = ms.incl;
+            if (ls == 0) break;
+            hs = ls;
+            ls = od.shift(level + 1);
+        }
+        tau = cand_tau<DT>(lo + prefix);
+    }
+    if (t == 0) {
+        const float l2s = (float)(log2((double)kept) - (double)kFixBits);
+        a.rows[row] = TruncRow{m, l2s, tau, 0u};
+    }
+    return true;
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kTB) void k_trunc_merge(TruncArgs a)
+{
+    static_assert(kKeptMax == kTB, "one kept key per thread");
+    static_assert(4 * kSplitMax <= kTB, "one header word per thread");
+    __shared__ Shared sh;              // the radix passes
+    __shared__ __attribute__((aligned(16))) MergeShared ms;
+    const int row = (int)blockIdx.x;
+    const int t = (int)threadIdx.x;
+    const int S = a.slices;
+    const uint32_t* const hdr = a.cand_hdr + (long long)row * S * 4;
+    const uint32_t* const cand = a.cand + (long long)row * S * kCandMax;
+    if (t < 4 * S) ms.hdr[t >> 2][t & 3] = hdr[t];
+    if (t == 0) {
+        ms.nk = 0u;
+        ms.nkept = 0u;
+    }
+    __syncthreads();
+    uint32_t Fr = 0u, mxk = 0u, over = 0u;
+    for (int sl = 0; sl < S; ++sl) {
+        Fr = ms.hdr[sl][0] > Fr ? ms.hdr[sl][0] : Fr;
+        mxk = ms.hdr[sl][1] > mxk ? ms.hdr[sl][1] : mxk;
+        over |= ms.hdr[sl][3];
+    }
+    if (!over && merge_row<DT>(a, row, Fr, mxk, cand, ms)) return;
+    // the slices overflowed, or too many candidates or kept keys: the radix passes
+    trunc_row_radix<DT>(a, row, sh, StreamRow<DT, VEC>{trunc_row_ptr<DT>(a, row), a.V});
+}
+
 // The current device's compute units (queried once per device).
 int compute_units()
 {
@@ -1896,13 +2277,30 @@ hipError_t launch_dt(bool vec, const TruncArgs& a, hipStream_t st)
         return hipLaunchKernel(marked, dim3(grid), dim3(kTB), args, 0, st);
     };
     const bool small_topk = a.top_k >= 1 && a.top_k <= kTopkMax && a.top_k < a.V;
+    // few rows under a small top-k: cut into slices, each summarised by its own
+    // workgroup, merged per row (the merge also runs the radix passes for rows
+    // a slice could not summarise)
+    if (small_topk && a.V >= 8 && a.slices > 1 && a.cand && a.cand_hdr) {
+        const void* f;
+        if constexpr (DT == DT_F32)
+            f = vec ? reinterpret_cast<const void*>(k_topk32<true, 256, true>)
+                    : reinterpret_cast<const void*>(k_topk32<false, 256, true>);
+        else
+            f = vec ? reinterpret_cast<const void*>(k_topk16<DT, true, 256, true>)
+                    : reinterpret_cast<const void*>(k_topk16<DT, false, 256, true>);
+        const hipError_t e = hipLaunchKernel(f, dim3((unsigned)(a.n_rows * a.slices)), dim3(256), args, 0, st);
+        if (e != hipSuccess) return e;
+        const void* g = vec ? reinterpret_cast<const void*>(k_trunc_merge<DT, true>)
+                            : reinterpret_cast<const void*>(k_trunc_merge<DT, false>);
+        return hipLaunchKernel(g, dim3((unsigned)a.n_rows), dim3(kTB), args, 0, st);
+    }
     if constexpr (DT == DT_F32) {
         if (small_topk && a.V >= 8) {
             const bool wide = a.n_rows <= compute_units();   // few rows: 1024 threads each
-            const void* f = wide ? (vec ? reinterpret_cast<const void*>(k_topk32<true, 1024>)
-                                        : reinterpret_cast<const void*>(k_topk32<false, 1024>))
-                                 : (vec ? reinterpret_cast<const void*>(k_topk32<true, 256>)
-                                        : reinterpret_cast<const void*>(k_topk32<false, 256>));
+            const void* f = wide ? (vec ? reinterpret_cast<const void*>(k_topk32<true, 1024, false>)
+                                        : reinterpret_cast<const void*>(k_topk32<false, 1024, false>))
+                                 : (vec ? reinterpret_cast<const void*>(k_topk32<true, 256, false>)
+                                        : reinterpret_cast<const void*>(k_topk32<false, 256, false>));
             const hipError_t e = hipLaunchKernel(f, dim3((unsigned)a.n_rows), dim3(wide ? 1024 : 256), args, 0, st);
             return e != hipSuccess ? e : run_marked();
         }
@@ -1918,10 +2316,10 @@ hipError_t launch_dt(bool vec, const TruncArgs& a, hipStream_t st)
         hipError_t e;
         if (small_topk) {
             const bool wide = a.n_rows <= compute_units();   // few rows: 1024 threads each
-            const void* f = wide ? (vec ? reinterpret_cast<const void*>(k_topk16<DT, true, 1024>)
-                                        : reinterpret_cast<const void*>(k_topk16<DT, false, 1024>))
-                                 : (vec ? reinterpret_cast<const void*>(k_topk16<DT, true, 256>)
-                                        : reinterpret_cast<const void*>(k_topk16<DT, false, 256>));
+            const void* f = wide ? (vec ? reinterpret_cast<const void*>(k_topk16<DT, true, 1024, false>)
+                                        : reinterpret_cast<const void*>(k_topk16<DT, false, 1024, false>))
+                                 : (vec ? reinterpret_cast<const void*>(k_topk16<DT, true, 256, false>)
+                                        : reinterpret_cast<const void*>(k_topk16<DT, false, 256, false>));
             e = hipLaunchKernel(f, dim3((unsigned)a.n_rows), dim3(wide ? 1024 : 256), args, 0, st);
         } else {
             const void* f = vec ? reinterpret_cast<const void*>(k_trunc16<DT, true>)

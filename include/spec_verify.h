@@ -92,7 +92,11 @@ const char* spec_verify_status_string(int status);
 
 /* Bytes of device workspace a call needs.  `rows_per_seq` is the number of
  * logit rows the call reads per sequence: k+1 for spec_verify_greedy, 2k+1 for
- * spec_verify_sample, C*R for spec_verify_greedy_candidates.  Pure host
+ * spec_verify_sample, C*R for spec_verify_greedy_candidates.  The figure
+ * covers every call with those rows; a truncated call with a top-k of at most
+ * 256 on few rows (at most 512, V >= 16384 for 16-bit logits, 8192 for
+ * fp32) needs up to 2 MiB more than the other calls, for the candidates of
+ * its row slices.  Pure host
  * function; returns 0 for arguments that any call would reject. */
 size_t spec_verify_workspace_bytes(int B, int rows_per_seq, int V, int dtype);
 
@@ -264,9 +268,11 @@ int spec_verify_greedy_lazy(const void* target_logits, long long target_row_stri
  * buffer of SV_NOALLOC_SCRATCH_BYTES (4 MiB) that the library holds on each
  * device it runs on until the process ends.  The call allocates and frees
  * nothing (no hipMalloc / hipFree, no allocating library routine).
- *  - Limit: shapes whose spec_verify_workspace_bytes(B, 2k+1, V, dtype)
- *    exceeds SV_NOALLOC_SCRATCH_BYTES are refused with SV_ESCRATCH before
- *    anything is launched (B = 512, k = 16, V = 128256 needs 0.86 MiB).
+ *  - Limit: shapes whose workspace for spec_verify_sample exceeds
+ *    SV_NOALLOC_SCRATCH_BYTES are refused with SV_ESCRATCH before anything
+ *    is launched (B = 512, k = 16, V = 128256 needs 0.86 MiB).  That
+ *    workspace is at most spec_verify_workspace_bytes(B, 2k+1, V, dtype),
+ *    which also counts the room only truncated calls use.
  *  - One buffer per device, shared by every call on it: the buffer keeps
  *    the last call's contents (nothing in it needs clearing), and calls that
  *    overlap on one device race on it, even on different streams.  Issue

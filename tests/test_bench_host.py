@@ -144,9 +144,15 @@ def test_one_pass_top_k_limit_matches_the_library():
     """bench.py names the truncation kernel from the library's dispatch rule:
     its top-k limit for the candidate-list pass must be the library's."""
     import re
-    src = open(os.path.join(ROOT, "draft_verification_verify_amd", "csrc", "sv_trunc.hip")).read()
-    m = re.search(r"constexpr int kTopkMax = (\d+);", src)
+    csrc = os.path.join(ROOT, "draft_verification_verify_amd", "csrc")
+    src = open(os.path.join(csrc, "sv_trunc.hip")).read()
+    hdr = open(os.path.join(csrc, "sv_launch.h")).read()
+    m = re.search(r"constexpr int kTopkMax = (\d+);", hdr)
     assert m and int(m.group(1)) == bench.TOPK_ONE_PASS_MAX
+    for name, val in (("kSplitTarget", bench.SPLIT_TARGET), ("kSplitMinBytes", bench.SPLIT_MIN_BYTES),
+                      ("kSplitMax", bench.SPLIT_MAX), ("kVec", 8)):
+        m = re.search(r"constexpr int %s = (\d+);" % name, hdr)
+        assert m and int(m.group(1)) == val, name
     m = re.search(r"constexpr int kLdsRowMax = (\d+);", src)
     assert m and int(m.group(1)) == bench.LDS_ROW_MAX
 
@@ -155,14 +161,26 @@ def test_truncation_kernel_names():
     """The launch bench.py times for truncated sampling, by element size,
     vocabulary and top-k, as the library dispatches it."""
     tk = bench.truncation_kernel
-    assert tk(2, 128256, 50) == "k_topk16"
-    assert tk(2, 128256, 256) == "k_topk16"
-    assert tk(2, 128256, 257) == "k_trunc16"
-    assert tk(2, 128256, 0) == "k_trunc16"
-    assert tk(2, 100, 100) == "k_trunc16"          # top-k >= V is off
-    assert tk(2, 7, 3) == "k_trunc_rows"          # no whole vector
-    assert tk(4, 32000, 50) == "k_topk32"
-    assert tk(4, 32000, 0) == "k_trunc_rows_lds"
-    assert tk(4, 32768, 300) == "k_trunc_rows_lds"
-    assert tk(4, 32769, 0) == "k_trunc_rows"
-    assert tk(4, 7, 3) == "k_trunc_rows_lds"
+    n = 512 * 33                                   # workload 5's rows: never sliced
+    assert tk(2, 128256, 50, n) == "k_topk16"
+    assert tk(2, 128256, 256, n) == "k_topk16"
+    assert tk(2, 128256, 257, n) == "k_trunc16"
+    assert tk(2, 128256, 0, n) == "k_trunc16"
+    assert tk(2, 100, 100, n) == "k_trunc16"       # top-k >= V is off
+    assert tk(2, 7, 3, n) == "k_trunc_rows"       # no whole vector
+    assert tk(4, 32000, 50, n) == "k_topk32"
+    assert tk(4, 32000, 0, n) == "k_trunc_rows_lds"
+    assert tk(4, 32768, 300, n) == "k_trunc_rows_lds"
+    assert tk(4, 32769, 0, n) == "k_trunc_rows"
+    assert tk(4, 7, 3, n) == "k_trunc_rows_lds"
+    # few rows: slices of at least 16 KB, about 1024 workgroups in all
+    assert tk(4, 32000, 50, 9) == "k_topk32_sliced"       # 7 slices of 512+ vectors
+    assert tk(2, 128256, 50, 9) == "k_topk16_sliced"      # 15 of 1024+
+    assert tk(2, 128256, 50, 513) == "k_topk16"           # 1024 // 513 = 1
+    assert tk(2, 16383, 50, 9) == "k_topk16"              # 2047 vectors: one slice
+    assert tk(4, 8191, 50, 9) == "k_topk32"               # 1023 vectors: one slice
+    assert tk(2, 128256, 0, 9) == "k_trunc16"             # no top-k: rows whole
+    assert bench.split_slices(9, 32000, 4) == 7
+    assert bench.split_slices(9, 32000, 2) == 3
+    assert bench.split_slices(1, 1 << 24, 2) == 32
+    assert bench.split_slices(512, 1 << 24, 4) == 2
