@@ -36,23 +36,23 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "verified positions/sec (B·(k+1) rows/s) and achieved HBM GB/s vs peak"
 STATS_SOURCES = ["sv_stats.hip", "sv_device.h", "sv_launch.h"]
 STREAM_KERNELS = ("k_softmax_stats", "k_argmax_stats")
-# Rows under a top-k of at most this take a candidate-list pass (k_topk16 for
-# 16-bit rows, k_topk32 for fp32); larger or no top-k, 16-bit rows take the
-# 65536-bin histogram pass (k_trunc16) and fp32 rows the radix passes
+# Rows under a top-k of at most this take a candidate-list pass: k_topk32 for
+# fp32 rows, k_topk16 for 16-bit rows that outnumber the compute units more
+# than LIST_ROWS_PER_CU times.  Other 16-bit rows take the 65536-bin
+# histogram pass (k_trunc16), other fp32 rows the radix passes
 TOPK_ONE_PASS_MAX = 256
+LIST_ROWS_PER_CU = 3
 LDS_ROW_MAX = 32768                    # fp32 rows up to this run the radix passes from LDS
-# Few rows under such a top-k are cut into slices of at least SPLIT_MIN_BYTES
-# of whole 8-logit vectors, about SPLIT_TARGET workgroups in all, at most
-# SPLIT_MAX per row; each slice's candidates go to k_trunc_merge
-SPLIT_TARGET, SPLIT_MIN_BYTES, SPLIT_MAX = 1024, 16384, 32
+# Few fp32 rows under such a top-k are cut into slices: about SPLIT_TARGET
+# workgroups in all, at most SPLIT_MAX per row, each of at least
+# SPLIT_MIN_VEC_FEW 8-logit vectors for at most SPLIT_FEW_ROWS rows, else
+# SPLIT_MIN_VEC_MANY; each slice's candidates go to k_trunc_merge
+SPLIT_TARGET, SPLIT_FEW_ROWS, SPLIT_MIN_VEC_FEW, SPLIT_MIN_VEC_MANY, SPLIT_MAX = 1024, 64, 512, 2048, 32
 TRUNC_NOTES = {
     "k_topk16": "k_topk16 (one pass per 16-bit row: per-wave lists of the candidates above a "
                 "rising floor) followed by k_trunc_rows over the rows it marked",
     "k_topk32": "k_topk32 (one pass per fp32 row: per-wave lists of the candidates above a "
                 "rising floor) followed by k_trunc_rows over the rows it marked",
-    "k_topk16_sliced": "k_topk16 on row slices (each slice's candidates above its own rising "
-                       "floor) followed by k_trunc_merge (one workgroup per row merges them; "
-                       "the radix passes for rows the slices could not summarise)",
     "k_topk32_sliced": "k_topk32 on row slices (each slice's candidates above its own rising "
                        "floor) followed by k_trunc_merge (one workgroup per row merges them; "
                        "the radix passes for rows the slices could not summarise)",
@@ -65,21 +65,23 @@ TRUNC_NOTES = {
 }
 
 
-def split_slices(n_rows: int, V: int, es: int) -> int:
-    """Slices per row for the candidate-list pass (1: rows whole), for rows
-    of V logits of es bytes."""
-    s = min(SPLIT_TARGET // max(n_rows, 1), (V // 8) // (SPLIT_MIN_BYTES // (8 * es)), SPLIT_MAX)
+def split_slices(n_rows: int, V: int) -> int:
+    """Slices per fp32 row for the candidate-list pass (1: rows whole)."""
+    min_vec = SPLIT_MIN_VEC_FEW if n_rows <= SPLIT_FEW_ROWS else SPLIT_MIN_VEC_MANY
+    s = min(SPLIT_TARGET // max(n_rows, 1), (V // 8) // min_vec, SPLIT_MAX)
     return s if s >= 2 else 1
 
 
-def truncation_kernel(es: int, V: int, top_k: int, n_rows: int) -> str:
+def truncation_kernel(es: int, V: int, top_k: int, n_rows: int, cus: int) -> str:
     """The launch that summarises every row for truncated sampling, for
-    n_rows rows of V logits of es bytes."""
+    n_rows rows of V logits of es bytes on a GPU of `cus` compute units."""
     small_topk = 1 <= top_k <= TOPK_ONE_PASS_MAX and top_k < V
-    if small_topk and V >= 8 and split_slices(n_rows, V, es) > 1:
-        return "k_topk16_sliced" if es == 2 else "k_topk32_sliced"
     if es == 2:
-        return "k_topk16" if small_topk and V >= 8 else ("k_trunc16" if V >= 8 else "k_trunc_rows")
+        if V < 8:
+            return "k_trunc_rows"
+        return "k_topk16" if small_topk and n_rows > LIST_ROWS_PER_CU * cus else "k_trunc16"
+    if small_topk and V >= 8 and split_slices(n_rows, V) > 1:
+        return "k_topk32_sliced"
     if small_topk and V >= 8:
         return "k_topk32"
     return "k_trunc_rows_lds" if V <= LDS_ROW_MAX else "k_trunc_rows"
@@ -429,7 +431,8 @@ def main():
         vecs = CEILING_VECS if args.ceiling_vec < 0 else (args.ceiling_vec,)
         ceiling = stream_ceiling(bufs, max(args.steps, 20), vecs)
     kernel_name = {"sample": "k_softmax_stats", "lenient": "k_softmax_stats",
-                   "truncated": truncation_kernel(es, V, args.top_k, cfg0.B * stream_rows)}.get(args.mode, "k_argmax_stats")
+                   "truncated": truncation_kernel(es, V, args.top_k, cfg0.B * stream_rows,
+                                                 torch.cuda.get_device_properties(0).multi_processor_count)}.get(args.mode, "k_argmax_stats")
     traffic = measured_traffic(kernel_name, cid) \
         if (kernel_name in STREAM_KERNELS and args.vocab_shard == 1 and args.mode != "tree"
             and not lazy) else None

@@ -617,7 +617,8 @@ size_t spec_verify_workspace_bytes(int B, int rows_per_seq, int V, int dtype)
     if (B < 1 || rows_per_seq < 1 || V < 1 || V > kMaxV || !dtype_ok(dtype)) return 0;
     const long long rows = (long long)B * rows_per_seq;
     if (!fits_grid(rows, V)) return 0;
-    return layout(nullptr, B, rows, V, split_slices(rows, V, elem_size(dtype))).bytes;   // enough for any call
+    // enough for any call: fp32 rows may be cut into slices
+    return layout(nullptr, B, rows, V, elem_size(dtype) == 4 ? split_slices(rows, V) : 1).bytes;
 }
 
 int spec_verify_greedy(const void* target_logits, long long target_row_stride,

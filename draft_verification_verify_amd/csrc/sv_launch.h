@@ -78,22 +78,25 @@ struct TruncRow {
     uint32_t pad;
 };
 
-// Few rows under a small top-k are cut into slices, each summarised by its
-// own workgroup as the candidates a row's top_k can come from (at most
+// Few fp32 rows under a small top-k are cut into slices, each summarised by
+// its own workgroup as the candidates a row's top_k can come from (at most
 // kCandMax keys per slice), and merged per row by a second launch.  Slices
-// per row: as many as give about kSplitTarget workgroups, each of at least
-// kSplitMinBytes of whole logical vectors (1024 of 16-bit logits, 512 of
-// fp32), at most kSplitMax; 1 (no split) otherwise.  Smaller slices stream
-// no faster and give the merge more candidates.
+// per row: as many as give about kSplitTarget workgroups, at most kSplitMax,
+// each of at least kSplitMinVecFew whole 8-logit vectors (16 KB) when the
+// rows number at most kSplitFewRows, else kSplitMinVecMany (64 KB); 1 (no
+// split) when that leaves fewer than two.  More rows keep the chip busy
+// whole, and smaller slices give the merge more candidates to gather.
 constexpr int kCandMax = 512;
 constexpr int kSplitTarget = 1024;
-constexpr int kSplitMinBytes = 16384;
+constexpr int kSplitFewRows = 64;
+constexpr int kSplitMinVecFew = 512;
+constexpr int kSplitMinVecMany = 2048;
 constexpr int kSplitMax = 32;
 
-inline int split_slices(long long n_rows, int V, int elem_bytes)
+inline int split_slices(long long n_rows, int V)
 {
     const long long nfull = V / kVec;
-    const long long min_vec = kSplitMinBytes / (kVec * (elem_bytes > 0 ? elem_bytes : 1));
+    const long long min_vec = n_rows <= kSplitFewRows ? kSplitMinVecFew : kSplitMinVecMany;
     long long s = n_rows > 0 ? kSplitTarget / n_rows : 1;
     if (s > nfull / min_vec) s = nfull / min_vec;
     if (s > kSplitMax) s = kSplitMax;
@@ -101,12 +104,17 @@ inline int split_slices(long long n_rows, int V, int elem_bytes)
 }
 
 // Top-k values of at most kTopkMax take the candidate lists (one pass per
-// row); the slices a truncated call cuts its rows into (1: none).
+// row): fp32 rows always, 16-bit rows when they outnumber the compute units
+// more than kListRowsPerCU times (fewer take the histogram pass).  Only fp32
+// rows are cut into slices; trunc_slices gives a truncated call's slices per
+// row (1: none).
 constexpr int kTopkMax = 256;
+constexpr int kListRowsPerCU = 3;
 
 inline int trunc_slices(long long n_rows, int V, int elem_bytes, int top_k)
 {
-    return top_k >= 1 && top_k <= kTopkMax && top_k < V && V >= 8 ? split_slices(n_rows, V, elem_bytes) : 1;
+    return elem_bytes == 4 && top_k >= 1 && top_k <= kTopkMax && top_k < V && V >= 8
+               ? split_slices(n_rows, V) : 1;
 }
 
 // Truncation of every row of a batch (sv_trunc.hip), rows numbered as in
@@ -126,7 +134,7 @@ struct TruncArgs {
     int only_marked;                   // radix kernel: only rows whose pad the exact kernel set to 1
     int* zero;                         // n_zero counters zeroed by the first launch, as in
     int n_zero;                        // StatsArgs (null, 0: none)
-    int slices;                        // split_slices(n_rows, V), for a top-k of at most 256
+    int slices;                        // trunc_slices: fp32 rows, a top-k of at most 256
     uint32_t* cand;                    // [n_rows][slices][kCandMax] candidate keys (slices > 1)
     uint32_t* cand_hdr;                // [n_rows][slices][4]: floor, largest key, count, overflow
 };

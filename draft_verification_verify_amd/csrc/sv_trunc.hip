@@ -933,9 +933,10 @@ __global__ __launch_bounds__(kT16) void k_trunc16(TruncArgs a)
 // With top-k on, only the top_k largest logits (with the ties at the
 // boundary) can be kept, so for top_k <= kTopkMax a row needs no histogram of
 // every pattern.  One 256-thread workgroup takes one row, eight to a CU (the
-// analysis of one row overlaps the streaming of the others), or, when the
-// rows do not outnumber the compute units, one 1024-thread workgroup with 16
-// list words per lane, so that few rows keep many loads in flight.  Each wave
+// analysis of one row overlaps the streaming of the others).  It runs when
+// the rows outnumber the compute units more than three times: fewer rows
+// take k_trunc16, whose stream has no compaction for a load to wait on, and
+// with so few rows the histograms' LDS atomics do not bound it.  Each wave
 // keeps, in LDS, a list of the 32-bit words (two logits each) it has streamed that
 // may still hold a kept logit, and a floor F: the list holds every word with
 // a logit whose key is at least F.  When a lane's part of the list fills up,
@@ -972,15 +973,13 @@ __global__ __launch_bounds__(kT16) void k_trunc16(TruncArgs a)
 
 constexpr int kKeptMax = 512;          // kept keys gathered after top-k
 
-// list words per lane: 16 with 1024 threads (one workgroup to a CU), 12 with
-// 256 (eight to a CU)
-template <int NT>
-constexpr int kSlots = NT == 1024 ? 16 : 12;
+constexpr int kTK = 256;               // threads per row
+constexpr int kTKW = kTK / 64;
+constexpr int kSlots = 12;             // list words per lane (eight workgroups to a CU)
 
-template <int NT>
 struct TopkShared {
-    static constexpr int NW = NT / 64;
-    uint32_t list[NW * kSlots<NT> * 64];  // wave w, lane l, word j: [w][j * 64 + l]
+    static constexpr int NW = kTKW;
+    uint32_t list[NW * kSlots * 64];    // wave w, lane l, word j: [w][j * 64 + l]
     uint32_t whist[NW * 256];           // each wave's radix histogram; after the stream, the kept keys
     u64 hist[256];                      // the workgroup's: counts (low 1 KB) or masses
     u64 red[NW];
@@ -1091,26 +1090,28 @@ struct OffDigits {
     }
 };
 
+constexpr int kMergeMax = 4096;        // candidates the merge of a row's slices gathers
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 {
     return (uint32_t)wave_max_int((int)(v ^ 0x80000000u)) ^ 0x80000000u;
 }
 
-// A slice's candidates, when rows are cut into slices: the keys at or above
-// the slice's floor Fs, the largest floor Fg of its waves when at most
-// kCandMax keys are at or above it, else the K1-th largest key of the lists
-// at or above Fg.  Either way K1 different logits of the row are at least Fs
-// (a wave raises its floor only under K1 of its own keys), so Fs never passes
-// the row's top_k-th largest key, and every key at or above the largest floor
-// of a row's slices is among the row's candidates.  kr: this lane's keys (0 for
+// A slice's candidates, when fp32 rows are cut into S slices: the keys at or
+// above the slice's floor Fs.  Fs is the largest floor Fg of its waves when
+// the n keys at or above Fg are few (at most K1, or S * n at most half of
+// what the merge gathers), else the K1-th largest of those n keys.  Either way K1 different
+// logits of the row are at least Fs (a wave raises its floor only under K1
+// of its own keys), so Fs never passes the row's top_k-th largest key, and
+// every key at or above the largest floor of a row's slices is among the
+// row's candidates.  kr: this lane's keys (0 for
 // none; keys below the wave's floor are skipped), F: its wave's floor.  Wave
 // 0 writes the keys and a header (Fs, the largest key, their number, and an
-// overflow flag, set when a wave's list overflowed, when more than CAP keys
-// are at or above the largest floor (the list area's words; two 16-bit keys
-// share a word), or when the keys at or above Fs outnumber kCandMax).  Called
-// by every thread of the workgroup.
-template <int NT, int J, int CAP>
-__device__ __forceinline__ void slice_candidates(const uint32_t (&kr)[J], uint32_t F, uint32_t K1, uint32_t* list, uint32_t* wh0, uint32_t* sF, uint32_t* smx,
+// overflow flag, set when a wave's list overflowed or when the keys at or
+// above Fs outnumber kCandMax).  The list area holds the J keys of each of
+// the NT lanes.  Called by every thread of the workgroup.
+template <int NT, int J>
+__device__ __forceinline__ void slice_candidates(const uint32_t (&kr)[J], uint32_t F, uint32_t K1, int S, uint32_t* list, uint32_t* wh0, uint32_t* sF, uint32_t* smx,
                                                  const uint32_t* sover, uint32_t* snk, uint32_t* cand, uint32_t* hdr)
 {
     constexpr int NW = NT / 64;
@@ -1152,24 +1153,15 @@ __device__ __forceinline__ void slice_candidates(const uint32_t (&kr)[J], uint32
             uint32_t base = 0;
             if (lane == first) base = atomicAdd(snk, (uint32_t)__popcll(bal));
             base = (uint32_t)__builtin_amdgcn_readlane((int)base, first);
-            const uint32_t pos = base + lane_prefix(bal);
-            if (keep && pos < (uint32_t)CAP) list[pos] = kr[j];
+            if (keep) list[base + lane_prefix(bal)] = kr[j];
         }
     }
     __syncthreads();
     if (wv != 0) return;
     const uint32_t n = *snk;
-    if (n > (uint32_t)CAP) {           // uniform: more than the list area holds
-        if (lane == 0) {
-            hdr[0] = 0u;
-            hdr[1] = 0u;
-            hdr[2] = 0u;
-            hdr[3] = 1u;
-        }
-        return;
-    }
     uint32_t Fs = Fg;
-    if (n > (uint32_t)kCandMax) {      // uniform: the K1-th largest (n > K1), one offset digit per level
+    if (n >= K1 && (n > (uint32_t)kCandMax || (long long)S * n > kMergeMax / 2)) {
+        // uniform: the K1-th largest, one offset digit per level
         const OffDigits od(mxk - Fg);
         uint32_t prefix = 0, need = K1;
         int hs = od.top, ls = od.shift(0);   // level 0 has no prefix
@@ -1210,28 +1202,18 @@ __device__ __forceinline__ void slice_candidates(const uint32_t (&kr)[J], uint32
     }
 }
 
-template <int DT, bool VEC, int NT, bool SPLIT>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 256 ? 8 : 4))) void k_topk16(TruncArgs a)
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kTK) __attribute__((amdgpu_waves_per_eu(8))) void k_topk16(TruncArgs a)
 {
-    constexpr int kTK = NT;
-    constexpr int kTKW = NT / 64;
-    constexpr int KS = kSlots<NT>;
+    constexpr int KS = kSlots;
     static_assert(kTKW * 256 >= kKeptMax, "the kept keys reuse the wave histograms");
-    __shared__ __attribute__((aligned(16))) TopkShared<NT> sh;
-    // SPLIT: workgroup (row, slice) streams the slice's whole vectors only
-    const int S = SPLIT ? a.slices : 1;
-    const int row = SPLIT ? (int)blockIdx.x / S : (int)blockIdx.x;
-    const int slice = (int)blockIdx.x - row * S;
+    __shared__ __attribute__((aligned(16))) TopkShared sh;
+    const int row = (int)blockIdx.x;
     const int t = (int)threadIdx.x;
     const int lane = t & 63, wv = t >> 6;
-    const char* const rrow = trunc_row_ptr<DT>(a, row);
+    const char* const rp = trunc_row_ptr<DT>(a, row);
     const int V = a.V;
-    const int nall = V >> 3;                                   // >= 1
-    const int vps = (nall + S - 1) / S;
-    const int vb = slice * vps;
-    const char* rp = rrow + 16LL * vb;                         // 16 bytes per logical vector
-    const int nfull = (vb + vps < nall ? vb + vps : nall) - vb; // >= 1
-    const bool last_slice = slice == S - 1;
+    const int nfull = V >> 3;                                  // >= 1
     const uint32_t K1 = (uint32_t)a.top_k + 1u;
     const uint32_t f0 = (~ninf_bits<DT>() & 0xFFFFu) + 2u;      // just above -inf
     uint32_t* const lst = sh.list + wv * (KS * 64);
@@ -1388,27 +1370,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 256 ? 
     Raw<DT> bufA[4], bufB[4];
     issue(bufA, 0);
     issue(bufB, 1);
-    if constexpr (NT == 1024) {        // the last two groups after the loop: no load past them
-        for (int g = 0; g + 2 < ngroups; g += 2) {
-            take_group(bufA, g);
-            issue(bufA, g + 2);        // unconditional: each group waits for its own loads only
-            take_group(bufB, g + 1);
-            issue(bufB, g + 3);
-        }
-        take_group(bufA, ngroups - 2);
-        take_group(bufB, ngroups - 1);
-    } else {
-        for (int g = 0; g < ngroups; g += 2) {
-            take_group(bufA, g);
-            issue(bufA, g + 2);        // unconditional: each group waits for its own loads only
-            take_group(bufB, g + 1);
-            issue(bufB, g + 3);
-        }
+    for (int g = 0; g < ngroups; g += 2) {
+        take_group(bufA, g);
+        issue(bufA, g + 2);            // unconditional: each group waits for its own loads only
+        take_group(bufB, g + 1);
+        issue(bufB, g + 3);
     }
     if (__ballot(wp > room)) compact();
-    if (last_slice && t == 0) {        // the partial last vector: at most four words, like a vector,
-        const unsigned short* e = reinterpret_cast<const unsigned short*>(rrow) + 8LL * nall;
-        const int n = V - 8 * nall;    // -inf past its end
+    if (t == 0) {                      // the partial last vector: at most four words, like a vector,
+        const unsigned short* e = reinterpret_cast<const unsigned short*>(rp) + 8LL * nfull;
+        const int n = V - 8 * nfull;   // -inf past its end
         for (int j = 0; j < n; j += 2) {
             const uint32_t hi = j + 1 < n ? (uint32_t)e[j + 1] : ninf_bits<DT>();
             const uint32_t x = (uint32_t)e[j] | (hi << 16);
@@ -1417,19 +1388,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 256 ? 
         }
     }
     c = (int)((wp - lane_list) >> 6);
-    if constexpr (SPLIT) {             // both keys of every word, 0 past the list
-        uint32_t kr[2 * KS];
-#pragma unroll
-        for (int j = 0; j < KS; ++j) {
-            const uint32_t u = j < c ? word_keys(lst[j * 64 + lane]) : 0u;
-            kr[2 * j] = u & 0xFFFFu;
-            kr[2 * j + 1] = u >> 16;
-        }
-        const long long sl = (long long)row * S + slice;
-        slice_candidates<NT, 2 * KS, NT * KS>(kr, F, K1, sh.list, sh.whist, sh.F, sh.mx, sh.over, &sh.nk,
-                                     a.cand + sl * kCandMax, a.cand_hdr + sl * 4);
-        return;
-    }
     if (lane == 0) sh.F[wv] = F;
     __syncthreads();
 
@@ -1848,7 +1806,7 @@ void k_topk32(TruncArgs a)
     if (F != 0xFFFFFFFFu) raise_floor([&](int j) { return kr[j]; }, KS);
     if constexpr (SPLIT) {
         const long long sl = (long long)row * S + slice;
-        slice_candidates<NT, KS, NT * KS>(kr, F, K1, sh.list, sh.whist, sh.F, sh.mx, sh.over, &sh.nk,
+        slice_candidates<NT, KS>(kr, F, K1, S, sh.list, sh.whist, sh.F, sh.mx, sh.over, &sh.nk,
                                  a.cand + sl * kCandMax, a.cand_hdr + sl * 4);
         return;
     }
@@ -2013,16 +1971,14 @@ void k_topk32(TruncArgs a)
 }
 
 // ---- the merge of a row's slices ---------------------------------------------
-// Rows cut into slices (split_slices > 1, top-k of at most 256): every key of
-// a row at or above the largest floor Fr of its slices is among the slices'
-// candidates, and Fr never passes the row's top_k-th largest key.  One
-// 512-thread workgroup per row gathers them and finds the top_k-th largest,
-// the kept keys' fixed-point masses and the top-p boundary as the one-pass
-// kernels do (the same integers, so the same summary); a row whose slices
-// overflowed, or with more candidates or kept keys than it can gather, takes
-// the radix passes in the same workgroup.  Keys are the slice kernels' own:
-// key_of for fp32, word_keys' form for the 16-bit formats.
-constexpr int kMergeMax = 4096;        // candidates gathered per row
+// fp32 rows cut into slices (split_slices > 1, top-k of at most 256): every
+// key of a row at or above the largest floor Fr of its slices is among the
+// slices' candidates, and Fr never passes the row's top_k-th largest key.
+// One 512-thread workgroup per row gathers them and finds the top_k-th
+// largest, the kept keys' fixed-point masses and the top-p boundary as the
+// one-pass kernels do (the same integers, so the same summary); a row whose
+// slices overflowed, or with more candidates or kept keys than it can
+// gather, takes the radix passes in the same workgroup.
 
 struct MergeShared {
     uint32_t hdr[kSplitMax][4];
@@ -2041,31 +1997,16 @@ struct MergeShared {
     u64 incl;
 };
 
-template <int DT>
-__device__ __forceinline__ float cand_value(uint32_t k)
-{
-    if constexpr (DT == DT_F32) return value_of_key32(k);
-    else return value_of_key<DT>(k);
-}
-
-template <int DT>
-__device__ __forceinline__ uint32_t cand_tau(uint32_t k)
-{
-    if constexpr (DT == DT_F32) return k;
-    else return std_key(k);
-}
-
 // One row's summary from its slices' candidates at or above Fr; false (uniform
 // over the workgroup) when there are more candidates or kept keys than it
 // gathers.
-template <int DT>
 __device__ __forceinline__ bool merge_row(const TruncArgs& a, int row, uint32_t Fr, uint32_t mxk,
                                           const uint32_t* cand, MergeShared& ms)
 {
     const int t = (int)threadIdx.x;
     const int lane = t & 63, wv = t >> 6;
     const int S = a.slices;
-    const uint32_t f0 = DT == DT_F32 ? key32(0xFF800000u) + 1u : (~ninf_bits<DT>() & 0xFFFFu) + 2u;
+    const uint32_t f0 = key32(0xFF800000u) + 1u;               // just above -inf
     if (mxk < Fr) {                    // no finite logit
         if (t == 0) a.rows[row] = TruncRow{-INFINITY, -INFINITY, 0u, 0u};
         return true;
@@ -2169,12 +2110,12 @@ __device__ __forceinline__ bool merge_row(const TruncArgs& a, int row, uint32_t 
     if (nk > (uint32_t)kKeptMax) return false;
 
     // the kept logits' masses, one per thread
-    const float m = cand_value<DT>(mxk);
+    const float m = value_of_key32(mxk);
     const uint32_t kt = t < (int)nk ? ms.kk[t] : 0u;
-    const u64 f = t < (int)nk ? fixed40_nb(weight(cand_value<DT>(kt), m, a.c)) : 0;
+    const u64 f = t < (int)nk ? fixed40_nb(weight(value_of_key32(kt), m, a.c)) : 0;
     u64 kept = block_sum_u64(f, ms.red);
     const u64 M = kept;
-    uint32_t tau = topk_on ? cand_tau<DT>(lo) : 0u;   // top-k off: every key
+    uint32_t tau = topk_on ? lo : 0u;  // top-k off: every key
 
     // top-p: the key at which the mass from the top first reaches top_p * M
     if (a.top_p < 1.f) {
@@ -2207,7 +2148,7 @@ __device__ __forceinline__ bool merge_row(const TruncArgs& a, int row, uint32_t 
             hs = ls;
             ls = od.shift(level + 1);
         }
-        tau = cand_tau<DT>(lo + prefix);
+        tau = lo + prefix;
     }
     if (t == 0) {
         const float l2s = (float)(log2((double)kept) - (double)kFixBits);
@@ -2216,7 +2157,7 @@ __device__ __forceinline__ bool merge_row(const TruncArgs& a, int row, uint32_t 
     return true;
 }
 
-template <int DT, bool VEC>
+template <bool VEC>
 __global__ __launch_bounds__(kTB) void k_trunc_merge(TruncArgs a)
 {
     static_assert(kKeptMax == kTB, "one kept key per thread");
@@ -2240,9 +2181,9 @@ __global__ __launch_bounds__(kTB) void k_trunc_merge(TruncArgs a)
         mxk = ms.hdr[sl][1] > mxk ? ms.hdr[sl][1] : mxk;
         over |= ms.hdr[sl][3];
     }
-    if (!over && merge_row<DT>(a, row, Fr, mxk, cand, ms)) return;
+    if (!over && merge_row(a, row, Fr, mxk, cand, ms)) return;
     // the slices overflowed, or too many candidates or kept keys: the radix passes
-    trunc_row_radix<DT>(a, row, sh, StreamRow<DT, VEC>{trunc_row_ptr<DT>(a, row), a.V});
+    trunc_row_radix<DT_F32>(a, row, sh, StreamRow<DT_F32, VEC>{trunc_row_ptr<DT_F32>(a, row), a.V});
 }
 
 // The current device's compute units (queried once per device).
@@ -2277,24 +2218,19 @@ hipError_t launch_dt(bool vec, const TruncArgs& a, hipStream_t st)
         return hipLaunchKernel(marked, dim3(grid), dim3(kTB), args, 0, st);
     };
     const bool small_topk = a.top_k >= 1 && a.top_k <= kTopkMax && a.top_k < a.V;
-    // few rows under a small top-k: cut into slices, each summarised by its own
-    // workgroup, merged per row (the merge also runs the radix passes for rows
-    // a slice could not summarise)
-    if (small_topk && a.V >= 8 && a.slices > 1 && a.cand && a.cand_hdr) {
-        const void* f;
-        if constexpr (DT == DT_F32)
-            f = vec ? reinterpret_cast<const void*>(k_topk32<true, 256, true>)
-                    : reinterpret_cast<const void*>(k_topk32<false, 256, true>);
-        else
-            f = vec ? reinterpret_cast<const void*>(k_topk16<DT, true, 256, true>)
-                    : reinterpret_cast<const void*>(k_topk16<DT, false, 256, true>);
-        const hipError_t e = hipLaunchKernel(f, dim3((unsigned)(a.n_rows * a.slices)), dim3(256), args, 0, st);
-        if (e != hipSuccess) return e;
-        const void* g = vec ? reinterpret_cast<const void*>(k_trunc_merge<DT, true>)
-                            : reinterpret_cast<const void*>(k_trunc_merge<DT, false>);
-        return hipLaunchKernel(g, dim3((unsigned)a.n_rows), dim3(kTB), args, 0, st);
-    }
     if constexpr (DT == DT_F32) {
+        // few rows under a small top-k: cut into slices, each summarised by its
+        // own workgroup, merged per row (the merge also runs the radix passes
+        // for rows a slice could not summarise)
+        if (small_topk && a.V >= 8 && a.slices > 1 && a.cand && a.cand_hdr) {
+            const void* f = vec ? reinterpret_cast<const void*>(k_topk32<true, 256, true>)
+                                : reinterpret_cast<const void*>(k_topk32<false, 256, true>);
+            const hipError_t e = hipLaunchKernel(f, dim3((unsigned)(a.n_rows * a.slices)), dim3(256), args, 0, st);
+            if (e != hipSuccess) return e;
+            const void* g = vec ? reinterpret_cast<const void*>(k_trunc_merge<true>)
+                                : reinterpret_cast<const void*>(k_trunc_merge<false>);
+            return hipLaunchKernel(g, dim3((unsigned)a.n_rows), dim3(kTB), args, 0, st);
+        }
         if (small_topk && a.V >= 8) {
             const bool wide = a.n_rows <= compute_units();   // few rows: 1024 threads each
             const void* f = wide ? (vec ? reinterpret_cast<const void*>(k_topk32<true, 1024, false>)
@@ -2314,17 +2250,16 @@ hipError_t launch_dt(bool vec, const TruncArgs& a, hipStream_t st)
         if (a.V < 8)                   // no whole vector: the radix kernel takes every row
             return hipLaunchKernel(marked, dim3((unsigned)a.n_rows), dim3(kTB), args, 0, st);
         hipError_t e;
-        if (small_topk) {
-            const bool wide = a.n_rows <= compute_units();   // few rows: 1024 threads each
-            const void* f = wide ? (vec ? reinterpret_cast<const void*>(k_topk16<DT, true, 1024, false>)
-                                        : reinterpret_cast<const void*>(k_topk16<DT, false, 1024, false>))
-                                 : (vec ? reinterpret_cast<const void*>(k_topk16<DT, true, 256, false>)
-                                        : reinterpret_cast<const void*>(k_topk16<DT, false, 256, false>));
-            e = hipLaunchKernel(f, dim3((unsigned)a.n_rows), dim3(wide ? 1024 : 256), args, 0, st);
+        const int cus = compute_units();
+        // a small top-k on many rows: the candidate lists; on fewer, the
+        // histogram pass (no compaction in its stream) is the faster
+        if (small_topk && (long long)a.n_rows > (long long)kListRowsPerCU * cus) {
+            const void* f = vec ? reinterpret_cast<const void*>(k_topk16<DT, true>)
+                                : reinterpret_cast<const void*>(k_topk16<DT, false>);
+            e = hipLaunchKernel(f, dim3((unsigned)a.n_rows), dim3(kTK), args, 0, st);
         } else {
             const void* f = vec ? reinterpret_cast<const void*>(k_trunc16<DT, true>)
                                 : reinterpret_cast<const void*>(k_trunc16<DT, false>);
-            const int cus = compute_units();
             const unsigned g16 = (unsigned)(a.n_rows < cus ? a.n_rows : cus);   // one workgroup fills a CU's LDS
             e = hipLaunchKernel(f, dim3(g16), dim3(kT16), args, 0, st);
         }

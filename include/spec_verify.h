@@ -93,10 +93,10 @@ const char* spec_verify_status_string(int status);
 /* Bytes of device workspace a call needs.  `rows_per_seq` is the number of
  * logit rows the call reads per sequence: k+1 for spec_verify_greedy, 2k+1 for
  * spec_verify_sample, C*R for spec_verify_greedy_candidates.  The figure
- * covers every call with those rows; a truncated call with a top-k of at most
- * 256 on few rows (at most 512, V >= 16384 for 16-bit logits, 8192 for
- * fp32) needs up to 2 MiB more than the other calls, for the candidates of
- * its row slices.  Pure host
+ * covers every call with those rows; a truncated call on fp32 logits with a
+ * top-k of at most 256 on few rows (at most 512; V >= 8192 for at most 64
+ * rows, else V >= 32768) needs up to 2 MiB more than the other calls, for
+ * the candidates of its row slices.  Pure host
  * function; returns 0 for arguments that any call would reject. */
 size_t spec_verify_workspace_bytes(int B, int rows_per_seq, int V, int dtype);
 

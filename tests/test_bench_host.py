@@ -149,8 +149,10 @@ def test_one_pass_top_k_limit_matches_the_library():
     hdr = open(os.path.join(csrc, "sv_launch.h")).read()
     m = re.search(r"constexpr int kTopkMax = (\d+);", hdr)
     assert m and int(m.group(1)) == bench.TOPK_ONE_PASS_MAX
-    for name, val in (("kSplitTarget", bench.SPLIT_TARGET), ("kSplitMinBytes", bench.SPLIT_MIN_BYTES),
-                      ("kSplitMax", bench.SPLIT_MAX), ("kVec", 8)):
+    for name, val in (("kListRowsPerCU", bench.LIST_ROWS_PER_CU), ("kSplitTarget", bench.SPLIT_TARGET),
+                      ("kSplitFewRows", bench.SPLIT_FEW_ROWS), ("kSplitMinVecFew", bench.SPLIT_MIN_VEC_FEW),
+                      ("kSplitMinVecMany", bench.SPLIT_MIN_VEC_MANY), ("kSplitMax", bench.SPLIT_MAX),
+                      ("kVec", 8)):
         m = re.search(r"constexpr int %s = (\d+);" % name, hdr)
         assert m and int(m.group(1)) == val, name
     m = re.search(r"constexpr int kLdsRowMax = (\d+);", src)
@@ -160,27 +162,31 @@ def test_one_pass_top_k_limit_matches_the_library():
 def test_truncation_kernel_names():
     """The launch bench.py times for truncated sampling, by element size,
     vocabulary and top-k, as the library dispatches it."""
-    tk = bench.truncation_kernel
-    n = 512 * 33                                   # workload 5's rows: never sliced
+    tk = lambda es, V, top_k, n: bench.truncation_kernel(es, V, top_k, n, 256)
+    n = 512 * 33                                   # workload 5's rows
     assert tk(2, 128256, 50, n) == "k_topk16"
     assert tk(2, 128256, 256, n) == "k_topk16"
     assert tk(2, 128256, 257, n) == "k_trunc16"
     assert tk(2, 128256, 0, n) == "k_trunc16"
     assert tk(2, 100, 100, n) == "k_trunc16"       # top-k >= V is off
     assert tk(2, 7, 3, n) == "k_trunc_rows"       # no whole vector
+    assert tk(2, 128256, 50, 768) == "k_trunc16"  # 3 rows per compute unit: the histogram pass
+    assert tk(2, 128256, 50, 769) == "k_topk16"
     assert tk(4, 32000, 50, n) == "k_topk32"
     assert tk(4, 32000, 0, n) == "k_trunc_rows_lds"
     assert tk(4, 32768, 300, n) == "k_trunc_rows_lds"
     assert tk(4, 32769, 0, n) == "k_trunc_rows"
     assert tk(4, 7, 3, n) == "k_trunc_rows_lds"
-    # few rows: slices of at least 16 KB, about 1024 workgroups in all
+    # few fp32 rows: slices of at least 16 KB (at most 64 rows) or 64 KB,
+    # about 1024 workgroups in all
     assert tk(4, 32000, 50, 9) == "k_topk32_sliced"       # 7 slices of 512+ vectors
-    assert tk(2, 128256, 50, 9) == "k_topk16_sliced"      # 15 of 1024+
-    assert tk(2, 128256, 50, 513) == "k_topk16"           # 1024 // 513 = 1
-    assert tk(2, 16383, 50, 9) == "k_topk16"              # 2047 vectors: one slice
+    assert tk(4, 32000, 50, 72) == "k_topk32"             # 4000 vectors: one 64 KB slice
+    assert tk(4, 128256, 50, 288) == "k_topk32_sliced"    # 3 slices
+    assert tk(4, 128256, 50, 513) == "k_topk32"           # 1024 // 513 = 1
     assert tk(4, 8191, 50, 9) == "k_topk32"               # 1023 vectors: one slice
-    assert tk(2, 128256, 0, 9) == "k_trunc16"             # no top-k: rows whole
-    assert bench.split_slices(9, 32000, 4) == 7
-    assert bench.split_slices(9, 32000, 2) == 3
-    assert bench.split_slices(1, 1 << 24, 2) == 32
-    assert bench.split_slices(512, 1 << 24, 4) == 2
+    assert tk(4, 128256, 0, 9) == "k_trunc_rows"          # no top-k: the radix passes
+    assert bench.split_slices(9, 32000) == 7
+    assert bench.split_slices(9, 128256) == 31
+    assert bench.split_slices(1, 1 << 24) == 32
+    assert bench.split_slices(144, 128256) == 7
+    assert bench.split_slices(512, 1 << 24) == 2

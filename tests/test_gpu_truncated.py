@@ -348,18 +348,20 @@ def small_top_k_rows(n, V, tdt, g):
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("V", [3001, 3004, 3005, 3007, 32000])
-@pytest.mark.parametrize("B", [12, 40])
+@pytest.mark.parametrize("B", [12, 40, 110])
 def test_truncated_small_top_k_equals_fp32(sv, dtype, V, B):
-    """Top-k up to 256 takes the one-pass candidate lists, 16-bit rows
-    k_topk16 and fp32 rows k_topk32: on rows built to stress them
-    (small_top_k_rows), at every top-k from 1 to 256 (and 257: the histogram
-    pass against the radix passes) and top-p from off to 1e-6, the 16-bit
-    result must equal, bit for bit, that of the same rows upcast to fp32;
-    some settings are checked against the oracle too.  B = 12 gives 84 rows
-    (1024 threads per fp32 row), B = 40 gives 280 rows, more than the compute
-    units (256 threads per row).  V = 3001, 3004, 3005 and 3007 end each row
-    with a partial vector of 1, 4, 5 and 7 logits, taken after the stream by
-    lanes whose lists may be nearly full (ascending rows)."""
+    """Top-k up to 256: fp32 rows take the candidate lists (k_topk32), 16-bit
+    rows the candidate lists (k_topk16) when they outnumber the compute units
+    more than three times, else the histogram pass (k_trunc16).  On rows
+    built to stress them (small_top_k_rows), at every top-k from 1 to 256
+    (and 257) and top-p from off to 1e-6, the 16-bit result must equal, bit
+    for bit, that of the same rows upcast to fp32; some settings are checked
+    against the oracle too.  B = 12 gives 84 rows (1024 fp32 threads per
+    row, or at V = 32000 its slices), B = 40 gives 280 rows (256 fp32
+    threads per row), both k_trunc16 for 16-bit rows; B = 110 gives 770 rows,
+    k_topk16's.  V = 3001, 3004, 3005 and 3007 end each row with a partial
+    vector of 1, 4, 5 and 7 logits, taken after the stream by lanes whose
+    lists may be nearly full (ascending rows)."""
     g = torch.Generator(device=DEV).manual_seed(V + B)
     tdt = synthetic.DTYPES[dtype]
     k = 3
@@ -419,6 +421,68 @@ def test_truncated_fp32_large_vocabulary(sv):
     check(sv, w, T, x, 0, 0.95)
 
 
+def sliced_rows(V, tdt, g):
+    """Rows for the sliced pass (B = 1, k = 4): five target rows, then four
+    draft rows.  Target: plain normal; 5000 logits tied at the top, spread
+    over every slice (more candidates than the merge gathers); 100 distinct
+    large logits over 600 tied just below them (at top-k 256 the kept tie
+    group outgrows the merge); the first half masked (whole slices with no
+    finite logit); ten finite logits, all in the last 300 (the last slice and
+    its partial vector).  Draft: normal; ascending (the largest in the last
+    slice); a dozen values (ties everywhere); one finite logit."""
+    n = torch.randn((9, V), generator=g, device=DEV)
+    z = n[:5].clone()
+    z[1, torch.arange(0, V, V // 5000, device=DEV)[:5000]] = 8.0
+    z[2] = z[2] - 5.0
+    p = torch.randperm(V, generator=g, device=DEV)
+    z[2, p[:100]] = 10.0 + 4.0 * torch.rand((100,), generator=g, device=DEV)
+    z[2, p[100:700]] = 9.0
+    z[3, :V // 2] = -float("inf")
+    last = V - 300 + torch.randperm(300, generator=g, device=DEV)[:10]
+    keep = z[4, last].clone()
+    z[4] = -float("inf")
+    z[4, last] = keep
+    y = n[5:].clone()
+    y[1] = torch.sort(y[1]).values
+    y[2] = torch.randint(-6, 6, (V,), generator=g, device=DEV).float() * 0.5
+    one = int(torch.randint(V, (1,), generator=g, device=DEV))
+    y[3] = -float("inf")
+    y[3, one] = 1.0
+    return z.to(tdt).view(1, 5, V), y.to(tdt).view(1, 4, V)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_truncated_sliced_rows(sv, dtype):
+    """B = 1 at V = 128259: fp32 rows are cut into 31 slices, summarised apart
+    and merged per row; 16-bit rows take the histogram pass.  Against the
+    oracle on rows built to reach the merge's limits (sliced_rows), and bit
+    for bit against the same sequence verified inside a batch of 100, whose
+    900 rows take the candidate lists whole (one workgroup per row)."""
+    V = 128259
+    g = torch.Generator(device=DEV).manual_seed(59)
+    tdt = synthetic.DTYPES[dtype]
+    z, y = sliced_rows(V, tdt, g)
+    u = synthetic.uniforms24((1, 5), g, DEV)
+    w = synthetic.Workload(synthetic.WORKLOADS[1], z, y, None, u, 0.9)
+    # the batch of 100: this sequence first, plain normal rows after it
+    NB = 100
+    zb = torch.randn((NB, 5, V), generator=g, device=DEV).to(tdt)
+    yb = torch.randn((NB, 4, V), generator=g, device=DEV).to(tdt)
+    zb[0], yb[0] = z[0], y[0]
+    ub = synthetic.uniforms24((NB, 5), g, DEV)
+    ub[0] = u[0]
+    for top_k, top_p in ((50, 1.0), (256, 0.9), (5, 0.5)):
+        x = torch.from_numpy(truncated_drafts(f32(y), 0.9, top_k, top_p, 23)).to(DEV)
+        check(sv, w, 0.9, x, top_k, top_p)
+        xb = torch.randint(0, V, (NB, 4), generator=g, device=DEV, dtype=torch.int32)
+        xb[0] = x[0]
+        a = sv.sample_truncated(z, y, x, u, 0.9, top_k, top_p, return_probs=True)
+        b = sv.sample_truncated(zb, yb, xb, ub, 0.9, top_k, top_p, return_probs=True)
+        torch.cuda.synchronize()
+        for ta, tb in zip(a, b):
+            assert torch.equal(ta[0], tb[0]), (top_k, top_p)
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_truncated_k63(sv, dtype):
     """The longest draft one wave decides (k = 63)."""
@@ -469,7 +533,9 @@ def random_small_top_k_case(i):
     r = np.random.default_rng(7000 + i)
     dtype = ["fp16", "bf16"][int(r.integers(2))]
     V = int(np.exp(r.uniform(np.log(8.0), np.log(200000.0))))
-    rows = int(max(1, min(24, 3_000_000 // V)))
+    # even cases: few rows (k_trunc16 for 16-bit, slices for long fp32 rows);
+    # odd: 780 rows (k_topk16, 256 fp32 threads per row)
+    rows = int(max(1, min(24, 3_000_000 // V))) if i % 2 == 0 else 780
     top_k = int(r.integers(1, 257))
     top_p = float(r.choice([1.0, 0.999, 0.9, 0.5, 0.1, 1e-6]))
     law = int(r.integers(4))
