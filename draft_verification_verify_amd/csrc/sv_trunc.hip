@@ -11,10 +11,13 @@
 //   together.  Both keep a set {t : key(z_t) >= tau} for an ordering key
 //   (key_of), so a row is summarised by (m, tau, kept mass).
 //
-// Four kernels find tau and the kept mass:
-//  - k_topk16 and k_topk32 (16-bit and fp32 rows under a top-k of at most
-//    256): one pass per row keeping only the logits that can still be among
-//    the top_k largest, the thresholds found among those;
+// Five kernels find tau and the kept mass:
+//  - k_topk16 and k_topk32 (16-bit rows under a top-k of at most 256 that
+//    outnumber the compute units more than three times; fp32 rows under such
+//    a top-k): one pass per row keeping only the logits that can still be
+//    among the top_k largest, the thresholds found among those;
+//  - k_trunc_merge: few fp32 rows are cut into slices, each k_topk32's, whose
+//    candidates one workgroup per row merges;
 //  - k_trunc16 (other fp16 / bf16 rows): one pass per row, an exact count of
 //    all 65536 bit patterns in LDS, the thresholds read off the histogram;
 //  - k_trunc_rows (other fp32 rows, and the rare row the one-pass kernels
@@ -1583,6 +1586,8 @@ __global__ __launch_bounds__(kTK) __attribute__((amdgpu_waves_per_eu(8))) void k
 // one row: 256 (eight workgroups to a CU) when the rows outnumber the compute
 // units, else 1024, so that few rows still keep many loads in flight (a
 // 32000-logit row is one load per 16 bytes of the workgroup's first round).
+// With SPLIT, a 256-thread workgroup takes one slice of a row (split_slices)
+// and ends with the slice's candidates (slice_candidates) for k_trunc_merge.
 
 // list entries per lane: 16 with 1024 threads (one workgroup to a CU), 12
 // with 256 (eight to a CU)
