@@ -327,6 +327,29 @@ __device__ __forceinline__ const char* trunc_row_ptr(const TruncArgs& a, int row
                                  : row_ptr(a.draft, row - a.n_target_rows, a.d_stride, ES);
 }
 
+// Radix digits of a key's offset o from a base, for keys spanning [base,
+// base + range]: the first level takes the top (up to) 8 of the bits the
+// range needs, each later one the next 8; level l's digit is o's bits
+// [ls, hs) (level 0: every bit from ls up), ls = shift(l), hs = shift(l - 1).
+struct OffDigits {
+    int top;                           // bits the range needs (0: a single key)
+    __device__ explicit OffDigits(uint32_t range) : top(range ? 32 - __clz((int)range) : 0) {}
+    __device__ int shift(int l) const
+    {
+        const int s = top - 8 * (l + 1);
+        return s > 0 ? s : 0;
+    }
+    __device__ static uint32_t digit(uint32_t o, int level, int hs, int ls)
+    {
+        return level == 0 ? o >> ls : (o >> ls) & ((1u << (hs - ls)) - 1u);
+    }
+};
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    return (uint32_t)wave_max_int((int)(v ^ 0x80000000u)) ^ 0x80000000u;
+}
+
 template <int DT, typename Src>
 __device__ __forceinline__ void trunc_row_radix(const TruncArgs& a, int row, Shared& sh, const Src& src)
 {
@@ -409,6 +432,230 @@ __device__ __forceinline__ void trunc_row_radix(const TruncArgs& a, int row, Sha
     __syncthreads();                   // the shared state is reused by the next row
 }
 
+// key_of's fp32 key back to the value (+0.0 for the merged zero)
+__device__ __forceinline__ float value_of_key32(uint32_t k)
+{
+    return __uint_as_float(k >= 0x80000000u ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// ---- fp32 rows: value bins first ---------------------------------------------
+// The radix passes' first digit of an fp32 key is its sign and top exponent
+// bits, so a row's logits fall into a handful of bins and the passes' LDS
+// atomics serialise on them.  For fp32 rows the first level instead bins the
+// finite logits by value, kBins equal intervals from the smallest finite
+// logit to the max: bin(z) = floor((z/2 - zlo/2) s), clamped (halving keeps
+// the difference finite; each step is monotone in z, so a bin never holds a
+// key above one of a higher bin, and equal keys share a bin).  One pass
+// counts (top-k) and sums the fixed-point masses (top-p, the kept mass) of
+// every bin; -inf logits are counted apart (they carry no mass).  The bin
+// where a selection crosses its threshold is then gathered, at most kBins
+// keys, and the threshold key found among them by radix levels on the
+// offset from their smallest key, with the radix passes' integer sums and
+// their >= rule, so tau and the kept mass are the radix passes' own.  A
+// boundary bin too full to gather (long runs of equal or nearly equal
+// logits) sends the row to the radix passes.
+
+struct BinShared {
+    uint32_t hc[256];
+    u64 hm[256];
+    uint32_t n;
+};
+
+__device__ __forceinline__ int value_bin(float z, float hz, float s)
+{
+    const float t = (0.5f * z - hz) * s;           // >= 0, finite
+    return (int)fminf(t, (float)(kBins - 1));
+}
+
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, u64* lds)
+{
+    v = wave_max_u32(v);
+    if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = v;
+    __syncthreads();
+    uint32_t r = 0;
+#pragma unroll
+    for (int w = 0; w < kTW; ++w) r = (uint32_t)lds[w] > r ? (uint32_t)lds[w] : r;
+    __syncthreads();
+    return r;
+}
+
+// The keys of the finite logits in value bin b into sh.cnt (any order);
+// their number, which exceeds kBins when they do not fit.
+template <typename Src>
+__device__ __forceinline__ uint32_t gather_bin(const Src& src, int b, float hz, float s, Shared& sh, BinShared& bs)
+{
+    if (threadIdx.x == 0) bs.n = 0;
+    __syncthreads();
+    src.each([&](float z) {
+        if (z != -INFINITY && value_bin(z, hz, s) == b) {
+            const uint32_t pos = atomicAdd(&bs.n, 1u);
+            if (pos < (uint32_t)kBins) sh.cnt[pos] = key_of<DT_F32>(z);
+        }
+    });
+    __syncthreads();
+    return bs.n;
+}
+
+// Among the n gathered keys (sh.cnt) at or above lo: the largest key tau
+// with base + (sum over the keys >= tau of 1, or of their masses if MASS) >=
+// thr, one 8-bit digit of the offset from the smallest key per level; the
+// caller guarantees that all of them reach thr.  *incl gets that sum.
+template <bool MASS>
+__device__ __forceinline__ void list_select(Shared& sh, BinShared& bs, uint32_t n, uint32_t lo, u64 base, double thr,
+                            float m, float c, uint32_t* tau, u64* incl)
+{
+    constexpr int P = kBins / kTB;
+    const int t = (int)threadIdx.x;
+    uint32_t k[P];
+    u64 v[P];
+    uint32_t kmx = 0u, nmn = 0u;       // the largest key, and the complement of the smallest
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        const uint32_t i = (uint32_t)(t + p * kTB);
+        const uint32_t key = i < n ? sh.cnt[i] : 0u;
+        k[p] = key >= lo ? key : 0u;   // 0: none (no finite logit has key 0)
+        v[p] = k[p] ? (MASS ? fixed40(weight(value_of_key32(k[p]), m, c)) : 1u) : 0u;
+        if (k[p]) {
+            kmx = k[p] > kmx ? k[p] : kmx;
+            nmn = ~k[p] > nmn ? ~k[p] : nmn;
+        }
+    }
+    kmx = block_max_u32(kmx, sh.red);
+    const uint32_t kmn = ~block_max_u32(nmn, sh.red);
+    const OffDigits od(kmx - kmn);
+    uint32_t prefix = 0u;
+    u64 b = base;
+    int hs = od.top, ls = od.shift(0);
+    for (int level = 0;; ++level) {
+        if (t < 256) {
+            if (MASS) bs.hm[t] = 0;
+            else bs.hc[t] = 0u;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const uint32_t o = k[p] - kmn;
+            if (k[p] && (level == 0 || (o >> hs) == prefix)) {
+                if (MASS) atomicAdd(&bs.hm[OffDigits::digit(o, level, hs, ls)], v[p]);
+                else atomicAdd(&bs.hc[OffDigits::digit(o, level, hs, ls)], 1u);
+            }
+        }
+        __syncthreads();
+        if (MASS) select_desc(bs.hm, 1 << (hs - ls), b, thr, sh);
+        else select_desc(bs.hc, 1 << (hs - ls), b, thr, sh);
+        const int d = sh.sel < 0 ? 0 : sh.sel;
+        const u64 own = MASS ? bs.hm[d] : (u64)bs.hc[d];
+        prefix = (prefix << (hs - ls)) | (uint32_t)d;
+        *incl = sh.incl;
+        b = sh.incl - own;             // everything above the chosen digit
+        __syncthreads();               // the histogram is cleared next
+        if (ls == 0) break;
+        hs = ls;
+        ls = od.shift(level + 1);
+    }
+    *tau = kmn + prefix;
+}
+
+// One fp32 row by value bins; false (uniform) when a boundary bin holds more
+// than kBins logits: the row is then left to the radix passes.
+template <typename Src>
+__device__ __forceinline__ bool trunc_row_binned(const TruncArgs& a, int row, Shared& sh, BinShared& bs, const Src& src)
+{
+    const int V = a.V;
+    const float c = a.c;
+    const bool topk = a.top_k >= 1 && a.top_k < V;
+    const bool topp = a.top_p < 1.f;
+    const int t = (int)threadIdx.x;
+
+    // pass 1: the max and the smallest finite logit
+    float mx = -INFINITY, mn = INFINITY;
+    src.each([&](float z) {
+        mx = fmaxf(mx, z);
+        if (z != -INFINITY) mn = fminf(mn, z);
+    });
+    const float m = block_max<kTW>(mx, sh.redf);
+    if (m == -INFINITY) {              // nothing to keep; the rule never reads such a row
+        if (t == 0) a.rows[row] = TruncRow{m, -INFINITY, 0u, 0u};
+        __syncthreads();
+        return true;
+    }
+    const float zlo = -block_max<kTW>(-mn, sh.redf);
+    const float hz = 0.5f * zlo;
+    const float s = m > zlo ? fminf((float)(kBins - 1) / (0.5f * m - hz), 1e30f) : 0.f;
+
+    // pass 2: each bin's count (top-k) and mass
+    for (int i = t; i < kBins; i += kTB) {
+        if (topk) sh.cnt[i] = 0u;
+        sh.mass[i] = 0;
+    }
+    __syncthreads();
+    src.each([&](float z) {
+        if (z == -INFINITY) return;
+        const int b = value_bin(z, hz, s);
+        if (topk) atomicAdd(&sh.cnt[b], 1u);
+        const u64 f = fixed40(weight(z, m, c));
+        if (f) atomicAdd(&sh.mass[b], f);
+    });
+    __syncthreads();
+
+    // top-k: the top_k-th largest key lo (keys >= lo survive); its bin bk
+    // (-1: every finite logit survives) and the survivors' mass M
+    uint32_t lo = 0u, nk = 0u;
+    int bk = -1;
+    u64 M = 0, mk = 0;                 // mk: the survivors' mass inside bin bk
+    if (topk) {
+        select_desc(sh.cnt, kBins, 0, (double)a.top_k, sh);
+        bk = sh.sel;
+        if (bk >= 0) {
+            const uint32_t above = (uint32_t)(sh.incl - sh.cnt[bk]);
+            __syncthreads();           // sh.cnt is overwritten by the gather
+            nk = gather_bin(src, bk, hz, s, sh, bs);
+            if (nk > (uint32_t)kBins) return false;
+            u64 incl;
+            list_select<false>(sh, bs, nk, 0u, above, (double)a.top_k, m, c, &lo, &incl);
+            u64 mine = 0;
+            for (int i = t; i < (int)nk; i += kTB) {
+                const uint32_t key = sh.cnt[i];
+                if (key >= lo) mine += fixed40(weight(value_of_key32(key), m, c));
+            }
+            mk = block_sum_u64(mine, sh.red);
+        } else {
+            lo = key_of<DT_F32>(-INFINITY);   // the top_k-th largest is -inf: every key survives
+        }
+    }
+    {
+        u64 mine = 0;
+        for (int i = t; i < kBins; i += kTB)
+            if (i > bk) mine += sh.mass[i];
+        M = block_sum_u64(mine, sh.red) + mk;
+    }
+
+    uint32_t tau = lo;
+    u64 kept = M;
+    if (topp) {
+        const double budget = (double)a.top_p * (double)M;
+        // the bins wholly above bk first, highest first
+        select_desc(sh.mass + (bk + 1), kBins - 1 - bk, 0, budget, sh);
+        const int sel = sh.sel;
+        if (sel >= 0) {
+            const int bp = bk + 1 + sel;
+            const u64 above = sh.incl - sh.mass[bp];
+            __syncthreads();
+            const uint32_t np = gather_bin(src, bp, hz, s, sh, bs);
+            if (np > (uint32_t)kBins) return false;
+            list_select<true>(sh, bs, np, 0u, above, budget, m, c, &tau, &kept);
+        } else {                       // inside bin bk, among the survivors
+            list_select<true>(sh, bs, nk, lo, M - mk, budget, m, c, &tau, &kept);
+        }
+    }
+    if (t == 0) {
+        const float l2s = (float)(log2((double)kept) - (double)kFixBits);
+        a.rows[row] = TruncRow{m, l2s, tau, 0u};
+    }
+    __syncthreads();                   // the shared state is reused by the next row
+    return true;
+}
+
 // fp32 rows of at most kLdsRowMax logits: each workgroup loads its row into
 // LDS once and runs the radix passes on the LDS copy, instead of streaming
 // the row again for every digit.  The copy and the radix state fill most of
@@ -417,11 +664,13 @@ template <bool VEC>
 __global__ __launch_bounds__(kTB) void k_trunc_rows_lds(TruncArgs a)
 {
     __shared__ Shared sh;
+    __shared__ BinShared bs;
     __shared__ __attribute__((aligned(16))) float buf[kLdsRowMax];
     zero_counters(a);
     for (int row = blockIdx.x; row < a.n_rows; row += gridDim.x) {
         load_row_lds<VEC>(buf, trunc_row_ptr<DT_F32>(a, row), a.V);
-        trunc_row_radix<DT_F32>(a, row, sh, LdsRow{buf, a.V});
+        if (!trunc_row_binned(a, row, sh, bs, LdsRow{buf, a.V}))
+            trunc_row_radix<DT_F32>(a, row, sh, LdsRow{buf, a.V});
     }
 }
 
@@ -433,12 +682,18 @@ template <int DT, bool VEC>
 __global__ __launch_bounds__(kTB) void k_trunc_rows(TruncArgs a)
 {
     __shared__ Shared sh;
+    __shared__ BinShared bs;
     __shared__ int marked[kTB];
     __shared__ int n_marked;
     if (!a.only_marked) {
         zero_counters(a);
-        for (int row = blockIdx.x; row < a.n_rows; row += gridDim.x)
-            trunc_row_radix<DT>(a, row, sh, StreamRow<DT, VEC>{trunc_row_ptr<DT>(a, row), a.V});
+        for (int row = blockIdx.x; row < a.n_rows; row += gridDim.x) {
+            const StreamRow<DT, VEC> src{trunc_row_ptr<DT>(a, row), a.V};
+            if constexpr (DT == DT_F32) {
+                if (trunc_row_binned(a, row, sh, bs, src)) continue;
+            }
+            trunc_row_radix<DT>(a, row, sh, src);
+        }
         return;
     }
     for (int base = blockIdx.x * kTB; base < a.n_rows; base += gridDim.x * kTB) {
@@ -1075,44 +1330,21 @@ __device__ __forceinline__ void find_desc_mass(const u64* h, u64 base, double bu
     above = readlane_u64(a, L);
 }
 
-// Radix digits of a key's offset o from a base, for keys spanning [base,
-// base + range]: the first level takes the top (up to) 8 of the bits the
-// range needs, each later one the next 8; level l's digit is o's bits
-// [ls, hs) (level 0: every bit from ls up), ls = shift(l), hs = shift(l - 1).
-struct OffDigits {
-    int top;                           // bits the range needs (0: a single key)
-    __device__ explicit OffDigits(uint32_t range) : top(range ? 32 - __clz((int)range) : 0) {}
-    __device__ int shift(int l) const
-    {
-        const int s = top - 8 * (l + 1);
-        return s > 0 ? s : 0;
-    }
-    __device__ static uint32_t digit(uint32_t o, int level, int hs, int ls)
-    {
-        return level == 0 ? o >> ls : (o >> ls) & ((1u << (hs - ls)) - 1u);
-    }
-};
-
 constexpr int kMergeMax = 4096;        // candidates the merge of a row's slices gathers
-
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
-{
-    return (uint32_t)wave_max_int((int)(v ^ 0x80000000u)) ^ 0x80000000u;
-}
 
 // A slice's candidates, when fp32 rows are cut into S slices: the keys at or
 // above the slice's floor Fs.  Fs is the largest floor Fg of its waves when
 // the n keys at or above Fg are few (at most K1, or S * n at most half of
-// what the merge gathers), else the K1-th largest of those n keys.  Either way K1 different
-// logits of the row are at least Fs (a wave raises its floor only under K1
-// of its own keys), so Fs never passes the row's top_k-th largest key, and
-// every key at or above the largest floor of a row's slices is among the
-// row's candidates.  kr: this lane's keys (0 for
-// none; keys below the wave's floor are skipped), F: its wave's floor.  Wave
-// 0 writes the keys and a header (Fs, the largest key, their number, and an
-// overflow flag, set when a wave's list overflowed or when the keys at or
-// above Fs outnumber kCandMax).  The list area holds the J keys of each of
-// the NT lanes.  Called by every thread of the workgroup.
+// what the merge gathers), else the K1-th largest of those n keys.  Either
+// way K1 different logits of the row are at least Fs (a wave raises its
+// floor only under K1 of its own keys), so Fs never passes the row's
+// top_k-th largest key, and every key at or above the largest floor of a
+// row's slices is among the row's candidates.  kr: this lane's keys (0 for
+// none; keys below the wave's floor are skipped), F: its wave's floor.
+// Wave 0 writes the keys and a header (Fs, the largest key, their number,
+// and an overflow flag, set when a wave's list overflowed or when the keys
+// at or above Fs outnumber kCandMax).  The list area holds the J keys of
+// each of the NT lanes.  Called by every thread of the workgroup.
 template <int NT, int J>
 __device__ __forceinline__ void slice_candidates(const uint32_t (&kr)[J], uint32_t F, uint32_t K1, int S, uint32_t* list, uint32_t* wh0, uint32_t* sF, uint32_t* smx,
                                                  const uint32_t* sover, uint32_t* snk, uint32_t* cand, uint32_t* hdr)
@@ -1605,12 +1837,6 @@ struct Topk32Shared {
     uint32_t over[NW];
     uint32_t nk;
 };
-
-// key_of's fp32 key back to the value (+0.0 for the merged zero)
-__device__ __forceinline__ float value_of_key32(uint32_t k)
-{
-    return __uint_as_float(k >= 0x80000000u ? (k & 0x7FFFFFFFu) : ~k);
-}
 
 __device__ __forceinline__ uint32_t key32(uint32_t x)
 {

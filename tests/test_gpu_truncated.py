@@ -402,6 +402,40 @@ def test_truncated_small_top_k_fp32(sv, V, B):
         check(sv, w, 0.8, x, top_k, top_p)
 
 
+@pytest.mark.parametrize("V", [3001, 32000, 40000])
+def test_truncated_fp32_value_bins(sv, V):
+    """fp32 rows under top-p alone, or a top-k beyond the candidate lists,
+    are binned by value first and the boundary bin gathered (V <= 32768 from
+    an LDS copy of the row, 40000 streamed): on rows built to stress it
+    (small_top_k_rows), bf16 values upcast to fp32 must give, bit for bit,
+    what the 16-bit histogram pass gives on the bf16 rows, at top-k 0, 257,
+    300, 1000 and V - 1 with top-p from off to 1e-6; fp32-only rows are
+    checked against the oracle.  Constant rows and a dozen repeated values
+    leave boundary bins too full to gather (the radix passes take them);
+    magnitudes near 3e38 make the bins' scale tiny."""
+    g = torch.Generator(device=DEV).manual_seed(V + 77)
+    B, k = 12, 3
+    z = small_top_k_rows(B * (k + 1), V, torch.bfloat16, g).view(B, k + 1, V)
+    y = small_top_k_rows(B * k + 5, V, torch.bfloat16, g)[5:].view(B, k, V)
+    u = synthetic.uniforms24((B, k + 1), g, DEV)
+    tok = torch.randint(0, V, (B, k), generator=g, device=DEV, dtype=torch.int32)
+    for top_k in (0, 257, 300, 1000, V - 1):
+        for top_p in (1.0, 0.9, 0.5, 1e-6):
+            if top_k == 0 and top_p >= 1.0:
+                continue
+            a = sv.sample_truncated(z, y, tok, u, 0.8, top_k, top_p, return_probs=True)
+            b = sv.sample_truncated(z.float(), y.float(), tok, u, 0.8, top_k, top_p, return_probs=True)
+            torch.cuda.synchronize()
+            for ta, tb in zip(a, b):
+                assert torch.equal(ta, tb), (top_k, top_p)
+    zf = small_top_k_rows(B * (k + 1), V, torch.float32, g).view(B, k + 1, V)
+    yf = small_top_k_rows(B * k + 5, V, torch.float32, g)[5:].view(B, k, V)
+    w = synthetic.Workload(synthetic.WORKLOADS[1], zf, yf, None, u, 0.8)
+    for top_k, top_p in ((0, 0.8), (0, 1e-6), (300, 0.9), (1000, 1.0)):
+        x = torch.from_numpy(truncated_drafts(f32(yf), 0.8, top_k, top_p, 19)).to(DEV)
+        check(sv, w, 0.8, x, top_k, top_p)
+
+
 @pytest.mark.parametrize("V", [32767, 32768, 32769])
 @pytest.mark.parametrize("top_k,top_p", [(0, 0.9), (300, 0.9), (40, 0.9)])
 def test_truncated_fp32_lds_boundary(sv, V, top_k, top_p):
