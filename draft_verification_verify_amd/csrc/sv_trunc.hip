@@ -21,10 +21,12 @@
 //  - k_trunc16 (other fp16 / bf16 rows): one pass per row, an exact count of
 //    all 65536 bit patterns in LDS, the thresholds read off the histogram;
 //  - k_trunc_rows (other fp32 rows, and the rare row the one-pass kernels
-//    cannot summarise): radix selection on the key, most significant digit first (11, 11
-//    and 10 bits for fp32 keys; 11 then 5 for 16-bit keys), one 512-thread
-//    workgroup per row streaming the row once per digit (the first pass from
-//    HBM, the rest mostly from cache) and histogramming the next digit of the
+//    cannot summarise): one 512-thread workgroup per row streaming the row
+//    once per pass (the first from HBM, the rest mostly from cache).  fp32
+//    rows are first binned by value and the threshold found among the keys
+//    of the boundary bin (trunc_row_binned); otherwise radix selection on
+//    the key, most significant digit first (11, 11 and 10 bits for fp32
+//    keys; 11 then 5 for 16-bit keys), histogramming the next digit of the
 //    keys that share the prefix chosen so far: counts for top-k, masses for
 //    top-p.  k_trunc_rows_lds runs the same passes on fp32 rows of at most
 //    32768 logits held in LDS, read from memory once.
