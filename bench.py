@@ -58,10 +58,11 @@ TRUNC_NOTES = {
                        "the radix passes for rows the slices could not summarise)",
     "k_trunc16": "k_trunc16 (one pass per 16-bit row: an exact LDS histogram of all 65536 bit "
                  "patterns) followed by k_trunc_rows over the rows it marked",
-    "k_trunc_rows_lds": "k_trunc_rows_lds (radix selection on an LDS copy of each fp32 row, "
-                        "read from HBM once)",
-    "k_trunc_rows": "k_trunc_rows (radix selection, one workgroup per row; the first digit's "
-                    "pass reads the row from HBM, later ones mostly from cache)",
+    "k_trunc_rows_lds": "k_trunc_rows_lds (on an LDS copy of each fp32 row, read from HBM once: "
+                        "value bins, then radix levels among the boundary bin's keys)",
+    "k_trunc_rows": "k_trunc_rows (one workgroup per row, each pass streaming the row, the first "
+                    "from HBM and later ones mostly from cache: value bins, then radix levels "
+                    "among the boundary bin's keys for fp32 rows, radix selection otherwise)",
 }
 
 
