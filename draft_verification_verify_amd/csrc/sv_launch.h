@@ -42,7 +42,7 @@ struct StatsArgs {
     float c;                           // log2(e) / T (softmax statistics only)
     void* partials;                    // [n_rows][splits] SoftPartial or ArgPartial
     int* zero;                         // softmax statistics: n_zero counters that a later
-    int n_zero;                        // kernel of the call needs at 0 (<= kBlock; else null, 0)
+    int n_zero;                        // kernel of the call needs at 0 (null, 0: none)
 };
 
 // One sampling step per sequence, prepared by the decision kernel: draw from

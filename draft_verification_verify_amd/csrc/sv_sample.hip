@@ -260,7 +260,11 @@ __device__ __forceinline__ void chunk_totals(const SampleArgs& a, int b, int g, 
             const int ch = rr / a.vec_per_chunk;
             const int cend = min((ch + 1) * a.vec_per_chunk, a.nvec);
             if (rr + kBlock >= cend) {            // the chunk's last round
-                if (threadIdx.x == 0) a.chunk_sums[(long long)b * a.nchunks + ch] = acc;
+                // written through to the device's coherence point (a relaxed
+                // agent-scope store), for a draw in this launch to read
+                if (threadIdx.x == 0)
+                    __hip_atomic_store(a.chunk_sums + (long long)b * a.nchunks + ch, acc, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
                 acc = 0.f;
             }
         }
@@ -337,8 +341,37 @@ __device__ __forceinline__ void pick_sequence(const SampleArgs& a, int b, const 
     }
 }
 
-// The chunk pass after a separate decision (early exit): the descriptor
-// comes from the decision kernels.
+// After the chunk totals of sequence b in a fused pass: true (uniform over
+// the workgroup) in the last of the sequence's workgroups to finish, which
+// then makes the draw.  The count is a per-sequence counter (a.done, zeroed
+// by the call's first kernel).  Thread 0 wrote this workgroup's totals with
+// relaxed agent-scope stores, which write through to the device's coherence
+// point; it waits for them to be acknowledged (vmcnt counts stores on this
+// architecture) before adding 1 to the counter, so a workgroup that sees
+// every other count finds every total there too and reads them with
+// agent-scope loads.  Neither side writes back or invalidates its XCD's L2,
+// as an acquire-release increment would.
+__device__ __forceinline__ bool last_of_sequence(const SampleArgs& a, int b, int* s_last)
+{
+    if (threadIdx.x == 0) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        const int before = __hip_atomic_fetch_add(a.done + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_last = before == a.blocks_per_seq - 1;
+    }
+    __syncthreads();
+    return *s_last != 0;
+}
+
+// This thread's chunk total for the draw (threads past the chunks repeat the last).
+__device__ __forceinline__ float draw_total(const SampleArgs& a, int b)
+{
+    const int ct = min((int)threadIdx.x, a.nchunks - 1);
+    return __hip_atomic_load(a.chunk_sums + (long long)b * a.nchunks + ct, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The chunk pass after a separate decision (large batches, early exit): the
+// descriptor comes from the decision kernels.
 template <int DT, bool VEC, bool MASK>
 __global__ __launch_bounds__(kBlock) void k_sample_chunks(SampleArgs a)
 {
@@ -357,13 +390,8 @@ __global__ __launch_bounds__(kBlock) void k_sample_chunks(SampleArgs a)
 // of reading the sequence's row statistics (a few hundred bytes) once per
 // workgroup.  MASK: truncated rows.
 //
-// PICK (small passes): the sequence's last workgroup to finish also makes the
-// draw, found with a per-sequence counter (a.done, zeroed by the call's first
-// kernel): each workgroup's thread 0, which wrote its chunk totals, adds 1 with
-// agent-scope release and acquire, and the workgroup that sees
-// blocks_per_seq - 1 reads every total after an agent-scope acquire.  On this
-// chip each such release writes back the XCD's L2 and each acquire
-// invalidates it: cheap for a few dozen workgroups, ruinous for thousands.
+// PICK: the sequence's last workgroup to finish also makes the draw
+// (last_of_sequence).
 template <int DT, bool VEC, bool MASK, bool PICK>
 __global__ __launch_bounds__(kBlock) void k_decide_chunks(DecideSampleArgs da, SampleArgs a)
 {
@@ -381,17 +409,9 @@ __global__ __launch_bounds__(kBlock) void k_decide_chunks(DecideSampleArgs da, S
     const SampleDesc d = s_desc;
     chunk_totals<DT, VEC, MASK>(a, b, g, d, lds);
     if constexpr (PICK) {
-        if (threadIdx.x == 0) {
-            const int before = __hip_atomic_fetch_add(a.done + b, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-            s_last = before == a.blocks_per_seq - 1;
-        }
-        __syncthreads();
-        if (!s_last) return;                      // uniform across the workgroup
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        if (!last_of_sequence(a, b, &s_last)) return;
         __shared__ PickShared ps;
-        const int ct = min((int)threadIdx.x, a.nchunks - 1);
-        const float my_sum = a.chunk_sums[(long long)b * a.nchunks + ct];
-        pick_sequence<DT, VEC, MASK>(a, b, d, my_sum, ps);
+        pick_sequence<DT, VEC, MASK>(a, b, d, draw_total(a, b), ps);
     }
 }
 

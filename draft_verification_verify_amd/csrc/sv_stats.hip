@@ -283,7 +283,8 @@ __global__ __launch_bounds__(kStatsBlock) void k_softmax_stats(StatsArgs a)
     const int split = unit - row * a.splits;
     const int v0 = split * a.vec_per_split;
     const int v1 = min(v0 + a.vec_per_split, a.nvec);
-    if (unit == 0 && (int)threadIdx.x < a.n_zero) a.zero[threadIdx.x] = 0;
+    if (unit == 0)
+        for (int i = (int)threadIdx.x; i < a.n_zero; i += kStatsBlock) a.zero[i] = 0;
     const SoftPartial r = slice_softmax<DT, VEC>(stats_row(a, row, ES), v0, v1, a.V, a.c, lds_m, lds_s);
     if (threadIdx.x == 0) reinterpret_cast<SoftPartial*>(a.partials)[unit] = r;
 }

@@ -318,7 +318,8 @@ __device__ __forceinline__ void hist_pass(const Src& src, int L, uint32_t prefix
 // launch's workgroup 0.
 __device__ __forceinline__ void zero_counters(const TruncArgs& a)
 {
-    if (blockIdx.x == 0 && (int)threadIdx.x < a.n_zero) a.zero[threadIdx.x] = 0;
+    if (blockIdx.x == 0)
+        for (int i = (int)threadIdx.x; i < a.n_zero; i += (int)blockDim.x) a.zero[i] = 0;
 }
 
 template <int DT>
