@@ -80,11 +80,12 @@ constexpr long long kFuseDecideBlocks = 2048;
 
 // Fused passes of at most this many workgroups also make the draw, in each
 // sequence's last workgroup (one dependent launch fewer), found with
-// per-sequence counters that the call's first kernel zeroes.  Larger passes
-// lose more than the launch: measured with the draw in every pass, workload
-// 5 went from 673 to 728 us per call, workload 3 from 201 to 223 us and
-// workload 2 from 22.7 to 25.8 us.
-constexpr long long kFusePickBlocks = 64;
+// per-sequence counters that the call's first kernel zeroes.  Measured from
+// graph replays: at 128 workgroups the fused draw saves 0.3-0.6 us a call
+// (B = 8 fp16 V = 32000 14.9 -> 14.3 us), at 256 it loses 0.7 us; with the
+// draw in every pass, workload 5 went from 673 to 728 us per call, workload
+// 3 from 201 to 223 us and workload 2 from 22.7 to 25.8 us.
+constexpr long long kFusePickBlocks = 128;
 
 struct SamplePlan {
     int nchunks;

@@ -17,7 +17,7 @@
 //  - k_sample_pick, one workgroup per sequence, accumulates the chunk totals
 //    in chunk order, finds the chunk where u * total is crossed, rescans only
 //    that chunk and resolves the token with a workgroup prefix scan.
-// A chunk pass of a few dozen workgroups makes the draw itself instead, in
+// A chunk pass of at most 128 workgroups makes the draw itself instead, in
 // the last workgroup of each sequence to finish (k_decide_chunks, PICK).
 // A round's total is the same block scan in both kernels and a chunk's total
 // is the sequential sum of its rounds' totals, so the two kernels agree bit

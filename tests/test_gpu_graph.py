@@ -60,15 +60,16 @@ def replay_and_compare(g, outs, load, eager, n):
 
 @pytest.mark.parametrize("mode", ["sample", "greedy", "sample_lazy", "greedy_lazy", "truncated",
                                   "truncated_top_p", "lenient"])
-@pytest.mark.parametrize("B,k,V,dtype", [(64, 6, 32000, "bf16"), (4, 4, 32000, "fp32")])
+@pytest.mark.parametrize("B,k,V,dtype", [(64, 6, 32000, "bf16"), (4, 4, 32000, "fp32"), (8, 4, 32000, "fp16")])
 def test_chain_entry_points_replay(sv, mode, B, k, V, dtype):
     """B = 64: the draw in a kernel of its own, and 832 16-bit rows, which
-    top-k 20 sends to the candidate lists (top-p alone: the histogram pass);
-    B = 4 (64 chunk workgroups, the most for which the chunk pass makes the
-    draw itself): the per-sequence counters must start every replay at zero,
-    cleared by the first kernel (no memset is captured); its 36 fp32 rows
-    take the candidate lists cut into slices and merged (top-k 20) and the
-    radix passes from LDS (top-p alone)."""
+    top-k 20 sends to the candidate lists (top-p alone: the histogram pass).
+    B = 4 (64 chunk workgroups) and B = 8 (128, the most for which the chunk
+    pass makes the draw itself): the per-sequence counters must start every
+    replay at zero, cleared by the first kernel (no memset is captured).
+    B = 4's 36 fp32 rows take the candidate lists cut into slices and merged
+    (top-k 20) and the value bins from LDS (top-p alone); B = 8's 72 fp16
+    rows the histogram pass."""
     sets = chain_sets(4, B, k, V, dtype)
     tgt = sets[0].target.clone()
     dft = sets[0].draft.clone()
