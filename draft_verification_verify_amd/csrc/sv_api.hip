@@ -74,9 +74,11 @@ constexpr long long kSampleBlocks = 16384;
 
 // Chunk passes of at most this many workgroups also decide the round (the
 // fused pass); measured: workload 1 (16 workgroups) 18.0 -> 15.9 us and
-// workload 2 (1024) 25.3 -> 22.6 us per call, while workload 3 (8192)
-// went from 200 to 210 us and workload 5 (16384) from 666 to 691 us.
-constexpr long long kFuseDecideBlocks = 2048;
+// workload 2 (1024) 25.3 -> 22.6 us per call, while at 2048 workgroups (B =
+// 128, k = 5, V = 32000 fp16) the fused pass lost 0.7 us (graph replays),
+// at 4096 2-3 us, and workload 3 (8192) went from 200 to 210 us and
+// workload 5 (16384) from 666 to 691 us.
+constexpr long long kFuseDecideBlocks = 1024;
 
 // Fused passes of at most this many workgroups also make the draw, in each
 // sequence's last workgroup (one dependent launch fewer), found with

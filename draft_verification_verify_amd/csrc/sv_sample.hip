@@ -12,8 +12,8 @@
 //    it alike) and streams the sampled row (pair) of every sequence once,
 //    writing the total weight of each chunk (a whole number of rounds of
 //    kBlock logical vectors), several rounds' loads in flight per thread;
-//    after the early-exit decision kernels, k_sample_chunks does the same
-//    from their descriptors;
+//    after a separate decision (large batches, early exit), k_sample_chunks
+//    does the same from its descriptors;
 //  - k_sample_pick, one workgroup per sequence, accumulates the chunk totals
 //    in chunk order, finds the chunk where u * total is crossed, rescans only
 //    that chunk and resolves the token with a workgroup prefix scan.
