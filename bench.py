@@ -143,7 +143,7 @@ def measured_traffic(kernel: str, cid: int):
 CHAIN_MODES = ("sample", "greedy", "greedy_ext", "lenient", "sample_lazy", "greedy_lazy", "truncated")
 CAND_MODES = ("candidates", "candidates_ext", "tree")
 MALL_DEFEAT_BYTES = 1 << 30            # inputs rotated over at least this many bytes (MALL: 256 MB)
-CPU_SHARE = 16                         # host CPUs the GPU machine gives one GPU's job
+CPU_SHARE = 16                         # host CPUs per GPU when one host serves several GPUs
 CEILING_VECS = (1024, 2048, 4096, 8192)  # workgroup sizes (16-byte vectors) of the plain streaming read
 
 
@@ -660,8 +660,9 @@ def cpu_baseline(w, out_t, out_n, budget_s):
         affinity = len(os.sched_getaffinity(0))
     except AttributeError:
         affinity = os.cpu_count() or 1
-    # the GPU machine gives one GPU's job a share of 16 of its host's CPUs (its
-    # worker pools are sized to that share, whatever the host has in all)
+    # a job that drives one GPU of a shared host gets a share of 16 of the
+    # host's CPUs (worker pools are sized to that share, whatever the host
+    # has in all)
     cores = max(1, min(CPU_SHARE, affinity))
     s1, t1 = run(1, budget_s / 4)
     sn, tn = run(cores, budget_s * 3 / 4)
