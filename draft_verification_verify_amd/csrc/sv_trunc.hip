@@ -596,8 +596,8 @@ __device__ __forceinline__ bool trunc_row_binned(const TruncArgs& a, int row, Sh
         if (z == -INFINITY) return;
         const int b = value_bin(z, hz, s);
         if (topk) atomicAdd(&sh.cnt[b], 1u);
-        const u64 f = fixed40(weight(z, m, c));
-        if (f) atomicAdd(&sh.mass[b], f);
+        // a zero mass is added too: a branch around the atomic costs more
+        atomicAdd(&sh.mass[b], fixed40(weight(z, m, c)));
     });
     __syncthreads();
 
